@@ -1,0 +1,178 @@
+"""fp64 CPU oracle for the R2L / forward selective scans -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg
+may import this package. The product (``reverse_mamba_selective_amd``) never
+imports it, and it never imports the product: the two share no code. The only
+common module is ``synth`` (seeded random inputs, no arithmetic of the method).
+
+The arithmetic lives in ``selective_scan_ref.c`` (plain fp64 loops; see its
+header for the passages of "Bifocal Diffusion Language Models" and "Training
+Hybrid Block Diffusion Language Models with Partial Bidirectionality" that it
+follows). This module only builds that file with gcc, marshals numpy arrays to
+contiguous fp64 and calls it.
+
+Function map (each a thin wrapper over the one C routine):
+
+* ``selective_scan``      -- the general routine (either direction, optional
+                             state in/out, readout, gated residual).
+* ``r2l_scan``            -- the R2L stream: reverse scan, readout, optional
+                             residual ``res + s * y`` (nl/fr summaries, section 2).
+* ``prefix_scan_state``   -- forward-only boundary state of each prefix
+                             (partial-bidirectionality summary, "Methodology" 1).
+* ``block_commit_state``  -- advance a cached boundary state over a committed
+                             block (same passage: finished blocks join the prefix).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "selective_scan_ref.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dptr = ctypes.POINTER(ctypes.c_double)
+_i64ptr = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, no FMA contraction)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class OracleLib:
+    """ctypes view of one build of selective_scan_ref.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        lib.ref_selective_scan.restype = ctypes.c_int
+        lib.ref_selective_scan.argtypes = [
+            ctypes.c_int, ctypes.c_int64, _i64ptr, ctypes.c_int64, ctypes.c_int64,
+            _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, ctypes.c_int,
+            _dptr, _dptr, _dptr, _dptr, ctypes.c_double, _dptr, ctypes.c_int]
+        lib.ref_max_threads.restype = ctypes.c_int
+        lib.ref_max_threads.argtypes = []
+        self.lib = lib
+        self.path = path
+
+
+def _load() -> OracleLib:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or \
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = OracleLib(_LIB_PATH)
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().lib.ref_max_threads())
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # a CPU torch tensor (bf16 is widened exactly)
+        import torch
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dptr)
+
+
+def _offsets(seq_offsets, batch, seqlen, tokens):
+    if seq_offsets is None:
+        if batch is None or seqlen is None:
+            raise ValueError("dense layout needs batch and seqlen")
+        off = np.arange(batch + 1, dtype=np.int64) * int(seqlen)
+    else:
+        off = np.ascontiguousarray(np.asarray(seq_offsets, dtype=np.int64))
+    if off[-1] != tokens:
+        raise ValueError("offsets end at %d but there are %d tokens" % (off[-1], tokens))
+    return off
+
+
+def selective_scan(x, dt, Bm, Cm, A, Dskip=None, *, reverse: bool,
+                   seq_offsets=None, batch=None, seqlen=None,
+                   delta_softplus: bool = True, h_in=None, want_h_out=False,
+                   want_y=True, res=None, s: float = 0.0, want_out=False,
+                   nthreads: int = 0, timing: dict | None = None,
+                   lib: OracleLib | None = None):
+    """Run the fp64 scan. x, dt: [tokens, D]; Bm, Cm: [tokens, N]; A: [D, N].
+
+    Returns a dict with fp64 numpy arrays ``y`` [tokens, D], ``out``
+    [tokens, D] and ``h_out`` [batch, D, N] as requested. If ``timing`` is a
+    dict, the wall time of the C call alone is stored under ``"seconds"``.
+    ``lib`` selects another build of the same source (the default is the
+    committed one).
+    """
+    x = _f64(x)
+    dt = _f64(dt)
+    Bm = _f64(Bm)
+    Cm = _f64(Cm)
+    A = _f64(A)
+    Dskip = _f64(Dskip)
+    h_in = _f64(h_in)
+    res = _f64(res)
+    tokens, D = x.shape
+    N = A.shape[1]
+    off = _offsets(seq_offsets, batch, seqlen, tokens)
+    nb = off.shape[0] - 1
+    assert dt.shape == (tokens, D) and Bm.shape == (tokens, N) and A.shape == (D, N)
+    if Cm is not None:
+        assert Cm.shape == (tokens, N)
+    if Dskip is not None:
+        assert Dskip.shape == (D,)
+    if h_in is not None:
+        h_in = h_in.reshape(nb, D, N)
+    if res is not None:
+        assert res.shape == (tokens, D)
+    y = np.empty((tokens, D)) if want_y else None
+    out = np.empty((tokens, D)) if want_out else None
+    h_out = np.empty((nb, D, N)) if want_h_out else None
+    t0 = time.perf_counter()
+    rc = (lib or _load()).lib.ref_selective_scan(
+        1 if reverse else 0, nb, off.ctypes.data_as(_i64ptr), D, N,
+        _ptr(x), _ptr(dt), _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
+        1 if delta_softplus else 0, _ptr(h_in), _ptr(h_out), _ptr(y),
+        _ptr(res), float(s), _ptr(out), int(nthreads))
+    if timing is not None:
+        timing["seconds"] = time.perf_counter() - t0
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
+    return {"y": y, "out": out, "h_out": h_out}
+
+
+def r2l_scan(x, dt, Bm, Cm, A, Dskip=None, *, res=None, s=0.0, **kw):
+    """R2L stream: reverse scan + readout, then out = res + s*y (s == 0: res)."""
+    kw.setdefault("want_out", True)
+    return selective_scan(x, dt, Bm, Cm, A, Dskip, reverse=True, res=res, s=s, **kw)
+
+
+def prefix_scan_state(x, dt, Bm, A, **kw):
+    """Forward-only boundary state after each prefix (state only, no readout)."""
+    r = selective_scan(x, dt, Bm, None, A, None, reverse=False, want_y=False,
+                       want_h_out=True, **kw)
+    return r["h_out"]
+
+
+def block_commit_state(state, x, dt, Bm, A, **kw):
+    """Cached boundary state advanced over each committed block."""
+    r = selective_scan(x, dt, Bm, None, A, None, reverse=False, want_y=False,
+                       want_h_out=True, h_in=state, **kw)
+    return r["h_out"]
