@@ -1,0 +1,532 @@
+#!/usr/bin/env python3
+"""Throughput of the R2L selective scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: one R2LM denoising step = 7 hooked reverse scans (every 4th
+of 28 decoder layers), each over a batch of 64 generation blocks of 32 tokens
+at D = 2048, N = 16, bf16 inputs with fp32 state, res = x and s ~ U(0, 0.1).
+Inputs are seeded synthetic tensors (``synth``), resident in HBM before the
+timed region; the buffer sets rotate over more than 1 GB so that every step
+reads HBM rather than the 256 MB Infinity Cache.
+
+One JSON line on stdout: ``value`` is token·channels per second of whole
+steps; ``roofline`` rates the dominant kernel (average launch duration from
+HIP events recorded around each launch during the timed region) against the
+roofline that binds it; ``cpu_baseline`` is the fp64 oracle timed on the host.
+Other workloads (``--workload``) are the prefill reverse scan (8 x 4096 x 4096),
+the ragged serving step (reverse scan + block commit over 256 blocks of
+U{16..64} tokens at D = 4096), the ragged prefix-state prefill, and the fp32
+block-restricted and tiny cases.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one fp32 VALU instruction per lane per clock
+VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# issue slots one v_exp_f32 / v_log_f32 takes, measured on gfx950
+TRANS_SLOTS = float(os.environ.get("R2L_TRANS_SLOTS", "2"))
+
+
+def alu_ops_per_tc(readout: bool, res: bool) -> float:
+    """Algorithmic VALU lane-ops per token·channel (N = 16), trans ops weighted.
+
+    per state n : exp(Delta*A) [trans] + Delta*A + B*(Delta*x) + state fma (+ readout fma)
+    per channel : softplus (2 trans + 4 ops) + Delta*x (+ Dskip fma) (+ gate fma)
+    """
+    per_n = TRANS_SLOTS + (4 if readout else 3)
+    per_tc = 2 * TRANS_SLOTS + 4 + 1 + (1 if readout else 0) + (1 if res else 0)
+    return 16 * per_n + per_tc
+
+
+def scan_bytes(tok, D, es, readout=True, res_separate=False, h_in=False, h_out=False, batch=0,
+               state_rw=False):
+    """Algorithmic HBM bytes: every input read once, every output written once."""
+    N = 16
+    b = tok * D * es * 2 + tok * N * es          # x, dt, Bm
+    b += 4 * D * N                               # A
+    if readout:
+        b += tok * N * es + tok * D * es + 4 * D  # Cm, out, Dskip
+        if res_separate:
+            b += tok * D * es
+    if h_in:
+        b += 4 * batch * D * N
+    if h_out:
+        b += 4 * batch * D * N
+    if state_rw:
+        b += 8 * batch * D * N
+    return b
+
+
+def kernel_sha() -> str:
+    p = os.path.join(ROOT, "reverse_mamba_selective_amd", "csrc", "scan_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(p):
+        return None
+    t = json.load(open(p))
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+class Workload:
+    name = ""
+    config: dict = {}
+    dtype = "bf16"
+
+    def setup(self, torch, r2l):
+        raise NotImplementedError
+
+    def step(self, i, stream, events=None):
+        raise NotImplementedError
+
+    def cpu_baseline(self, budget_s):
+        raise NotImplementedError
+
+
+def _dev(torch, a, dtype):
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).to("cuda")
+
+
+def _rotation(set_bytes, floor=1 << 30):
+    return max(1, math.ceil(floor / max(set_bytes, 1)))
+
+
+class Denoise(Workload):
+    """7 hooked reverse scans of one denoising step, 64 x 32 x 2048, bf16."""
+    name = "denoise_step_bf16_b64_blk32_D2048_N16_7hooks"
+    HOOKS, B, L, D = 7, 64, 32, 2048
+
+    def setup(self, torch, r2l):
+        import synth
+        self.torch = torch
+        self.gates = synth.denoise_gates()
+        self.inputs = [synth.denoise_hook_inputs(h) for h in range(self.HOOKS)]
+        tok = self.B * self.L
+        self.tc_per_launch = tok * self.D
+        self.tc_per_step = self.tc_per_launch * self.HOOKS
+        self.bytes_per_launch = scan_bytes(tok, self.D, 2, readout=True)
+        self.alu_per_launch = self.tc_per_launch * alu_ops_per_tc(True, True)
+        self.launches_per_step = self.HOOKS
+        base = []
+        for h, inp in enumerate(self.inputs):
+            g = {k: _dev(torch, getattr(inp, k), "bf16").view(self.B, self.L, -1)
+                 for k in ("x", "dt", "Bm", "Cm")}
+            g["A"] = torch.from_numpy(inp.A).cuda()
+            g["Dskip"] = torch.from_numpy(inp.Dskip).cuda()
+            base.append(g)
+        set_bytes = self.bytes_per_launch * self.HOOKS
+        self.R = _rotation(set_bytes)
+        self.calls = []
+        for r in range(self.R):
+            row = []
+            for h, g in enumerate(base):
+                x = g["x"].clone()
+                out = torch.empty_like(x)
+                row.append(r2l.bind("r2l_scan", x=x, dt=g["dt"].clone(), Bm=g["Bm"].clone(),
+                                    Cm=g["Cm"].clone(), A=g["A"], Dskip=g["Dskip"], res=x,
+                                    s=float(self.gates[h]), out=out))
+            self.calls.append(row)
+        self.config = {"workload": self.name, "batch": self.B, "block_tokens": self.L,
+                       "D": self.D, "N": 16, "hooks_per_step": self.HOOKS,
+                       "in_dtype": "bf16", "state_dtype": "fp32", "res": "x",
+                       "rotating_sets": self.R, "rotating_bytes": set_bytes * self.R,
+                       "parallelism": "single_gpu"}
+
+    def step(self, i, stream, events=None):
+        row = self.calls[i % self.R]
+        if events is None:
+            for c in row:
+                c.launch(stream)
+        else:
+            for c in row:
+                e0, e1 = events.next()
+                e0.record()
+                c.launch(stream)
+                e1.record()
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        tc, secs, reps = 0, 0.0, 0
+        while secs < budget_s and reps < 200:
+            for h, inp in enumerate(self.inputs):
+                t = {}
+                oracle.r2l_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, res=inp.x,
+                                s=float(self.gates[h]), seq_offsets=inp.offsets, timing=t,
+                                want_y=False)
+                secs += t["seconds"]
+                tc += inp.x.size
+            reps += 1
+        return {"value": tc / secs, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
+                "kind": "oracle",
+                "sample": "the full 7-hook step (%d token-channels), %d times, %.1f s of oracle "
+                          "time" % (self.tc_per_step, reps, secs)}
+
+
+class Events:
+    """Pre-created HIP event pairs recorded around launches on the current stream."""
+
+    def __init__(self, torch, count):
+        self.torch = torch
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(count)]
+        self.used = 0
+
+    def next(self):
+        e = self.pairs[self.used]
+        self.used += 1
+        return e
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in self.pairs[:self.used]]
+        return sum(ts) / len(ts), len(ts)
+
+
+def sleep_cycles_per_ms(torch):
+    """Calibrate torch.cuda._sleep (a spinning kernel) in cycles per millisecond."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    a.record()
+    torch.cuda._sleep(2_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / max(a.elapsed_time(b), 1e-3)
+
+
+def device_inputs(torch, key, lengths, D, dtype):
+    """Seeded inputs drawn on the GPU (same distributions as synth) for the large
+    workloads: x ~ N(0,1), dt ~ N(-2, 0.5), Bm, Cm ~ N(0,1), A = -(n+1), Dskip ~ N(0,1)."""
+    import numpy as np
+    tok = int(np.sum(lengths))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(key))
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.randn((tok, D), generator=g, device="cuda").to(td)
+    dt = (torch.randn((tok, D), generator=g, device="cuda") * 0.5 - 2.0).to(td)
+    Bm = torch.randn((tok, 16), generator=g, device="cuda").to(td)
+    Cm = torch.randn((tok, 16), generator=g, device="cuda").to(td)
+    A = -(torch.arange(16, device="cuda", dtype=torch.float32) + 1).repeat(D, 1).contiguous()
+    Dskip = torch.randn((D,), generator=g, device="cuda")
+    return {"x": x, "dt": dt, "Bm": Bm, "Cm": Cm, "A": A, "Dskip": Dskip}
+
+
+def oracle_sample_rate(torch, g, offsets, seqs, budget_s, reverse=True, readout=True):
+    """Oracle token·channels/s over the listed sequences (copied back from the GPU)."""
+    import numpy as np
+    import oracle
+    tc, secs = 0, 0.0
+    for b in seqs:
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        x = g["x"][r0:r1].float().cpu().numpy()
+        dt = g["dt"][r0:r1].float().cpu().numpy()
+        Bm = g["Bm"][r0:r1].float().cpu().numpy()
+        Cm = g["Cm"][r0:r1].float().cpu().numpy() if readout else None
+        t = {}
+        oracle.selective_scan(x, dt, Bm, Cm, g["A"].cpu().numpy(), g["Dskip"].cpu().numpy(),
+                              reverse=reverse, seq_offsets=np.array([0, r1 - r0]),
+                              want_y=readout, want_h_out=not readout, timing=t)
+        secs += t["seconds"]
+        tc += x.size
+        if secs >= budget_s:
+            break
+    return tc / secs, tc, secs
+
+
+class Prefill(Workload):
+    """Full reverse scan, 8 x 4096 x 4096, bf16, out = y."""
+    name = "prefill_r2l_bf16_b8_L4096_D4096_N16"
+    B, L, D = 8, 4096, 4096
+
+    def setup(self, torch, r2l):
+        import numpy as np
+        self.torch = torch
+        self.g = device_inputs(torch, 103, [self.L] * self.B, self.D, "bf16")
+        tok = self.B * self.L
+        self.offsets = np.arange(self.B + 1) * self.L
+        self.tc_per_launch = tok * self.D
+        self.tc_per_step = self.tc_per_launch
+        self.bytes_per_launch = scan_bytes(tok, self.D, 2, readout=True)
+        self.alu_per_launch = self.tc_per_launch * alu_ops_per_tc(True, False)
+        self.launches_per_step = 1
+        g = self.g
+        view = lambda t: t.view(self.B, self.L, -1)
+        self.R = _rotation(self.bytes_per_launch)
+        self.calls = []
+        for r in range(self.R):
+            src = g if r == 0 else {k: v.clone() for k, v in g.items()}
+            out = torch.empty_like(view(src["x"]))
+            self.calls.append(r2l.bind("r2l_scan", x=view(src["x"]), dt=view(src["dt"]),
+                                       Bm=view(src["Bm"]), Cm=view(src["Cm"]), A=g["A"],
+                                       Dskip=g["Dskip"], out=out))
+        self.config = {"workload": self.name, "batch": self.B, "seqlen": self.L, "D": self.D,
+                       "N": 16, "in_dtype": "bf16", "state_dtype": "fp32", "res": None,
+                       "rotating_sets": self.R, "parallelism": "single_gpu",
+                       "plan": {"state_split": self.calls[0].args.state_split,
+                                "workspace_bytes": int(self.calls[0].args.workspace_bytes)}}
+
+    def step(self, i, stream, events=None):
+        c = self.calls[i % self.R]
+        if events is None:
+            c.launch(stream)
+        else:
+            e0, e1 = events.next()
+            e0.record()
+            c.launch(stream)
+            e1.record()
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        rate, tc, secs = oracle_sample_rate(self.torch, self.g, self.offsets, range(self.B),
+                                            budget_s)
+        return {"value": rate, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
+                "kind": "oracle", "sample": "%d of the %d sequences (%d token-channels), %.1f s"
+                % (tc // (self.L * self.D), self.B, tc, secs)}
+
+
+class RaggedServing(Workload):
+    """256 ragged blocks of U{16..64} tokens at D = 4096, bf16: the reverse scan over
+    the active blocks and block_commit_state over the committed blocks."""
+    name = "ragged_serving_bf16_b256_blk16to64_D4096_N16"
+    D = 4096
+
+    def setup(self, torch, r2l):
+        import numpy as np
+        import synth
+        self.torch = torch
+        lens = synth.ragged_block_lengths()
+        self.offsets = synth.offsets(lens)
+        tok = int(self.offsets[-1])
+        self.g = device_inputs(torch, 104, lens, self.D, "bf16")
+        self.gc = device_inputs(torch, 1104, lens, self.D, "bf16")
+        cu = torch.from_numpy(self.offsets.astype(np.int32)).cuda()
+        B = len(lens)
+        self.tc_per_launch = tok * self.D
+        self.tc_per_step = 2 * tok * self.D
+        self.bytes_per_launch = scan_bytes(tok, self.D, 2, readout=True)
+        self.commit_bytes = scan_bytes(tok, self.D, 2, readout=False, batch=B, state_rw=True)
+        self.alu_per_launch = self.tc_per_launch * alu_ops_per_tc(True, False)
+        self.launches_per_step = 1
+        self.R = _rotation(self.bytes_per_launch + self.commit_bytes)
+        self.calls = []
+        for r in range(self.R):
+            g = self.g if r == 0 else {k: v.clone() for k, v in self.g.items()}
+            gc = self.gc if r == 0 else {k: v.clone() for k, v in self.gc.items()}
+            out = torch.empty_like(g["x"])
+            state = torch.randn((B, self.D, 16), device="cuda")
+            scan = r2l.bind("r2l_scan", x=g["x"], dt=g["dt"], Bm=g["Bm"], Cm=g["Cm"], A=g["A"],
+                            Dskip=g["Dskip"], out=out, cu_seqlens=cu, max_seqlen=int(lens.max()))
+            commit = r2l.bind("block_commit_state", state=state, x=gc["x"], dt=gc["dt"],
+                              Bm=gc["Bm"], A=gc["A"], cu_seqlens=cu, max_seqlen=int(lens.max()))
+            self.calls.append((scan, commit))
+        self.config = {"workload": self.name, "batch": B, "tokens": tok, "D": self.D, "N": 16,
+                       "block_len": "U{16..64}", "in_dtype": "bf16", "state_dtype": "fp32",
+                       "ops": ["r2l_scan (out = y)", "block_commit_state (in place)"],
+                       "rotating_sets": self.R, "parallelism": "single_gpu"}
+
+    def step(self, i, stream, events=None):
+        scan, commit = self.calls[i % self.R]
+        if events is None:
+            scan.launch(stream)
+        else:
+            e0, e1 = events.next()
+            e0.record()
+            scan.launch(stream)
+            e1.record()
+        commit.launch(stream)
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        rate, tc, secs = oracle_sample_rate(self.torch, self.g, self.offsets,
+                                            range(len(self.offsets) - 1), budget_s)
+        return {"value": rate, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
+                "kind": "oracle", "sample": "reverse scan of the first sequences (%d "
+                "token-channels), %.1f s" % (tc, secs)}
+
+
+class RaggedPrefix(Workload):
+    """prefix_scan_state over 256 ragged prefixes of U{256..8192} tokens at D = 4096."""
+    name = "ragged_prefix_state_bf16_b256_P256to8192_D4096_N16"
+    D = 4096
+
+    def setup(self, torch, r2l):
+        import numpy as np
+        import synth
+        self.torch = torch
+        lens = synth.ragged_prefix_lengths()
+        self.offsets = synth.offsets(lens)
+        tok = int(self.offsets[-1])
+        B = len(lens)
+        self.g = device_inputs(torch, 2104, lens, self.D, "bf16")
+        cu = torch.from_numpy(self.offsets.astype(np.int32)).cuda()
+        self.tc_per_launch = tok * self.D
+        self.tc_per_step = self.tc_per_launch
+        self.bytes_per_launch = scan_bytes(tok, self.D, 2, readout=False, batch=B, h_out=True)
+        self.alu_per_launch = self.tc_per_launch * alu_ops_per_tc(False, False)
+        self.launches_per_step = 1
+        self.R = 1  # 17.8 GB per launch: far beyond every cache
+        h = torch.empty((B, self.D, 16), device="cuda")
+        g = self.g
+        self.calls = [r2l.bind("prefix_scan_state", x=g["x"], dt=g["dt"], Bm=g["Bm"], A=g["A"],
+                               h_out=h, cu_seqlens=cu, max_seqlen=int(lens.max()))]
+        self.config = {"workload": self.name, "batch": B, "tokens": tok, "D": self.D, "N": 16,
+                       "prefix_len": "U{256..8192}", "in_dtype": "bf16", "state_dtype": "fp32",
+                       "parallelism": "single_gpu",
+                       "plan": {"chunk_tokens": int(self.calls[0].args.chunk_tokens),
+                                "workspace_bytes": int(self.calls[0].args.workspace_bytes)}}
+
+    step = Prefill.step
+
+    def cpu_baseline(self, budget_s):
+        import oracle
+        rate, tc, secs = oracle_sample_rate(self.torch, self.g, self.offsets,
+                                            range(len(self.offsets) - 1), budget_s,
+                                            reverse=False, readout=False)
+        return {"value": rate, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
+                "kind": "oracle", "sample": "prefix states of the first prefixes (%d "
+                "token-channels), %.1f s" % (tc, secs)}
+
+
+WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
+             "prefix": RaggedPrefix}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="denoise", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget of the CPU baseline (0: skip it)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the scan is independent per (sequence, channel), "
+              "so more GPUs only split the batch; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import reverse_mamba_selective_amd as r2l
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]()
+    wl.setup(torch, r2l)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # (1) eager: every step launched from the host loop
+    for i in range(args.warmup):
+        wl.step(i, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step(i, stream)
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / args.steps
+
+    # (2) the step captured once per rotating set in a hipGraph and replayed
+    graph_s = None
+    if not args.no_graph and wl.launches_per_step > 1:
+        graphs = []
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            for r in range(wl.R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    wl.step(r, s.cuda_stream)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % wl.R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % wl.R].replay()
+        torch.cuda.synchronize()
+        graph_s = (time.perf_counter() - t0) / args.steps
+
+    # (3) kernel duration: the same steps queued behind a spinning kernel, so
+    # that the host is far ahead of the GPU, with HIP events around every
+    # launch of the dominant kernel on the stream it runs on
+    ev = Events(torch, args.steps * wl.launches_per_step)
+    per_ms = sleep_cycles_per_ms(torch)
+    host_est_ms = args.steps * wl.launches_per_step * 0.05 + 20.0
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(per_ms * host_est_ms))
+    for i in range(args.steps):
+        wl.step(i, stream, ev)
+    kern_ms, n_launch = ev.mean_ms()
+
+    step_s = min(eager_s, graph_s) if graph_s else eager_s
+    value = wl.tc_per_step / step_s
+    kern_s = kern_ms * 1e-3
+    hbm_gbs = wl.bytes_per_launch / kern_s / 1e9
+    alu_t = wl.alu_per_launch / kern_s / 1e12
+    rl_hbm = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload)}
+    rl_alu = {"bound": "alu", "achieved": round(alu_t, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
+              "unit": "Tlane-op/s", "frac": round(alu_t / VALU_PEAK_TLANEOPS, 4),
+              "traffic": rl_hbm["traffic"]}
+    binding = rl_alu if rl_alu["frac"] >= rl_hbm["frac"] else rl_hbm
+    other = rl_hbm if binding is rl_alu else rl_alu
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = wl.cpu_baseline(args.cpu_seconds)
+
+    line = {
+        "metric": "R2L selective-scan tokens*channels/s and HBM GB/s (% of peak), 1xMI355X",
+        "value": value,
+        "unit": "tokens*channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.config.get("in_dtype", "bf16") + " in, f32 compute",
+        "data": "synthetic (seeded)",
+        "config": wl.config,
+        "roofline": binding,
+        "roofline_other": other,
+        "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_frac_of_8TBs": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "kernel": {"name": "segment_scan_kernel", "avg_launch_us": round(kern_s * 1e6, 3),
+                   "launches_timed": n_launch, "bytes_per_launch": wl.bytes_per_launch,
+                   "tc_per_launch": wl.tc_per_launch,
+                   "alu_lane_ops_per_tc": alu_ops_per_tc(True, True),
+                   "trans_slots": TRANS_SLOTS, "source_sha": kernel_sha()},
+        "ms_per_step_eager": eager_s * 1e3,
+        "ms_per_step_graph": graph_s * 1e3 if graph_s else None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

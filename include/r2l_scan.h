@@ -1,0 +1,217 @@
+/*
+ * r2l_scan.h -- C ABI of the MI355X (gfx950) selective-scan library libr2l_scan.so.
+ *
+ * The library runs the hot path of the Bifocal dLLM / R2LM method and of its
+ * block-diffusion companion:
+ *
+ *  - r2l_scan: the right-to-left (R2L) stream. "Bifocal Diffusion Language
+ *    Models" (gist.science nl and fr technical summaries, section 2
+ *    "Methodology") describes a sidecar that reverses the backbone's hidden
+ *    states, runs a Mamba selective scan over them and reverses the result
+ *    back, producing a residual correction Delta^R2L that a learnable scalar s
+ *    (initialised at zero, so that the model starts out identical to the
+ *    causal backbone) adds to the hidden states. During denoising the scan
+ *    covers the generation block only. The reversal is folded into the index
+ *    math here: nothing is flipped in memory.
+ *  - prefix_scan_state: the forward-only Mamba boundary state after each
+ *    prefix ("Training Hybrid Block Diffusion Language Models with Partial
+ *    Bidirectionality", nl summary, "Methodology" item 1: completed prefix
+ *    blocks are cached as forward-only boundary states that depend on the
+ *    clean prefix alone).
+ *  - block_commit_state: the same cache advanced over a committed block (same
+ *    passage and item 3: the cache is built by scanning the clean prefix, and
+ *    finished blocks become prefix).
+ *
+ * The recurrence (the pages name "selective scan (Mamba)" without writing it
+ * out; this is the Mamba-1 reading, with zero-order hold for A and an Euler
+ * step for B). For each sequence, channel d < D and state n < N, visiting the
+ * tokens right to left (r2l_scan) or left to right (the other two):
+ *
+ *     Delta_t = delta_softplus ? log(1 + exp(dt[t,d])) : dt[t,d]
+ *     h_n     = exp(Delta_t * A[d,n]) * h_n + Delta_t * Bm[t,n] * x[t,d]
+ *     y_t     = sum_n Cm[t,n] * h_n + Dskip[d] * x[t,d]
+ *     out[t,d] = res == NULL ? y_t : (s == 0 ? res[t,d] : res[t,d] + s * y_t)
+ *
+ * h starts from h_in (or zero) before the first visited token; h_out receives
+ * the state after the last visited token. All arithmetic is fp32 (state, Delta,
+ * exponentials, sums) whatever the storage type of the inputs.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ *  Layout   Token-major, the last dimension contiguous. x, dt, res and out are
+ *           [tokens, D] with a token stride in elements (>= D); Bm and Cm are
+ *           [tokens, N] with a token stride (>= N), shared by all channels.
+ *           In the dense layout each of them also has a batch stride, so a
+ *           slice [:, a:b] of a [batch, L, .] tensor is taken as it is;
+ *           A is [D, N] fp32 contiguous; Dskip is [D] fp32; h_in / h_out are
+ *           [batch, D, N] fp32 contiguous.
+ *  Batches  Dense: batch sequences of seqlen tokens each, sequence b owning
+ *           rows b*seqlen .. (b+1)*seqlen-1. Ragged: cu_seqlens (device memory,
+ *           int32 [batch+1], cu_seqlens[0] = 0, non-decreasing) gives each
+ *           sequence's rows; total_tokens (host) must equal cu_seqlens[batch]
+ *           and max_seqlen (host) must bound every length. Length-0 sequences
+ *           are legal: they write no rows and h_out = h_in (or zero). The
+ *           ragged fields are taken on trust (they live on the device); the
+ *           library only checks them when the environment variable
+ *           R2L_CHECK_SEQLENS=1 is set, at the price of a synchronous copy.
+ *  Memory   Every pointer except `a` itself is device memory. The caller owns
+ *           every buffer; the library allocates nothing, keeps no state
+ *           between calls and is safe to call from several host threads.
+ *  Streams  `stream` is a hipStream_t (NULL: the null stream). Work is queued
+ *           on it and the call returns without waiting.
+ *  Aliasing out may be exactly x and/or exactly res (same base pointer and
+ *           strides): the in-place hook update. h_out may be exactly h_in. Any
+ *           other overlap between an output and any other buffer returns
+ *           R2L_ERR_ALIAS. Overlap is judged on the address span each tensor's
+ *           strides reach, so interleaved layouts count as overlapping.
+ *  Alignment Element alignment for x, dt, Bm, Cm, res, out; 16 bytes for A,
+ *           h_in and h_out; 4 bytes for Dskip.
+ *  Errors   Every argument is checked on the host before anything is queued;
+ *           on error nothing is launched and nothing is written.
+ *           r2l_last_error() then describes the first failed check. Faults
+ *           inside kernels surface at the caller's next synchronisation.
+ *  NaN/Inf  Propagate; nothing is trapped. With s == 0 the output is the
+ *           residual bit for bit, whatever y holds.
+ */
+#ifndef R2L_SCAN_H_
+#define R2L_SCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define R2L_ABI_VERSION 1
+
+/* exported from libr2l_scan.so (everything else in it is hidden) */
+#if defined(__GNUC__)
+#define R2L_API __attribute__((visibility("default")))
+#else
+#define R2L_API
+#endif
+
+typedef int32_t r2l_status;
+#define R2L_OK 0
+#define R2L_ERR_INVALID_ARG (-1) /* a required pointer is NULL, a size or stride is out of range */
+#define R2L_ERR_UNSUPPORTED (-2) /* dtype or state size N not built (N must be 16) */
+#define R2L_ERR_ALIAS (-3)       /* an output overlaps another buffer other than as allowed */
+#define R2L_ERR_MISALIGNED (-4)  /* a pointer breaks the alignment rules above */
+#define R2L_ERR_WORKSPACE (-5)   /* workspace missing or smaller than r2l_workspace_size */
+#define R2L_ERR_HIP (-6)         /* the HIP runtime refused a launch or a query */
+
+/* element type of x, dt, Bm, Cm, res and out */
+#define R2L_DTYPE_F32 0
+#define R2L_DTYPE_BF16 1
+
+/* operation codes for r2l_workspace_size */
+#define R2L_OP_SCAN 0
+#define R2L_OP_PREFIX 1
+#define R2L_OP_COMMIT 2
+
+typedef struct r2l_scan_args {
+    /* ---- shape ---- */
+    int64_t batch;              /* sequences, >= 0 */
+    int64_t seqlen;             /* dense: tokens per sequence, >= 0 (ignored when ragged) */
+    const int32_t *cu_seqlens;  /* ragged: device int32 [batch+1]; NULL selects dense */
+    int64_t total_tokens;       /* ragged: cu_seqlens[batch], known on the host */
+    int64_t max_seqlen;         /* ragged: an upper bound of every sequence length */
+    int64_t dim;                /* D, channels, >= 1 */
+    int32_t dstate;             /* N, state size; 16 is built */
+    int32_t dtype;              /* R2L_DTYPE_* of x, dt, Bm, Cm, res, out */
+
+    /* ---- inputs ----
+     * Each token-major tensor has a token stride and, for the dense layout, a
+     * batch stride (elements between sequence b and b+1; 0 = seqlen * token
+     * stride, i.e. packed). Ragged layouts ignore the batch strides. */
+    const void *x;   int64_t x_stride;  int64_t x_batch_stride;  /* [tokens, D] scan input (hidden states) */
+    const void *dt;  int64_t dt_stride; int64_t dt_batch_stride; /* [tokens, D] step input before softplus */
+    const void *Bm;  int64_t Bm_stride; int64_t Bm_batch_stride; /* [tokens, N] input matrix rows */
+    const void *Cm;  int64_t Cm_stride; int64_t Cm_batch_stride; /* [tokens, N] readout rows (unused by state-only calls) */
+    const float *A;                      /* [D, N] state matrix (diagonal per channel), fp32 */
+    const float *Dskip;                  /* [D] skip weights, fp32, or NULL for zero */
+    int32_t delta_softplus;              /* 1: Delta = softplus(dt); 0: Delta = dt */
+
+    /* ---- planning hints (0 = let the library choose) ----
+     * chunk_tokens  > 0: split every sequence into chunks of this many tokens
+     *               and join them with the carry pass (needs workspace);
+     *               < 0: never split; 0: split when the shape needs it.
+     * state_split   1, 2 or 4 lanes share one channel's N states; 0: choose.
+     * Results differ between plans by rounding only. */
+    int32_t chunk_tokens;
+    int32_t state_split;
+
+    /* ---- state ---- */
+    const float *h_in;                   /* [batch, D, N] initial state, or NULL for zero */
+    float *h_out;                        /* [batch, D, N] final state, or NULL */
+
+    /* ---- output ---- */
+    const void *res; int64_t res_stride; int64_t res_batch_stride; /* [tokens, D] residual base, or NULL */
+    float s;                                                       /* residual gate */
+    void *out; int64_t out_stride; int64_t out_batch_stride;       /* [tokens, D] */
+
+    /* ---- scratch for chunked plans ---- */
+    void *workspace;                     /* device, 256-byte aligned, or NULL */
+    size_t workspace_bytes;
+} r2l_scan_args;
+
+/*
+ * r2l_scan -- the R2L stream over each sequence (the generation block during
+ * denoising, the whole prompt at prefill). Tokens are visited right to left
+ * starting from h_in (NULL: zero state at the right edge), y is read out at
+ * every token and out receives y or the gated residual at the token's own
+ * position. Required: x, dt, Bm, Cm, A, out. Optional: Dskip, h_in, h_out,
+ * res. h_out receives the state after the leftmost token.
+ * Source: "Bifocal Diffusion Language Models", section 2 (reverse, scan,
+ * reverse back, residual through s; scan over generation tokens only), and
+ * "Training Hybrid Block Diffusion ...", "Methodology" item 1 (reverse scan
+ * limited to the active block).
+ */
+R2L_API r2l_status r2l_scan(const r2l_scan_args *a, void *stream);
+
+/*
+ * prefix_scan_state -- the forward-only boundary state of each prefix: tokens
+ * visited left to right from h_in (NULL: zero), h_out = the state after the
+ * last token. If out is given, y (or the gated residual) is also written,
+ * which is the forward continuation of a block resumed from a cached state;
+ * Cm is then required. At least one of h_out and out is required.
+ * Source: "Training Hybrid Block Diffusion ...", "Methodology" items 1-2
+ * (forward-only boundary states; a timestep-free prefix operator followed by
+ * the active-block continuation).
+ */
+R2L_API r2l_status prefix_scan_state(const r2l_scan_args *a, void *stream);
+
+/*
+ * block_commit_state -- advance cached boundary states over committed blocks,
+ * in place: h_out holds the state before the call and receives the state
+ * after each sequence's block. h_in must be NULL or equal to h_out. out is an
+ * optional forward readout over the block (then Cm is required).
+ * Source: "Training Hybrid Block Diffusion ...", "Methodology" items 1 and 3
+ * (the cache is built by scanning the clean prefix; completed blocks join it).
+ */
+R2L_API r2l_status block_commit_state(const r2l_scan_args *a, void *stream);
+
+/*
+ * r2l_workspace_size -- bytes of workspace that the plan for operation `op`
+ * (R2L_OP_*) with these arguments needs; 0 when the plan does not chunk.
+ * Only the shape fields and the planning hints are read. Returns R2L_OK and
+ * writes *bytes, or an error status.
+ */
+R2L_API r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes);
+
+/* Short static description of a status code. */
+R2L_API const char *r2l_status_string(r2l_status status);
+
+/* Description of the last error returned on the calling host thread ("" if none). */
+R2L_API const char *r2l_last_error(void);
+
+/* R2L_ABI_VERSION of the library. */
+R2L_API int32_t r2l_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* R2L_SCAN_H_ */

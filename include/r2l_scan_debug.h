@@ -1,0 +1,40 @@
+/*
+ * r2l_scan_debug.h -- a host-only test aid of libr2l_scan.so (declared apart
+ * from the main ABI in r2l_scan.h because no production caller needs it).
+ */
+#ifndef R2L_SCAN_DEBUG_H_
+#define R2L_SCAN_DEBUG_H_
+
+#include "r2l_scan.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct r2l_access_report {
+    int64_t launches;   /* kernel launches replayed */
+    int64_t accesses;   /* memory accesses checked */
+    char message[512];  /* the first out-of-bounds access, or "" */
+} r2l_access_report;
+
+/*
+ * r2l_check_access -- replays on the host every memory access that the call
+ * `op` (R2L_OP_*) with these arguments would make on the GPU: the same
+ * argument checks, the same plan and launches, the kernels' own index math.
+ * Nothing is launched and no pointer is dereferenced: device pointers are
+ * compared as numbers against the buffers the arguments describe (a buffer of
+ * zero bytes admits no access). For the ragged layout `cu_seqlens_host` is a
+ * host copy of the [batch+1] offsets (ignored for the dense layout).
+ * Returns the entry point's status when an argument check fails, R2L_OK when
+ * every access is in bounds, and R2L_ERR_INVALID_ARG with report->message
+ * naming the first access that is not. Callers: the test suite, before a
+ * kernel change reaches a GPU.
+ */
+R2L_API r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *cu_seqlens_host,
+                            r2l_access_report *report);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* R2L_SCAN_DEBUG_H_ */

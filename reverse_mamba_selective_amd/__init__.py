@@ -1,0 +1,260 @@
+"""MI355X-native R2L / forward selective scans (the hot path of the Bifocal dLLM /
+R2LM method and of block-diffusion Mamba prefix caching).
+
+Thin PyTorch-facing binding over the C ABI in ``include/r2l_scan.h``: it only
+checks tensor layouts, fills the argument struct and passes torch's current
+HIP stream. Every step of the computation runs in the library's gfx950
+kernels; torch provides device memory and streams. The first call fails
+(ImportError) when ``libr2l_scan.so`` is not built: there is no fallback.
+
+Tensor layouts
+    x, dt, res, out   [batch, L, D] (dense) or [tokens, D] (ragged, with cu_seqlens)
+    Bm, Cm            [batch, L, N] or [tokens, N]
+    A                 [D, N] fp32;  Dskip [D] fp32
+    h_in, h_out       [batch, D, N] fp32
+The last dimension must be contiguous and the token rows evenly strided.
+x, dt, Bm, Cm, res and out share one dtype: float32 or bfloat16.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _abi
+from ._abi import R2LError  # noqa: F401
+
+__all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "workspace_size", "bind",
+           "BoundCall", "R2LError", "library_path"]
+
+_DTYPES = {torch.float32: _abi.R2L_DTYPE_F32, torch.bfloat16: _abi.R2L_DTYPE_BF16}
+
+
+def library_path() -> str:
+    return _abi.LIB_PATH
+
+
+def _rows(t, cols, name):
+    """(pointer, token stride, batch stride, rows) of a [batch, L, cols] or
+    [tokens, cols] view; strides in elements."""
+    if t is None:
+        return None, 0, 0, 0
+    if t.dim() not in (2, 3) or t.shape[-1] != cols:
+        raise ValueError("%s must be [batch, L, %d] or [tokens, %d], got %s"
+                         % (name, cols, cols, tuple(t.shape)))
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("%s: last dimension must be contiguous" % name)
+    if any(st < 0 for st in t.stride()):
+        raise ValueError("%s: negative strides are not supported" % name)
+    rs = max(int(t.stride(-2)), cols)
+    if t.dim() == 3:
+        return t.data_ptr(), rs, int(t.stride(0)), int(t.shape[0] * t.shape[1])
+    return t.data_ptr(), rs, 0, int(t.shape[0])
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_f32(t, shape, name):
+    if t is None:
+        return
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be a contiguous float32 tensor of shape %s, got %s %s"
+                         % (name, tuple(shape), t.dtype, tuple(t.shape)))
+
+
+def _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
+          delta_softplus, chunk_tokens, state_split):
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be float32 or bfloat16, got %s" % x.dtype)
+    for t, n in ((dt, "dt"), (Bm, "Bm"), (Cm, "Cm"), (res, "res"), (out, "out")):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("%s has dtype %s but x has %s" % (n, t.dtype, x.dtype))
+    D = int(x.shape[-1])
+    if A.dim() != 2 or A.shape[0] != D:
+        raise ValueError("A must be [D, N] with D = %d" % D)
+    N = int(A.shape[1])
+    a = _abi.ScanArgs()
+    if cu_seqlens is not None:
+        if x.dim() != 2:
+            raise ValueError("ragged layout takes [tokens, D] tensors")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        batch = int(cu_seqlens.shape[0]) - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if batch > 0 else 0
+        a.cu_seqlens = cu_seqlens.data_ptr()
+        a.total_tokens = int(x.shape[0])
+        a.max_seqlen = int(max_seqlen)
+        a.batch = batch
+    elif x.dim() == 3:
+        a.batch, a.seqlen = int(x.shape[0]), int(x.shape[1])
+    else:
+        a.batch, a.seqlen = 1, int(x.shape[0])
+    a.dim, a.dstate, a.dtype = D, N, _DTYPES[x.dtype]
+    a.x, a.x_stride, a.x_batch_stride, rows = _rows(x, D, "x")
+    for t, n, cols in ((dt, "dt", D), (Bm, "Bm", N), (Cm, "Cm", N), (res, "res", D),
+                       (out, "out", D)):
+        if t is None:
+            continue
+        if t.dim() != x.dim() or (t.dim() == 3 and t.shape[:2] != x.shape[:2]):
+            raise ValueError("%s has shape %s, x has %s" % (n, tuple(t.shape), tuple(x.shape)))
+        p, st, bst, r = _rows(t, cols, n)
+        if r != rows:
+            raise ValueError("%s has %d token rows, x has %d" % (n, r, rows))
+        setattr(a, n, p)
+        setattr(a, n + "_stride", st)
+        setattr(a, n + "_batch_stride", bst)
+    _check_f32(A, (D, N), "A")
+    _check_f32(Dskip, (D,), "Dskip")
+    _check_f32(h_in, (a.batch, D, N), "h_in")
+    _check_f32(h_out, (a.batch, D, N), "h_out")
+    a.A, a.Dskip = A.data_ptr(), _ptr(Dskip)
+    a.h_in, a.h_out = _ptr(h_in), _ptr(h_out)
+    a.s = float(s)
+    a.delta_softplus = 1 if delta_softplus else 0
+    a.chunk_tokens, a.state_split = int(chunk_tokens), int(state_split)
+    return a
+
+
+def _attach_workspace(op, a, workspace, device):
+    need = _abi.workspace_size(op, a)
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        elif workspace.numel() * workspace.element_size() < need:
+            raise ValueError("workspace has %d bytes, the plan needs %d"
+                             % (workspace.numel() * workspace.element_size(), need))
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    return workspace
+
+
+def _run(func, op, a, workspace, device):
+    workspace = _attach_workspace(op, a, workspace, device)
+    with torch.cuda.device(device):
+        stream = torch.cuda.current_stream(device).cuda_stream
+    _abi.call(func, a, stream)
+
+
+class BoundCall:
+    """One entry-point call with its argument struct filled once.
+
+    ``launch()`` queues it again on torch's current stream of the tensors'
+    device (or on ``stream``, a raw hipStream_t). The tensors given to ``bind``
+    (and the workspace) are kept alive by this object; their contents may
+    change between launches, their storage may not.
+    """
+
+    def __init__(self, func, op, args, keep, workspace, device):
+        self.func, self.op, self.args = func, op, args
+        self._keep, self.workspace, self.device = keep, workspace, device
+        self._fn = getattr(_abi.load(), func)
+        self._ref = _abi.ctypes.byref(args)
+
+    def launch(self, stream=None):
+        """Queue the call on ``stream`` (a raw hipStream_t handle) or, when None,
+        on torch's current stream of the device."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        st = self._fn(self._ref, _abi._vp(stream))
+        if st != _abi.R2L_OK:
+            raise R2LError(st, self.func, _abi.last_error())
+
+
+def bind(op: str, **kw) -> BoundCall:
+    """Check and marshal the arguments of ``r2l_scan``, ``prefix_scan_state`` or
+    ``block_commit_state`` once (same keywords as those functions; outputs must
+    be given) and return a :class:`BoundCall`.
+    """
+    kw = dict(kw)
+    ws = kw.pop("workspace", None)
+    if op == "r2l_scan":
+        func, code = "r2l_scan", _abi.R2L_OP_SCAN
+    elif op == "prefix_scan_state":
+        func, code = "prefix_scan_state", _abi.R2L_OP_PREFIX
+    elif op == "block_commit_state":
+        func, code = "block_commit_state", _abi.R2L_OP_COMMIT
+        kw["h_out"] = kw.pop("state")
+    else:
+        raise ValueError("unknown entry point %r" % op)
+    x = kw["x"]
+    if op == "r2l_scan" and kw.get("out") is None:
+        raise ValueError("bind() needs the output tensor")
+    names = ("x", "dt", "Bm", "Cm", "A", "Dskip", "cu_seqlens", "max_seqlen", "h_in", "h_out",
+             "res", "s", "out", "delta_softplus", "chunk_tokens", "state_split")
+    defaults = {"Cm": None, "Dskip": None, "cu_seqlens": None, "max_seqlen": None,
+                "h_in": None, "h_out": None, "res": None, "s": 0.0, "out": None,
+                "delta_softplus": True, "chunk_tokens": 0, "state_split": 0}
+    unknown = set(kw) - set(names)
+    if unknown:
+        raise ValueError("unknown arguments %s" % sorted(unknown))
+    vals = [kw.get(n, defaults.get(n)) for n in names]
+    a = _fill(*vals)
+    ws = _attach_workspace(code, a, ws, x.device)
+    keep = [v for v in vals if isinstance(v, torch.Tensor)]
+    return BoundCall(func, code, a, keep, ws, x.device)
+
+
+def workspace_size(op: str, x, A, *, cu_seqlens=None, max_seqlen=None, out=True,
+                   chunk_tokens=0, state_split=0) -> int:
+    """Workspace bytes for op in {"r2l_scan", "prefix_scan_state", "block_commit_state"}."""
+    codes = {"r2l_scan": _abi.R2L_OP_SCAN, "prefix_scan_state": _abi.R2L_OP_PREFIX,
+             "block_commit_state": _abi.R2L_OP_COMMIT}
+    a = _fill(x, None, None, None, A, None, cu_seqlens, max_seqlen, None, None, None, 0.0,
+              None, True, chunk_tokens, state_split)
+    if out:
+        a.out = 1  # only "is a readout requested" is read
+    return _abi.workspace_size(codes[op], a)
+
+
+def r2l_scan(x, dt, Bm, Cm, A, Dskip=None, *, cu_seqlens=None, max_seqlen=None, h_in=None,
+             h_out=None, res=None, s=0.0, out=None, delta_softplus=True, chunk_tokens=0,
+             state_split=0, workspace=None):
+    """The R2L stream: reverse selective scan with readout and gated residual.
+
+    out[t] = y_t (res None) or res[t] + s*y_t (s == 0: res[t] bit for bit). ``out``
+    may be ``x`` or ``res`` itself (in-place hook update). ``h_out`` receives the
+    state after the leftmost token. Returns ``out``.
+    """
+    if out is None:
+        out = torch.empty_like(x)
+    a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
+              delta_softplus, chunk_tokens, state_split)
+    _run("r2l_scan", _abi.R2L_OP_SCAN, a, workspace, x.device)
+    return out
+
+
+def prefix_scan_state(x, dt, Bm, A, *, cu_seqlens=None, max_seqlen=None, h_in=None,
+                      h_out=None, Cm=None, Dskip=None, res=None, s=0.0, out=None,
+                      delta_softplus=True, chunk_tokens=0, state_split=0, workspace=None):
+    """Forward-only boundary state of each prefix (left to right from h_in).
+
+    Returns h_out [batch, D, N] (allocated when not given). With ``Cm`` (and an
+    optional ``out``) the forward readout is written too and (h_out, out) is
+    returned.
+    """
+    batch = int(cu_seqlens.shape[0]) - 1 if cu_seqlens is not None else \
+        (int(x.shape[0]) if x.dim() == 3 else 1)
+    if h_out is None:
+        h_out = torch.empty((batch, x.shape[-1], A.shape[1]), dtype=torch.float32,
+                            device=x.device)
+    if Cm is not None and out is None:
+        out = torch.empty_like(x)
+    a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
+              delta_softplus, chunk_tokens, state_split)
+    _run("prefix_scan_state", _abi.R2L_OP_PREFIX, a, workspace, x.device)
+    return (h_out, out) if Cm is not None else h_out
+
+
+def block_commit_state(state, x, dt, Bm, A, *, cu_seqlens=None, max_seqlen=None, Cm=None,
+                       Dskip=None, res=None, s=0.0, out=None, delta_softplus=True,
+                       chunk_tokens=0, state_split=0, workspace=None):
+    """Advance cached boundary states [batch, D, N] over committed blocks, in place.
+
+    Returns ``state`` (and ``out`` when ``Cm`` asks for the block's forward readout).
+    """
+    if Cm is not None and out is None:
+        out = torch.empty_like(x)
+    a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, None, state, res, s, out,
+              delta_softplus, chunk_tokens, state_split)
+    _run("block_commit_state", _abi.R2L_OP_COMMIT, a, workspace, x.device)
+    return (state, out) if Cm is not None else state

@@ -1,0 +1,140 @@
+"""ctypes view of include/r2l_scan.h (argument marshalling only).
+
+Loading fails loudly when libr2l_scan.so has not been built: there is no other
+implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libr2l_scan.so")
+
+R2L_OK = 0
+R2L_ERR_INVALID_ARG = -1
+R2L_ERR_UNSUPPORTED = -2
+R2L_ERR_ALIAS = -3
+R2L_ERR_MISALIGNED = -4
+R2L_ERR_WORKSPACE = -5
+R2L_ERR_HIP = -6
+
+R2L_DTYPE_F32 = 0
+R2L_DTYPE_BF16 = 1
+
+R2L_OP_SCAN = 0
+R2L_OP_PREFIX = 1
+R2L_OP_COMMIT = 2
+
+ABI_VERSION = 1
+
+EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
+           "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access")
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class ScanArgs(ctypes.Structure):
+    """Mirror of ``r2l_scan_args`` (same field order, natural alignment)."""
+    _fields_ = [
+        ("batch", _i64), ("seqlen", _i64), ("cu_seqlens", _vp), ("total_tokens", _i64),
+        ("max_seqlen", _i64), ("dim", _i64), ("dstate", _i32), ("dtype", _i32),
+        ("x", _vp), ("x_stride", _i64), ("x_batch_stride", _i64),
+        ("dt", _vp), ("dt_stride", _i64), ("dt_batch_stride", _i64),
+        ("Bm", _vp), ("Bm_stride", _i64), ("Bm_batch_stride", _i64),
+        ("Cm", _vp), ("Cm_stride", _i64), ("Cm_batch_stride", _i64),
+        ("A", _vp), ("Dskip", _vp), ("delta_softplus", _i32),
+        ("chunk_tokens", _i32), ("state_split", _i32),
+        ("h_in", _vp), ("h_out", _vp),
+        ("res", _vp), ("res_stride", _i64), ("res_batch_stride", _i64), ("s", ctypes.c_float),
+        ("out", _vp), ("out_stride", _i64), ("out_batch_stride", _i64),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class AccessReport(ctypes.Structure):
+    """Mirror of ``r2l_access_report`` (include/r2l_scan_debug.h)."""
+    _fields_ = [("launches", _i64), ("accesses", _i64), ("message", ctypes.c_char * 512)]
+
+
+class R2LError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d): %s" % (func, status_string(status), status, detail))
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library once; raises if it is missing or from another ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            "libr2l_scan.so is not built at %s; run `python -m reverse_mamba_selective_amd.build` "
+            "(hipcc for gfx950). There is no fallback implementation." % path)
+    lib = ctypes.CDLL(path)
+    ptr = ctypes.POINTER(ScanArgs)
+    for name in ("r2l_scan", "prefix_scan_state", "block_commit_state"):
+        f = getattr(lib, name)
+        f.restype = _i32
+        f.argtypes = [ptr, _vp]
+    lib.r2l_workspace_size.restype = _i32
+    lib.r2l_workspace_size.argtypes = [_i32, ptr, ctypes.POINTER(ctypes.c_size_t)]
+    lib.r2l_status_string.restype = ctypes.c_char_p
+    lib.r2l_status_string.argtypes = [_i32]
+    lib.r2l_last_error.restype = ctypes.c_char_p
+    lib.r2l_last_error.argtypes = []
+    lib.r2l_abi_version.restype = _i32
+    lib.r2l_abi_version.argtypes = []
+    lib.r2l_check_access.restype = _i32
+    lib.r2l_check_access.argtypes = [_i32, ptr, ctypes.POINTER(_i32), ctypes.POINTER(AccessReport)]
+    if lib.r2l_abi_version() != ABI_VERSION:
+        raise ImportError("libr2l_scan.so ABI %d, binding expects %d"
+                          % (lib.r2l_abi_version(), ABI_VERSION))
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().r2l_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().r2l_last_error().decode()
+
+
+def call(func: str, args: ScanArgs, stream: int | None) -> None:
+    lib = load()
+    st = getattr(lib, func)(ctypes.byref(args), _vp(stream or 0))
+    if st != R2L_OK:
+        raise R2LError(st, func, last_error())
+
+
+def workspace_size(op: int, args: ScanArgs) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    st = lib.r2l_workspace_size(op, ctypes.byref(args), ctypes.byref(n))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_workspace_size", last_error())
+    return int(n.value)
+
+
+def check_access(op: int, args: ScanArgs, cu_seqlens_host=None):
+    """Host replay of every access the call would make (no device touched).
+
+    Returns (status, report); status 0 means every access is in bounds.
+    ``cu_seqlens_host``: sequence of batch+1 ints for the ragged layout.
+    """
+    lib = load()
+    rep = AccessReport()
+    cu = None
+    if cu_seqlens_host is not None:
+        arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
+        cu = ctypes.cast(arr, ctypes.POINTER(_i32))
+    st = lib.r2l_check_access(op, ctypes.byref(args), cu, ctypes.byref(rep))
+    return st, rep

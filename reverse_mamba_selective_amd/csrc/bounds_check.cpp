@@ -1,0 +1,233 @@
+// bounds_check.cpp -- host-side replay of every memory access that the
+// launches of one entry-point call would make, using the kernels' own index
+// math (scan_geometry.h) and the same launch list (scan_plan.h). Nothing here
+// touches a device: pointers are only compared as numbers.
+//
+// An access is in bounds when it lies inside the buffer its base pointer
+// points into (a zero-size buffer admits no access). Per-token rows must also
+// be rows of the segment's own sequence, and buffer-resource offsets must fit
+// the resource (the hardware checks only the lane offset).
+#include "bounds_check.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <vector>
+
+#include "scan_geometry.h"
+
+namespace r2l {
+namespace {
+
+struct Region {
+    const char *name;
+    uintptr_t lo, hi;
+};
+
+class Checker {
+  public:
+    Checker(std::vector<Region> regions, r2l_access_report *rep) : regions_(std::move(regions)), rep_(rep) {}
+
+    // The region that holds pointer p (nullptr if none).
+    const Region *region_of(const void *p) const {
+        const uintptr_t v = reinterpret_cast<uintptr_t>(p);
+        const Region *best = nullptr;
+        for (const Region &r : regions_)
+            if (r.lo <= v && v < r.hi && (!best || r.hi - r.lo < best->hi - best->lo)) best = &r;
+        return best;
+    }
+
+    bool ok() const { return !failed_; }
+
+    // [addr, addr + bytes) inside the region of `base`.
+    void access(const char *what, const Region *reg, uintptr_t addr, uint64_t bytes) {
+        ++rep_->accesses;
+        if (failed_) return;
+        if (!reg) return fail("%s: base pointer is in no argument buffer (addr 0x%llx)", what,
+                              (unsigned long long)addr);
+        if (addr < reg->lo || addr + bytes > reg->hi)
+            fail("%s: byte 0x%llx..+%llu outside %s [0x%llx, 0x%llx)", what,
+                 (unsigned long long)addr, (unsigned long long)bytes, reg->name,
+                 (unsigned long long)reg->lo, (unsigned long long)reg->hi);
+    }
+
+    void fail(const char *fmt, ...) __attribute__((format(printf, 2, 3))) {
+        if (failed_) return;
+        failed_ = true;
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(rep_->message, sizeof(rep_->message), fmt, ap);
+        va_end(ap);
+    }
+
+  private:
+    std::vector<Region> regions_;
+    r2l_access_report *rep_;
+    bool failed_ = false;
+};
+
+uintptr_t U(const void *p) { return reinterpret_cast<uintptr_t>(p); }
+
+void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
+    const SegParams &p = l.seg;
+    const bool readout = l.mode != kModeState;
+    const int G = l.G, NS = kN / G, NBC = readout ? 2 * kN : kN, STAGE = kTile * NBC / kWG;
+    const int64_t es = l.dtype == R2L_DTYPE_BF16 ? 2 : 4;
+    const Region *rA = ck.region_of(p.A), *rDs = p.Dskip ? ck.region_of(p.Dskip) : nullptr;
+    const Region *rHin = p.hin ? ck.region_of(p.hin) : nullptr;
+    const Region *rHfin = p.hfin ? ck.region_of(p.hfin) : nullptr;
+    const Region *rSd = p.sdelta ? ck.region_of(p.sdelta) : nullptr;
+    const Region *rX = ck.region_of(p.x), *rD = ck.region_of(p.dt), *rB = ck.region_of(p.Bm);
+    const Region *rC = readout ? ck.region_of(p.Cm) : nullptr;
+    const Region *rR = l.mode == kModeRes ? ck.region_of(p.res) : nullptr;
+    const Region *rO = readout ? ck.region_of(p.out) : nullptr;
+
+    for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
+        const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, bid);
+        if (!bg.valid) continue;
+        const int64_t s0 = p.cu_seqlens ? cu_host[bg.b] : 0;
+        const int64_t s1 = p.cu_seqlens ? cu_host[bg.b + 1] : 0;
+        const SeqGeom sq = seq_geom(p, bg.b, s0, s1);
+        const SegGeom sg = seg_geom(l.reverse, bg.c, p.chunk_len, sq.len);
+        if (!sg.run) continue;
+        if (p.cu_seqlens) ck.access("cu_seqlens", ck.region_of(p.cu_seqlens),
+                                    U(p.cu_seqlens) + bg.b * 4, 8);
+
+        // per-lane loads and stores outside the token loop
+        uint32_t dmin = UINT32_MAX, dmax = 0;
+        for (int lane = 0; lane < kWG; ++lane) {
+            const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
+            dmin = lg.d < dmin ? lg.d : dmin;
+            dmax = lg.d > dmax ? lg.d : dmax;
+            const int64_t st = static_cast<int64_t>(lg.d) * kN + lg.sub * NS;
+            ck.access("A", rA, U(p.A) + st * 4, NS * 4);
+            if (p.hin) ck.access("h_in", rHin, U(p.hin) + (bg.b * p.hin_b + bg.c * p.hin_c + st) * 4, NS * 4);
+            if (readout && p.Dskip) ck.access("Dskip", rDs, U(p.Dskip) + lg.d * 4, 4);
+            if (p.hfin && lg.active)
+                ck.access("h_final", rHfin, U(p.hfin) + (bg.b * p.hfin_b + bg.c * p.hfin_c + st) * 4, NS * 4);
+            if (p.sdelta && lg.active && lg.sub == 0)
+                ck.access("delta_sum", rSd, U(p.sdelta) + (bg.b * p.sd_b + bg.c * p.sd_c + lg.d) * 4, 4);
+        }
+        if (!ck.ok()) return;
+
+        // buffer-resource rows: row must be one of the sequence's rows; the
+        // scalar offset row * row_bytes must fit 32 bits; the lane offset
+        // must lie inside the resource; the address inside the tensor.
+        auto row_access = [&](const char *what, const Region *reg, const void *base, int64_t elem_off,
+                              int64_t row_elems, int k) {
+            const int row = seg_row(sg, k);
+            if (row < 0 || row >= sq.len)
+                return ck.fail("%s: row %d outside the sequence of %lld rows (block %lld)", what, row,
+                               (long long)sq.len, (long long)bid);
+            const uint64_t soff = static_cast<uint64_t>(row) * static_cast<uint64_t>(row_elems * es);
+            if (soff > UINT32_MAX) return ck.fail("%s: scalar offset %llu above 32 bits", what,
+                                                  (unsigned long long)soff);
+            const uint32_t nrec = seq_span_bytes(sq.len, row_elems, p.D, es);
+            if (static_cast<uint64_t>(dmax) * es + es > nrec)
+                return ck.fail("%s: lane offset beyond the buffer resource", what);
+            const uintptr_t b0 = U(base) + elem_off * es + soff;
+            ck.access(what, reg, b0 + static_cast<uint64_t>(dmin) * es, es);
+            ck.access(what, reg, b0 + static_cast<uint64_t>(dmax) * es, es);
+        };
+        auto load_pos = [&](int k) {
+            row_access("x", rX, p.x, sq.xo, p.xs, k);
+            row_access("dt", rD, p.dt, sq.dto, p.dts, k);
+            if (l.mode == kModeRes) row_access("res", rR, p.res, sq.ro, p.rs, k);
+        };
+        const int ntok = sg.ntok;
+        if (ntok > 0)
+            for (int j = 0; j < kPrefetch; ++j) load_pos(prefetch_pos(j, ntok));
+        for (int k = 0; k < ntok && ck.ok(); ++k) {
+            load_pos(prefetch_pos(k + kPrefetch, ntok));
+            if (readout) row_access("out", rO, p.out, sq.oo, p.os, k);
+        }
+
+        // Bm/Cm staging, tile by tile
+        for (int base = 0; base < ntok && ck.ok(); base += kTile) {
+            const int cnt = ntok - base < kTile ? ntok - base : kTile;
+            for (int lane = 0; lane < kWG; ++lane)
+                for (int i = 0; i < STAGE; ++i) {
+                    const int k = stage_token(i, lane, NBC), col = stage_col(i, lane, NBC);
+                    if (i * kWG + lane >= kTile * NBC) ck.fail("LDS slot past the tile");
+                    if (k >= cnt) continue;
+                    const int64_t row = seg_row(sg, base + k);
+                    if (row < 0 || row >= sq.len) ck.fail("staging row %lld outside the sequence", (long long)row);
+                    if (col < kN)
+                        ck.access("Bm", rB, U(p.Bm) + (sq.Bo + row * p.Bs + col) * es, es);
+                    else
+                        ck.access("Cm", rC, U(p.Cm) + (sq.Co + row * p.Cs + col - kN) * es, es);
+                }
+        }
+    }
+}
+
+void check_carry(Checker &ck, const Launch &l, const int32_t *cu_host) {
+    const CarryParams &p = l.carry;
+    const Region *rA = ck.region_of(p.A), *rQ = ck.region_of(p.Q), *rS = ck.region_of(p.S);
+    const Region *rH = p.Hc ? ck.region_of(p.Hc) : nullptr, *rin = p.hin ? ck.region_of(p.hin) : nullptr;
+    const Region *rout = p.hout ? ck.region_of(p.hout) : nullptr;
+    const int64_t total = p.batch * p.D * kN, grid = (total + 255) / 256 * 256;
+    for (int64_t i = 0; i < grid && ck.ok(); ++i) {
+        const CarryGeom g = carry_geom(p.batch, p.D, i);
+        if (!g.valid) continue;
+        const int64_t len = p.cu_seqlens ? static_cast<int64_t>(cu_host[g.b + 1]) - cu_host[g.b] : p.seqlen;
+        const int nc = carry_chunks(len, p.chunk_len, p.nchunks);
+        ck.access("A", rA, U(p.A) + (g.d * kN + g.n) * 4, 4);
+        if (p.hin) ck.access("h_in", rin, U(p.hin) + ((g.b * p.D + g.d) * kN + g.n) * 4, 4);
+        for (int c = 0; c < nc; ++c) {
+            const int64_t sc = (g.b * p.nchunks + c) * p.D + g.d;
+            if (p.Hc) ck.access("H", rH, U(p.Hc) + (sc * kN + g.n) * 4, 4);
+            ck.access("S", rS, U(p.S) + sc * 4, 4);
+            ck.access("Q", rQ, U(p.Q) + (sc * kN + g.n) * 4, 4);
+        }
+        if (p.hout) ck.access("h_out", rout, U(p.hout) + ((g.b * p.D + g.d) * kN + g.n) * 4, 4);
+    }
+}
+
+}  // namespace
+
+r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const int32_t *cu_host,
+                          r2l_access_report *rep) {
+    const int64_t es = elem_size(a->dtype), D = a->dim, N = kN;
+    const int64_t tok = tokens_of(a);
+    std::vector<Region> regs;
+    auto add = [&](const char *name, const void *p, uint64_t bytes) {
+        if (p && bytes) regs.push_back({name, U(p), U(p) + bytes});
+    };
+    auto tspan = [&](const void *p, int64_t stride, int64_t bstride, int64_t cols) -> uint64_t {
+        if (!p || tok <= 0) return 0;
+        const int64_t ext = is_ragged(a)
+            ? (tok - 1) * stride + cols
+            : (a->batch - 1) * eff_bstride(a, bstride, stride) + (a->seqlen - 1) * stride + cols;
+        return static_cast<uint64_t>(ext * es);
+    };
+    add("x", a->x, tspan(a->x, a->x_stride, a->x_batch_stride, D));
+    add("dt", a->dt, tspan(a->dt, a->dt_stride, a->dt_batch_stride, D));
+    add("Bm", a->Bm, tspan(a->Bm, a->Bm_stride, a->Bm_batch_stride, N));
+    add("Cm", a->Cm, tspan(a->Cm, a->Cm_stride, a->Cm_batch_stride, N));
+    add("res", a->res, tspan(a->res, a->res_stride, a->res_batch_stride, D));
+    add("out", a->out, tspan(a->out, a->out_stride, a->out_batch_stride, D));
+    add("A", a->A, static_cast<uint64_t>(D * N * 4));
+    add("Dskip", a->Dskip, static_cast<uint64_t>(D * 4));
+    add("h_in", a->h_in, static_cast<uint64_t>(a->batch * D * N * 4));
+    add("h_out", a->h_out, static_cast<uint64_t>(a->batch * D * N * 4));
+    add("cu_seqlens", a->cu_seqlens, static_cast<uint64_t>((a->batch + 1) * 4));
+    if (pl.chunked) {
+        const char *ws = static_cast<const char *>(a->workspace);
+        add("workspace Q", ws, pl.off_S);
+        add("workspace S", ws + pl.off_S, (wants_readout(op, a) ? pl.off_H : pl.ws_bytes) - pl.off_S);
+        if (wants_readout(op, a)) add("workspace H", ws + pl.off_H, pl.ws_bytes - pl.off_H);
+    }
+    Checker ck(std::move(regs), rep);
+    Launch ls[3];
+    const int n = build_launches(op, a, pl, ls);
+    for (int i = 0; i < n && ck.ok(); ++i) {
+        ++rep->launches;
+        if (ls[i].kind == Launch::Segment)
+            check_segment(ck, ls[i], cu_host);
+        else
+            check_carry(ck, ls[i], cu_host);
+    }
+    return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;
+}
+
+}  // namespace r2l

@@ -1,0 +1,14 @@
+// bounds_check.h -- host replay of the kernels' memory accesses (internal).
+#pragma once
+
+#include "r2l_scan_debug.h"
+#include "scan_plan.h"
+
+namespace r2l {
+
+// Checks every access of the launches of (op, a, pl); the arguments must have
+// passed the entry point's checks. cu_host: host copy of cu_seqlens (ragged).
+r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const int32_t *cu_host,
+                          r2l_access_report *rep);
+
+}  // namespace r2l

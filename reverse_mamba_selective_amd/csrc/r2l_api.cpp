@@ -1,0 +1,344 @@
+// r2l_api.cpp -- host side of libr2l_scan.so: argument checks, planning and
+// launches for the entry points declared in include/r2l_scan.h.
+//
+// Every check runs before anything is queued, so a failed call leaves device
+// memory untouched. The library allocates nothing: chunked plans use the
+// caller's workspace, whose size r2l_workspace_size reports for the same plan.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "r2l_scan.h"
+#include "scan_internal.h"
+#include "bounds_check.h"
+#include "scan_plan.h"
+
+namespace {
+
+using r2l::elem_size;
+using r2l::eff_bstride;
+using r2l::Launch;
+using r2l::max_len_of;
+using r2l::Op;
+using r2l::Plan;
+using r2l::tokens_of;
+using r2l::wants_readout;
+
+thread_local char g_last_error[512] = "";
+
+r2l_status fail(r2l_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+r2l_status ok() {
+    g_last_error[0] = '\0';
+    return R2L_OK;
+}
+
+bool ragged(const r2l_scan_args *a) { return r2l::is_ragged(a); }
+
+// ---- shape checks shared by planning and the entry points -------------------
+r2l_status check_shape(const r2l_scan_args *a) {
+    if (!a) return fail(R2L_ERR_INVALID_ARG, "args is NULL");
+    if (a->batch < 0) return fail(R2L_ERR_INVALID_ARG, "batch < 0");
+    if (a->dim < 1) return fail(R2L_ERR_INVALID_ARG, "dim < 1");
+    if (a->dim > (int64_t(1) << 31) / 4) return fail(R2L_ERR_UNSUPPORTED, "dim too large");
+    if (a->dstate != r2l::kN)
+        return fail(R2L_ERR_UNSUPPORTED, "dstate %d is not built (only %d)", a->dstate, r2l::kN);
+    if (a->dtype != R2L_DTYPE_F32 && a->dtype != R2L_DTYPE_BF16)
+        return fail(R2L_ERR_UNSUPPORTED, "dtype %d is not built", a->dtype);
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(R2L_ERR_INVALID_ARG, "delta_softplus must be 0 or 1");
+    if (a->state_split != 0 && a->state_split != 1 && a->state_split != 2 && a->state_split != 4)
+        return fail(R2L_ERR_INVALID_ARG, "state_split must be 0, 1, 2 or 4");
+    if (ragged(a)) {
+        if (a->total_tokens < 0) return fail(R2L_ERR_INVALID_ARG, "total_tokens < 0");
+        if (a->max_seqlen < 0) return fail(R2L_ERR_INVALID_ARG, "max_seqlen < 0");
+        if (a->total_tokens > INT32_MAX)
+            return fail(R2L_ERR_UNSUPPORTED, "ragged layout limited to 2^31-1 tokens (int32 offsets)");
+        if (a->batch > 0 && a->max_seqlen > a->total_tokens)
+            return fail(R2L_ERR_INVALID_ARG, "max_seqlen %lld exceeds total_tokens %lld",
+                        (long long)a->max_seqlen, (long long)a->total_tokens);
+        if (a->batch == 0 && a->total_tokens != 0)
+            return fail(R2L_ERR_INVALID_ARG, "batch 0 with total_tokens != 0");
+    } else {
+        if (a->seqlen < 0) return fail(R2L_ERR_INVALID_ARG, "seqlen < 0");
+        if (a->seqlen > INT32_MAX) return fail(R2L_ERR_UNSUPPORTED, "seqlen above 2^31-1");
+    }
+    return R2L_OK;
+}
+
+// ---- buffer checks -----------------------------------------------------------
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi), empty when lo == hi
+    bool is_output;
+};
+
+Range span(const char *name, const void *p, int64_t rows, int64_t stride, int64_t cols, int64_t es,
+           bool out) {
+    Range r{name, 0, 0, out};
+    if (!p || rows <= 0 || cols <= 0) return r;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + static_cast<uintptr_t>(((rows - 1) * stride + cols) * es);
+    return r;
+}
+
+// Address span of a token-major tensor [tokens, cols] (either layout).
+Range token_span(const char *name, const r2l_scan_args *a, const void *p, int64_t stride,
+                 int64_t bstride, int64_t cols, int64_t es, bool out) {
+    Range r{name, 0, 0, out};
+    const int64_t tok = tokens_of(a);
+    if (!p || tok <= 0 || cols <= 0) return r;
+    int64_t extent;
+    if (ragged(a)) {
+        extent = (tok - 1) * stride + cols;
+    } else {
+        extent = (a->batch - 1) * eff_bstride(a, bstride, stride) + (a->seqlen - 1) * stride + cols;
+    }
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + static_cast<uintptr_t>(extent * es);
+    return r;
+}
+
+bool overlap(const Range &x, const Range &y) {
+    return x.lo < x.hi && y.lo < y.hi && x.lo < y.hi && y.lo < x.hi;
+}
+
+bool aligned(const void *p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) % al) == 0; }
+
+r2l_status check_buffers(Op op, const r2l_scan_args *a, const Plan &pl) {
+    const int64_t tok = tokens_of(a);
+    const int64_t D = a->dim, N = r2l::kN, es = elem_size(a->dtype);
+    const bool readout = wants_readout(op, a);
+
+    if (ragged(a) && a->batch > 0 && !a->cu_seqlens)
+        return fail(R2L_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    if (tok > 0) {
+        if (!a->x) return fail(R2L_ERR_INVALID_ARG, "x is NULL");
+        if (!a->dt) return fail(R2L_ERR_INVALID_ARG, "dt is NULL");
+        if (!a->Bm) return fail(R2L_ERR_INVALID_ARG, "Bm is NULL");
+        if (readout && !a->Cm) return fail(R2L_ERR_INVALID_ARG, "Cm is NULL (readout requested)");
+        if (readout && !a->out) return fail(R2L_ERR_INVALID_ARG, "out is NULL");
+        if (a->x_stride < D) return fail(R2L_ERR_INVALID_ARG, "x_stride < dim");
+        if (a->dt_stride < D) return fail(R2L_ERR_INVALID_ARG, "dt_stride < dim");
+        if (a->Bm_stride < N) return fail(R2L_ERR_INVALID_ARG, "Bm_stride < dstate");
+        if (readout && a->Cm_stride < N) return fail(R2L_ERR_INVALID_ARG, "Cm_stride < dstate");
+        if (readout && a->out_stride < D) return fail(R2L_ERR_INVALID_ARG, "out_stride < dim");
+        if (a->res && a->res_stride < D) return fail(R2L_ERR_INVALID_ARG, "res_stride < dim");
+        if (a->x_batch_stride < 0 || a->dt_batch_stride < 0 || a->Bm_batch_stride < 0 ||
+            a->Cm_batch_stride < 0 || a->res_batch_stride < 0 || a->out_batch_stride < 0)
+            return fail(R2L_ERR_INVALID_ARG, "negative batch stride");
+        if (readout && !ragged(a) && a->batch > 1 &&
+            eff_bstride(a, a->out_batch_stride, a->out_stride) < a->seqlen * a->out_stride)
+            return fail(R2L_ERR_ALIAS, "out: sequences overlap (batch stride < seqlen * stride)");
+        // The kernels address the rows of one sequence with 32-bit byte offsets.
+        const int64_t L = max_len_of(a);
+        const int64_t strides[] = {a->x_stride, a->dt_stride, a->res ? a->res_stride : 0,
+                                   readout ? a->out_stride : 0};
+        for (int64_t st : strides)
+            if (L > 0 && st > 0 && ((L - 1) * st + D) * es > (int64_t)UINT32_MAX)
+                return fail(R2L_ERR_UNSUPPORTED, "one sequence spans more than 4 GiB of a tensor");
+    }
+    if (a->batch > 0 && !a->A) return fail(R2L_ERR_INVALID_ARG, "A is NULL");
+    if (op == Op::Prefix && !a->h_out && !a->out)
+        return fail(R2L_ERR_INVALID_ARG, "prefix_scan_state needs h_out or out");
+    if (op == Op::Commit) {
+        if (!a->h_out) return fail(R2L_ERR_INVALID_ARG, "block_commit_state needs h_out (the state)");
+        if (a->h_in && a->h_in != a->h_out)
+            return fail(R2L_ERR_INVALID_ARG, "block_commit_state: h_in must be NULL or equal h_out");
+    }
+
+    // alignment
+    const struct { const void *p; uintptr_t al; const char *n; } al[] = {
+        {a->x, (uintptr_t)es, "x"},     {a->dt, (uintptr_t)es, "dt"},   {a->Bm, (uintptr_t)es, "Bm"},
+        {a->Cm, (uintptr_t)es, "Cm"},   {a->res, (uintptr_t)es, "res"}, {a->out, (uintptr_t)es, "out"},
+        {a->A, 16, "A"},                {a->Dskip, 4, "Dskip"},         {a->h_in, 16, "h_in"},
+        {a->h_out, 16, "h_out"},        {a->cu_seqlens, 4, "cu_seqlens"},
+        {a->workspace, 256, "workspace"}};
+    for (const auto &e : al)
+        if (e.p && !aligned(e.p, e.al))
+            return fail(R2L_ERR_MISALIGNED, "%s is not %u-byte aligned", e.n, (unsigned)e.al);
+
+    if (pl.chunked && (!a->workspace || a->workspace_bytes < pl.ws_bytes))
+        return fail(R2L_ERR_WORKSPACE, "chunked plan needs %zu workspace bytes, got %zu",
+                    pl.ws_bytes, a->workspace ? a->workspace_bytes : (size_t)0);
+
+    // aliasing
+    const bool commit_inplace = (op == Op::Commit);
+    std::vector<Range> rs = {
+        token_span("x", a, a->x, a->x_stride, a->x_batch_stride, D, es, false),
+        token_span("dt", a, a->dt, a->dt_stride, a->dt_batch_stride, D, es, false),
+        token_span("Bm", a, a->Bm, a->Bm_stride, a->Bm_batch_stride, N, es, false),
+        token_span("Cm", a, readout ? a->Cm : nullptr, a->Cm_stride, a->Cm_batch_stride, N, es,
+                   false),
+        token_span("res", a, readout ? a->res : nullptr, a->res_stride, a->res_batch_stride, D, es,
+                   false),
+        span("A", a->A, D, N, N, 4, false),
+        span("Dskip", readout ? a->Dskip : nullptr, 1, D, D, 4, false),
+        span("cu_seqlens", a->cu_seqlens, 1, a->batch + 1, a->batch + 1, 4, false),
+        span("h_in", commit_inplace ? nullptr : a->h_in, a->batch, D * N, D * N, 4, false),
+        token_span("out", a, readout ? a->out : nullptr, a->out_stride, a->out_batch_stride, D, es,
+                   true),
+        span("h_out", a->h_out, a->batch, D * N, D * N, 4, true),
+        span("workspace", pl.chunked ? a->workspace : nullptr, 1, (int64_t)pl.ws_bytes,
+             (int64_t)pl.ws_bytes, 1, true),
+    };
+    for (size_t i = 0; i < rs.size(); ++i) {
+        for (size_t j = i + 1; j < rs.size(); ++j) {
+            const Range &u = rs[i], &v = rs[j];
+            if (!(u.is_output || v.is_output) || !overlap(u, v)) continue;
+            const Range &o = u.is_output ? u : v;
+            const Range &other = u.is_output ? v : u;
+            const char *on = o.name, *tn = other.name;
+            // allowed exact aliases
+            if (!strcmp(on, "out") && (!strcmp(tn, "x") || !strcmp(tn, "res"))) {
+                const bool is_x = !strcmp(tn, "x");
+                const void *tp = is_x ? a->x : a->res;
+                const int64_t ts = is_x ? a->x_stride : a->res_stride;
+                const int64_t tbs = is_x ? a->x_batch_stride : a->res_batch_stride;
+                if (tp == a->out && ts == a->out_stride &&
+                    eff_bstride(a, tbs, ts) == eff_bstride(a, a->out_batch_stride, a->out_stride))
+                    continue;
+            }
+            if (!strcmp(on, "h_out") && !strcmp(tn, "h_in") && a->h_in == a->h_out) continue;
+            return fail(R2L_ERR_ALIAS, "%s overlaps %s", on, tn);
+        }
+    }
+    return R2L_OK;
+}
+
+// Optional host-side check of device offsets (R2L_CHECK_SEQLENS=1).
+r2l_status check_seqlens_on_device(const r2l_scan_args *a) {
+    const char *env = getenv("R2L_CHECK_SEQLENS");
+    if (!env || strcmp(env, "1") != 0 || !ragged(a) || a->batch == 0) return R2L_OK;
+    std::vector<int32_t> cu(static_cast<size_t>(a->batch) + 1);
+    hipError_t e = hipMemcpy(cu.data(), a->cu_seqlens, cu.size() * sizeof(int32_t),
+                             hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(R2L_ERR_HIP, "cu_seqlens copy: %s", hipGetErrorString(e));
+    if (cu[0] != 0) return fail(R2L_ERR_INVALID_ARG, "cu_seqlens[0] != 0");
+    for (int64_t b = 0; b < a->batch; ++b) {
+        const int64_t L = static_cast<int64_t>(cu[b + 1]) - cu[b];
+        if (L < 0) return fail(R2L_ERR_INVALID_ARG, "cu_seqlens decreases at %lld", (long long)b);
+        if (L > a->max_seqlen)
+            return fail(R2L_ERR_INVALID_ARG, "sequence %lld longer than max_seqlen", (long long)b);
+    }
+    if (cu[a->batch] != a->total_tokens)
+        return fail(R2L_ERR_INVALID_ARG, "cu_seqlens[batch] != total_tokens");
+    return R2L_OK;
+}
+
+// ---- launching ----------------------------------------------------------------
+r2l_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(R2L_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    const Plan pl = r2l::make_plan(op, a);
+    st = check_buffers(op, a, pl);
+    if (st != R2L_OK) return st;
+    st = check_seqlens_on_device(a);
+    if (st != R2L_OK) return st;
+    if (a->batch * pl.nchunks * pl.tiles > INT32_MAX - 8)
+        return fail(R2L_ERR_UNSUPPORTED, "grid too large");
+
+    Launch ls[3];
+    const int n = r2l::build_launches(op, a, pl, ls);
+    for (int i = 0; i < n; ++i) {
+        const Launch &l = ls[i];
+        const hipError_t e =
+            l.kind == Launch::Segment
+                ? r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream)
+                : r2l::launch_carry(l.carry, stream);
+        st = hip_status(e, l.kind == Launch::Segment ? "segment scan launch" : "carry launch");
+        if (st != R2L_OK) return st;
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+r2l_status r2l_scan(const r2l_scan_args *a, void *stream) {
+    return run(Op::Scan, a, static_cast<hipStream_t>(stream));
+}
+
+r2l_status prefix_scan_state(const r2l_scan_args *a, void *stream) {
+    return run(Op::Prefix, a, static_cast<hipStream_t>(stream));
+}
+
+r2l_status block_commit_state(const r2l_scan_args *a, void *stream) {
+    return run(Op::Commit, a, static_cast<hipStream_t>(stream));
+}
+
+r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes) {
+    if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
+    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT)
+        return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    const Op o = op == R2L_OP_SCAN ? Op::Scan : (op == R2L_OP_PREFIX ? Op::Prefix : Op::Commit);
+    *bytes = r2l::make_plan(o, a).ws_bytes;
+    return ok();
+}
+
+r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *cu_seqlens_host,
+                            r2l_access_report *report) {
+    if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
+    report->launches = report->accesses = 0;
+    report->message[0] = '\0';
+    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT)
+        return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    const Op o = op == R2L_OP_SCAN ? Op::Scan : (op == R2L_OP_PREFIX ? Op::Prefix : Op::Commit);
+    const Plan pl = r2l::make_plan(o, a);
+    st = check_buffers(o, a, pl);
+    if (st != R2L_OK) return st;
+    if (ragged(a) && a->batch > 0) {
+        if (!cu_seqlens_host) return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[a->batch] != a->total_tokens)
+            return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host does not span total_tokens");
+        for (int64_t b = 0; b < a->batch; ++b) {
+            const int64_t L = static_cast<int64_t>(cu_seqlens_host[b + 1]) - cu_seqlens_host[b];
+            if (L < 0 || L > a->max_seqlen)
+                return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host: bad length at %lld", (long long)b);
+        }
+    }
+    st = r2l::check_accesses(o, a, pl, cu_seqlens_host, report);
+    if (st != R2L_OK) return fail(st, "%s", report->message);
+    return ok();
+}
+
+const char *r2l_status_string(r2l_status s) {
+    switch (s) {
+        case R2L_OK: return "ok";
+        case R2L_ERR_INVALID_ARG: return "invalid argument";
+        case R2L_ERR_UNSUPPORTED: return "unsupported dtype or size";
+        case R2L_ERR_ALIAS: return "buffers overlap";
+        case R2L_ERR_MISALIGNED: return "misaligned pointer";
+        case R2L_ERR_WORKSPACE: return "workspace missing or too small";
+        case R2L_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *r2l_last_error(void) { return g_last_error; }
+
+int32_t r2l_abi_version(void) { return R2L_ABI_VERSION; }
+
+}  // extern "C"

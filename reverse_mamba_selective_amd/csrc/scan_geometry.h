@@ -1,0 +1,148 @@
+// scan_geometry.h -- the index math of the segment-scan and carry kernels,
+// shared by the kernels (device) and by the host-side access checker
+// (bounds_check.cpp), so that the checker sees exactly the addresses the
+// kernels form.
+#pragma once
+
+#include <stdint.h>
+
+#include "scan_internal.h"
+
+#if defined(__HIPCC__)
+#define R2L_HD __host__ __device__ __forceinline__
+#else
+#define R2L_HD inline
+#endif
+
+namespace r2l {
+
+constexpr int kPrefetch = 8;   // tokens of x/dt/res loaded ahead of use
+
+// Block -> (sequence b, chunk c, channel tile). Launches pad the grid to a
+// multiple of 8 and remap ids so that consecutive logical blocks (the tiles of
+// one segment) land on one XCD: hardware block i goes to XCD i % 8.
+struct BlockGeom {
+    bool valid;
+    int tile;
+    int c;
+    int64_t b;
+};
+
+R2L_HD int64_t padded_grid(int64_t nblocks) { return ((nblocks + 7) / 8) * 8; }
+
+R2L_HD BlockGeom block_geom(int64_t nblocks, int32_t tiles, int32_t nchunks, int64_t bid) {
+    BlockGeom g{false, 0, 0, 0};
+    const int64_t per = (nblocks + 7) >> 3;
+    const int64_t logical = (bid & 7) * per + (bid >> 3);
+    if (logical >= nblocks) return g;
+    g.valid = true;
+    g.tile = static_cast<int>(logical % tiles);
+    const int64_t seg = logical / tiles;
+    g.c = static_cast<int>(seg % nchunks);
+    g.b = seg / nchunks;
+    return g;
+}
+
+// Sequence b: its length and the element offset of its first row in each
+// token-major tensor. s0, s1 are cu_seqlens[b], cu_seqlens[b+1] (ragged).
+struct SeqGeom {
+    int64_t len, xo, dto, Bo, Co, ro, oo;
+};
+
+R2L_HD SeqGeom seq_geom(const SegParams &p, int64_t b, int64_t s0, int64_t s1) {
+    SeqGeom q;
+    if (p.cu_seqlens) {
+        q.len = s1 - s0;
+        q.xo = s0 * p.xs; q.dto = s0 * p.dts; q.Bo = s0 * p.Bs; q.Co = s0 * p.Cs;
+        q.ro = s0 * p.rs; q.oo = s0 * p.os;
+    } else {
+        q.len = p.seqlen;
+        q.xo = b * p.xbs; q.dto = b * p.dtbs; q.Bo = b * p.Bbs; q.Co = b * p.Cbs;
+        q.ro = b * p.rbs; q.oo = b * p.obs;
+    }
+    return q;
+}
+
+// Chunk c of a sequence of len tokens, in visiting order. `run` is false for
+// a chunk past the end (the block exits); chunk 0 always runs, possibly with
+// no token, because it writes the final state. The k-th visited token of the
+// segment is sequence row t_first + step * k, for 0 <= k < ntok.
+struct SegGeom {
+    bool run;
+    int ntok;
+    int t_first;
+    int step;
+};
+
+R2L_HD SegGeom seg_geom(bool rev, int c, int64_t chunk_len, int64_t len) {
+    SegGeom g{false, 0, 0, rev ? -1 : 1};
+    const int64_t v0 = static_cast<int64_t>(c) * chunk_len;
+    if (c > 0 && v0 >= len) return g;
+    const int64_t v1 = v0 + chunk_len < len ? v0 + chunk_len : len;
+    g.run = true;
+    g.ntok = v1 > v0 ? static_cast<int>(v1 - v0) : 0;
+    g.t_first = static_cast<int>(rev ? len - 1 - v0 : v0);
+    return g;
+}
+
+R2L_HD int seg_row(const SegGeom &g, int k) { return g.t_first + g.step * k; }
+
+// The visited position whose inputs are loaded into the register ring when
+// position k is wanted: k itself while it exists, else the last one (a
+// harmless reload). Only meaningful when ntok > 0.
+R2L_HD int prefetch_pos(int k, int ntok) { return k < ntok ? k : ntok - 1; }
+
+// Lane -> channel: G adjacent lanes share channel d and hold states
+// sub*NS .. sub*NS+NS-1. Lanes past the last channel shadow it (same inputs,
+// bit-identical results) so that every lane can run the same code.
+struct LaneGeom {
+    bool active;
+    int sub;
+    uint32_t d;
+};
+
+R2L_HD LaneGeom lane_geom(int tile, int lane, int G, int64_t D) {
+    LaneGeom g;
+    const int64_t gl = static_cast<int64_t>(tile) * kWG + lane;
+    const int64_t own = gl / G;
+    g.sub = static_cast<int>(gl % G);
+    g.active = own < D;
+    g.d = static_cast<uint32_t>(g.active ? own : D - 1);
+    return g;
+}
+
+// Bm/Cm staging of one tile: thread `lane`, element i covers LDS slot
+// q = i*kWG + lane = k*NBC + col, i.e. token k of the tile, column col
+// (col < kN: Bm[.., col]; else Cm[.., col - kN]).
+R2L_HD int stage_token(int i, int lane, int nbc) { return (i * kWG + lane) / nbc; }
+R2L_HD int stage_col(int i, int lane, int nbc) { return (i * kWG + lane) % nbc; }
+
+// Bytes a raw buffer resource over one sequence of a tensor covers.
+R2L_HD uint32_t seq_span_bytes(int64_t len, int64_t row_elems, int64_t D, int64_t es) {
+    const int64_t rows = len > 0 ? len - 1 : 0;
+    return static_cast<uint32_t>((rows * row_elems + D) * es);
+}
+
+// Carry kernel: thread i -> (b, d, n); chunks of sequence b actually present.
+struct CarryGeom {
+    bool valid;
+    int n;
+    int64_t d, b;
+};
+
+R2L_HD CarryGeom carry_geom(int64_t batch, int64_t D, int64_t i) {
+    CarryGeom g{false, 0, 0, 0};
+    if (i >= batch * D * kN) return g;
+    g.valid = true;
+    g.n = static_cast<int>(i % kN);
+    g.d = (i / kN) % D;
+    g.b = i / (kN * D);
+    return g;
+}
+
+R2L_HD int carry_chunks(int64_t len, int32_t chunk_len, int32_t nchunks) {
+    const int64_t nc = (len + chunk_len - 1) / chunk_len;
+    return static_cast<int>(nc < nchunks ? nc : nchunks);
+}
+
+}  // namespace r2l

@@ -1,0 +1,76 @@
+// scan_internal.h -- parameters shared by the host dispatcher (r2l_api.cpp) and
+// the gfx950 kernels (scan_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace r2l {
+
+constexpr int kN = 16;      // state size the kernels are built for
+constexpr int kWG = 256;    // threads per workgroup (4 wave64s)
+constexpr int kTile = 64;   // tokens of Bm/Cm rows staged in LDS at a time
+
+// What a segment scan writes per token: nothing (state only), y, or the gated
+// residual with x itself or a separate tensor as the residual.
+constexpr int kModeState = 0;
+constexpr int kModeY = 1;
+constexpr int kModeResX = 2;
+constexpr int kModeRes = 3;
+
+// One launch of the segment kernel scans "segments": chunk c (in visiting
+// order) of sequence b, for a tile of kWG lanes. With G lanes per channel a
+// tile covers kWG / G channels.
+struct SegParams {
+    int64_t seqlen;              // dense tokens per sequence (when cu_seqlens == nullptr)
+    const int32_t *cu_seqlens;   // ragged offsets [batch+1] or nullptr
+    int64_t D;
+    int32_t chunk_len;           // tokens per chunk, visiting order
+    int32_t nchunks;             // chunks per sequence in the grid
+    int32_t tiles;               // channel tiles per segment
+    int64_t nblocks;             // batch * nchunks * tiles (logical blocks)
+
+    // token strides (xs, ...) and, dense layout only, batch strides (xbs, ...), in elements
+    const void *x;  int64_t xs, xbs;
+    const void *dt; int64_t dts, dtbs;
+    const void *Bm; int64_t Bs, Bbs;
+    const void *Cm; int64_t Cs, Cbs;
+    const float *A;
+    const float *Dskip;
+    int32_t softplus;
+
+    // state before the segment's first visited token: hin + b*hin_b + c*hin_c + d*kN
+    const float *hin; int64_t hin_b, hin_c;
+    // state after its last visited token
+    float *hfin; int64_t hfin_b, hfin_c;
+    // sum of Delta over the segment per channel: sdelta + b*sd_b + c*sd_c + d
+    float *sdelta; int64_t sd_b, sd_c;
+
+    const void *res; int64_t rs, rbs;
+    float s;
+    void *out; int64_t os, obs;
+};
+
+// Joins chunk results (local final state Q from a zero start and the Delta sum
+// S of each chunk) into the state entering every chunk and the final state.
+struct CarryParams {
+    int64_t batch;
+    int64_t seqlen;
+    const int32_t *cu_seqlens;
+    int64_t D;
+    int32_t chunk_len;
+    int32_t nchunks;
+    const float *A;
+    const float *hin;            // [batch, D, N] or nullptr (zero)
+    const float *Q;              // [batch, nchunks, D, N]
+    const float *S;              // [batch, nchunks, D]
+    float *Hc;                   // [batch, nchunks, D, N] state entering each chunk, or nullptr
+    float *hout;                 // [batch, D, N] or nullptr
+};
+
+// dtype: 0 fp32, 1 bf16. G in {1, 2, 4}. mode: kMode*.
+hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode,
+                               const SegParams &p, hipStream_t stream);
+hipError_t launch_carry(const CarryParams &p, hipStream_t stream);
+
+}  // namespace r2l

@@ -1,0 +1,389 @@
+// scan_kernels.hip -- gfx950 kernels of the R2L / forward selective scans.
+//
+// The operation (see include/r2l_scan.h for the full contract and its sources):
+// per sequence, channel d and state n, tokens visited right to left (the R2L
+// stream of "Bifocal Diffusion Language Models", section 2) or left to right
+// (the forward-only boundary states of "Training Hybrid Block Diffusion
+// Language Models with Partial Bidirectionality", "Methodology" item 1):
+//     Delta = softplus(dt);  h_n = exp(Delta*A[d,n])*h_n + Delta*Bm[t,n]*x[t,d]
+//     y = sum_n Cm[t,n]*h_n + Dskip[d]*x[t,d];  out = res + s*y  (s == 0: res)
+//
+// Mapping onto CDNA4. This is a recurrence over tokens with one exp per
+// (token, channel, state): vector ALU work, no dense contraction, so no MFMA.
+//  * Lanes run over channels: G lanes (1, 2 or 4) own one channel and hold its
+//    N/G fp32 states in VGPRs for the whole segment. A wave reads 64/G
+//    consecutive channels of a token row: one coalesced 64/G*sizeof(T) span
+//    per tensor and token.
+//  * Bm/Cm rows are shared by every channel. A workgroup stages kTile rows of
+//    them in LDS as fp32 (converted once), and every wave reads them back as
+//    broadcasts.
+//  * The reversal is only the sign of the token step in the address math; the
+//    output goes back to the token's own row, so nothing is flipped in memory.
+//  * Softplus and the decay are computed in-kernel with the hardware base-2
+//    exponential and logarithm (v_exp_f32 / v_log_f32), log2(e) being folded
+//    into A once per lane.
+//  * The gated residual (res + s*y, or the raw residual bits when s == 0) is
+//    fused into the store; bf16 outputs use the hardware round-to-nearest-even
+//    conversion.
+//  * Long sequences can be cut into chunks scanned from a zero state in
+//    parallel; the carry kernel then chains the chunk results. Because the
+//    recurrence is linear, a chunk's contribution to the state after it is its
+//    local final state Q plus exp(A * sum(Delta)) times the state entering it.
+//  * Block ids are remapped so that the tiles of one segment, which read the
+//    same Bm/Cm rows, are dispatched to the same XCD (blocks go round-robin
+//    over the 8 XCDs, each with its own L2).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_geometry.h"
+#include "scan_internal.h"
+
+namespace r2l {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- element access -------------------------------------------------------
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    using raw_t = uint32_t;
+    static __device__ __forceinline__ float ld(const float *p) { return *p; }
+    static __device__ __forceinline__ void st(float *p, float v) { *p = v; }
+    static __device__ __forceinline__ raw_t ld_raw(const float *p) {
+        return *reinterpret_cast<const uint32_t *>(p);
+    }
+    static __device__ __forceinline__ void st_raw(float *p, raw_t v) {
+        *reinterpret_cast<uint32_t *>(p) = v;
+    }
+    static __device__ __forceinline__ float widen(raw_t v) { return __uint_as_float(v); }
+    static __device__ __forceinline__ raw_t pack(float v) { return __float_as_uint(v); }
+    static __device__ __forceinline__ raw_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ void bstore(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+    }
+};
+
+// bf16 is carried as its 16 raw bits.
+template <>
+struct Elem<uint16_t> {
+    using raw_t = uint16_t;
+    static __device__ __forceinline__ float ld(const uint16_t *p) {
+        return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+    }
+    static __device__ __forceinline__ void st(uint16_t *p, float v) {
+        *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // v_cvt_pk_bf16_f32, RNE
+    }
+    static __device__ __forceinline__ raw_t ld_raw(const uint16_t *p) { return *p; }
+    static __device__ __forceinline__ void st_raw(uint16_t *p, raw_t v) { *p = v; }
+    static __device__ __forceinline__ float widen(raw_t v) {
+        return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    }
+    static __device__ __forceinline__ raw_t pack(float v) {
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // v_cvt_pk_bf16_f32, RNE
+    }
+    static __device__ __forceinline__ raw_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    }
+    static __device__ __forceinline__ void bstore(raw_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
+    }
+};
+
+// Raw buffer resource over [base, base + bytes) (word 3: the gfx9 raw-buffer
+// format). Its bound applies to the per-lane offset only; the scalar offset
+// added to it is not checked by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+// log(1 + e^v) = max(v, 0) + log(1 + e^-|v|), with base-2 hardware ops;
+// max(v, 0) is the median of (v, 0, +inf), one instruction.
+__device__ __forceinline__ float softplus(float v) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
+    const float l = __builtin_amdgcn_logf(1.0f + e);
+    return fmaf(l, kLn2, __builtin_amdgcn_fmed3f(v, 0.0f, __builtin_inff()));
+}
+
+// Sum of y over the G lanes (adjacent, same quad) that share a channel.
+template <int G>
+__device__ __forceinline__ float group_sum(float y) {
+    if constexpr (G >= 2) {
+        const int o = __builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+        y += __int_as_float(o);
+    }
+    if constexpr (G >= 4) {
+        const int o = __builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+        y += __int_as_float(o);
+    }
+    return y;
+}
+
+// ---- the segment scan ------------------------------------------------------
+// One workgroup scans one segment (a chunk of one sequence) for kWG/G channels.
+// Per lane and token: Delta, then for each of its NS states one exp, the state
+// update and (READOUT) the readout term; the G partial readouts are summed
+// across the lane group; then the skip term and the gated residual.
+//
+// Latency hiding: x / dt / res of the token PF positions ahead are loaded into
+// a register ring before the current token is computed, and the Bm/Cm rows of
+// the next kTile tokens are fetched into registers during the current tile and
+// written to the other half of a double-buffered LDS area at its end (one
+// barrier per tile). Row addresses are uniform (scalar) and the lane adds a
+// 32-bit channel offset.
+template <bool REV, typename T, int G, int MODE>
+__global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
+    constexpr bool READOUT = MODE != kModeState;
+    constexpr int NS = kN / G;                   // states per lane
+    constexpr int NBC = READOUT ? 2 * kN : kN;   // staged floats per token (B, then C)
+    constexpr int STAGE = kTile * NBC / kWG;     // staged elements per thread per tile
+    constexpr int PF = kPrefetch;
+    static_assert(kTile * NBC % kWG == 0 && kTile % PF == 0, "tile shape");
+    __shared__ float lds_bc[2][kTile * NBC];
+    using E = Elem<T>;
+    using R = typename E::raw_t;
+
+    const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
+    if (!bg.valid) return;
+    const int64_t b = bg.b;
+    const int c = bg.c;
+    const int64_t s0 = p.cu_seqlens ? p.cu_seqlens[b] : 0;
+    const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[b + 1] : 0;
+    const SeqGeom sq = seq_geom(p, b, s0, s1);
+    const SegGeom sg = seg_geom(REV, c, p.chunk_len, sq.len);
+    if (!sg.run) return;                          // chunk beyond this sequence
+    const int ntok = sg.ntok;
+
+    const LaneGeom lg = lane_geom(bg.tile, threadIdx.x, G, p.D);
+    const uint32_t dl = lg.d;
+    const int sub = lg.sub;
+
+    float a2[NS], h[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) a2[j] = p.A[dl * kN + sub * NS + j] * kLog2e;
+    if (p.hin) {
+        const float *hp = p.hin + b * p.hin_b + c * p.hin_c + dl * kN + sub * NS;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) h[j] = hp[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) h[j] = 0.0f;
+    }
+    const float dskip = (READOUT && p.Dskip) ? p.Dskip[dl] : 0.0f;
+    const bool softplus_on = p.softplus != 0;
+    float dsum = 0.0f;
+
+    // Per-token rows go through raw buffer resources based at the sequence's
+    // first row: the row offset is a scalar (row * row bytes) and the lane
+    // adds its fixed 32-bit channel offset. The resource bound only checks the
+    // lane offset, so every row used below is one of the segment's own rows;
+    // the host guarantees that one sequence of one tensor spans < 4 GiB.
+    const uint32_t es = static_cast<uint32_t>(sizeof(T));
+    const uint32_t doff = dl * es;
+    const uint32_t xrb = static_cast<uint32_t>(p.xs) * es, drb = static_cast<uint32_t>(p.dts) * es;
+    const uint32_t rrb = static_cast<uint32_t>(p.rs) * es, orb = static_cast<uint32_t>(p.os) * es;
+    const auto rx = make_rsrc(static_cast<const T *>(p.x) + sq.xo,
+                              seq_span_bytes(sq.len, p.xs, p.D, es));
+    const auto rd = make_rsrc(static_cast<const T *>(p.dt) + sq.dto,
+                              seq_span_bytes(sq.len, p.dts, p.D, es));
+    const auto rr_ = make_rsrc(MODE == kModeRes ? static_cast<const T *>(p.res) + sq.ro : nullptr,
+                               MODE == kModeRes ? seq_span_bytes(sq.len, p.rs, p.D, es) : 0);
+    const auto ro_ = make_rsrc(READOUT ? static_cast<T *>(p.out) + sq.oo : nullptr,
+                               READOUT ? seq_span_bytes(sq.len, p.os, p.D, es) : 0);
+    const T *Bseq = static_cast<const T *>(p.Bm) + sq.Bo;
+    const T *Cseq = READOUT ? static_cast<const T *>(p.Cm) + sq.Co : nullptr;
+    const float gate = p.s;
+    const bool gate_zero = gate == 0.0f;
+
+    // ---- register ring of per-token inputs (slot = position % PF)
+    R xq[PF], dq[PF], rq[PF];
+    auto load_pos = [&](int k, int slot) {       // k: a visited position of this segment
+        const uint32_t row = static_cast<uint32_t>(seg_row(sg, k));
+        xq[slot] = E::bload(rx, doff, row * xrb);
+        dq[slot] = E::bload(rd, doff, row * drb);
+        if constexpr (MODE == kModeRes) rq[slot] = E::bload(rr_, doff, row * rrb);
+    };
+#pragma unroll
+    for (int j = 0; j < PF; ++j) rq[j] = 0;
+    if (ntok > 0) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) load_pos(prefetch_pos(j, ntok), j);
+    }
+
+    // ---- Bm/Cm staging of one tile of kTile tokens
+    R stg[STAGE];
+    auto stage_load = [&](int tbase, int tcnt) {
+#pragma unroll
+        for (int i = 0; i < STAGE; ++i) {
+            const int k = stage_token(i, threadIdx.x, NBC);
+            const int col = stage_col(i, threadIdx.x, NBC);
+            if (k < tcnt) {
+                const int64_t l = seg_row(sg, tbase + k);
+                stg[i] = col < kN ? E::ld_raw(Bseq + l * p.Bs + col)
+                                  : E::ld_raw(Cseq + l * p.Cs + (col - kN));
+            }
+        }
+    };
+    auto stage_store = [&](int buf, int tcnt) {
+#pragma unroll
+        for (int i = 0; i < STAGE; ++i)
+            if (stage_token(i, threadIdx.x, NBC) < tcnt)
+                lds_bc[buf][i * kWG + threadIdx.x] = E::widen(stg[i]);
+    };
+
+    // One visited position k: consume ring slot `slot`, refill it with the
+    // position PF ahead, update the state and store the output row.
+    auto token = [&](int k, const float *bcrow, int slot) {
+        const R xr = xq[slot], dr = dq[slot], rr = rq[slot];
+        load_pos(prefetch_pos(k + PF, ntok), slot);
+        const float xv = E::widen(xr);
+        const float dv = E::widen(dr);
+        const float delta = softplus_on ? softplus(dv) : dv;
+        if constexpr (!READOUT) dsum += delta;
+        const float dx = delta * xv;
+        const float *row = bcrow + sub * NS;
+        float y = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float abar = __builtin_amdgcn_exp2f(delta * a2[n]);
+            h[n] = fmaf(abar, h[n], row[n] * dx);
+            if constexpr (READOUT) y = fmaf(row[kN + n], h[n], y);
+        }
+        if constexpr (READOUT) {
+            y = group_sum<G>(y);
+            y = fmaf(dskip, xv, y);
+            // Every lane stores: the G lanes of a channel, and idle lanes
+            // shadowing the last channel, hold bit-identical values for the
+            // same address.
+            R o;
+            if constexpr (MODE == kModeY) {
+                o = E::pack(y);
+            } else {
+                const R rbits = MODE == kModeRes ? rr : xr;
+                const R gated = E::pack(fmaf(gate, y, E::widen(rbits)));
+                o = gate_zero ? rbits : gated;   // s == 0: the residual bits themselves
+            }
+            const uint32_t orow = static_cast<uint32_t>(seg_row(sg, k));
+            E::bstore(o, ro_, doff, orow * orb);
+        }
+    };
+
+    const int ntiles = (ntok + kTile - 1) / kTile;
+    if (ntok > 0) {
+        const int cnt0 = ntok < kTile ? ntok : kTile;
+        stage_load(0, cnt0);
+        stage_store(0, cnt0);
+    }
+    __syncthreads();
+
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int base = ti * kTile;
+        const int cnt = ntok - base < kTile ? ntok - base : kTile;
+        const bool more = ti + 1 < ntiles;
+        const int ncnt = more ? (ntok - base - kTile < kTile ? ntok - base - kTile : kTile) : 0;
+        if (more) stage_load(base + kTile, ncnt);
+        const float *bc = lds_bc[ti & 1];
+
+        const int full = cnt - cnt % PF;
+        for (int k0 = 0; k0 < full; k0 += PF) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j) token(base + k0 + j, bc + (k0 + j) * NBC, j);
+        }
+#pragma unroll
+        for (int j = 0; j < PF; ++j)            // the last tile's partial group
+            if (full + j < cnt) token(base + full + j, bc + (full + j) * NBC, j);
+
+        if (more) stage_store((ti + 1) & 1, ncnt);
+        __syncthreads();
+    }
+
+    if (p.hfin && lg.active) {
+        float *hp = p.hfin + b * p.hfin_b + c * p.hfin_c + dl * kN + sub * NS;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) hp[j] = h[j];
+    }
+    if (p.sdelta && lg.active && sub == 0) p.sdelta[b * p.sd_b + c * p.sd_c + dl] = dsum;
+}
+
+// ---- the carry over chunks -------------------------------------------------
+// One lane per (sequence, channel, state); the chunk loop is short and its
+// loads do not depend on the carried value, so they pipeline.
+__global__ __launch_bounds__(256) void carry_kernel(const CarryParams p) {
+    const CarryGeom g = carry_geom(p.batch, p.D, static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+    if (!g.valid) return;
+    const int64_t len = p.cu_seqlens
+        ? static_cast<int64_t>(p.cu_seqlens[g.b + 1]) - p.cu_seqlens[g.b] : p.seqlen;
+    const int nc = carry_chunks(len, p.chunk_len, p.nchunks);
+    const float a2 = p.A[g.d * kN + g.n] * kLog2e;
+    float H = p.hin ? p.hin[(g.b * p.D + g.d) * kN + g.n] : 0.0f;
+    for (int c = 0; c < nc; ++c) {
+        const int64_t sc = (g.b * p.nchunks + c) * p.D + g.d;
+        if (p.Hc) p.Hc[sc * kN + g.n] = H;
+        const float P = __builtin_amdgcn_exp2f(a2 * p.S[sc]);
+        H = fmaf(P, H, p.Q[sc * kN + g.n]);
+    }
+    if (p.hout) p.hout[(g.b * p.D + g.d) * kN + g.n] = H;
+}
+
+template <bool REV, typename T, int MODE>
+hipError_t launch_g(int G, const SegParams &p, hipStream_t stream) {
+    const int64_t grid = padded_grid(p.nblocks);
+    switch (G) {
+        case 1:
+            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 1, MODE>), dim3(grid), dim3(kWG), 0,
+                               stream, p);
+            break;
+        case 2:
+            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 2, MODE>), dim3(grid), dim3(kWG), 0,
+                               stream, p);
+            break;
+        case 4:
+            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 4, MODE>), dim3(grid), dim3(kWG), 0,
+                               stream, p);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <bool REV, typename T>
+hipError_t launch_m(int mode, int G, const SegParams &p, hipStream_t stream) {
+    switch (mode) {
+        case kModeState: return launch_g<REV, T, kModeState>(G, p, stream);
+        case kModeY: return launch_g<REV, T, kModeY>(G, p, stream);
+        case kModeResX: return launch_g<REV, T, kModeResX>(G, p, stream);
+        case kModeRes: return launch_g<REV, T, kModeRes>(G, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode, const SegParams &p,
+                               hipStream_t stream) {
+    if (reverse)
+        return dtype == 1 ? launch_m<true, uint16_t>(mode, G, p, stream)
+                          : launch_m<true, float>(mode, G, p, stream);
+    return dtype == 1 ? launch_m<false, uint16_t>(mode, G, p, stream)
+                      : launch_m<false, float>(mode, G, p, stream);
+}
+
+hipError_t launch_carry(const CarryParams &p, hipStream_t stream) {
+    const int64_t total = p.batch * p.D * kN;
+    const int64_t grid = (total + 255) / 256;
+    hipLaunchKernelGGL(carry_kernel, dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace r2l

@@ -1,0 +1,175 @@
+// scan_plan.cpp -- planning (lanes per channel, chunking, workspace layout)
+// and the launch list of one entry-point call.
+#include "scan_plan.h"
+
+#include <algorithm>
+
+namespace r2l {
+namespace {
+
+// Lanes the planner aims for: 2048 wave64s, two per SIMD of the 256 CUs.
+constexpr int64_t kTargetLanes = 2048 * 64;
+// Longest chunk a state-only plan keeps, so that ragged prefixes of very
+// different lengths balance across the machine.
+constexpr int64_t kMaxStateChunk = 1024;
+
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+SegParams base_params(const r2l_scan_args *a, const Plan &pl) {
+    SegParams p{};
+    p.seqlen = is_ragged(a) ? 0 : a->seqlen;
+    p.cu_seqlens = a->cu_seqlens;
+    p.D = a->dim;
+    p.chunk_len = static_cast<int32_t>(pl.chunk_len);
+    p.nchunks = static_cast<int32_t>(pl.nchunks);
+    p.tiles = static_cast<int32_t>(pl.tiles);
+    p.nblocks = a->batch * pl.nchunks * pl.tiles;
+    p.x = a->x;   p.xs = a->x_stride;  p.xbs = eff_bstride(a, a->x_batch_stride, a->x_stride);
+    p.dt = a->dt; p.dts = a->dt_stride; p.dtbs = eff_bstride(a, a->dt_batch_stride, a->dt_stride);
+    p.Bm = a->Bm; p.Bs = a->Bm_stride;  p.Bbs = eff_bstride(a, a->Bm_batch_stride, a->Bm_stride);
+    p.Cm = a->Cm; p.Cs = a->Cm_stride;  p.Cbs = eff_bstride(a, a->Cm_batch_stride, a->Cm_stride);
+    p.A = a->A;
+    p.Dskip = a->Dskip;
+    p.softplus = a->delta_softplus;
+    p.res = a->res; p.rs = a->res_stride;
+    p.rbs = eff_bstride(a, a->res_batch_stride, a->res_stride);
+    p.s = a->s;
+    p.out = a->out; p.os = a->out_stride;
+    p.obs = eff_bstride(a, a->out_batch_stride, a->out_stride);
+    return p;
+}
+
+// What the readout writes: y, or the gated residual reading x itself (when
+// res is exactly x) or a separate residual tensor.
+int out_mode(const r2l_scan_args *a, const SegParams &p) {
+    if (!a->res) return kModeY;
+    if (a->res == a->x && a->res_stride == a->x_stride && p.rbs == p.xbs) return kModeResX;
+    return kModeRes;
+}
+
+}  // namespace
+
+Plan make_plan(Op op, const r2l_scan_args *a) {
+    Plan pl;
+    const int64_t channels = a->batch * a->dim;
+    const int64_t maxlen = max_len_of(a);
+    if (a->state_split) {
+        pl.G = a->state_split;
+    } else {
+        pl.G = 4;
+        for (int g : {1, 2, 4})
+            if (channels * g >= kTargetLanes) {
+                pl.G = g;
+                break;
+            }
+    }
+    const bool readout = wants_readout(op, a);
+    int64_t chunk = 0;
+    if (a->chunk_tokens > 0) {
+        chunk = a->chunk_tokens;
+    } else if (a->chunk_tokens == 0 && maxlen > 0) {
+        const int64_t lanes = std::max<int64_t>(channels * pl.G, 1);
+        if (!readout) {
+            // State-only scans chunk for free (the carry is one fma per chunk).
+            const int64_t want = std::max<int64_t>((kTargetLanes + lanes - 1) / lanes,
+                                                   (maxlen + kMaxStateChunk - 1) / kMaxStateChunk);
+            if (want > 1) chunk = std::max<int64_t>(32, (maxlen + want - 1) / want);
+        } else if (lanes * 4 < kTargetLanes && maxlen >= 1024) {
+            // Readout scans rescan every chunk once the carry is known (about
+            // 1.9x the vector work), so split only when the machine would
+            // otherwise be mostly idle.
+            const int64_t want = (kTargetLanes + lanes - 1) / lanes;
+            chunk = std::max<int64_t>(256, (maxlen + want - 1) / want);
+        }
+    }
+    if (chunk > 0 && chunk < maxlen) {
+        pl.chunked = true;
+        pl.chunk_len = chunk;
+        pl.nchunks = (maxlen + chunk - 1) / chunk;
+    } else {
+        pl.chunked = false;
+        pl.chunk_len = std::max<int64_t>(maxlen, 1);
+        pl.nchunks = 1;
+    }
+    pl.tiles = (a->dim * pl.G + kWG - 1) / kWG;
+    if (pl.chunked) {
+        const size_t q = static_cast<size_t>(a->batch) * pl.nchunks * a->dim * kN * 4;
+        const size_t s = static_cast<size_t>(a->batch) * pl.nchunks * a->dim * 4;
+        pl.off_S = align256(q);
+        pl.off_H = pl.off_S + align256(s);
+        pl.ws_bytes = pl.off_H + (readout ? align256(q) : 0);
+    }
+    return pl;
+}
+
+int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3]) {
+    if (a->batch == 0) return 0;
+    const bool reverse = (op == Op::Scan);
+    const bool readout = wants_readout(op, a);
+    const int64_t DN = a->dim * kN;
+    // block_commit_state reads the state it updates from h_out
+    const float *h_init = (op == Op::Commit) ? a->h_out : a->h_in;
+
+    auto seg = [&](const SegParams &p, int mode) {
+        Launch l{};
+        l.kind = Launch::Segment;
+        l.reverse = reverse;
+        l.dtype = a->dtype;
+        l.G = pl.G;
+        l.mode = mode;
+        l.seg = p;
+        return l;
+    };
+
+    if (!pl.chunked) {
+        if (tokens_of(a) == 0 && !a->h_out) return 0;
+        SegParams p = base_params(a, pl);
+        p.hin = h_init; p.hin_b = DN; p.hin_c = 0;
+        p.hfin = a->h_out; p.hfin_b = DN; p.hfin_c = 0;
+        out[0] = seg(p, readout ? out_mode(a, p) : kModeState);
+        return 1;
+    }
+
+    char *ws = static_cast<char *>(a->workspace);
+    float *Q = reinterpret_cast<float *>(ws);
+    float *S = reinterpret_cast<float *>(ws + pl.off_S);
+    float *H = readout ? reinterpret_cast<float *>(ws + pl.off_H) : nullptr;
+
+    // 1. every chunk from a zero state: local final state Q and Delta sum S
+    SegParams p1 = base_params(a, pl);
+    p1.hin = nullptr;
+    p1.hfin = Q; p1.hfin_b = pl.nchunks * DN; p1.hfin_c = DN;
+    p1.sdelta = S; p1.sd_b = pl.nchunks * a->dim; p1.sd_c = a->dim;
+    p1.res = nullptr;
+    p1.out = nullptr;
+    out[0] = seg(p1, kModeState);
+
+    // 2. chain the chunks: the state entering each chunk, and the final state
+    Launch c{};
+    c.kind = Launch::Carry;
+    c.reverse = reverse;
+    c.dtype = a->dtype;
+    c.carry.batch = a->batch;
+    c.carry.seqlen = is_ragged(a) ? 0 : a->seqlen;
+    c.carry.cu_seqlens = a->cu_seqlens;
+    c.carry.D = a->dim;
+    c.carry.chunk_len = static_cast<int32_t>(pl.chunk_len);
+    c.carry.nchunks = static_cast<int32_t>(pl.nchunks);
+    c.carry.A = a->A;
+    c.carry.hin = h_init;
+    c.carry.Q = Q;
+    c.carry.S = S;
+    c.carry.Hc = H;
+    c.carry.hout = a->h_out;
+    out[1] = c;
+    if (!readout) return 2;
+
+    // 3. readout: rescan every chunk from the state that enters it
+    SegParams p3 = base_params(a, pl);
+    p3.hin = H; p3.hin_b = pl.nchunks * DN; p3.hin_c = DN;
+    p3.hfin = nullptr;
+    out[2] = seg(p3, out_mode(a, p3));
+    return 3;
+}
+
+}  // namespace r2l

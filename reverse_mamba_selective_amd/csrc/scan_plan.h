@@ -1,0 +1,60 @@
+// scan_plan.h -- how one entry-point call becomes kernel launches. Used by the
+// entry points (r2l_api.cpp) and by the host-side access checker
+// (bounds_check.cpp), so both see the same launches with the same parameters.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "r2l_scan.h"
+#include "scan_internal.h"
+
+namespace r2l {
+
+enum class Op { Scan, Prefix, Commit };
+
+struct Plan {
+    int G = 1;               // lanes per channel
+    bool chunked = false;
+    int64_t chunk_len = 0;   // tokens per chunk (visiting order)
+    int64_t nchunks = 1;
+    int64_t tiles = 0;       // channel tiles per segment
+    size_t ws_bytes = 0;     // Q, S (+ H for readout plans), each 256-byte aligned
+    size_t off_S = 0, off_H = 0;
+};
+
+struct Launch {
+    enum Kind { Segment, Carry } kind;
+    bool reverse;
+    int dtype;
+    int G;
+    int mode;                // kMode* (segment launches)
+    SegParams seg;
+    CarryParams carry;
+};
+
+inline bool is_ragged(const r2l_scan_args *a) { return a->cu_seqlens != nullptr; }
+inline int64_t tokens_of(const r2l_scan_args *a) {
+    return is_ragged(a) ? a->total_tokens : a->batch * a->seqlen;
+}
+inline int64_t max_len_of(const r2l_scan_args *a) {
+    return is_ragged(a) ? a->max_seqlen : a->seqlen;
+}
+inline bool wants_readout(Op op, const r2l_scan_args *a) {
+    return op == Op::Scan || a->out != nullptr;
+}
+inline int64_t elem_size(int32_t dtype) { return dtype == R2L_DTYPE_BF16 ? 2 : 4; }
+
+// Batch stride actually used by a token-major tensor in the dense layout.
+inline int64_t eff_bstride(const r2l_scan_args *a, int64_t bstride, int64_t stride) {
+    if (is_ragged(a)) return 0;
+    return bstride ? bstride : a->seqlen * stride;
+}
+
+Plan make_plan(Op op, const r2l_scan_args *a);
+
+// The launches of a call, in order (at most 3). Arguments must have passed
+// the entry point's checks. Returns the count.
+int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3]);
+
+}  // namespace r2l

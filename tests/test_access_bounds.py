@@ -1,0 +1,184 @@
+"""Every memory access the kernels would make, replayed on the CPU.
+
+``r2l_check_access`` runs a call's argument checks, plan and launch list and
+walks the kernels' own index math (scan_geometry.h) over every block, lane,
+token and staging slot, with fake device addresses that are only compared,
+never dereferenced. Each case here must come back with every access inside
+the buffer its base pointer belongs to. This runs before any kernel change
+goes to a GPU.
+"""
+import random
+
+import numpy as np
+import pytest
+
+from reverse_mamba_selective_amd import _abi
+
+BASE = 0x7E0000000000
+OPS = {"scan": _abi.R2L_OP_SCAN, "prefix": _abi.R2L_OP_PREFIX, "commit": _abi.R2L_OP_COMMIT}
+
+
+class FakeHeap:
+    """Page-aligned fake allocations separated by guard gaps; size 0 gives NULL,
+    as torch does for an empty tensor."""
+
+    def __init__(self):
+        self.next = BASE
+
+    def alloc(self, nbytes):
+        if nbytes == 0:
+            return None
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 65536
+        return p
+
+
+def make_args(op, *, dtype="bf16", D=64, batch=None, seqlen=None, lengths=None, res="none",
+              h_in=False, h_out=False, out=True, chunk=-1, split=0, pad_row=0, pad_batch=0):
+    """A call with every buffer sized exactly as the layout says."""
+    es = 2 if dtype == "bf16" else 4
+    N = 16
+    heap = FakeHeap()
+    a = _abi.ScanArgs()
+    a.dim, a.dstate = D, N
+    a.dtype = _abi.R2L_DTYPE_BF16 if dtype == "bf16" else _abi.R2L_DTYPE_F32
+    a.delta_softplus = 1
+    a.chunk_tokens, a.state_split = chunk, split
+    cu = None
+    if lengths is not None:
+        lengths = list(lengths)
+        a.batch = len(lengths)
+        cu = [0] + list(np.cumsum(lengths))
+        a.total_tokens, a.max_seqlen = int(cu[-1]), max(lengths) if lengths else 0
+        a.cu_seqlens = heap.alloc(4 * (a.batch + 1))
+        tok = a.total_tokens
+
+        def tensor(cols):
+            stride = cols + pad_row
+            return heap.alloc(((tok - 1) * stride + cols) * es if tok else 0), stride, 0
+    else:
+        a.batch, a.seqlen = batch, seqlen
+        tok = batch * seqlen
+
+        def tensor(cols):
+            stride = cols + pad_row
+            bstride = seqlen * stride + pad_batch
+            ext = ((batch - 1) * bstride + (seqlen - 1) * stride + cols) if tok else 0
+            return heap.alloc(ext * es), stride, bstride if pad_batch else 0
+
+    a.x, a.x_stride, a.x_batch_stride = tensor(D)
+    a.dt, a.dt_stride, a.dt_batch_stride = tensor(D)
+    a.Bm, a.Bm_stride, a.Bm_batch_stride = tensor(N)
+    readout = op == "scan" or out
+    if readout:
+        a.Cm, a.Cm_stride, a.Cm_batch_stride = tensor(N)
+        a.out, a.out_stride, a.out_batch_stride = tensor(D)
+        a.Dskip = heap.alloc(4 * D)
+        if res == "x":
+            a.res, a.res_stride, a.res_batch_stride = a.x, a.x_stride, a.x_batch_stride
+        elif res == "sep":
+            a.res, a.res_stride, a.res_batch_stride = tensor(D)
+        elif res == "inplace":  # out is x is res
+            a.res, a.res_stride, a.res_batch_stride = a.x, a.x_stride, a.x_batch_stride
+            a.out, a.out_stride, a.out_batch_stride = a.x, a.x_stride, a.x_batch_stride
+        a.s = 0.05
+    a.A = heap.alloc(4 * D * N)
+    if h_in and op != "commit":
+        a.h_in = heap.alloc(4 * a.batch * D * N)
+    if h_out or op == "commit" or (op == "prefix" and (not out or tok == 0)):
+        a.h_out = heap.alloc(4 * a.batch * D * N)
+    need = _abi.workspace_size(OPS[op], a)
+    if need:
+        a.workspace, a.workspace_bytes = heap.alloc(need), need
+    return a, cu
+
+
+def check(op, **kw):
+    a, cu = make_args(op, **kw)
+    st, rep = _abi.check_access(OPS[op], a, cu)
+    msg = rep.message.decode() or _abi.last_error()
+    assert st == _abi.R2L_OK, "%s %s: %s" % (op, kw, msg)
+    return rep
+
+
+# ---- explicit edge cases -----------------------------------------------------
+EDGE = [
+    dict(lengths=[0, 0, 0], h_in=True, h_out=True),           # only empty sequences
+    dict(lengths=[5, 0, 1, 64, 17, 3, 0], h_out=True),
+    dict(lengths=[1]),
+    dict(lengths=[65, 64, 63, 128, 129]),
+    dict(batch=3, seqlen=0, h_in=True, h_out=True),           # dense, no token at all
+    dict(batch=1, seqlen=1),
+    dict(batch=2, seqlen=200, D=37),
+    dict(batch=2, seqlen=97, D=1),
+    dict(batch=4, seqlen=33, D=300, pad_row=8, pad_batch=40),  # padded rows and batches
+    dict(lengths=[700, 1, 0, 333, 64, 1025], D=96, chunk=100, h_in=True, h_out=True),
+    dict(lengths=[700, 1, 0, 333, 64, 1025], D=96, chunk=32, h_out=True),
+    dict(batch=2, seqlen=300, D=256, chunk=64, h_out=True),
+]
+
+
+@pytest.mark.parametrize("op", ["scan", "prefix", "commit"])
+@pytest.mark.parametrize("case", range(len(EDGE)))
+@pytest.mark.parametrize("split", [1, 2, 4])
+def test_edge_cases(op, case, split):
+    kw = dict(EDGE[case])
+    for res in (["none", "x", "sep", "inplace"] if op == "scan" else ["none"]):
+        check(op, split=split, res=res, **kw)
+    if op == "prefix":
+        check(op, split=split, out=False, **kw)
+        check(op, split=split, **{**kw, "out": True, "h_out": True})
+    if op == "commit":
+        check(op, split=split, out=False, **kw)
+
+
+def test_random_plans():
+    rng = random.Random(1234)
+    for _ in range(300):
+        op = rng.choice(["scan", "prefix", "commit"])
+        kw = dict(dtype=rng.choice(["bf16", "f32"]), D=rng.choice([1, 5, 64, 100, 256, 513]),
+                  split=rng.choice([0, 1, 2, 4]), chunk=rng.choice([-1, 0, 16, 33, 64, 200]),
+                  h_in=rng.random() < 0.5, h_out=rng.random() < 0.5,
+                  pad_row=rng.choice([0, 0, 2, 16]))
+        if rng.random() < 0.5:
+            kw["lengths"] = [rng.choice([0, 1, 2, 31, 64, 65, 130, 300]) for _ in range(rng.randint(1, 6))]
+        else:
+            kw.update(batch=rng.randint(1, 5), seqlen=rng.choice([0, 1, 8, 63, 64, 65, 257]),
+                      pad_batch=rng.choice([0, 0, 24]))
+        if op == "scan":
+            kw["res"] = rng.choice(["none", "x", "sep", "inplace"])
+        else:
+            kw["out"] = rng.random() < 0.4
+        check(op, **kw)
+
+
+# ---- the benchmarked shapes, at full size --------------------------------------
+# (chunk=0: the plan the library picks, as the benchmark runs it)
+def test_denoise_hook_shape():
+    rep = check("scan", batch=64, seqlen=32, D=2048, res="x", chunk=0)
+    assert rep.launches == 1 and rep.accesses > 0
+
+
+def test_prefill_shape():
+    rep = check("scan", batch=8, seqlen=4096, D=4096, chunk=0)
+    assert rep.accesses > 10**7
+
+
+def test_block_restricted_shapes():
+    rep = check("prefix", batch=8, seqlen=512, D=256, dtype="f32", out=False, chunk=0)
+    assert rep.launches == 2  # chunked: chunk pass + carry
+    check("scan", batch=8, seqlen=32, D=256, dtype="f32", res="x", chunk=0)
+    check("commit", batch=8, seqlen=32, D=256, dtype="f32", out=False, chunk=0)
+
+
+def test_ragged_serving_shapes():
+    import synth
+    lens = synth.ragged_block_lengths()
+    check("scan", lengths=lens, D=4096, chunk=0)
+    check("commit", lengths=lens, D=4096, out=False, chunk=0)
+
+
+def test_ragged_prefix_shape():
+    import synth
+    rep = check("prefix", lengths=synth.ragged_prefix_lengths(), D=4096, out=False, chunk=0)
+    assert rep.launches == 2 and rep.accesses > 10**8
