@@ -75,9 +75,9 @@ def kernel_sha() -> str:
 
 
 def load_traffic(workload: str):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
+    """HBM traffic per call from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    p = os.path.join(ROOT, "profiles", "segment_scan__%s__traffic.json" % workload)
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
@@ -95,8 +95,13 @@ class Workload:
     def setup(self, torch, r2l):
         raise NotImplementedError
 
-    def step(self, i, stream, events=None):
-        raise NotImplementedError
+    step_calls: list = []   # per rotating set: the entry-point calls of one step
+    measure: list = []      # per timed kernel: label, calls, bytes, alu, tc per launch
+    launches_per_step = 1
+
+    def step(self, i, stream):
+        for c in self.step_calls[i % len(self.step_calls)]:
+            c.launch(stream)
 
     def cpu_baseline(self, budget_s):
         raise NotImplementedError
@@ -137,7 +142,7 @@ class Denoise(Workload):
             base.append(g)
         set_bytes = self.bytes_per_launch * self.HOOKS
         self.R = _rotation(set_bytes)
-        self.calls = []
+        self.step_calls = []
         for r in range(self.R):
             row = []
             for h, g in enumerate(base):
@@ -146,24 +151,16 @@ class Denoise(Workload):
                 row.append(r2l.bind("r2l_scan", x=x, dt=g["dt"].clone(), Bm=g["Bm"].clone(),
                                     Cm=g["Cm"].clone(), A=g["A"], Dskip=g["Dskip"], res=x,
                                     s=float(self.gates[h]), out=out))
-            self.calls.append(row)
+            self.step_calls.append(row)
+        self.measure = [dict(label="r2l_scan (one hook)", calls=[c for row in self.step_calls
+                                                               for c in row],
+                             bytes=self.bytes_per_launch, alu=self.alu_per_launch,
+                             tc=self.tc_per_launch)]
         self.config = {"workload": self.name, "batch": self.B, "block_tokens": self.L,
                        "D": self.D, "N": 16, "hooks_per_step": self.HOOKS,
                        "in_dtype": "bf16", "state_dtype": "fp32", "res": "x",
                        "rotating_sets": self.R, "rotating_bytes": set_bytes * self.R,
                        "parallelism": "single_gpu"}
-
-    def step(self, i, stream, events=None):
-        row = self.calls[i % self.R]
-        if events is None:
-            for c in row:
-                c.launch(stream)
-        else:
-            for c in row:
-                e0, e1 = events.next()
-                e0.record()
-                c.launch(stream)
-                e1.record()
 
     def cpu_baseline(self, budget_s):
         import oracle
@@ -183,24 +180,20 @@ class Denoise(Workload):
                           "time" % (self.tc_per_step, reps, secs)}
 
 
-class Events:
-    """Pre-created HIP event pairs recorded around launches on the current stream."""
-
-    def __init__(self, torch, count):
-        self.torch = torch
-        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for _ in range(count)]
-        self.used = 0
-
-    def next(self):
-        e = self.pairs[self.used]
-        self.used += 1
-        return e
-
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        ts = [a.elapsed_time(b) for a, b in self.pairs[:self.used]]
-        return sum(ts) / len(ts), len(ts)
+def time_back_to_back(torch, calls, reps, per_ms):
+    """Average duration (ms) of `reps` launches queued back to back behind a
+    spinning kernel (so the host is far ahead of the GPU), from one pair of HIP
+    events recorded on the stream the launches run on."""
+    stream = torch.cuda.current_stream().cuda_stream
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(per_ms * (reps * 0.05 + 20.0)))
+    a.record()
+    for i in range(reps):
+        calls[i % len(calls)].launch(stream)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 def sleep_cycles_per_ms(torch):
@@ -279,21 +272,13 @@ class Prefill(Workload):
             self.calls.append(r2l.bind("r2l_scan", x=view(src["x"]), dt=view(src["dt"]),
                                        Bm=view(src["Bm"]), Cm=view(src["Cm"]), A=g["A"],
                                        Dskip=g["Dskip"], out=out))
+        self.step_calls = [[c] for c in self.calls]
+        self.measure = [dict(label="r2l_scan", calls=self.calls, bytes=self.bytes_per_launch,
+                             alu=self.alu_per_launch, tc=self.tc_per_launch)]
         self.config = {"workload": self.name, "batch": self.B, "seqlen": self.L, "D": self.D,
                        "N": 16, "in_dtype": "bf16", "state_dtype": "fp32", "res": None,
                        "rotating_sets": self.R, "parallelism": "single_gpu",
-                       "plan": {"state_split": self.calls[0].args.state_split,
-                                "workspace_bytes": int(self.calls[0].args.workspace_bytes)}}
-
-    def step(self, i, stream, events=None):
-        c = self.calls[i % self.R]
-        if events is None:
-            c.launch(stream)
-        else:
-            e0, e1 = events.next()
-            e0.record()
-            c.launch(stream)
-            e1.record()
+                       "plan": self.calls[0].plan()}
 
     def cpu_baseline(self, budget_s):
         import oracle
@@ -339,21 +324,17 @@ class RaggedServing(Workload):
             commit = r2l.bind("block_commit_state", state=state, x=gc["x"], dt=gc["dt"],
                               Bm=gc["Bm"], A=gc["A"], cu_seqlens=cu, max_seqlen=int(lens.max()))
             self.calls.append((scan, commit))
+        self.step_calls = [list(sc) for sc in self.calls]
+        self.measure = [
+            dict(label="r2l_scan (ragged blocks)", calls=[sc[0] for sc in self.calls],
+                 bytes=self.bytes_per_launch, alu=self.alu_per_launch, tc=self.tc_per_launch),
+            dict(label="block_commit_state (ragged blocks)", calls=[sc[1] for sc in self.calls],
+                 bytes=self.commit_bytes, alu=self.tc_per_launch * alu_ops_per_tc(False, False),
+                 tc=self.tc_per_launch)]
         self.config = {"workload": self.name, "batch": B, "tokens": tok, "D": self.D, "N": 16,
                        "block_len": "U{16..64}", "in_dtype": "bf16", "state_dtype": "fp32",
                        "ops": ["r2l_scan (out = y)", "block_commit_state (in place)"],
                        "rotating_sets": self.R, "parallelism": "single_gpu"}
-
-    def step(self, i, stream, events=None):
-        scan, commit = self.calls[i % self.R]
-        if events is None:
-            scan.launch(stream)
-        else:
-            e0, e1 = events.next()
-            e0.record()
-            scan.launch(stream)
-            e1.record()
-        commit.launch(stream)
 
     def cpu_baseline(self, budget_s):
         import oracle
@@ -389,13 +370,14 @@ class RaggedPrefix(Workload):
         g = self.g
         self.calls = [r2l.bind("prefix_scan_state", x=g["x"], dt=g["dt"], Bm=g["Bm"], A=g["A"],
                                h_out=h, cu_seqlens=cu, max_seqlen=int(lens.max()))]
+        self.step_calls = [self.calls]
+        self.measure = [dict(label="prefix_scan_state (ragged prefill)", calls=self.calls,
+                             bytes=self.bytes_per_launch, alu=self.alu_per_launch,
+                             tc=self.tc_per_launch)]
         self.config = {"workload": self.name, "batch": B, "tokens": tok, "D": self.D, "N": 16,
                        "prefix_len": "U{256..8192}", "in_dtype": "bf16", "state_dtype": "fp32",
                        "parallelism": "single_gpu",
-                       "plan": {"chunk_tokens": int(self.calls[0].args.chunk_tokens),
-                                "workspace_bytes": int(self.calls[0].args.workspace_bytes)}}
-
-    step = Prefill.step
+                       "plan": self.calls[0].plan()}
 
     def cpu_baseline(self, budget_s):
         import oracle
@@ -420,7 +402,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget of the CPU baseline (0: skip it)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run torch copies of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the scan is independent per (sequence, channel), "
               "so more GPUs only split the batch; run it with --gpus 1.", file=sys.stderr)
@@ -437,6 +431,7 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream().cuda_stream
+    wl.launches_per_step = len(wl.step_calls[0])
 
     # (1) eager: every step launched from the host loop
     for i in range(args.warmup):
@@ -469,30 +464,37 @@ def main():
         torch.cuda.synchronize()
         graph_s = (time.perf_counter() - t0) / args.steps
 
-    # (3) kernel duration: the same steps queued behind a spinning kernel, so
-    # that the host is far ahead of the GPU, with HIP events around every
-    # launch of the dominant kernel on the stream it runs on
-    ev = Events(torch, args.steps * wl.launches_per_step)
+    # (3) kernel durations: each timed entry point launched back to back
     per_ms = sleep_cycles_per_ms(torch)
-    host_est_ms = args.steps * wl.launches_per_step * 0.05 + 20.0
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(per_ms * host_est_ms))
-    for i in range(args.steps):
-        wl.step(i, stream, ev)
-    kern_ms, n_launch = ev.mean_ms()
+    timed = []
+    for m in wl.measure:
+        reps = max(len(m["calls"]), min(args.steps * wl.launches_per_step, 2000))
+        ms = time_back_to_back(torch, m["calls"], reps, per_ms)
+        timed.append(dict(m, ms=ms, reps=reps))
 
     step_s = min(eager_s, graph_s) if graph_s else eager_s
     value = wl.tc_per_step / step_s
-    kern_s = kern_ms * 1e-3
-    hbm_gbs = wl.bytes_per_launch / kern_s / 1e9
-    alu_t = wl.alu_per_launch / kern_s / 1e12
-    rl_hbm = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-              "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload)}
-    rl_alu = {"bound": "alu", "achieved": round(alu_t, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
-              "unit": "Tlane-op/s", "frac": round(alu_t / VALU_PEAK_TLANEOPS, 4),
-              "traffic": rl_hbm["traffic"]}
-    binding = rl_alu if rl_alu["frac"] >= rl_hbm["frac"] else rl_hbm
-    other = rl_hbm if binding is rl_alu else rl_alu
+
+    def rooflines(m):
+        kern_s = m["ms"] * 1e-3
+        hbm_gbs = m["bytes"] / kern_s / 1e9
+        alu_t = m["alu"] / kern_s / 1e12
+        hbm = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.name)}
+        alu = {"bound": "alu", "achieved": round(alu_t, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
+               "unit": "Tlane-op/s", "frac": round(alu_t / VALU_PEAK_TLANEOPS, 4),
+               "traffic": hbm["traffic"]}
+        return (alu, hbm) if alu["frac"] >= hbm["frac"] else (hbm, alu)
+
+    kernels = []
+    for m in timed:
+        bind_, other_ = rooflines(m)
+        kernels.append({"entry": m["label"], "avg_launch_us": round(m["ms"] * 1e3, 3),
+                        "launches_timed": m["reps"], "bytes_per_launch": m["bytes"],
+                        "tc_per_launch": m["tc"], "tc_per_s": m["tc"] / (m["ms"] * 1e-3),
+                        "roofline": bind_, "roofline_other": other_})
+    binding, other = kernels[0]["roofline"], kernels[0]["roofline_other"]
+    hbm_gbs = (binding if binding["bound"] == "hbm" else other)["achieved"]
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -514,13 +516,13 @@ def main():
         "config": wl.config,
         "roofline": binding,
         "roofline_other": other,
-        "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_gbs": hbm_gbs,
         "hbm_frac_of_8TBs": round(hbm_gbs / HBM_PEAK_GBS, 4),
-        "kernel": {"name": "segment_scan_kernel", "avg_launch_us": round(kern_s * 1e6, 3),
-                   "launches_timed": n_launch, "bytes_per_launch": wl.bytes_per_launch,
-                   "tc_per_launch": wl.tc_per_launch,
-                   "alu_lane_ops_per_tc": alu_ops_per_tc(True, True),
-                   "trans_slots": TRANS_SLOTS, "source_sha": kernel_sha()},
+        "kernels": kernels,
+        "alu_model": {"lane_ops_per_tc_readout_res": alu_ops_per_tc(True, True),
+                      "lane_ops_per_tc_state_only": alu_ops_per_tc(False, False),
+                      "trans_slots": TRANS_SLOTS},
+        "source_sha": kernel_sha(),
         "ms_per_step_eager": eager_s * 1e3,
         "ms_per_step_graph": graph_s * 1e3 if graph_s else None,
         "cpu_baseline": cpu,

@@ -33,6 +33,22 @@ typedef struct r2l_access_report {
 R2L_API r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *cu_seqlens_host,
                             r2l_access_report *report);
 
+typedef struct r2l_plan_info {
+    int32_t lanes_per_channel; /* 1, 2 or 4 */
+    int32_t chunked;           /* 1: chunk pass + carry (+ readout pass) */
+    int64_t chunk_tokens;      /* tokens per chunk (the longest sequence when not chunked) */
+    int64_t chunks;            /* chunks per sequence in the grid */
+    int64_t workspace_bytes;
+    int32_t launches;          /* kernel launches the call makes */
+} r2l_plan_info;
+
+/*
+ * r2l_describe_plan -- the plan the library picks for call `op` with these
+ * arguments (only the shape fields and planning hints are read). For
+ * benchmark reports and tests. Returns R2L_OK or a shape-check status.
+ */
+R2L_API r2l_status r2l_describe_plan(int32_t op, const r2l_scan_args *a, r2l_plan_info *info);
+
 #ifdef __cplusplus
 }
 #endif

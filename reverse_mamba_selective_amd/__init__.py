@@ -150,6 +150,11 @@ class BoundCall:
         self._fn = getattr(_abi.load(), func)
         self._ref = _abi.ctypes.byref(args)
 
+    def plan(self) -> dict:
+        """The plan the library picks for this call (lanes per channel, chunking,
+        workspace bytes, launches)."""
+        return _abi.describe_plan(self.op, self.args)
+
     def launch(self, stream=None):
         """Queue the call on ``stream`` (a raw hipStream_t handle) or, when None,
         on torch's current stream of the device."""

@@ -29,7 +29,8 @@ R2L_OP_COMMIT = 2
 ABI_VERSION = 1
 
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
-           "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access")
+           "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
+           "r2l_describe_plan")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -57,6 +58,12 @@ class ScanArgs(ctypes.Structure):
 class AccessReport(ctypes.Structure):
     """Mirror of ``r2l_access_report`` (include/r2l_scan_debug.h)."""
     _fields_ = [("launches", _i64), ("accesses", _i64), ("message", ctypes.c_char * 512)]
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``r2l_plan_info`` (include/r2l_scan_debug.h)."""
+    _fields_ = [("lanes_per_channel", _i32), ("chunked", _i32), ("chunk_tokens", _i64),
+                ("chunks", _i64), ("workspace_bytes", _i64), ("launches", _i32)]
 
 
 class R2LError(RuntimeError):
@@ -91,6 +98,8 @@ def load(path: str = LIB_PATH):
     lib.r2l_last_error.argtypes = []
     lib.r2l_abi_version.restype = _i32
     lib.r2l_abi_version.argtypes = []
+    lib.r2l_describe_plan.restype = _i32
+    lib.r2l_describe_plan.argtypes = [_i32, ptr, ctypes.POINTER(PlanInfo)]
     lib.r2l_check_access.restype = _i32
     lib.r2l_check_access.argtypes = [_i32, ptr, ctypes.POINTER(_i32), ctypes.POINTER(AccessReport)]
     if lib.r2l_abi_version() != ABI_VERSION:
@@ -138,3 +147,12 @@ def check_access(op: int, args: ScanArgs, cu_seqlens_host=None):
         cu = ctypes.cast(arr, ctypes.POINTER(_i32))
     st = lib.r2l_check_access(op, ctypes.byref(args), cu, ctypes.byref(rep))
     return st, rep
+
+
+def describe_plan(op: int, args: ScanArgs) -> dict:
+    """The plan the library picks for this call (see r2l_describe_plan)."""
+    info = PlanInfo()
+    st = load().r2l_describe_plan(op, ctypes.byref(args), ctypes.byref(info))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_describe_plan", last_error())
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_}

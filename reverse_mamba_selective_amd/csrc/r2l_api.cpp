@@ -324,6 +324,23 @@ r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *c
     return ok();
 }
 
+r2l_status r2l_describe_plan(int32_t op, const r2l_scan_args *a, r2l_plan_info *info) {
+    if (!info) return fail(R2L_ERR_INVALID_ARG, "info is NULL");
+    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT)
+        return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    const Op o = op == R2L_OP_SCAN ? Op::Scan : (op == R2L_OP_PREFIX ? Op::Prefix : Op::Commit);
+    const Plan pl = r2l::make_plan(o, a);
+    info->lanes_per_channel = pl.G;
+    info->chunked = pl.chunked ? 1 : 0;
+    info->chunk_tokens = pl.chunk_len;
+    info->chunks = pl.nchunks;
+    info->workspace_bytes = static_cast<int64_t>(pl.ws_bytes);
+    info->launches = a->batch == 0 ? 0 : (pl.chunked ? (wants_readout(o, a) ? 3 : 2) : 1);
+    return ok();
+}
+
 const char *r2l_status_string(r2l_status s) {
     switch (s) {
         case R2L_OK: return "ok";

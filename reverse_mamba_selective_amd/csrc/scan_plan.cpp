@@ -7,11 +7,23 @@
 namespace r2l {
 namespace {
 
-// Lanes the planner aims for: 2048 wave64s, two per SIMD of the 256 CUs.
-constexpr int64_t kTargetLanes = 2048 * 64;
+// Measured on MI355X (bf16, N = 16): one lane per channel runs the token loop
+// at ~90% of the VALU issue rate once a few waves share each SIMD, while
+// splitting a channel's states over 2 or 4 lanes costs more instructions per
+// token (softplus repeated, a cross-lane sum) than its extra waves win back.
+// So the planner keeps one lane per channel and, when a shape has too few
+// channels to fill the machine, cuts sequences into chunks instead:
+//  * state-only scans chunk for free (the carry is one fma per chunk);
+//  * readout scans pay a second, state-only pass over each chunk (about 1.8x
+//    the vector work) and still come out ahead below ~4096 waves (e.g. 8 x
+//    4096 x 4096: 0.90 ms chunked vs 1.01 ms with 4 lanes per channel and
+//    1.64 ms with one wave per channel tile and no chunking).
+constexpr int64_t kTargetLanes = 4096 * 64;
 // Longest chunk a state-only plan keeps, so that ragged prefixes of very
 // different lengths balance across the machine.
 constexpr int64_t kMaxStateChunk = 1024;
+// Shortest chunk worth a carry pass.
+constexpr int64_t kMinChunk = 256;
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -53,34 +65,18 @@ Plan make_plan(Op op, const r2l_scan_args *a) {
     Plan pl;
     const int64_t channels = a->batch * a->dim;
     const int64_t maxlen = max_len_of(a);
-    if (a->state_split) {
-        pl.G = a->state_split;
-    } else {
-        pl.G = 4;
-        for (int g : {1, 2, 4})
-            if (channels * g >= kTargetLanes) {
-                pl.G = g;
-                break;
-            }
-    }
+    pl.G = a->state_split ? a->state_split : 1;
     const bool readout = wants_readout(op, a);
     int64_t chunk = 0;
     if (a->chunk_tokens > 0) {
         chunk = a->chunk_tokens;
     } else if (a->chunk_tokens == 0 && maxlen > 0) {
         const int64_t lanes = std::max<int64_t>(channels * pl.G, 1);
-        if (!readout) {
-            // State-only scans chunk for free (the carry is one fma per chunk).
-            const int64_t want = std::max<int64_t>((kTargetLanes + lanes - 1) / lanes,
-                                                   (maxlen + kMaxStateChunk - 1) / kMaxStateChunk);
-            if (want > 1) chunk = std::max<int64_t>(32, (maxlen + want - 1) / want);
-        } else if (lanes * 4 < kTargetLanes && maxlen >= 1024) {
-            // Readout scans rescan every chunk once the carry is known (about
-            // 1.9x the vector work), so split only when the machine would
-            // otherwise be mostly idle.
-            const int64_t want = (kTargetLanes + lanes - 1) / lanes;
-            chunk = std::max<int64_t>(256, (maxlen + want - 1) / want);
-        }
+        const int64_t fill = (kTargetLanes + lanes - 1) / lanes;  // chunks to fill the machine
+        const int64_t want = readout ? fill
+                                     : std::max<int64_t>(fill, (maxlen + kMaxStateChunk - 1) /
+                                                                   kMaxStateChunk);
+        if (want > 1) chunk = std::max<int64_t>(kMinChunk, (maxlen + want - 1) / want);
     }
     if (chunk > 0 && chunk < maxlen) {
         pl.chunked = true;
