@@ -165,9 +165,10 @@ void check_carry(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const Region *rA = ck.region_of(p.A), *rQ = ck.region_of(p.Q), *rS = ck.region_of(p.S);
     const Region *rH = p.Hc ? ck.region_of(p.Hc) : nullptr, *rin = p.hin ? ck.region_of(p.hin) : nullptr;
     const Region *rout = p.hout ? ck.region_of(p.hout) : nullptr;
-    const int64_t total = p.batch * p.D * kN, grid = (total + 255) / 256 * 256;
-    for (int64_t i = 0; i < grid && ck.ok(); ++i) {
-        const CarryGeom g = carry_geom(p.batch, p.D, i);
+    for (int64_t i = 0; i < p.batch * carry_tiles(p.D) * kCarryThreads && ck.ok(); ++i) {
+        const int64_t bx = i / (carry_tiles(p.D) * kCarryThreads);
+        const int64_t rem = i % (carry_tiles(p.D) * kCarryThreads);
+        const CarryGeom g = carry_geom(p.D, bx, rem / kCarryThreads, static_cast<int>(rem % kCarryThreads));
         if (!g.valid) continue;
         const int64_t len = p.cu_seqlens ? static_cast<int64_t>(cu_host[g.b + 1]) - cu_host[g.b] : p.seqlen;
         const int nc = carry_chunks(len, p.chunk_len, p.nchunks);

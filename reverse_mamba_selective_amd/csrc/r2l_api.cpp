@@ -52,7 +52,8 @@ r2l_status check_shape(const r2l_scan_args *a) {
     if (!a) return fail(R2L_ERR_INVALID_ARG, "args is NULL");
     if (a->batch < 0) return fail(R2L_ERR_INVALID_ARG, "batch < 0");
     if (a->dim < 1) return fail(R2L_ERR_INVALID_ARG, "dim < 1");
-    if (a->dim > (int64_t(1) << 31) / 4) return fail(R2L_ERR_UNSUPPORTED, "dim too large");
+    if (a->dim > 65535 * 16) return fail(R2L_ERR_UNSUPPORTED, "dim above 1048560");
+    if (a->batch > INT32_MAX) return fail(R2L_ERR_UNSUPPORTED, "batch above 2^31-1");
     if (a->dstate != r2l::kN)
         return fail(R2L_ERR_UNSUPPORTED, "dstate %d is not built (only %d)", a->dstate, r2l::kN);
     if (a->dtype != R2L_DTYPE_F32 && a->dtype != R2L_DTYPE_BF16)

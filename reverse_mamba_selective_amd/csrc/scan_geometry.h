@@ -17,6 +17,7 @@
 namespace r2l {
 
 constexpr int kPrefetch = 8;   // tokens of x/dt/res loaded ahead of use
+static_assert(kN == 16, "carry_geom splits (channel, state) with a 4-bit shift");
 
 // Block -> (sequence b, chunk c, channel tile). Launches pad the grid to a
 // multiple of 8 and remap ids so that consecutive logical blocks (the tiles of
@@ -30,16 +31,20 @@ struct BlockGeom {
 
 R2L_HD int64_t padded_grid(int64_t nblocks) { return ((nblocks + 7) / 8) * 8; }
 
+// 32-bit arithmetic: the host keeps the padded grid below 2^31 blocks.
 R2L_HD BlockGeom block_geom(int64_t nblocks, int32_t tiles, int32_t nchunks, int64_t bid) {
     BlockGeom g{false, 0, 0, 0};
-    const int64_t per = (nblocks + 7) >> 3;
-    const int64_t logical = (bid & 7) * per + (bid >> 3);
-    if (logical >= nblocks) return g;
+    const uint32_t nb = static_cast<uint32_t>(nblocks);
+    const uint32_t id = static_cast<uint32_t>(bid);
+    const uint32_t per = (nb + 7) >> 3;
+    const uint32_t logical = (id & 7) * per + (id >> 3);
+    if (logical >= nb) return g;
     g.valid = true;
-    g.tile = static_cast<int>(logical % tiles);
-    const int64_t seg = logical / tiles;
-    g.c = static_cast<int>(seg % nchunks);
-    g.b = seg / nchunks;
+    const uint32_t t = static_cast<uint32_t>(tiles), nc = static_cast<uint32_t>(nchunks);
+    g.tile = static_cast<int>(logical % t);
+    const uint32_t seg = logical / t;
+    g.c = static_cast<int>(seg % nc);
+    g.b = static_cast<int64_t>(seg / nc);
     return g;
 }
 
@@ -123,20 +128,26 @@ R2L_HD uint32_t seq_span_bytes(int64_t len, int64_t row_elems, int64_t D, int64_
     return static_cast<uint32_t>((rows * row_elems + D) * es);
 }
 
-// Carry kernel: thread i -> (b, d, n); chunks of sequence b actually present.
+// Carry kernel: a 2-D grid, x = sequence b, y = tile of kCarryThreads
+// (channel, state) pairs; thread t of tile y covers channel (y*kCarryThreads +
+// t) / kN and state t % kN. No division.
+constexpr int kCarryThreads = 256;
 struct CarryGeom {
     bool valid;
     int n;
     int64_t d, b;
 };
 
-R2L_HD CarryGeom carry_geom(int64_t batch, int64_t D, int64_t i) {
+R2L_HD int64_t carry_tiles(int64_t D) { return (D * kN + kCarryThreads - 1) / kCarryThreads; }
+
+R2L_HD CarryGeom carry_geom(int64_t D, int64_t bx, int64_t by, int tid) {
     CarryGeom g{false, 0, 0, 0};
-    if (i >= batch * D * kN) return g;
+    const int64_t i = by * kCarryThreads + tid;
+    if (i >= D * kN) return g;
     g.valid = true;
-    g.n = static_cast<int>(i % kN);
-    g.d = (i / kN) % D;
-    g.b = i / (kN * D);
+    g.n = static_cast<int>(i & (kN - 1));
+    g.d = i >> 4;
+    g.b = bx;
     return g;
 }
 

@@ -107,12 +107,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              static_cast<int>(bytes), 0x00020000);
 }
 
-// log(1 + e^v) = max(v, 0) + log(1 + e^-|v|), with base-2 hardware ops;
-// max(v, 0) is the median of (v, 0, +inf), one instruction.
+// log(1 + e^v) = max(v, 0) + log(1 + e^-|v|), with base-2 hardware ops.
+// max(v, 0) is taken as a signed-integer max of the bit patterns (one
+// instruction; a float max would add a canonicalising one): positive floats
+// order like their bits, every negative one has a negative pattern.
 __device__ __forceinline__ float softplus(float v) {
     const float e = __builtin_amdgcn_exp2f(-fabsf(v) * kLog2e);
     const float l = __builtin_amdgcn_logf(1.0f + e);
-    return fmaf(l, kLn2, __builtin_amdgcn_fmed3f(v, 0.0f, __builtin_inff()));
+    return fmaf(l, kLn2, __int_as_float(max(__float_as_int(v), 0)));
 }
 
 // Sum of y over the G lanes (adjacent, same quad) that share a channel.
@@ -213,12 +215,6 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
         dq[slot] = E::bload(rd, doff, row * drb);
         if constexpr (MODE == kModeRes) rq[slot] = E::bload(rr_, doff, row * rrb);
     };
-#pragma unroll
-    for (int j = 0; j < PF; ++j) rq[j] = 0;
-    if (ntok > 0) {
-#pragma unroll
-        for (int j = 0; j < PF; ++j) load_pos(prefetch_pos(j, ntok), j);
-    }
 
     // ---- Bm/Cm staging of one tile of kTile tokens
     R stg[STAGE];
@@ -252,15 +248,22 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
         if constexpr (!READOUT) dsum += delta;
         const float dx = delta * xv;
         const float *row = bcrow + sub * NS;
-        float y = 0.0f;
+        // the readout sums even and odd states separately: two short
+        // dependency chains instead of one of NS fmas
+        float y0 = 0.0f, y1 = 0.0f;
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const float abar = __builtin_amdgcn_exp2f(delta * a2[n]);
             h[n] = fmaf(abar, h[n], row[n] * dx);
-            if constexpr (READOUT) y = fmaf(row[kN + n], h[n], y);
+            if constexpr (READOUT) {
+                if (n & 1)
+                    y1 = fmaf(row[kN + n], h[n], y1);
+                else
+                    y0 = fmaf(row[kN + n], h[n], y0);
+            }
         }
         if constexpr (READOUT) {
-            y = group_sum<G>(y);
+            float y = group_sum<G>(y0 + y1);
             y = fmaf(dskip, xv, y);
             // Every lane stores: the G lanes of a channel, and idle lanes
             // shadowing the last channel, hold bit-identical values for the
@@ -278,10 +281,16 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
         }
     };
 
+    // Start-up: the first tile's Bm/Cm rows are requested first (they gate
+    // the barrier), then the first PF tokens of x/dt/res.
     const int ntiles = (ntok + kTile - 1) / kTile;
+    const int cnt0 = ntok < kTile ? ntok : kTile;
+    if (ntok > 0) stage_load(0, cnt0);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) rq[j] = 0;
     if (ntok > 0) {
-        const int cnt0 = ntok < kTile ? ntok : kTile;
-        stage_load(0, cnt0);
+#pragma unroll
+        for (int j = 0; j < PF; ++j) load_pos(prefetch_pos(j, ntok), j);
         stage_store(0, cnt0);
     }
     __syncthreads();
@@ -318,8 +327,8 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
 // ---- the carry over chunks -------------------------------------------------
 // One lane per (sequence, channel, state); the chunk loop is short and its
 // loads do not depend on the carried value, so they pipeline.
-__global__ __launch_bounds__(256) void carry_kernel(const CarryParams p) {
-    const CarryGeom g = carry_geom(p.batch, p.D, static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+__global__ __launch_bounds__(kCarryThreads) void carry_kernel(const CarryParams p) {
+    const CarryGeom g = carry_geom(p.D, blockIdx.x, blockIdx.y, threadIdx.x);
     if (!g.valid) return;
     const int64_t len = p.cu_seqlens
         ? static_cast<int64_t>(p.cu_seqlens[g.b + 1]) - p.cu_seqlens[g.b] : p.seqlen;
@@ -380,9 +389,8 @@ hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode, const S
 }
 
 hipError_t launch_carry(const CarryParams &p, hipStream_t stream) {
-    const int64_t total = p.batch * p.D * kN;
-    const int64_t grid = (total + 255) / 256;
-    hipLaunchKernelGGL(carry_kernel, dim3(grid), dim3(256), 0, stream, p);
+    const dim3 grid(static_cast<uint32_t>(p.batch), static_cast<uint32_t>(carry_tiles(p.D)));
+    hipLaunchKernelGGL(carry_kernel, grid, dim3(kCarryThreads), 0, stream, p);
     return hipGetLastError();
 }
 
