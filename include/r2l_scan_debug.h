@@ -14,6 +14,8 @@ extern "C" {
 typedef struct r2l_access_report {
     int64_t launches;   /* kernel launches replayed */
     int64_t accesses;   /* memory accesses checked */
+    int64_t vector_staging; /* segment launches that stage Bm/Cm with vector loads
+                               (every row start aligned for them) */
     char message[512];  /* the first out-of-bounds access, or "" */
 } r2l_access_report;
 

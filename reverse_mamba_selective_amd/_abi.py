@@ -57,7 +57,8 @@ class ScanArgs(ctypes.Structure):
 
 class AccessReport(ctypes.Structure):
     """Mirror of ``r2l_access_report`` (include/r2l_scan_debug.h)."""
-    _fields_ = [("launches", _i64), ("accesses", _i64), ("message", ctypes.c_char * 512)]
+    _fields_ = [("launches", _i64), ("accesses", _i64), ("vector_staging", _i64),
+                ("message", ctypes.c_char * 512)]
 
 
 class PlanInfo(ctypes.Structure):

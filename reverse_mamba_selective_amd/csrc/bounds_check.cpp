@@ -141,21 +141,31 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
             if (readout) row_access("out", rO, p.out, sq.oo, p.os, k);
         }
 
-        // Bm/Cm staging, tile by tile
+        // Bm/Cm staging, tile by tile: per thread one run of STAGE elements
+        // at lane offset row * row_bytes + col0 * es of its matrix's resource
+        const int al = stage_align(NBC, static_cast<int>(es));
         for (int base = 0; base < ntok && ck.ok(); base += kTile) {
             const int cnt = ntok - base < kTile ? ntok - base : kTile;
-            for (int lane = 0; lane < kWG; ++lane)
-                for (int i = 0; i < STAGE; ++i) {
-                    const int k = stage_token(i, lane, NBC), col = stage_col(i, lane, NBC);
-                    if (i * kWG + lane >= kTile * NBC) ck.fail("LDS slot past the tile");
-                    if (k >= cnt) continue;
-                    const int64_t row = seg_row(sg, base + k);
-                    if (row < 0 || row >= sq.len) ck.fail("staging row %lld outside the sequence", (long long)row);
-                    if (col < kN)
-                        ck.access("Bm", rB, U(p.Bm) + (sq.Bo + row * p.Bs + col) * es, es);
-                    else
-                        ck.access("Cm", rC, U(p.Cm) + (sq.Co + row * p.Cs + col - kN) * es, es);
-                }
+            for (int lane = 0; lane < kWG && ck.ok(); ++lane) {
+                const StageSlot ss = stage_slot(lane, NBC);
+                if (ss.mat > (readout ? 1 : 0) || ss.k >= kTile || ss.col0 + STAGE > kN)
+                    return ck.fail("staging slot of thread %d outside the tile", lane);
+                if (ss.mat != stage_slot(lane & ~63, NBC).mat)
+                    return ck.fail("staging matrix not uniform in the wave of thread %d", lane);
+                const int64_t row = seg_row(sg, base + stage_pos(ss.k, cnt));
+                if (row < 0 || row >= sq.len)
+                    return ck.fail("staging row %lld outside the sequence", (long long)row);
+                const bool isC = ss.mat != 0;
+                const int64_t st = isC ? p.Cs : p.Bs;
+                const uint64_t voff = static_cast<uint64_t>(row * st + ss.col0) * es;
+                if (voff + STAGE * es > seq_span_bytes(sq.len, st, kN, es))
+                    return ck.fail("staging run beyond the buffer resource (block %lld)", (long long)bid);
+                const uintptr_t addr = U(isC ? p.Cm : p.Bm) + (isC ? sq.Co : sq.Bo) * es + voff;
+                if (p.bc_vec && addr % al)
+                    return ck.fail("staging vector load at 0x%llx not %d-byte aligned",
+                                   (unsigned long long)addr, al);
+                ck.access(isC ? "Cm" : "Bm", isC ? rC : rB, addr, STAGE * es);
+            }
         }
     }
 }
@@ -223,8 +233,10 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
     const int n = build_launches(op, a, pl, ls);
     for (int i = 0; i < n && ck.ok(); ++i) {
         ++rep->launches;
-        if (ls[i].kind == Launch::Segment)
+        if (ls[i].kind == Launch::Segment) {
+            if (ls[i].seg.bc_vec) ++rep->vector_staging;
             check_segment(ck, ls[i], cu_host);
+        }
         else
             check_carry(ck, ls[i], cu_host);
     }

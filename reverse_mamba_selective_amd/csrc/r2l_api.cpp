@@ -145,10 +145,11 @@ r2l_status check_buffers(Op op, const r2l_scan_args *a, const Plan &pl) {
             return fail(R2L_ERR_ALIAS, "out: sequences overlap (batch stride < seqlen * stride)");
         // The kernels address the rows of one sequence with 32-bit byte offsets.
         const int64_t L = max_len_of(a);
-        const int64_t strides[] = {a->x_stride, a->dt_stride, a->res ? a->res_stride : 0,
-                                   readout ? a->out_stride : 0};
-        for (int64_t st : strides)
-            if (L > 0 && st > 0 && ((L - 1) * st + D) * es > (int64_t)UINT32_MAX)
+        const struct { int64_t st, cols; } rows[] = {
+            {a->x_stride, D}, {a->dt_stride, D}, {a->res ? a->res_stride : 0, D},
+            {readout ? a->out_stride : 0, D}, {a->Bm_stride, N}, {readout ? a->Cm_stride : 0, N}};
+        for (const auto &r : rows)
+            if (L > 0 && r.st > 0 && ((L - 1) * r.st + r.cols) * es > (int64_t)UINT32_MAX)
                 return fail(R2L_ERR_UNSUPPORTED, "one sequence spans more than 4 GiB of a tensor");
     }
     if (a->batch > 0 && !a->A) return fail(R2L_ERR_INVALID_ARG, "A is NULL");

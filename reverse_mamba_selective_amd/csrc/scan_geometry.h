@@ -116,11 +116,35 @@ R2L_HD LaneGeom lane_geom(int tile, int lane, int G, int64_t D) {
     return g;
 }
 
-// Bm/Cm staging of one tile: thread `lane`, element i covers LDS slot
-// q = i*kWG + lane = k*NBC + col, i.e. token k of the tile, column col
-// (col < kN: Bm[.., col]; else Cm[.., col - kN]).
-R2L_HD int stage_token(int i, int lane, int nbc) { return (i * kWG + lane) / nbc; }
-R2L_HD int stage_col(int i, int lane, int nbc) { return (i * kWG + lane) % nbc; }
+// Bm/Cm staging of one tile of kTile tokens, nbc staged columns per token (kN
+// of Bm, then kN of Cm when the readout needs them). Thread tid fills
+// stage_cols(nbc) consecutive columns, from col0 on, of matrix `mat` (0: Bm,
+// 1: Cm) for tile token k: LDS floats k*nbc + mat*kN + col0 ... Threads
+// 0..127 take Bm and 128..255 Cm (readout), so the matrix is uniform per wave.
+struct StageSlot {
+    int mat, k, col0;
+};
+
+R2L_HD constexpr int stage_cols(int nbc) { return kTile * nbc / kWG; }
+
+R2L_HD StageSlot stage_slot(int tid, int nbc) {
+    const int cols = stage_cols(nbc);
+    const int per_row = kN / cols;             // threads per matrix row
+    const int per_mat = kTile * per_row;
+    const int r = tid % per_mat;
+    return StageSlot{tid / per_mat, r / per_row, (r % per_row) * cols};
+}
+
+// Byte alignment that lets a thread fetch its columns with one or two
+// vector loads (8 or 16 bytes each).
+R2L_HD constexpr int stage_align(int nbc, int es) {
+    return stage_cols(nbc) * es < 16 ? stage_cols(nbc) * es : 16;
+}
+
+// The tile token whose row a thread loads for slot token k: slots past the
+// tile's last token (a short last tile) repeat that token's row, so every
+// thread loads and stores without a branch; those slots are never read.
+R2L_HD int stage_pos(int k, int tcnt) { return k < tcnt ? k : tcnt - 1; }
 
 // Bytes a raw buffer resource over one sequence of a tensor covers.
 R2L_HD uint32_t seq_span_bytes(int64_t len, int64_t row_elems, int64_t D, int64_t es) {

@@ -35,6 +35,8 @@ struct SegParams {
     const void *dt; int64_t dts, dtbs;
     const void *Bm; int64_t Bs, Bbs;
     const void *Cm; int64_t Cs, Cbs;
+    // every Bm/Cm row start is aligned for the staging's vector loads
+    int32_t bc_vec;
     const float *A;
     const float *Dskip;
     int32_t softplus;

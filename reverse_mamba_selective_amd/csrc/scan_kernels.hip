@@ -69,6 +69,17 @@ struct Elem<float> {
                                                   uint32_t soff) {
         __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
     }
+    // element j of a run of staged elements held as 32-bit words
+    static __device__ __forceinline__ float word_elem(const uint32_t *w, int j) {
+        return __uint_as_float(w[j]);
+    }
+    // the run of NE elements at voff, one buffer load per element
+    template <int NE>
+    static __device__ __forceinline__ void bload_elems(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                       uint32_t *w) {
+#pragma unroll
+        for (int j = 0; j < NE; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * j, 0, 0);
+    }
 };
 
 // bf16 is carried as its 16 raw bits.
@@ -97,7 +108,43 @@ struct Elem<uint16_t> {
                                                   uint32_t soff) {
         __builtin_amdgcn_raw_buffer_store_b16(v, r, voff, soff, 0);
     }
+    // element j of a run held as words: two bf16 per word, the first in the
+    // low half (little-endian)
+    static __device__ __forceinline__ float word_elem(const uint32_t *w, int j) {
+        return __uint_as_float((j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16));
+    }
+    template <int NE>
+    static __device__ __forceinline__ void bload_elems(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                       uint32_t *w) {
+#pragma unroll
+        for (int j = 0; j < NE; j += 2) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2 * j, 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2 * j + 2, 0, 0);
+            w[j >> 1] = lo | (hi << 16);
+        }
+    }
 };
+
+// NW words at voff with 8- or 16-byte loads (voff and the resource base
+// aligned to the load width).
+template <int NW>
+__device__ __forceinline__ void bload_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t *w) {
+    static_assert(NW == 2 || NW % 4 == 0, "staging run width");
+    if constexpr (NW == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+        w[0] = v[0];
+        w[1] = v[1];
+    } else {
+#pragma unroll
+        for (int q = 0; q < NW / 4; ++q) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * q, 0, 0);
+            w[4 * q] = v[0];
+            w[4 * q + 1] = v[1];
+            w[4 * q + 2] = v[2];
+            w[4 * q + 3] = v[3];
+        }
+    }
+}
 
 // Raw buffer resource over [base, base + bytes) (word 3: the gfx9 raw-buffer
 // format). Its bound applies to the per-lane offset only; the scalar offset
@@ -148,10 +195,12 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     constexpr bool READOUT = MODE != kModeState;
     constexpr int NS = kN / G;                   // states per lane
     constexpr int NBC = READOUT ? 2 * kN : kN;   // staged floats per token (B, then C)
-    constexpr int STAGE = kTile * NBC / kWG;     // staged elements per thread per tile
+    constexpr int STAGE = stage_cols(NBC);       // staged elements per thread per tile
+    constexpr int SW = STAGE * static_cast<int>(sizeof(T)) / 4;   // ... as 32-bit words
     constexpr int PF = kPrefetch;
-    static_assert(kTile * NBC % kWG == 0 && kTile % PF == 0, "tile shape");
-    __shared__ float lds_bc[2][kTile * NBC];
+    static_assert(kTile * NBC == STAGE * kWG && kN % STAGE == 0 && STAGE % 4 == 0 &&
+                  kTile % PF == 0, "tile shape");
+    __shared__ __align__(16) float lds_bc[2][kTile * NBC];
     using E = Elem<T>;
     using R = typename E::raw_t;
 
@@ -202,8 +251,15 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
                                MODE == kModeRes ? seq_span_bytes(sq.len, p.rs, p.D, es) : 0);
     const auto ro_ = make_rsrc(READOUT ? static_cast<T *>(p.out) + sq.oo : nullptr,
                                READOUT ? seq_span_bytes(sq.len, p.os, p.D, es) : 0);
-    const T *Bseq = static_cast<const T *>(p.Bm) + sq.Bo;
-    const T *Cseq = READOUT ? static_cast<const T *>(p.Cm) + sq.Co : nullptr;
+    // Staging: this thread's matrix (uniform per wave) as one resource.
+    const StageSlot ss = stage_slot(threadIdx.x, NBC);
+    const bool stage_c = READOUT && __builtin_amdgcn_readfirstlane(ss.mat) != 0;
+    const auto rbc = stage_c
+        ? make_rsrc(static_cast<const T *>(p.Cm) + sq.Co, seq_span_bytes(sq.len, p.Cs, kN, es))
+        : make_rsrc(static_cast<const T *>(p.Bm) + sq.Bo, seq_span_bytes(sq.len, p.Bs, kN, es));
+    const uint32_t bcrb = static_cast<uint32_t>(stage_c ? p.Cs : p.Bs) * es;
+    const uint32_t bccol = static_cast<uint32_t>(ss.col0) * es;
+    const bool bc_vec = p.bc_vec != 0;
     const float gate = p.s;
     const bool gate_zero = gate == 0.0f;
 
@@ -217,24 +273,21 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     };
 
     // ---- Bm/Cm staging of one tile of kTile tokens
-    R stg[STAGE];
-    auto stage_load = [&](int tbase, int tcnt) {
-#pragma unroll
-        for (int i = 0; i < STAGE; ++i) {
-            const int k = stage_token(i, threadIdx.x, NBC);
-            const int col = stage_col(i, threadIdx.x, NBC);
-            if (k < tcnt) {
-                const int64_t l = seg_row(sg, tbase + k);
-                stg[i] = col < kN ? E::ld_raw(Bseq + l * p.Bs + col)
-                                  : E::ld_raw(Cseq + l * p.Cs + (col - kN));
-            }
-        }
+    uint32_t stw[SW];
+    auto stage_load = [&](int tbase, int tcnt) {   // tcnt >= 1
+        const uint32_t row = static_cast<uint32_t>(seg_row(sg, tbase + stage_pos(ss.k, tcnt)));
+        const uint32_t voff = row * bcrb + bccol;
+        if (bc_vec)
+            bload_words<SW>(rbc, voff, stw);
+        else
+            E::template bload_elems<STAGE>(rbc, voff, stw);
     };
-    auto stage_store = [&](int buf, int tcnt) {
+    auto stage_store = [&](int buf) {
+        float4 *dst = reinterpret_cast<float4 *>(&lds_bc[buf][ss.k * NBC + ss.mat * kN + ss.col0]);
 #pragma unroll
-        for (int i = 0; i < STAGE; ++i)
-            if (stage_token(i, threadIdx.x, NBC) < tcnt)
-                lds_bc[buf][i * kWG + threadIdx.x] = E::widen(stg[i]);
+        for (int q = 0; q < STAGE / 4; ++q)
+            dst[q] = make_float4(E::word_elem(stw, 4 * q), E::word_elem(stw, 4 * q + 1),
+                                 E::word_elem(stw, 4 * q + 2), E::word_elem(stw, 4 * q + 3));
     };
 
     // One visited position k: consume ring slot `slot`, refill it with the
@@ -291,7 +344,7 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     if (ntok > 0) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) load_pos(prefetch_pos(j, ntok), j);
-        stage_store(0, cnt0);
+        stage_store(0);
     }
     __syncthreads();
 
@@ -312,7 +365,7 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
         for (int j = 0; j < PF; ++j)            // the last tile's partial group
             if (full + j < cnt) token(base + full + j, bc + (full + j) * NBC, j);
 
-        if (more) stage_store((ti + 1) & 1, ncnt);
+        if (more) stage_store((ti + 1) & 1);
         __syncthreads();
     }
 

@@ -4,6 +4,8 @@
 
 #include <algorithm>
 
+#include "scan_geometry.h"
+
 namespace r2l {
 namespace {
 
@@ -49,6 +51,19 @@ SegParams base_params(const r2l_scan_args *a, const Plan &pl) {
     p.out = a->out; p.os = a->out_stride;
     p.obs = eff_bstride(a, a->out_batch_stride, a->out_stride);
     return p;
+}
+
+// Whether every Bm (and, when staged, Cm) row starts on the alignment the
+// staging's vector loads need: base pointer, row stride and batch stride.
+bool bc_vector_ok(const r2l_scan_args *a, bool readout) {
+    const int64_t es = elem_size(a->dtype);
+    const int64_t al = stage_align(readout ? 2 * kN : kN, static_cast<int>(es));
+    auto ok = [&](const void *p, int64_t st, int64_t bst) {
+        return reinterpret_cast<uintptr_t>(p) % al == 0 && (st * es) % al == 0 &&
+               (eff_bstride(a, bst, st) * es) % al == 0;
+    };
+    return ok(a->Bm, a->Bm_stride, a->Bm_batch_stride) &&
+           (!readout || ok(a->Cm, a->Cm_stride, a->Cm_batch_stride));
 }
 
 // What the readout writes: y, or the gated residual reading x itself (when
@@ -114,6 +129,7 @@ int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3])
         l.G = pl.G;
         l.mode = mode;
         l.seg = p;
+        l.seg.bc_vec = bc_vector_ok(a, mode != kModeState) ? 1 : 0;
         return l;
     };
 

@@ -34,8 +34,11 @@ class FakeHeap:
 
 
 def make_args(op, *, dtype="bf16", D=64, batch=None, seqlen=None, lengths=None, res="none",
-              h_in=False, h_out=False, out=True, chunk=-1, split=0, pad_row=0, pad_batch=0):
-    """A call with every buffer sized exactly as the layout says."""
+              h_in=False, h_out=False, out=True, chunk=-1, split=0, pad_row=0, pad_batch=0,
+              bc_shift=0):
+    """A call with every buffer sized exactly as the layout says. bc_shift
+    starts Bm and Cm that many elements into their allocation (which grows by
+    as much), breaking the alignment of the staging's vector loads."""
     es = 2 if dtype == "bf16" else 4
     N = 16
     heap = FakeHeap()
@@ -53,25 +56,29 @@ def make_args(op, *, dtype="bf16", D=64, batch=None, seqlen=None, lengths=None, 
         a.cu_seqlens = heap.alloc(4 * (a.batch + 1))
         tok = a.total_tokens
 
-        def tensor(cols):
+        def tensor(cols, lead=0):
             stride = cols + pad_row
-            return heap.alloc(((tok - 1) * stride + cols) * es if tok else 0), stride, 0
+            return offset(heap.alloc(((tok - 1) * stride + cols + lead) * es if tok else 0),
+                          lead), stride, 0
     else:
         a.batch, a.seqlen = batch, seqlen
         tok = batch * seqlen
 
-        def tensor(cols):
+        def tensor(cols, lead=0):
             stride = cols + pad_row
             bstride = seqlen * stride + pad_batch
-            ext = ((batch - 1) * bstride + (seqlen - 1) * stride + cols) if tok else 0
-            return heap.alloc(ext * es), stride, bstride if pad_batch else 0
+            ext = ((batch - 1) * bstride + (seqlen - 1) * stride + cols + lead) if tok else 0
+            return offset(heap.alloc(ext * es), lead), stride, bstride if pad_batch else 0
+
+    def offset(p, lead):   # `lead` elements into the allocation
+        return p + lead * es if p is not None else None
 
     a.x, a.x_stride, a.x_batch_stride = tensor(D)
     a.dt, a.dt_stride, a.dt_batch_stride = tensor(D)
-    a.Bm, a.Bm_stride, a.Bm_batch_stride = tensor(N)
+    a.Bm, a.Bm_stride, a.Bm_batch_stride = tensor(N, bc_shift)
     readout = op == "scan" or out
     if readout:
-        a.Cm, a.Cm_stride, a.Cm_batch_stride = tensor(N)
+        a.Cm, a.Cm_stride, a.Cm_batch_stride = tensor(N, bc_shift)
         a.out, a.out_stride, a.out_batch_stride = tensor(D)
         a.Dskip = heap.alloc(4 * D)
         if res == "x":
@@ -139,7 +146,7 @@ def test_random_plans():
         kw = dict(dtype=rng.choice(["bf16", "f32"]), D=rng.choice([1, 5, 64, 100, 256, 513]),
                   split=rng.choice([0, 1, 2, 4]), chunk=rng.choice([-1, 0, 16, 33, 64, 200]),
                   h_in=rng.random() < 0.5, h_out=rng.random() < 0.5,
-                  pad_row=rng.choice([0, 0, 2, 16]))
+                  pad_row=rng.choice([0, 0, 1, 2, 8, 16]), bc_shift=rng.choice([0, 0, 0, 1, 2]))
         if rng.random() < 0.5:
             kw["lengths"] = [rng.choice([0, 1, 2, 31, 64, 65, 130, 300]) for _ in range(rng.randint(1, 6))]
         else:
@@ -150,6 +157,29 @@ def test_random_plans():
         else:
             kw["out"] = rng.random() < 0.4
         check(op, **kw)
+
+
+# ---- Bm/Cm staging: vector loads only where every row start is aligned -------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("op", ["scan", "prefix"])
+def test_staging_vector_choice(dtype, op):
+    kw = dict(dtype=dtype, lengths=[70, 0, 130, 1], D=96, chunk=64, h_out=True)
+    if op == "prefix":
+        kw["out"] = False                  # state only: chunk pass and carry
+    launches = 3 if op == "scan" else 2   # chunk pass, carry (, readout pass)
+    assert check(op, **kw).vector_staging == launches - 1
+    # row strides of 17 or 18 elements: rows on 2- or 4-byte boundaries only
+    # (bf16), or on 4- or 8-byte ones (f32): element loads
+    for pad in (1, 2):
+        assert check(op, pad_row=pad, **kw).vector_staging == 0
+    # base one element in: element loads
+    assert check(op, bc_shift=1, **kw).vector_staging == 0
+    # a row stride of 24 elements keeps 16-byte rows for bf16 and f32
+    assert check(op, pad_row=8, **kw).vector_staging == launches - 1
+    # dense batches: a batch stride off the alignment
+    dense = dict(dtype=dtype, batch=3, seqlen=65, D=64, chunk=32, h_out=True, out=op == "scan")
+    assert check(op, **dense).vector_staging == launches - 1
+    assert check(op, pad_batch=1, **dense).vector_staging == 0
 
 
 # ---- the benchmarked shapes, at full size --------------------------------------
