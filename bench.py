@@ -86,6 +86,83 @@ def load_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
+class Parity:
+    """Error of the GPU results of the timed calls against the oracle's values
+    on the CPU-baseline sample: max|err| / max|ref| against the tolerance and,
+    for bf16 outputs, the worst element measured in (one bf16 ulp of the
+    oracle's value + the fp32 bound 1e-5 * max|ref|), which must stay <= 1."""
+
+    def __init__(self, what, dtype, tol):
+        self.what, self.dtype, self.tol = what, dtype, tol
+        self.err = self.ref = self.worst = 0.0
+        self.n = 0
+
+    def add(self, got, ref):
+        import numpy as np
+        ref = np.asarray(ref, dtype=np.float64)
+        got = np.asarray(got, dtype=np.float64).reshape(ref.shape)
+        if ref.size == 0:
+            return
+        d = np.abs(got - ref)
+        scale = float(np.max(np.abs(ref)))
+        self.err = max(self.err, float(np.max(d)))
+        self.ref = max(self.ref, scale)
+        self.n += ref.size
+        if self.dtype == "bf16":
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+            self.worst = max(self.worst, float(np.max(d / (ulp + 1e-5 * scale))))
+
+    def result(self):
+        rel = self.err / max(self.ref, 1e-30)
+        r = {"what": self.what, "elements": self.n, "max_err_over_max_ref": rel,
+             "tol": self.tol}
+        ok = rel <= self.tol
+        if self.dtype == "bf16":
+            r["worst_vs_ulp_bound"] = self.worst
+            ok = ok and self.worst <= 1.0
+        r["pass"] = bool(ok)
+        return r
+
+
+def host_cpu():
+    """Model string and CPU count of the host the oracle runs on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "cpus_available": avail}
+
+
+def copy_bandwidth_gbs(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate of HBM (bytes read + bytes written per second)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def percentiles(v):
+    import numpy as np
+    p10, p50, p90 = np.percentile(np.asarray(v, dtype=np.float64), [10, 50, 90])
+    return {"p10": float(p10), "median": float(p50), "p90": float(p90)}
+
+
 # ---------------------------------------------------------------------------
 class Workload:
     name = ""
@@ -103,7 +180,9 @@ class Workload:
         for c in self.step_calls[i % len(self.step_calls)]:
             c.launch(stream)
 
-    def cpu_baseline(self, budget_s):
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
+        """Oracle token·channels/s on a bounded sample of the workload; with a
+        Parity object, also compares the GPU results of the timed calls."""
         raise NotImplementedError
 
 
@@ -143,11 +222,14 @@ class Denoise(Workload):
         set_bytes = self.bytes_per_launch * self.HOOKS
         self.R = _rotation(set_bytes)
         self.step_calls = []
+        self.outs0 = []
         for r in range(self.R):
             row = []
             for h, g in enumerate(base):
                 x = g["x"].clone()
                 out = torch.empty_like(x)
+                if r == 0:
+                    self.outs0.append(out)
                 row.append(r2l.bind("r2l_scan", x=x, dt=g["dt"].clone(), Bm=g["Bm"].clone(),
                                     Cm=g["Cm"].clone(), A=g["A"], Dskip=g["Dskip"], res=x,
                                     s=float(self.gates[h]), out=out))
@@ -162,22 +244,31 @@ class Denoise(Workload):
                        "rotating_sets": self.R, "rotating_bytes": set_bytes * self.R,
                        "parallelism": "single_gpu"}
 
-    def cpu_baseline(self, budget_s):
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
         import oracle
-        tc, secs, reps = 0, 0.0, 0
+        tc, secs, reps, hooks = 0, 0.0, 0, 0
         while secs < budget_s and reps < 200:
             for h, inp in enumerate(self.inputs):
                 t = {}
-                oracle.r2l_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, res=inp.x,
-                                s=float(self.gates[h]), seq_offsets=inp.offsets, timing=t,
-                                want_y=False)
+                r = oracle.r2l_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, res=inp.x,
+                                    s=float(self.gates[h]), seq_offsets=inp.offsets, timing=t,
+                                    want_y=False, nthreads=nthreads)
+                if parity is not None and reps == 0:
+                    parity.add(self.outs0[h].float().cpu().numpy().reshape(r["out"].shape),
+                               r["out"])
                 secs += t["seconds"]
                 tc += inp.x.size
+                hooks += 1
+                if nthreads == 1 and secs >= budget_s:
+                    break
             reps += 1
-        return {"value": tc / secs, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
-                "kind": "oracle",
-                "sample": "the full 7-hook step (%d token-channels), %d times, %.1f s of oracle "
-                          "time" % (self.tc_per_step, reps, secs)}
+        return {"value": tc / secs, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "%d hooks of the 7-hook step (%d token-channels), %.1f s of oracle "
+                          "time" % (hooks, tc, secs)}
+
+    parity_spec = ("out", "bf16", 2e-2,
+                   "out = x + s*y of all 7 hooks (first buffer set) vs the oracle's")
 
 
 def time_back_to_back(torch, calls, reps, per_ms):
@@ -224,8 +315,11 @@ def device_inputs(torch, key, lengths, D, dtype):
     return {"x": x, "dt": dt, "Bm": Bm, "Cm": Cm, "A": A, "Dskip": Dskip}
 
 
-def oracle_sample_rate(torch, g, offsets, seqs, budget_s, reverse=True, readout=True):
-    """Oracle token·channels/s over the listed sequences (copied back from the GPU)."""
+def oracle_sample_rate(torch, g, offsets, seqs, budget_s, reverse=True, readout=True,
+                       nthreads=0, parity=None, got=None):
+    """Oracle token·channels/s over the listed sequences (copied back from the GPU).
+    With `parity`, the GPU result `got` (token-major y, or [batch, D, N] states
+    when not `readout`) of each sampled sequence is compared with the oracle's."""
     import numpy as np
     import oracle
     tc, secs = 0, 0.0
@@ -236,9 +330,15 @@ def oracle_sample_rate(torch, g, offsets, seqs, budget_s, reverse=True, readout=
         Bm = g["Bm"][r0:r1].float().cpu().numpy()
         Cm = g["Cm"][r0:r1].float().cpu().numpy() if readout else None
         t = {}
-        oracle.selective_scan(x, dt, Bm, Cm, g["A"].cpu().numpy(), g["Dskip"].cpu().numpy(),
-                              reverse=reverse, seq_offsets=np.array([0, r1 - r0]),
-                              want_y=readout, want_h_out=not readout, timing=t)
+        r = oracle.selective_scan(x, dt, Bm, Cm, g["A"].cpu().numpy(), g["Dskip"].cpu().numpy(),
+                                  reverse=reverse, seq_offsets=np.array([0, r1 - r0]),
+                                  want_y=readout, want_h_out=not readout, timing=t,
+                                  nthreads=nthreads)
+        if parity is not None:
+            if readout:
+                parity.add(got[r0:r1].float().cpu().numpy(), r["y"])
+            else:
+                parity.add(got[b].cpu().numpy(), r["h_out"][0])
         secs += t["seconds"]
         tc += x.size
         if secs >= budget_s:
@@ -269,6 +369,8 @@ class Prefill(Workload):
         for r in range(self.R):
             src = g if r == 0 else {k: v.clone() for k, v in g.items()}
             out = torch.empty_like(view(src["x"]))
+            if r == 0:
+                self.out0 = out.view(tok, self.D)
             self.calls.append(r2l.bind("r2l_scan", x=view(src["x"]), dt=view(src["dt"]),
                                        Bm=view(src["Bm"]), Cm=view(src["Cm"]), A=g["A"],
                                        Dskip=g["Dskip"], out=out))
@@ -280,13 +382,17 @@ class Prefill(Workload):
                        "rotating_sets": self.R, "parallelism": "single_gpu",
                        "plan": self.calls[0].plan()}
 
-    def cpu_baseline(self, budget_s):
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
         import oracle
         rate, tc, secs = oracle_sample_rate(self.torch, self.g, self.offsets, range(self.B),
-                                            budget_s)
-        return {"value": rate, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
-                "kind": "oracle", "sample": "%d of the %d sequences (%d token-channels), %.1f s"
+                                            budget_s, nthreads=nthreads, parity=parity,
+                                            got=self.out0)
+        return {"value": rate, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "%d of the %d sequences (%d token-channels), %.1f s"
                 % (tc // (self.L * self.D), self.B, tc, secs)}
+
+    parity_spec = ("y", "bf16", 2e-2, "y of the sampled sequences (first buffer set)")
 
 
 class RaggedServing(Workload):
@@ -318,6 +424,8 @@ class RaggedServing(Workload):
             g = self.g if r == 0 else {k: v.clone() for k, v in self.g.items()}
             gc = self.gc if r == 0 else {k: v.clone() for k, v in self.gc.items()}
             out = torch.empty_like(g["x"])
+            if r == 0:
+                self.out0 = out
             state = torch.randn((B, self.D, 16), device="cuda")
             scan = r2l.bind("r2l_scan", x=g["x"], dt=g["dt"], Bm=g["Bm"], Cm=g["Cm"], A=g["A"],
                             Dskip=g["Dskip"], out=out, cu_seqlens=cu, max_seqlen=int(lens.max()))
@@ -336,13 +444,18 @@ class RaggedServing(Workload):
                        "ops": ["r2l_scan (out = y)", "block_commit_state (in place)"],
                        "rotating_sets": self.R, "parallelism": "single_gpu"}
 
-    def cpu_baseline(self, budget_s):
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
         import oracle
         rate, tc, secs = oracle_sample_rate(self.torch, self.g, self.offsets,
-                                            range(len(self.offsets) - 1), budget_s)
-        return {"value": rate, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
-                "kind": "oracle", "sample": "reverse scan of the first sequences (%d "
-                "token-channels), %.1f s" % (tc, secs)}
+                                            range(len(self.offsets) - 1), budget_s,
+                                            nthreads=nthreads, parity=parity, got=self.out0)
+        return {"value": rate, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "reverse scan of the first sequences (%d token-channels), %.1f s"
+                % (tc, secs)}
+
+    parity_spec = ("y", "bf16", 2e-2,
+                   "y of the reverse scan over the sampled blocks (first buffer set)")
 
 
 class RaggedPrefix(Workload):
@@ -367,6 +480,7 @@ class RaggedPrefix(Workload):
         self.launches_per_step = 1
         self.R = 1  # 17.8 GB per launch: far beyond every cache
         h = torch.empty((B, self.D, 16), device="cuda")
+        self.h = h
         g = self.g
         self.calls = [r2l.bind("prefix_scan_state", x=g["x"], dt=g["dt"], Bm=g["Bm"], A=g["A"],
                                h_out=h, cu_seqlens=cu, max_seqlen=int(lens.max()))]
@@ -379,14 +493,18 @@ class RaggedPrefix(Workload):
                        "parallelism": "single_gpu",
                        "plan": self.calls[0].plan()}
 
-    def cpu_baseline(self, budget_s):
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
         import oracle
         rate, tc, secs = oracle_sample_rate(self.torch, self.g, self.offsets,
                                             range(len(self.offsets) - 1), budget_s,
-                                            reverse=False, readout=False)
-        return {"value": rate, "unit": "tokens*channels/s", "cores": oracle.max_threads(),
-                "kind": "oracle", "sample": "prefix states of the first prefixes (%d "
-                "token-channels), %.1f s" % (tc, secs)}
+                                            reverse=False, readout=False, nthreads=nthreads,
+                                            parity=parity, got=self.h)
+        return {"value": rate, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "prefix states of the first prefixes (%d token-channels), %.1f s"
+                % (tc, secs)}
+
+    parity_spec = ("h_out", "f32", 1e-5, "final state of the sampled prefixes")
 
 
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
@@ -464,13 +582,20 @@ def main():
         torch.cuda.synchronize()
         graph_s = (time.perf_counter() - t0) / args.steps
 
-    # (3) kernel durations: each timed entry point launched back to back
+    # (3) kernel durations: each timed entry point launched back to back, in
+    # several rounds (the average over all launches, and the spread of the
+    # per-round averages)
     per_ms = sleep_cycles_per_ms(torch)
     timed = []
+    rounds = 9
     for m in wl.measure:
-        reps = max(len(m["calls"]), min(args.steps * wl.launches_per_step, 2000))
-        ms = time_back_to_back(torch, m["calls"], reps, per_ms)
-        timed.append(dict(m, ms=ms, reps=reps))
+        per_round = max(len(m["calls"]), min(args.steps * wl.launches_per_step, 2000) // rounds)
+        ms_rounds = [time_back_to_back(torch, m["calls"], per_round, per_ms)
+                     for _ in range(rounds)]
+        timed.append(dict(m, ms=sum(ms_rounds) / rounds, reps=per_round * rounds,
+                          spread_us={k: round(v * 1e3, 3)
+                                     for k, v in percentiles(ms_rounds).items()}))
+    copy_gbs = copy_bandwidth_gbs(torch)
 
     step_s = min(eager_s, graph_s) if graph_s else eager_s
     value = wl.tc_per_step / step_s
@@ -490,15 +615,22 @@ def main():
     for m in timed:
         bind_, other_ = rooflines(m)
         kernels.append({"entry": m["label"], "avg_launch_us": round(m["ms"] * 1e3, 3),
+                        "launch_us_spread_over_rounds": m["spread_us"],
                         "launches_timed": m["reps"], "bytes_per_launch": m["bytes"],
                         "tc_per_launch": m["tc"], "tc_per_s": m["tc"] / (m["ms"] * 1e-3),
                         "roofline": bind_, "roofline_other": other_})
     binding, other = kernels[0]["roofline"], kernels[0]["roofline_other"]
     hbm_gbs = (binding if binding["bound"] == "hbm" else other)["achieved"]
 
-    cpu = None
+    cpu = parity = None
     if args.cpu_seconds > 0:
-        cpu = wl.cpu_baseline(args.cpu_seconds)
+        what, pdtype, tol, sample = wl.parity_spec
+        par = Parity(what, pdtype, tol)
+        cpu = wl.cpu_baseline(args.cpu_seconds, parity=par)
+        parity = dict(par.result(), sample=sample)
+        single = wl.cpu_baseline(args.cpu_seconds / 4, nthreads=1)
+        cpu.update(single_thread_value=single["value"], single_thread_sample=single["sample"],
+                   **host_cpu())
 
     line = {
         "metric": "R2L selective-scan tokens*channels/s and HBM GB/s (% of peak), 1xMI355X",
@@ -518,6 +650,8 @@ def main():
         "roofline_other": other,
         "hbm_gbs": hbm_gbs,
         "hbm_frac_of_8TBs": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "copy_gbs_measured": round(copy_gbs, 1),
+        "hbm_frac_of_copy": round(hbm_gbs / copy_gbs, 4),
         "kernels": kernels,
         "alu_model": {"lane_ops_per_tc_readout_res": alu_ops_per_tc(True, True),
                       "lane_ops_per_tc_state_only": alu_ops_per_tc(False, False),
@@ -526,6 +660,7 @@ def main():
         "ms_per_step_eager": eager_s * 1e3,
         "ms_per_step_graph": graph_s * 1e3 if graph_s else None,
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
     }
     print(json.dumps(line))
 

@@ -50,6 +50,25 @@ class Checker {
                  (unsigned long long)reg->lo, (unsigned long long)reg->hi);
     }
 
+    // Workspace words written so far by the call's launches, in order: every
+    // read of the workspace must find its words written by an earlier launch.
+    void set_workspace(const void *base, uint64_t bytes) {
+        ws_lo_ = reinterpret_cast<uintptr_t>(base);
+        ws_written_.assign(base ? bytes / 4 : 0, false);
+    }
+    void wrote(uintptr_t addr, uint64_t bytes) {
+        if (!in_ws(addr)) return;
+        for (uint64_t w = (addr - ws_lo_) / 4; w < (addr - ws_lo_ + bytes) / 4; ++w)
+            if (w < ws_written_.size()) ws_written_[w] = true;
+    }
+    void read_written(const char *what, uintptr_t addr, uint64_t bytes) {
+        if (!in_ws(addr) || failed_) return;
+        for (uint64_t w = (addr - ws_lo_) / 4; w < (addr - ws_lo_ + bytes) / 4; ++w)
+            if (w >= ws_written_.size() || !ws_written_[w])
+                return fail("%s: reads workspace byte 0x%llx that no earlier launch wrote", what,
+                            (unsigned long long)(ws_lo_ + 4 * w));
+    }
+
     void fail(const char *fmt, ...) __attribute__((format(printf, 2, 3))) {
         if (failed_) return;
         failed_ = true;
@@ -60,26 +79,32 @@ class Checker {
     }
 
   private:
+    bool in_ws(uintptr_t a) const {
+        return !ws_written_.empty() && a >= ws_lo_ && a < ws_lo_ + 4 * ws_written_.size();
+    }
+
     std::vector<Region> regions_;
     r2l_access_report *rep_;
     bool failed_ = false;
+    uintptr_t ws_lo_ = 0;
+    std::vector<bool> ws_written_;
 };
 
 uintptr_t U(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
 void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const SegParams &p = l.seg;
-    const bool readout = l.mode != kModeState;
-    const int G = l.G, NS = kN / G, NBC = readout ? 2 * kN : kN, STAGE = kTile * NBC / kWG;
+    const bool launch_readout = l.mode != kModeState;
+    const int G = l.G, NS = kN / G;
     const int64_t es = l.dtype == R2L_DTYPE_BF16 ? 2 : 4;
     const Region *rA = ck.region_of(p.A), *rDs = p.Dskip ? ck.region_of(p.Dskip) : nullptr;
     const Region *rHin = p.hin ? ck.region_of(p.hin) : nullptr;
     const Region *rHfin = p.hfin ? ck.region_of(p.hfin) : nullptr;
     const Region *rSd = p.sdelta ? ck.region_of(p.sdelta) : nullptr;
     const Region *rX = ck.region_of(p.x), *rD = ck.region_of(p.dt), *rB = ck.region_of(p.Bm);
-    const Region *rC = readout ? ck.region_of(p.Cm) : nullptr;
+    const Region *rC = launch_readout ? ck.region_of(p.Cm) : nullptr;
     const Region *rR = l.mode == kModeRes ? ck.region_of(p.res) : nullptr;
-    const Region *rO = readout ? ck.region_of(p.out) : nullptr;
+    const Region *rO = launch_readout ? ck.region_of(p.out) : nullptr;
 
     for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
         const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, bid);
@@ -88,9 +113,14 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
         const int64_t s1 = p.cu_seqlens ? cu_host[bg.b + 1] : 0;
         const SeqGeom sq = seq_geom(p, bg.b, s0, s1);
         const SegGeom sg = seg_geom(l.reverse, bg.c, p.chunk_len, sq.len);
-        if (!sg.run) continue;
         if (p.cu_seqlens) ck.access("cu_seqlens", ck.region_of(p.cu_seqlens),
                                     U(p.cu_seqlens) + bg.b * 4, 8);
+        if (!segment_runs(p, sg, bg.c)) continue;
+        // the body this block runs: a split chunk pass scans chunks > 0 state only
+        const bool readout = launch_readout && !(p.split_c0 && bg.c > 0);
+        const int mode = readout ? l.mode : kModeState;
+        const int NBC = readout ? 2 * kN : kN, STAGE = stage_cols(NBC);
+        const float *hin = segment_hin(p, bg.b, bg.c);
 
         // per-lane loads and stores outside the token loop
         uint32_t dmin = UINT32_MAX, dmax = 0;
@@ -100,12 +130,21 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
             dmax = lg.d > dmax ? lg.d : dmax;
             const int64_t st = static_cast<int64_t>(lg.d) * kN + lg.sub * NS;
             ck.access("A", rA, U(p.A) + st * 4, NS * 4);
-            if (p.hin) ck.access("h_in", rHin, U(p.hin) + (bg.b * p.hin_b + bg.c * p.hin_c + st) * 4, NS * 4);
+            if (hin) {
+                ck.access("h_in", rHin, U(hin) + st * 4, NS * 4);
+                ck.read_written("h_in", U(hin) + st * 4, NS * 4);
+            }
             if (readout && p.Dskip) ck.access("Dskip", rDs, U(p.Dskip) + lg.d * 4, 4);
-            if (p.hfin && lg.active)
-                ck.access("h_final", rHfin, U(p.hfin) + (bg.b * p.hfin_b + bg.c * p.hfin_c + st) * 4, NS * 4);
-            if (p.sdelta && lg.active && lg.sub == 0)
-                ck.access("delta_sum", rSd, U(p.sdelta) + (bg.b * p.sd_b + bg.c * p.sd_c + lg.d) * 4, 4);
+            if (p.hfin && lg.active) {
+                const uintptr_t a = U(p.hfin) + (bg.b * p.hfin_b + bg.c * p.hfin_c + st) * 4;
+                ck.access("h_final", rHfin, a, NS * 4);
+                ck.wrote(a, NS * 4);
+            }
+            if (!readout && p.sdelta && lg.active && lg.sub == 0) {
+                const uintptr_t a = U(p.sdelta) + (bg.b * p.sd_b + bg.c * p.sd_c + lg.d) * 4;
+                ck.access("delta_sum", rSd, a, 4);
+                ck.wrote(a, 4);
+            }
         }
         if (!ck.ok()) return;
 
@@ -131,7 +170,7 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
         auto load_pos = [&](int k) {
             row_access("x", rX, p.x, sq.xo, p.xs, k);
             row_access("dt", rD, p.dt, sq.dto, p.dts, k);
-            if (l.mode == kModeRes) row_access("res", rR, p.res, sq.ro, p.rs, k);
+            if (mode == kModeRes) row_access("res", rR, p.res, sq.ro, p.rs, k);
         };
         const int ntok = sg.ntok;
         if (ntok > 0)
@@ -183,12 +222,24 @@ void check_carry(Checker &ck, const Launch &l, const int32_t *cu_host) {
         const int64_t len = p.cu_seqlens ? static_cast<int64_t>(cu_host[g.b + 1]) - cu_host[g.b] : p.seqlen;
         const int nc = carry_chunks(len, p.chunk_len, p.nchunks);
         ck.access("A", rA, U(p.A) + (g.d * kN + g.n) * 4, 4);
-        if (p.hin) ck.access("h_in", rin, U(p.hin) + ((g.b * p.D + g.d) * kN + g.n) * 4, 4);
-        for (int c = 0; c < nc; ++c) {
+        if (p.c0_seeded) {
+            const uintptr_t q0 = U(p.Q) + ((g.b * p.nchunks * p.D + g.d) * kN + g.n) * 4;
+            ck.access("Q", rQ, q0, 4);
+            ck.read_written("Q of chunk 0", q0, 4);
+        } else if (p.hin) {
+            ck.access("h_in", rin, U(p.hin) + ((g.b * p.D + g.d) * kN + g.n) * 4, 4);
+        }
+        for (int c = p.c0_seeded ? 1 : 0; c < nc && ck.ok(); ++c) {
             const int64_t sc = (g.b * p.nchunks + c) * p.D + g.d;
-            if (p.Hc) ck.access("H", rH, U(p.Hc) + (sc * kN + g.n) * 4, 4);
+            if (p.Hc) {
+                ck.access("H", rH, U(p.Hc) + (sc * kN + g.n) * 4, 4);
+                ck.wrote(U(p.Hc) + (sc * kN + g.n) * 4, 4);
+            }
+            if (c == nc - 1 && !p.hout) break;
             ck.access("S", rS, U(p.S) + sc * 4, 4);
+            ck.read_written("S", U(p.S) + sc * 4, 4);
             ck.access("Q", rQ, U(p.Q) + (sc * kN + g.n) * 4, 4);
+            ck.read_written("Q", U(p.Q) + (sc * kN + g.n) * 4, 4);
         }
         if (p.hout) ck.access("h_out", rout, U(p.hout) + ((g.b * p.D + g.d) * kN + g.n) * 4, 4);
     }
@@ -229,6 +280,7 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
         if (wants_readout(op, a)) add("workspace H", ws + pl.off_H, pl.ws_bytes - pl.off_H);
     }
     Checker ck(std::move(regs), rep);
+    if (pl.chunked) ck.set_workspace(a->workspace, pl.ws_bytes);
     Launch ls[3];
     const int n = build_launches(op, a, pl, ls);
     for (int i = 0; i < n && ck.ok(); ++i) {

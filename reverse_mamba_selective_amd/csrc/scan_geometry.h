@@ -74,20 +74,41 @@ R2L_HD SeqGeom seq_geom(const SegParams &p, int64_t b, int64_t s0, int64_t s1) {
 // segment is sequence row t_first + step * k, for 0 <= k < ntok.
 struct SegGeom {
     bool run;
+    bool last;    // the sequence's last chunk
     int ntok;
     int t_first;
     int step;
 };
 
 R2L_HD SegGeom seg_geom(bool rev, int c, int64_t chunk_len, int64_t len) {
-    SegGeom g{false, 0, 0, rev ? -1 : 1};
+    SegGeom g{false, false, 0, 0, rev ? -1 : 1};
     const int64_t v0 = static_cast<int64_t>(c) * chunk_len;
     if (c > 0 && v0 >= len) return g;
     const int64_t v1 = v0 + chunk_len < len ? v0 + chunk_len : len;
     g.run = true;
+    g.last = v1 >= len;
     g.ntok = v1 > v0 ? static_cast<int>(v1 - v0) : 0;
     g.t_first = static_cast<int>(rev ? len - 1 - v0 : v0);
     return g;
+}
+
+// Whether a launch scans chunk c at all: the readout pass of a plan whose
+// chunk pass already wrote chunk 0 skips it, and a chunk pass whose caller
+// wants no final state skips each sequence's last chunk (c > 0), whose local
+// results nothing reads.
+R2L_HD bool segment_runs(const SegParams &p, const SegGeom &sg, int c) {
+    if (!sg.run) return false;
+    if (p.skip_c0 && c == 0) return false;
+    if (p.skip_last && c > 0 && sg.last) return false;
+    return true;
+}
+
+// State a segment starts from: its slot of hin, except in a split chunk pass,
+// where only chunk 0 starts from the call's initial state (hin) and the others
+// from zero.
+R2L_HD const float *segment_hin(const SegParams &p, int64_t b, int c) {
+    if (!p.hin || (p.split_c0 && c > 0)) return nullptr;
+    return p.hin + b * p.hin_b + c * p.hin_c;
 }
 
 R2L_HD int seg_row(const SegGeom &g, int k) { return g.t_first + g.step * k; }

@@ -51,6 +51,11 @@ struct SegParams {
     const void *res; int64_t rs, rbs;
     float s;
     void *out; int64_t os, obs;
+
+    // chunked readout plans:
+    int32_t split_c0;   // chunk pass: chunk 0 reads out from hin, chunks > 0 are state only from 0
+    int32_t skip_c0;    // readout pass: chunk 0 was written by the chunk pass
+    int32_t skip_last;  // chunk pass: skip each sequence's last chunk (c > 0)
 };
 
 // Joins chunk results (local final state Q from a zero start and the Delta sum
@@ -68,6 +73,7 @@ struct CarryParams {
     const float *S;              // [batch, nchunks, D]
     float *Hc;                   // [batch, nchunks, D, N] state entering each chunk, or nullptr
     float *hout;                 // [batch, D, N] or nullptr
+    int32_t c0_seeded;           // Q of chunk 0 is the true state after it (hin is not read)
 };
 
 // dtype: 0 fp32, 1 bf16. G in {1, 2, 4}. mode: kMode*.

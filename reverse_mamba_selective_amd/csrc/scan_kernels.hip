@@ -191,7 +191,9 @@ __device__ __forceinline__ float group_sum(float y) {
 // barrier per tile). Row addresses are uniform (scalar) and the lane adds a
 // 32-bit channel offset.
 template <bool REV, typename T, int G, int MODE>
-__global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
+__device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, const BlockGeom &bg,
+                                             const SeqGeom &sq, const SegGeom &sg,
+                                             const float *hin) {
     constexpr bool READOUT = MODE != kModeState;
     constexpr int NS = kN / G;                   // states per lane
     constexpr int NBC = READOUT ? 2 * kN : kN;   // staged floats per token (B, then C)
@@ -200,19 +202,12 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     constexpr int PF = kPrefetch;
     static_assert(kTile * NBC == STAGE * kWG && kN % STAGE == 0 && STAGE % 4 == 0 &&
                   kTile % PF == 0, "tile shape");
-    __shared__ __align__(16) float lds_bc[2][kTile * NBC];
+    float (*lds_bc)[kTile * NBC] = reinterpret_cast<float (*)[kTile * NBC]>(lds);
     using E = Elem<T>;
     using R = typename E::raw_t;
 
-    const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
-    if (!bg.valid) return;
     const int64_t b = bg.b;
     const int c = bg.c;
-    const int64_t s0 = p.cu_seqlens ? p.cu_seqlens[b] : 0;
-    const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[b + 1] : 0;
-    const SeqGeom sq = seq_geom(p, b, s0, s1);
-    const SegGeom sg = seg_geom(REV, c, p.chunk_len, sq.len);
-    if (!sg.run) return;                          // chunk beyond this sequence
     const int ntok = sg.ntok;
 
     const LaneGeom lg = lane_geom(bg.tile, threadIdx.x, G, p.D);
@@ -222,8 +217,8 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     float a2[NS], h[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) a2[j] = p.A[dl * kN + sub * NS + j] * kLog2e;
-    if (p.hin) {
-        const float *hp = p.hin + b * p.hin_b + c * p.hin_c + dl * kN + sub * NS;
+    if (hin) {
+        const float *hp = hin + dl * kN + sub * NS;
 #pragma unroll
         for (int j = 0; j < NS; ++j) h[j] = hp[j];
     } else {
@@ -374,7 +369,34 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) hp[j] = h[j];
     }
-    if (p.sdelta && lg.active && sub == 0) p.sdelta[b * p.sd_b + c * p.sd_c + dl] = dsum;
+    if (!READOUT && p.sdelta && lg.active && sub == 0) p.sdelta[b * p.sd_b + c * p.sd_c + dl] = dsum;
+}
+
+// One workgroup per (sequence b, chunk c, channel tile). Chunk passes of
+// readout plans (split_c0) run the readout on chunk 0, which starts from the
+// call's own initial state, and the state-only scan from zero on the others.
+template <bool REV, typename T, int G, int MODE>
+__global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
+    constexpr int NBC_MAX = MODE != kModeState ? 2 * kN : kN;
+    __shared__ __align__(16) float lds[2 * kTile * NBC_MAX];
+
+    const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
+    if (!bg.valid) return;
+    const int64_t b = bg.b;
+    const int c = bg.c;
+    const int64_t s0 = p.cu_seqlens ? p.cu_seqlens[b] : 0;
+    const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[b + 1] : 0;
+    const SeqGeom sq = seq_geom(p, b, s0, s1);
+    const SegGeom sg = seg_geom(REV, c, p.chunk_len, sq.len);
+    if (!segment_runs(p, sg, c)) return;
+    const float *hin = segment_hin(p, b, c);
+    if constexpr (MODE != kModeState) {
+        if (p.split_c0 && c > 0) {
+            scan_segment<REV, T, G, kModeState>(p, lds, bg, sq, sg, hin);
+            return;
+        }
+    }
+    scan_segment<REV, T, G, MODE>(p, lds, bg, sq, sg, hin);
 }
 
 // ---- the carry over chunks -------------------------------------------------
@@ -387,10 +409,14 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const CarryParams 
         ? static_cast<int64_t>(p.cu_seqlens[g.b + 1]) - p.cu_seqlens[g.b] : p.seqlen;
     const int nc = carry_chunks(len, p.chunk_len, p.nchunks);
     const float a2 = p.A[g.d * kN + g.n] * kLog2e;
-    float H = p.hin ? p.hin[(g.b * p.D + g.d) * kN + g.n] : 0.0f;
-    for (int c = 0; c < nc; ++c) {
+    // seeded: chunk 0 was scanned from the call's initial state, so its
+    // local final state is already the true state after it
+    float H = p.c0_seeded ? p.Q[(g.b * p.nchunks * p.D + g.d) * kN + g.n]
+                          : (p.hin ? p.hin[(g.b * p.D + g.d) * kN + g.n] : 0.0f);
+    for (int c = p.c0_seeded ? 1 : 0; c < nc; ++c) {
         const int64_t sc = (g.b * p.nchunks + c) * p.D + g.d;
         if (p.Hc) p.Hc[sc * kN + g.n] = H;
+        if (c == nc - 1 && !p.hout) break;   // the last chunk's local results are not needed
         const float P = __builtin_amdgcn_exp2f(a2 * p.S[sc]);
         H = fmaf(P, H, p.Q[sc * kN + g.n]);
     }

@@ -16,10 +16,14 @@ namespace {
 // So the planner keeps one lane per channel and, when a shape has too few
 // channels to fill the machine, cuts sequences into chunks instead:
 //  * state-only scans chunk for free (the carry is one fma per chunk);
-//  * readout scans pay a second, state-only pass over each chunk (about 1.8x
-//    the vector work) and still come out ahead below ~4096 waves (e.g. 8 x
-//    4096 x 4096: 0.90 ms chunked vs 1.01 ms with 4 lanes per channel and
-//    1.64 ms with one wave per channel tile and no chunking).
+//  * readout scans pay a second, state-only pass over the chunks after the
+//    first (about 1.65x the vector work of one pass at 9 chunks) and still
+//    come out ahead below ~4096 waves. Each of their two passes runs one chunk
+//    fewer than the plan has (the chunk pass skips the last chunk when no
+//    final state is wanted, the readout pass the first), so they take one
+//    chunk more than the machine needs: 8 x 4096 x 4096 runs in 0.78 ms with
+//    9 chunks, 0.84 ms with 8, 1.01 ms with 4 lanes per channel and 1.64 ms
+//    with one wave per channel tile and no chunking.
 constexpr int64_t kTargetLanes = 4096 * 64;
 // Longest chunk a state-only plan keeps, so that ragged prefixes of very
 // different lengths balance across the machine.
@@ -88,10 +92,12 @@ Plan make_plan(Op op, const r2l_scan_args *a) {
     } else if (a->chunk_tokens == 0 && maxlen > 0) {
         const int64_t lanes = std::max<int64_t>(channels * pl.G, 1);
         const int64_t fill = (kTargetLanes + lanes - 1) / lanes;  // chunks to fill the machine
-        const int64_t want = readout ? fill
+        const int64_t want = readout ? (fill > 1 ? fill + 1 : 1)
                                      : std::max<int64_t>(fill, (maxlen + kMaxStateChunk - 1) /
                                                                    kMaxStateChunk);
         if (want > 1) chunk = std::max<int64_t>(kMinChunk, (maxlen + want - 1) / want);
+        // a readout plan of two chunks runs one chunk per pass: no gain
+        if (readout && chunk > 0 && (maxlen + chunk - 1) / chunk < 3) chunk = 0;
     }
     if (chunk > 0 && chunk < maxlen) {
         pl.chunked = true;
@@ -147,14 +153,24 @@ int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3])
     float *S = reinterpret_cast<float *>(ws + pl.off_S);
     float *H = readout ? reinterpret_cast<float *>(ws + pl.off_H) : nullptr;
 
-    // 1. every chunk from a zero state: local final state Q and Delta sum S
+    // 1. every chunk from a zero state: local final state Q and Delta sum S.
+    // Readout plans: chunk 0 starts from the call's own initial state, so this
+    // pass already writes its outputs, and the readout pass skips it; without
+    // h_out nothing reads the last chunk's Q and S, so this pass skips it.
     SegParams p1 = base_params(a, pl);
-    p1.hin = nullptr;
     p1.hfin = Q; p1.hfin_b = pl.nchunks * DN; p1.hfin_c = DN;
     p1.sdelta = S; p1.sd_b = pl.nchunks * a->dim; p1.sd_c = a->dim;
-    p1.res = nullptr;
-    p1.out = nullptr;
-    out[0] = seg(p1, kModeState);
+    if (readout) {
+        p1.hin = h_init; p1.hin_b = DN; p1.hin_c = 0;
+        p1.split_c0 = 1;
+        p1.skip_last = a->h_out ? 0 : 1;
+        out[0] = seg(p1, out_mode(a, p1));
+    } else {
+        p1.hin = nullptr;
+        p1.res = nullptr;
+        p1.out = nullptr;
+        out[0] = seg(p1, kModeState);
+    }
 
     // 2. chain the chunks: the state entering each chunk, and the final state
     Launch c{};
@@ -168,7 +184,8 @@ int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3])
     c.carry.chunk_len = static_cast<int32_t>(pl.chunk_len);
     c.carry.nchunks = static_cast<int32_t>(pl.nchunks);
     c.carry.A = a->A;
-    c.carry.hin = h_init;
+    c.carry.hin = readout ? nullptr : h_init;
+    c.carry.c0_seeded = readout ? 1 : 0;
     c.carry.Q = Q;
     c.carry.S = S;
     c.carry.Hc = H;
@@ -176,10 +193,11 @@ int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3])
     out[1] = c;
     if (!readout) return 2;
 
-    // 3. readout: rescan every chunk from the state that enters it
+    // 3. readout: rescan every chunk but the first from the state that enters it
     SegParams p3 = base_params(a, pl);
     p3.hin = H; p3.hin_b = pl.nchunks * DN; p3.hin_c = DN;
     p3.hfin = nullptr;
+    p3.skip_c0 = 1;
     out[2] = seg(p3, out_mode(a, p3));
     return 3;
 }

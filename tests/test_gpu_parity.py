@@ -299,6 +299,51 @@ def test_chunked_plans_carry_state(gpu, dtype, chunk):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("res", ["none", "x", "separate", "x_s0", "in_place"])
+def test_chunked_readout_plans(gpu, dtype, res):
+    """Chunked readout plans write chunk 0 in the chunk pass (from the call's
+    initial state) and the other chunks in the readout pass; without h_out the
+    chunk pass skips each sequence's last chunk. Every combination of h_in,
+    h_out and residual form, on sequences shorter than, equal to and longer
+    than a chunk, and empty ones."""
+    lengths = [300, 1, 0, 64, 65, 129, 40, 192]
+    D, chunk = 80, 64
+    inp = synth.scan_inputs(19, lengths, D=D, dtype=dtype, dt_mean=-4.0)
+    g = on_gpu(inp, dense=False)
+    h0 = synth.initial_state(19, len(lengths), D, 16)
+    s = 0.0 if res == "x_s0" else 0.3
+    res_np = {"none": None, "separate": synth.scan_inputs(20, lengths, D=D, dtype=dtype).x}.get(
+        res, inp.x)
+    for with_hin in (False, True):
+        for with_hout in (False, True):
+            ref = oracle_scan(inp, res=res_np, s=s, h_in=h0 if with_hin else None,
+                              want_h_out=with_hout, want_out=res_np is not None)
+            x = g["x"].clone()
+            kw = dict(scan_kw(g), x=x, chunk_tokens=chunk)
+            if with_hin:
+                kw["h_in"] = dev32(h0)
+            if with_hout:
+                kw["h_out"] = torch.full((len(lengths), D, 16), float("nan"), device="cuda")
+            if res_np is not None:
+                kw.update(res=x if res != "separate" else dev(res_np, dtype), s=s)
+            if res == "in_place":
+                kw["out"] = x
+            out = r2l.r2l_scan(**kw)
+            what = "%s h_in=%d h_out=%d" % (res, with_hin, with_hout)
+            if res_np is None:
+                check_y(out, ref["y"], dtype, what)
+            elif s == 0.0:
+                assert np.array_equal(bits(out), bits(dev(res_np, dtype))), what
+            else:
+                check_y(out, ref["out"], dtype, what)
+            if with_hout:
+                check_state(kw["h_out"], ref["h_out"], what)
+            plan = r2l.bind("r2l_scan", **{**kw, "out": out}).plan()
+            assert plan["chunked"] and plan["launches"] == 3
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
