@@ -11,9 +11,11 @@ timed region; the buffer sets rotate over more than 1 GB so that every step
 reads HBM rather than the 256 MB Infinity Cache.
 
 One JSON line on stdout: ``value`` is token·channels per second of whole
-steps; ``roofline`` rates the dominant kernel (average launch duration from
-HIP events recorded around each launch during the timed region) against the
-roofline that binds it; ``cpu_baseline`` is the fp64 oracle timed on the host.
+steps; ``roofline`` rates the dominant entry point's launches (one call's
+kernels; average duration from HIP events on the launch stream over the timed
+region) against the roofline that binds it; ``cpu_baseline`` is the fp64
+oracle timed on the host, and ``parity_vs_oracle`` compares the timed calls'
+GPU results with the oracle's on that sample.
 Other workloads (``--workload``) are the prefill reverse scan (8 x 4096 x 4096),
 the ragged serving step (reverse scan + block commit over 256 blocks of
 U{16..64} tokens at D = 4096), the ragged prefix-state prefill, and the fp32
@@ -173,7 +175,8 @@ class Workload:
         raise NotImplementedError
 
     step_calls: list = []   # per rotating set: the entry-point calls of one step
-    measure: list = []      # per timed kernel: label, calls, bytes, alu, tc per launch
+    measure: list = []      # per timed entry point: label, calls, bytes, alu, tc per launch
+    step_entries: list = [0]  # index into measure of each call of a step
     launches_per_step = 1
 
     def step(self, i, stream):
@@ -234,6 +237,7 @@ class Denoise(Workload):
                                     Cm=g["Cm"].clone(), A=g["A"], Dskip=g["Dskip"], res=x,
                                     s=float(self.gates[h]), out=out))
             self.step_calls.append(row)
+        self.step_entries = [0] * self.HOOKS
         self.measure = [dict(label="r2l_scan (one hook)", calls=[c for row in self.step_calls
                                                                for c in row],
                              bytes=self.bytes_per_launch, alu=self.alu_per_launch,
@@ -269,22 +273,6 @@ class Denoise(Workload):
 
     parity_spec = ("out", "bf16", 2e-2,
                    "out = x + s*y of all 7 hooks (first buffer set) vs the oracle's")
-
-
-def time_back_to_back(torch, calls, reps, per_ms):
-    """Average duration (ms) of `reps` launches queued back to back behind a
-    spinning kernel (so the host is far ahead of the GPU), from one pair of HIP
-    events recorded on the stream the launches run on."""
-    stream = torch.cuda.current_stream().cuda_stream
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(per_ms * (reps * 0.05 + 20.0)))
-    a.record()
-    for i in range(reps):
-        calls[i % len(calls)].launch(stream)
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps
 
 
 def sleep_cycles_per_ms(torch):
@@ -433,6 +421,7 @@ class RaggedServing(Workload):
                               Bm=gc["Bm"], A=gc["A"], cu_seqlens=cu, max_seqlen=int(lens.max()))
             self.calls.append((scan, commit))
         self.step_calls = [list(sc) for sc in self.calls]
+        self.step_entries = [0, 1]
         self.measure = [
             dict(label="r2l_scan (ragged blocks)", calls=[sc[0] for sc in self.calls],
                  bytes=self.bytes_per_launch, alu=self.alu_per_launch, tc=self.tc_per_launch),
@@ -520,6 +509,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget of the CPU baseline (0: skip it)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--queue-ahead", action="store_true",
+                    help="queue the timed launches behind a spinning kernel and time them with "
+                         "GPU events only (for kernel-trace profiles: no host gaps between "
+                         "dispatches); implies --no-graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -551,19 +544,70 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     wl.launches_per_step = len(wl.step_calls[0])
 
-    # (1) eager: every step launched from the host loop
+    # (1) eager: every step launched from the host loop. HIP events on the
+    # launch stream bracket the timed region; with more than one entry point
+    # per step, an event also precedes every call, so that each entry point's
+    # average duration comes from the timed region itself.
+    entries = wl.step_entries
+    per_call = len(wl.measure) > 1
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev_start, ev_end = ev(), ev()
+    call_ev = [ev() for _ in range(args.steps * len(entries))] if per_call else []
     for i in range(args.warmup):
         wl.step(i, stream)
     torch.cuda.synchronize()
+    if args.queue_ahead:
+        # hold the stream with a spinning kernel long enough for the host to
+        # queue every timed launch first (3x the warm-up's enqueue rate + 50 ms)
+        h0 = time.perf_counter()
+        wl.step(0, stream)
+        enqueue_ms = (time.perf_counter() - h0) * 1e3
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(sleep_cycles_per_ms(torch) * (3 * enqueue_ms * args.steps + 50)))
     t0 = time.perf_counter()
+    ev_start.record()
     for i in range(args.steps):
-        wl.step(i, stream)
+        for j, c in enumerate(wl.step_calls[i % len(wl.step_calls)]):
+            if per_call:
+                call_ev[i * len(entries) + j].record()
+            c.launch(stream)
+    ev_end.record()
     torch.cuda.synchronize()
     eager_s = (time.perf_counter() - t0) / args.steps
+    region_ms = ev_start.elapsed_time(ev_end)
+    timed = []
+    if per_call:
+        marks = call_ev + [ev_end]
+        dur = [marks[k].elapsed_time(marks[k + 1]) for k in range(len(call_ev))]
+        for e, m in enumerate(wl.measure):
+            mine = [d for k, d in enumerate(dur) if entries[k % len(entries)] == e]
+            timed.append(dict(m, ms=sum(mine) / len(mine), reps=len(mine)))
+        n = len(entries)
+        step_ms = [sum(dur[i * n:(i + 1) * n]) for i in range(args.steps)]
+        spread_how = "per-step sums of the per-call events of the timed region"
+    elif args.queue_ahead:
+        launches = args.steps * len(entries)
+        timed.append(dict(wl.measure[0], ms=region_ms / launches, reps=launches))
+        step_ms = [region_ms / args.steps]
+        spread_how = "not measured (queued-ahead run)"
+    else:
+        launches = args.steps * len(entries)
+        timed.append(dict(wl.measure[0], ms=region_ms / launches, reps=launches))
+        # spread: a second, instrumented pass with one event per step
+        marks = [ev() for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        marks[0].record()
+        for i in range(args.steps):
+            wl.step(i, stream)
+            marks[i + 1].record()
+        torch.cuda.synchronize()
+        step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+        spread_how = "a second pass of the same steps with one event after each step"
+    step_spread = {k: round(v * 1e3, 3) for k, v in percentiles(step_ms).items()}
 
     # (2) the step captured once per rotating set in a hipGraph and replayed
     graph_s = None
-    if not args.no_graph and wl.launches_per_step > 1:
+    if not (args.no_graph or args.queue_ahead) and wl.launches_per_step > 1:
         graphs = []
         s = torch.cuda.Stream()
         with torch.cuda.stream(s):
@@ -582,22 +626,11 @@ def main():
         torch.cuda.synchronize()
         graph_s = (time.perf_counter() - t0) / args.steps
 
-    # (3) kernel durations: each timed entry point launched back to back, in
-    # several rounds (the average over all launches, and the spread of the
-    # per-round averages)
-    per_ms = sleep_cycles_per_ms(torch)
-    timed = []
-    rounds = 9
-    for m in wl.measure:
-        per_round = max(len(m["calls"]), min(args.steps * wl.launches_per_step, 2000) // rounds)
-        ms_rounds = [time_back_to_back(torch, m["calls"], per_round, per_ms)
-                     for _ in range(rounds)]
-        timed.append(dict(m, ms=sum(ms_rounds) / rounds, reps=per_round * rounds,
-                          spread_us={k: round(v * 1e3, 3)
-                                     for k, v in percentiles(ms_rounds).items()}))
     copy_gbs = copy_bandwidth_gbs(torch)
 
     step_s = min(eager_s, graph_s) if graph_s else eager_s
+    if args.queue_ahead:   # the host clock also ran over the spin: GPU time only
+        step_s = region_ms * 1e-3 / args.steps
     value = wl.tc_per_step / step_s
 
     def rooflines(m):
@@ -615,7 +648,6 @@ def main():
     for m in timed:
         bind_, other_ = rooflines(m)
         kernels.append({"entry": m["label"], "avg_launch_us": round(m["ms"] * 1e3, 3),
-                        "launch_us_spread_over_rounds": m["spread_us"],
                         "launches_timed": m["reps"], "bytes_per_launch": m["bytes"],
                         "tc_per_launch": m["tc"], "tc_per_s": m["tc"] / (m["ms"] * 1e-3),
                         "roofline": bind_, "roofline_other": other_})
@@ -657,7 +689,11 @@ def main():
                       "lane_ops_per_tc_state_only": alu_ops_per_tc(False, False),
                       "trans_slots": TRANS_SLOTS},
         "source_sha": kernel_sha(),
+        "timing": ("queued ahead of a spinning kernel, GPU events" if args.queue_ahead
+                   else "host clock around the steps (synchronised); GPU events per entry point"),
         "ms_per_step_eager": eager_s * 1e3,
+        "ms_per_step_eager_gpu_events": region_ms / args.steps,
+        "step_us_spread": dict(step_spread, how=spread_how),
         "ms_per_step_graph": graph_s * 1e3 if graph_s else None,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
