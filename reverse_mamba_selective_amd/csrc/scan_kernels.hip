@@ -287,12 +287,19 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
 
     // One visited position k: consume ring slot `slot`, refill it with the
     // position PF ahead, update the state and store the output row.
+    // Delta of the next visited position is computed one token ahead, off
+    // the critical path of the current token (its dt is already in the ring).
+    float dnext = 0.0f;
+    auto delta_of = [&](R dr) {
+        const float dv = E::widen(dr);
+        return softplus_on ? softplus(dv) : dv;
+    };
     auto token = [&](int k, const float *bcrow, int slot) {
-        const R xr = xq[slot], dr = dq[slot], rr = rq[slot];
+        const R xr = xq[slot], rr = rq[slot];
+        const float delta = dnext;
+        dnext = delta_of(dq[(slot + 1) % PF]);
         load_pos(prefetch_pos(k + PF, ntok), slot);
         const float xv = E::widen(xr);
-        const float dv = E::widen(dr);
-        const float delta = softplus_on ? softplus(dv) : dv;
         if constexpr (!READOUT) dsum += delta;
         const float dx = delta * xv;
         const float *row = bcrow + sub * NS;
@@ -340,6 +347,7 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
 #pragma unroll
         for (int j = 0; j < PF; ++j) load_pos(prefetch_pos(j, ntok), j);
         stage_store(0);
+        dnext = delta_of(dq[0]);
     }
     __syncthreads();
 
