@@ -73,6 +73,10 @@
  *           inside kernels surface at the caller's next synchronisation.
  *  NaN/Inf  Propagate; nothing is trapped. With s == 0 the output is the
  *           residual bit for bit, whatever y holds.
+ *  s == 0   (with res given) No readout runs: out receives a copy of res (no
+ *           launch at all when out is res itself), and the state is still
+ *           scanned when h_out is given (bit-identical to the state of the
+ *           same call with s != 0).
  */
 #ifndef R2L_SCAN_H_
 #define R2L_SCAN_H_

@@ -245,6 +245,18 @@ void check_carry(Checker &ck, const Launch &l, const int32_t *cu_host) {
     }
 }
 
+void check_copy(Checker &ck, const Launch &l) {
+    const CopyParams &p = l.copy;
+    const int64_t es = l.dtype == R2L_DTYPE_BF16 ? 2 : 4;
+    const Region *rs = ck.region_of(p.src), *rd = ck.region_of(p.dst);
+    for (int64_t r = 0; r < p.rows && ck.ok(); ++r) {
+        const CopyRow cr = copy_row(p, r);
+        // columns 0 .. D-1 of the row (one thread per column)
+        ck.access("res (copied)", rs, U(p.src) + cr.src * es, p.D * es);
+        ck.access("out (copy)", rd, U(p.dst) + cr.dst * es, p.D * es);
+    }
+}
+
 }  // namespace
 
 r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const int32_t *cu_host,
@@ -276,8 +288,8 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
     if (pl.chunked) {
         const char *ws = static_cast<const char *>(a->workspace);
         add("workspace Q", ws, pl.off_S);
-        add("workspace S", ws + pl.off_S, (wants_readout(op, a) ? pl.off_H : pl.ws_bytes) - pl.off_S);
-        if (wants_readout(op, a)) add("workspace H", ws + pl.off_H, pl.ws_bytes - pl.off_H);
+        add("workspace S", ws + pl.off_S, (runs_readout(op, a) ? pl.off_H : pl.ws_bytes) - pl.off_S);
+        if (runs_readout(op, a)) add("workspace H", ws + pl.off_H, pl.ws_bytes - pl.off_H);
     }
     Checker ck(std::move(regs), rep);
     if (pl.chunked) ck.set_workspace(a->workspace, pl.ws_bytes);
@@ -288,9 +300,11 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
         if (ls[i].kind == Launch::Segment) {
             if (ls[i].seg.bc_vec) ++rep->vector_staging;
             check_segment(ck, ls[i], cu_host);
-        }
-        else
+        } else if (ls[i].kind == Launch::Copy) {
+            check_copy(ck, ls[i]);
+        } else {
             check_carry(ck, ls[i], cu_host);
+        }
     }
     return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;
 }

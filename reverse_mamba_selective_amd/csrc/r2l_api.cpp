@@ -261,11 +261,22 @@ r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
     const int n = r2l::build_launches(op, a, pl, ls);
     for (int i = 0; i < n; ++i) {
         const Launch &l = ls[i];
-        const hipError_t e =
-            l.kind == Launch::Segment
-                ? r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream)
-                : r2l::launch_carry(l.carry, stream);
-        st = hip_status(e, l.kind == Launch::Segment ? "segment scan launch" : "carry launch");
+        hipError_t e = hipSuccess;
+        const char *what = "segment scan launch";
+        switch (l.kind) {
+            case Launch::Segment:
+                e = r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream);
+                break;
+            case Launch::Carry:
+                e = r2l::launch_carry(l.carry, stream);
+                what = "carry launch";
+                break;
+            case Launch::Copy:
+                e = r2l::launch_copy(l.dtype, l.copy, stream);
+                what = "residual copy launch";
+                break;
+        }
+        st = hip_status(e, what);
         if (st != R2L_OK) return st;
     }
     return ok();
@@ -339,7 +350,8 @@ r2l_status r2l_describe_plan(int32_t op, const r2l_scan_args *a, r2l_plan_info *
     info->chunk_tokens = pl.chunk_len;
     info->chunks = pl.nchunks;
     info->workspace_bytes = static_cast<int64_t>(pl.ws_bytes);
-    info->launches = a->batch == 0 ? 0 : (pl.chunked ? (wants_readout(o, a) ? 3 : 2) : 1);
+    Launch ls[3];
+    info->launches = r2l::build_launches(o, a, pl, ls);
     return ok();
 }
 

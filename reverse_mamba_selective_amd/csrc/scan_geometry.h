@@ -196,6 +196,22 @@ R2L_HD CarryGeom carry_geom(int64_t D, int64_t bx, int64_t by, int tid) {
     return g;
 }
 
+// Row copy: kCopyThreads columns per block along x, rows along y (looping
+// when there are more rows than kCopyMaxRowBlocks).
+constexpr int kCopyThreads = 256;
+constexpr int64_t kCopyMaxRowBlocks = 65535;
+struct CopyRow {
+    int64_t src, dst;   // element offsets of the row's first column
+};
+
+R2L_HD CopyRow copy_row(const CopyParams &p, int64_t r) {
+    if (p.seqlen > 0) {
+        const int64_t b = r / p.seqlen, l = r % p.seqlen;
+        return CopyRow{b * p.sbs + l * p.ss, b * p.dbs + l * p.ds};
+    }
+    return CopyRow{r * p.ss, r * p.ds};
+}
+
 R2L_HD int carry_chunks(int64_t len, int32_t chunk_len, int32_t nchunks) {
     const int64_t nc = (len + chunk_len - 1) / chunk_len;
     return static_cast<int>(nc < nchunks ? nc : nchunks);

@@ -76,9 +76,22 @@ struct CarryParams {
     int32_t c0_seeded;           // Q of chunk 0 is the true state after it (hin is not read)
 };
 
+// Copies D elements of each token row from src to dst (a call with s == 0
+// writes the residual itself). Dense layout (seqlen > 0): row r is token
+// r % seqlen of sequence r / seqlen, at b * batch stride + l * stride;
+// packed layout (seqlen == 0): row r at r * stride. Strides in elements.
+struct CopyParams {
+    int64_t rows;
+    int64_t seqlen;
+    int64_t D;
+    const void *src; int64_t ss, sbs;
+    void *dst; int64_t ds, dbs;
+};
+
 // dtype: 0 fp32, 1 bf16. G in {1, 2, 4}. mode: kMode*.
 hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode,
                                const SegParams &p, hipStream_t stream);
 hipError_t launch_carry(const CarryParams &p, hipStream_t stream);
+hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream);
 
 }  // namespace r2l

@@ -22,9 +22,10 @@
 //  * Softplus and the decay are computed in-kernel with the hardware base-2
 //    exponential and logarithm (v_exp_f32 / v_log_f32), log2(e) being folded
 //    into A once per lane.
-//  * The gated residual (res + s*y, or the raw residual bits when s == 0) is
-//    fused into the store; bf16 outputs use the hardware round-to-nearest-even
-//    conversion.
+//  * The gated residual res + s*y is fused into the store; bf16 outputs use
+//    the hardware round-to-nearest-even conversion. (With s == 0 the output is
+//    the residual bit for bit: the planner copies it, or leaves it in place,
+//    and runs no readout.)
 //  * Long sequences can be cut into chunks scanned from a zero state in
 //    parallel; the carry kernel then chains the chunk results. Because the
 //    recurrence is linear, a chunk's contribution to the state after it is its
@@ -190,7 +191,7 @@ __device__ __forceinline__ float group_sum(float y) {
 // written to the other half of a double-buffered LDS area at its end (one
 // barrier per tile). Row addresses are uniform (scalar) and the lane adds a
 // 32-bit channel offset.
-template <bool REV, typename T, int G, int MODE>
+template <bool REV, typename T, int G, int MODE, bool SP>
 __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, const BlockGeom &bg,
                                              const SeqGeom &sq, const SegGeom &sg,
                                              const float *hin) {
@@ -226,7 +227,6 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
         for (int j = 0; j < NS; ++j) h[j] = 0.0f;
     }
     const float dskip = (READOUT && p.Dskip) ? p.Dskip[dl] : 0.0f;
-    const bool softplus_on = p.softplus != 0;
     float dsum = 0.0f;
 
     // Per-token rows go through raw buffer resources based at the sequence's
@@ -255,8 +255,7 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     const uint32_t bcrb = static_cast<uint32_t>(stage_c ? p.Cs : p.Bs) * es;
     const uint32_t bccol = static_cast<uint32_t>(ss.col0) * es;
     const bool bc_vec = p.bc_vec != 0;
-    const float gate = p.s;
-    const bool gate_zero = gate == 0.0f;
+    const float gate = p.s;   // never 0 in the residual modes
 
     // ---- register ring of per-token inputs (slot = position % PF)
     R xq[PF], dq[PF], rq[PF];
@@ -292,7 +291,10 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     float dnext = 0.0f;
     auto delta_of = [&](R dr) {
         const float dv = E::widen(dr);
-        return softplus_on ? softplus(dv) : dv;
+        if constexpr (SP)
+            return softplus(dv);
+        else
+            return dv;
     };
     auto token = [&](int k, const float *bcrow, int slot) {
         const R xr = xq[slot], rr = rq[slot];
@@ -328,8 +330,7 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
                 o = E::pack(y);
             } else {
                 const R rbits = MODE == kModeRes ? rr : xr;
-                const R gated = E::pack(fmaf(gate, y, E::widen(rbits)));
-                o = gate_zero ? rbits : gated;   // s == 0: the residual bits themselves
+                o = E::pack(fmaf(gate, y, E::widen(rbits)));
             }
             const uint32_t orow = static_cast<uint32_t>(seg_row(sg, k));
             E::bstore(o, ro_, doff, orow * orb);
@@ -383,7 +384,7 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
 // One workgroup per (sequence b, chunk c, channel tile). Chunk passes of
 // readout plans (split_c0) run the readout on chunk 0, which starts from the
 // call's own initial state, and the state-only scan from zero on the others.
-template <bool REV, typename T, int G, int MODE>
+template <bool REV, typename T, int G, int MODE, bool SP>
 __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     constexpr int NBC_MAX = MODE != kModeState ? 2 * kN : kN;
     __shared__ __align__(16) float lds[2 * kTile * NBC_MAX];
@@ -400,11 +401,11 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     const float *hin = segment_hin(p, b, c);
     if constexpr (MODE != kModeState) {
         if (p.split_c0 && c > 0) {
-            scan_segment<REV, T, G, kModeState>(p, lds, bg, sq, sg, hin);
+            scan_segment<REV, T, G, kModeState, SP>(p, lds, bg, sq, sg, hin);
             return;
         }
     }
-    scan_segment<REV, T, G, MODE>(p, lds, bg, sq, sg, hin);
+    scan_segment<REV, T, G, MODE, SP>(p, lds, bg, sq, sg, hin);
 }
 
 // ---- the carry over chunks -------------------------------------------------
@@ -431,21 +432,34 @@ __global__ __launch_bounds__(kCarryThreads) void carry_kernel(const CarryParams 
     if (p.hout) p.hout[(g.b * p.D + g.d) * kN + g.n] = H;
 }
 
-template <bool REV, typename T, int MODE>
+// ---- copy of token rows (the output of a call with s == 0 is the residual) -
+template <typename R>
+__global__ __launch_bounds__(kCopyThreads) void copy_rows_kernel(const CopyParams p) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
+    if (col >= p.D) return;
+    const R *src = static_cast<const R *>(p.src);
+    R *dst = static_cast<R *>(p.dst);
+    for (int64_t r = blockIdx.y; r < p.rows; r += gridDim.y) {
+        const CopyRow cr = copy_row(p, r);
+        dst[cr.dst + col] = src[cr.src + col];
+    }
+}
+
+template <bool REV, typename T, int MODE, bool SP>
 hipError_t launch_g(int G, const SegParams &p, hipStream_t stream) {
     const int64_t grid = padded_grid(p.nblocks);
     switch (G) {
         case 1:
-            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 1, MODE>), dim3(grid), dim3(kWG), 0,
-                               stream, p);
+            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 1, MODE, SP>), dim3(grid), dim3(kWG),
+                               0, stream, p);
             break;
         case 2:
-            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 2, MODE>), dim3(grid), dim3(kWG), 0,
-                               stream, p);
+            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 2, MODE, SP>), dim3(grid), dim3(kWG),
+                               0, stream, p);
             break;
         case 4:
-            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 4, MODE>), dim3(grid), dim3(kWG), 0,
-                               stream, p);
+            hipLaunchKernelGGL((segment_scan_kernel<REV, T, 4, MODE, SP>), dim3(grid), dim3(kWG),
+                               0, stream, p);
             break;
         default:
             return hipErrorInvalidValue;
@@ -453,15 +467,21 @@ hipError_t launch_g(int G, const SegParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <bool REV, typename T>
+template <bool REV, typename T, bool SP>
 hipError_t launch_m(int mode, int G, const SegParams &p, hipStream_t stream) {
     switch (mode) {
-        case kModeState: return launch_g<REV, T, kModeState>(G, p, stream);
-        case kModeY: return launch_g<REV, T, kModeY>(G, p, stream);
-        case kModeResX: return launch_g<REV, T, kModeResX>(G, p, stream);
-        case kModeRes: return launch_g<REV, T, kModeRes>(G, p, stream);
+        case kModeState: return launch_g<REV, T, kModeState, SP>(G, p, stream);
+        case kModeY: return launch_g<REV, T, kModeY, SP>(G, p, stream);
+        case kModeResX: return launch_g<REV, T, kModeResX, SP>(G, p, stream);
+        case kModeRes: return launch_g<REV, T, kModeRes, SP>(G, p, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <bool REV, typename T>
+hipError_t launch_s(int mode, int G, const SegParams &p, hipStream_t stream) {
+    return p.softplus ? launch_m<REV, T, true>(mode, G, p, stream)
+                      : launch_m<REV, T, false>(mode, G, p, stream);
 }
 
 }  // namespace
@@ -469,10 +489,21 @@ hipError_t launch_m(int mode, int G, const SegParams &p, hipStream_t stream) {
 hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode, const SegParams &p,
                                hipStream_t stream) {
     if (reverse)
-        return dtype == 1 ? launch_m<true, uint16_t>(mode, G, p, stream)
-                          : launch_m<true, float>(mode, G, p, stream);
-    return dtype == 1 ? launch_m<false, uint16_t>(mode, G, p, stream)
-                      : launch_m<false, float>(mode, G, p, stream);
+        return dtype == 1 ? launch_s<true, uint16_t>(mode, G, p, stream)
+                          : launch_s<true, float>(mode, G, p, stream);
+    return dtype == 1 ? launch_s<false, uint16_t>(mode, G, p, stream)
+                      : launch_s<false, float>(mode, G, p, stream);
+}
+
+hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream) {
+    if (p.rows <= 0 || p.D <= 0) return hipSuccess;
+    const dim3 grid(static_cast<uint32_t>((p.D + kCopyThreads - 1) / kCopyThreads),
+                    static_cast<uint32_t>(p.rows < kCopyMaxRowBlocks ? p.rows : kCopyMaxRowBlocks));
+    if (dtype == 1)
+        hipLaunchKernelGGL(copy_rows_kernel<uint16_t>, grid, dim3(kCopyThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, grid, dim3(kCopyThreads), 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_carry(const CarryParams &p, hipStream_t stream) {

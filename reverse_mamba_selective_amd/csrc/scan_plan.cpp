@@ -85,9 +85,11 @@ Plan make_plan(Op op, const r2l_scan_args *a) {
     const int64_t channels = a->batch * a->dim;
     const int64_t maxlen = max_len_of(a);
     pl.G = a->state_split ? a->state_split : 1;
-    const bool readout = wants_readout(op, a);
+    const bool readout = runs_readout(op, a);
     int64_t chunk = 0;
-    if (a->chunk_tokens > 0) {
+    if (!runs_scan(op, a)) {
+        // nothing is scanned: no chunks, no workspace
+    } else if (a->chunk_tokens > 0) {
         chunk = a->chunk_tokens;
     } else if (a->chunk_tokens == 0 && maxlen > 0) {
         const int64_t lanes = std::max<int64_t>(channels * pl.G, 1);
@@ -119,10 +121,44 @@ Plan make_plan(Op op, const r2l_scan_args *a) {
     return pl;
 }
 
+namespace {
+
+// The residual copied to out when the gate is closed (nothing when out is
+// the residual itself).
+int copy_launch(const r2l_scan_args *a, Launch *out) {
+    const int64_t rbs = eff_bstride(a, a->res_batch_stride, a->res_stride);
+    const int64_t obs = eff_bstride(a, a->out_batch_stride, a->out_stride);
+    if (a->out == a->res && a->out_stride == a->res_stride && obs == rbs) return 0;
+    if (tokens_of(a) == 0) return 0;
+    Launch l{};
+    l.kind = Launch::Copy;
+    l.dtype = a->dtype;
+    l.copy.rows = tokens_of(a);
+    l.copy.seqlen = is_ragged(a) ? 0 : a->seqlen;
+    l.copy.D = a->dim;
+    l.copy.src = a->res; l.copy.ss = a->res_stride; l.copy.sbs = rbs;
+    l.copy.dst = a->out; l.copy.ds = a->out_stride; l.copy.dbs = obs;
+    *out = l;
+    return 1;
+}
+
+int build_scan_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3]);
+
+}  // namespace
+
 int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3]) {
     if (a->batch == 0) return 0;
+    int n = runs_scan(op, a) ? build_scan_launches(op, a, pl, out) : 0;
+    // after the scan, which may read x when out is x
+    if (gate_closed(op, a)) n += copy_launch(a, out + n);
+    return n;
+}
+
+namespace {
+
+int build_scan_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3]) {
     const bool reverse = (op == Op::Scan);
-    const bool readout = wants_readout(op, a);
+    const bool readout = runs_readout(op, a);
     const int64_t DN = a->dim * kN;
     // block_commit_state reads the state it updates from h_out
     const float *h_init = (op == Op::Commit) ? a->h_out : a->h_in;
@@ -202,4 +238,5 @@ int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3])
     return 3;
 }
 
+}  // namespace
 }  // namespace r2l

@@ -24,13 +24,14 @@ struct Plan {
 };
 
 struct Launch {
-    enum Kind { Segment, Carry } kind;
+    enum Kind { Segment, Carry, Copy } kind;
     bool reverse;
     int dtype;
     int G;
     int mode;                // kMode* (segment launches)
     SegParams seg;
     CarryParams carry;
+    CopyParams copy;
 };
 
 inline bool is_ragged(const r2l_scan_args *a) { return a->cu_seqlens != nullptr; }
@@ -42,6 +43,19 @@ inline int64_t max_len_of(const r2l_scan_args *a) {
 }
 inline bool wants_readout(Op op, const r2l_scan_args *a) {
     return op == Op::Scan || a->out != nullptr;
+}
+// A readout call whose gate s is 0 outputs its residual bit for bit: no
+// readout runs; the residual is copied to out (or already is out), and the
+// state is scanned only when h_out is wanted.
+inline bool gate_closed(Op op, const r2l_scan_args *a) {
+    return wants_readout(op, a) && a->res != nullptr && a->s == 0.0f;
+}
+inline bool runs_readout(Op op, const r2l_scan_args *a) {
+    return wants_readout(op, a) && !gate_closed(op, a);
+}
+// Whether any segment scan runs at all.
+inline bool runs_scan(Op op, const r2l_scan_args *a) {
+    return !gate_closed(op, a) || a->h_out != nullptr;
 }
 inline int64_t elem_size(int32_t dtype) { return dtype == R2L_DTYPE_BF16 ? 2 : 4; }
 

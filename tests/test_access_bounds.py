@@ -35,7 +35,7 @@ class FakeHeap:
 
 def make_args(op, *, dtype="bf16", D=64, batch=None, seqlen=None, lengths=None, res="none",
               h_in=False, h_out=False, out=True, chunk=-1, split=0, pad_row=0, pad_batch=0,
-              bc_shift=0):
+              bc_shift=0, s=0.05):
     """A call with every buffer sized exactly as the layout says. bc_shift
     starts Bm and Cm that many elements into their allocation (which grows by
     as much), breaking the alignment of the staging's vector loads."""
@@ -88,7 +88,7 @@ def make_args(op, *, dtype="bf16", D=64, batch=None, seqlen=None, lengths=None, 
         elif res == "inplace":  # out is x is res
             a.res, a.res_stride, a.res_batch_stride = a.x, a.x_stride, a.x_batch_stride
             a.out, a.out_stride, a.out_batch_stride = a.x, a.x_stride, a.x_batch_stride
-        a.s = 0.05
+        a.s = s
     a.A = heap.alloc(4 * D * N)
     if h_in and op != "commit":
         a.h_in = heap.alloc(4 * a.batch * D * N)
@@ -154,6 +154,7 @@ def test_random_plans():
                       pad_batch=rng.choice([0, 0, 24]))
         if op == "scan":
             kw["res"] = rng.choice(["none", "x", "sep", "inplace"])
+            kw["s"] = rng.choice([0.05, 0.05, 0.0])
         else:
             kw["out"] = rng.random() < 0.4
         check(op, **kw)
@@ -180,6 +181,29 @@ def test_staging_vector_choice(dtype, op):
     dense = dict(dtype=dtype, batch=3, seqlen=65, D=64, chunk=32, h_out=True, out=op == "scan")
     assert check(op, **dense).vector_staging == launches - 1
     assert check(op, pad_batch=1, **dense).vector_staging == 0
+
+
+# ---- s == 0: the output is the residual; no readout runs -------------------
+@pytest.mark.parametrize("layout", [
+    dict(lengths=[5, 0, 1, 64, 17, 300]),
+    dict(batch=3, seqlen=70, pad_row=8, pad_batch=40),
+    dict(batch=2, seqlen=0)])
+def test_gate_closed_plans(layout):
+    kw = dict(D=96, s=0.0, **layout)
+    tok = sum(layout.get("lengths", [])) or layout.get("batch", 0) * layout.get("seqlen", 0)
+    copies = 1 if tok else 0
+    # out == x == res: nothing to do at all
+    assert check("scan", res="inplace", **kw).launches == 0
+    # a new out: one row copy of the residual (x or a separate tensor)
+    for res in ("x", "sep"):
+        assert check("scan", res=res, **kw).launches == copies
+        # the state is still scanned when h_out is wanted (state only), before the copy
+        assert check("scan", res=res, h_out=True, h_in=True, **kw).launches == 1 + copies
+        rep = check("scan", res=res, h_out=True, chunk=32, **kw)
+        assert rep.launches == (2 if tok else 1) + copies
+    assert check("scan", res="inplace", h_out=True, **kw).launches == 1
+    a, _ = make_args("scan", res="x", **kw)
+    assert _abi.workspace_size(_abi.R2L_OP_SCAN, a) == 0
 
 
 # ---- the benchmarked shapes, at full size --------------------------------------

@@ -206,6 +206,31 @@ def test_gate_zero_returns_residual_bits(gpu, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gate_zero_state_and_strided_copy(gpu, dtype):
+    """s == 0 runs no readout: h_out comes from the state-only scan and equals,
+    bit for bit, the state of the same call with the gate open; the residual
+    is copied row by row into a strided out, leaving the padding alone."""
+    inp = synth.scan_inputs(21, [40] * 3, D=72, dtype=dtype)
+    g = on_gpu(inp)
+    h0 = dev32(synth.initial_state(21, 3, 72, 16))
+    h_open, h_closed = torch.empty_like(h0), torch.empty_like(h0)
+    r2l.r2l_scan(**scan_kw(g), res=g["x"], s=0.5, h_in=h0, h_out=h_open, chunk_tokens=-1)
+    out = r2l.r2l_scan(**scan_kw(g), res=g["x"], s=0.0, h_in=h0, h_out=h_closed, chunk_tokens=-1)
+    assert np.array_equal(bits(h_closed), bits(h_open))
+    assert np.array_equal(bits(out), bits(g["x"]))
+    check_state(h_closed, oracle_scan(inp, h_in=synth.initial_state(21, 3, 72, 16),
+                                      want_h_out=True)["h_out"])
+    # strided residual and strided out (padded rows), dense batches
+    wide_r = torch.full((3, 40, 100), 3.0, dtype=g["x"].dtype, device="cuda")
+    wide_r[:, :, 10:82] = g["x"]
+    wide_o = torch.full((3, 40, 90), 7.0, dtype=g["x"].dtype, device="cuda")
+    r2l.r2l_scan(**scan_kw(g), res=wide_r[:, :, 10:82], s=0.0, out=wide_o[:, :, 5:77])
+    assert np.array_equal(bits(wide_o[:, :, 5:77].contiguous()), bits(g["x"]))
+    assert (wide_o[:, :, :5] == 7.0).all() and (wide_o[:, :, 77:] == 7.0).all()
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("split", [1, 4])
 def test_reverse_equals_forward_on_flipped_input(gpu, dtype, split):
     inp = synth.scan_inputs(12, [75] * 3, D=130, dtype=dtype)
@@ -300,7 +325,7 @@ def test_chunked_plans_carry_state(gpu, dtype, chunk):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("res", ["none", "x", "separate", "x_s0", "in_place"])
+@pytest.mark.parametrize("res", ["none", "x", "separate", "x_s0", "in_place", "in_place_s0"])
 def test_chunked_readout_plans(gpu, dtype, res):
     """Chunked readout plans write chunk 0 in the chunk pass (from the call's
     initial state) and the other chunks in the readout pass; without h_out the
@@ -312,7 +337,7 @@ def test_chunked_readout_plans(gpu, dtype, res):
     inp = synth.scan_inputs(19, lengths, D=D, dtype=dtype, dt_mean=-4.0)
     g = on_gpu(inp, dense=False)
     h0 = synth.initial_state(19, len(lengths), D, 16)
-    s = 0.0 if res == "x_s0" else 0.3
+    s = 0.0 if res.endswith("_s0") else 0.3
     res_np = {"none": None, "separate": synth.scan_inputs(20, lengths, D=D, dtype=dtype).x}.get(
         res, inp.x)
     for with_hin in (False, True):
@@ -327,7 +352,7 @@ def test_chunked_readout_plans(gpu, dtype, res):
                 kw["h_out"] = torch.full((len(lengths), D, 16), float("nan"), device="cuda")
             if res_np is not None:
                 kw.update(res=x if res != "separate" else dev(res_np, dtype), s=s)
-            if res == "in_place":
+            if res.startswith("in_place"):
                 kw["out"] = x
             out = r2l.r2l_scan(**kw)
             what = "%s h_in=%d h_out=%d" % (res, with_hin, with_hout)
@@ -340,7 +365,10 @@ def test_chunked_readout_plans(gpu, dtype, res):
             if with_hout:
                 check_state(kw["h_out"], ref["h_out"], what)
             plan = r2l.bind("r2l_scan", **{**kw, "out": out}).plan()
-            assert plan["chunked"] and plan["launches"] == 3
+            if s != 0.0:
+                assert plan["chunked"] and plan["launches"] == 3
+            else:   # no readout: the state-only plan when h_out is wanted, then the copy
+                assert plan["launches"] == (2 if with_hout else 0) + (res == "x_s0")
     torch.cuda.synchronize()
 
 
