@@ -203,6 +203,8 @@ class Denoise(Workload):
     """7 hooked reverse scans of one denoising step, 64 x 32 x 2048, bf16."""
     name = "denoise_step_bf16_b64_blk32_D2048_N16_7hooks"
     HOOKS, B, L, D = 7, 64, 32, 2048
+    reverse = True
+    entry = "r2l_scan"
 
     def setup(self, torch, r2l):
         import synth
@@ -233,13 +235,13 @@ class Denoise(Workload):
                 out = torch.empty_like(x)
                 if r == 0:
                     self.outs0.append(out)
-                row.append(r2l.bind("r2l_scan", x=x, dt=g["dt"].clone(), Bm=g["Bm"].clone(),
+                row.append(r2l.bind(self.entry, x=x, dt=g["dt"].clone(), Bm=g["Bm"].clone(),
                                     Cm=g["Cm"].clone(), A=g["A"], Dskip=g["Dskip"], res=x,
                                     s=float(self.gates[h]), out=out))
             self.step_calls.append(row)
         self.step_entries = [0] * self.HOOKS
-        self.measure = [dict(label="r2l_scan (one hook)", calls=[c for row in self.step_calls
-                                                               for c in row],
+        self.measure = [dict(label="%s (one hook)" % self.entry,
+                             calls=[c for row in self.step_calls for c in row],
                              bytes=self.bytes_per_launch, alu=self.alu_per_launch,
                              tc=self.tc_per_launch)]
         self.config = {"workload": self.name, "batch": self.B, "block_tokens": self.L,
@@ -254,9 +256,11 @@ class Denoise(Workload):
         while secs < budget_s and reps < 200:
             for h, inp in enumerate(self.inputs):
                 t = {}
-                r = oracle.r2l_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, res=inp.x,
-                                    s=float(self.gates[h]), seq_offsets=inp.offsets, timing=t,
-                                    want_y=False, nthreads=nthreads)
+                r = oracle.selective_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip,
+                                          reverse=self.reverse, res=inp.x,
+                                          s=float(self.gates[h]), seq_offsets=inp.offsets,
+                                          timing=t, want_y=False, want_out=True,
+                                          nthreads=nthreads)
                 if parity is not None and reps == 0:
                     parity.add(self.outs0[h].float().cpu().numpy().reshape(r["out"].shape),
                                r["out"])
@@ -273,6 +277,14 @@ class Denoise(Workload):
 
     parity_spec = ("out", "bf16", 2e-2,
                    "out = x + s*y of all 7 hooks (first buffer set) vs the oracle's")
+
+
+class DenoiseL2R(Denoise):
+    """The L2R-Mamba ablation of the same step: 7 hooked forward scans with readout and
+    gated residual (prefix_scan_state with Cm, res and out), 64 x 32 x 2048, bf16."""
+    name = "l2r_ablation_step_bf16_b64_blk32_D2048_N16_7hooks"
+    reverse = False
+    entry = "prefix_scan_state"
 
 
 def sleep_cycles_per_ms(torch):
@@ -497,7 +509,7 @@ class RaggedPrefix(Workload):
 
 
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
-             "prefix": RaggedPrefix}
+             "prefix": RaggedPrefix, "l2r": DenoiseL2R}
 
 
 def main():
@@ -675,7 +687,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.config.get("in_dtype", "bf16") + " in, f32 compute",
+        "dtype": "f32",   # arithmetic type (storage type: config.in_dtype)
         "data": "synthetic (seeded)",
         "config": wl.config,
         "roofline": binding,

@@ -206,6 +206,18 @@ def test_gate_closed_plans(layout):
     assert _abi.workspace_size(_abi.R2L_OP_SCAN, a) == 0
 
 
+# ---- the largest shapes the GPU tests run --------------------------------------
+def test_maximum_size_shapes():
+    D = 65535 * 16
+    check("scan", lengths=[3, 5], D=D, dtype="f32", h_in=True, h_out=True, chunk=0)
+    check("prefix", lengths=[3, 5], D=D, dtype="f32", h_in=True, out=False, chunk=2)
+    rep = check("scan", lengths=[1 << 20], D=16, h_out=True, chunk=0)
+    assert rep.launches == 3
+    check("prefix", lengths=[1 << 20], D=16, out=False, chunk=0)
+    lengths = np.random.default_rng(25).integers(0, 4, size=60_000)
+    check("scan", lengths=lengths, D=16, h_out=True, chunk=0, dtype="f32")
+
+
 # ---- the benchmarked shapes, at full size --------------------------------------
 # (chunk=0: the plan the library picks, as the benchmark runs it)
 def test_denoise_hook_shape():

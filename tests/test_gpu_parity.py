@@ -372,6 +372,52 @@ def test_chunked_readout_plans(gpu, dtype, res):
     torch.cuda.synchronize()
 
 
+def test_graph_replays_match_eager(gpu):
+    """Calls captured once in a hipGraph (the benchmark replays its steps this
+    way) give the eager results on every replay, with eager work between the
+    replays: a chunked plan (chunk pass, carry, readout pass through the bound
+    workspace), a gated in-place hook and an s == 0 residual copy."""
+    lengths = [300, 17, 0, 129]
+    inp = synth.scan_inputs(22, lengths, D=96, dtype="bf16", dt_mean=-4.0)
+    g = on_gpu(inp, dense=False)
+    h0 = dev32(synth.initial_state(22, len(lengths), 96, 16))
+    x_hook = g["x"].clone()
+    res = torch.randn_like(g["x"])
+    bufs = {"y": torch.empty_like(g["x"]), "h": torch.empty_like(h0),
+            "copy": torch.empty_like(g["x"])}
+    calls = [r2l.bind("r2l_scan", **scan_kw(g), h_in=h0, h_out=bufs["h"], out=bufs["y"],
+                      chunk_tokens=64),
+             r2l.bind("r2l_scan", **{**scan_kw(g), "x": x_hook}, res=x_hook, s=0.3, out=x_hook),
+             r2l.bind("r2l_scan", **scan_kw(g), res=res, s=0.0, out=bufs["copy"])]
+    assert calls[0].plan()["launches"] == 3 and calls[2].plan()["launches"] == 1
+    x_start = x_hook.clone()
+    for c in calls:
+        c.launch()
+    eager = {k: bits(v) for k, v in bufs.items()}
+    eager["hook"] = bits(x_hook)
+
+    x_hook.copy_(x_start)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for c in calls:
+                c.launch(stream.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for v in bufs.values():          # eager work between replays
+            v.fill_(float("nan"))
+        x_hook.copy_(x_start)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in bufs.items():
+            assert np.array_equal(bits(v), eager[k]), "replay %d: %s" % (rep, k)
+        assert np.array_equal(bits(x_hook), eager["hook"]), "replay %d: hook" % rep
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
@@ -394,6 +440,60 @@ def test_empty_batch_and_empty_sequences(gpu):
     b3 = torch.zeros((3, 0, 16), device="cuda")
     hp = r2l.prefix_scan_state(x3, x3, b3, A, h_in=h0)
     assert torch.equal(hp, h0)
+    torch.cuda.synchronize()
+
+
+def test_maximum_dim(gpu):
+    """dim at the largest value the library takes (65535 * 16 channels: the
+    carry grid's y limit), with a chunked state-only call that uses that grid."""
+    D = 65535 * 16
+    inp = synth.scan_inputs(23, [3, 5], D=D)
+    g = on_gpu(inp, dense=False)
+    h0 = synth.initial_state(23, 2, D, 16)
+    ref = oracle_scan(inp, h_in=h0, want_h_out=True)
+    h = torch.empty((2, D, 16), device="cuda")
+    y = r2l.r2l_scan(**scan_kw(g), h_in=dev32(h0), h_out=h)
+    check_y(y, ref["y"], "f32", "max dim y")
+    check_state(h, ref["h_out"], "max dim state")
+    fref = oracle_scan(inp, reverse=False, h_in=h0, want_h_out=True)
+    hp = r2l.prefix_scan_state(g["x"], g["dt"], g["Bm"], g["A"], cu_seqlens=g["cu_seqlens"],
+                               max_seqlen=g["max_seqlen"], h_in=dev32(h0), chunk_tokens=2)
+    check_state(hp, fref["h_out"], "max dim chunked prefix state")
+    torch.cuda.synchronize()
+
+
+def test_million_token_sequence(gpu):
+    """One sequence of 2^20 tokens: the planner cuts it into thousands of
+    chunks (a long carry per lane)."""
+    L, D = 1 << 20, 16
+    inp = synth.scan_inputs(24, [L], D=D, dtype="bf16", dt_mean=-5.0)
+    g = on_gpu(inp, dense=False)
+    ref = oracle_scan(inp, want_h_out=True)
+    h = torch.empty((1, D, 16), device="cuda")
+    kw = dict(scan_kw(g), h_out=h)
+    plan = r2l.bind("r2l_scan", **kw, out=torch.empty_like(g["x"])).plan()
+    assert plan["chunked"] and plan["chunks"] > 1000
+    y = r2l.r2l_scan(**kw)
+    check_y(y, ref["y"], "bf16", "2^20 tokens y")
+    check_state(h, ref["h_out"], "2^20 tokens state")
+    fref = oracle_scan(inp, reverse=False, want_h_out=True)
+    hp = r2l.prefix_scan_state(g["x"], g["dt"], g["Bm"], g["A"], cu_seqlens=g["cu_seqlens"],
+                               max_seqlen=g["max_seqlen"])
+    check_state(hp, fref["h_out"], "2^20 tokens prefix state")
+    torch.cuda.synchronize()
+
+
+def test_many_short_sequences(gpu):
+    """60 000 ragged sequences of 0 to 3 tokens (one block each)."""
+    rng = np.random.default_rng(25)
+    lengths = rng.integers(0, 4, size=60_000)
+    inp = synth.scan_inputs(25, lengths, D=16)
+    g = on_gpu(inp, dense=False)
+    ref = oracle_scan(inp, want_h_out=True)
+    h = torch.empty((len(lengths), 16, 16), device="cuda")
+    y = r2l.r2l_scan(**scan_kw(g), h_out=h)
+    check_y(y, ref["y"], "f32", "short sequences y")
+    check_state(h, ref["h_out"], "short sequences state")
     torch.cuda.synchronize()
 
 
@@ -458,6 +558,24 @@ def test_denoise_hooks_bf16(gpu):
         x = g["x"].clone()
         r2l.r2l_scan(**{**scan_kw(g), "x": x}, res=x, s=float(s[hook]), out=x)
         check_y(flat(x), ref["out"], "bf16", "hook %d out" % hook)
+    torch.cuda.synchronize()
+
+
+def test_l2r_ablation_hooks_bf16(gpu):
+    """The L2R-Mamba ablation at the denoising hook shape: forward scan with
+    readout and gated residual in place, through prefix_scan_state."""
+    s = synth.denoise_gates()
+    for hook in (0, 6):
+        inp = synth.denoise_hook_inputs(hook)
+        ref = oracle_scan(inp, reverse=False, res=inp.x, s=float(s[hook]), want_out=True,
+                          want_h_out=True)
+        g = on_gpu(inp)
+        x = g["x"].clone()
+        h = torch.empty((64, 2048, 16), device="cuda")
+        r2l.prefix_scan_state(x, g["dt"], g["Bm"], g["A"], Cm=g["Cm"], Dskip=g["Dskip"], res=x,
+                              s=float(s[hook]), out=x, h_out=h)
+        check_y(flat(x), ref["out"], "bf16", "hook %d forward out" % hook)
+        check_state(h, ref["h_out"], "hook %d forward state" % hook)
     torch.cuda.synchronize()
 
 
