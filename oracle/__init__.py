@@ -21,6 +21,8 @@ Function map (each a thin wrapper over the one C routine):
                              (partial-bidirectionality summary, "Methodology" 1).
 * ``block_commit_state``  -- advance a cached boundary state over a committed
                              block (same passage: finished blocks join the prefix).
+* ``selective_scan_backward`` -- the gradients of the scan with readout and
+                             residual (training the R2L stream).
 """
 from __future__ import annotations
 
@@ -64,6 +66,13 @@ class OracleLib:
             _dptr, _dptr, _dptr, _dptr, ctypes.c_double, _dptr, ctypes.c_int]
         lib.ref_max_threads.restype = ctypes.c_int
         lib.ref_max_threads.argtypes = []
+        if hasattr(lib, "ref_selective_scan_backward"):
+            lib.ref_selective_scan_backward.restype = ctypes.c_int
+            lib.ref_selective_scan_backward.argtypes = [
+                ctypes.c_int, ctypes.c_int64, _i64ptr, ctypes.c_int64, ctypes.c_int64,
+                _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, ctypes.c_int, _dptr,
+                ctypes.c_int, ctypes.c_double, _dptr, _dptr,
+                _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, ctypes.c_int]
         self.lib = lib
         self.path = path
 
@@ -156,6 +165,51 @@ def selective_scan(x, dt, Bm, Cm, A, Dskip=None, *, reverse: bool,
     if rc != 0:
         raise ValueError("oracle rejected its arguments (rc=%d)" % rc)
     return {"y": y, "out": out, "h_out": h_out}
+
+
+RES_KINDS = {"none": 0, "x": 1, "separate": 2}
+
+
+def selective_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, reverse: bool, dout,
+                            dh_out=None, res_kind: str = "none", s: float = 0.0,
+                            seq_offsets=None, batch=None, seqlen=None,
+                            delta_softplus: bool = True, h_in=None, nthreads: int = 0,
+                            timing: dict | None = None, lib: OracleLib | None = None):
+    """Gradients of the scan with readout (and residual ``res_kind``: "none",
+    "x" or "separate") for ``dout`` = dL/dout [tokens, D] and ``dh_out`` =
+    dL/dh_out [batch, D, N] (or None). Returns fp64 arrays ``dx``, ``ddt``
+    [tokens, D], ``dBm``, ``dCm`` [tokens, N], ``dA`` [D, N], ``dDskip`` [D],
+    ``dh_in`` [batch, D, N] and the scalar ``ds``. A separate residual's
+    gradient is dout itself and is not returned."""
+    x, dt, Bm, Cm, A = _f64(x), _f64(dt), _f64(Bm), _f64(Cm), _f64(A)
+    Dskip, h_in, dout, dh_out = _f64(Dskip), _f64(h_in), _f64(dout), _f64(dh_out)
+    tokens, D = x.shape
+    N = A.shape[1]
+    off = _offsets(seq_offsets, batch, seqlen, tokens)
+    nb = off.shape[0] - 1
+    assert dt.shape == (tokens, D) and dout.shape == (tokens, D)
+    assert Bm.shape == (tokens, N) and Cm.shape == (tokens, N) and A.shape == (D, N)
+    if h_in is not None:
+        h_in = h_in.reshape(nb, D, N)
+    if dh_out is not None:
+        dh_out = dh_out.reshape(nb, D, N)
+    r = {"dx": np.empty((tokens, D)), "ddt": np.empty((tokens, D)),
+         "dBm": np.empty((tokens, N)), "dCm": np.empty((tokens, N)), "dA": np.empty((D, N)),
+         "dDskip": np.empty(D), "dh_in": np.empty((nb, D, N)), "ds": np.empty(1)}
+    t0 = time.perf_counter()
+    rc = (lib or _load()).lib.ref_selective_scan_backward(
+        1 if reverse else 0, nb, off.ctypes.data_as(_i64ptr), D, N,
+        _ptr(x), _ptr(dt), _ptr(Bm), _ptr(Cm), _ptr(A), _ptr(Dskip),
+        1 if delta_softplus else 0, _ptr(h_in), RES_KINDS[res_kind], float(s),
+        _ptr(dout), _ptr(dh_out), _ptr(r["dx"]), _ptr(r["ddt"]), _ptr(r["dBm"]),
+        _ptr(r["dCm"]), _ptr(r["dA"]), _ptr(r["dDskip"]), _ptr(r["dh_in"]), _ptr(r["ds"]),
+        int(nthreads))
+    if timing is not None:
+        timing["seconds"] = time.perf_counter() - t0
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments (rc=%d)" % rc)
+    r["ds"] = float(r["ds"][0])
+    return r
 
 
 def r2l_scan(x, dt, Bm, Cm, A, Dskip=None, *, res=None, s=0.0, **kw):

@@ -172,3 +172,206 @@ int ref_max_threads(void)
     return 1;
 #endif
 }
+
+/* d softplus(v) / dv = 1 / (1 + exp(-v)), in a form that does not overflow. */
+static double ref_sigmoid(double v)
+{
+    if (v >= 0.0)
+        return 1.0 / (1.0 + exp(-v));
+    const double e = exp(v);
+    return e / (1.0 + e);
+}
+
+/*
+ * Gradients of one selective scan (the same forward as ref_selective_scan,
+ * with readout), for training the R2L stream: "Bifocal Diffusion Language
+ * Models" trains the sidecar (and, plug-in, only the sidecar and s); this
+ * is the reverse-mode derivative of the loop above, written out.
+ *
+ * Given dout = dL/dout [tokens, D] and dh_out = dL/dh_out [batch, D, N] (or
+ * NULL), with dy = s * dout when there is a residual and dout otherwise, and
+ * g the gradient with respect to the state, visiting the tokens of each
+ * sequence in the opposite order of the forward scan:
+ *     g  += dy_t * Cm[t,:]                 (the readout of token t)
+ *     dCm[t,:] += dy_t * h_t               (summed over channels)
+ *     dx_t = dy_t * Dskip + Delta_t * sum_n g_n * Bm[t,n]  (+ dout_t if res is x)
+ *     dBm[t,:] += g * Delta_t * x_t        (summed over channels)
+ *     dDelta_t = sum_n g_n * (Bm[t,n] * x_t + A[d,n] * abar_n * h_prev_n)
+ *     dA[d,:] += g * Delta_t * abar * h_prev   (summed over tokens and sequences)
+ *     g *= abar                            (now the gradient of h_prev)
+ *     ddt_t = dDelta_t * sigmoid(dt_t) (softplus on) or dDelta_t
+ * then dh_in = g; dDskip[d] = sum_t dy_t * x_t; ds = sum dout * y.
+ *
+ *   res_kind   0: no residual (out = y); 1: the residual is x; 2: a separate
+ *              residual (its gradient is dout itself and is not written).
+ *   outputs    dx, ddt [tokens, D]; dBm, dCm [tokens, N]; dA [D, N];
+ *              dDskip [D]; dh_in [batch, D, N]; ds [1]: each may be NULL.
+ *
+ * Work runs in parallel over (sequence, group of 64 channels); the sums over
+ * channel groups and over sequences are then taken in a fixed order, so the
+ * result does not depend on the thread count.
+ * Returns 0, or -1 on an invalid argument (nothing is written then).
+ */
+int ref_selective_scan_backward(int reverse, int64_t batch, const int64_t *seq_off,
+                                int64_t D, int64_t N,
+                                const double *x, const double *dt,
+                                const double *Bm, const double *Cm,
+                                const double *A, const double *Dskip,
+                                int delta_softplus, const double *h_in,
+                                int res_kind, double s,
+                                const double *dout, const double *dh_out,
+                                double *dx, double *ddt, double *dBm, double *dCm,
+                                double *dA, double *dDskip, double *dh_in, double *ds,
+                                int nthreads)
+{
+    if (batch < 0 || D <= 0 || N <= 0 || N > 4096 || !seq_off)
+        return -1;
+    if (!x || !dt || !Bm || !Cm || !A || !dout || res_kind < 0 || res_kind > 2)
+        return -1;
+    if (seq_off[0] != 0)
+        return -1;
+    for (int64_t b = 0; b < batch; ++b)
+        if (seq_off[b + 1] < seq_off[b])
+            return -1;
+    const int64_t tokens = seq_off[batch];
+    const int64_t G = 64;                       /* channels per task */
+    const int64_t groups = (D + G - 1) / G;
+
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+
+    /* per-task partial sums, reduced in a fixed order afterwards */
+    double *pB = calloc((size_t)(tokens * groups * N) + 1, sizeof(double));
+    double *pC = calloc((size_t)(tokens * groups * N) + 1, sizeof(double));
+    double *pA = calloc((size_t)(batch * D * N) + 1, sizeof(double));
+    double *pD = calloc((size_t)(batch * D) + 1, sizeof(double));
+    double *pS = calloc((size_t)(batch * groups) + 1, sizeof(double));
+    if (!pB || !pC || !pA || !pD || !pS)
+        abort();
+
+    const int64_t tasks = batch * groups;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t task = 0; task < tasks; ++task) {
+        const int64_t b = task / groups;
+        const int64_t grp = task % groups;
+        const int64_t start = seq_off[b];
+        const int64_t len = seq_off[b + 1] - start;
+        /* H[i*N + n]: state before visiting position i (H[0] = h_in), and
+         * after the last one at i = len */
+        double *H = malloc((size_t)((len + 1) * N) * sizeof(double));
+        double *abar = malloc((size_t)(len * N + 1) * sizeof(double));
+        double *delta = malloc((size_t)(len + 1) * sizeof(double));
+        double *g = malloc((size_t)N * sizeof(double));
+        if (!H || !abar || !delta || !g)
+            abort();
+
+        for (int64_t d = grp * G; d < D && d < (grp + 1) * G; ++d) {
+            /* forward, keeping every state */
+            for (int64_t n = 0; n < N; ++n)
+                H[n] = h_in ? h_in[(b * D + d) * N + n] : 0.0;
+            for (int64_t i = 0; i < len; ++i) {
+                const int64_t t = reverse ? start + len - 1 - i : start + i;
+                const double xv = x[t * D + d];
+                const double raw = dt[t * D + d];
+                delta[i] = delta_softplus ? ref_softplus(raw) : raw;
+                for (int64_t n = 0; n < N; ++n) {
+                    abar[i * N + n] = exp(delta[i] * A[d * N + n]);
+                    H[(i + 1) * N + n] = abar[i * N + n] * H[i * N + n] +
+                                         (delta[i] * Bm[t * N + n]) * xv;
+                }
+            }
+
+            /* backward, in the opposite visiting order */
+            for (int64_t n = 0; n < N; ++n)
+                g[n] = dh_out ? dh_out[(b * D + d) * N + n] : 0.0;
+            const double dsk = Dskip ? Dskip[d] : 0.0;
+            for (int64_t i = len - 1; i >= 0; --i) {
+                const int64_t t = reverse ? start + len - 1 - i : start + i;
+                const double xv = x[t * D + d];
+                const double dv = dout[t * D + d];
+                const double dy = res_kind ? s * dv : dv;
+                const double *h_now = H + (i + 1) * N;
+                const double *h_prev = H + i * N;
+
+                double yv = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    yv += Cm[t * N + n] * h_now[n];
+                yv += dsk * xv;
+                if (res_kind)
+                    pS[task] += dv * yv;
+
+                for (int64_t n = 0; n < N; ++n) {
+                    g[n] += dy * Cm[t * N + n];
+                    pC[(t * groups + grp) * N + n] += dy * h_now[n];
+                }
+                pD[b * D + d] += dy * xv;
+
+                double dxv = dy * dsk + (res_kind == 1 ? dv : 0.0);
+                double ddelta = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double a = abar[i * N + n];
+                    dxv += g[n] * delta[i] * Bm[t * N + n];
+                    pB[(t * groups + grp) * N + n] += g[n] * delta[i] * xv;
+                    ddelta += g[n] * (Bm[t * N + n] * xv + A[d * N + n] * a * h_prev[n]);
+                    pA[(b * D + d) * N + n] += g[n] * delta[i] * a * h_prev[n];
+                    g[n] *= a;
+                }
+                if (dx)
+                    dx[t * D + d] = dxv;
+                if (ddt)
+                    ddt[t * D + d] = delta_softplus ? ddelta * ref_sigmoid(dt[t * D + d]) : ddelta;
+            }
+            if (dh_in)
+                for (int64_t n = 0; n < N; ++n)
+                    dh_in[(b * D + d) * N + n] = g[n];
+        }
+        free(H);
+        free(abar);
+        free(delta);
+        free(g);
+    }
+
+    /* the fixed-order sums */
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            double sb = 0.0, sc = 0.0;
+            for (int64_t grp = 0; grp < groups; ++grp) {
+                sb += pB[(t * groups + grp) * N + n];
+                sc += pC[(t * groups + grp) * N + n];
+            }
+            if (dBm)
+                dBm[t * N + n] = sb;
+            if (dCm)
+                dCm[t * N + n] = sc;
+        }
+    for (int64_t d = 0; d < D; ++d) {
+        for (int64_t n = 0; n < N; ++n) {
+            double sa = 0.0;
+            for (int64_t b = 0; b < batch; ++b)
+                sa += pA[(b * D + d) * N + n];
+            if (dA)
+                dA[d * N + n] = sa;
+        }
+        double sd = 0.0;
+        for (int64_t b = 0; b < batch; ++b)
+            sd += pD[b * D + d];
+        if (dDskip)
+            dDskip[d] = sd;
+    }
+    if (ds) {
+        double ss = 0.0;
+        for (int64_t task = 0; task < tasks; ++task)
+            ss += pS[task];
+        ds[0] = ss;
+    }
+    free(pB);
+    free(pC);
+    free(pA);
+    free(pD);
+    free(pS);
+    return 0;
+}

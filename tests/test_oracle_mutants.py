@@ -11,6 +11,7 @@ import tempfile
 import pytest
 
 import oracle
+from oracle_bwd_pins import BWD_PINS
 from oracle_pins import PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "selective_scan_ref.c")
@@ -37,6 +38,42 @@ MUTANTS = {
     "state_never_updated": (
         "h[n] = abar * h[n] + (delta * Bm[t * N + n]) * xv;\n            }",
         "h[n] = h[n];\n            }\n            double hn_tmp = 0;"),
+}
+
+
+# Mistakes in the backward (anchors are searched from the function named
+# first; the forward code is left as committed).
+BWD_MUTANTS = {
+    "bwd_drop_decay_term": ("ref_selective_scan_backward(",
+                            "A[d * N + n] * a * h_prev[n]);", "0.0 * a * h_prev[n]);"),
+    "bwd_no_sigmoid": ("ref_selective_scan_backward(",
+                       "ddelta * ref_sigmoid(dt[t * D + d])", "ddelta"),
+    "bwd_sigmoid_sign": ("static double ref_sigmoid",
+                         "return 1.0 / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(v));"),
+    "bwd_g_not_decayed": ("ref_selective_scan_backward(", "g[n] *= a;", "g[n] *= 1.0;"),
+    "bwd_dA_uses_h_now": ("ref_selective_scan_backward(",
+                          "+= g[n] * delta[i] * a * h_prev[n];", "+= g[n] * delta[i] * a * h_now[n];"),
+    "bwd_dC_uses_h_prev": ("ref_selective_scan_backward(",
+                           "+= dy * h_now[n];", "+= dy * h_prev[n];"),
+    "bwd_dx_no_residual": ("ref_selective_scan_backward(", "(res_kind == 1 ? dv : 0.0)", "0.0"),
+    "bwd_dy_ungated": ("ref_selective_scan_backward(",
+                       "const double dy = res_kind ? s * dv : dv;", "const double dy = dv;"),
+    "bwd_dB_without_delta": ("ref_selective_scan_backward(",
+                             "+= g[n] * delta[i] * xv;", "+= g[n] * xv;"),
+    "bwd_ds_uses_dy": ("ref_selective_scan_backward(", "pS[task] += dv * yv;",
+                       "pS[task] += dy * yv;"),
+    "bwd_dDskip_uses_dout": ("ref_selective_scan_backward(", "pD[b * D + d] += dy * xv;",
+                             "pD[b * D + d] += dv * xv;"),
+    "bwd_g_skips_readout": ("ref_selective_scan_backward(", "g[n] += dy * Cm[t * N + n];",
+                            "g[n] += 0.0 * Cm[t * N + n];"),
+    "bwd_ignores_dh_out": ("ref_selective_scan_backward(",
+                           "g[n] = dh_out ? dh_out[(b * D + d) * N + n] : 0.0;", "g[n] = 0.0;"),
+    "bwd_dx_without_delta": ("ref_selective_scan_backward(",
+                             "dxv += g[n] * delta[i] * Bm[t * N + n];",
+                             "dxv += g[n] * Bm[t * N + n];"),
+    "bwd_same_direction": ("ref_selective_scan_backward(",
+                           "for (int64_t i = len - 1; i >= 0; --i) {",
+                           "for (int64_t i = 0; i < len; ++i) {"),
 }
 
 
@@ -73,3 +110,28 @@ def test_some_pin_catches_mutant(workdir, name):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, "no pin catches the planted mistake %r" % name
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_some_backward_pin_catches_mutant(workdir, name):
+    start, old, new = BWD_MUTANTS[name]
+    text = open(SRC).read()
+    at = text.index(start)
+    assert text.find(old, at) >= 0, "mutation anchor not found: %s" % name
+    at = text.find(old, at)
+    src = os.path.join(workdir, name + ".c")
+    with open(src, "w") as f:
+        f.write(text[:at] + new + text[at + len(old):])
+    so = os.path.join(workdir, name + ".so")
+    oracle.build(src=src, out=so)
+    lib = oracle.OracleLib(so)
+
+    def bwd(*a, **k):
+        return oracle.selective_scan_backward(*a, lib=lib, **k)
+
+    for pin in BWD_PINS:   # the first failing pin is enough
+        try:
+            pin(bwd)
+        except (AssertionError, ValueError, FloatingPointError):
+            return
+    pytest.fail("no backward pin catches the planted mistake %r" % name)

@@ -3,12 +3,32 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle_bwd_pins import BWD_PINS
 from oracle_pins import PINS
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
 def test_pin(pin):
     pin(oracle.selective_scan)
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=[p.__name__ for p in BWD_PINS])
+def test_backward_pin(pin):
+    pin(oracle.selective_scan_backward)
+
+
+def test_backward_thread_count_does_not_change_results():
+    r = np.random.default_rng(2)
+    T, D, N = 200, 130, 16
+    args = (r.standard_normal((T, D)), r.normal(-2, 0.5, (T, D)), r.standard_normal((T, N)),
+            r.standard_normal((T, N)), -np.tile(np.arange(1.0, 17.0), (D, 1)),
+            r.standard_normal(D))
+    kw = dict(reverse=True, dout=r.standard_normal((T, D)), seq_offsets=[0, 120, 120, 200],
+              res_kind="x", s=0.2)
+    a = oracle.selective_scan_backward(*args, nthreads=1, **kw)
+    b = oracle.selective_scan_backward(*args, nthreads=8, **kw)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
 
 
 def test_thread_count_does_not_change_results():
