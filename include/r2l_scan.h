@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define R2L_ABI_VERSION 1
+#define R2L_ABI_VERSION 2
 
 /* exported from libr2l_scan.so (everything else in it is hidden) */
 #if defined(__GNUC__)
@@ -204,6 +204,55 @@ R2L_API r2l_status block_commit_state(const r2l_scan_args *a, void *stream);
  * writes *bytes, or an error status.
  */
 R2L_API r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes);
+
+/*
+ * Gradients of r2l_scan, for training the R2L stream (the pages train the
+ * sidecar jointly with the backbone, or, plug-in, only the sidecar and s).
+ * The forward call is described by the same r2l_scan_args (x, dt, Bm, Cm, A,
+ * Dskip, h_in, res, s, delta_softplus, layout; out, h_out, chunk_tokens,
+ * state_split and the workspace fields are not read). With a residual,
+ * dL/dy = s * dout; without, dL/dy = dout. A separate residual's gradient is
+ * dout itself and is not written; when the residual is x, dx includes dout.
+ *
+ * Layout: dout, dx, ddt are token-major like x (element strides, batch
+ * strides in the dense layout, 0 = contiguous) in the storage type of x;
+ * every other gradient is fp32 and contiguous: dBm, dCm [tokens, dstate]
+ * with tokens packed (dense: row b * seqlen + l), dA [dim, dstate],
+ * dDskip [dim], dh_in [batch, dim, dstate], ds [1]. dh_out (dL/dh_out) is
+ * optional. Every output may be NULL (not computed); ds needs a residual.
+ * Outputs may not overlap each other or any input.
+ */
+typedef struct r2l_grad_args {
+    const void *dout;   int64_t dout_stride, dout_batch_stride;   /* dL/dout, required */
+    const float *dh_out;                                        /* [batch, dim, dstate] or NULL */
+    void *dx;           int64_t dx_stride, dx_batch_stride;
+    void *ddt;          int64_t ddt_stride, ddt_batch_stride;
+    float *dBm;
+    float *dCm;
+    float *dA;
+    float *dDskip;
+    float *dh_in;
+    float *ds;
+    void *workspace;                  /* device memory, 256-byte aligned */
+    size_t workspace_bytes;           /* at least r2l_backward_workspace_size() */
+} r2l_grad_args;
+
+/*
+ * r2l_scan_backward -- the gradients of r2l_scan at `fwd` for dL/dout (and
+ * dL/dh_out): the adjoint of the reverse scan, visiting the tokens of each
+ * sequence left to right. Every sum (over channels for dBm and dCm, over
+ * tokens and sequences for dA, dDskip and ds) is taken in a fixed order, so
+ * repeated calls give the same bits. All arithmetic is fp32.
+ * Source: "Bifocal Diffusion Language Models", section 2 (the R2L stream,
+ * its residual through s, and its training).
+ */
+R2L_API r2l_status r2l_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                     void *stream);
+
+/* Bytes of workspace r2l_scan_backward needs for these arguments (only shape
+ * fields and which outputs are wanted are read). */
+R2L_API r2l_status r2l_backward_workspace_size(const r2l_scan_args *fwd,
+                                               const r2l_grad_args *grad, size_t *bytes);
 
 /* Short static description of a status code. */
 R2L_API const char *r2l_status_string(r2l_status status);

@@ -23,7 +23,7 @@ from . import _abi
 from ._abi import R2LError  # noqa: F401
 
 __all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "workspace_size", "bind",
-           "BoundCall", "R2LError", "library_path"]
+           "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "R2LScan", "GRADS"]
 
 _DTYPES = {torch.float32: _abi.R2L_DTYPE_F32, torch.bfloat16: _abi.R2L_DTYPE_BF16}
 
@@ -263,3 +263,97 @@ def block_commit_state(state, x, dt, Bm, A, *, cu_seqlens=None, max_seqlen=None,
               delta_softplus, chunk_tokens, state_split)
     _run("block_commit_state", _abi.R2L_OP_COMMIT, a, workspace, x.device)
     return (state, out) if Cm is not None else state
+
+
+# ---- backward ---------------------------------------------------------------
+GRADS = ("dx", "ddt", "dBm", "dCm", "dA", "dDskip", "dh_in", "ds")
+
+
+def _fill_grad(a, x, Bm, dout, dh_out, outs):
+    g = _abi.GradArgs()
+    D, N = int(a.dim), int(a.dstate)
+    if dout.dtype != x.dtype or tuple(dout.shape) != tuple(x.shape):
+        raise ValueError("dout must match x in shape and dtype")
+    g.dout, g.dout_stride, g.dout_batch_stride, _ = _rows(dout, D, "dout")
+    _check_f32(dh_out, (a.batch, D, N), "dh_out")
+    g.dh_out = _ptr(dh_out)
+    for n in ("dx", "ddt"):
+        t = outs.get(n)
+        if t is not None:
+            if t.dtype != x.dtype or tuple(t.shape) != tuple(x.shape):
+                raise ValueError("%s must match x in shape and dtype" % n)
+            p, st, bst, _ = _rows(t, D, n)
+            setattr(g, n, p)
+            setattr(g, n + "_stride", st)
+            setattr(g, n + "_batch_stride", bst)
+    shapes = {"dBm": tuple(Bm.shape), "dCm": tuple(Bm.shape), "dA": (D, N), "dDskip": (D,),
+              "dh_in": (a.batch, D, N), "ds": (1,)}
+    for n, shape in shapes.items():
+        _check_f32(outs.get(n), shape, n)
+        setattr(g, n, _ptr(outs.get(n)))
+    return g
+
+
+def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seqlens=None,
+                      max_seqlen=None, h_in=None, res=None, s=0.0, delta_softplus=True,
+                      grads=GRADS, out=None, workspace=None):
+    """Gradients of ``r2l_scan`` (same forward arguments) for ``dout`` = dL/dout
+    and ``dh_out`` = dL/dh_out. Returns a dict of the names in ``grads``: dx,
+    ddt (like x), dBm, dCm (fp32, shaped like Bm), dA [D, N], dDskip [D],
+    dh_in [batch, D, N], ds [1] (with a residual only). ``out`` may hold
+    preallocated tensors for some of them. A separate residual's gradient is
+    dout itself; when res is x, dx includes it."""
+    a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, None, res, s, None,
+              delta_softplus, 0, 0)
+    D, N = int(a.dim), int(a.dstate)
+    outs = dict(out or {})
+    wanted = [n for n in grads if n != "ds" or res is not None]
+    make = {"dx": lambda: torch.empty_like(x), "ddt": lambda: torch.empty_like(x),
+            "dBm": lambda: torch.empty(Bm.shape, dtype=torch.float32, device=x.device),
+            "dCm": lambda: torch.empty(Bm.shape, dtype=torch.float32, device=x.device),
+            "dA": lambda: torch.empty((D, N), dtype=torch.float32, device=x.device),
+            "dDskip": lambda: torch.empty((D,), dtype=torch.float32, device=x.device),
+            "dh_in": lambda: torch.empty((a.batch, D, N), dtype=torch.float32, device=x.device),
+            "ds": lambda: torch.empty((1,), dtype=torch.float32, device=x.device)}
+    for n in wanted:
+        if outs.get(n) is None:
+            outs[n] = make[n]()
+    outs = {n: outs[n] for n in wanted}
+    g = _fill_grad(a, x, Bm, dout, dh_out, outs)
+    need = _abi.backward_workspace_size(a, g)
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        elif workspace.numel() * workspace.element_size() < need:
+            raise ValueError("workspace has %d bytes, the backward needs %d"
+                             % (workspace.numel() * workspace.element_size(), need))
+        g.workspace, g.workspace_bytes = workspace.data_ptr(), need
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _abi.call_backward(a, g, stream)
+    return outs
+
+
+class R2LScan(torch.autograd.Function):
+    """The R2L stream as a differentiable op (dense [batch, L, D] tensors):
+    out = x + s * y (the hook; ``s`` a float) or y (``s`` None). Gradients flow
+    to x, dt, Bm, Cm, A and Dskip through ``r2l_scan_backward``."""
+
+    @staticmethod
+    def forward(ctx, x, dt, Bm, Cm, A, Dskip, s=None):
+        res = x if s is not None else None
+        out = r2l_scan(x, dt, Bm, Cm, A, Dskip, res=res, s=0.0 if s is None else float(s))
+        ctx.save_for_backward(x, dt, Bm, Cm, A, Dskip)
+        ctx.s = s
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, dt, Bm, Cm, A, Dskip = ctx.saved_tensors
+        s = ctx.s
+        g = r2l_scan_backward(x, dt, Bm, Cm, A, Dskip, dout=dout.contiguous(),
+                              res=x if s is not None else None,
+                              s=0.0 if s is None else float(s),
+                              grads=("dx", "ddt", "dBm", "dCm", "dA", "dDskip"))
+        return (g["dx"], g["ddt"], g["dBm"].to(Bm.dtype), g["dCm"].to(Cm.dtype), g["dA"],
+                g["dDskip"] if Dskip is not None else None, None)

@@ -26,11 +26,12 @@ R2L_OP_SCAN = 0
 R2L_OP_PREFIX = 1
 R2L_OP_COMMIT = 2
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
-           "r2l_describe_plan")
+           "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
+           "r2l_check_access_backward")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -51,6 +52,18 @@ class ScanArgs(ctypes.Structure):
         ("h_in", _vp), ("h_out", _vp),
         ("res", _vp), ("res_stride", _i64), ("res_batch_stride", _i64), ("s", ctypes.c_float),
         ("out", _vp), ("out_stride", _i64), ("out_batch_stride", _i64),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class GradArgs(ctypes.Structure):
+    """Mirror of ``r2l_grad_args``."""
+    _fields_ = [
+        ("dout", _vp), ("dout_stride", _i64), ("dout_batch_stride", _i64),
+        ("dh_out", _vp),
+        ("dx", _vp), ("dx_stride", _i64), ("dx_batch_stride", _i64),
+        ("ddt", _vp), ("ddt_stride", _i64), ("ddt_batch_stride", _i64),
+        ("dBm", _vp), ("dCm", _vp), ("dA", _vp), ("dDskip", _vp), ("dh_in", _vp), ("ds", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -103,6 +116,14 @@ def load(path: str = LIB_PATH):
     lib.r2l_describe_plan.argtypes = [_i32, ptr, ctypes.POINTER(PlanInfo)]
     lib.r2l_check_access.restype = _i32
     lib.r2l_check_access.argtypes = [_i32, ptr, ctypes.POINTER(_i32), ctypes.POINTER(AccessReport)]
+    gptr = ctypes.POINTER(GradArgs)
+    lib.r2l_scan_backward.restype = _i32
+    lib.r2l_scan_backward.argtypes = [ptr, gptr, _vp]
+    lib.r2l_backward_workspace_size.restype = _i32
+    lib.r2l_backward_workspace_size.argtypes = [ptr, gptr, ctypes.POINTER(ctypes.c_size_t)]
+    lib.r2l_check_access_backward.restype = _i32
+    lib.r2l_check_access_backward.argtypes = [ptr, gptr, ctypes.POINTER(_i32),
+                                              ctypes.POINTER(AccessReport)]
     if lib.r2l_abi_version() != ABI_VERSION:
         raise ImportError("libr2l_scan.so ABI %d, binding expects %d"
                           % (lib.r2l_abi_version(), ABI_VERSION))
@@ -147,6 +168,32 @@ def check_access(op: int, args: ScanArgs, cu_seqlens_host=None):
         arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
         cu = ctypes.cast(arr, ctypes.POINTER(_i32))
     st = lib.r2l_check_access(op, ctypes.byref(args), cu, ctypes.byref(rep))
+    return st, rep
+
+
+def backward_workspace_size(args: ScanArgs, grad: GradArgs) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().r2l_backward_workspace_size(ctypes.byref(args), ctypes.byref(grad), ctypes.byref(n))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_backward_workspace_size", last_error())
+    return int(n.value)
+
+
+def call_backward(args: ScanArgs, grad: GradArgs, stream: int | None) -> None:
+    st = load().r2l_scan_backward(ctypes.byref(args), ctypes.byref(grad), _vp(stream or 0))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_scan_backward", last_error())
+
+
+def check_access_backward(args: ScanArgs, grad: GradArgs, cu_seqlens_host=None):
+    """Host replay of every access r2l_scan_backward would make; (status, report)."""
+    lib = load()
+    rep = AccessReport()
+    cu = None
+    if cu_seqlens_host is not None:
+        arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
+        cu = ctypes.cast(arr, ctypes.POINTER(_i32))
+    st = lib.r2l_check_access_backward(ctypes.byref(args), ctypes.byref(grad), cu, ctypes.byref(rep))
     return st, rep
 
 

@@ -173,6 +173,18 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
             if (mode == kModeRes) row_access("res", rR, p.res, sq.ro, p.rs, k);
         };
         const int ntok = sg.ntok;
+        // backward phase 1: the state entering every group of kCkptTokens
+        // positions (state-only scans), written by the active lanes
+        if (p.ckpt && !readout)
+            for (int pos = 0; pos < ntok && ck.ok(); pos += kCkptTokens)
+                for (int lane = 0; lane < kWG; ++lane) {
+                    const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
+                    if (!lg.active) continue;
+                    const uintptr_t a = U(p.ckpt) +
+                        ((ckpt_row(bg.b, sq.s0p, pos) * p.D + lg.d) * kN + lg.sub * NS) * 4;
+                    ck.access("checkpoint", ck.region_of(p.ckpt), a, NS * 4);
+                    ck.wrote(a, NS * 4);
+                }
         if (ntok > 0)
             for (int j = 0; j < kPrefetch; ++j) load_pos(prefetch_pos(j, ntok));
         for (int k = 0; k < ntok && ck.ok(); ++k) {
@@ -257,7 +269,194 @@ void check_copy(Checker &ck, const Launch &l) {
     }
 }
 
+void check_backward(Checker &ck, const Launch &l, const int32_t *cu_host) {
+    const BwdParams &p = l.bwd;
+    const int G = l.G, NS = kN / G, K = kCkptTokens, NBC = 2 * kN, STAGE = stage_cols(NBC);
+    const int64_t es = l.dtype == R2L_DTYPE_BF16 ? 2 : 4;
+    const Region *rA = ck.region_of(p.A), *rDs = p.Dskip ? ck.region_of(p.Dskip) : nullptr;
+    const Region *rX = ck.region_of(p.x), *rD = ck.region_of(p.dt), *rG = ck.region_of(p.dout);
+    const Region *rB = ck.region_of(p.Bm), *rC = ck.region_of(p.Cm);
+    const Region *rdx = p.dx ? ck.region_of(p.dx) : nullptr, *rdd = p.ddt ? ck.region_of(p.ddt) : nullptr;
+    const Region *rCk = p.ckpt ? ck.region_of(p.ckpt) : nullptr;
+    const Region *rHo = p.dh_out ? ck.region_of(p.dh_out) : nullptr;
+    const Region *rHi = p.dh_in ? ck.region_of(p.dh_in) : nullptr;
+    for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
+        const BlockGeom bg = block_geom(p.nblocks, p.tiles, 1, bid);
+        if (!bg.valid) continue;
+        const int64_t s0 = p.cu_seqlens ? cu_host[bg.b] : 0;
+        const int64_t s1 = p.cu_seqlens ? cu_host[bg.b + 1] : 0;
+        if (p.cu_seqlens) ck.access("cu_seqlens", ck.region_of(p.cu_seqlens), U(p.cu_seqlens) + bg.b * 4, 8);
+        const BwdSeqGeom sq = bwd_seq_geom(p, bg.b, s0, s1);
+        const SegGeom sg = seg_geom(l.reverse, 0, sq.len > 0 ? sq.len : 1, sq.len);
+        const int ntok = sg.ntok;
+
+        uint32_t dmin = UINT32_MAX, dmax = 0;
+        for (int lane = 0; lane < kWG; ++lane) {
+            const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
+            dmin = lg.d < dmin ? lg.d : dmin;
+            dmax = lg.d > dmax ? lg.d : dmax;
+            const int64_t st = static_cast<int64_t>(lg.d) * kN + lg.sub * NS;
+            ck.access("A", rA, U(p.A) + st * 4, NS * 4);
+            if (p.Dskip) ck.access("Dskip", rDs, U(p.Dskip) + lg.d * 4, 4);
+            if (!lg.active) continue;
+            const int64_t bs = bg.b * p.D * kN + st;
+            if (p.dh_out) ck.access("dh_out", rHo, U(p.dh_out) + bs * 4, NS * 4);
+            if (p.dh_in) ck.access("dh_in", rHi, U(p.dh_in) + bs * 4, NS * 4);
+            if (p.partA) {
+                ck.access("partial dA", ck.region_of(p.partA), U(p.partA) + bs * 4, NS * 4);
+                ck.wrote(U(p.partA) + bs * 4, NS * 4);
+            }
+            if (p.partD && lg.sub == 0) {
+                const uintptr_t a = U(p.partD) + (bg.b * p.D + lg.d) * 4;
+                ck.access("partial dDskip", ck.region_of(p.partD), a, 4);
+                ck.wrote(a, 4);
+            }
+        }
+        if (p.partS) {
+            const uintptr_t a = U(p.partS) + (bg.b * p.tiles + bg.tile) * 4;
+            ck.access("partial ds", ck.region_of(p.partS), a, 4);
+            ck.wrote(a, 4);
+        }
+        // per-token rows through buffer resources (see check_segment)
+        auto row_access = [&](const char *what, const Region *reg, const void *base, int64_t elem_off,
+                              int64_t row_elems, int pos) {
+            const int row = seg_row(sg, pos);
+            if (row < 0 || row >= sq.len)
+                return ck.fail("%s: row %d outside the sequence of %lld rows", what, row, (long long)sq.len);
+            const uint64_t soff = static_cast<uint64_t>(row) * static_cast<uint64_t>(row_elems * es);
+            if (soff > UINT32_MAX) return ck.fail("%s: scalar offset above 32 bits", what);
+            if (static_cast<uint64_t>(dmax) * es + es > seq_span_bytes(sq.len, row_elems, p.D, es))
+                return ck.fail("%s: lane offset beyond the buffer resource", what);
+            const uintptr_t b0 = U(base) + elem_off * es + soff;
+            ck.access(what, reg, b0 + static_cast<uint64_t>(dmin) * es, es);
+            ck.access(what, reg, b0 + static_cast<uint64_t>(dmax) * es, es);
+        };
+        for (int gpos = 0; gpos < ntok && ck.ok(); gpos += K) {
+            const int gcnt = ntok - gpos < K ? ntok - gpos : K;
+            for (int j = 0; j < K; ++j) {
+                const int pos = gpos + (j < gcnt ? j : gcnt - 1);
+                row_access("x", rX, p.x, sq.xo, p.xs, pos);
+                row_access("dt", rD, p.dt, sq.dto, p.dts, pos);
+                row_access("dout", rG, p.dout, sq.go, p.gs, pos);
+            }
+            for (int j = 0; j < gcnt; ++j) {
+                if (p.dx) row_access("dx", rdx, p.dx, sq.dxo, p.dxs, gpos + j);
+                if (p.ddt) row_access("ddt", rdd, p.ddt, sq.ddo, p.dds, gpos + j);
+                const int64_t t = sq.s0p + seg_row(sg, gpos + j);
+                if (t < 0 || t >= p.tokens) return ck.fail("partial row %lld outside the tokens", (long long)t);
+                for (float *part : {p.partB, p.partC}) {
+                    if (!part) continue;
+                    const uintptr_t a = U(part) + ((bg.tile * p.tokens + t) * kN) * 4;
+                    ck.access("partial dBm/dCm", ck.region_of(part), a, kN * 4);
+                    ck.wrote(a, kN * 4);
+                }
+            }
+            for (int lane = 0; lane < kWG; ++lane) {
+                const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
+                const uintptr_t a = U(p.ckpt) +
+                    ((ckpt_row(bg.b, sq.s0p, gpos) * p.D + lg.d) * kN + lg.sub * NS) * 4;
+                ck.access("checkpoint", rCk, a, NS * 4);
+                ck.read_written("checkpoint", a, NS * 4);
+            }
+        }
+        // Bm / Cm staging: the last tile first, then each earlier (full) tile
+        const int ntiles = (ntok + kTile - 1) / kTile;
+        for (int ti = ntiles - 1; ti >= 0 && ck.ok(); --ti) {
+            const int base = ti * kTile, cnt = ntok - base < kTile ? ntok - base : kTile;
+            if (ti < ntiles - 1 && cnt != kTile) return ck.fail("an earlier tile is not full");
+            for (int lane = 0; lane < kWG; ++lane) {
+                const StageSlot ss = stage_slot(lane, NBC);
+                const int64_t row = seg_row(sg, base + stage_pos(ss.k, cnt));
+                if (row < 0 || row >= sq.len) return ck.fail("staging row outside the sequence");
+                const bool isC = ss.mat != 0;
+                const int64_t st = isC ? p.Cs : p.Bs;
+                const uint64_t voff = static_cast<uint64_t>(row * st + ss.col0) * es;
+                if (voff + STAGE * es > seq_span_bytes(sq.len, st, kN, es))
+                    return ck.fail("staging run beyond the buffer resource");
+                const uintptr_t addr = U(isC ? p.Cm : p.Bm) + (isC ? sq.Co : sq.Bo) * es + voff;
+                if (p.bc_vec && addr % stage_align(NBC, static_cast<int>(es)))
+                    return ck.fail("staging vector load not aligned");
+                ck.access(isC ? "Cm" : "Bm", isC ? rC : rB, addr, STAGE * es);
+            }
+        }
+    }
+}
+
+void check_sum(Checker &ck, const Launch &l) {
+    const SumParams &p = l.sum;
+    const Region *rs = p.P > 0 ? ck.region_of(p.src) : nullptr, *rd = ck.region_of(p.dst);
+    ck.access("gradient (sum)", rd, U(p.dst), p.n * 4);
+    for (int64_t q = 0; q < p.P && ck.ok(); ++q) {
+        ck.access("partial (sum)", rs, U(p.src) + q * p.pstride * 4, p.n * 4);
+        ck.read_written("partial (sum)", U(p.src) + q * p.pstride * 4, p.n * 4);
+    }
+}
+
 }  // namespace
+
+r2l_status check_backward_accesses(const r2l_scan_args *a, const r2l_grad_args *g, const BwdPlan &pl,
+                                   const int32_t *cu_host, r2l_access_report *rep) {
+    const int64_t es = elem_size(a->dtype), D = a->dim, N = kN;
+    const int64_t tok = tokens_of(a);
+    std::vector<Region> regs;
+    auto add = [&](const char *name, const void *p, uint64_t bytes) {
+        if (p && bytes) regs.push_back({name, U(p), U(p) + bytes});
+    };
+    auto tspan = [&](const void *p, int64_t stride, int64_t bstride, int64_t cols) -> uint64_t {
+        if (!p || tok <= 0) return 0;
+        const int64_t ext = is_ragged(a)
+            ? (tok - 1) * stride + cols
+            : (a->batch - 1) * eff_bstride(a, bstride, stride) + (a->seqlen - 1) * stride + cols;
+        return static_cast<uint64_t>(ext * es);
+    };
+    add("x", a->x, tspan(a->x, a->x_stride, a->x_batch_stride, D));
+    add("dt", a->dt, tspan(a->dt, a->dt_stride, a->dt_batch_stride, D));
+    add("Bm", a->Bm, tspan(a->Bm, a->Bm_stride, a->Bm_batch_stride, N));
+    add("Cm", a->Cm, tspan(a->Cm, a->Cm_stride, a->Cm_batch_stride, N));
+    add("dout", g->dout, tspan(g->dout, g->dout_stride, g->dout_batch_stride, D));
+    add("dx", g->dx, tspan(g->dx, g->dx_stride, g->dx_batch_stride, D));
+    add("ddt", g->ddt, tspan(g->ddt, g->ddt_stride, g->ddt_batch_stride, D));
+    add("A", a->A, static_cast<uint64_t>(D * N * 4));
+    add("Dskip", a->Dskip, static_cast<uint64_t>(D * 4));
+    add("h_in", a->h_in, static_cast<uint64_t>(a->batch * D * N * 4));
+    add("dh_out", g->dh_out, static_cast<uint64_t>(a->batch * D * N * 4));
+    add("dh_in", g->dh_in, static_cast<uint64_t>(a->batch * D * N * 4));
+    add("dBm", g->dBm, static_cast<uint64_t>(tok * N * 4));
+    add("dCm", g->dCm, static_cast<uint64_t>(tok * N * 4));
+    add("dA", g->dA, static_cast<uint64_t>(D * N * 4));
+    add("dDskip", g->dDskip, static_cast<uint64_t>(D * 4));
+    add("ds", g->ds, 4);
+    add("cu_seqlens", a->cu_seqlens, static_cast<uint64_t>((a->batch + 1) * 4));
+    const char *ws = static_cast<const char *>(g->workspace);
+    const size_t offs[] = {pl.off_ck, pl.off_B, pl.off_C, pl.off_A, pl.off_D, pl.off_S, pl.ws_bytes};
+    const char *names[] = {"workspace checkpoints", "workspace dBm partials", "workspace dCm partials",
+                           "workspace dA partials", "workspace dDskip partials", "workspace ds partials"};
+    for (int i = 0; i < 6; ++i)
+        if (ws) add(names[i], ws + offs[i], offs[i + 1] - offs[i]);
+    Checker ck(std::move(regs), rep);
+    ck.set_workspace(g->workspace, pl.ws_bytes);
+    Launch ls[kMaxBwdLaunches];
+    const int n = build_bwd_launches(a, g, pl, ls);
+    for (int i = 0; i < n && ck.ok(); ++i) {
+        ++rep->launches;
+        switch (ls[i].kind) {
+            case Launch::Segment:
+                if (ls[i].seg.bc_vec) ++rep->vector_staging;
+                check_segment(ck, ls[i], cu_host);
+                break;
+            case Launch::Backward:
+                if (ls[i].bwd.bc_vec) ++rep->vector_staging;
+                check_backward(ck, ls[i], cu_host);
+                break;
+            case Launch::Sum:
+                check_sum(ck, ls[i]);
+                break;
+            default:
+                ck.fail("unexpected launch kind in a backward plan");
+        }
+    }
+    return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;
+}
 
 r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const int32_t *cu_host,
                           r2l_access_report *rep) {

@@ -1,0 +1,348 @@
+// bwd_kernels.hip -- gfx950 kernels of the backward of a selective scan with
+// readout: the gradients that training the R2L stream needs ("Bifocal
+// Diffusion Language Models" trains the sidecar jointly, or only the sidecar
+// and s in the plug-in variant).
+//
+// With dy = dyscale * dout and g the gradient with respect to the state,
+// visiting the tokens in the opposite order of the forward scan:
+//     g += dy * Cm[t]             dCm[t] += dy * h_t        (over channels)
+//     dDelta = sum_n g_n (Bm[t,n] x + A_n abar_n h_prev_n)
+//     dA += g Delta abar h_prev   dBm[t] += g Delta x       (over channels)
+//     dx = dy Dskip + Delta sum_n g_n Bm[t,n] (+ dout if the residual is x)
+//     g *= abar;  ddt = dDelta * sigmoid(dt) (softplus on)
+// and at the end dh_in = g.
+//
+// Mapping onto CDNA4:
+//  * Phase 1 (the forward segment kernel, state only) stored the state
+//    entering every group of kCkptTokens visited positions. Here one workgroup
+//    owns (sequence, tile of kWG / G channels), G lanes per channel holding
+//    kN / G states each, and walks the groups backwards: it recomputes the
+//    group's states in registers from its checkpoint, then runs the adjoint
+//    over the group in reverse.
+//  * dBm and dCm are sums over channels of per-lane products: a wave sums its
+//    64 / G channels with a transpose-reduce (each shuffle step halves the
+//    values a lane carries: 2 * (kN / G) - 1 exchanges instead of
+//    kN * log2(64 / G)), the four waves add up in LDS, and the block writes
+//    one partial row per token and tile; the sums over tiles, over sequences
+//    (dA, dDskip) and over blocks (ds) are separate launches in a fixed order,
+//    so the result is deterministic (no atomics).
+//  * Bm / Cm rows are staged in LDS per tile of kTile tokens (double-buffered,
+//    walking the tiles backwards) as in the forward kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_device.h"
+#include "scan_geometry.h"
+#include "scan_internal.h"
+
+namespace r2l {
+namespace {
+
+using namespace dev;
+
+// 1 / (1 + e^-v): the derivative of softplus. v_exp_f32 saturates to 0 or
+// +inf, which gives 1 or 0.
+__device__ __forceinline__ float sigmoid(float v) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
+
+// Sum of v[] over the channels of a wave (the lanes that hold the same slice
+// of states: lanes with the same index mod G). Lane l < kN returns the total
+// of state reduced_state(G, l).
+template <int G>
+__device__ __forceinline__ float wave_state_sum(float (&v)[kN / G]) {
+    constexpr int NS = kN / G;
+    constexpr int LG = G == 1 ? 0 : (G == 2 ? 1 : 2);
+    constexpr int STAGES = NS == 16 ? 4 : (NS == 8 ? 3 : (NS == 4 ? 2 : (NS == 2 ? 1 : 0)));
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < STAGES; ++j) {
+        const int bit = 1 << (LG + j);
+        const bool up = (lane & bit) != 0;
+        const int half = NS >> (j + 1);
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = up ? v[i] : v[i + half];
+            const float keep = up ? v[i + half] : v[i];
+            v[i] = keep + __shfl_xor(send, bit);
+        }
+    }
+    float r = v[0];
+#pragma unroll
+    for (int bit = 1 << (LG + STAGES); bit < 64; bit <<= 1) r += __shfl_xor(r, bit);
+    return r;
+}
+
+template <bool REV, typename T, int G, bool SP>
+__global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
+    constexpr int NS = kN / G;
+    constexpr int K = kCkptTokens;
+    constexpr int NBC = 2 * kN;                  // staged floats per token (Bm, then Cm)
+    constexpr int STAGE = stage_cols(NBC);
+    constexpr int SW = STAGE * static_cast<int>(sizeof(T)) / 4;
+    constexpr int WAVES = kWG / 64;
+    static_assert(K * NBC == kWG, "one thread per (group token, column) in the block sum");
+    __shared__ __align__(16) float lds_bc[2][kTile * NBC];
+    __shared__ float red[WAVES][K][NBC];
+    __shared__ float red_s[WAVES];
+    using E = Elem<T>;
+    using R = typename E::raw_t;
+
+    const BlockGeom bg = block_geom(p.nblocks, p.tiles, 1, blockIdx.x);
+    if (!bg.valid) return;
+    const int64_t b = bg.b;
+    const int64_t s0 = p.cu_seqlens ? p.cu_seqlens[b] : 0;
+    const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[b + 1] : 0;
+    const BwdSeqGeom sq = bwd_seq_geom(p, b, s0, s1);
+    const SegGeom sg = seg_geom(REV, 0, sq.len > 0 ? sq.len : 1, sq.len);
+    const int ntok = sg.ntok;
+    const LaneGeom lg = lane_geom(bg.tile, threadIdx.x, G, p.D);
+    const uint32_t dl = lg.d;
+    const int sub = lg.sub;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    float An[NS], a2[NS], g[NS], dA[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        An[j] = p.A[dl * kN + sub * NS + j];
+        a2[j] = An[j] * kLog2e;
+        dA[j] = 0.0f;
+        g[j] = (p.dh_out && lg.active) ? p.dh_out[(b * p.D + dl) * kN + sub * NS + j] : 0.0f;
+    }
+    const float dsk = p.Dskip ? p.Dskip[dl] : 0.0f;
+    // lanes past the last channel shadow it; they must add nothing to any sum
+    const float dys = lg.active ? p.dyscale : 0.0f;
+    const float dxr = lg.active ? p.dxres : 0.0f;
+    const float dsw = (lg.active && sub == 0 && p.want_ds) ? 1.0f : 0.0f;
+    float dD = 0.0f, dsum = 0.0f;
+
+    // per-token rows through raw buffer resources based at the sequence's first
+    // row (scalar row offset, 32-bit lane offset), as in the forward kernel
+    const uint32_t es = static_cast<uint32_t>(sizeof(T));
+    const uint32_t doff = dl * es;
+    const uint32_t xrb = static_cast<uint32_t>(p.xs) * es, drb = static_cast<uint32_t>(p.dts) * es;
+    const uint32_t grb = static_cast<uint32_t>(p.gs) * es;
+    const uint32_t dxrb = static_cast<uint32_t>(p.dxs) * es, ddrb = static_cast<uint32_t>(p.dds) * es;
+    const auto rx = make_rsrc(static_cast<const T *>(p.x) + sq.xo, seq_span_bytes(sq.len, p.xs, p.D, es));
+    const auto rd = make_rsrc(static_cast<const T *>(p.dt) + sq.dto, seq_span_bytes(sq.len, p.dts, p.D, es));
+    const auto rg = make_rsrc(static_cast<const T *>(p.dout) + sq.go, seq_span_bytes(sq.len, p.gs, p.D, es));
+    const auto rdx = make_rsrc(p.dx ? static_cast<T *>(p.dx) + sq.dxo : nullptr,
+                               p.dx ? seq_span_bytes(sq.len, p.dxs, p.D, es) : 0);
+    const auto rdd = make_rsrc(p.ddt ? static_cast<T *>(p.ddt) + sq.ddo : nullptr,
+                               p.ddt ? seq_span_bytes(sq.len, p.dds, p.D, es) : 0);
+
+    // Bm / Cm staging: threads 0..127 fetch Bm runs, 128..255 Cm runs
+    const StageSlot ss = stage_slot(threadIdx.x, NBC);
+    const bool stage_c = __builtin_amdgcn_readfirstlane(ss.mat) != 0;
+    const auto rbc = stage_c
+        ? make_rsrc(static_cast<const T *>(p.Cm) + sq.Co, seq_span_bytes(sq.len, p.Cs, kN, es))
+        : make_rsrc(static_cast<const T *>(p.Bm) + sq.Bo, seq_span_bytes(sq.len, p.Bs, kN, es));
+    const uint32_t bcrb = static_cast<uint32_t>(stage_c ? p.Cs : p.Bs) * es;
+    const uint32_t bccol = static_cast<uint32_t>(ss.col0) * es;
+    uint32_t stw[SW];
+    auto stage_load = [&](int tbase, int tcnt) {   // tcnt >= 1
+        const uint32_t row = static_cast<uint32_t>(seg_row(sg, tbase + stage_pos(ss.k, tcnt)));
+        const uint32_t voff = row * bcrb + bccol;
+        if (p.bc_vec)
+            bload_words<SW>(rbc, voff, stw);
+        else
+            E::template bload_elems<STAGE>(rbc, voff, stw);
+    };
+    auto stage_store = [&](int buf) {
+        float4 *dst = reinterpret_cast<float4 *>(&lds_bc[buf][ss.k * NBC + ss.mat * kN + ss.col0]);
+#pragma unroll
+        for (int q = 0; q < STAGE / 4; ++q)
+            dst[q] = make_float4(E::word_elem(stw, 4 * q), E::word_elem(stw, 4 * q + 1),
+                                 E::word_elem(stw, 4 * q + 2), E::word_elem(stw, 4 * q + 3));
+    };
+
+    // tiles (and the groups inside them) from the last visited to the first
+    const int ntiles = (ntok + kTile - 1) / kTile;
+    if (ntok > 0) {
+        const int lb = (ntiles - 1) * kTile;
+        stage_load(lb, ntok - lb);
+        stage_store((ntiles - 1) & 1);
+    }
+    __syncthreads();
+    for (int ti = ntiles - 1; ti >= 0; --ti) {
+        const int tbase = ti * kTile;
+        const int tcnt = ntok - tbase < kTile ? ntok - tbase : kTile;
+        const bool more = ti > 0;
+        if (more) stage_load(tbase - kTile, kTile);   // every tile but the last is full
+        const float *bc = lds_bc[ti & 1];
+
+        for (int gi = (tcnt - 1) / K; gi >= 0; --gi) {
+            const int gpos = tbase + gi * K;
+            const int gcnt = ntok - gpos < K ? ntok - gpos : K;
+            // the group's per-token inputs (positions past its end repeat its last one)
+            R xr[K], dr[K], gr[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const uint32_t row = static_cast<uint32_t>(seg_row(sg, gpos + (j < gcnt ? j : gcnt - 1)));
+                xr[j] = E::bload(rx, doff, row * xrb);
+                dr[j] = E::bload(rd, doff, row * drb);
+                gr[j] = E::bload(rg, doff, row * grb);
+            }
+            float hck[NS];
+            const float *cp = p.ckpt + (ckpt_row(b, sq.s0p, gpos) * p.D + dl) * kN + sub * NS;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) hck[n] = cp[n];
+
+            // the group's states, recomputed forward from the checkpoint
+            float hs[K][NS], delta[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float dv = E::widen(dr[j]);
+                if constexpr (SP)
+                    delta[j] = softplus(dv);
+                else
+                    delta[j] = dv;
+                const float dx_ = delta[j] * E::widen(xr[j]);
+                const float *brow = bc + (gi * K + j) * NBC + sub * NS;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const float hp = j > 0 ? hs[j - 1][n] : hck[n];
+                    hs[j][n] = fmaf(__builtin_amdgcn_exp2f(delta[j] * a2[n]), hp, brow[n] * dx_);
+                }
+            }
+
+            // the adjoint over the group, last visited position first
+#pragma unroll
+            for (int j = K - 1; j >= 0; --j) {
+                if (j >= gcnt) continue;
+                const float *row = bc + (gi * K + j) * NBC + sub * NS;   // Bm slice; Cm at + kN
+                const float xv = E::widen(xr[j]);
+                const float gv = E::widen(gr[j]);
+                const float dy = dys * gv;
+                float yp = 0.0f;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) yp = fmaf(row[kN + n], hs[j][n], yp);
+                const float y = fmaf(dsk, xv, group_sum<G>(yp));
+                dsum = fmaf(dsw * gv, y, dsum);
+                dD = fmaf(dy, xv, dD);
+                const float dlx = delta[j] * xv;
+                float pb[NS], pc[NS];
+                float dd = 0.0f, dxs = 0.0f;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    g[n] = fmaf(dy, row[kN + n], g[n]);
+                    pc[n] = dy * hs[j][n];
+                    const float hp = j > 0 ? hs[j - 1][n] : hck[n];
+                    const float a = __builtin_amdgcn_exp2f(delta[j] * a2[n]);
+                    const float ah = a * hp;
+                    const float bn = row[n];
+                    dd = fmaf(g[n], fmaf(bn, xv, An[n] * ah), dd);
+                    dA[n] = fmaf(g[n] * delta[j], ah, dA[n]);
+                    dxs = fmaf(g[n], bn, dxs);
+                    pb[n] = g[n] * dlx;
+                    g[n] *= a;
+                }
+                const float ddelta = group_sum<G>(dd);
+                const float dxv = fmaf(delta[j], group_sum<G>(dxs), fmaf(dy, dsk, dxr * gv));
+                float ddtv = ddelta;
+                if constexpr (SP) ddtv *= sigmoid(E::widen(dr[j]));
+                const uint32_t orow = static_cast<uint32_t>(seg_row(sg, gpos + j));
+                if (lg.active) {
+                    if (p.dx) E::bstore(E::pack(dxv), rdx, doff, orow * dxrb);
+                    if (p.ddt) E::bstore(E::pack(ddtv), rdd, doff, orow * ddrb);
+                }
+                const float rb = wave_state_sum<G>(pb);
+                const float rc = wave_state_sum<G>(pc);
+                if (lane < kN) {
+                    const int n = reduced_state(G, lane);
+                    red[wave][j][n] = rb;
+                    red[wave][j][kN + n] = rc;
+                }
+            }
+            __syncthreads();
+            {   // the block's sums over its channels: one thread per (token, column)
+                const int j = threadIdx.x / NBC, col = threadIdx.x % NBC;
+                float *dst = col < kN ? p.partB : p.partC;
+                if (j < gcnt && dst) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < WAVES; ++w) v += red[w][j][col];
+                    const int64_t t = sq.s0p + seg_row(sg, gpos + j);
+                    dst[(bg.tile * p.tokens + t) * kN + (col % kN)] = v;
+                }
+            }
+            __syncthreads();
+        }
+        if (more) stage_store((ti - 1) & 1);
+        __syncthreads();
+    }
+
+    if (lg.active) {
+        const int64_t st = (b * p.D + dl) * kN + sub * NS;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            if (p.dh_in) p.dh_in[st + n] = g[n];
+            if (p.partA) p.partA[st + n] = dA[n];
+        }
+        if (p.partD && sub == 0) p.partD[b * p.D + dl] = dD;
+    }
+    if (p.partS) {   // uniform: every thread of the block reaches the barrier
+        float v = dsum;
+#pragma unroll
+        for (int bit = 1; bit < 64; bit <<= 1) v += __shfl_xor(v, bit);
+        if (lane == 0) red_s[wave] = v;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float t = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) t += red_s[w];
+            p.partS[b * p.tiles + bg.tile] = t;
+        }
+    }
+}
+
+constexpr int kSumThreads = 256;
+
+__global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumParams p) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kSumThreads + threadIdx.x;
+    if (i >= p.n) return;
+    float acc = 0.0f;
+    for (int64_t q = 0; q < p.P; ++q) acc += p.src[q * p.pstride + i];
+    p.dst[i] = acc;
+}
+
+template <bool REV, typename T, bool SP>
+hipError_t launch_bwd_g(int G, const BwdParams &p, hipStream_t stream) {
+    const int64_t grid = padded_grid(p.nblocks);
+    switch (G) {
+        case 2:
+            hipLaunchKernelGGL((bwd_kernel<REV, T, 2, SP>), dim3(grid), dim3(kWG), 0, stream, p);
+            break;
+        case 4:
+            hipLaunchKernelGGL((bwd_kernel<REV, T, 4, SP>), dim3(grid), dim3(kWG), 0, stream, p);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <bool REV, typename T>
+hipError_t launch_bwd_s(int G, const BwdParams &p, hipStream_t stream) {
+    return p.softplus ? launch_bwd_g<REV, T, true>(G, p, stream)
+                      : launch_bwd_g<REV, T, false>(G, p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, hipStream_t stream) {
+    if (reverse)
+        return dtype == 1 ? launch_bwd_s<true, uint16_t>(G, p, stream)
+                          : launch_bwd_s<true, float>(G, p, stream);
+    return dtype == 1 ? launch_bwd_s<false, uint16_t>(G, p, stream)
+                      : launch_bwd_s<false, float>(G, p, stream);
+}
+
+hipError_t launch_sum(const SumParams &p, hipStream_t stream) {
+    if (p.n <= 0) return hipSuccess;
+    const int64_t grid = (p.n + kSumThreads - 1) / kSumThreads;
+    hipLaunchKernelGGL(sum_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kSumThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace r2l

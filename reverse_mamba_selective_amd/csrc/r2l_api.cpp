@@ -246,19 +246,7 @@ r2l_status hip_status(hipError_t e, const char *what) {
     return ok();
 }
 
-r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
-    r2l_status st = check_shape(a);
-    if (st != R2L_OK) return st;
-    const Plan pl = r2l::make_plan(op, a);
-    st = check_buffers(op, a, pl);
-    if (st != R2L_OK) return st;
-    st = check_seqlens_on_device(a);
-    if (st != R2L_OK) return st;
-    if (a->batch * pl.nchunks * pl.tiles > INT32_MAX - 8)
-        return fail(R2L_ERR_UNSUPPORTED, "grid too large");
-
-    Launch ls[3];
-    const int n = r2l::build_launches(op, a, pl, ls);
+r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
     for (int i = 0; i < n; ++i) {
         const Launch &l = ls[i];
         hipError_t e = hipSuccess;
@@ -275,16 +263,176 @@ r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
                 e = r2l::launch_copy(l.dtype, l.copy, stream);
                 what = "residual copy launch";
                 break;
+            case Launch::Backward:
+                e = r2l::launch_backward(l.reverse, l.dtype, l.G, l.bwd, stream);
+                what = "backward launch";
+                break;
+            case Launch::Sum:
+                e = r2l::launch_sum(l.sum, stream);
+                what = "gradient sum launch";
+                break;
         }
-        st = hip_status(e, what);
+        r2l_status st = hip_status(e, what);
         if (st != R2L_OK) return st;
     }
     return ok();
 }
 
+r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    const Plan pl = r2l::make_plan(op, a);
+    st = check_buffers(op, a, pl);
+    if (st != R2L_OK) return st;
+    st = check_seqlens_on_device(a);
+    if (st != R2L_OK) return st;
+    if (a->batch * pl.nchunks * pl.tiles > INT32_MAX - 8)
+        return fail(R2L_ERR_UNSUPPORTED, "grid too large");
+
+    Launch ls[3];
+    const int n = r2l::build_launches(op, a, pl, ls);
+    return execute(ls, n, stream);
+}
+
+// ---- backward -------------------------------------------------------------------
+r2l_status check_backward(const r2l_scan_args *a, const r2l_grad_args *g, const r2l::BwdPlan &pl) {
+    if (!g) return fail(R2L_ERR_INVALID_ARG, "grad is NULL");
+    const int64_t tok = tokens_of(a);
+    const int64_t D = a->dim, N = r2l::kN, es = elem_size(a->dtype);
+    if (ragged(a) && a->batch > 0 && !a->cu_seqlens)
+        return fail(R2L_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    if (a->batch > 0 && !a->A) return fail(R2L_ERR_INVALID_ARG, "A is NULL");
+    if (tok > 0) {
+        const struct { const void *p; const char *n; } req[] = {
+            {a->x, "x"}, {a->dt, "dt"}, {a->Bm, "Bm"}, {a->Cm, "Cm"}, {g->dout, "dout"}};
+        for (const auto &r : req)
+            if (!r.p) return fail(R2L_ERR_INVALID_ARG, "%s is NULL", r.n);
+        if (a->x_stride < D || a->dt_stride < D || g->dout_stride < D)
+            return fail(R2L_ERR_INVALID_ARG, "x, dt or dout stride < dim");
+        if (a->Bm_stride < N || a->Cm_stride < N)
+            return fail(R2L_ERR_INVALID_ARG, "Bm or Cm stride < dstate");
+        if ((g->dx && g->dx_stride < D) || (g->ddt && g->ddt_stride < D))
+            return fail(R2L_ERR_INVALID_ARG, "dx or ddt stride < dim");
+        if (a->res && a->res_stride < D) return fail(R2L_ERR_INVALID_ARG, "res_stride < dim");
+        if (a->x_batch_stride < 0 || a->dt_batch_stride < 0 || a->Bm_batch_stride < 0 ||
+            a->Cm_batch_stride < 0 || g->dout_batch_stride < 0 || g->dx_batch_stride < 0 ||
+            g->ddt_batch_stride < 0)
+            return fail(R2L_ERR_INVALID_ARG, "negative batch stride");
+        const int64_t L = max_len_of(a);
+        const struct { int64_t st, cols; } rows[] = {
+            {a->x_stride, D}, {a->dt_stride, D}, {g->dout_stride, D}, {g->dx ? g->dx_stride : 0, D},
+            {g->ddt ? g->ddt_stride : 0, D}, {a->Bm_stride, N}, {a->Cm_stride, N}};
+        for (const auto &r : rows)
+            if (L > 0 && r.st > 0 && ((L - 1) * r.st + r.cols) * es > (int64_t)UINT32_MAX)
+                return fail(R2L_ERR_UNSUPPORTED, "one sequence spans more than 4 GiB of a tensor");
+        if (!ragged(a) && a->batch > 1) {
+            if (g->dx && eff_bstride(a, g->dx_batch_stride, g->dx_stride) < a->seqlen * g->dx_stride)
+                return fail(R2L_ERR_ALIAS, "dx: sequences overlap");
+            if (g->ddt && eff_bstride(a, g->ddt_batch_stride, g->ddt_stride) < a->seqlen * g->ddt_stride)
+                return fail(R2L_ERR_ALIAS, "ddt: sequences overlap");
+        }
+    }
+    // (with no token there is nothing to tell an empty residual from none: ds is 0)
+    if (g->ds && !a->res && tok > 0)
+        return fail(R2L_ERR_INVALID_ARG, "ds needs a residual (out = y has no gate)");
+    if (pl.ws_bytes > 0 && (!g->workspace || g->workspace_bytes < pl.ws_bytes))
+        return fail(R2L_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", pl.ws_bytes,
+                    g->workspace ? g->workspace_bytes : (size_t)0);
+    if (a->batch * pl.tiles > INT32_MAX - 8) return fail(R2L_ERR_UNSUPPORTED, "grid too large");
+
+    const struct { const void *p; uintptr_t al; const char *n; } al[] = {
+        {a->x, (uintptr_t)es, "x"},       {a->dt, (uintptr_t)es, "dt"},     {a->Bm, (uintptr_t)es, "Bm"},
+        {a->Cm, (uintptr_t)es, "Cm"},     {g->dout, (uintptr_t)es, "dout"}, {g->dx, (uintptr_t)es, "dx"},
+        {g->ddt, (uintptr_t)es, "ddt"},   {a->A, 16, "A"},                  {a->Dskip, 4, "Dskip"},
+        {a->h_in, 16, "h_in"},            {g->dh_out, 16, "dh_out"},        {g->dh_in, 16, "dh_in"},
+        {g->dBm, 4, "dBm"},               {g->dCm, 4, "dCm"},               {g->dA, 4, "dA"},
+        {g->dDskip, 4, "dDskip"},         {g->ds, 4, "ds"},                 {a->cu_seqlens, 4, "cu_seqlens"},
+        {g->workspace, 256, "workspace"}};
+    for (const auto &e : al)
+        if (e.p && !aligned(e.p, e.al))
+            return fail(R2L_ERR_MISALIGNED, "%s is not %u-byte aligned", e.n, (unsigned)e.al);
+
+    // no output may overlap an input or another output
+    const int64_t B = a->batch;
+    std::vector<Range> rs = {
+        token_span("x", a, a->x, a->x_stride, a->x_batch_stride, D, es, false),
+        token_span("dt", a, a->dt, a->dt_stride, a->dt_batch_stride, D, es, false),
+        token_span("Bm", a, a->Bm, a->Bm_stride, a->Bm_batch_stride, N, es, false),
+        token_span("Cm", a, a->Cm, a->Cm_stride, a->Cm_batch_stride, N, es, false),
+        token_span("res", a, a->res, a->res_stride, a->res_batch_stride, D, es, false),
+        token_span("dout", a, g->dout, g->dout_stride, g->dout_batch_stride, D, es, false),
+        span("A", a->A, D, N, N, 4, false),
+        span("Dskip", a->Dskip, 1, D, D, 4, false),
+        span("h_in", a->h_in, B, D * N, D * N, 4, false),
+        span("dh_out", g->dh_out, B, D * N, D * N, 4, false),
+        span("cu_seqlens", a->cu_seqlens, 1, B + 1, B + 1, 4, false),
+        token_span("dx", a, g->dx, g->dx_stride, g->dx_batch_stride, D, es, true),
+        token_span("ddt", a, g->ddt, g->ddt_stride, g->ddt_batch_stride, D, es, true),
+        span("dBm", g->dBm, tok, N, N, 4, true),
+        span("dCm", g->dCm, tok, N, N, 4, true),
+        span("dA", g->dA, D, N, N, 4, true),
+        span("dDskip", g->dDskip, 1, D, D, 4, true),
+        span("dh_in", g->dh_in, B, D * N, D * N, 4, true),
+        span("ds", g->ds, 1, 1, 1, 4, true),
+        span("workspace", pl.ws_bytes ? g->workspace : nullptr, 1, (int64_t)pl.ws_bytes,
+             (int64_t)pl.ws_bytes, 1, true)};
+    for (size_t i = 0; i < rs.size(); ++i)
+        for (size_t j = i + 1; j < rs.size(); ++j)
+            if ((rs[i].is_output || rs[j].is_output) && overlap(rs[i], rs[j]))
+                return fail(R2L_ERR_ALIAS, "%s overlaps %s", rs[i].is_output ? rs[i].name : rs[j].name,
+                            rs[i].is_output ? rs[j].name : rs[i].name);
+    return R2L_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+r2l_status r2l_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad, void *stream) {
+    r2l_status st = check_shape(fwd);
+    if (st != R2L_OK) return st;
+    if (!grad) return fail(R2L_ERR_INVALID_ARG, "grad is NULL");
+    const r2l::BwdPlan pl = r2l::make_bwd_plan(fwd, grad);
+    st = check_backward(fwd, grad, pl);
+    if (st != R2L_OK) return st;
+    st = check_seqlens_on_device(fwd);
+    if (st != R2L_OK) return st;
+    Launch ls[r2l::kMaxBwdLaunches];
+    const int n = r2l::build_bwd_launches(fwd, grad, pl, ls);
+    return execute(ls, n, static_cast<hipStream_t>(stream));
+}
+
+r2l_status r2l_check_access_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                     const int32_t *cu_seqlens_host, r2l_access_report *report) {
+    if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
+    report->launches = report->accesses = report->vector_staging = 0;
+    report->message[0] = '\0';
+    r2l_status st = check_shape(fwd);
+    if (st != R2L_OK) return st;
+    if (!grad) return fail(R2L_ERR_INVALID_ARG, "grad is NULL");
+    const r2l::BwdPlan pl = r2l::make_bwd_plan(fwd, grad);
+    st = check_backward(fwd, grad, pl);
+    if (st != R2L_OK) return st;
+    if (ragged(fwd) && fwd->batch > 0) {
+        if (!cu_seqlens_host) return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[fwd->batch] != fwd->total_tokens)
+            return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host does not span total_tokens");
+    }
+    st = r2l::check_backward_accesses(fwd, grad, pl, cu_seqlens_host, report);
+    if (st != R2L_OK && report->message[0]) fail(st, "%s", report->message);
+    return st == R2L_OK ? ok() : st;
+}
+
+r2l_status r2l_backward_workspace_size(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                       size_t *bytes) {
+    if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
+    r2l_status st = check_shape(fwd);
+    if (st != R2L_OK) return st;
+    if (!grad) return fail(R2L_ERR_INVALID_ARG, "grad is NULL");
+    *bytes = r2l::make_bwd_plan(fwd, grad).ws_bytes;
+    return ok();
+}
+
 
 r2l_status r2l_scan(const r2l_scan_args *a, void *stream) {
     return run(Op::Scan, a, static_cast<hipStream_t>(stream));
@@ -312,7 +460,7 @@ r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes)
 r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *cu_seqlens_host,
                             r2l_access_report *report) {
     if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
-    report->launches = report->accesses = 0;
+    report->launches = report->accesses = report->vector_staging = 0;
     report->message[0] = '\0';
     if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT)
         return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);

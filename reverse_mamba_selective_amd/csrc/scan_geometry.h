@@ -48,14 +48,22 @@ R2L_HD BlockGeom block_geom(int64_t nblocks, int32_t tiles, int32_t nchunks, int
     return g;
 }
 
-// Sequence b: its length and the element offset of its first row in each
-// token-major tensor. s0, s1 are cu_seqlens[b], cu_seqlens[b+1] (ragged).
+// Packed token index of sequence b's first row (the row space of the
+// workspace's per-token arrays): the ragged offset, or b * seqlen.
+R2L_HD int64_t packed_start(const int32_t *cu_seqlens, int64_t seqlen, int64_t b, int64_t s0) {
+    return cu_seqlens ? s0 : b * seqlen;
+}
+
+// Sequence b: its length, its packed start and the element offset of its
+// first row in each token-major tensor. s0, s1 are cu_seqlens[b],
+// cu_seqlens[b+1] (ragged).
 struct SeqGeom {
-    int64_t len, xo, dto, Bo, Co, ro, oo;
+    int64_t len, s0p, xo, dto, Bo, Co, ro, oo;
 };
 
 R2L_HD SeqGeom seq_geom(const SegParams &p, int64_t b, int64_t s0, int64_t s1) {
     SeqGeom q;
+    q.s0p = packed_start(p.cu_seqlens, p.seqlen, b, s0);
     if (p.cu_seqlens) {
         q.len = s1 - s0;
         q.xo = s0 * p.xs; q.dto = s0 * p.dts; q.Bo = s0 * p.Bs; q.Co = s0 * p.Cs;
@@ -194,6 +202,46 @@ R2L_HD CarryGeom carry_geom(int64_t D, int64_t bx, int64_t by, int tid) {
     g.d = i >> 4;
     g.b = bx;
     return g;
+}
+
+// ---- backward ---------------------------------------------------------------
+// Checkpoint row of the group starting at visited position pos (a multiple
+// of kCkptTokens) of the sequence starting at packed token s0p: distinct for
+// every (sequence, group), below ckpt_rows().
+R2L_HD int64_t ckpt_row(int64_t b, int64_t s0p, int64_t pos) { return (s0p + pos) / kCkptTokens + b; }
+R2L_HD int64_t ckpt_rows(int64_t tokens, int64_t batch) { return tokens / kCkptTokens + batch + 1; }
+
+// Sequence b in the backward's tensors (element offsets of its first row).
+struct BwdSeqGeom {
+    int64_t len, s0p, xo, dto, Bo, Co, go, dxo, ddo;
+};
+
+R2L_HD BwdSeqGeom bwd_seq_geom(const BwdParams &p, int64_t b, int64_t s0, int64_t s1) {
+    BwdSeqGeom q;
+    q.s0p = packed_start(p.cu_seqlens, p.seqlen, b, s0);
+    if (p.cu_seqlens) {
+        q.len = s1 - s0;
+        q.xo = s0 * p.xs; q.dto = s0 * p.dts; q.Bo = s0 * p.Bs; q.Co = s0 * p.Cs;
+        q.go = s0 * p.gs; q.dxo = s0 * p.dxs; q.ddo = s0 * p.dds;
+    } else {
+        q.len = p.seqlen;
+        q.xo = b * p.xbs; q.dto = b * p.dtbs; q.Bo = b * p.Bbs; q.Co = b * p.Cbs;
+        q.go = b * p.gbs; q.dxo = b * p.dxbs; q.ddo = b * p.ddbs;
+    }
+    return q;
+}
+
+// The state index whose sum over a wave's channels lane `lane` (< 16) holds
+// after the transpose-reduce with G lanes per channel (each exchange step on
+// lane bit log2(G) + j keeps the upper half of the remaining states in the
+// lanes whose bit is set).
+R2L_HD int reduced_state(int G, int lane) {
+    const int lg = G == 1 ? 0 : (G == 2 ? 1 : 2);
+    const int ns = kN / G;
+    int n = (lane & (G - 1)) * ns;
+    for (int j = 0; (ns >> j) > 1; ++j)
+        if ((lane >> (lg + j)) & 1) n += ns >> (j + 1);
+    return n;
 }
 
 // Row copy: kCopyThreads columns per block along x, rows along y (looping

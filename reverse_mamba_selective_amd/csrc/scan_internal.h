@@ -56,6 +56,58 @@ struct SegParams {
     int32_t split_c0;   // chunk pass: chunk 0 reads out from hin, chunks > 0 are state only from 0
     int32_t skip_c0;    // readout pass: chunk 0 was written by the chunk pass
     int32_t skip_last;  // chunk pass: skip each sequence's last chunk (c > 0)
+
+    // backward, phase 1 (state-only, unchunked): the state before every
+    // kCkptTokens-th visited position, at ckpt + (ckpt_row * D + d) * kN
+    float *ckpt;
+};
+
+// ---- backward (gradients of a scan with readout) ----------------------------
+// Visited positions are taken in groups of kCkptTokens; phase 1 stores the
+// state entering each group, phase 2 recomputes a group's states from it and
+// runs the adjoint over the group backwards.
+constexpr int kCkptTokens = 8;
+
+struct BwdParams {
+    int64_t seqlen;              // dense tokens per sequence (when cu_seqlens == nullptr)
+    const int32_t *cu_seqlens;
+    int64_t D;
+    int32_t tiles;               // channel tiles per sequence (kWG / G channels each)
+    int64_t nblocks;             // batch * tiles
+    int64_t tokens;              // packed token count (row space of the partial sums)
+
+    const void *x;  int64_t xs, xbs;
+    const void *dt; int64_t dts, dtbs;
+    const void *Bm; int64_t Bs, Bbs;
+    const void *Cm; int64_t Cs, Cbs;
+    int32_t bc_vec;
+    const float *A;
+    const float *Dskip;
+    int32_t softplus;
+
+    float dyscale;               // dL/dy = dyscale * dout (s with a residual, else 1)
+    float dxres;                 // 1 when the residual is x itself (dx += dout), else 0
+    int32_t want_ds;             // accumulate dout * y for ds
+
+    const float *ckpt;           // phase 1's checkpoints
+    const void *dout; int64_t gs, gbs;
+    const float *dh_out;         // [batch, D, kN] or nullptr
+    void *dx;  int64_t dxs, dxbs;     // or nullptr
+    void *ddt; int64_t dds, ddbs;     // or nullptr
+    float *dh_in;                // [batch, D, kN] or nullptr
+
+    // partial sums, reduced by sum launches in a fixed order
+    float *partB, *partC;        // [tiles][tokens][kN]: over the block's channels
+    float *partA;                // [batch][D][kN]: over the sequence's tokens
+    float *partD;                // [batch][D]
+    float *partS;                // [nblocks]
+};
+
+// dst[i] = sum over p < P of src[p * pstride + i], for i < n (in order of p).
+struct SumParams {
+    const float *src;
+    int64_t P, pstride, n;
+    float *dst;
 };
 
 // Joins chunk results (local final state Q from a zero start and the Delta sum
@@ -93,5 +145,8 @@ hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode,
                                const SegParams &p, hipStream_t stream);
 hipError_t launch_carry(const CarryParams &p, hipStream_t stream);
 hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream);
+// G in {2, 4}
+hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, hipStream_t stream);
+hipError_t launch_sum(const SumParams &p, hipStream_t stream);
 
 }  // namespace r2l

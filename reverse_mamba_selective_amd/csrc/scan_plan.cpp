@@ -239,4 +239,122 @@ int build_scan_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch ou
 }
 
 }  // namespace
+
+// ---- backward ------------------------------------------------------------------
+BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
+    BwdPlan pl;
+    pl.G = 4;
+    pl.tiles = (a->dim * pl.G + kWG - 1) / kWG;
+    pl.fwd_tiles = (a->dim + kWG - 1) / kWG;
+    pl.tokens = tokens_of(a);
+    pl.ck_rows = ckpt_rows(pl.tokens, a->batch);
+    if (a->res) {
+        const bool is_x = a->res == a->x && a->res_stride == a->x_stride &&
+                          eff_bstride(a, a->res_batch_stride, a->res_stride) ==
+                              eff_bstride(a, a->x_batch_stride, a->x_stride);
+        pl.res_kind = is_x ? 1 : 2;
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    const size_t D = static_cast<size_t>(a->dim), B = static_cast<size_t>(a->batch);
+    const size_t T = static_cast<size_t>(pl.tokens), tiles = static_cast<size_t>(pl.tiles);
+    pl.off_ck = take(pl.tokens > 0 ? static_cast<size_t>(pl.ck_rows) * D * kN * 4 : 0);
+    pl.off_B = take(g->dBm ? tiles * T * kN * 4 : 0);
+    pl.off_C = take(g->dCm ? tiles * T * kN * 4 : 0);
+    pl.off_A = take(g->dA ? B * D * kN * 4 : 0);
+    pl.off_D = take(g->dDskip ? B * D * 4 : 0);
+    pl.off_S = take(g->ds ? B * tiles * 4 : 0);
+    pl.ws_bytes = off;
+    return pl;
+}
+
+int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const BwdPlan &pl,
+                       Launch out[kMaxBwdLaunches]) {
+    char *ws = static_cast<char *>(g->workspace);
+    auto at = [&](size_t off, bool want) { return want ? reinterpret_cast<float *>(ws + off) : nullptr; };
+    float *ck = at(pl.off_ck, pl.tokens > 0);
+    float *pB = at(pl.off_B, g->dBm != nullptr), *pC = at(pl.off_C, g->dCm != nullptr);
+    float *pA = at(pl.off_A, g->dA != nullptr), *pD = at(pl.off_D, g->dDskip != nullptr);
+    float *pS = at(pl.off_S, g->ds != nullptr);
+    const int64_t D = a->dim;
+    int n = 0;
+
+    if (a->batch > 0) {
+        // phase 1: the forward state scan, one lane per channel, unchunked, with checkpoints
+        if (pl.tokens > 0) {
+            Plan fp;
+            fp.G = 1;
+            fp.chunk_len = std::max<int64_t>(max_len_of(a), 1);
+            fp.nchunks = 1;
+            fp.tiles = pl.fwd_tiles;
+            SegParams p = base_params(a, fp);
+            p.hin = a->h_in; p.hin_b = D * kN; p.hin_c = 0;
+            p.res = nullptr;
+            p.out = nullptr;
+            p.ckpt = ck;
+            p.bc_vec = bc_vector_ok(a, false) ? 1 : 0;
+            Launch l{};
+            l.kind = Launch::Segment;
+            l.reverse = true;
+            l.dtype = a->dtype;
+            l.G = 1;
+            l.mode = kModeState;
+            l.seg = p;
+            out[n++] = l;
+        }
+        // phase 2: the adjoint
+        BwdParams q{};
+        q.seqlen = is_ragged(a) ? 0 : a->seqlen;
+        q.cu_seqlens = a->cu_seqlens;
+        q.D = D;
+        q.tiles = static_cast<int32_t>(pl.tiles);
+        q.nblocks = a->batch * pl.tiles;
+        q.tokens = pl.tokens;
+        q.x = a->x;   q.xs = a->x_stride;   q.xbs = eff_bstride(a, a->x_batch_stride, a->x_stride);
+        q.dt = a->dt; q.dts = a->dt_stride; q.dtbs = eff_bstride(a, a->dt_batch_stride, a->dt_stride);
+        q.Bm = a->Bm; q.Bs = a->Bm_stride;  q.Bbs = eff_bstride(a, a->Bm_batch_stride, a->Bm_stride);
+        q.Cm = a->Cm; q.Cs = a->Cm_stride;  q.Cbs = eff_bstride(a, a->Cm_batch_stride, a->Cm_stride);
+        q.bc_vec = bc_vector_ok(a, true) ? 1 : 0;
+        q.A = a->A;
+        q.Dskip = a->Dskip;
+        q.softplus = a->delta_softplus;
+        q.dyscale = pl.res_kind ? a->s : 1.0f;
+        q.dxres = pl.res_kind == 1 ? 1.0f : 0.0f;
+        q.want_ds = g->ds ? 1 : 0;
+        q.ckpt = ck;
+        q.dout = g->dout; q.gs = g->dout_stride;
+        q.gbs = eff_bstride(a, g->dout_batch_stride, g->dout_stride);
+        q.dh_out = g->dh_out;
+        q.dx = g->dx;   q.dxs = g->dx_stride;   q.dxbs = eff_bstride(a, g->dx_batch_stride, g->dx_stride);
+        q.ddt = g->ddt; q.dds = g->ddt_stride;  q.ddbs = eff_bstride(a, g->ddt_batch_stride, g->ddt_stride);
+        q.dh_in = g->dh_in;
+        q.partB = pB; q.partC = pC; q.partA = pA; q.partD = pD; q.partS = pS;
+        Launch l{};
+        l.kind = Launch::Backward;
+        l.reverse = true;
+        l.dtype = a->dtype;
+        l.G = pl.G;
+        l.bwd = q;
+        out[n++] = l;
+    }
+    // the ordered sums (with no sequence they write zeros)
+    auto sum = [&](const float *src, int64_t P, int64_t pstride, int64_t cnt, float *dst) {
+        Launch l{};
+        l.kind = Launch::Sum;
+        l.sum = SumParams{src, P, pstride, cnt, dst};
+        out[n++] = l;
+    };
+    const int64_t T = pl.tokens;
+    if (g->dBm && T > 0) sum(pB, pl.tiles, T * kN, T * kN, g->dBm);
+    if (g->dCm && T > 0) sum(pC, pl.tiles, T * kN, T * kN, g->dCm);
+    if (g->dA) sum(pA, a->batch, D * kN, D * kN, g->dA);
+    if (g->dDskip) sum(pD, a->batch, D, D, g->dDskip);
+    if (g->ds) sum(pS, a->batch * pl.tiles, 1, 1, g->ds);
+    return n;
+}
+
 }  // namespace r2l

@@ -24,7 +24,7 @@ struct Plan {
 };
 
 struct Launch {
-    enum Kind { Segment, Carry, Copy } kind;
+    enum Kind { Segment, Carry, Copy, Backward, Sum } kind;
     bool reverse;
     int dtype;
     int G;
@@ -32,7 +32,27 @@ struct Launch {
     SegParams seg;
     CarryParams carry;
     CopyParams copy;
+    BwdParams bwd;
+    SumParams sum;
 };
+
+// The backward of r2l_scan: phase 1 (state-only segment scan writing
+// checkpoints), phase 2 (the adjoint) and up to five ordered sums.
+constexpr int kMaxBwdLaunches = 7;
+struct BwdPlan {
+    int G = 4;               // lanes per channel in phase 2
+    int64_t tiles = 0;       // phase-2 channel tiles per sequence
+    int64_t fwd_tiles = 0;   // phase-1 tiles (one lane per channel)
+    int64_t tokens = 0;
+    int64_t ck_rows = 0;
+    size_t ws_bytes = 0;
+    size_t off_ck = 0, off_B = 0, off_C = 0, off_A = 0, off_D = 0, off_S = 0;
+    int res_kind = 0;        // 0: none, 1: the residual is x, 2: a separate residual
+};
+
+BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g);
+int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const BwdPlan &pl,
+                       Launch out[kMaxBwdLaunches]);
 
 inline bool is_ragged(const r2l_scan_args *a) { return a->cu_seqlens != nullptr; }
 inline int64_t tokens_of(const r2l_scan_args *a) {

@@ -49,11 +49,15 @@ def test_abi_version_and_status_strings():
     assert _abi.status_string(-99) == "unknown status"
 
 
-def test_struct_layout_matches_c():
-    fields = [f[0] for f in _abi.ScanArgs._fields_]
-    prog = ["#include <stddef.h>", "#include <stdio.h>", '#include "r2l_scan.h"', "int main(void){",
-            'printf("%zu\\n", sizeof(r2l_scan_args));']
-    prog += ['printf("%%zu\\n", offsetof(r2l_scan_args, %s));' % f for f in fields]
+@pytest.mark.parametrize("cls,cname", [(_abi.ScanArgs, "r2l_scan_args"),
+                                        (_abi.GradArgs, "r2l_grad_args"),
+                                        (_abi.AccessReport, "r2l_access_report"),
+                                        (_abi.PlanInfo, "r2l_plan_info")])
+def test_struct_layout_matches_c(cls, cname):
+    fields = [f[0] for f in cls._fields_]
+    prog = ["#include <stddef.h>", "#include <stdio.h>", '#include "r2l_scan_debug.h"',
+            "int main(void){", 'printf("%%zu\\n", sizeof(%s));' % cname]
+    prog += ['printf("%%zu\\n", offsetof(%s, %s));' % (cname, f) for f in fields]
     prog += ["return 0;}"]
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "layout.c")
@@ -62,9 +66,9 @@ def test_struct_layout_matches_c():
         subprocess.run(["gcc", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
         vals = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
                                                check=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(_abi.ScanArgs)
+    assert vals[0] == ctypes.sizeof(cls)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(_abi.ScanArgs, f).offset == off, f
+        assert getattr(cls, f).offset == off, f
 
 
 # ---- argument checks (fake device addresses: nothing is ever launched) ------

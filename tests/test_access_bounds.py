@@ -248,3 +248,92 @@ def test_ragged_prefix_shape():
     import synth
     rep = check("prefix", lengths=synth.ragged_prefix_lengths(), D=4096, out=False, chunk=0)
     assert rep.launches == 2 and rep.accesses > 10**8
+
+
+# ---- the backward ---------------------------------------------------------------
+def make_grad(a, heap, *, dtype="bf16", grads=("dx", "ddt", "dBm", "dCm", "dA", "dDskip", "dh_in",
+                                               "ds"), dh_out=True, pad_row=0):
+    """Gradient buffers for the forward call `a` (layout as its x)."""
+    es = 2 if dtype == "bf16" else 4
+    D, N = a.dim, 16
+    tok = a.total_tokens if a.cu_seqlens else a.batch * a.seqlen
+    g = _abi.GradArgs()
+
+    def tensor():
+        stride = D + pad_row
+        if a.cu_seqlens:
+            return heap.alloc(((tok - 1) * stride + D) * es if tok else 0), stride, 0
+        bst = a.seqlen * stride
+        ext = ((a.batch - 1) * bst + (a.seqlen - 1) * stride + D) if tok else 0
+        return heap.alloc(ext * es), stride, 0
+
+    g.dout, g.dout_stride, g.dout_batch_stride = tensor()
+    if dh_out:
+        g.dh_out = heap.alloc(4 * a.batch * D * N)
+    for n in ("dx", "ddt"):
+        if n in grads:
+            p, st, bst = tensor()
+            setattr(g, n, p)
+            setattr(g, n + "_stride", st)
+            setattr(g, n + "_batch_stride", bst)
+    sizes = {"dBm": tok * N, "dCm": tok * N, "dA": D * N, "dDskip": D, "dh_in": a.batch * D * N,
+             "ds": 1}
+    for n, cnt in sizes.items():
+        if n in grads and (n != "ds" or a.res):
+            setattr(g, n, heap.alloc(4 * cnt))
+    need = _abi.backward_workspace_size(a, g)
+    if need:
+        g.workspace, g.workspace_bytes = heap.alloc(need), need
+    return g
+
+
+def check_bwd(grads=None, dh_out=True, **kw):
+    res = kw.pop("res", "none")
+    a, cu = make_args("scan", res=res, **kw)
+    heap = FakeHeap()
+    heap.next = BASE + (1 << 40)   # away from the forward buffers
+    g = make_grad(a, heap, dtype=kw.get("dtype", "bf16"), dh_out=dh_out,
+                  pad_row=kw.get("pad_row", 0),
+                  **({"grads": grads} if grads is not None else {}))
+    st, rep = _abi.check_access_backward(a, g, cu)
+    msg = rep.message.decode() or _abi.last_error()
+    assert st == _abi.R2L_OK, "backward %s: %s" % (kw, msg)
+    return rep
+
+
+BWD_EDGE = [
+    dict(lengths=[0, 0]),
+    dict(lengths=[5, 0, 1, 7, 8, 9, 64, 65, 130]),
+    dict(batch=3, seqlen=0),
+    dict(batch=2, seqlen=1),
+    dict(batch=2, seqlen=73, D=37),
+    dict(batch=2, seqlen=200, D=100, pad_row=8, pad_batch=40),
+    dict(lengths=[300, 17], D=1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BWD_EDGE)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_edge_cases(case, dtype):
+    kw = dict(BWD_EDGE[case], dtype=dtype)
+    kw.setdefault("D", 64)
+    for res in ("none", "x", "sep"):
+        check_bwd(res=res, h_in=True, **kw)
+    check_bwd(grads=("dx",), dh_out=False, **kw)
+    check_bwd(grads=("dBm", "dA"), **kw)
+    check_bwd(grads=(), **kw)
+
+
+def test_backward_workspace_tracks_the_outputs():
+    a, _ = make_args("scan", batch=4, seqlen=100, D=64)
+    heap = FakeHeap()
+    heap.next = BASE + (1 << 40)
+    full = _abi.backward_workspace_size(a, make_grad(a, heap))
+    only_dx = _abi.backward_workspace_size(a, make_grad(a, heap, grads=("dx",)))
+    assert full > only_dx > 0   # checkpoints always; partial sums only when wanted
+
+
+def test_backward_benchmarked_shapes():
+    check_bwd(batch=64, seqlen=32, D=2048, res="x")
+    rep = check_bwd(batch=8, seqlen=4096, D=4096)
+    assert rep.launches == 6   # phase 1, phase 2, sums for dBm, dCm, dA, dDskip (no ds: no residual)
