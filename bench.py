@@ -228,6 +228,7 @@ class Denoise(Workload):
         self.R = _rotation(set_bytes)
         self.step_calls = []
         self.outs0 = []
+        self._bound_inputs = {}
         for r in range(self.R):
             row = []
             for h, g in enumerate(base):
@@ -235,9 +236,11 @@ class Denoise(Workload):
                 out = torch.empty_like(x)
                 if r == 0:
                     self.outs0.append(out)
-                row.append(r2l.bind(self.entry, x=x, dt=g["dt"].clone(), Bm=g["Bm"].clone(),
-                                    Cm=g["Cm"].clone(), A=g["A"], Dskip=g["Dskip"], res=x,
-                                    s=float(self.gates[h]), out=out))
+                ins = {"dt": g["dt"].clone(), "Bm": g["Bm"].clone(), "Cm": g["Cm"].clone(),
+                       "A": g["A"], "Dskip": g["Dskip"]}
+                self._bound_inputs.setdefault(r, {})[h] = dict(ins, x=x)
+                row.append(r2l.bind(self.entry, x=x, res=x, s=float(self.gates[h]), out=out,
+                                    **ins))
             self.step_calls.append(row)
         self.step_entries = [0] * self.HOOKS
         self.measure = [dict(label="%s (one hook)" % self.entry,
@@ -277,6 +280,80 @@ class Denoise(Workload):
 
     parity_spec = ("out", "bf16", 2e-2,
                    "out = x + s*y of all 7 hooks (first buffer set) vs the oracle's")
+
+
+def bwd_alu_ops_per_tc() -> float:
+    """Algorithmic VALU lane-ops per token·channel of the backward (N = 16,
+    trans ops weighted), without recomputation: the forward states (89), per
+    state the adjoint (g += dy*C; dy*h and its sum over channels; the dDelta
+    term B*x + A*(abar*h_prev) and its fma; dA += g*Delta*(abar*h_prev); dx's
+    g*B; g*Delta*x and its sum over channels; g *= abar: 13), per channel the
+    readout for ds (17), dy, ds, dDskip, dx (2) and sigmoid (2 trans + 2)."""
+    return alu_ops_per_tc(False, False) + 16 * 13 + 17 + 1 + 1 + 1 + 2 + (2 * TRANS_SLOTS + 2)
+
+
+class DenoiseBackward(Denoise):
+    """The backward of the 7 hooked reverse scans of one denoising step (training
+    the R2L stream): r2l_scan_backward with res = x, all gradients."""
+    name = "denoise_backward_bf16_b64_blk32_D2048_N16_7hooks"
+
+    def setup(self, torch, r2l):
+        import synth
+        super().setup(torch, r2l)
+        tok = self.B * self.L
+        # bytes: x, dt, dout in; dx, ddt out (bf16); Bm, Cm in (bf16); dBm, dCm out (fp32);
+        # A in, dA out, Dskip in, dDskip out, ds
+        self.bytes_per_launch = (tok * self.D * 2 * 5 + tok * 16 * (2 * 2 + 4 * 2) +
+                                 self.D * 16 * 4 * 2 + self.D * 4 * 2 + 4)
+        self.alu_per_launch = self.tc_per_launch * bwd_alu_ops_per_tc()
+        self.bwd_calls, self.bwd_grads = [], []
+        for r, row in enumerate(self.step_calls):
+            brow = []
+            for h in range(len(row)):
+                x = self._bound_inputs[r][h]["x"]
+                g = torch.Generator(device="cuda")
+                g.manual_seed(5000 + 7 * r + h)
+                dout = torch.randn(x.shape, generator=g, device="cuda").to(x.dtype)
+                inp_args = self._bound_inputs[r][h]
+                bc = r2l.bind_backward(x, inp_args["dt"], inp_args["Bm"], inp_args["Cm"],
+                                       inp_args["A"], inp_args["Dskip"], dout=dout, res=x,
+                                       s=float(self.gates[h]))
+                brow.append(bc)
+                if r == 0:
+                    self.bwd_grads.append((h, dout, bc.grads))
+            self.bwd_calls.append(brow)
+        self.step_calls = self.bwd_calls
+        self.measure = [dict(label="r2l_scan_backward (one hook)",
+                             calls=[c for row in self.bwd_calls for c in row],
+                             bytes=self.bytes_per_launch, alu=self.alu_per_launch,
+                             tc=self.tc_per_launch)]
+        self.config = dict(self.config, workload=self.name, op="r2l_scan_backward",
+                           grads=list(r2l.GRADS))
+
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
+        import oracle
+        tc, secs, hooks = 0, 0.0, 0
+        while secs < budget_s and hooks < 7 * 20:
+            h, dout, grads = self.bwd_grads[hooks % len(self.bwd_grads)]
+            inp = self.inputs[h]
+            t = {}
+            ref = oracle.selective_scan_backward(
+                inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=True,
+                dout=dout.float().cpu().numpy().reshape(inp.x.shape), res_kind="x",
+                s=float(self.gates[h]), seq_offsets=inp.offsets, timing=t, nthreads=nthreads)
+            if parity is not None and hooks < len(self.bwd_grads):
+                parity.add(grads["dA"].cpu().numpy(), ref["dA"])
+                parity.add(grads["dBm"].cpu().numpy().reshape(ref["dBm"].shape), ref["dBm"])
+            secs += t["seconds"]
+            tc += inp.x.size
+            hooks += 1
+        return {"value": tc / secs, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "%d hook backwards (%d token-channels), %.1f s of oracle time"
+                          % (hooks, tc, secs)}
+
+    parity_spec = ("dA, dBm", "f32", 1e-4,
+                   "dA and dBm of all 7 hooks (first buffer set) vs the oracle's fp64 backward")
 
 
 class DenoiseL2R(Denoise):
@@ -509,7 +586,7 @@ class RaggedPrefix(Workload):
 
 
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
-             "prefix": RaggedPrefix, "l2r": DenoiseL2R}
+             "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward}
 
 
 def main():

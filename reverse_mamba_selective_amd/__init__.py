@@ -23,7 +23,8 @@ from . import _abi
 from ._abi import R2LError  # noqa: F401
 
 __all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "workspace_size", "bind",
-           "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "R2LScan", "GRADS"]
+           "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "bind_backward",
+           "BoundBackward", "R2LScan", "GRADS"]
 
 _DTYPES = {torch.float32: _abi.R2L_DTYPE_F32, torch.bfloat16: _abi.R2L_DTYPE_BF16}
 
@@ -294,9 +295,35 @@ def _fill_grad(a, x, Bm, dout, dh_out, outs):
     return g
 
 
+class BoundBackward:
+    """One r2l_scan_backward call with its argument structs filled once (see
+    BoundCall); ``grads`` holds the output tensors."""
+
+    def __init__(self, args, grad, keep, grads, workspace, device):
+        self.args, self.grad, self._keep = args, grad, keep
+        self.grads, self.workspace, self.device = grads, workspace, device
+        self._fn = _abi.load().r2l_scan_backward
+        self._a, self._g = _abi.ctypes.byref(args), _abi.ctypes.byref(grad)
+
+    def launch(self, stream=None):
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        st = self._fn(self._a, self._g, _abi._vp(stream))
+        if st != _abi.R2L_OK:
+            raise R2LError(st, "r2l_scan_backward", _abi.last_error())
+
+
+def bind_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, **kw) -> BoundBackward:
+    """Check and marshal a ``r2l_scan_backward`` call once (same keywords);
+    the outputs are allocated here (or taken from ``out``)."""
+    kw = dict(kw)
+    kw["_bind"] = True
+    return r2l_scan_backward(x, dt, Bm, Cm, A, Dskip, dout=dout, **kw)
+
+
 def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seqlens=None,
                       max_seqlen=None, h_in=None, res=None, s=0.0, delta_softplus=True,
-                      grads=GRADS, out=None, workspace=None):
+                      grads=GRADS, out=None, workspace=None, _bind=False):
     """Gradients of ``r2l_scan`` (same forward arguments) for ``dout`` = dL/dout
     and ``dh_out`` = dL/dh_out. Returns a dict of the names in ``grads``: dx,
     ddt (like x), dBm, dCm (fp32, shaped like Bm), dA [D, N], dDskip [D],
@@ -328,6 +355,9 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
             raise ValueError("workspace has %d bytes, the backward needs %d"
                              % (workspace.numel() * workspace.element_size(), need))
         g.workspace, g.workspace_bytes = workspace.data_ptr(), need
+    if _bind:
+        keep = (x, dt, Bm, Cm, A, Dskip, dout, dh_out, cu_seqlens, h_in, res)
+        return BoundBackward(a, g, keep, outs, workspace, x.device)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
     _abi.call_backward(a, g, stream)

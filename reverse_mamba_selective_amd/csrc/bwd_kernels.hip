@@ -156,11 +156,25 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                                  E::word_elem(stw, 4 * q + 2), E::word_elem(stw, 4 * q + 3));
     };
 
+    // per-token inputs of one group (positions past its end repeat its last one)
+    R nx[K], nd[K], ng[K];
+    auto load_group = [&](int gpos, int gcnt) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint32_t row = static_cast<uint32_t>(seg_row(sg, gpos + (j < gcnt ? j : gcnt - 1)));
+            nx[j] = E::bload(rx, doff, row * xrb);
+            nd[j] = E::bload(rd, doff, row * drb);
+            ng[j] = E::bload(rg, doff, row * grb);
+        }
+    };
+
     // tiles (and the groups inside them) from the last visited to the first
     const int ntiles = (ntok + kTile - 1) / kTile;
     if (ntok > 0) {
         const int lb = (ntiles - 1) * kTile;
         stage_load(lb, ntok - lb);
+        const int lg0 = (ntok - 1) / K * K;   // the last group
+        load_group(lg0, ntok - lg0);
         stage_store((ntiles - 1) & 1);
     }
     __syncthreads();
@@ -174,22 +188,23 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
         for (int gi = (tcnt - 1) / K; gi >= 0; --gi) {
             const int gpos = tbase + gi * K;
             const int gcnt = ntok - gpos < K ? ntok - gpos : K;
-            // the group's per-token inputs (positions past its end repeat its last one)
+            // this group's per-token inputs were requested during the previous
+            // group; request the next group's (gpos - K) now
             R xr[K], dr[K], gr[K];
 #pragma unroll
             for (int j = 0; j < K; ++j) {
-                const uint32_t row = static_cast<uint32_t>(seg_row(sg, gpos + (j < gcnt ? j : gcnt - 1)));
-                xr[j] = E::bload(rx, doff, row * xrb);
-                dr[j] = E::bload(rd, doff, row * drb);
-                gr[j] = E::bload(rg, doff, row * grb);
+                xr[j] = nx[j];
+                dr[j] = nd[j];
+                gr[j] = ng[j];
             }
+            if (gpos > 0) load_group(gpos - K, K);
             float hck[NS];
             const float *cp = p.ckpt + (ckpt_row(b, sq.s0p, gpos) * p.D + dl) * kN + sub * NS;
 #pragma unroll
             for (int n = 0; n < NS; ++n) hck[n] = cp[n];
 
-            // the group's states, recomputed forward from the checkpoint
-            float hs[K][NS], delta[K];
+            // the group's states and decays, recomputed forward from the checkpoint
+            float hs[K][NS], ab[K][NS], delta[K];
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 const float dv = E::widen(dr[j]);
@@ -202,7 +217,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
                     const float hp = j > 0 ? hs[j - 1][n] : hck[n];
-                    hs[j][n] = fmaf(__builtin_amdgcn_exp2f(delta[j] * a2[n]), hp, brow[n] * dx_);
+                    ab[j][n] = __builtin_amdgcn_exp2f(delta[j] * a2[n]);
+                    hs[j][n] = fmaf(ab[j][n], hp, brow[n] * dx_);
                 }
             }
 
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                     g[n] = fmaf(dy, row[kN + n], g[n]);
                     pc[n] = dy * hs[j][n];
                     const float hp = j > 0 ? hs[j - 1][n] : hck[n];
-                    const float a = __builtin_amdgcn_exp2f(delta[j] * a2[n]);
+                    const float a = ab[j][n];
                     const float ah = a * hp;
                     const float bn = row[n];
                     dd = fmaf(g[n], fmaf(bn, xv, An[n] * ah), dd);
@@ -297,13 +313,40 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 }
 
 constexpr int kSumThreads = 256;
+// Outputs below this count are summed by a whole block each (threads split
+// the partials, then a fixed tree in LDS); above it, one thread per output.
+constexpr int64_t kNarrowSum = 4096;
 
 __global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumParams p) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kSumThreads + threadIdx.x;
     if (i >= p.n) return;
+    // partials in order of q, four independent loads in flight
     float acc = 0.0f;
-    for (int64_t q = 0; q < p.P; ++q) acc += p.src[q * p.pstride + i];
+    int64_t q = 0;
+    for (; q + 4 <= p.P; q += 4) {
+        const float v0 = p.src[q * p.pstride + i], v1 = p.src[(q + 1) * p.pstride + i];
+        const float v2 = p.src[(q + 2) * p.pstride + i], v3 = p.src[(q + 3) * p.pstride + i];
+        acc = (((acc + v0) + v1) + v2) + v3;
+    }
+    for (; q < p.P; ++q) acc += p.src[q * p.pstride + i];
     p.dst[i] = acc;
+}
+
+// One block per output: thread t sums partials t, t + 256, ... in order, then
+// a fixed binary tree over the threads.
+__global__ __launch_bounds__(kSumThreads) void sum_narrow_kernel(const SumParams p) {
+    __shared__ float part[kSumThreads];
+    const int64_t i = blockIdx.x;
+    float acc = 0.0f;
+    for (int64_t q = threadIdx.x; q < p.P; q += kSumThreads) acc += p.src[q * p.pstride + i];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int w = kSumThreads / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) p.dst[i] = part[0];
 }
 
 template <bool REV, typename T, bool SP>
@@ -340,8 +383,14 @@ hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, h
 
 hipError_t launch_sum(const SumParams &p, hipStream_t stream) {
     if (p.n <= 0) return hipSuccess;
-    const int64_t grid = (p.n + kSumThreads - 1) / kSumThreads;
-    hipLaunchKernelGGL(sum_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kSumThreads), 0, stream, p);
+    if (p.n < kNarrowSum) {
+        hipLaunchKernelGGL(sum_narrow_kernel, dim3(static_cast<uint32_t>(p.n)), dim3(kSumThreads), 0,
+                           stream, p);
+    } else {
+        const int64_t grid = (p.n + kSumThreads - 1) / kSumThreads;
+        hipLaunchKernelGGL(sum_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kSumThreads), 0,
+                           stream, p);
+    }
     return hipGetLastError();
 }
 
