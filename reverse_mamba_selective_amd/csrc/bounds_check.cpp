@@ -383,12 +383,14 @@ void check_backward(Checker &ck, const Launch &l, const int32_t *cu_host) {
 }
 
 void check_sum(Checker &ck, const Launch &l) {
-    const SumParams &p = l.sum;
-    const Region *rs = p.P > 0 ? ck.region_of(p.src) : nullptr, *rd = ck.region_of(p.dst);
-    ck.access("gradient (sum)", rd, U(p.dst), p.n * 4);
-    for (int64_t q = 0; q < p.P && ck.ok(); ++q) {
-        ck.access("partial (sum)", rs, U(p.src) + q * p.pstride * 4, p.n * 4);
-        ck.read_written("partial (sum)", U(p.src) + q * p.pstride * 4, p.n * 4);
+    for (int k = 0; k < l.sums.count && ck.ok(); ++k) {
+        const SumParams &p = l.sums.seg[k];
+        const Region *rs = p.P > 0 ? ck.region_of(p.src) : nullptr, *rd = ck.region_of(p.dst);
+        ck.access("gradient (sum)", rd, U(p.dst), p.n * 4);
+        for (int64_t q = 0; q < p.P && ck.ok(); ++q) {
+            ck.access("partial (sum)", rs, U(p.src) + q * p.pstride * 4, p.n * 4);
+            ck.read_written("partial (sum)", U(p.src) + q * p.pstride * 4, p.n * 4);
+        }
     }
 }
 

@@ -46,11 +46,12 @@ __device__ __forceinline__ float sigmoid(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
 }
 
-// Sum of v[] over the channels of a wave (the lanes that hold the same slice
-// of states: lanes with the same index mod G). Lane l < kN returns the total
-// of state reduced_state(G, l).
+// Sum of v[] over the channels of each 16-lane row of a wave (the lanes that
+// hold the same slice of states: lanes with the same index mod G). Lane l
+// returns its row's total of state reduced_state(G, l % 16); the rows are
+// added up later, with the other waves, in the block sum.
 template <int G>
-__device__ __forceinline__ float wave_state_sum(float (&v)[kN / G]) {
+__device__ __forceinline__ float row_state_sum(float (&v)[kN / G]) {
     constexpr int NS = kN / G;
     constexpr int LG = G == 1 ? 0 : (G == 2 ? 1 : 2);
     constexpr int STAGES = NS == 16 ? 4 : (NS == 8 ? 3 : (NS == 4 ? 2 : (NS == 2 ? 1 : 0)));
@@ -67,10 +68,8 @@ __device__ __forceinline__ float wave_state_sum(float (&v)[kN / G]) {
             v[i] = keep + __shfl_xor(send, bit);
         }
     }
-    float r = v[0];
-#pragma unroll
-    for (int bit = 1 << (LG + STAGES); bit < 64; bit <<= 1) r += __shfl_xor(r, bit);
-    return r;
+    static_assert(LG + STAGES == 4, "a row of 16 lanes ends up holding all kN states");
+    return v[0];
 }
 
 template <bool REV, typename T, int G, bool SP>
@@ -83,7 +82,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
     constexpr int WAVES = kWG / 64;
     static_assert(K * NBC == kWG, "one thread per (group token, column) in the block sum");
     __shared__ __align__(16) float lds_bc[2][kTile * NBC];
-    __shared__ float red[WAVES][K][NBC];
+    constexpr int ROWS = WAVES * 4;              // 16-lane rows per block
+    __shared__ float red[ROWS][K][NBC];
     __shared__ float red_s[WAVES];
     using E = Elem<T>;
     using R = typename E::raw_t;
@@ -223,9 +223,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             }
 
             // the adjoint over the group, last visited position first
-#pragma unroll
-            for (int j = K - 1; j >= 0; --j) {
-                if (j >= gcnt) continue;
+            auto adjoint = [&](const int j) {
                 const float *row = bc + (gi * K + j) * NBC + sub * NS;   // Bm slice; Cm at + kN
                 const float xv = E::widen(xr[j]);
                 const float gv = E::widen(gr[j]);
@@ -262,13 +260,19 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                     if (p.dx) E::bstore(E::pack(dxv), rdx, doff, orow * dxrb);
                     if (p.ddt) E::bstore(E::pack(ddtv), rdd, doff, orow * ddrb);
                 }
-                const float rb = wave_state_sum<G>(pb);
-                const float rc = wave_state_sum<G>(pc);
-                if (lane < kN) {
-                    const int n = reduced_state(G, lane);
-                    red[wave][j][n] = rb;
-                    red[wave][j][kN + n] = rc;
-                }
+                const float rb = row_state_sum<G>(pb);
+                const float rc = row_state_sum<G>(pc);
+                const int n = reduced_state(G, lane & 15);
+                red[wave * 4 + (lane >> 4)][j][n] = rb;
+                red[wave * 4 + (lane >> 4)][j][kN + n] = rc;
+            };
+            if (gcnt == K) {   // every group but a sequence's last: no branch per token
+#pragma unroll
+                for (int j = K - 1; j >= 0; --j) adjoint(j);
+            } else {
+#pragma unroll
+                for (int j = K - 1; j >= 0; --j)
+                    if (j < gcnt) adjoint(j);
             }
             __syncthreads();
             {   // the block's sums over its channels: one thread per (token, column)
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 if (j < gcnt && dst) {
                     float v = 0.0f;
 #pragma unroll
-                    for (int w = 0; w < WAVES; ++w) v += red[w][j][col];
+                    for (int w = 0; w < ROWS; ++w) v += red[w][j][col];
                     const int64_t t = sq.s0p + seg_row(sg, gpos + j);
                     dst[(bg.tile * p.tokens + t) * kN + (col % kN)] = v;
                 }
@@ -313,14 +317,34 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 }
 
 constexpr int kSumThreads = 256;
-// Outputs below this count are summed by a whole block each (threads split
-// the partials, then a fixed tree in LDS); above it, one thread per output.
 constexpr int64_t kNarrowSum = 4096;
 
-__global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumParams p) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kSumThreads + threadIdx.x;
+// The ordered sums of one backward call in one launch: segment k owns blocks
+// [first[k], first[k + 1]). Segments with fewer than kNarrowSum outputs give
+// each output a whole block (threads split the partials in order, then a
+// fixed tree in LDS); the others give each thread one output, its partials
+// summed in order with four independent loads in flight.
+__global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumBatch sb) {
+    __shared__ float part[kSumThreads];
+    int k = 0;
+    while (k + 1 < sb.count && blockIdx.x >= sb.first[k + 1]) ++k;
+    const SumParams &p = sb.seg[k];
+    const int64_t blk = static_cast<int64_t>(blockIdx.x) - sb.first[k];
+    if (p.n < kNarrowSum) {
+        float acc = 0.0f;
+        for (int64_t q = threadIdx.x; q < p.P; q += kSumThreads) acc += p.src[q * p.pstride + blk];
+        part[threadIdx.x] = acc;
+        __syncthreads();
+#pragma unroll
+        for (int w = kSumThreads / 2; w > 0; w >>= 1) {
+            if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) p.dst[blk] = part[0];
+        return;
+    }
+    const int64_t i = blk * kSumThreads + threadIdx.x;
     if (i >= p.n) return;
-    // partials in order of q, four independent loads in flight
     float acc = 0.0f;
     int64_t q = 0;
     for (; q + 4 <= p.P; q += 4) {
@@ -330,23 +354,6 @@ __global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumParams p) {
     }
     for (; q < p.P; ++q) acc += p.src[q * p.pstride + i];
     p.dst[i] = acc;
-}
-
-// One block per output: thread t sums partials t, t + 256, ... in order, then
-// a fixed binary tree over the threads.
-__global__ __launch_bounds__(kSumThreads) void sum_narrow_kernel(const SumParams p) {
-    __shared__ float part[kSumThreads];
-    const int64_t i = blockIdx.x;
-    float acc = 0.0f;
-    for (int64_t q = threadIdx.x; q < p.P; q += kSumThreads) acc += p.src[q * p.pstride + i];
-    part[threadIdx.x] = acc;
-    __syncthreads();
-#pragma unroll
-    for (int w = kSumThreads / 2; w > 0; w >>= 1) {
-        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) p.dst[i] = part[0];
 }
 
 template <bool REV, typename T, bool SP>
@@ -381,16 +388,21 @@ hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, h
                       : launch_bwd_s<false, float>(G, p, stream);
 }
 
-hipError_t launch_sum(const SumParams &p, hipStream_t stream) {
-    if (p.n <= 0) return hipSuccess;
-    if (p.n < kNarrowSum) {
-        hipLaunchKernelGGL(sum_narrow_kernel, dim3(static_cast<uint32_t>(p.n)), dim3(kSumThreads), 0,
-                           stream, p);
-    } else {
-        const int64_t grid = (p.n + kSumThreads - 1) / kSumThreads;
-        hipLaunchKernelGGL(sum_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kSumThreads), 0,
-                           stream, p);
+int64_t sum_blocks(const SumParams &p) {
+    if (p.n <= 0) return 0;
+    return p.n < kNarrowSum ? p.n : (p.n + kSumThreads - 1) / kSumThreads;
+}
+
+hipError_t launch_sums(const SumBatch &in, hipStream_t stream) {
+    SumBatch sb = in;
+    int64_t total = 0;
+    for (int k = 0; k < sb.count; ++k) {
+        sb.first[k] = total;
+        total += sum_blocks(sb.seg[k]);
     }
+    sb.first[sb.count] = total;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(sum_kernel, dim3(static_cast<uint32_t>(total)), dim3(kSumThreads), 0, stream, sb);
     return hipGetLastError();
 }
 

@@ -268,7 +268,7 @@ r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
                 what = "backward launch";
                 break;
             case Launch::Sum:
-                e = r2l::launch_sum(l.sum, stream);
+                e = r2l::launch_sums(l.sums, stream);
                 what = "gradient sum launch";
                 break;
         }

@@ -109,6 +109,13 @@ struct SumParams {
     int64_t P, pstride, n;
     float *dst;
 };
+// Up to five such sums in one launch (first[] is filled at launch).
+constexpr int kMaxSums = 5;
+struct SumBatch {
+    SumParams seg[kMaxSums];
+    int32_t count;
+    int64_t first[kMaxSums + 1];
+};
 
 // Joins chunk results (local final state Q from a zero start and the Delta sum
 // S of each chunk) into the state entering every chunk and the final state.
@@ -147,6 +154,6 @@ hipError_t launch_carry(const CarryParams &p, hipStream_t stream);
 hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream);
 // G in {2, 4}
 hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, hipStream_t stream);
-hipError_t launch_sum(const SumParams &p, hipStream_t stream);
+hipError_t launch_sums(const SumBatch &p, hipStream_t stream);
 
 }  // namespace r2l

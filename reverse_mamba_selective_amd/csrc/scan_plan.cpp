@@ -341,12 +341,11 @@ int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const Bwd
         l.bwd = q;
         out[n++] = l;
     }
-    // the ordered sums (with no sequence they write zeros)
+    // the ordered sums, one launch (with no sequence they write zeros)
+    Launch l{};
+    l.kind = Launch::Sum;
     auto sum = [&](const float *src, int64_t P, int64_t pstride, int64_t cnt, float *dst) {
-        Launch l{};
-        l.kind = Launch::Sum;
-        l.sum = SumParams{src, P, pstride, cnt, dst};
-        out[n++] = l;
+        l.sums.seg[l.sums.count++] = SumParams{src, P, pstride, cnt, dst};
     };
     const int64_t T = pl.tokens;
     if (g->dBm && T > 0) sum(pB, pl.tiles, T * kN, T * kN, g->dBm);
@@ -354,6 +353,7 @@ int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const Bwd
     if (g->dA) sum(pA, a->batch, D * kN, D * kN, g->dA);
     if (g->dDskip) sum(pD, a->batch, D, D, g->dDskip);
     if (g->ds) sum(pS, a->batch * pl.tiles, 1, 1, g->ds);
+    if (l.sums.count) out[n++] = l;
     return n;
 }
 

@@ -33,12 +33,12 @@ struct Launch {
     CarryParams carry;
     CopyParams copy;
     BwdParams bwd;
-    SumParams sum;
+    SumBatch sums;
 };
 
 // The backward of r2l_scan: phase 1 (state-only segment scan writing
-// checkpoints), phase 2 (the adjoint) and up to five ordered sums.
-constexpr int kMaxBwdLaunches = 7;
+// checkpoints), phase 2 (the adjoint) and one launch of ordered sums.
+constexpr int kMaxBwdLaunches = 3;
 struct BwdPlan {
     int G = 4;               // lanes per channel in phase 2
     int64_t tiles = 0;       // phase-2 channel tiles per sequence
