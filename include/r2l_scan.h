@@ -249,8 +249,19 @@ typedef struct r2l_grad_args {
 R2L_API r2l_status r2l_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad,
                                      void *stream);
 
-/* Bytes of workspace r2l_scan_backward needs for these arguments (only shape
- * fields and which outputs are wanted are read). */
+/*
+ * prefix_scan_backward -- the same for the forward-direction scan with readout
+ * (prefix_scan_state with Cm and out: the left-to-right stream of the L2R
+ * ablation), visiting the tokens of each sequence right to left. dh_out is the
+ * gradient of its final state. Same arguments, layouts and guarantees.
+ * Source: "Bifocal Diffusion Language Models", section 4 (the L2R-Mamba
+ * ablation trains the same sidecar scanning left to right).
+ */
+R2L_API r2l_status prefix_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                        void *stream);
+
+/* Bytes of workspace r2l_scan_backward or prefix_scan_backward needs for these
+ * arguments (only shape fields and which outputs are wanted are read). */
 R2L_API r2l_status r2l_backward_workspace_size(const r2l_scan_args *fwd,
                                                const r2l_grad_args *grad, size_t *bytes);
 

@@ -36,12 +36,14 @@ R2L_API r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const in
                             r2l_access_report *report);
 
 /*
- * r2l_check_access_backward -- the same replay for r2l_scan_backward with
- * these arguments (its checks, its launches, every access), which also
- * requires that each workspace word a launch reads (checkpoints, partial
- * sums) was written by an earlier launch of the call.
+ * r2l_check_access_backward -- the same replay for r2l_scan_backward
+ * (reverse = 1) or prefix_scan_backward (reverse = 0) with these arguments
+ * (their checks, their launches, every access), which also requires that
+ * each workspace word a launch reads (checkpoints, partial sums) was written
+ * by an earlier launch of the call.
  */
-R2L_API r2l_status r2l_check_access_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+R2L_API r2l_status r2l_check_access_backward(int32_t reverse, const r2l_scan_args *fwd,
+                                             const r2l_grad_args *grad,
                                              const int32_t *cu_seqlens_host,
                                              r2l_access_report *report);
 

@@ -23,7 +23,8 @@ from . import _abi
 from ._abi import R2LError  # noqa: F401
 
 __all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "workspace_size", "bind",
-           "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "bind_backward",
+           "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "prefix_scan_backward",
+           "bind_backward",
            "BoundBackward", "R2LScan", "GRADS"]
 
 _DTYPES = {torch.float32: _abi.R2L_DTYPE_F32, torch.bfloat16: _abi.R2L_DTYPE_BF16}
@@ -299,10 +300,11 @@ class BoundBackward:
     """One r2l_scan_backward call with its argument structs filled once (see
     BoundCall); ``grads`` holds the output tensors."""
 
-    def __init__(self, args, grad, keep, grads, workspace, device):
+    def __init__(self, args, grad, keep, grads, workspace, device, reverse=True):
         self.args, self.grad, self._keep = args, grad, keep
         self.grads, self.workspace, self.device = grads, workspace, device
-        self._fn = _abi.load().r2l_scan_backward
+        self.func = "r2l_scan_backward" if reverse else "prefix_scan_backward"
+        self._fn = getattr(_abi.load(), self.func)
         self._a, self._g = _abi.ctypes.byref(args), _abi.ctypes.byref(grad)
 
     def launch(self, stream=None):
@@ -310,7 +312,7 @@ class BoundBackward:
             stream = torch.cuda.current_stream(self.device).cuda_stream
         st = self._fn(self._a, self._g, _abi._vp(stream))
         if st != _abi.R2L_OK:
-            raise R2LError(st, "r2l_scan_backward", _abi.last_error())
+            raise R2LError(st, self.func, _abi.last_error())
 
 
 def bind_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, **kw) -> BoundBackward:
@@ -321,9 +323,15 @@ def bind_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, **kw) -> BoundBackward:
     return r2l_scan_backward(x, dt, Bm, Cm, A, Dskip, dout=dout, **kw)
 
 
+def prefix_scan_backward(x, dt, Bm, Cm, A, Dskip=None, **kw):
+    """Gradients of ``prefix_scan_state`` with readout (``Cm``, residual and
+    out: the left-to-right stream), same keywords as ``r2l_scan_backward``."""
+    return r2l_scan_backward(x, dt, Bm, Cm, A, Dskip, _reverse=False, **kw)
+
+
 def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seqlens=None,
                       max_seqlen=None, h_in=None, res=None, s=0.0, delta_softplus=True,
-                      grads=GRADS, out=None, workspace=None, _bind=False):
+                      grads=GRADS, out=None, workspace=None, _bind=False, _reverse=True):
     """Gradients of ``r2l_scan`` (same forward arguments) for ``dout`` = dL/dout
     and ``dh_out`` = dL/dh_out. Returns a dict of the names in ``grads``: dx,
     ddt (like x), dBm, dCm (fp32, shaped like Bm), dA [D, N], dDskip [D],
@@ -357,10 +365,10 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
         g.workspace, g.workspace_bytes = workspace.data_ptr(), need
     if _bind:
         keep = (x, dt, Bm, Cm, A, Dskip, dout, dh_out, cu_seqlens, h_in, res)
-        return BoundBackward(a, g, keep, outs, workspace, x.device)
+        return BoundBackward(a, g, keep, outs, workspace, x.device, reverse=_reverse)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    _abi.call_backward(a, g, stream)
+    _abi.call_backward(a, g, stream, reverse=_reverse)
     return outs
 
 

@@ -31,7 +31,7 @@ ABI_VERSION = 2
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
            "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
-           "r2l_check_access_backward")
+           "r2l_check_access_backward", "prefix_scan_backward")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -117,12 +117,13 @@ def load(path: str = LIB_PATH):
     lib.r2l_check_access.restype = _i32
     lib.r2l_check_access.argtypes = [_i32, ptr, ctypes.POINTER(_i32), ctypes.POINTER(AccessReport)]
     gptr = ctypes.POINTER(GradArgs)
-    lib.r2l_scan_backward.restype = _i32
-    lib.r2l_scan_backward.argtypes = [ptr, gptr, _vp]
+    for fn in (lib.r2l_scan_backward, lib.prefix_scan_backward):
+        fn.restype = _i32
+        fn.argtypes = [ptr, gptr, _vp]
     lib.r2l_backward_workspace_size.restype = _i32
     lib.r2l_backward_workspace_size.argtypes = [ptr, gptr, ctypes.POINTER(ctypes.c_size_t)]
     lib.r2l_check_access_backward.restype = _i32
-    lib.r2l_check_access_backward.argtypes = [ptr, gptr, ctypes.POINTER(_i32),
+    lib.r2l_check_access_backward.argtypes = [_i32, ptr, gptr, ctypes.POINTER(_i32),
                                               ctypes.POINTER(AccessReport)]
     if lib.r2l_abi_version() != ABI_VERSION:
         raise ImportError("libr2l_scan.so ABI %d, binding expects %d"
@@ -179,21 +180,24 @@ def backward_workspace_size(args: ScanArgs, grad: GradArgs) -> int:
     return int(n.value)
 
 
-def call_backward(args: ScanArgs, grad: GradArgs, stream: int | None) -> None:
-    st = load().r2l_scan_backward(ctypes.byref(args), ctypes.byref(grad), _vp(stream or 0))
+def call_backward(args: ScanArgs, grad: GradArgs, stream: int | None, reverse: bool = True) -> None:
+    func = "r2l_scan_backward" if reverse else "prefix_scan_backward"
+    st = getattr(load(), func)(ctypes.byref(args), ctypes.byref(grad), _vp(stream or 0))
     if st != R2L_OK:
-        raise R2LError(st, "r2l_scan_backward", last_error())
+        raise R2LError(st, func, last_error())
 
 
-def check_access_backward(args: ScanArgs, grad: GradArgs, cu_seqlens_host=None):
-    """Host replay of every access r2l_scan_backward would make; (status, report)."""
+def check_access_backward(args: ScanArgs, grad: GradArgs, cu_seqlens_host=None, reverse=True):
+    """Host replay of every access r2l_scan_backward (or, reverse=False,
+    prefix_scan_backward) would make; (status, report)."""
     lib = load()
     rep = AccessReport()
     cu = None
     if cu_seqlens_host is not None:
         arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
         cu = ctypes.cast(arr, ctypes.POINTER(_i32))
-    st = lib.r2l_check_access_backward(ctypes.byref(args), ctypes.byref(grad), cu, ctypes.byref(rep))
+    st = lib.r2l_check_access_backward(1 if reverse else 0, ctypes.byref(args), ctypes.byref(grad),
+                                       cu, ctypes.byref(rep))
     return st, rep
 
 

@@ -396,8 +396,8 @@ void check_sum(Checker &ck, const Launch &l) {
 
 }  // namespace
 
-r2l_status check_backward_accesses(const r2l_scan_args *a, const r2l_grad_args *g, const BwdPlan &pl,
-                                   const int32_t *cu_host, r2l_access_report *rep) {
+r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r2l_grad_args *g,
+                                   const BwdPlan &pl, const int32_t *cu_host, r2l_access_report *rep) {
     const int64_t es = elem_size(a->dtype), D = a->dim, N = kN;
     const int64_t tok = tokens_of(a);
     std::vector<Region> regs;
@@ -438,7 +438,7 @@ r2l_status check_backward_accesses(const r2l_scan_args *a, const r2l_grad_args *
     Checker ck(std::move(regs), rep);
     ck.set_workspace(g->workspace, pl.ws_bytes);
     Launch ls[kMaxBwdLaunches];
-    const int n = build_bwd_launches(a, g, pl, ls);
+    const int n = build_bwd_launches(reverse, a, g, pl, ls);
     for (int i = 0; i < n && ck.ok(); ++i) {
         ++rep->launches;
         switch (ls[i].kind) {

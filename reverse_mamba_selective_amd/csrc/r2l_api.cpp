@@ -384,11 +384,8 @@ r2l_status check_backward(const r2l_scan_args *a, const r2l_grad_args *g, const 
     return R2L_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-r2l_status r2l_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad, void *stream) {
+r2l_status run_backward(bool reverse, const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                        hipStream_t stream) {
     r2l_status st = check_shape(fwd);
     if (st != R2L_OK) return st;
     if (!grad) return fail(R2L_ERR_INVALID_ARG, "grad is NULL");
@@ -398,12 +395,25 @@ r2l_status r2l_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad
     st = check_seqlens_on_device(fwd);
     if (st != R2L_OK) return st;
     Launch ls[r2l::kMaxBwdLaunches];
-    const int n = r2l::build_bwd_launches(fwd, grad, pl, ls);
-    return execute(ls, n, static_cast<hipStream_t>(stream));
+    const int n = r2l::build_bwd_launches(reverse, fwd, grad, pl, ls);
+    return execute(ls, n, stream);
 }
 
-r2l_status r2l_check_access_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad,
-                                     const int32_t *cu_seqlens_host, r2l_access_report *report) {
+}  // namespace
+
+extern "C" {
+
+r2l_status r2l_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad, void *stream) {
+    return run_backward(true, fwd, grad, static_cast<hipStream_t>(stream));
+}
+
+r2l_status prefix_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad, void *stream) {
+    return run_backward(false, fwd, grad, static_cast<hipStream_t>(stream));
+}
+
+r2l_status r2l_check_access_backward(int32_t reverse, const r2l_scan_args *fwd,
+                                     const r2l_grad_args *grad, const int32_t *cu_seqlens_host,
+                                     r2l_access_report *report) {
     if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
     report->launches = report->accesses = report->vector_staging = 0;
     report->message[0] = '\0';
@@ -418,7 +428,7 @@ r2l_status r2l_check_access_backward(const r2l_scan_args *fwd, const r2l_grad_ar
         if (cu_seqlens_host[0] != 0 || cu_seqlens_host[fwd->batch] != fwd->total_tokens)
             return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host does not span total_tokens");
     }
-    st = r2l::check_backward_accesses(fwd, grad, pl, cu_seqlens_host, report);
+    st = r2l::check_backward_accesses(reverse != 0, fwd, grad, pl, cu_seqlens_host, report);
     if (st != R2L_OK && report->message[0]) fail(st, "%s", report->message);
     return st == R2L_OK ? ok() : st;
 }

@@ -272,8 +272,8 @@ BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
     return pl;
 }
 
-int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const BwdPlan &pl,
-                       Launch out[kMaxBwdLaunches]) {
+int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args *g,
+                       const BwdPlan &pl, Launch out[kMaxBwdLaunches]) {
     char *ws = static_cast<char *>(g->workspace);
     auto at = [&](size_t off, bool want) { return want ? reinterpret_cast<float *>(ws + off) : nullptr; };
     float *ck = at(pl.off_ck, pl.tokens > 0);
@@ -299,7 +299,7 @@ int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const Bwd
             p.bc_vec = bc_vector_ok(a, false) ? 1 : 0;
             Launch l{};
             l.kind = Launch::Segment;
-            l.reverse = true;
+            l.reverse = reverse;
             l.dtype = a->dtype;
             l.G = 1;
             l.mode = kModeState;
@@ -335,7 +335,7 @@ int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const Bwd
         q.partB = pB; q.partC = pC; q.partA = pA; q.partD = pD; q.partS = pS;
         Launch l{};
         l.kind = Launch::Backward;
-        l.reverse = true;
+        l.reverse = reverse;
         l.dtype = a->dtype;
         l.G = pl.G;
         l.bwd = q;

@@ -51,8 +51,9 @@ struct BwdPlan {
 };
 
 BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g);
-int build_bwd_launches(const r2l_scan_args *a, const r2l_grad_args *g, const BwdPlan &pl,
-                       Launch out[kMaxBwdLaunches]);
+// reverse: the backward of r2l_scan (true) or of the forward-direction readout (false)
+int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args *g,
+                       const BwdPlan &pl, Launch out[kMaxBwdLaunches]);
 
 inline bool is_ragged(const r2l_scan_args *a) { return a->cu_seqlens != nullptr; }
 inline int64_t tokens_of(const r2l_scan_args *a) {

@@ -287,7 +287,7 @@ def make_grad(a, heap, *, dtype="bf16", grads=("dx", "ddt", "dBm", "dCm", "dA", 
     return g
 
 
-def check_bwd(grads=None, dh_out=True, **kw):
+def check_bwd(grads=None, dh_out=True, reverse=True, **kw):
     res = kw.pop("res", "none")
     a, cu = make_args("scan", res=res, **kw)
     heap = FakeHeap()
@@ -295,7 +295,7 @@ def check_bwd(grads=None, dh_out=True, **kw):
     g = make_grad(a, heap, dtype=kw.get("dtype", "bf16"), dh_out=dh_out,
                   pad_row=kw.get("pad_row", 0),
                   **({"grads": grads} if grads is not None else {}))
-    st, rep = _abi.check_access_backward(a, g, cu)
+    st, rep = _abi.check_access_backward(a, g, cu, reverse=reverse)
     msg = rep.message.decode() or _abi.last_error()
     assert st == _abi.R2L_OK, "backward %s: %s" % (kw, msg)
     return rep
@@ -319,6 +319,7 @@ def test_backward_edge_cases(case, dtype):
     kw.setdefault("D", 64)
     for res in ("none", "x", "sep"):
         check_bwd(res=res, h_in=True, **kw)
+        check_bwd(res=res, h_in=True, reverse=False, **kw)
     check_bwd(grads=("dx",), dh_out=False, **kw)
     check_bwd(grads=("dBm", "dA"), **kw)
     check_bwd(grads=(), **kw)

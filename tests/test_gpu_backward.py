@@ -47,7 +47,7 @@ def check_grad(name, got_t, ref, dtype):
         assert worst <= 1.0, "%s: an element is %.2f x (1 bf16 ulp + bound) off" % (name, worst)
 
 
-def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None):
+def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None, reverse=True):
     dtype = dtype or inp.dtype
     B, D = inp.batch, inp.x.shape[1]
     rng = np.random.default_rng(seed)
@@ -58,7 +58,7 @@ def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None):
     res_np = {"none": None, "x": inp.x,
               "separate": synth.scan_inputs(seed + 1, inp.lengths, D=D, dtype=dtype).x}[res_kind]
     ref = oracle.selective_scan_backward(
-        inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=True, dout=dout_np,
+        inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=reverse, dout=dout_np,
         dh_out=dh_out_np, res_kind=res_kind, s=s, seq_offsets=inp.offsets, h_in=h0)
 
     def shaped(t):
@@ -74,7 +74,8 @@ def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None):
         kw.update(cu_seqlens=torch.from_numpy(inp.offsets.astype(np.int32)).cuda(),
                   max_seqlen=int(inp.lengths.max()) if B else 0)
     res = None if res_np is None else (x if res_kind == "x" else shaped(dev(res_np, dtype)))
-    g = r2l.r2l_scan_backward(x, **kw, dout=shaped(dev(dout_np, dtype)),
+    bwd = r2l.r2l_scan_backward if reverse else r2l.prefix_scan_backward
+    g = bwd(x, **kw, dout=shaped(dev(dout_np, dtype)),
                               dh_out=dev32(dh_out_np) if with_dhout else None,
                               h_in=dev32(h0) if with_hin else None, res=res, s=s)
     torch.cuda.synchronize()
@@ -94,16 +95,17 @@ def test_backward_tiny_fp32(gpu, res_kind, s):
     run_case(inp, True, res_kind, s, with_hin=True, with_dhout=True, seed=31)
 
 
+@pytest.mark.parametrize("reverse", [True, False], ids=["r2l", "forward"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("res_kind", ["none", "x", "separate"])
-def test_backward_ragged_edges(gpu, dtype, res_kind):
+def test_backward_ragged_edges(gpu, dtype, res_kind, reverse):
     """Sequences of 0, 1 and 7..130 tokens (partial and full checkpoint groups
     and tiles), a channel tail (100 channels: one full tile of 64 and 36)."""
     lengths = [5, 0, 1, 7, 8, 9, 64, 65, 130]
     inp = synth.scan_inputs(32, lengths, D=100, dtype=dtype, dt_mean=-3.0)
     for with_hin, with_dhout in ((False, False), (True, True)):
         run_case(inp, False, res_kind, 0.0 if res_kind == "none" else 0.4, with_hin, with_dhout,
-                 seed=33)
+                 seed=33, reverse=reverse)
 
 
 def test_backward_gate_zero(gpu):
@@ -118,6 +120,13 @@ def test_backward_denoise_hook_bf16(gpu):
     s = float(synth.denoise_gates()[2])
     inp = synth.denoise_hook_inputs(2)
     run_case(inp, True, "x", s, with_hin=False, with_dhout=False, seed=36)
+
+
+def test_backward_l2r_ablation_hook_bf16(gpu):
+    """prefix_scan_backward at the denoising hook's full size (the L2R ablation)."""
+    s = float(synth.denoise_gates()[4])
+    inp = synth.denoise_hook_inputs(4)
+    run_case(inp, True, "x", s, with_hin=False, with_dhout=True, seed=40, reverse=False)
 
 
 def test_backward_is_deterministic(gpu):
