@@ -21,6 +21,9 @@ Function map (each a thin wrapper over the one C routine):
                              (partial-bidirectionality summary, "Methodology" 1).
 * ``block_commit_state``  -- advance a cached boundary state over a committed
                              block (same passage: finished blocks join the prefix).
+* ``bidir_scan``          -- forward plus reverse scan of the same x, each with
+                             its own parameters, readouts added (the full-window
+                             bidirectional scan of the earlier hybrids).
 * ``selective_scan_backward`` -- the gradients of the scan with readout and
                              residual (training the R2L stream).
 """
@@ -73,6 +76,12 @@ class OracleLib:
                 _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, ctypes.c_int, _dptr,
                 ctypes.c_int, ctypes.c_double, _dptr, _dptr,
                 _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, ctypes.c_int]
+        if hasattr(lib, "ref_bidir_scan"):
+            lib.ref_bidir_scan.restype = ctypes.c_int
+            lib.ref_bidir_scan.argtypes = [
+                ctypes.c_int64, _i64ptr, ctypes.c_int64, ctypes.c_int64, _dptr,
+                _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr, _dptr,
+                ctypes.c_int, _dptr, _dptr, _dptr, _dptr, ctypes.c_double, _dptr, ctypes.c_int]
         self.lib = lib
         self.path = path
 
@@ -210,6 +219,51 @@ def selective_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, reverse: bool, dout
         raise ValueError("oracle backward rejected its arguments (rc=%d)" % rc)
     r["ds"] = float(r["ds"][0])
     return r
+
+
+def bidir_scan(x, dt, Bm, Cm, A, Dskip=None, *, rev=None, res=None, s: float = 0.0,
+               seq_offsets=None, batch=None, seqlen=None, delta_softplus: bool = True,
+               h_in=None, want_h_out=False, want_out=True, nthreads: int = 0,
+               timing: dict | None = None, lib: OracleLib | None = None):
+    """Bidirectional full-window scan: the forward scan (parameters dt, Bm, Cm,
+    A, Dskip; from h_in) plus the reverse scan (parameters ``rev``, a dict with
+    the same keys, each defaulting to the forward's; from zero) of the same x.
+    Returns fp64 ``y`` = y_forward + y_reverse, ``out`` (res + s*y, s == 0:
+    res; y without res) and the forward's final state ``h_out``."""
+    rev = dict(rev or {})
+    unknown = set(rev) - {"dt", "Bm", "Cm", "A", "Dskip"}
+    if unknown:
+        raise ValueError("unknown reverse parameters %s" % sorted(unknown))
+    f = {"dt": _f64(dt), "Bm": _f64(Bm), "Cm": _f64(Cm), "A": _f64(A), "Dskip": _f64(Dskip)}
+    r = {k: (_f64(rev[k]) if k in rev else f[k]) for k in f}
+    x, h_in, res = _f64(x), _f64(h_in), _f64(res)
+    tokens, D = x.shape
+    N = f["A"].shape[1]
+    off = _offsets(seq_offsets, batch, seqlen, tokens)
+    nb = off.shape[0] - 1
+    for p in (f, r):
+        assert p["dt"].shape == (tokens, D) and p["A"].shape == (D, N)
+        assert p["Bm"].shape == (tokens, N) and p["Cm"].shape == (tokens, N)
+        assert p["Dskip"] is None or p["Dskip"].shape == (D,)
+    if h_in is not None:
+        h_in = h_in.reshape(nb, D, N)
+    if res is not None:
+        assert res.shape == (tokens, D)
+    y = np.empty((tokens, D))
+    out = np.empty((tokens, D)) if want_out else None
+    h_out = np.empty((nb, D, N)) if want_h_out else None
+    t0 = time.perf_counter()
+    rc = (lib or _load()).lib.ref_bidir_scan(
+        nb, off.ctypes.data_as(_i64ptr), D, N, _ptr(x),
+        _ptr(f["dt"]), _ptr(f["Bm"]), _ptr(f["Cm"]), _ptr(f["A"]), _ptr(f["Dskip"]),
+        _ptr(r["dt"]), _ptr(r["Bm"]), _ptr(r["Cm"]), _ptr(r["A"]), _ptr(r["Dskip"]),
+        1 if delta_softplus else 0, _ptr(h_in), _ptr(h_out), _ptr(y), _ptr(res), float(s),
+        _ptr(out), int(nthreads))
+    if timing is not None:
+        timing["seconds"] = time.perf_counter() - t0
+    if rc != 0:
+        raise ValueError("oracle bidirectional scan rejected its arguments (rc=%d)" % rc)
+    return {"y": y, "out": out, "h_out": h_out}
 
 
 def r2l_scan(x, dt, Bm, Cm, A, Dskip=None, *, res=None, s=0.0, **kw):

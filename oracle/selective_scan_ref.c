@@ -375,3 +375,65 @@ int ref_selective_scan_backward(int reverse, int64_t batch, const int64_t *seq_o
     free(pS);
     return 0;
 }
+
+/*
+ * The bidirectional full-window scan that the block-diffusion page contrasts
+ * with its partial reverse scan ("Training Hybrid Block Diffusion Language
+ * Models with Partial Bidirectionality", nl summary, "Probleemstelling", the
+ * problem statement: the earlier hybrids, DiffuMamba among them, scan the
+ * whole denoising window in both directions), and the left-to-right and
+ * right-to-left streams that "Bifocal Diffusion Language Models" compares in
+ * its ablations (section 4, experimental results).
+ * The pages do not say how the two directions combine. The plain reading
+ * taken here: each direction is the scan above with its own parameter set
+ * (dt, Bm, Cm, A, Dskip; _f forward, _r reverse, which may be the same
+ * arrays), both read the same x, and their readouts add:
+ *     y_t = y_t(forward from h_in) + y_t(reverse from zero)
+ *     out = res == NULL ? y : (s == 0 ? res : res + s * y)
+ * h_out receives the forward direction's final state (the reverse one
+ * depends on the whole window and is not a cacheable boundary state).
+ * Arguments otherwise as in ref_selective_scan; y and out may be NULL.
+ */
+int ref_bidir_scan(int64_t batch, const int64_t *seq_off, int64_t D, int64_t N,
+                   const double *x,
+                   const double *dt_f, const double *Bm_f, const double *Cm_f,
+                   const double *A_f, const double *Dskip_f,
+                   const double *dt_r, const double *Bm_r, const double *Cm_r,
+                   const double *A_r, const double *Dskip_r,
+                   int delta_softplus, const double *h_in, double *h_out,
+                   double *y, const double *res, double s, double *out, int nthreads)
+{
+    if (batch < 0 || D <= 0 || !seq_off || !Cm_f || !Cm_r)
+        return -1;
+    const int64_t tokens = seq_off[batch];
+    if (tokens < 0)
+        return -1;
+    const size_t cells = (size_t)tokens * (size_t)D;
+    double *yf = (double *)malloc((cells ? cells : 1) * sizeof(double));
+    double *yr = (double *)malloc((cells ? cells : 1) * sizeof(double));
+    if (!yf || !yr)
+        abort();
+    int rc = ref_selective_scan(0, batch, seq_off, D, N, x, dt_f, Bm_f, Cm_f, A_f, Dskip_f,
+                                delta_softplus, h_in, h_out, yf, NULL, 0.0, NULL, nthreads);
+    if (rc == 0)
+        rc = ref_selective_scan(1, batch, seq_off, D, N, x, dt_r, Bm_r, Cm_r, A_r, Dskip_r,
+                                delta_softplus, NULL, NULL, yr, NULL, 0.0, NULL, nthreads);
+    if (rc == 0) {
+        for (size_t i = 0; i < cells; ++i) {
+            const double yv = yf[i] + yr[i];
+            if (y)
+                y[i] = yv;
+            if (out) {
+                if (!res)
+                    out[i] = yv;
+                else if (s == 0.0)
+                    out[i] = res[i];
+                else
+                    out[i] = res[i] + s * yv;
+            }
+        }
+    }
+    free(yf);
+    free(yr);
+    return rc;
+}

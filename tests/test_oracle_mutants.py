@@ -11,6 +11,7 @@ import tempfile
 import pytest
 
 import oracle
+from oracle_bidir_pins import BIDIR_PINS
 from oracle_bwd_pins import BWD_PINS
 from oracle_pins import PINS
 
@@ -77,6 +78,36 @@ BWD_MUTANTS = {
 }
 
 
+# Mistakes in the bidirectional combination (anchors searched from its name).
+BIDIR_MUTANTS = {
+    "bidir_drop_reverse": ("ref_bidir_scan(", "const double yv = yf[i] + yr[i];",
+                           "const double yv = yf[i];"),
+    "bidir_reverse_with_forward_params": ("ref_bidir_scan(", "x, dt_r, Bm_r, Cm_r, A_r, Dskip_r,",
+                                          "x, dt_f, Bm_f, Cm_f, A_f, Dskip_f,"),
+    "bidir_both_forward": ("ref_bidir_scan(", "rc = ref_selective_scan(1, batch",
+                           "rc = ref_selective_scan(0, batch"),
+    "bidir_reverse_from_h_in": ("ref_bidir_scan(", "delta_softplus, NULL, NULL, yr",
+                                "delta_softplus, h_in, NULL, yr"),
+    "bidir_no_h_out": ("ref_bidir_scan(", "delta_softplus, h_in, h_out, yf",
+                       "delta_softplus, h_in, NULL, yf"),
+    "bidir_ungated": ("ref_bidir_scan(", "out[i] = res[i] + s * yv;", "out[i] = res[i] + yv;"),
+    "bidir_lost_gate_select": ("ref_bidir_scan(", "else if (s == 0.0)", "else if (0)"),
+}
+
+
+def _build_anchored(workdir, name, start, old, new):
+    text = open(SRC).read()
+    at = text.index(start)
+    at = text.find(old, at)
+    assert at >= 0, "mutation anchor not found: %s" % name
+    src = os.path.join(workdir, name + ".c")
+    with open(src, "w") as f:
+        f.write(text[:at] + new + text[at + len(old):])
+    so = os.path.join(workdir, name + ".so")
+    oracle.build(src=src, out=so)
+    return oracle.OracleLib(so)
+
+
 @pytest.fixture(scope="module")
 def workdir():
     with tempfile.TemporaryDirectory() as d:
@@ -135,3 +166,18 @@ def test_some_backward_pin_catches_mutant(workdir, name):
         except (AssertionError, ValueError, FloatingPointError):
             return
     pytest.fail("no backward pin catches the planted mistake %r" % name)
+
+
+@pytest.mark.parametrize("name", sorted(BIDIR_MUTANTS))
+def test_some_bidir_pin_catches_mutant(workdir, name):
+    lib = _build_anchored(workdir, name, *BIDIR_MUTANTS[name])
+
+    def bidir(*a, **k):
+        return oracle.bidir_scan(*a, lib=lib, **k)
+
+    for pin in BIDIR_PINS:
+        try:
+            pin(bidir)
+        except (AssertionError, ValueError, FloatingPointError):
+            return
+    pytest.fail("no bidirectional pin catches the planted mistake %r" % name)

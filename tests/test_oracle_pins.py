@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle_bidir_pins import BIDIR_PINS
 from oracle_bwd_pins import BWD_PINS
 from oracle_pins import PINS
 
@@ -10,6 +11,11 @@ from oracle_pins import PINS
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
 def test_pin(pin):
     pin(oracle.selective_scan)
+
+
+@pytest.mark.parametrize("pin", BIDIR_PINS, ids=[p.__name__ for p in BIDIR_PINS])
+def test_bidir_pin(pin):
+    pin(oracle.bidir_scan)
 
 
 @pytest.mark.parametrize("pin", BWD_PINS, ids=[p.__name__ for p in BWD_PINS])
