@@ -71,9 +71,16 @@ def scan_bytes(tok, D, es, readout=True, res_separate=False, h_in=False, h_out=F
     return b
 
 
+KERNEL_SOURCES = ("scan_device.h", "scan_geometry.h", "scan_internal.h", "scan_segment.h",
+                  "scan_kernels.hip", "bidir_kernels.hip", "bwd_kernels.hip")
+
+
 def kernel_sha() -> str:
-    p = os.path.join(ROOT, "reverse_mamba_selective_amd", "csrc", "scan_kernels.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the device code (every kernel source and the headers they include)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "reverse_mamba_selective_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
@@ -585,8 +592,94 @@ class RaggedPrefix(Workload):
     parity_spec = ("h_out", "f32", 1e-5, "final state of the sampled prefixes")
 
 
+class DenoiseBidir(Denoise):
+    """The full-window bidirectional variant of the same step: 7 hooked bidir_scan
+    calls over the denoising window (forward scan + reverse scan of x, each
+    direction with its own dt, Bm, Cm, A, Dskip, readouts added, gated residual
+    in place), 64 x 32 x 2048, bf16."""
+    name = "bidir_window_step_bf16_b64_L32_D2048_N16_7hooks"
+    entry = "bidir_scan"
+
+    def setup(self, torch, r2l):
+        import synth
+        self.torch = torch
+        self.gates = synth.bidir_gates()
+        self.inputs = [synth.bidir_inputs(h) for h in range(self.HOOKS)]
+        self.revs = [synth.bidir_reverse(h) for h in range(self.HOOKS)]
+        tok = self.B * self.L
+        N = 16
+        self.tc_per_launch = tok * self.D
+        self.tc_per_step = self.tc_per_launch * self.HOOKS
+        # x, out; dt of each direction (bf16); Bm, Cm of each direction; A, Dskip of each
+        self.bytes_per_launch = (tok * self.D * 2 * 4 + tok * N * 2 * 4 +
+                                 2 * (self.D * N * 4 + self.D * 4))
+        # the reverse readout, then the forward readout with the residual and the sum
+        self.alu_per_launch = self.tc_per_launch * (alu_ops_per_tc(True, False) +
+                                                    alu_ops_per_tc(True, True) + 1)
+        self.launches_per_step = self.HOOKS
+        set_bytes = self.bytes_per_launch * self.HOOKS
+        self.R = _rotation(set_bytes)
+        self.step_calls, self.outs0 = [], []
+        shape = lambda t: t.view(self.B, self.L, -1)   # noqa: E731
+        for r in range(self.R):
+            row = []
+            for h, (inp, rv) in enumerate(zip(self.inputs, self.revs)):
+                x = shape(_dev(torch, inp.x, "bf16"))
+                ins = {k: shape(_dev(torch, getattr(inp, k), "bf16")) for k in ("dt", "Bm", "Cm")}
+                ins["A"] = torch.from_numpy(inp.A).cuda()
+                ins["Dskip"] = torch.from_numpy(inp.Dskip).cuda()
+                rev = {k: shape(_dev(torch, rv[k], "bf16")) for k in ("dt", "Bm", "Cm")}
+                rev["A"] = torch.from_numpy(rv["A"]).cuda()
+                rev["Dskip"] = torch.from_numpy(rv["Dskip"]).cuda()
+                out = torch.empty_like(x)
+                if r == 0:
+                    self.outs0.append(out)
+                row.append(r2l.bind("bidir_scan", x=x, res=x, s=float(self.gates[h]), out=out,
+                                    rev=rev, **ins))
+            self.step_calls.append(row)
+        self.step_entries = [0] * self.HOOKS
+        self.measure = [dict(label="bidir_scan (one hook)",
+                             calls=[c for row in self.step_calls for c in row],
+                             bytes=self.bytes_per_launch, alu=self.alu_per_launch,
+                             tc=self.tc_per_launch)]
+        self.config = {"workload": self.name, "batch": self.B, "window_tokens": self.L,
+                       "D": self.D, "N": 16, "hooks_per_step": self.HOOKS,
+                       "in_dtype": "bf16", "state_dtype": "fp32", "res": "x",
+                       "reverse_parameters": "separate", "op": "bidir_scan",
+                       "rotating_sets": self.R, "rotating_bytes": set_bytes * self.R,
+                       "parallelism": "single_gpu"}
+
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
+        import oracle
+        tc, secs, reps, hooks = 0, 0.0, 0, 0
+        while secs < budget_s and reps < 200:
+            for h, (inp, rv) in enumerate(zip(self.inputs, self.revs)):
+                t = {}
+                r = oracle.bidir_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, rev=rv,
+                                      res=inp.x, s=float(self.gates[h]), seq_offsets=inp.offsets,
+                                      timing=t, nthreads=nthreads)
+                if parity is not None and reps == 0:
+                    parity.add(self.outs0[h].float().cpu().numpy().reshape(r["out"].shape),
+                               r["out"])
+                secs += t["seconds"]
+                tc += inp.x.size
+                hooks += 1
+                if nthreads == 1 and secs >= budget_s:
+                    break
+            reps += 1
+        return {"value": tc / secs, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "%d bidirectional hooks of the 7-hook step (%d token-channels), "
+                          "%.1f s of oracle time" % (hooks, tc, secs)}
+
+    parity_spec = ("out", "bf16", 2e-2,
+                   "out = x + s*(y_forward + y_reverse) of all 7 hooks (first buffer set) vs "
+                   "the oracle's")
+
+
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
-             "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward}
+             "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward,
+             "bidir": DenoiseBidir}
 
 
 def main():

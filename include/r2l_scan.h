@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define R2L_ABI_VERSION 2
+#define R2L_ABI_VERSION 3
 
 /* exported from libr2l_scan.so (everything else in it is hidden) */
 #if defined(__GNUC__)
@@ -114,6 +114,7 @@ typedef int32_t r2l_status;
 #define R2L_OP_SCAN 0
 #define R2L_OP_PREFIX 1
 #define R2L_OP_COMMIT 2
+#define R2L_OP_BIDIR 3
 
 typedef struct r2l_scan_args {
     /* ---- shape ---- */
@@ -199,7 +200,8 @@ R2L_API r2l_status block_commit_state(const r2l_scan_args *a, void *stream);
 
 /*
  * r2l_workspace_size -- bytes of workspace that the plan for operation `op`
- * (R2L_OP_*) with these arguments needs; 0 when the plan does not chunk.
+ * (R2L_OP_*) with these arguments needs; 0 when the plan does not chunk (and,
+ * for R2L_OP_BIDIR, runs no readout).
  * Only the shape fields and the planning hints are read. Returns R2L_OK and
  * writes *bytes, or an error status.
  */
@@ -264,6 +266,47 @@ R2L_API r2l_status prefix_scan_backward(const r2l_scan_args *fwd, const r2l_grad
  * arguments (only shape fields and which outputs are wanted are read). */
 R2L_API r2l_status r2l_backward_workspace_size(const r2l_scan_args *fwd,
                                                const r2l_grad_args *grad, size_t *bytes);
+
+/*
+ * bidir_scan -- the bidirectional full-window scan: over each whole sequence,
+ * the forward scan of x (left to right from h_in, the parameters of `a`) plus
+ * the reverse scan of the same x (right to left from zero, the parameters of
+ * `rev`), their readouts added:
+ *     y_t   = y_t(forward) + y_t(reverse)
+ *     out   = res == NULL ? y : (s == 0 ? res : res + s * y)
+ * h_out (optional) receives the forward direction's final state. Each
+ * direction's readout includes its own Dskip * x term.
+ * Source: "Training Hybrid Block Diffusion Language Models with Partial
+ * Bidirectionality", nl summary, problem statement (the earlier hybrids,
+ * DiffuMamba among them, run bidirectional Mamba scans over the whole
+ * denoising window, which is what prevents exact caching); "Bifocal Diffusion
+ * Language Models", section 4 (the streams of either direction in the
+ * ablations). How the two directions combine is not on the pages: adding the
+ * two readouts, each direction with its own parameters, is the reading taken.
+ *
+ * rev: the reverse direction's dt, Bm, Cm (same layout rules and dtype as in
+ * `a`), A and Dskip. rev == NULL, or a NULL pointer in it, shares the forward
+ * direction's tensor (with the forward's strides); a reverse direction without
+ * a skip term needs an explicit zero Dskip. Everything else (shape, x, res, s,
+ * out, h_in, h_out, delta_softplus, chunk_tokens) comes from `a`; state_split
+ * must be 0 or 1 (one lane per channel).
+ * Required: x, dt, Bm, Cm, A, out. The workspace (r2l_workspace_size with
+ * R2L_OP_BIDIR) holds the reverse readout as fp32 [tokens, D] rows plus the
+ * chunked plans' carry data; it is needed whenever the readout runs. With
+ * s == 0 (and res) no readout runs, as in the other entry points: out is res
+ * bit for bit and only the forward state is scanned when h_out is given.
+ * out may be exactly x and/or res; any other overlap with an input of either
+ * direction is R2L_ERR_ALIAS.
+ */
+typedef struct r2l_dir_args {
+    const void *dt;  int64_t dt_stride; int64_t dt_batch_stride;
+    const void *Bm;  int64_t Bm_stride; int64_t Bm_batch_stride;
+    const void *Cm;  int64_t Cm_stride; int64_t Cm_batch_stride;
+    const float *A;
+    const float *Dskip;
+} r2l_dir_args;
+
+R2L_API r2l_status bidir_scan(const r2l_scan_args *a, const r2l_dir_args *rev, void *stream);
 
 /* Short static description of a status code. */
 R2L_API const char *r2l_status_string(r2l_status status);

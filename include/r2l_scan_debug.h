@@ -47,6 +47,15 @@ R2L_API r2l_status r2l_check_access_backward(int32_t reverse, const r2l_scan_arg
                                              const int32_t *cu_seqlens_host,
                                              r2l_access_report *report);
 
+/*
+ * r2l_check_access_bidir -- the same replay for bidir_scan with these
+ * arguments (the workspace's fp32 rows that the forward pass adds must have
+ * been written by the reverse pass).
+ */
+R2L_API r2l_status r2l_check_access_bidir(const r2l_scan_args *a, const r2l_dir_args *rev,
+                                          const int32_t *cu_seqlens_host,
+                                          r2l_access_report *report);
+
 typedef struct r2l_plan_info {
     int32_t lanes_per_channel; /* 1, 2 or 4 */
     int32_t chunked;           /* 1: chunk pass + carry (+ readout pass) */

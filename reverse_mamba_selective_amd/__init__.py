@@ -22,7 +22,8 @@ import torch
 from . import _abi
 from ._abi import R2LError  # noqa: F401
 
-__all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "workspace_size", "bind",
+__all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "bidir_scan",
+           "workspace_size", "bind",
            "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "prefix_scan_backward",
            "bind_backward",
            "BoundBackward", "R2LScan", "GRADS"]
@@ -146,11 +147,14 @@ class BoundCall:
     change between launches, their storage may not.
     """
 
-    def __init__(self, func, op, args, keep, workspace, device):
+    def __init__(self, func, op, args, keep, workspace, device, rev=None):
         self.func, self.op, self.args = func, op, args
         self._keep, self.workspace, self.device = keep, workspace, device
         self._fn = getattr(_abi.load(), func)
         self._ref = _abi.ctypes.byref(args)
+        # bidir_scan takes the reverse direction's struct (or NULL) as well
+        self.rev = rev
+        self._refs = (self._ref, _abi._dir_ref(rev)) if func == "bidir_scan" else (self._ref,)
 
     def plan(self) -> dict:
         """The plan the library picks for this call (lanes per channel, chunking,
@@ -162,19 +166,24 @@ class BoundCall:
         on torch's current stream of the device."""
         if stream is None:
             stream = torch.cuda.current_stream(self.device).cuda_stream
-        st = self._fn(self._ref, _abi._vp(stream))
+        st = self._fn(*self._refs, _abi._vp(stream))
         if st != _abi.R2L_OK:
             raise R2LError(st, self.func, _abi.last_error())
 
 
 def bind(op: str, **kw) -> BoundCall:
-    """Check and marshal the arguments of ``r2l_scan``, ``prefix_scan_state`` or
-    ``block_commit_state`` once (same keywords as those functions; outputs must
-    be given) and return a :class:`BoundCall`.
+    """Check and marshal the arguments of ``r2l_scan``, ``prefix_scan_state``,
+    ``block_commit_state`` or ``bidir_scan`` once (same keywords as those
+    functions; outputs must be given) and return a :class:`BoundCall`.
     """
     kw = dict(kw)
     ws = kw.pop("workspace", None)
-    if op == "r2l_scan":
+    rev = kw.pop("rev", None)
+    if rev is not None and op != "bidir_scan":
+        raise ValueError("rev is an argument of bidir_scan only")
+    if op == "bidir_scan":
+        func, code = "bidir_scan", _abi.R2L_OP_BIDIR
+    elif op == "r2l_scan":
         func, code = "r2l_scan", _abi.R2L_OP_SCAN
     elif op == "prefix_scan_state":
         func, code = "prefix_scan_state", _abi.R2L_OP_PREFIX
@@ -184,7 +193,7 @@ def bind(op: str, **kw) -> BoundCall:
     else:
         raise ValueError("unknown entry point %r" % op)
     x = kw["x"]
-    if op == "r2l_scan" and kw.get("out") is None:
+    if op in ("r2l_scan", "bidir_scan") and kw.get("out") is None:
         raise ValueError("bind() needs the output tensor")
     names = ("x", "dt", "Bm", "Cm", "A", "Dskip", "cu_seqlens", "max_seqlen", "h_in", "h_out",
              "res", "s", "out", "delta_softplus", "chunk_tokens", "state_split")
@@ -196,16 +205,18 @@ def bind(op: str, **kw) -> BoundCall:
         raise ValueError("unknown arguments %s" % sorted(unknown))
     vals = [kw.get(n, defaults.get(n)) for n in names]
     a = _fill(*vals)
+    r = _fill_dir(a, x, rev) if op == "bidir_scan" else None
     ws = _attach_workspace(code, a, ws, x.device)
-    keep = [v for v in vals if isinstance(v, torch.Tensor)]
-    return BoundCall(func, code, a, keep, ws, x.device)
+    keep = [v for v in vals if isinstance(v, torch.Tensor)] + list((rev or {}).values())
+    return BoundCall(func, code, a, keep, ws, x.device, rev=r)
 
 
 def workspace_size(op: str, x, A, *, cu_seqlens=None, max_seqlen=None, out=True,
                    chunk_tokens=0, state_split=0) -> int:
-    """Workspace bytes for op in {"r2l_scan", "prefix_scan_state", "block_commit_state"}."""
+    """Workspace bytes for op in {"r2l_scan", "prefix_scan_state", "block_commit_state",
+    "bidir_scan"}."""
     codes = {"r2l_scan": _abi.R2L_OP_SCAN, "prefix_scan_state": _abi.R2L_OP_PREFIX,
-             "block_commit_state": _abi.R2L_OP_COMMIT}
+             "block_commit_state": _abi.R2L_OP_COMMIT, "bidir_scan": _abi.R2L_OP_BIDIR}
     a = _fill(x, None, None, None, A, None, cu_seqlens, max_seqlen, None, None, None, 0.0,
               None, True, chunk_tokens, state_split)
     if out:
@@ -265,6 +276,64 @@ def block_commit_state(state, x, dt, Bm, A, *, cu_seqlens=None, max_seqlen=None,
               delta_softplus, chunk_tokens, state_split)
     _run("block_commit_state", _abi.R2L_OP_COMMIT, a, workspace, x.device)
     return (state, out) if Cm is not None else state
+
+
+# ---- bidirectional scan -------------------------------------------------------
+_DIR_KEYS = ("dt", "Bm", "Cm", "A", "Dskip")
+
+
+def _fill_dir(a, x, rev):
+    """``r2l_dir_args`` of the reverse direction from a dict with any of the
+    keys dt, Bm, Cm, A, Dskip (a missing key shares the forward's tensor);
+    None when nothing is given."""
+    if not rev:
+        return None
+    unknown = set(rev) - set(_DIR_KEYS)
+    if unknown:
+        raise ValueError("unknown reverse-direction parameters %s" % sorted(unknown))
+    D, N = int(a.dim), int(a.dstate)
+    rows = _rows(x, D, "x")[3]
+    r = _abi.DirArgs()
+    for n, cols in (("dt", D), ("Bm", N), ("Cm", N)):
+        t = rev.get(n)
+        if t is None:
+            continue
+        if t.dtype != x.dtype:
+            raise ValueError("reverse %s has dtype %s but x has %s" % (n, t.dtype, x.dtype))
+        if t.dim() != x.dim() or (t.dim() == 3 and t.shape[:2] != x.shape[:2]):
+            raise ValueError("reverse %s has shape %s, x has %s"
+                             % (n, tuple(t.shape), tuple(x.shape)))
+        p, st, bst, nr = _rows(t, cols, "reverse " + n)
+        if nr != rows:
+            raise ValueError("reverse %s has %d token rows, x has %d" % (n, nr, rows))
+        setattr(r, n, p)
+        setattr(r, n + "_stride", st)
+        setattr(r, n + "_batch_stride", bst)
+    _check_f32(rev.get("A"), (D, N), "reverse A")
+    _check_f32(rev.get("Dskip"), (D,), "reverse Dskip")
+    r.A, r.Dskip = _ptr(rev.get("A")), _ptr(rev.get("Dskip"))
+    return r
+
+
+def bidir_scan(x, dt, Bm, Cm, A, Dskip=None, *, rev=None, cu_seqlens=None, max_seqlen=None,
+               h_in=None, h_out=None, res=None, s=0.0, out=None, delta_softplus=True,
+               chunk_tokens=0, workspace=None):
+    """Bidirectional full-window scan: the forward scan of x (dt, Bm, Cm, A,
+    Dskip; from h_in) plus the reverse scan of x (``rev``: a dict with any of
+    dt, Bm, Cm, A, Dskip, the rest shared; from zero), readouts added, then
+    out = y (res None) or res + s*y (s == 0: res bit for bit). ``h_out``
+    receives the forward direction's final state. Returns ``out``.
+    """
+    if out is None:
+        out = torch.empty_like(x)
+    a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
+              delta_softplus, chunk_tokens, 0)
+    r = _fill_dir(a, x, rev)
+    workspace = _attach_workspace(_abi.R2L_OP_BIDIR, a, workspace, x.device)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _abi.call_bidir(a, r, stream)
+    return out
 
 
 # ---- backward ---------------------------------------------------------------

@@ -25,13 +25,15 @@ R2L_DTYPE_BF16 = 1
 R2L_OP_SCAN = 0
 R2L_OP_PREFIX = 1
 R2L_OP_COMMIT = 2
+R2L_OP_BIDIR = 3
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
            "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
-           "r2l_check_access_backward", "prefix_scan_backward")
+           "r2l_check_access_backward", "prefix_scan_backward", "bidir_scan",
+           "r2l_check_access_bidir")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -65,6 +67,16 @@ class GradArgs(ctypes.Structure):
         ("ddt", _vp), ("ddt_stride", _i64), ("ddt_batch_stride", _i64),
         ("dBm", _vp), ("dCm", _vp), ("dA", _vp), ("dDskip", _vp), ("dh_in", _vp), ("ds", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class DirArgs(ctypes.Structure):
+    """Mirror of ``r2l_dir_args`` (the reverse direction of bidir_scan)."""
+    _fields_ = [
+        ("dt", _vp), ("dt_stride", _i64), ("dt_batch_stride", _i64),
+        ("Bm", _vp), ("Bm_stride", _i64), ("Bm_batch_stride", _i64),
+        ("Cm", _vp), ("Cm_stride", _i64), ("Cm_batch_stride", _i64),
+        ("A", _vp), ("Dskip", _vp),
     ]
 
 
@@ -125,6 +137,12 @@ def load(path: str = LIB_PATH):
     lib.r2l_check_access_backward.restype = _i32
     lib.r2l_check_access_backward.argtypes = [_i32, ptr, gptr, ctypes.POINTER(_i32),
                                               ctypes.POINTER(AccessReport)]
+    dptr = ctypes.POINTER(DirArgs)
+    lib.bidir_scan.restype = _i32
+    lib.bidir_scan.argtypes = [ptr, dptr, _vp]
+    lib.r2l_check_access_bidir.restype = _i32
+    lib.r2l_check_access_bidir.argtypes = [ptr, dptr, ctypes.POINTER(_i32),
+                                           ctypes.POINTER(AccessReport)]
     if lib.r2l_abi_version() != ABI_VERSION:
         raise ImportError("libr2l_scan.so ABI %d, binding expects %d"
                           % (lib.r2l_abi_version(), ABI_VERSION))
@@ -198,6 +216,28 @@ def check_access_backward(args: ScanArgs, grad: GradArgs, cu_seqlens_host=None, 
         cu = ctypes.cast(arr, ctypes.POINTER(_i32))
     st = lib.r2l_check_access_backward(1 if reverse else 0, ctypes.byref(args), ctypes.byref(grad),
                                        cu, ctypes.byref(rep))
+    return st, rep
+
+
+def _dir_ref(rev):
+    return None if rev is None else ctypes.byref(rev)
+
+
+def call_bidir(args: ScanArgs, rev: DirArgs | None, stream: int | None) -> None:
+    st = load().bidir_scan(ctypes.byref(args), _dir_ref(rev), _vp(stream or 0))
+    if st != R2L_OK:
+        raise R2LError(st, "bidir_scan", last_error())
+
+
+def check_access_bidir(args: ScanArgs, rev: DirArgs | None, cu_seqlens_host=None):
+    """Host replay of every access bidir_scan would make; (status, report)."""
+    lib = load()
+    rep = AccessReport()
+    cu = None
+    if cu_seqlens_host is not None:
+        arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
+        cu = ctypes.cast(arr, ctypes.POINTER(_i32))
+    st = lib.r2l_check_access_bidir(ctypes.byref(args), _dir_ref(rev), cu, ctypes.byref(rep))
     return st, rep
 
 

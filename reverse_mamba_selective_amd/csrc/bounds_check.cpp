@@ -94,7 +94,8 @@ uintptr_t U(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
 void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const SegParams &p = l.seg;
-    const bool launch_readout = l.mode != kModeState;
+    const bool launch_readout = (l.mode & kModeOutMask) != kModeState;
+    const bool to_ws = (l.mode & kModeOutMask) == kModeWs;
     const int G = l.G, NS = kN / G;
     const int64_t es = l.dtype == R2L_DTYPE_BF16 ? 2 : 4;
     const Region *rA = ck.region_of(p.A), *rDs = p.Dskip ? ck.region_of(p.Dskip) : nullptr;
@@ -103,8 +104,10 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const Region *rSd = p.sdelta ? ck.region_of(p.sdelta) : nullptr;
     const Region *rX = ck.region_of(p.x), *rD = ck.region_of(p.dt), *rB = ck.region_of(p.Bm);
     const Region *rC = launch_readout ? ck.region_of(p.Cm) : nullptr;
-    const Region *rR = l.mode == kModeRes ? ck.region_of(p.res) : nullptr;
-    const Region *rO = launch_readout ? ck.region_of(p.out) : nullptr;
+    const Region *rR = (l.mode & kModeOutMask) == kModeRes ? ck.region_of(p.res) : nullptr;
+    const Region *rO = launch_readout && !to_ws ? ck.region_of(p.out) : nullptr;
+    const Region *rW = to_ws ? ck.region_of(p.yws) : nullptr;
+    const Region *rAdd = (l.mode & kModeAdd) ? ck.region_of(p.yadd) : nullptr;
 
     for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
         const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, bid);
@@ -167,10 +170,32 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
             ck.access(what, reg, b0 + static_cast<uint64_t>(dmin) * es, es);
             ck.access(what, reg, b0 + static_cast<uint64_t>(dmax) * es, es);
         };
+        // fp32 [packed token, D] workspace rows (bidirectional scan): the
+        // resource starts at the sequence's first packed row
+        auto ws_row = [&](const char *what, const Region *reg, const float *base, int k, bool write) {
+            const int row = seg_row(sg, k);
+            if (row < 0 || row >= sq.len)
+                return ck.fail("%s: row %d outside the sequence of %lld rows (block %lld)", what, row,
+                               (long long)sq.len, (long long)bid);
+            const uint64_t soff = static_cast<uint64_t>(row) * static_cast<uint64_t>(p.D * 4);
+            if (soff > UINT32_MAX) return ck.fail("%s: scalar offset %llu above 32 bits", what,
+                                                  (unsigned long long)soff);
+            if (static_cast<uint64_t>(dmax) * 4 + 4 > seq_span_bytes(sq.len, p.D, p.D, 4))
+                return ck.fail("%s: lane offset beyond the buffer resource", what);
+            const uintptr_t b0 = U(base) + static_cast<uint64_t>(sq.s0p * p.D) * 4 + soff;
+            for (uint32_t d : {dmin, dmax}) {
+                ck.access(what, reg, b0 + static_cast<uint64_t>(d) * 4, 4);
+                if (write)
+                    ck.wrote(b0 + static_cast<uint64_t>(d) * 4, 4);
+                else
+                    ck.read_written(what, b0 + static_cast<uint64_t>(d) * 4, 4);
+            }
+        };
         auto load_pos = [&](int k) {
             row_access("x", rX, p.x, sq.xo, p.xs, k);
             row_access("dt", rD, p.dt, sq.dto, p.dts, k);
-            if (mode == kModeRes) row_access("res", rR, p.res, sq.ro, p.rs, k);
+            if ((mode & kModeOutMask) == kModeRes) row_access("res", rR, p.res, sq.ro, p.rs, k);
+            if (mode & kModeAdd) ws_row("reverse readout rows", rAdd, p.yadd, k, false);
         };
         const int ntok = sg.ntok;
         // backward phase 1: the state entering every group of kCkptTokens
@@ -189,7 +214,10 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
             for (int j = 0; j < kPrefetch; ++j) load_pos(prefetch_pos(j, ntok));
         for (int k = 0; k < ntok && ck.ok(); ++k) {
             load_pos(prefetch_pos(k + kPrefetch, ntok));
-            if (readout) row_access("out", rO, p.out, sq.oo, p.os, k);
+            if (readout && to_ws)
+                ws_row("readout rows", rW, p.yws, k, true);
+            else if (readout)
+                row_access("out", rO, p.out, sq.oo, p.os, k);
         }
 
         // Bm/Cm staging, tile by tile: per thread one run of STAGE elements
@@ -455,6 +483,82 @@ r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r
                 break;
             default:
                 ck.fail("unexpected launch kind in a backward plan");
+        }
+    }
+    return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;
+}
+
+r2l_status check_bidir_accesses(const r2l_scan_args *a, const r2l_dir_args *rev, const BidirPlan &bp,
+                                const int32_t *cu_host, r2l_access_report *rep) {
+    const int64_t es = elem_size(a->dtype), D = a->dim, N = kN;
+    const int64_t tok = tokens_of(a);
+    const r2l_scan_args r = reverse_view(a, rev);
+    std::vector<Region> regs;
+    auto add = [&](const char *name, const void *p, uint64_t bytes) {
+        if (p && bytes) regs.push_back({name, U(p), U(p) + bytes});
+    };
+    auto tspan = [&](const void *p, int64_t stride, int64_t bstride, int64_t cols) -> uint64_t {
+        if (!p || tok <= 0) return 0;
+        const int64_t ext = is_ragged(a)
+            ? (tok - 1) * stride + cols
+            : (a->batch - 1) * eff_bstride(a, bstride, stride) + (a->seqlen - 1) * stride + cols;
+        return static_cast<uint64_t>(ext * es);
+    };
+    add("x", a->x, tspan(a->x, a->x_stride, a->x_batch_stride, D));
+    add("dt", a->dt, tspan(a->dt, a->dt_stride, a->dt_batch_stride, D));
+    add("Bm", a->Bm, tspan(a->Bm, a->Bm_stride, a->Bm_batch_stride, N));
+    add("Cm", a->Cm, tspan(a->Cm, a->Cm_stride, a->Cm_batch_stride, N));
+    add("reverse dt", r.dt, tspan(r.dt, r.dt_stride, r.dt_batch_stride, D));
+    add("reverse Bm", r.Bm, tspan(r.Bm, r.Bm_stride, r.Bm_batch_stride, N));
+    add("reverse Cm", r.Cm, tspan(r.Cm, r.Cm_stride, r.Cm_batch_stride, N));
+    add("res", a->res, tspan(a->res, a->res_stride, a->res_batch_stride, D));
+    add("out", a->out, tspan(a->out, a->out_stride, a->out_batch_stride, D));
+    add("A", a->A, static_cast<uint64_t>(D * N * 4));
+    add("reverse A", r.A, static_cast<uint64_t>(D * N * 4));
+    add("Dskip", a->Dskip, static_cast<uint64_t>(D * 4));
+    add("reverse Dskip", r.Dskip, static_cast<uint64_t>(D * 4));
+    add("h_in", a->h_in, static_cast<uint64_t>(a->batch * D * N * 4));
+    add("h_out", a->h_out, static_cast<uint64_t>(a->batch * D * N * 4));
+    add("cu_seqlens", a->cu_seqlens, static_cast<uint64_t>((a->batch + 1) * 4));
+    const char *ws = static_cast<const char *>(a->workspace);
+    const Plan &pl = bp.pl;
+    const size_t c0 = bp.off_chunk;
+    if (ws && bp.readout) add("workspace readout rows", ws, c0);
+    if (ws && pl.chunked) {
+        add("workspace Q", ws + c0, pl.off_S);
+        add("workspace S", ws + c0 + pl.off_S, (bp.readout ? pl.off_H : pl.ws_bytes) - pl.off_S);
+        if (bp.readout) add("workspace H", ws + c0 + pl.off_H, pl.ws_bytes - pl.off_H);
+    }
+    Checker ck(std::move(regs), rep);
+    ck.set_workspace(a->workspace, bp.ws_bytes);
+    Launch ls[kMaxBidirLaunches];
+    const int n = build_bidir_launches(a, rev, bp, ls);
+    for (int i = 0; i < n && ck.ok(); ++i) {
+        ++rep->launches;
+        const Launch &l = ls[i];
+        if (l.kind == Launch::Bidir) {
+            // the fused launch: the reverse pass, then the forward pass
+            Launch pass = l;
+            pass.kind = Launch::Segment;
+            pass.reverse = true;
+            pass.mode = kModeWs;
+            pass.seg = l.seg;
+            if (pass.seg.bc_vec) ++rep->vector_staging;
+            check_segment(ck, pass, cu_host);
+            pass.reverse = false;
+            pass.mode = l.mode;
+            pass.seg = l.seg2;
+            if (pass.seg.bc_vec) ++rep->vector_staging;
+            if (ck.ok()) check_segment(ck, pass, cu_host);
+        } else if (l.kind == Launch::Segment) {
+            if (l.seg.bc_vec) ++rep->vector_staging;
+            check_segment(ck, l, cu_host);
+        } else if (l.kind == Launch::Copy) {
+            check_copy(ck, l);
+        } else if (l.kind == Launch::Carry) {
+            check_carry(ck, l, cu_host);
+        } else {
+            ck.fail("unexpected launch kind in a bidirectional plan");
         }
     }
     return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;

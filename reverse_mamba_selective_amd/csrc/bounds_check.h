@@ -15,4 +15,8 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
 r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r2l_grad_args *g,
                                    const BwdPlan &pl, const int32_t *cu_host, r2l_access_report *rep);
 
+// The same for bidir_scan (after its checks).
+r2l_status check_bidir_accesses(const r2l_scan_args *a, const r2l_dir_args *rev, const BidirPlan &bp,
+                                const int32_t *cu_host, r2l_access_report *rep);
+
 }  // namespace r2l

@@ -253,7 +253,14 @@ r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
         const char *what = "segment scan launch";
         switch (l.kind) {
             case Launch::Segment:
-                e = r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream);
+                e = l.mode >= r2l::kModeWs
+                    ? r2l::launch_bidir_segment(l.reverse, l.dtype, l.mode, l.seg, stream)
+                    : r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream);
+                break;
+            case Launch::Bidir:
+                e = r2l::launch_bidir_fused(l.dtype, l.mode & r2l::kModeOutMask, l.seg, l.seg2,
+                                            stream);
+                what = "bidirectional scan launch";
                 break;
             case Launch::Carry:
                 e = r2l::launch_carry(l.carry, stream);
@@ -292,6 +299,95 @@ r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
     Launch ls[3];
     const int n = r2l::build_launches(op, a, pl, ls);
     return execute(ls, n, stream);
+}
+
+// ---- bidirectional scan -----------------------------------------------------------
+// Each direction is checked as a scan with readout into out: the forward one
+// with the call's residual and states, the reverse one with its own
+// parameters and neither residual nor state (so that out may be
+// exactly x but overlaps nothing else of either direction), both without the
+// workspace, which is then checked against every buffer of both.
+r2l_status check_bidir(const r2l_scan_args *a, const r2l_dir_args *rev, const r2l::BidirPlan &bp) {
+    if (a->state_split > 1)
+        return fail(R2L_ERR_UNSUPPORTED, "bidir_scan runs one lane per channel (state_split 0 or 1)");
+    const int64_t tok = tokens_of(a);
+    if (tok > 0 && !a->out) return fail(R2L_ERR_INVALID_ARG, "out is NULL");
+    Plan bare = bp.pl;
+    bare.chunked = false;
+    r2l_scan_args f = *a;
+    f.workspace = nullptr;
+    f.workspace_bytes = 0;
+    r2l_status st = check_buffers(Op::Scan, &f, bare);   // (a readout is always wanted)
+    if (st != R2L_OK) return st;
+    r2l_scan_args r = r2l::reverse_view(&f, rev);
+    st = check_buffers(Op::Scan, &r, bare);
+    if (st != R2L_OK) return st;
+    if (bp.readout && a->dim * r2l::max_len_of(a) * 4 > (int64_t)UINT32_MAX)
+        return fail(R2L_ERR_UNSUPPORTED, "one sequence's fp32 rows span more than 4 GiB");
+    if (bp.ws_bytes == 0) return R2L_OK;
+    if (!a->workspace || a->workspace_bytes < bp.ws_bytes)
+        return fail(R2L_ERR_WORKSPACE, "bidir_scan needs %zu workspace bytes, got %zu", bp.ws_bytes,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned(a->workspace, 256)) return fail(R2L_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+    const int64_t D = a->dim, N = r2l::kN, es = elem_size(a->dtype);
+    const Range ws = span("workspace", a->workspace, 1, (int64_t)bp.ws_bytes, (int64_t)bp.ws_bytes, 1, true);
+    const Range others[] = {
+        token_span("x", a, a->x, a->x_stride, a->x_batch_stride, D, es, false),
+        token_span("dt", a, a->dt, a->dt_stride, a->dt_batch_stride, D, es, false),
+        token_span("Bm", a, a->Bm, a->Bm_stride, a->Bm_batch_stride, N, es, false),
+        token_span("Cm", a, a->Cm, a->Cm_stride, a->Cm_batch_stride, N, es, false),
+        token_span("reverse dt", a, r.dt, r.dt_stride, r.dt_batch_stride, D, es, false),
+        token_span("reverse Bm", a, r.Bm, r.Bm_stride, r.Bm_batch_stride, N, es, false),
+        token_span("reverse Cm", a, r.Cm, r.Cm_stride, r.Cm_batch_stride, N, es, false),
+        token_span("res", a, a->res, a->res_stride, a->res_batch_stride, D, es, false),
+        token_span("out", a, a->out, a->out_stride, a->out_batch_stride, D, es, false),
+        span("A", a->A, D, N, N, 4, false),
+        span("reverse A", r.A, D, N, N, 4, false),
+        span("Dskip", a->Dskip, 1, D, D, 4, false),
+        span("reverse Dskip", r.Dskip, 1, D, D, 4, false),
+        span("cu_seqlens", a->cu_seqlens, 1, a->batch + 1, a->batch + 1, 4, false),
+        span("h_in", a->h_in, a->batch, D * N, D * N, 4, false),
+        span("h_out", a->h_out, a->batch, D * N, D * N, 4, false),
+    };
+    for (const Range &o : others)
+        if (overlap(ws, o)) return fail(R2L_ERR_ALIAS, "workspace overlaps %s", o.name);
+    return R2L_OK;
+}
+
+r2l_status prepare_bidir(const r2l_scan_args *a, const r2l_dir_args *rev, r2l::BidirPlan *bp) {
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    *bp = r2l::make_bidir_plan(a);
+    st = check_bidir(a, rev, *bp);
+    if (st != R2L_OK) return st;
+    if (a->batch * bp->pl.nchunks * bp->pl.tiles > INT32_MAX - 8)
+        return fail(R2L_ERR_UNSUPPORTED, "grid too large");
+    return R2L_OK;
+}
+
+r2l_status run_bidir(const r2l_scan_args *a, const r2l_dir_args *rev, hipStream_t stream) {
+    r2l::BidirPlan bp;
+    r2l_status st = prepare_bidir(a, rev, &bp);
+    if (st != R2L_OK) return st;
+    st = check_seqlens_on_device(a);
+    if (st != R2L_OK) return st;
+    Launch ls[r2l::kMaxBidirLaunches];
+    const int n = r2l::build_bidir_launches(a, rev, bp, ls);
+    return execute(ls, n, stream);
+}
+
+// Host offsets handed to an access replay: they must describe the call.
+r2l_status check_host_offsets(const r2l_scan_args *a, const int32_t *cu) {
+    if (!ragged(a) || a->batch == 0) return R2L_OK;
+    if (!cu) return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+    if (cu[0] != 0 || cu[a->batch] != a->total_tokens)
+        return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host does not span total_tokens");
+    for (int64_t b = 0; b < a->batch; ++b) {
+        const int64_t L = static_cast<int64_t>(cu[b + 1]) - cu[b];
+        if (L < 0 || L > a->max_seqlen)
+            return fail(R2L_ERR_INVALID_ARG, "cu_seqlens_host: bad length at %lld", (long long)b);
+    }
+    return R2L_OK;
 }
 
 // ---- backward -------------------------------------------------------------------
@@ -444,6 +540,25 @@ r2l_status r2l_backward_workspace_size(const r2l_scan_args *fwd, const r2l_grad_
 }
 
 
+r2l_status bidir_scan(const r2l_scan_args *a, const r2l_dir_args *rev, void *stream) {
+    return run_bidir(a, rev, static_cast<hipStream_t>(stream));
+}
+
+r2l_status r2l_check_access_bidir(const r2l_scan_args *a, const r2l_dir_args *rev,
+                                  const int32_t *cu_seqlens_host, r2l_access_report *report) {
+    if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
+    report->launches = report->accesses = report->vector_staging = 0;
+    report->message[0] = '\0';
+    r2l::BidirPlan bp;
+    r2l_status st = prepare_bidir(a, rev, &bp);
+    if (st != R2L_OK) return st;
+    st = check_host_offsets(a, cu_seqlens_host);
+    if (st != R2L_OK) return st;
+    st = r2l::check_bidir_accesses(a, rev, bp, cu_seqlens_host, report);
+    if (st != R2L_OK) return fail(st, "%s", report->message);
+    return ok();
+}
+
 r2l_status r2l_scan(const r2l_scan_args *a, void *stream) {
     return run(Op::Scan, a, static_cast<hipStream_t>(stream));
 }
@@ -458,10 +573,14 @@ r2l_status block_commit_state(const r2l_scan_args *a, void *stream) {
 
 r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes) {
     if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
-    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT)
+    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT && op != R2L_OP_BIDIR)
         return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);
     r2l_status st = check_shape(a);
     if (st != R2L_OK) return st;
+    if (op == R2L_OP_BIDIR) {
+        *bytes = r2l::make_bidir_plan(a).ws_bytes;
+        return ok();
+    }
     const Op o = op == R2L_OP_SCAN ? Op::Scan : (op == R2L_OP_PREFIX ? Op::Prefix : Op::Commit);
     *bytes = r2l::make_plan(o, a).ws_bytes;
     return ok();
@@ -497,10 +616,21 @@ r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *c
 
 r2l_status r2l_describe_plan(int32_t op, const r2l_scan_args *a, r2l_plan_info *info) {
     if (!info) return fail(R2L_ERR_INVALID_ARG, "info is NULL");
-    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT)
+    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT && op != R2L_OP_BIDIR)
         return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);
     r2l_status st = check_shape(a);
     if (st != R2L_OK) return st;
+    if (op == R2L_OP_BIDIR) {
+        const r2l::BidirPlan bp = r2l::make_bidir_plan(a);
+        info->lanes_per_channel = 1;
+        info->chunked = bp.pl.chunked ? 1 : 0;
+        info->chunk_tokens = bp.pl.chunk_len;
+        info->chunks = bp.pl.nchunks;
+        info->workspace_bytes = static_cast<int64_t>(bp.ws_bytes);
+        Launch ls[r2l::kMaxBidirLaunches];
+        info->launches = r2l::build_bidir_launches(a, nullptr, bp, ls);
+        return ok();
+    }
     const Op o = op == R2L_OP_SCAN ? Op::Scan : (op == R2L_OP_PREFIX ? Op::Prefix : Op::Commit);
     const Plan pl = r2l::make_plan(o, a);
     info->lanes_per_channel = pl.G;

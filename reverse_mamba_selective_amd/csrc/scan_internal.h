@@ -17,6 +17,12 @@ constexpr int kModeState = 0;
 constexpr int kModeY = 1;
 constexpr int kModeResX = 2;
 constexpr int kModeRes = 3;
+// The bidirectional scan's two passes: the first writes its y as fp32 rows to
+// the workspace (kModeWs), the second adds them to its own y before its
+// output rule (kModeAdd combined with kModeY, kModeResX or kModeRes).
+constexpr int kModeWs = 4;
+constexpr int kModeOutMask = 7;
+constexpr int kModeAdd = 8;
 
 // One launch of the segment kernel scans "segments": chunk c (in visiting
 // order) of sequence b, for a tile of kWG lanes. With G lanes per channel a
@@ -60,6 +66,11 @@ struct SegParams {
     // backward, phase 1 (state-only, unchunked): the state before every
     // kCkptTokens-th visited position, at ckpt + (ckpt_row * D + d) * kN
     float *ckpt;
+
+    // bidirectional scan: fp32 [packed tokens, D] rows of y written by the
+    // first pass (kModeWs) and added by the second (kModeAdd)
+    float *yws;
+    const float *yadd;
 };
 
 // ---- backward (gradients of a scan with readout) ----------------------------
@@ -151,6 +162,12 @@ struct CopyParams {
 hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode,
                                const SegParams &p, hipStream_t stream);
 hipError_t launch_carry(const CarryParams &p, hipStream_t stream);
+// bidirectional scan: one launch running both passes (unchunked plans), or a
+// segment launch of one direction's chunked plan (modes kModeWs, kModeAdd | m)
+hipError_t launch_bidir_fused(int dtype, int out_mode, const SegParams &pr, const SegParams &pf,
+                              hipStream_t stream);
+hipError_t launch_bidir_segment(bool reverse, int dtype, int mode, const SegParams &p,
+                                hipStream_t stream);
 hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream);
 // G in {2, 4}
 hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, hipStream_t stream);

@@ -240,6 +240,94 @@ int build_scan_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch ou
 
 }  // namespace
 
+// ---- bidirectional scan ------------------------------------------------------------
+BidirPlan make_bidir_plan(const r2l_scan_args *a) {
+    BidirPlan bp;
+    r2l_scan_args v = *a;
+    v.state_split = 1;
+    bp.readout = runs_readout(Op::Prefix, &v);
+    bp.pl = make_plan(Op::Prefix, &v);
+    if (!bp.readout) {
+        bp.ws_bytes = bp.pl.ws_bytes;
+        return bp;
+    }
+    bp.fused = !bp.pl.chunked;
+    bp.off_chunk = align256(static_cast<size_t>(tokens_of(a)) * static_cast<size_t>(a->dim) * 4);
+    bp.ws_bytes = bp.off_chunk + bp.pl.ws_bytes;
+    return bp;
+}
+
+r2l_scan_args reverse_view(const r2l_scan_args *a, const r2l_dir_args *rev) {
+    r2l_scan_args r = *a;
+    if (rev) {
+        if (rev->dt) { r.dt = rev->dt; r.dt_stride = rev->dt_stride; r.dt_batch_stride = rev->dt_batch_stride; }
+        if (rev->Bm) { r.Bm = rev->Bm; r.Bm_stride = rev->Bm_stride; r.Bm_batch_stride = rev->Bm_batch_stride; }
+        if (rev->Cm) { r.Cm = rev->Cm; r.Cm_stride = rev->Cm_stride; r.Cm_batch_stride = rev->Cm_batch_stride; }
+        if (rev->A) r.A = rev->A;
+        if (rev->Dskip) r.Dskip = rev->Dskip;
+    }
+    r.res = nullptr; r.res_stride = 0; r.res_batch_stride = 0;
+    r.s = 0.0f;
+    r.h_in = nullptr;
+    r.h_out = nullptr;
+    r.state_split = 1;
+    return r;
+}
+
+int build_bidir_launches(const r2l_scan_args *a, const r2l_dir_args *rev, const BidirPlan &bp,
+                         Launch out[kMaxBidirLaunches]) {
+    if (a->batch == 0) return 0;
+    r2l_scan_args f = *a;
+    f.state_split = 1;
+    if (!bp.readout) return build_launches(Op::Prefix, &f, bp.pl, out);
+    if (tokens_of(a) == 0 && !a->h_out) return 0;
+
+    char *ws = static_cast<char *>(a->workspace);
+    float *rows = reinterpret_cast<float *>(ws);
+    r2l_scan_args r = reverse_view(a, rev);
+    r.workspace = ws + bp.off_chunk;
+    r.workspace_bytes = bp.pl.ws_bytes;
+    f.workspace = ws + bp.off_chunk;
+    f.workspace_bytes = bp.pl.ws_bytes;
+    const int64_t DN = a->dim * kN;
+
+    if (bp.fused) {
+        SegParams pr = base_params(&r, bp.pl);
+        pr.out = nullptr;
+        pr.yws = rows;
+        pr.bc_vec = bc_vector_ok(&r, true) ? 1 : 0;
+        SegParams pf = base_params(&f, bp.pl);
+        pf.hin = a->h_in; pf.hin_b = DN; pf.hin_c = 0;
+        pf.hfin = a->h_out; pf.hfin_b = DN; pf.hfin_c = 0;
+        pf.yadd = rows;
+        pf.bc_vec = bc_vector_ok(&f, true) ? 1 : 0;
+        Launch l{};
+        l.kind = Launch::Bidir;
+        l.dtype = a->dtype;
+        l.G = 1;
+        l.mode = kModeAdd | out_mode(&f, pf);
+        l.seg = pr;
+        l.seg2 = pf;
+        out[0] = l;
+        return 1;
+    }
+    // chunked: each direction's own plan, the readout launches retargeted
+    int n = build_scan_launches(Op::Scan, &r, bp.pl, out);
+    for (int i = 0; i < n; ++i)
+        if (out[i].kind == Launch::Segment && out[i].mode != kModeState) {
+            out[i].mode = kModeWs;
+            out[i].seg.out = nullptr;
+            out[i].seg.yws = rows;
+        }
+    const int m = build_scan_launches(Op::Prefix, &f, bp.pl, out + n);
+    for (int i = n; i < n + m; ++i)
+        if (out[i].kind == Launch::Segment && out[i].mode != kModeState) {
+            out[i].mode |= kModeAdd;
+            out[i].seg.yadd = rows;
+        }
+    return n + m;
+}
+
 // ---- backward ------------------------------------------------------------------
 BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
     BwdPlan pl;

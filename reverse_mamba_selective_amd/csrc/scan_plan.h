@@ -24,12 +24,13 @@ struct Plan {
 };
 
 struct Launch {
-    enum Kind { Segment, Carry, Copy, Backward, Sum } kind;
+    enum Kind { Segment, Carry, Copy, Backward, Sum, Bidir } kind;
     bool reverse;
     int dtype;
     int G;
     int mode;                // kMode* (segment launches)
-    SegParams seg;
+    SegParams seg;           // (Bidir: the reverse pass)
+    SegParams seg2;          // Bidir: the forward pass
     CarryParams carry;
     CopyParams copy;
     BwdParams bwd;
@@ -87,6 +88,25 @@ inline int64_t eff_bstride(const r2l_scan_args *a, int64_t bstride, int64_t stri
 }
 
 Plan make_plan(Op op, const r2l_scan_args *a);
+
+// The bidirectional scan (bidir_scan): the reverse direction's readout into
+// fp32 workspace rows, then the forward direction's readout adding them; one
+// fused launch when the plan does not chunk. Both directions share one plan
+// (same shape, one lane per channel).
+constexpr int kMaxBidirLaunches = 6;
+struct BidirPlan {
+    Plan pl;                 // either direction's plan (the forward's alone when the gate is closed)
+    bool readout = false;    // false: s == 0 with a residual (out = res, forward state only)
+    bool fused = false;
+    size_t off_chunk = 0;    // the plans' carry workspace after the fp32 rows
+    size_t ws_bytes = 0;
+};
+BidirPlan make_bidir_plan(const r2l_scan_args *a);
+// The reverse direction's arguments: x and the shape from `a`, the parameters
+// from `rev` (NULL pointers: the forward's), no residual, state or output.
+r2l_scan_args reverse_view(const r2l_scan_args *a, const r2l_dir_args *rev);
+int build_bidir_launches(const r2l_scan_args *a, const r2l_dir_args *rev, const BidirPlan &bp,
+                         Launch out[kMaxBidirLaunches]);
 
 // The launches of a call, in order (at most 3). Arguments must have passed
 // the entry point's checks. Returns the count.

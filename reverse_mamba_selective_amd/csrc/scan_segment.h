@@ -1,0 +1,283 @@
+// scan_segment.h -- the segment scan of the gfx950 selective-scan kernels
+// (device code, included by the .hip files that instantiate it: the scans of
+// the three entry points in scan_kernels.hip, the bidirectional scan's in
+// bidir_kernels.hip). See scan_kernels.hip for how it maps onto CDNA4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_device.h"
+#include "scan_geometry.h"
+#include "scan_internal.h"
+
+namespace r2l {
+namespace {
+
+using namespace dev;
+
+// ---- the segment scan ------------------------------------------------------
+// One workgroup scans one segment (a chunk of one sequence) for kWG/G channels.
+// Per lane and token: Delta, then for each of its NS states one exp, the state
+// update and (READOUT) the readout term; the G partial readouts are summed
+// across the lane group; then the skip term and the gated residual.
+//
+// Latency hiding: x / dt / res of the token PF positions ahead are loaded into
+// a register ring before the current token is computed, and the Bm/Cm rows of
+// the next kTile tokens are fetched into registers during the current tile and
+// written to the other half of a double-buffered LDS area at its end (one
+// barrier per tile). Row addresses are uniform (scalar) and the lane adds a
+// 32-bit channel offset.
+template <bool REV, typename T, int G, int MODE, bool SP>
+__device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, const BlockGeom &bg,
+                                             const SeqGeom &sq, const SegGeom &sg,
+                                             const float *hin) {
+    constexpr int OUT = MODE & kModeOutMask;     // what the readout writes
+    constexpr bool ADD = (MODE & kModeAdd) != 0;  // y += an fp32 addend per token
+    constexpr bool READOUT = OUT != kModeState;
+    constexpr int NS = kN / G;                   // states per lane
+    constexpr int NBC = READOUT ? 2 * kN : kN;   // staged floats per token (B, then C)
+    constexpr int STAGE = stage_cols(NBC);       // staged elements per thread per tile
+    constexpr int SW = STAGE * static_cast<int>(sizeof(T)) / 4;   // ... as 32-bit words
+    constexpr int PF = kPrefetch;
+    static_assert(kTile * NBC == STAGE * kWG && kN % STAGE == 0 && STAGE % 4 == 0 &&
+                  kTile % PF == 0, "tile shape");
+    float (*lds_bc)[kTile * NBC] = reinterpret_cast<float (*)[kTile * NBC]>(lds);
+    using E = Elem<T>;
+    using R = typename E::raw_t;
+
+    const int64_t b = bg.b;
+    const int c = bg.c;
+    const int ntok = sg.ntok;
+
+    const LaneGeom lg = lane_geom(bg.tile, threadIdx.x, G, p.D);
+    const uint32_t dl = lg.d;
+    const int sub = lg.sub;
+
+    float a2[NS], h[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) a2[j] = p.A[dl * kN + sub * NS + j] * kLog2e;
+    if (hin) {
+        const float *hp = hin + dl * kN + sub * NS;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) h[j] = hp[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) h[j] = 0.0f;
+    }
+    const float dskip = (READOUT && p.Dskip) ? p.Dskip[dl] : 0.0f;
+    float dsum = 0.0f;
+
+    // Per-token rows go through raw buffer resources based at the sequence's
+    // first row: the row offset is a scalar (row * row bytes) and the lane
+    // adds its fixed 32-bit channel offset. The resource bound only checks the
+    // lane offset, so every row used below is one of the segment's own rows;
+    // the host guarantees that one sequence of one tensor spans < 4 GiB.
+    const uint32_t es = static_cast<uint32_t>(sizeof(T));
+    const uint32_t doff = dl * es;
+    const uint32_t xrb = static_cast<uint32_t>(p.xs) * es, drb = static_cast<uint32_t>(p.dts) * es;
+    const uint32_t rrb = static_cast<uint32_t>(p.rs) * es, orb = static_cast<uint32_t>(p.os) * es;
+    const auto rx = make_rsrc(static_cast<const T *>(p.x) + sq.xo,
+                              seq_span_bytes(sq.len, p.xs, p.D, es));
+    const auto rd = make_rsrc(static_cast<const T *>(p.dt) + sq.dto,
+                              seq_span_bytes(sq.len, p.dts, p.D, es));
+    const auto rr_ = make_rsrc(OUT == kModeRes ? static_cast<const T *>(p.res) + sq.ro : nullptr,
+                               OUT == kModeRes ? seq_span_bytes(sq.len, p.rs, p.D, es) : 0);
+    constexpr bool TO_OUT = READOUT && OUT != kModeWs;
+    const auto ro_ = make_rsrc(TO_OUT ? static_cast<T *>(p.out) + sq.oo : nullptr,
+                               TO_OUT ? seq_span_bytes(sq.len, p.os, p.D, es) : 0);
+    // fp32 rows [packed token, D] of the workspace: y written (kModeWs) or the
+    // addend read (kModeAdd), at the sequence's packed rows
+    const uint32_t wrb = static_cast<uint32_t>(p.D) * 4u, woff = dl * 4u;
+    const auto rw_ = make_rsrc(OUT == kModeWs ? p.yws + sq.s0p * p.D : nullptr,
+                               OUT == kModeWs ? seq_span_bytes(sq.len, p.D, p.D, 4) : 0);
+    const auto ra_ = make_rsrc(ADD ? p.yadd + sq.s0p * p.D : nullptr,
+                               ADD ? seq_span_bytes(sq.len, p.D, p.D, 4) : 0);
+    // Staging: this thread's matrix (uniform per wave) as one resource.
+    const StageSlot ss = stage_slot(threadIdx.x, NBC);
+    const bool stage_c = READOUT && __builtin_amdgcn_readfirstlane(ss.mat) != 0;
+    const auto rbc = stage_c
+        ? make_rsrc(static_cast<const T *>(p.Cm) + sq.Co, seq_span_bytes(sq.len, p.Cs, kN, es))
+        : make_rsrc(static_cast<const T *>(p.Bm) + sq.Bo, seq_span_bytes(sq.len, p.Bs, kN, es));
+    const uint32_t bcrb = static_cast<uint32_t>(stage_c ? p.Cs : p.Bs) * es;
+    const uint32_t bccol = static_cast<uint32_t>(ss.col0) * es;
+    const bool bc_vec = p.bc_vec != 0;
+    const float gate = p.s;   // never 0 in the residual modes
+
+    // ---- register ring of per-token inputs (slot = position % PF)
+    R xq[PF], dq[PF], rq[PF];
+    uint32_t aq[PF];
+    auto load_pos = [&](int k, int slot) {       // k: a visited position of this segment
+        const uint32_t row = static_cast<uint32_t>(seg_row(sg, k));
+        xq[slot] = E::bload(rx, doff, row * xrb);
+        dq[slot] = E::bload(rd, doff, row * drb);
+        if constexpr (OUT == kModeRes) rq[slot] = E::bload(rr_, doff, row * rrb);
+        if constexpr (ADD) aq[slot] = __builtin_amdgcn_raw_buffer_load_b32(ra_, woff, row * wrb, 0);
+    };
+
+    // ---- Bm/Cm staging of one tile of kTile tokens
+    uint32_t stw[SW];
+    auto stage_load = [&](int tbase, int tcnt) {   // tcnt >= 1
+        const uint32_t row = static_cast<uint32_t>(seg_row(sg, tbase + stage_pos(ss.k, tcnt)));
+        const uint32_t voff = row * bcrb + bccol;
+        if (bc_vec)
+            bload_words<SW>(rbc, voff, stw);
+        else
+            E::template bload_elems<STAGE>(rbc, voff, stw);
+    };
+    auto stage_store = [&](int buf) {
+        float4 *dst = reinterpret_cast<float4 *>(&lds_bc[buf][ss.k * NBC + ss.mat * kN + ss.col0]);
+#pragma unroll
+        for (int q = 0; q < STAGE / 4; ++q)
+            dst[q] = make_float4(E::word_elem(stw, 4 * q), E::word_elem(stw, 4 * q + 1),
+                                 E::word_elem(stw, 4 * q + 2), E::word_elem(stw, 4 * q + 3));
+    };
+
+    // One visited position k: consume ring slot `slot`, refill it with the
+    // position PF ahead, update the state and store the output row.
+    // Delta of the next visited position is computed one token ahead, off
+    // the critical path of the current token (its dt is already in the ring).
+    float dnext = 0.0f;
+    auto delta_of = [&](R dr) {
+        const float dv = E::widen(dr);
+        if constexpr (SP)
+            return softplus(dv);
+        else
+            return dv;
+    };
+    auto token = [&](int k, const float *bcrow, int slot) {
+        const R xr = xq[slot], rr = rq[slot];
+        const uint32_t addend = aq[slot];
+        const float delta = dnext;
+        dnext = delta_of(dq[(slot + 1) % PF]);
+        load_pos(prefetch_pos(k + PF, ntok), slot);
+        const float xv = E::widen(xr);
+        if constexpr (!READOUT) dsum += delta;
+        const float dx = delta * xv;
+        const float *row = bcrow + sub * NS;
+        // the readout sums even and odd states separately: two short
+        // dependency chains instead of one of NS fmas
+        float y0 = 0.0f, y1 = 0.0f;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float abar = __builtin_amdgcn_exp2f(delta * a2[n]);
+            h[n] = fmaf(abar, h[n], row[n] * dx);
+            if constexpr (READOUT) {
+                if (n & 1)
+                    y1 = fmaf(row[kN + n], h[n], y1);
+                else
+                    y0 = fmaf(row[kN + n], h[n], y0);
+            }
+        }
+        if constexpr (READOUT) {
+            float y = group_sum<G>(y0 + y1);
+            y = fmaf(dskip, xv, y);
+            if constexpr (ADD) y += __uint_as_float(addend);
+            // Every lane stores: the G lanes of a channel, and idle lanes
+            // shadowing the last channel, hold bit-identical values for the
+            // same address.
+            const uint32_t orow = static_cast<uint32_t>(seg_row(sg, k));
+            if constexpr (OUT == kModeWs) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rw_, woff, orow * wrb, 0);
+            } else {
+                R o;
+                if constexpr (OUT == kModeY) {
+                    o = E::pack(y);
+                } else {
+                    const R rbits = OUT == kModeRes ? rr : xr;
+                    o = E::pack(fmaf(gate, y, E::widen(rbits)));
+                }
+                E::bstore(o, ro_, doff, orow * orb);
+            }
+        }
+    };
+
+    // Backward phase 1: the state entering each group of kCkptTokens visited
+    // positions (the groups are the prefetch groups).
+    static_assert(PF == kCkptTokens, "checkpoint groups are the prefetch groups");
+    auto checkpoint = [&](int pos) {
+        if (!p.ckpt || !lg.active) return;
+        float *cp = p.ckpt + (ckpt_row(b, sq.s0p, pos) * p.D + dl) * kN + sub * NS;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) cp[j] = h[j];
+    };
+
+    // Start-up: the first tile's Bm/Cm rows are requested first (they gate
+    // the barrier), then the first PF tokens of x/dt/res.
+    const int ntiles = (ntok + kTile - 1) / kTile;
+    const int cnt0 = ntok < kTile ? ntok : kTile;
+    if (ntok > 0) stage_load(0, cnt0);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        rq[j] = 0;
+        aq[j] = 0;
+    }
+    if (ntok > 0) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) load_pos(prefetch_pos(j, ntok), j);
+        stage_store(0);
+        dnext = delta_of(dq[0]);
+    }
+    __syncthreads();
+
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int base = ti * kTile;
+        const int cnt = ntok - base < kTile ? ntok - base : kTile;
+        const bool more = ti + 1 < ntiles;
+        const int ncnt = more ? (ntok - base - kTile < kTile ? ntok - base - kTile : kTile) : 0;
+        if (more) stage_load(base + kTile, ncnt);
+        const float *bc = lds_bc[ti & 1];
+
+        const int full = cnt - cnt % PF;
+        for (int k0 = 0; k0 < full; k0 += PF) {
+            if constexpr (!READOUT) checkpoint(base + k0);
+#pragma unroll
+            for (int j = 0; j < PF; ++j) token(base + k0 + j, bc + (k0 + j) * NBC, j);
+        }
+        if constexpr (!READOUT)
+            if (full < cnt) checkpoint(base + full);
+#pragma unroll
+        for (int j = 0; j < PF; ++j)            // the last tile's partial group
+            if (full + j < cnt) token(base + full + j, bc + (full + j) * NBC, j);
+
+        if (more) stage_store((ti + 1) & 1);
+        __syncthreads();
+    }
+
+    if (p.hfin && lg.active) {
+        float *hp = p.hfin + b * p.hfin_b + c * p.hfin_c + dl * kN + sub * NS;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) hp[j] = h[j];
+    }
+    if (!READOUT && p.sdelta && lg.active && sub == 0) p.sdelta[b * p.sd_b + c * p.sd_c + dl] = dsum;
+}
+
+// One workgroup per (sequence b, chunk c, channel tile). Chunk passes of
+// readout plans (split_c0) run the readout on chunk 0, which starts from the
+// call's own initial state, and the state-only scan from zero on the others.
+template <bool REV, typename T, int G, int MODE, bool SP>
+__global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
+    constexpr int NBC_MAX = (MODE & kModeOutMask) != kModeState ? 2 * kN : kN;
+    __shared__ __align__(16) float lds[2 * kTile * NBC_MAX];
+
+    const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
+    if (!bg.valid) return;
+    const int64_t b = bg.b;
+    const int c = bg.c;
+    const int64_t s0 = p.cu_seqlens ? p.cu_seqlens[b] : 0;
+    const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[b + 1] : 0;
+    const SeqGeom sq = seq_geom(p, b, s0, s1);
+    const SegGeom sg = seg_geom(REV, c, p.chunk_len, sq.len);
+    if (!segment_runs(p, sg, c)) return;
+    const float *hin = segment_hin(p, b, c);
+    if constexpr ((MODE & kModeOutMask) != kModeState) {
+        if (p.split_c0 && c > 0) {
+            scan_segment<REV, T, G, kModeState, SP>(p, lds, bg, sq, sg, hin);
+            return;
+        }
+    }
+    scan_segment<REV, T, G, MODE, SP>(p, lds, bg, sq, sg, hin);
+}
+
+}  // namespace
+}  // namespace r2l

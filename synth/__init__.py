@@ -171,7 +171,13 @@ RAGGED = Workload(104, "ragged_serving_bf16_b256_blk16to64_D4096_N16",
                   "scan over the blocks (out = y) and block_commit_state over each block; "
                   "prefixes of U{256..8192} tokens for the prefill that builds the states")
 
-WORKLOADS = {w.name: w for w in (TINY, BLOCK, DENOISE, PREFILL, RAGGED)}
+BIDIR = Workload(105, "bidir_window_step_bf16_b64_L32_D2048_N16_7hooks",
+                 "bidirectional full-window scans over the denoising window: batch 64, 32 "
+                 "tokens, D=2048, N=16, bf16 inputs, fp32 state, 7 hooked layers; the forward "
+                 "and the reverse direction each with its own dt, Bm, Cm, A, Dskip; res = x, "
+                 "s ~ U(0, 0.1) per hook")
+
+WORKLOADS = {w.name: w for w in (TINY, BLOCK, DENOISE, PREFILL, RAGGED, BIDIR)}
 
 
 def tiny_inputs() -> ScanInputs:
@@ -218,3 +224,26 @@ def ragged_commit_inputs(seqs=None) -> ScanInputs:
 def ragged_prefix_inputs(seqs=None) -> ScanInputs:
     return scan_inputs(RAGGED.key + 2000, ragged_prefix_lengths(), D=4096, N=16, dtype="bf16",
                        seqs=seqs)
+
+
+def reverse_params(key: int, lengths, D: int, N: int = 16, dtype: str = "f32",
+                   dt_mean: float = -2.0, seqs=None) -> dict:
+    """The reverse direction's own parameters for a bidirectional scan over
+    inputs drawn with ``key``: dt, Bm, Cm and Dskip drawn independently, A the
+    S4D-real matrix at half the rates (so that the two directions differ)."""
+    r = scan_inputs(key + 5000, lengths, D, N, dtype, dt_mean=dt_mean, seqs=seqs)
+    return {"dt": r.dt, "Bm": r.Bm, "Cm": r.Cm, "A": (0.5 * r.A).astype(np.float32),
+            "Dskip": r.Dskip}
+
+
+def bidir_inputs(hook: int = 0, seqs=None) -> ScanInputs:
+    return scan_inputs(BIDIR.key * 100 + hook, [32] * 64, D=2048, N=16, dtype="bf16", seqs=seqs)
+
+
+def bidir_reverse(hook: int = 0, seqs=None) -> dict:
+    return reverse_params(BIDIR.key * 100 + hook, [32] * 64, D=2048, N=16, dtype="bf16",
+                          seqs=seqs)
+
+
+def bidir_gates() -> np.ndarray:
+    return gates(BIDIR.key, 7, 0.0, 0.1)

@@ -338,3 +338,118 @@ def test_backward_benchmarked_shapes():
     check_bwd(batch=64, seqlen=32, D=2048, res="x")
     rep = check_bwd(batch=8, seqlen=4096, D=4096)
     assert rep.launches == 3   # phase 1, phase 2, the sums (dBm, dCm, dA, dDskip: no residual, no ds)
+
+
+# ---- the bidirectional scan ---------------------------------------------------------
+def make_dir(a, heap, kind, *, dtype="bf16", pad_row=0, bc_shift=0):
+    """Reverse-direction parameters for the forward call `a`: "shared" (NULL
+    struct), "separate" (every tensor its own) or "partial" (dt and A only)."""
+    if kind == "shared":
+        return None
+    es = 2 if dtype == "bf16" else 4
+    D, N = a.dim, 16
+    tok = a.total_tokens if a.cu_seqlens else a.batch * a.seqlen
+
+    def tensor(cols, lead=0):
+        stride = cols + pad_row
+        if a.cu_seqlens:
+            p = heap.alloc(((tok - 1) * stride + cols + lead) * es if tok else 0)
+        else:
+            ext = ((a.batch - 1) * a.seqlen * stride + (a.seqlen - 1) * stride + cols + lead) \
+                if tok else 0
+            p = heap.alloc(ext * es)
+        return (p + lead * es if p is not None else None), stride, 0
+
+    r = _abi.DirArgs()
+    r.dt, r.dt_stride, r.dt_batch_stride = tensor(D)
+    r.A = heap.alloc(4 * D * N)
+    if kind == "separate":
+        r.Bm, r.Bm_stride, r.Bm_batch_stride = tensor(N, bc_shift)
+        r.Cm, r.Cm_stride, r.Cm_batch_stride = tensor(N, bc_shift)
+        r.Dskip = heap.alloc(4 * D)
+    return r
+
+
+def check_bidir(rev="separate", **kw):
+    a, cu = make_args("scan", **kw)
+    heap = FakeHeap()
+    heap.next = BASE + (1 << 40)   # away from the forward buffers
+    a.workspace, a.workspace_bytes = None, 0
+    r = make_dir(a, heap, rev, dtype=kw.get("dtype", "bf16"), pad_row=kw.get("pad_row", 0),
+                 bc_shift=kw.get("bc_shift", 0))
+    need = _abi.workspace_size(_abi.R2L_OP_BIDIR, a)
+    if need:
+        a.workspace, a.workspace_bytes = heap.alloc(need), need
+    st, rep = _abi.check_access_bidir(a, r, cu)
+    msg = rep.message.decode() or _abi.last_error()
+    assert st == _abi.R2L_OK, "bidir %s %s: %s" % (rev, kw, msg)
+    return rep
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+@pytest.mark.parametrize("rev", ["shared", "separate", "partial"])
+def test_bidir_edge_cases(case, rev):
+    kw = dict(EDGE[case])
+    for res in ("none", "x", "sep", "inplace"):
+        for dtype in ("bf16", "f32"):
+            check_bidir(rev, res=res, dtype=dtype, **kw)
+    check_bidir(rev, res="x", s=0.0, **kw)     # gate closed: copy (+ forward state)
+    check_bidir(rev, res="x", bc_shift=1, **kw)
+
+
+def test_bidir_plans():
+    # unchunked: one fused launch; the workspace holds the fp32 reverse rows
+    rep = check_bidir(batch=64, seqlen=32, D=2048, res="x", chunk=0)
+    assert rep.launches == 1 and rep.vector_staging == 2
+    a, _ = make_args("scan", batch=64, seqlen=32, D=2048, res="x", chunk=0)
+    assert _abi.workspace_size(_abi.R2L_OP_BIDIR, a) == 64 * 32 * 2048 * 4
+    # chunked: the reverse plan (chunk pass, carry, readout pass), then the forward one
+    rep = check_bidir(batch=2, seqlen=900, D=64, chunk=100, h_in=True, h_out=True)
+    assert rep.launches == 6
+    rep = check_bidir(batch=8, seqlen=4096, D=4096, chunk=0)
+    assert rep.launches == 6 and rep.accesses > 10**7
+    # gate closed: the residual copied, the forward state scanned when wanted
+    assert check_bidir(batch=3, seqlen=40, D=64, res="x", s=0.0).launches == 1
+    assert check_bidir(batch=3, seqlen=40, D=64, res="x", s=0.0, h_out=True).launches == 2
+    assert check_bidir(batch=3, seqlen=40, D=64, res="inplace", s=0.0).launches == 0
+
+
+def test_bidir_random_plans():
+    rng = random.Random(4321)
+    for _ in range(150):
+        kw = dict(dtype=rng.choice(["bf16", "f32"]), D=rng.choice([1, 5, 64, 100, 256, 513]),
+                  chunk=rng.choice([-1, 0, 16, 33, 64, 200]), h_in=rng.random() < 0.5,
+                  h_out=rng.random() < 0.5, pad_row=rng.choice([0, 0, 1, 8]),
+                  bc_shift=rng.choice([0, 0, 1]), res=rng.choice(["none", "x", "sep", "inplace"]),
+                  s=rng.choice([0.05, 0.05, 0.0]))
+        if rng.random() < 0.5:
+            kw["lengths"] = [rng.choice([0, 1, 2, 31, 64, 65, 130, 300]) for _ in range(rng.randint(1, 6))]
+        else:
+            kw.update(batch=rng.randint(1, 5), seqlen=rng.choice([0, 1, 8, 63, 64, 65, 257]),
+                      pad_batch=rng.choice([0, 0, 24]))
+        check_bidir(rng.choice(["shared", "separate", "partial"]), **kw)
+
+
+def test_bidir_rejects_bad_arguments():
+    a, cu = make_args("scan", batch=2, seqlen=40, D=64, res="x")
+    heap = FakeHeap()
+    heap.next = BASE + (1 << 40)
+    need = _abi.workspace_size(_abi.R2L_OP_BIDIR, a)
+    a.workspace, a.workspace_bytes = heap.alloc(need), need
+    r = make_dir(a, heap, "separate")
+    assert _abi.check_access_bidir(a, r, cu)[0] == _abi.R2L_OK
+    # the reverse dt overlapping out
+    bad = _abi.DirArgs.from_buffer_copy(r)
+    bad.dt = a.out
+    assert _abi.check_access_bidir(a, bad, cu)[0] == _abi.R2L_ERR_ALIAS
+    # too little workspace
+    a.workspace_bytes = need - 4
+    assert _abi.check_access_bidir(a, r, cu)[0] == _abi.R2L_ERR_WORKSPACE
+    a.workspace_bytes = need
+    # the workspace overlapping the reverse Bm
+    bad = _abi.DirArgs.from_buffer_copy(r)
+    bad.Bm = a.workspace
+    assert _abi.check_access_bidir(a, bad, cu)[0] == _abi.R2L_ERR_ALIAS
+    # several lanes per channel are not built for it
+    a.state_split = 2
+    assert _abi.check_access_bidir(a, r, cu)[0] == _abi.R2L_ERR_UNSUPPORTED
