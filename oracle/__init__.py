@@ -24,6 +24,9 @@ Function map (each a thin wrapper over the one C routine):
 * ``bidir_scan``          -- forward plus reverse scan of the same x, each with
                              its own parameters, readouts added (the full-window
                              bidirectional scan of the earlier hybrids).
+* ``sidecar_forward``     -- the sidecar block around the reverse scan (a reading:
+                             the Mamba block's projections, conv and gate; numpy
+                             matmuls plus the C scan).
 * ``selective_scan_backward`` -- the gradients of the scan with readout and
                              residual (training the R2L stream).
 """
@@ -264,6 +267,78 @@ def bidir_scan(x, dt, Bm, Cm, A, Dskip=None, *, rev=None, res=None, s: float = 0
     if rc != 0:
         raise ValueError("oracle bidirectional scan rejected its arguments (rc=%d)" % rc)
     return {"y": y, "out": out, "h_out": h_out}
+
+
+def _round_to(a, store):
+    """The value of fp64 array ``a`` once stored as ``store`` ("f32": IEEE
+    single; "bf16": the upper 16 bits of the single after round-to-nearest-even;
+    None: kept in fp64)."""
+    if store is None:
+        return a
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    if store == "f32":
+        return f.astype(np.float64)
+    u = f.view(np.uint32).astype(np.uint64)
+    keep = (u >> 16) & 1                           # ties go to the even upper half
+    u = ((u + 0x7FFF + keep) >> 16) << 16
+    out = (u & 0xFFFFFFFF).astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.float64("nan"), out)
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def sidecar_forward(hidden, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, W_out, *,
+                    s: float, seq_offsets=None, batch=None, seqlen=None, store=None,
+                    nthreads: int = 0, timing: dict | None = None):
+    """The R2L sidecar block around the reverse scan, one plain reading of a
+    Mamba block run over the reversed sequence (the pages name a Mamba sidecar
+    and give none of its internals):
+
+        [x | z] = hidden W_in^T                       (d_model -> 2 d_inner)
+        u_t     = SiLU(conv_b + sum_j conv_w[:, K-1-j] * x_{t+j})   (the causal
+                  depthwise conv of the reversed sequence: taps look right,
+                  zero past each sequence's last token)
+        [r | B | C] = u W_x^T                          (d_inner -> R + 2N)
+        dt      = r W_dt^T + dt_bias                   (Delta = softplus(dt) in the scan)
+        y       = reverse selective scan of u (dt, B, C, A, Dskip)
+        g       = y * SiLU(z)
+        out     = hidden + s * g W_out^T               (s == 0: hidden itself)
+
+    All arrays are fp64 [rows, cols] with the weights as [out, in]. ``store``
+    ("bf16", "f32" or None) rounds every intermediate the GPU path stores
+    (x|z, u, r|B|C, r W_dt^T, g) to that type, as the GPU does; the sums
+    themselves are fp64. Returns a dict with ``out`` and the intermediates."""
+    hidden, W_in, W_x, W_dt, W_out = (_f64(a) for a in (hidden, W_in, W_x, W_dt, W_out))
+    conv_w, conv_b, dt_bias, A, Dskip = (_f64(a) for a in (conv_w, conv_b, dt_bias, A, Dskip))
+    T, dm = hidden.shape
+    di, N, K = W_dt.shape[0], A.shape[1], conv_w.shape[1]
+    R = W_dt.shape[1]
+    off = _offsets(seq_offsets, batch, seqlen, T)
+    t0 = time.perf_counter()
+    xz = _round_to(hidden @ W_in.T, store)
+    x, z = xz[:, :di], xz[:, di:]
+    pre = np.empty((T, di))
+    for b in range(off.shape[0] - 1):
+        for t in range(off[b], off[b + 1]):
+            acc = conv_b.copy()
+            for j in range(K):
+                if t + j < off[b + 1]:
+                    acc = acc + conv_w[:, K - 1 - j] * x[t + j]
+            pre[t] = acc
+    u = _round_to(_silu(pre), store)
+    xdbl = _round_to(u @ W_x.T, store)
+    dt = _round_to(xdbl[:, :R] @ W_dt.T, store) + dt_bias[None, :]
+    Bm, Cm = xdbl[:, R:R + N], xdbl[:, R + N:R + 2 * N]
+    y = selective_scan(u, dt, Bm, Cm, A, Dskip, reverse=True, seq_offsets=off,
+                       nthreads=nthreads)["y"]
+    g = _round_to(y * _silu(z), store)
+    o = g @ W_out.T
+    out = hidden.copy() if s == 0.0 else hidden + s * o
+    if timing is not None:
+        timing["seconds"] = time.perf_counter() - t0
+    return {"out": out, "xz": xz, "u": u, "xdbl": xdbl, "dt": dt, "y": y, "g": g, "o": o}
 
 
 def r2l_scan(x, dt, Bm, Cm, A, Dskip=None, *, res=None, s=0.0, **kw):

@@ -13,6 +13,7 @@ import pytest
 import oracle
 from oracle_bidir_pins import BIDIR_PINS
 from oracle_bwd_pins import BWD_PINS
+from oracle_sidecar_pins import SIDECAR_PINS
 from oracle_pins import PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "selective_scan_ref.c")
@@ -181,3 +182,44 @@ def test_some_bidir_pin_catches_mutant(workdir, name):
         except (AssertionError, ValueError, FloatingPointError):
             return
     pytest.fail("no bidirectional pin catches the planted mistake %r" % name)
+
+
+# Mistakes in the sidecar block (Python: a patched copy of oracle/__init__.py
+# is executed as its own module, sharing the committed C build).
+SIDECAR_MUTANTS = {
+    "sidecar_taps_reversed": ("acc = acc + conv_w[:, K - 1 - j] * x[t + j]",
+                              "acc = acc + conv_w[:, j] * x[t + j]"),
+    "sidecar_conv_looks_left": ("""                if t + j < off[b + 1]:
+                    acc = acc + conv_w[:, K - 1 - j] * x[t + j]""",
+                                """                if t - j >= off[b]:
+                    acc = acc + conv_w[:, K - 1 - j] * x[t - j]"""),
+    "sidecar_no_conv_silu": ("u = _round_to(_silu(pre), store)", "u = _round_to(pre, store)"),
+    "sidecar_gate_with_x": ("g = _round_to(y * _silu(z), store)", "g = _round_to(y * _silu(x), store)"),
+    "sidecar_halves_swapped": ("x, z = xz[:, :di], xz[:, di:]", "z, x = xz[:, :di], xz[:, di:]"),
+    "sidecar_no_dt_bias": ("_round_to(xdbl[:, :R] @ W_dt.T, store) + dt_bias[None, :]",
+                           "_round_to(xdbl[:, :R] @ W_dt.T, store)"),
+    "sidecar_B_C_swapped": ("Bm, Cm = xdbl[:, R:R + N], xdbl[:, R + N:R + 2 * N]",
+                            "Cm, Bm = xdbl[:, R:R + N], xdbl[:, R + N:R + 2 * N]"),
+    "sidecar_forward_scan": ("y = selective_scan(u, dt, Bm, Cm, A, Dskip, reverse=True,",
+                             "y = selective_scan(u, dt, Bm, Cm, A, Dskip, reverse=False,"),
+    "sidecar_ungated": ("hidden + s * o", "hidden + o"),
+    "sidecar_conv_without_bias": ("acc = conv_b.copy()", "acc = 0.0 * conv_b"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SIDECAR_MUTANTS))
+def test_some_sidecar_pin_catches_mutant(name):
+    import types
+    old, new = SIDECAR_MUTANTS[name]
+    path = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+    text = open(path).read()
+    assert text.count(old) == 1, "mutation anchor not found: %s" % name
+    mod = types.ModuleType("oracle_mutant_" + name)
+    mod.__file__ = path
+    exec(compile(text.replace(old, new), path, "exec"), mod.__dict__)
+    for pin in SIDECAR_PINS:
+        try:
+            pin(mod.sidecar_forward)
+        except (AssertionError, ValueError, FloatingPointError):
+            return
+    pytest.fail("no sidecar pin catches the planted mistake %r" % name)

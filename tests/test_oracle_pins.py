@@ -5,6 +5,7 @@ import pytest
 import oracle
 from oracle_bidir_pins import BIDIR_PINS
 from oracle_bwd_pins import BWD_PINS
+from oracle_sidecar_pins import SIDECAR_PINS
 from oracle_pins import PINS
 
 
@@ -16,6 +17,11 @@ def test_pin(pin):
 @pytest.mark.parametrize("pin", BIDIR_PINS, ids=[p.__name__ for p in BIDIR_PINS])
 def test_bidir_pin(pin):
     pin(oracle.bidir_scan)
+
+
+@pytest.mark.parametrize("pin", SIDECAR_PINS, ids=[p.__name__ for p in SIDECAR_PINS])
+def test_sidecar_pin(pin):
+    pin(oracle.sidecar_forward)
 
 
 @pytest.mark.parametrize("pin", BWD_PINS, ids=[p.__name__ for p in BWD_PINS])
