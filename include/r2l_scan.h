@@ -308,6 +308,73 @@ typedef struct r2l_dir_args {
 
 R2L_API r2l_status bidir_scan(const r2l_scan_args *a, const r2l_dir_args *rev, void *stream);
 
+/*
+ * r2l_sidecar_forward -- the sidecar block around the R2L scan, as a hook:
+ * out = hidden + s * sidecar(hidden). The pages name a Mamba SSM sidecar run
+ * over the reversed sequence ("Bifocal Diffusion Language Models", section 2)
+ * and give none of its internals; this is the plain Mamba block, whose
+ * left-to-right form run on the reversed sequence reads, in the original
+ * order (per sequence; weights stored [out, in] as in a linear layer):
+ *     [x | z] = hidden W_in^T                        (d_model -> 2 d_inner)
+ *     u_t     = SiLU(conv_b + sum_{j<K} conv_w[:, K-1-j] * x_{t+j})
+ *               (the causal depthwise conv of the reversed sequence; zero
+ *               past each sequence's last token)
+ *     [r | B | C] = u W_x^T                          (d_inner -> dt_rank + 2 N)
+ *     y       = the R2L scan of u with dt = r W_dt^T + dt_bias (softplus
+ *               applied), B, C, A, Dskip, from a zero state
+ *     out     = hidden + s * (y * SiLU(z)) W_out^T
+ * With s == 0, out is hidden bit for bit and nothing else runs.
+ *
+ * Storage: hidden, out and W_in, W_x, W_dt, W_out in `dtype`; conv_w [d_inner,
+ * d_conv], conv_b [d_inner], dt_bias [d_inner], A [d_inner, dstate] and
+ * Dskip [d_inner] fp32 (conv_b, dt_bias, Dskip may be NULL: zero). Every
+ * intermediate (x|z, u, r|B|C, r W_dt^T, the gated y) is stored in `dtype` in
+ * the workspace, as a model in that dtype stores its activations; the GEMMs
+ * and the scan accumulate in fp32. Tokens are packed rows of hidden and out
+ * (row stride in elements, >= d_model): dense sequence b owns rows
+ * b*seqlen .. (b+1)*seqlen-1, ragged ones follow cu_seqlens. Weights are
+ * contiguous. out may be exactly hidden; any other overlap is R2L_ERR_ALIAS.
+ * d_conv is 1..4, dstate 16; d_model, d_inner and dt_rank are multiples of 8
+ * and the rows of hidden and out start on 16-byte boundaries (the GEMMs'
+ * operands). The four projections run as
+ * hipBLASLt GEMMs: the library keeps one hipBLASLt handle per device and one
+ * algorithm per GEMM shape (host memory) for the life of the process; their
+ * scratch is part of the workspace (r2l_sidecar_workspace_size).
+ */
+typedef struct r2l_sidecar_args {
+    int64_t batch;
+    int64_t seqlen;             /* dense */
+    const int32_t *cu_seqlens;  /* ragged, device [batch+1], or NULL */
+    int64_t total_tokens;       /* ragged */
+    int64_t max_seqlen;         /* ragged */
+    int64_t d_model;
+    int64_t d_inner;
+    int32_t dstate;
+    int32_t dt_rank;
+    int32_t d_conv;
+    int32_t dtype;              /* R2L_DTYPE_* */
+    const void *hidden; int64_t hidden_stride;
+    const void *W_in;           /* [2 d_inner, d_model] */
+    const float *conv_w;        /* [d_inner, d_conv] */
+    const float *conv_b;        /* [d_inner] or NULL */
+    const void *W_x;            /* [dt_rank + 2 dstate, d_inner] */
+    const void *W_dt;           /* [d_inner, dt_rank] */
+    const float *dt_bias;       /* [d_inner] or NULL */
+    const float *A;             /* [d_inner, dstate] */
+    const float *Dskip;         /* [d_inner] or NULL */
+    const void *W_out;          /* [d_model, d_inner] */
+    float s;
+    void *out; int64_t out_stride;
+    void *workspace;            /* device, 256-byte aligned */
+    size_t workspace_bytes;
+} r2l_sidecar_args;
+
+R2L_API r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream);
+
+/* Bytes of workspace r2l_sidecar_forward needs for these arguments (shape
+ * fields and s only). */
+R2L_API r2l_status r2l_sidecar_workspace_size(const r2l_sidecar_args *a, size_t *bytes);
+
 /* Short static description of a status code. */
 R2L_API const char *r2l_status_string(r2l_status status);
 

@@ -56,6 +56,15 @@ R2L_API r2l_status r2l_check_access_bidir(const r2l_scan_args *a, const r2l_dir_
                                           const int32_t *cu_seqlens_host,
                                           r2l_access_report *report);
 
+/*
+ * r2l_check_access_sidecar -- the same replay for r2l_sidecar_forward: every
+ * access of its own kernels (conv, scan, residual copy) and, for each library
+ * GEMM, that every matrix it is given lies inside its buffer.
+ */
+R2L_API r2l_status r2l_check_access_sidecar(const r2l_sidecar_args *a,
+                                            const int32_t *cu_seqlens_host,
+                                            r2l_access_report *report);
+
 typedef struct r2l_plan_info {
     int32_t lanes_per_channel; /* 1, 2 or 4 */
     int32_t chunked;           /* 1: chunk pass + carry (+ readout pass) */

@@ -315,6 +315,8 @@ def sidecar_forward(hidden, W_in, conv_w, conv_b, W_x, W_dt, dt_bias, A, Dskip, 
     T, dm = hidden.shape
     di, N, K = W_dt.shape[0], A.shape[1], conv_w.shape[1]
     R = W_dt.shape[1]
+    conv_b = np.zeros(di) if conv_b is None else conv_b      # absent terms are zero
+    dt_bias = np.zeros(di) if dt_bias is None else dt_bias
     off = _offsets(seq_offsets, batch, seqlen, T)
     t0 = time.perf_counter()
     xz = _round_to(hidden @ W_in.T, store)

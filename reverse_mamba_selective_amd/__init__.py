@@ -22,7 +22,8 @@ import torch
 from . import _abi
 from ._abi import R2LError  # noqa: F401
 
-__all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "bidir_scan",
+__all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "bidir_scan", "sidecar_forward",
+           "bind_sidecar", "SIDECAR_WEIGHTS",
            "workspace_size", "bind",
            "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "prefix_scan_backward",
            "bind_backward",
@@ -334,6 +335,116 @@ def bidir_scan(x, dt, Bm, Cm, A, Dskip=None, *, rev=None, cu_seqlens=None, max_s
         stream = torch.cuda.current_stream(x.device).cuda_stream
     _abi.call_bidir(a, r, stream)
     return out
+
+
+# ---- sidecar block --------------------------------------------------------------
+SIDECAR_WEIGHTS = ("W_in", "conv_w", "conv_b", "W_x", "W_dt", "dt_bias", "A", "Dskip", "W_out")
+
+
+def _fill_sidecar(hidden, w, s, cu_seqlens, max_seqlen, out):
+    if hidden.dtype not in _DTYPES:
+        raise ValueError("hidden must be float32 or bfloat16, got %s" % hidden.dtype)
+    unknown = set(w) - set(SIDECAR_WEIGHTS)
+    if unknown:
+        raise ValueError("unknown sidecar weights %s" % sorted(unknown))
+    for k in ("W_in", "conv_w", "W_x", "W_dt", "A", "W_out"):
+        if w.get(k) is None:
+            raise ValueError("the sidecar needs %s" % k)
+    dm = int(hidden.shape[-1])
+    di, N = int(w["A"].shape[0]), int(w["A"].shape[1])
+    R, K = int(w["W_dt"].shape[1]), int(w["conv_w"].shape[1])
+    a = _abi.SidecarArgs()
+    if cu_seqlens is not None:
+        if hidden.dim() != 2:
+            raise ValueError("ragged layout takes [tokens, d_model] tensors")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        a.batch = int(cu_seqlens.shape[0]) - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if a.batch > 0 else 0
+        a.cu_seqlens, a.total_tokens, a.max_seqlen = cu_seqlens.data_ptr(), int(hidden.shape[0]), \
+            int(max_seqlen)
+    elif hidden.dim() == 3:
+        a.batch, a.seqlen = int(hidden.shape[0]), int(hidden.shape[1])
+    else:
+        a.batch, a.seqlen = 1, int(hidden.shape[0])
+    a.d_model, a.d_inner, a.dstate, a.dt_rank, a.d_conv = dm, di, N, R, K
+    a.dtype = _DTYPES[hidden.dtype]
+    for t, n in ((hidden, "hidden"), (out, "out")):
+        if t.dtype != hidden.dtype or tuple(t.shape) != tuple(hidden.shape):
+            raise ValueError("%s must match hidden in shape and dtype" % n)
+        if t.dim() == 3 and t.shape[0] > 1 and t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError("%s: the sequences' rows must be evenly strided" % n)
+    a.hidden, a.hidden_stride = _rows(hidden, dm, "hidden")[:2]
+    a.out, a.out_stride = _rows(out, dm, "out")[:2]
+    shapes = {"W_in": (2 * di, dm), "W_x": (R + 2 * N, di), "W_dt": (di, R), "W_out": (dm, di)}
+    for n, shape in shapes.items():
+        t = w[n]
+        if t.dtype != hidden.dtype or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s tensor of shape %s" % (n, hidden.dtype, shape))
+        setattr(a, n, t.data_ptr())
+    for n, shape in (("conv_w", (di, K)), ("conv_b", (di,)), ("dt_bias", (di,)), ("A", (di, N)),
+                     ("Dskip", (di,))):
+        _check_f32(w.get(n), shape, n)
+        setattr(a, n, _ptr(w.get(n)))
+    a.s = float(s)
+    return a
+
+
+def _sidecar_workspace(a, workspace, device):
+    need = _abi.sidecar_workspace_size(a)
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        elif workspace.numel() * workspace.element_size() < need:
+            raise ValueError("workspace has %d bytes, the sidecar needs %d"
+                             % (workspace.numel() * workspace.element_size(), need))
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    return workspace
+
+
+def sidecar_forward(hidden, weights: dict, *, s, cu_seqlens=None, max_seqlen=None, out=None,
+                    workspace=None):
+    """The R2L sidecar block as a hook: out = hidden + s * sidecar(hidden)
+    (in-projection, anti-causal depthwise conv + SiLU, x/dt projections, the
+    R2L scan, SiLU(z) gate, out-projection; see r2l_sidecar_forward).
+    ``weights``: W_in [2 di, dm], W_x [R + 2N, di], W_dt [di, R], W_out [dm, di]
+    in hidden's dtype; conv_w [di, K], conv_b [di], dt_bias [di], A [di, N],
+    Dskip [di] fp32 (conv_b, dt_bias, Dskip optional). ``out`` may be
+    ``hidden``. Returns ``out``."""
+    if out is None:
+        out = torch.empty_like(hidden)
+    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out)
+    workspace = _sidecar_workspace(a, workspace, hidden.device)
+    with torch.cuda.device(hidden.device):
+        stream = torch.cuda.current_stream(hidden.device).cuda_stream
+    _abi.call_sidecar(a, stream)
+    return out
+
+
+class BoundSidecar:
+    """One r2l_sidecar_forward call with its argument struct filled once."""
+
+    def __init__(self, args, keep, workspace, device):
+        self.args, self._keep, self.workspace, self.device = args, keep, workspace, device
+        self._fn = _abi.load().r2l_sidecar_forward
+        self._ref = _abi.ctypes.byref(args)
+
+    def launch(self, stream=None):
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        st = self._fn(self._ref, _abi._vp(stream))
+        if st != _abi.R2L_OK:
+            raise R2LError(st, "r2l_sidecar_forward", _abi.last_error())
+
+
+def bind_sidecar(hidden, weights: dict, *, s, out, cu_seqlens=None, max_seqlen=None,
+                 workspace=None) -> BoundSidecar:
+    """Check and marshal a ``sidecar_forward`` call once (``out`` required)."""
+    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out)
+    workspace = _sidecar_workspace(a, workspace, hidden.device)
+    keep = [hidden, out, cu_seqlens] + [v for v in weights.values() if v is not None]
+    return BoundSidecar(a, keep, workspace, hidden.device)
 
 
 # ---- backward ---------------------------------------------------------------

@@ -33,7 +33,8 @@ EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
            "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
            "r2l_check_access_backward", "prefix_scan_backward", "bidir_scan",
-           "r2l_check_access_bidir")
+           "r2l_check_access_bidir", "r2l_sidecar_forward", "r2l_sidecar_workspace_size",
+           "r2l_check_access_sidecar")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -77,6 +78,19 @@ class DirArgs(ctypes.Structure):
         ("Bm", _vp), ("Bm_stride", _i64), ("Bm_batch_stride", _i64),
         ("Cm", _vp), ("Cm_stride", _i64), ("Cm_batch_stride", _i64),
         ("A", _vp), ("Dskip", _vp),
+    ]
+
+
+class SidecarArgs(ctypes.Structure):
+    """Mirror of ``r2l_sidecar_args``."""
+    _fields_ = [
+        ("batch", _i64), ("seqlen", _i64), ("cu_seqlens", _vp), ("total_tokens", _i64),
+        ("max_seqlen", _i64), ("d_model", _i64), ("d_inner", _i64), ("dstate", _i32),
+        ("dt_rank", _i32), ("d_conv", _i32), ("dtype", _i32),
+        ("hidden", _vp), ("hidden_stride", _i64), ("W_in", _vp), ("conv_w", _vp), ("conv_b", _vp),
+        ("W_x", _vp), ("W_dt", _vp), ("dt_bias", _vp), ("A", _vp), ("Dskip", _vp), ("W_out", _vp),
+        ("s", ctypes.c_float), ("out", _vp), ("out_stride", _i64),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -143,6 +157,13 @@ def load(path: str = LIB_PATH):
     lib.r2l_check_access_bidir.restype = _i32
     lib.r2l_check_access_bidir.argtypes = [ptr, dptr, ctypes.POINTER(_i32),
                                            ctypes.POINTER(AccessReport)]
+    sptr = ctypes.POINTER(SidecarArgs)
+    lib.r2l_sidecar_forward.restype = _i32
+    lib.r2l_sidecar_forward.argtypes = [sptr, _vp]
+    lib.r2l_sidecar_workspace_size.restype = _i32
+    lib.r2l_sidecar_workspace_size.argtypes = [sptr, ctypes.POINTER(ctypes.c_size_t)]
+    lib.r2l_check_access_sidecar.restype = _i32
+    lib.r2l_check_access_sidecar.argtypes = [sptr, ctypes.POINTER(_i32), ctypes.POINTER(AccessReport)]
     if lib.r2l_abi_version() != ABI_VERSION:
         raise ImportError("libr2l_scan.so ABI %d, binding expects %d"
                           % (lib.r2l_abi_version(), ABI_VERSION))
@@ -238,6 +259,32 @@ def check_access_bidir(args: ScanArgs, rev: DirArgs | None, cu_seqlens_host=None
         arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
         cu = ctypes.cast(arr, ctypes.POINTER(_i32))
     st = lib.r2l_check_access_bidir(ctypes.byref(args), _dir_ref(rev), cu, ctypes.byref(rep))
+    return st, rep
+
+
+def sidecar_workspace_size(args: SidecarArgs) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().r2l_sidecar_workspace_size(ctypes.byref(args), ctypes.byref(n))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_sidecar_workspace_size", last_error())
+    return int(n.value)
+
+
+def call_sidecar(args: SidecarArgs, stream: int | None) -> None:
+    st = load().r2l_sidecar_forward(ctypes.byref(args), _vp(stream or 0))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_sidecar_forward", last_error())
+
+
+def check_access_sidecar(args: SidecarArgs, cu_seqlens_host=None):
+    """Host replay of r2l_sidecar_forward's accesses; (status, report)."""
+    lib = load()
+    rep = AccessReport()
+    cu = None
+    if cu_seqlens_host is not None:
+        arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
+        cu = ctypes.cast(arr, ctypes.POINTER(_i32))
+    st = lib.r2l_check_access_sidecar(ctypes.byref(args), cu, ctypes.byref(rep))
     return st, rep
 
 

@@ -104,7 +104,9 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const Region *rSd = p.sdelta ? ck.region_of(p.sdelta) : nullptr;
     const Region *rX = ck.region_of(p.x), *rD = ck.region_of(p.dt), *rB = ck.region_of(p.Bm);
     const Region *rC = launch_readout ? ck.region_of(p.Cm) : nullptr;
-    const Region *rR = (l.mode & kModeOutMask) == kModeRes ? ck.region_of(p.res) : nullptr;
+    const bool reads_res = (l.mode & kModeOutMask) == kModeRes || (l.mode & kModeOutMask) == kModeGate;
+    const Region *rR = reads_res ? ck.region_of(p.res) : nullptr;
+    const Region *rBias = (l.mode & kModeBias) && p.dt_bias ? ck.region_of(p.dt_bias) : nullptr;
     const Region *rO = launch_readout && !to_ws ? ck.region_of(p.out) : nullptr;
     const Region *rW = to_ws ? ck.region_of(p.yws) : nullptr;
     const Region *rAdd = (l.mode & kModeAdd) ? ck.region_of(p.yadd) : nullptr;
@@ -138,6 +140,7 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
                 ck.read_written("h_in", U(hin) + st * 4, NS * 4);
             }
             if (readout && p.Dskip) ck.access("Dskip", rDs, U(p.Dskip) + lg.d * 4, 4);
+            if (rBias) ck.access("dt_bias", rBias, U(p.dt_bias) + lg.d * 4, 4);
             if (p.hfin && lg.active) {
                 const uintptr_t a = U(p.hfin) + (bg.b * p.hfin_b + bg.c * p.hfin_c + st) * 4;
                 ck.access("h_final", rHfin, a, NS * 4);
@@ -194,7 +197,14 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
         auto load_pos = [&](int k) {
             row_access("x", rX, p.x, sq.xo, p.xs, k);
             row_access("dt", rD, p.dt, sq.dto, p.dts, k);
-            if ((mode & kModeOutMask) == kModeRes) row_access("res", rR, p.res, sq.ro, p.rs, k);
+            const int64_t rw = seg_row(sg, k);
+            ck.read_written("x", U(p.x) + (sq.xo + rw * p.xs + dmin) * es, es);
+            ck.read_written("dt", U(p.dt) + (sq.dto + rw * p.dts + dmin) * es, es);
+            if ((mode & kModeOutMask) == kModeRes || (mode & kModeOutMask) == kModeGate) {
+                row_access("res", rR, p.res, sq.ro, p.rs, k);
+                ck.read_written("res", U(p.res) + (sq.ro + static_cast<int64_t>(seg_row(sg, k)) * p.rs) * es
+                                       + static_cast<uint64_t>(dmin) * es, es);
+            }
             if (mode & kModeAdd) ws_row("reverse readout rows", rAdd, p.yadd, k, false);
         };
         const int ntok = sg.ntok;
@@ -216,8 +226,11 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
             load_pos(prefetch_pos(k + kPrefetch, ntok));
             if (readout && to_ws)
                 ws_row("readout rows", rW, p.yws, k, true);
-            else if (readout)
+            else if (readout) {
                 row_access("out", rO, p.out, sq.oo, p.os, k);
+                const uint64_t o0 = U(p.out) + (sq.oo + static_cast<int64_t>(seg_row(sg, k)) * p.os) * es;
+                ck.wrote(o0 + static_cast<uint64_t>(dmin) * es, (dmax - dmin + 1) * es);
+            }
         }
 
         // Bm/Cm staging, tile by tile: per thread one run of STAGE elements
@@ -559,6 +572,134 @@ r2l_status check_bidir_accesses(const r2l_scan_args *a, const r2l_dir_args *rev,
             check_carry(ck, l, cu_host);
         } else {
             ck.fail("unexpected launch kind in a bidirectional plan");
+        }
+    }
+    return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;
+}
+
+namespace {
+
+void check_conv(Checker &ck, const Launch &l, const int32_t *cu_host) {
+    const ConvParams &p = l.conv;
+    const int64_t es = l.dtype == R2L_DTYPE_BF16 ? 2 : 4;
+    const Region *rx = ck.region_of(p.x), *ru = ck.region_of(p.u), *rw = ck.region_of(p.w);
+    const Region *rb = p.b ? ck.region_of(p.b) : nullptr;
+    if (p.K < 1 || p.K > kConvMaxTaps) return ck.fail("conv: %d taps", p.K);
+    for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
+        const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, bid);
+        if (!bg.valid) continue;
+        const int64_t s0 = p.cu_seqlens ? cu_host[bg.b] : bg.b * p.seqlen;
+        const int64_t len = p.cu_seqlens ? cu_host[bg.b + 1] - cu_host[bg.b] : p.seqlen;
+        if (p.cu_seqlens) ck.access("cu_seqlens", ck.region_of(p.cu_seqlens), U(p.cu_seqlens) + bg.b * 4, 8);
+        const int64_t lo = static_cast<int64_t>(bg.c) * kConvTokens;
+        if (lo >= len) continue;
+        const int64_t hi = lo + kConvTokens < len ? lo + kConvTokens : len;
+        const int64_t d0 = static_cast<int64_t>(bg.tile) * kWG;
+        const int64_t d1 = (d0 + kWG < p.D ? d0 + kWG : p.D) - 1;   // last active channel
+        if (d0 > d1) continue;
+        for (int64_t d : {d0, d1}) {
+            ck.access("conv_w", rw, U(p.w) + d * p.K * 4, p.K * 4);
+            if (rb) ck.access("conv_b", rb, U(p.b) + d * 4, 4);
+        }
+        // loads: rows lo .. min(hi + K - 1, len) - 1 (the window's start-up and its steps)
+        const int64_t last = hi - 1 + p.K - 1 < len ? hi - 1 + p.K - 1 : len - 1;
+        for (int64_t t = lo; t <= last && ck.ok(); ++t)
+            for (int64_t d : {d0, d1}) {
+                const uintptr_t addr = U(p.x) + ((s0 + t) * p.xs + d) * es;
+                ck.access("conv x", rx, addr, es);
+                ck.read_written("conv x", addr, es);
+            }
+        for (int64_t t = lo; t < hi && ck.ok(); ++t) {
+            const uintptr_t a0 = U(p.u) + ((s0 + t) * p.us + d0) * es;
+            ck.access("conv u", ru, a0, es);
+            ck.access("conv u", ru, a0 + (d1 - d0) * es, es);
+            ck.wrote(a0, (d1 - d0 + 1) * es);
+        }
+    }
+}
+
+// A library GEMM: every matrix it is given lies inside its buffer, and its
+// inputs that live in the workspace were written before.
+void check_gemm(Checker &ck, const Launch &l) {
+    const GemmParams &g = l.gemm;
+    const int64_t es = l.dtype == R2L_DTYPE_BF16 ? 2 : 4;
+    auto mat = [&](const char *what, const void *p, int64_t rows, int64_t cols, int64_t ld, bool write) {
+        if (ld < cols) return ck.fail("%s: leading dimension %lld < %lld", what, (long long)ld, (long long)cols);
+        const uint64_t bytes = static_cast<uint64_t>((rows - 1) * ld + cols) * es;
+        ck.access(what, ck.region_of(p), U(p), bytes);
+        for (int64_t r = 0; r < rows && ck.ok(); ++r) {
+            const uintptr_t a0 = U(p) + static_cast<uint64_t>(r * ld) * es;
+            if (write)
+                ck.wrote(a0, cols * es);
+            else
+                ck.read_written(what, a0, cols * es);
+        }
+    };
+    if (g.M <= 0 || g.N <= 0 || g.K <= 0) return ck.fail("gemm: empty shape");
+    mat("gemm X", g.X, g.M, g.K, g.ldx, false);
+    mat("gemm W", g.W, g.N, g.K, g.ldw, false);
+    if (g.beta != 0.0f) mat("gemm C", g.C, g.M, g.N, g.ldc, false);
+    mat("gemm Y", g.Y, g.M, g.N, g.ldy, true);
+    if (g.ws) ck.access("gemm scratch", ck.region_of(g.ws), U(g.ws), g.ws_bytes);
+}
+
+}  // namespace
+
+r2l_status check_sidecar_accesses(const r2l_sidecar_args *a, const SidecarPlan &sp,
+                                  const int32_t *cu_host, r2l_access_report *rep) {
+    const int64_t es = a->dtype == R2L_DTYPE_BF16 ? 2 : 4, di = a->d_inner, dm = a->d_model;
+    const int64_t T = sp.tokens, N = kN, R = a->dt_rank;
+    std::vector<Region> regs;
+    auto add = [&](const char *name, const void *p, uint64_t bytes) {
+        if (p && bytes) regs.push_back({name, U(p), U(p) + bytes});
+    };
+    auto rows = [&](int64_t n, int64_t ld, int64_t cols) -> uint64_t {
+        return n > 0 ? static_cast<uint64_t>(((n - 1) * ld + cols) * es) : 0;
+    };
+    add("hidden", a->hidden, rows(T, a->hidden_stride, dm));
+    add("out", a->out, rows(T, a->out_stride, dm));
+    add("W_in", a->W_in, rows(2 * di, dm, dm));
+    add("W_x", a->W_x, rows(R + 2 * N, di, di));
+    add("W_dt", a->W_dt, rows(di, R, R));
+    add("W_out", a->W_out, rows(dm, di, di));
+    add("conv_w", a->conv_w, static_cast<uint64_t>(di * a->d_conv * 4));
+    add("conv_b", a->conv_b, static_cast<uint64_t>(di * 4));
+    add("dt_bias", a->dt_bias, static_cast<uint64_t>(di * 4));
+    add("A", a->A, static_cast<uint64_t>(di * N * 4));
+    add("Dskip", a->Dskip, static_cast<uint64_t>(di * 4));
+    add("cu_seqlens", a->cu_seqlens, static_cast<uint64_t>((a->batch + 1) * 4));
+    const char *ws = static_cast<const char *>(a->workspace);
+    if (ws && sp.runs) {
+        add("workspace x|z", ws + sp.off_xz, sp.off_u - sp.off_xz);
+        add("workspace u", ws + sp.off_u, sp.off_xdbl - sp.off_u);
+        add("workspace r|B|C", ws + sp.off_xdbl, sp.off_dt - sp.off_xdbl);
+        add("workspace dt", ws + sp.off_dt, sp.off_g - sp.off_dt);
+        add("workspace gated y", ws + sp.off_g, sp.off_chunk - sp.off_g);
+        if (sp.pl.chunked) {
+            const char *c = ws + sp.off_chunk;
+            add("workspace Q", c, sp.pl.off_S);
+            add("workspace S", c + sp.pl.off_S, sp.pl.off_H - sp.pl.off_S);
+            add("workspace H", c + sp.pl.off_H, sp.pl.ws_bytes - sp.pl.off_H);
+        }
+        add("workspace gemm scratch", ws + sp.off_gemm, sp.ws_bytes - sp.off_gemm);
+    }
+    Checker ck(std::move(regs), rep);
+    ck.set_workspace(sp.runs ? a->workspace : nullptr, sp.runs ? sp.ws_bytes : 0);
+    Launch ls[kMaxSidecarLaunches];
+    const int n = build_sidecar_launches(a, sp, ls);
+    for (int i = 0; i < n && ck.ok(); ++i) {
+        ++rep->launches;
+        const Launch &l = ls[i];
+        switch (l.kind) {
+            case Launch::Segment:
+                if (l.seg.bc_vec) ++rep->vector_staging;
+                check_segment(ck, l, cu_host);
+                break;
+            case Launch::Carry: check_carry(ck, l, cu_host); break;
+            case Launch::Copy: check_copy(ck, l); break;
+            case Launch::Conv: check_conv(ck, l, cu_host); break;
+            case Launch::Gemm: check_gemm(ck, l); break;
+            default: ck.fail("unexpected launch kind in a sidecar plan");
         }
     }
     return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;

@@ -19,4 +19,8 @@ r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r
 r2l_status check_bidir_accesses(const r2l_scan_args *a, const r2l_dir_args *rev, const BidirPlan &bp,
                                 const int32_t *cu_host, r2l_access_report *rep);
 
+// The same for r2l_sidecar_forward (after its checks).
+r2l_status check_sidecar_accesses(const r2l_sidecar_args *a, const SidecarPlan &sp,
+                                  const int32_t *cu_host, r2l_access_report *rep);
+
 }  // namespace r2l

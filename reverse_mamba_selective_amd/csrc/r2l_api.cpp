@@ -253,10 +253,22 @@ r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
         const char *what = "segment scan launch";
         switch (l.kind) {
             case Launch::Segment:
-                e = l.mode >= r2l::kModeWs
-                    ? r2l::launch_bidir_segment(l.reverse, l.dtype, l.mode, l.seg, stream)
-                    : r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream);
+                if (l.mode & r2l::kModeBias)
+                    e = r2l::launch_sidecar_segment(l.dtype, l.mode, l.seg, stream);
+                else if (l.mode >= r2l::kModeWs)
+                    e = r2l::launch_bidir_segment(l.reverse, l.dtype, l.mode, l.seg, stream);
+                else
+                    e = r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream);
                 break;
+            case Launch::Conv:
+                e = r2l::launch_conv(l.dtype, l.conv, stream);
+                what = "sidecar conv launch";
+                break;
+            case Launch::Gemm: {
+                const char *err = r2l::run_gemm(l.dtype, l.gemm, stream);
+                if (err) return fail(R2L_ERR_HIP, "sidecar projection: %s", err);
+                break;
+            }
             case Launch::Bidir:
                 e = r2l::launch_bidir_fused(l.dtype, l.mode & r2l::kModeOutMask, l.seg, l.seg2,
                                             stream);
@@ -373,6 +385,107 @@ r2l_status run_bidir(const r2l_scan_args *a, const r2l_dir_args *rev, hipStream_
     if (st != R2L_OK) return st;
     Launch ls[r2l::kMaxBidirLaunches];
     const int n = r2l::build_bidir_launches(a, rev, bp, ls);
+    return execute(ls, n, stream);
+}
+
+// ---- sidecar block ------------------------------------------------------------------
+r2l_status check_sidecar(const r2l_sidecar_args *a, const r2l::SidecarPlan &sp) {
+    const int64_t tok = sp.tokens, di = a->d_inner, dm = a->d_model;
+    const int64_t es = elem_size(a->dtype);
+    if (a->d_model < 1 || a->d_inner < 1) return fail(R2L_ERR_INVALID_ARG, "d_model and d_inner must be >= 1");
+    if (a->d_model % 8 || a->d_inner % 8)
+        return fail(R2L_ERR_UNSUPPORTED, "d_model and d_inner must be multiples of 8");
+    if (a->dt_rank < 1) return fail(R2L_ERR_INVALID_ARG, "dt_rank < 1");
+    if (a->dt_rank % 8) return fail(R2L_ERR_UNSUPPORTED, "dt_rank must be a multiple of 8");
+    if (a->d_conv < 1 || a->d_conv > r2l::kConvMaxTaps)
+        return fail(R2L_ERR_UNSUPPORTED, "d_conv must be 1..%d", r2l::kConvMaxTaps);
+    if (tok == 0) return R2L_OK;
+    const struct { const void *p; const char *n; bool need; } req[] = {
+        {a->hidden, "hidden", true}, {a->out, "out", true}, {a->W_in, "W_in", sp.runs},
+        {a->conv_w, "conv_w", sp.runs}, {a->W_x, "W_x", sp.runs}, {a->W_dt, "W_dt", sp.runs},
+        {a->A, "A", sp.runs}, {a->W_out, "W_out", sp.runs}};
+    for (const auto &r : req)
+        if (r.need && !r.p) return fail(R2L_ERR_INVALID_ARG, "%s is NULL", r.n);
+    if (a->hidden_stride < dm || a->out_stride < dm)
+        return fail(R2L_ERR_INVALID_ARG, "hidden or out stride < d_model");
+    // the GEMM operands: 16-byte aligned rows
+    const struct { const void *p; int64_t ld; const char *n; } al[] = {
+        {a->hidden, a->hidden_stride, "hidden"}, {a->out, a->out_stride, "out"},
+        {a->W_in, dm, "W_in"}, {a->W_x, di, "W_x"}, {a->W_dt, a->dt_rank, "W_dt"},
+        {a->W_out, di, "W_out"}};
+    for (const auto &e : al)
+        if (e.p && (!aligned(e.p, 16) || (e.ld * es) % 16))
+            return fail(R2L_ERR_MISALIGNED, "%s: rows must start on 16-byte boundaries", e.n);
+    const struct { const void *p; const char *n; } f4[] = {
+        {a->conv_w, "conv_w"}, {a->conv_b, "conv_b"}, {a->dt_bias, "dt_bias"}, {a->A, "A"},
+        {a->Dskip, "Dskip"}, {a->cu_seqlens, "cu_seqlens"}};
+    for (const auto &e : f4)
+        if (e.p && !aligned(e.p, 4)) return fail(R2L_ERR_MISALIGNED, "%s is not 4-byte aligned", e.n);
+    if (!sp.runs && !(a->out == a->hidden && a->out_stride == a->hidden_stride)) {
+        const Range h = span("hidden", a->hidden, tok, a->hidden_stride, dm, es, false);
+        const Range o = span("out", a->out, tok, a->out_stride, dm, es, true);
+        if (overlap(h, o)) return fail(R2L_ERR_ALIAS, "out overlaps hidden");
+    }
+    if (!sp.runs) return R2L_OK;
+    if (!a->workspace || a->workspace_bytes < sp.ws_bytes)
+        return fail(R2L_ERR_WORKSPACE, "the sidecar needs %zu workspace bytes, got %zu", sp.ws_bytes,
+                    a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned(a->workspace, 256)) return fail(R2L_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+    const int64_t R = a->dt_rank, N = r2l::kN;
+    std::vector<Range> rs = {
+        span("hidden", a->hidden, tok, a->hidden_stride, dm, es, false),
+        span("W_in", a->W_in, 2 * di, dm, dm, es, false),
+        span("conv_w", a->conv_w, di, a->d_conv, a->d_conv, 4, false),
+        span("conv_b", a->conv_b, 1, di, di, 4, false),
+        span("W_x", a->W_x, R + 2 * N, di, di, es, false),
+        span("W_dt", a->W_dt, di, R, R, es, false),
+        span("dt_bias", a->dt_bias, 1, di, di, 4, false),
+        span("A", a->A, di, N, N, 4, false),
+        span("Dskip", a->Dskip, 1, di, di, 4, false),
+        span("W_out", a->W_out, dm, di, di, es, false),
+        span("cu_seqlens", a->cu_seqlens, 1, a->batch + 1, a->batch + 1, 4, false),
+        span("out", a->out, tok, a->out_stride, dm, es, true),
+        span("workspace", a->workspace, 1, (int64_t)sp.ws_bytes, (int64_t)sp.ws_bytes, 1, true),
+    };
+    for (size_t i = 0; i < rs.size(); ++i)
+        for (size_t j = i + 1; j < rs.size(); ++j) {
+            if (!(rs[i].is_output || rs[j].is_output) || !overlap(rs[i], rs[j])) continue;
+            const bool out_hidden = (!strcmp(rs[i].name, "hidden") && !strcmp(rs[j].name, "out"));
+            if (out_hidden && a->out == a->hidden && a->out_stride == a->hidden_stride) continue;
+            return fail(R2L_ERR_ALIAS, "%s overlaps %s", rs[j].is_output ? rs[j].name : rs[i].name,
+                        rs[j].is_output ? rs[i].name : rs[j].name);
+        }
+    // the scan on the workspace, as r2l_scan would check it
+    const r2l_scan_args v = r2l::sidecar_scan_view(a, sp);
+    return check_buffers(Op::Scan, &v, sp.pl);
+}
+
+r2l_status prepare_sidecar(const r2l_sidecar_args *a, r2l::SidecarPlan *sp) {
+    if (!a) return fail(R2L_ERR_INVALID_ARG, "args is NULL");
+    *sp = r2l::make_sidecar_plan(a);
+    const r2l_scan_args v = r2l::sidecar_scan_view(a, *sp);
+    r2l_status st = check_shape(&v);
+    if (st != R2L_OK) return st;
+    if (a->d_model > 65535 * 16) return fail(R2L_ERR_UNSUPPORTED, "d_model above 1048560");
+    st = check_sidecar(a, *sp);
+    if (st != R2L_OK) return st;
+    const int64_t maxlen = ragged(&v) ? v.max_seqlen : v.seqlen;
+    const int64_t conv_blocks = a->batch * ((maxlen + r2l::kConvTokens - 1) / r2l::kConvTokens + 1) *
+                                ((a->d_inner + r2l::kWG - 1) / r2l::kWG);
+    if (a->batch * sp->pl.nchunks * sp->pl.tiles > INT32_MAX - 8 || conv_blocks > INT32_MAX - 8)
+        return fail(R2L_ERR_UNSUPPORTED, "grid too large");
+    return R2L_OK;
+}
+
+r2l_status run_sidecar(const r2l_sidecar_args *a, hipStream_t stream) {
+    r2l::SidecarPlan sp;
+    r2l_status st = prepare_sidecar(a, &sp);
+    if (st != R2L_OK) return st;
+    const r2l_scan_args v = r2l::sidecar_scan_view(a, sp);
+    st = check_seqlens_on_device(&v);
+    if (st != R2L_OK) return st;
+    Launch ls[r2l::kMaxSidecarLaunches];
+    const int n = r2l::build_sidecar_launches(a, sp, ls);
     return execute(ls, n, stream);
 }
 
@@ -555,6 +668,37 @@ r2l_status r2l_check_access_bidir(const r2l_scan_args *a, const r2l_dir_args *re
     st = check_host_offsets(a, cu_seqlens_host);
     if (st != R2L_OK) return st;
     st = r2l::check_bidir_accesses(a, rev, bp, cu_seqlens_host, report);
+    if (st != R2L_OK) return fail(st, "%s", report->message);
+    return ok();
+}
+
+r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream) {
+    return run_sidecar(a, static_cast<hipStream_t>(stream));
+}
+
+r2l_status r2l_sidecar_workspace_size(const r2l_sidecar_args *a, size_t *bytes) {
+    if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
+    if (!a) return fail(R2L_ERR_INVALID_ARG, "args is NULL");
+    const r2l::SidecarPlan sp = r2l::make_sidecar_plan(a);
+    const r2l_scan_args v = r2l::sidecar_scan_view(a, sp);
+    r2l_status st = check_shape(&v);
+    if (st != R2L_OK) return st;
+    *bytes = sp.ws_bytes;
+    return ok();
+}
+
+r2l_status r2l_check_access_sidecar(const r2l_sidecar_args *a, const int32_t *cu_seqlens_host,
+                                    r2l_access_report *report) {
+    if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
+    report->launches = report->accesses = report->vector_staging = 0;
+    report->message[0] = '\0';
+    r2l::SidecarPlan sp;
+    r2l_status st = prepare_sidecar(a, &sp);
+    if (st != R2L_OK) return st;
+    const r2l_scan_args v = r2l::sidecar_scan_view(a, sp);
+    st = check_host_offsets(&v, cu_seqlens_host);
+    if (st != R2L_OK) return st;
+    st = r2l::check_sidecar_accesses(a, sp, cu_seqlens_host, report);
     if (st != R2L_OK) return fail(st, "%s", report->message);
     return ok();
 }

@@ -23,6 +23,11 @@ constexpr int kModeRes = 3;
 constexpr int kModeWs = 4;
 constexpr int kModeOutMask = 7;
 constexpr int kModeAdd = 8;
+// The sidecar block's scan: out = y * SiLU(z), z read through the residual
+// slot (kModeGate); Delta = softplus(dt + dt_bias[d]) (kModeBias, also in the
+// state-only chunks of its plans).
+constexpr int kModeGate = 5;
+constexpr int kModeBias = 16;
 
 // One launch of the segment kernel scans "segments": chunk c (in visiting
 // order) of sequence b, for a tile of kWG lanes. With G lanes per channel a
@@ -71,6 +76,42 @@ struct SegParams {
     // first pass (kModeWs) and added by the second (kModeAdd)
     float *yws;
     const float *yadd;
+
+    // sidecar block (kModeBias): added to dt before softplus, [D]
+    const float *dt_bias;
+};
+
+// The sidecar's depthwise conv + SiLU over the x half of the in-projection:
+// u[t,d] = SiLU(b[d] + sum_{j<K} w[d, K-1-j] * x[t+j, d]) within each
+// sequence. One workgroup per (sequence, chunk of kConvTokens, tile of kWG
+// channels).
+constexpr int kConvTokens = 64;
+constexpr int kConvMaxTaps = 4;
+struct ConvParams {
+    int64_t seqlen;              // dense tokens per sequence (cu_seqlens == nullptr)
+    const int32_t *cu_seqlens;
+    int64_t D;
+    int32_t K;
+    int32_t nchunks;             // ceil(longest sequence / kConvTokens)
+    int32_t tiles;
+    int64_t nblocks;             // batch * nchunks * tiles
+    const void *x; int64_t xs;   // token rows (packed tokens)
+    const float *w;              // [D, K]
+    const float *b;              // [D] or nullptr
+    void *u; int64_t us;
+};
+
+// One library GEMM of the sidecar, row-major: Y[M, N] = alpha * X[M, K] W[N, K]^T
+// + beta * C[M, N] (C read only when beta != 0), in the storage type (fp32
+// accumulation).
+struct GemmParams {
+    int64_t M, N, K;
+    const void *X; int64_t ldx;
+    const void *W; int64_t ldw;
+    const void *C; int64_t ldc;
+    void *Y; int64_t ldy;
+    float alpha, beta;
+    void *ws; size_t ws_bytes;   // the library's scratch, inside the caller's workspace
 };
 
 // ---- backward (gradients of a scan with readout) ----------------------------
@@ -169,6 +210,12 @@ hipError_t launch_bidir_fused(int dtype, int out_mode, const SegParams &pr, cons
 hipError_t launch_bidir_segment(bool reverse, int dtype, int mode, const SegParams &p,
                                 hipStream_t stream);
 hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream);
+// sidecar: the conv + SiLU, and a segment launch of its scan (modes
+// kModeGate | kModeBias, or kModeState | kModeBias)
+hipError_t launch_conv(int dtype, const ConvParams &p, hipStream_t stream);
+hipError_t launch_sidecar_segment(int dtype, int mode, const SegParams &p, hipStream_t stream);
+// a GEMM through hipBLASLt; returns a description of a failure, or nullptr
+const char *run_gemm(int dtype, const GemmParams &p, hipStream_t stream);
 // G in {2, 4}
 hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, hipStream_t stream);
 hipError_t launch_sums(const SumBatch &p, hipStream_t stream);

@@ -328,6 +328,135 @@ int build_bidir_launches(const r2l_scan_args *a, const r2l_dir_args *rev, const 
     return n + m;
 }
 
+// ---- sidecar block -----------------------------------------------------------------
+SidecarPlan make_sidecar_plan(const r2l_sidecar_args *a) {
+    SidecarPlan sp;
+    sp.tokens = a->cu_seqlens ? a->total_tokens : a->batch * a->seqlen;
+    sp.runs = a->s != 0.0f;
+    if (!sp.runs) return sp;
+    const size_t T = static_cast<size_t>(sp.tokens), di = static_cast<size_t>(a->d_inner);
+    const size_t es = a->dtype == R2L_DTYPE_BF16 ? 2 : 4;
+    sp.ldx = ((a->dt_rank + 2 * kN) + 7) / 8 * 8;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    sp.off_xz = take(T * 2 * di * es);
+    sp.off_u = take(T * di * es);
+    sp.off_xdbl = take(T * static_cast<size_t>(sp.ldx) * es);
+    sp.off_dt = take(T * di * es);
+    sp.off_g = take(T * di * es);
+    sp.off_chunk = off;
+    sp.ws_bytes = off;   // for the view below
+    const r2l_scan_args v = sidecar_scan_view(a, sp);
+    sp.pl = make_plan(Op::Scan, &v);
+    sp.off_chunk = take(sp.pl.ws_bytes);
+    sp.off_gemm = take(kGemmWorkspace);
+    sp.ws_bytes = off;
+    return sp;
+}
+
+r2l_scan_args sidecar_scan_view(const r2l_sidecar_args *a, const SidecarPlan &sp) {
+    r2l_scan_args v{};
+    v.batch = a->batch;
+    v.seqlen = a->seqlen;
+    v.cu_seqlens = a->cu_seqlens;
+    v.total_tokens = a->total_tokens;
+    v.max_seqlen = a->max_seqlen;
+    v.dim = a->d_inner;
+    v.dstate = a->dstate;
+    v.dtype = a->dtype;
+    const int64_t es = a->dtype == R2L_DTYPE_BF16 ? 2 : 4, di = a->d_inner;
+    char *ws = static_cast<char *>(a->workspace);
+    auto at = [&](size_t off, int64_t elems) { return ws ? ws + off + elems * es : nullptr; };
+    v.x = at(sp.off_u, 0);          v.x_stride = di;
+    v.dt = at(sp.off_dt, 0);        v.dt_stride = di;
+    v.Bm = at(sp.off_xdbl, a->dt_rank);        v.Bm_stride = sp.ldx;
+    v.Cm = at(sp.off_xdbl, a->dt_rank + kN);   v.Cm_stride = sp.ldx;
+    v.A = a->A;
+    v.Dskip = a->Dskip;
+    v.delta_softplus = 1;
+    v.res = at(sp.off_xz, di);      v.res_stride = 2 * di;    // z
+    v.s = 1.0f;
+    v.out = at(sp.off_g, 0);        v.out_stride = di;
+    v.workspace = at(sp.off_chunk, 0);
+    v.workspace_bytes = sp.pl.ws_bytes;
+    return v;
+}
+
+int build_sidecar_launches(const r2l_sidecar_args *a, const SidecarPlan &sp,
+                           Launch out[kMaxSidecarLaunches]) {
+    const int64_t T = sp.tokens, di = a->d_inner, dm = a->d_model;
+    if (a->batch == 0 || T == 0) return 0;
+    if (!sp.runs) {   // s == 0: out is hidden
+        if (a->out == a->hidden && a->out_stride == a->hidden_stride) return 0;
+        Launch l{};
+        l.kind = Launch::Copy;
+        l.dtype = a->dtype;
+        l.copy.rows = T;
+        l.copy.seqlen = 0;
+        l.copy.D = dm;
+        l.copy.src = a->hidden; l.copy.ss = a->hidden_stride; l.copy.sbs = 0;
+        l.copy.dst = a->out;    l.copy.ds = a->out_stride;    l.copy.dbs = 0;
+        out[0] = l;
+        return 1;
+    }
+    char *ws = static_cast<char *>(a->workspace);
+    void *xz = ws + sp.off_xz, *u = ws + sp.off_u, *xdbl = ws + sp.off_xdbl;
+    void *dtb = ws + sp.off_dt, *g = ws + sp.off_g, *gws = ws + sp.off_gemm;
+    int n = 0;
+    auto gemm = [&](int64_t N, int64_t K, const void *X, int64_t ldx, const void *W, void *Y,
+                    int64_t ldy, const void *C, int64_t ldc, float alpha, float beta) {
+        Launch l{};
+        l.kind = Launch::Gemm;
+        l.dtype = a->dtype;
+        l.gemm = GemmParams{T, N, K, X, ldx, W, K, C, ldc, Y, ldy, alpha, beta, gws, kGemmWorkspace};
+        out[n++] = l;
+    };
+    // 1. [x | z] = hidden W_in^T
+    gemm(2 * di, dm, a->hidden, a->hidden_stride, a->W_in, xz, 2 * di, nullptr, 0, 1.0f, 0.0f);
+    // 2. u = SiLU(conv(x))
+    {
+        Launch l{};
+        l.kind = Launch::Conv;
+        l.dtype = a->dtype;
+        ConvParams &c = l.conv;
+        c.seqlen = a->cu_seqlens ? 0 : a->seqlen;
+        c.cu_seqlens = a->cu_seqlens;
+        c.D = di;
+        c.K = a->d_conv;
+        const int64_t maxlen = a->cu_seqlens ? a->max_seqlen : a->seqlen;
+        c.nchunks = static_cast<int32_t>(std::max<int64_t>((maxlen + kConvTokens - 1) / kConvTokens, 1));
+        c.tiles = static_cast<int32_t>((di + kWG - 1) / kWG);
+        c.nblocks = a->batch * c.nchunks * c.tiles;
+        c.x = xz; c.xs = 2 * di;
+        c.w = a->conv_w;
+        c.b = a->conv_b;
+        c.u = u; c.us = di;
+        out[n++] = l;
+    }
+    // 3. [r | B | C] = u W_x^T
+    gemm(a->dt_rank + 2 * kN, di, u, di, a->W_x, xdbl, sp.ldx, nullptr, 0, 1.0f, 0.0f);
+    // 4. r W_dt^T (the bias is added in the scan)
+    gemm(di, a->dt_rank, xdbl, sp.ldx, a->W_dt, dtb, di, nullptr, 0, 1.0f, 0.0f);
+    // 5. the gated R2L scan
+    const r2l_scan_args v = sidecar_scan_view(a, sp);
+    Launch ls[3];
+    const int m = build_launches(Op::Scan, &v, sp.pl, ls);
+    for (int i = 0; i < m; ++i) {
+        if (ls[i].kind == Launch::Segment) {
+            ls[i].mode = ls[i].mode == kModeState ? (kModeState | kModeBias) : (kModeGate | kModeBias);
+            ls[i].seg.dt_bias = a->dt_bias;
+        }
+        out[n++] = ls[i];
+    }
+    // 6. out = hidden + s * g W_out^T
+    gemm(dm, di, g, di, a->W_out, a->out, a->out_stride, a->hidden, a->hidden_stride, a->s, 1.0f);
+    return n;
+}
+
 // ---- backward ------------------------------------------------------------------
 BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
     BwdPlan pl;

@@ -24,7 +24,7 @@ struct Plan {
 };
 
 struct Launch {
-    enum Kind { Segment, Carry, Copy, Backward, Sum, Bidir } kind;
+    enum Kind { Segment, Carry, Copy, Backward, Sum, Bidir, Conv, Gemm } kind;
     bool reverse;
     int dtype;
     int G;
@@ -35,6 +35,8 @@ struct Launch {
     CopyParams copy;
     BwdParams bwd;
     SumBatch sums;
+    ConvParams conv;
+    GemmParams gemm;
 };
 
 // The backward of r2l_scan: phase 1 (state-only segment scan writing
@@ -107,6 +109,26 @@ BidirPlan make_bidir_plan(const r2l_scan_args *a);
 r2l_scan_args reverse_view(const r2l_scan_args *a, const r2l_dir_args *rev);
 int build_bidir_launches(const r2l_scan_args *a, const r2l_dir_args *rev, const BidirPlan &bp,
                          Launch out[kMaxBidirLaunches]);
+
+// The sidecar block (r2l_sidecar_forward): in-projection GEMM, conv + SiLU,
+// x-projection GEMM, dt-projection GEMM, the gated R2L scan (its own plan),
+// out-projection GEMM with the residual; or only the residual copy when s == 0.
+constexpr int kMaxSidecarLaunches = 8;
+constexpr size_t kGemmWorkspace = size_t(32) << 20;   // hipBLASLt scratch
+struct SidecarPlan {
+    bool runs = false;       // false: s == 0 (out = hidden)
+    Plan pl;                 // the scan's plan
+    int64_t tokens = 0;
+    int64_t ldx = 0;         // elements per [r | B | C] row (dt_rank + 2 N, rounded up to 8)
+    size_t off_xz = 0, off_u = 0, off_xdbl = 0, off_dt = 0, off_g = 0, off_chunk = 0,
+           off_gemm = 0, ws_bytes = 0;
+};
+SidecarPlan make_sidecar_plan(const r2l_sidecar_args *a);
+// The scan of the block as an r2l_scan call on the workspace: x = u, dt,
+// Bm, Cm = the columns of [r | B | C], the residual slot = z, out = the gated y.
+r2l_scan_args sidecar_scan_view(const r2l_sidecar_args *a, const SidecarPlan &sp);
+int build_sidecar_launches(const r2l_sidecar_args *a, const SidecarPlan &sp,
+                           Launch out[kMaxSidecarLaunches]);
 
 // The launches of a call, in order (at most 3). Arguments must have passed
 // the entry point's checks. Returns the count.

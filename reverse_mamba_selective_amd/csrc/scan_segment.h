@@ -34,6 +34,8 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
                                              const float *hin) {
     constexpr int OUT = MODE & kModeOutMask;     // what the readout writes
     constexpr bool ADD = (MODE & kModeAdd) != 0;  // y += an fp32 addend per token
+    constexpr bool BIAS = (MODE & kModeBias) != 0;  // dt += dt_bias[d] before softplus
+    constexpr bool READS_RES = OUT == kModeRes || OUT == kModeGate;
     constexpr bool READOUT = OUT != kModeState;
     constexpr int NS = kN / G;                   // states per lane
     constexpr int NBC = READOUT ? 2 * kN : kN;   // staged floats per token (B, then C)
@@ -81,8 +83,8 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
                               seq_span_bytes(sq.len, p.xs, p.D, es));
     const auto rd = make_rsrc(static_cast<const T *>(p.dt) + sq.dto,
                               seq_span_bytes(sq.len, p.dts, p.D, es));
-    const auto rr_ = make_rsrc(OUT == kModeRes ? static_cast<const T *>(p.res) + sq.ro : nullptr,
-                               OUT == kModeRes ? seq_span_bytes(sq.len, p.rs, p.D, es) : 0);
+    const auto rr_ = make_rsrc(READS_RES ? static_cast<const T *>(p.res) + sq.ro : nullptr,
+                               READS_RES ? seq_span_bytes(sq.len, p.rs, p.D, es) : 0);
     constexpr bool TO_OUT = READOUT && OUT != kModeWs;
     const auto ro_ = make_rsrc(TO_OUT ? static_cast<T *>(p.out) + sq.oo : nullptr,
                                TO_OUT ? seq_span_bytes(sq.len, p.os, p.D, es) : 0);
@@ -111,7 +113,7 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
         const uint32_t row = static_cast<uint32_t>(seg_row(sg, k));
         xq[slot] = E::bload(rx, doff, row * xrb);
         dq[slot] = E::bload(rd, doff, row * drb);
-        if constexpr (OUT == kModeRes) rq[slot] = E::bload(rr_, doff, row * rrb);
+        if constexpr (READS_RES) rq[slot] = E::bload(rr_, doff, row * rrb);
         if constexpr (ADD) aq[slot] = __builtin_amdgcn_raw_buffer_load_b32(ra_, woff, row * wrb, 0);
     };
 
@@ -138,8 +140,9 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     // Delta of the next visited position is computed one token ahead, off
     // the critical path of the current token (its dt is already in the ring).
     float dnext = 0.0f;
+    const float dtb = (BIAS && p.dt_bias) ? p.dt_bias[dl] : 0.0f;
     auto delta_of = [&](R dr) {
-        const float dv = E::widen(dr);
+        const float dv = BIAS ? E::widen(dr) + dtb : E::widen(dr);
         if constexpr (SP)
             return softplus(dv);
         else
@@ -183,6 +186,9 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
                 R o;
                 if constexpr (OUT == kModeY) {
                     o = E::pack(y);
+                } else if constexpr (OUT == kModeGate) {
+                    const float zv = E::widen(rr);   // y * SiLU(z) = y * z / (1 + e^-z)
+                    o = E::pack(y * zv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * kLog2e)));
                 } else {
                     const R rbits = OUT == kModeRes ? rr : xr;
                     o = E::pack(fmaf(gate, y, E::widen(rbits)));
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     const float *hin = segment_hin(p, b, c);
     if constexpr ((MODE & kModeOutMask) != kModeState) {
         if (p.split_c0 && c > 0) {
-            scan_segment<REV, T, G, kModeState, SP>(p, lds, bg, sq, sg, hin);
+            scan_segment<REV, T, G, kModeState | (MODE & kModeBias), SP>(p, lds, bg, sq, sg, hin);
             return;
         }
     }

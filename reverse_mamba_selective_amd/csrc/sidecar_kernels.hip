@@ -1,0 +1,101 @@
+// sidecar_kernels.hip -- gfx950 kernels of the sidecar block around the R2L
+// scan ("Bifocal Diffusion Language Models", section 2, names a Mamba SSM
+// sidecar run over the reversed sequence and gives none of its internals;
+// this is the plain Mamba block): the depthwise conv + SiLU, and the scan
+// instantiations with the dt bias and the SiLU(z) gate. The four projections
+// are library GEMMs (gemm.cpp).
+//
+// The conv of the reversed sequence is, in the original order, an
+// anti-causal conv: tap K-1-j weighs the token j positions to the right. A
+// lane owns one channel and walks its chunk of tokens right to left with a
+// register window of the K inputs it needs, so each x is loaded once (plus a
+// K-1 halo per chunk); a wave reads 64 consecutive channels of a token row.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_device.h"
+#include "scan_geometry.h"
+#include "scan_internal.h"
+#include "scan_segment.h"
+
+namespace r2l {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(kWG) void conv_silu_kernel(const ConvParams p) {
+    using E = Elem<T>;
+    const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
+    if (!bg.valid) return;
+    const int64_t b = bg.b;
+    int64_t s0, len;
+    if (p.cu_seqlens) {
+        s0 = p.cu_seqlens[b];
+        len = p.cu_seqlens[b + 1] - s0;
+    } else {
+        s0 = b * p.seqlen;
+        len = p.seqlen;
+    }
+    const int64_t lo = static_cast<int64_t>(bg.c) * kConvTokens;
+    if (lo >= len) return;
+    const int64_t hi = lo + kConvTokens < len ? lo + kConvTokens : len;
+    const int64_t d = static_cast<int64_t>(bg.tile) * kWG + threadIdx.x;
+    if (d >= p.D) return;
+
+    // w_eff[j] weighs x[t + j]; taps past K are zero
+    float w[kConvMaxTaps];
+#pragma unroll
+    for (int j = 0; j < kConvMaxTaps; ++j) w[j] = j < p.K ? p.w[d * p.K + (p.K - 1 - j)] : 0.0f;
+    const float bias = p.b ? p.b[d] : 0.0f;
+    const T *x = static_cast<const T *>(p.x) + s0 * p.xs + d;
+    T *u = static_cast<T *>(p.u) + s0 * p.us + d;
+
+    float win[kConvMaxTaps];   // win[j] = x[t + j] (zero past the sequence)
+#pragma unroll
+    for (int j = 0; j < kConvMaxTaps; ++j) {
+        const int64_t t = hi - 1 + j;
+        win[j] = (j < p.K && t < len) ? E::ld(x + t * p.xs) : 0.0f;
+    }
+    for (int64_t t = hi - 1; t >= lo; --t) {
+        float acc = bias;
+#pragma unroll
+        for (int j = 0; j < kConvMaxTaps; ++j) acc = fmaf(w[j], win[j], acc);
+        // SiLU(v) = v / (1 + e^-v)
+        E::st(u + t * p.us, acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * kLog2e)));
+#pragma unroll
+        for (int j = kConvMaxTaps - 1; j > 0; --j) win[j] = win[j - 1];
+        win[0] = t > lo ? E::ld(x + (t - 1) * p.xs) : 0.0f;
+    }
+}
+
+template <typename T, int MODE>
+hipError_t seg(const SegParams &p, hipStream_t stream) {
+    hipLaunchKernelGGL((segment_scan_kernel<true, T, 1, MODE, true>), dim3(padded_grid(p.nblocks)),
+                       dim3(kWG), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t seg_m(int mode, const SegParams &p, hipStream_t stream) {
+    switch (mode) {
+        case kModeGate | kModeBias: return seg<T, kModeGate | kModeBias>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_conv(int dtype, const ConvParams &p, hipStream_t stream) {
+    if (p.nblocks <= 0) return hipSuccess;
+    const dim3 grid(static_cast<uint32_t>(padded_grid(p.nblocks)));
+    if (dtype == 1)
+        hipLaunchKernelGGL(conv_silu_kernel<uint16_t>, grid, dim3(kWG), 0, stream, p);
+    else
+        hipLaunchKernelGGL(conv_silu_kernel<float>, grid, dim3(kWG), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_sidecar_segment(int dtype, int mode, const SegParams &p, hipStream_t stream) {
+    return dtype == 1 ? seg_m<uint16_t>(mode, p, stream) : seg_m<float>(mode, p, stream);
+}
+
+}  // namespace r2l

@@ -177,7 +177,13 @@ BIDIR = Workload(105, "bidir_window_step_bf16_b64_L32_D2048_N16_7hooks",
                  "and the reverse direction each with its own dt, Bm, Cm, A, Dskip; res = x, "
                  "s ~ U(0, 0.1) per hook")
 
-WORKLOADS = {w.name: w for w in (TINY, BLOCK, DENOISE, PREFILL, RAGGED, BIDIR)}
+SIDECAR = Workload(106, "sidecar_step_bf16_b64_blk32_dm2048_di4096_N16_7hooks",
+                   "R2LM denoising step with the whole sidecar block per hook: batch 64, "
+                   "generation block 32, d_model 2048 (the hook's hidden width), d_inner 4096, "
+                   "N=16, dt_rank 128, conv width 4, bf16 activations and projection weights, "
+                   "fp32 state; 7 hooks, out = hidden + s * block(hidden), s ~ U(0, 0.1)")
+
+WORKLOADS = {w.name: w for w in (TINY, BLOCK, DENOISE, PREFILL, RAGGED, BIDIR, SIDECAR)}
 
 
 def tiny_inputs() -> ScanInputs:
@@ -247,3 +253,40 @@ def bidir_reverse(hook: int = 0, seqs=None) -> dict:
 
 def bidir_gates() -> np.ndarray:
     return gates(BIDIR.key, 7, 0.0, 0.1)
+
+
+def sidecar_weights(key: int, dm: int, di: int, R: int, N: int = 16, K: int = 4,
+                    dtype: str = "f32") -> dict:
+    """Random-init weights of the sidecar block (no trained weights exist):
+    projections N(0, 1/fan_in) stored [out, in] in ``dtype``; conv taps N(0, 1/K),
+    conv bias N(0, 0.1^2), dt bias N(-2, 0.5^2) (Delta ~ softplus(-2) at
+    init), A = S4D-real, Dskip N(0, 1), all fp32."""
+    g = lambda t: rng(key, 50 + t)   # noqa: E731
+    f32 = lambda a: np.asarray(a, dtype=np.float32)   # noqa: E731
+    return {
+        "W_in": as_dtype(f32(g(0).standard_normal((2 * di, dm)) / np.sqrt(dm)), dtype),
+        "conv_w": f32(g(1).standard_normal((di, K)) / np.sqrt(K)),
+        "conv_b": f32(g(2).standard_normal(di) * 0.1),
+        "W_x": as_dtype(f32(g(3).standard_normal((R + 2 * N, di)) / np.sqrt(di)), dtype),
+        "W_dt": as_dtype(f32(g(4).standard_normal((di, R)) / np.sqrt(R)), dtype),
+        "dt_bias": f32(g(5).normal(-2.0, 0.5, di)),
+        "A": s4d_real_A(di, N),
+        "Dskip": f32(g(6).standard_normal(di)),
+        "W_out": as_dtype(f32(g(7).standard_normal((dm, di)) / np.sqrt(di)), dtype),
+    }
+
+
+def hidden_states(key: int, lengths, dm: int, dtype: str = "f32") -> np.ndarray:
+    """Stand-in hidden states [tokens, dm] ~ N(0, 1), one generator per sequence."""
+    parts = [rng(key, X, b).standard_normal((int(L), dm), dtype=np.float32)
+             for b, L in enumerate(lengths)]
+    a = np.concatenate(parts, axis=0) if parts else np.zeros((0, dm), dtype=np.float32)
+    return as_dtype(a, dtype)
+
+
+def sidecar_hook(hook: int):
+    """(hidden [2048, 2048] bf16 values, weights, s) of one hook of the sidecar step."""
+    key = SIDECAR.key * 100 + hook
+    return (hidden_states(key, [32] * 64, 2048, "bf16"),
+            sidecar_weights(key, 2048, 4096, 128, dtype="bf16"),
+            float(gates(SIDECAR.key, 7, 0.0, 0.1)[hook]))

@@ -52,6 +52,7 @@ def test_abi_version_and_status_strings():
 @pytest.mark.parametrize("cls,cname", [(_abi.ScanArgs, "r2l_scan_args"),
                                         (_abi.GradArgs, "r2l_grad_args"),
                                         (_abi.DirArgs, "r2l_dir_args"),
+                                        (_abi.SidecarArgs, "r2l_sidecar_args"),
                                         (_abi.AccessReport, "r2l_access_report"),
                                         (_abi.PlanInfo, "r2l_plan_info")])
 def test_struct_layout_matches_c(cls, cname):

@@ -453,3 +453,100 @@ def test_bidir_rejects_bad_arguments():
     # several lanes per channel are not built for it
     a.state_split = 2
     assert _abi.check_access_bidir(a, r, cu)[0] == _abi.R2L_ERR_UNSUPPORTED
+
+
+# ---- the sidecar block ---------------------------------------------------------------
+def make_sidecar(*, dtype="bf16", dm=64, di=128, R=8, K=4, batch=None, seqlen=None, lengths=None,
+                 s=0.5, in_place=False, pad_row=0, bias=True):
+    es = 2 if dtype == "bf16" else 4
+    N = 16
+    heap = FakeHeap()
+    a = _abi.SidecarArgs()
+    a.d_model, a.d_inner, a.dstate, a.dt_rank, a.d_conv = dm, di, N, R, K
+    a.dtype = _abi.R2L_DTYPE_BF16 if dtype == "bf16" else _abi.R2L_DTYPE_F32
+    cu = None
+    if lengths is not None:
+        a.batch = len(lengths)
+        cu = [0] + [int(v) for v in np.cumsum(lengths)]
+        a.total_tokens, a.max_seqlen = cu[-1], max(lengths) if lengths else 0
+        a.cu_seqlens = heap.alloc(4 * (a.batch + 1))
+        T = cu[-1]
+    else:
+        a.batch, a.seqlen = batch, seqlen
+        T = batch * seqlen
+    stride = dm + pad_row
+
+    def rows(n, ld, cols):
+        return heap.alloc(((n - 1) * ld + cols) * es if n else 0)
+
+    a.hidden, a.hidden_stride = rows(T, stride, dm), stride
+    a.out, a.out_stride = (a.hidden, stride) if in_place else (rows(T, stride, dm), stride)
+    a.W_in = heap.alloc(2 * di * dm * es)
+    a.conv_w = heap.alloc(4 * di * K)
+    a.W_x = heap.alloc((R + 2 * N) * di * es)
+    a.W_dt = heap.alloc(di * R * es)
+    a.A = heap.alloc(4 * di * N)
+    a.W_out = heap.alloc(dm * di * es)
+    if bias:
+        a.conv_b, a.dt_bias, a.Dskip = heap.alloc(4 * di), heap.alloc(4 * di), heap.alloc(4 * di)
+    a.s = s
+    need = _abi.sidecar_workspace_size(a)
+    if need:
+        a.workspace, a.workspace_bytes = heap.alloc(need), need
+    return a, cu
+
+
+def check_sidecar(**kw):
+    a, cu = make_sidecar(**kw)
+    st, rep = _abi.check_access_sidecar(a, cu)
+    msg = rep.message.decode() or _abi.last_error()
+    assert st == _abi.R2L_OK, "sidecar %s: %s" % (kw, msg)
+    return rep
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_sidecar_plans(dtype):
+    # six launches: 4 GEMMs, the conv, one scan launch (unchunked)
+    rep = check_sidecar(dtype=dtype, batch=2, seqlen=40)
+    assert rep.launches == 6
+    # ragged edges, short and long sequences (the scan chunks: 8 launches)
+    check_sidecar(dtype=dtype, lengths=[5, 0, 1, 64, 65, 130, 3])
+    rep = check_sidecar(dtype=dtype, lengths=[2000, 1, 700], di=64)
+    assert rep.launches == 8
+    check_sidecar(dtype=dtype, batch=3, seqlen=33, K=1, R=16, bias=False, pad_row=8)
+    check_sidecar(dtype=dtype, batch=1, seqlen=7, K=2, in_place=True)
+    # s = 0: a copy of hidden, or nothing in place
+    assert check_sidecar(dtype=dtype, batch=2, seqlen=9, s=0.0).launches == 1
+    assert check_sidecar(dtype=dtype, batch=2, seqlen=9, s=0.0, in_place=True).launches == 0
+    assert check_sidecar(dtype=dtype, lengths=[0, 0]).launches == 0
+
+
+def test_sidecar_benchmarked_shape():
+    rep = check_sidecar(batch=64, seqlen=32, dm=2048, di=4096, R=128)
+    assert rep.launches == 6 and rep.vector_staging == 1
+
+
+def test_sidecar_rejects_bad_arguments():
+    a, cu = make_sidecar(batch=2, seqlen=16)
+    assert _abi.check_access_sidecar(a, cu)[0] == _abi.R2L_OK
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.d_conv = 5
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_UNSUPPORTED
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.d_inner = 100
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_UNSUPPORTED
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.workspace_bytes -= 256
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_WORKSPACE
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.out = bad.W_in            # the output over a weight
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_ALIAS
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.hidden_stride = 65        # rows off 16-byte boundaries
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_MISALIGNED
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.dt_rank = 3
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_UNSUPPORTED
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.W_x = None
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_INVALID_ARG

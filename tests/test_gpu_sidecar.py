@@ -1,0 +1,140 @@
+"""GPU parity of r2l_sidecar_forward (through the C ABI) against the oracle's
+fp64 sidecar block on the same seeded inputs and weights.
+
+The oracle rounds each intermediate the GPU stores (x|z, u, r|B|C, r W_dt^T,
+the gated y) to the storage type, so the two differ by fp32 accumulation
+order and by the rounding decisions that order flips. Bar:
+* fp32: on the block's contribution c = out - hidden against the oracle's
+  s * o, max|err| / max|ref| <= 1e-5 (fp32 GEMMs and scan; measured ~7e-7);
+* bf16 (out is hidden + c rounded once to bf16): max|err| / max|ref| <= 2e-2
+  on out, and every out element within one bf16 ulp of the oracle's out plus
+  2e-2 * max|s * o| (a flipped bf16 rounding of an intermediate moves the
+  result by a small fraction of the contribution's scale).
+s = 0 gives hidden bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import reverse_mamba_selective_amd as r2l
+import synth
+from gpu_util import bf16_ulp, bits, dev, dev32, gpu, host, report  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+F32_WEIGHTS = ("conv_w", "conv_b", "dt_bias", "A", "Dskip")
+
+
+def to_gpu(w, dtype):
+    return {k: (dev32(v) if k in F32_WEIGHTS else dev(v, dtype)) for k, v in w.items()}
+
+
+def run(hidden_np, w_np, s, lengths, dtype, *, dense, in_place=False, drop=()):
+    w_np = {k: v for k, v in w_np.items() if k not in drop}
+    off = synth.offsets(lengths)
+    ref = oracle.sidecar_forward(hidden_np, w_np["W_in"], w_np["conv_w"], w_np.get("conv_b"),
+                                 w_np["W_x"], w_np["W_dt"], w_np.get("dt_bias"), w_np["A"],
+                                 w_np.get("Dskip"), w_np["W_out"], s=s, seq_offsets=off,
+                                 store=dtype)
+    h = dev(hidden_np, dtype)
+    kw = {}
+    if dense:
+        h = h.view(len(lengths), int(lengths[0]), -1)
+    else:
+        kw = dict(cu_seqlens=torch.from_numpy(off.astype(np.int32)).cuda())
+    h0 = h.clone()
+    out = r2l.sidecar_forward(h, to_gpu(w_np, dtype), s=s, out=h if in_place else None, **kw)
+    torch.cuda.synchronize()
+    return h0, out, ref
+
+
+def check(hidden_np, w_np, s, lengths, dtype, what, **kw):
+    h0, out, ref = run(hidden_np, w_np, s, lengths, dtype, **kw)
+    dm = hidden_np.shape[1]
+    got = host(out).reshape(-1, dm)
+    hid = host(h0).reshape(-1, dm)
+    want = s * ref["o"]
+    if not want.size:
+        return out
+    scale = max(float(np.max(np.abs(want))), 1e-30)
+    if dtype == "f32":   # the contribution itself (out's fp32 rounding is far below the bar)
+        e = float(np.max(np.abs((got - hid) - want))) / scale
+    else:                # out, which carries one bf16 rounding of hidden + contribution
+        e = float(np.max(np.abs(got - ref["out"]))) / float(np.max(np.abs(ref["out"])))
+    report(what, e, TOL[dtype])
+    assert e <= TOL[dtype], "%s: max|err|/max|ref| = %.3e" % (what, e)
+    if dtype == "bf16":
+        slack = bf16_ulp(ref["out"]) + TOL["bf16"] * scale
+        worst = float(np.max(np.abs(got - ref["out"]) / slack))
+        assert worst <= 1.0, "%s: an element is %.2f x (1 bf16 ulp + bound) off" % (what, worst)
+    return out
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sidecar_small_dense(gpu, dtype):
+    lengths = [40, 40]
+    w = synth.sidecar_weights(71, 64, 128, 8, dtype=dtype)
+    h = synth.hidden_states(72, lengths, 64, dtype)
+    check(h, w, 0.5, lengths, dtype, "dense %s" % dtype, dense=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sidecar_ragged_edges_in_place(gpu, dtype):
+    """Sequences of 0, 1, 3, 5, 64, 65, 130 tokens (conv windows cut at every
+    sequence end, conv chunks and scan tiles with tails), out = hidden."""
+    lengths = [5, 0, 1, 64, 65, 130, 3]
+    w = synth.sidecar_weights(73, 64, 256, 16, K=3, dtype=dtype)
+    h = synth.hidden_states(74, lengths, 64, dtype)
+    check(h, w, -0.8, lengths, dtype, "ragged %s" % dtype, dense=False, in_place=True)
+
+
+def test_sidecar_optional_terms_and_short_conv(gpu):
+    """No conv bias, dt bias or skip term; a 1-tap and a 2-tap conv."""
+    lengths = [17, 9]
+    for K in (1, 2):
+        w = synth.sidecar_weights(75 + K, 64, 128, 8, K=K, dtype="f32")
+        h = synth.hidden_states(77, lengths, 64, "f32")
+        check(h, w, 0.3, lengths, "f32", "K=%d" % K, dense=False,
+              drop=("conv_b", "dt_bias", "Dskip"))
+
+
+def test_sidecar_long_sequences_chunked_scan(gpu):
+    """Few channels and long sequences: the scan inside the block runs its chunked
+    plan (chunk pass, carry, readout pass)."""
+    lengths = [2000, 1, 700]
+    w = synth.sidecar_weights(78, 64, 64, 8, dtype="f32")
+    h = synth.hidden_states(79, lengths, 64, "f32")
+    check(h, w, 0.5, lengths, "f32", "chunked", dense=False)
+
+
+def test_sidecar_gate_zero(gpu):
+    lengths = [12, 7]
+    w = synth.sidecar_weights(80, 64, 128, 8, dtype="bf16")
+    h = synth.hidden_states(81, lengths, 64, "bf16")
+    h0, out, _ = run(h, w, 0.0, lengths, "bf16", dense=False)
+    assert np.array_equal(bits(out), bits(h0))
+    h0, out, _ = run(h, w, 0.0, lengths, "bf16", dense=False, in_place=True)
+    assert np.array_equal(bits(out), bits(h0))
+
+
+def test_sidecar_hook_bf16(gpu):
+    """One hook of the benchmarked step at full size: 64 x 32 tokens, d_model
+    2048, d_inner 4096, dt_rank 128, bf16."""
+    h, w, s = synth.sidecar_hook(3)
+    check(h, w, s, [32] * 64, "bf16", "hook 3", dense=True)
+
+
+def test_sidecar_is_deterministic(gpu):
+    lengths = [33, 64]
+    w = to_gpu(synth.sidecar_weights(82, 128, 256, 16, dtype="bf16"), "bf16")
+    h = dev(synth.hidden_states(83, lengths, 128, "bf16"), "bf16")
+    cu = torch.from_numpy(synth.offsets(lengths).astype(np.int32)).cuda()
+    a = r2l.sidecar_forward(h, w, s=0.7, cu_seqlens=cu)
+    b = r2l.sidecar_forward(h, w, s=0.7, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b))
