@@ -106,7 +106,9 @@ class Parity:
         self.err = self.ref = self.worst = 0.0
         self.n = 0
 
-    def add(self, got, ref):
+    def add(self, got, ref, slack=0.0):
+        """slack: an absolute allowance added to the fp32 bound of the bf16
+        element check (the sidecar's bf16 intermediates)."""
         import numpy as np
         ref = np.asarray(ref, dtype=np.float64)
         got = np.asarray(got, dtype=np.float64).reshape(ref.shape)
@@ -119,7 +121,7 @@ class Parity:
         self.n += ref.size
         if self.dtype == "bf16":
             ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
-            self.worst = max(self.worst, float(np.max(d / (ulp + 1e-5 * scale))))
+            self.worst = max(self.worst, float(np.max(d / (ulp + max(1e-5 * scale, slack)))))
 
     def result(self):
         rel = self.err / max(self.ref, 1e-30)
@@ -185,6 +187,7 @@ class Workload:
     measure: list = []      # per timed entry point: label, calls, bytes, alu, tc per launch
     step_entries: list = [0]  # index into measure of each call of a step
     launches_per_step = 1
+    graph_ok = True           # the step may be captured in a hipGraph
 
     def step(self, i, stream):
         for c in self.step_calls[i % len(self.step_calls)]:
@@ -677,9 +680,102 @@ class DenoiseBidir(Denoise):
                    "the oracle's")
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+class DenoiseSidecar(Denoise):
+    """The denoising step with the whole sidecar block per hook (r2l_sidecar_forward):
+    in-projection, conv + SiLU, x/dt projections, the gated R2L scan, out-projection
+    with the s-gated residual, 7 hooks over 64 x 32 tokens at d_model 2048,
+    d_inner 4096, bf16."""
+    name = "sidecar_step_bf16_b64_blk32_dm2048_di4096_N16_7hooks"
+    DM, DI, R = 2048, 4096, 128
+    # library GEMMs may record memsets (split-K scratch) that graph replays do
+    # not repeat reliably here: eager launches only
+    graph_ok = False
+
+    def setup(self, torch, r2l):
+        import synth
+        self.torch = torch
+        self.hooks = [synth.sidecar_hook(h) for h in range(self.HOOKS)]
+        tok = self.B * self.L
+        N = 16
+        self.tc_per_launch = tok * self.DI          # token-channels of the scan inside
+        self.tc_per_step = self.tc_per_launch * self.HOOKS
+        dm, di, R = self.DM, self.DI, self.R
+        self.gemm_flops = 2 * tok * (dm * 2 * di + di * (R + 2 * N) + R * di + di * dm)
+        # bytes: hidden in, out; the four weights; conv, dt bias, A, Dskip
+        self.bytes_per_launch = (tok * dm * 2 * 2 + 2 * (2 * di * dm + (R + 2 * N) * di +
+                                                         di * R + dm * di) +
+                                 4 * (di * 4 + di + di * N + di + di))
+        self.alu_per_launch = self.tc_per_launch * alu_ops_per_tc(True, False)
+        self.launches_per_step = self.HOOKS
+        set_bytes = self.bytes_per_launch * self.HOOKS
+        self.R = _rotation(set_bytes)
+        self.step_calls, self.outs0 = [], []
+        weights = []
+        for hid, w, s in self.hooks:
+            weights.append({k: (torch.from_numpy(v).cuda() if k in
+                                ("conv_w", "conv_b", "dt_bias", "A", "Dskip")
+                                else _dev(torch, v, "bf16")) for k, v in w.items()})
+        ws = None
+        for r in range(self.R):
+            row = []
+            for h, (hid, w, s) in enumerate(self.hooks):
+                x = _dev(torch, hid, "bf16").view(self.B, self.L, -1)
+                out = torch.empty_like(x)
+                if r == 0:
+                    self.outs0.append(out)
+                call = r2l.bind_sidecar(x, weights[h], s=s, out=out, workspace=ws)
+                ws = call.workspace          # one workspace serves every call (stream-ordered)
+                row.append(call)
+            self.step_calls.append(row)
+        self.step_entries = [0] * self.HOOKS
+        self.measure = [dict(label="r2l_sidecar_forward (one hook)",
+                             calls=[c for row in self.step_calls for c in row],
+                             bytes=self.bytes_per_launch, alu=self.alu_per_launch,
+                             tc=self.tc_per_launch, flops=self.gemm_flops)]
+        self.config = {"workload": self.name, "batch": self.B, "block_tokens": self.L,
+                       "d_model": dm, "d_inner": di, "N": 16, "dt_rank": R, "d_conv": 4,
+                       "hooks_per_step": self.HOOKS, "in_dtype": "bf16", "state_dtype": "fp32",
+                       "op": "r2l_sidecar_forward", "rotating_sets": self.R,
+                       "rotating_bytes": set_bytes * self.R, "parallelism": "single_gpu",
+                       "weights": "random init (synthetic)"}
+
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
+        import numpy as np
+        import oracle
+        tc, secs, hooks = 0, 0.0, 0
+        while secs < budget_s and hooks < 7 * 5:
+            h = hooks % self.HOOKS
+            hid, w, s = self.hooks[h]
+            t = {}
+            r = oracle.sidecar_forward(hid, w["W_in"], w["conv_w"], w["conv_b"], w["W_x"],
+                                       w["W_dt"], w["dt_bias"], w["A"], w["Dskip"], w["W_out"],
+                                       s=s, batch=self.B, seqlen=self.L, store="bf16",
+                                       nthreads=nthreads, timing=t)
+            if parity is not None and hooks < self.HOOKS:
+                # bar of the sidecar's GPU tests: one bf16 ulp + 2e-2 * max|s * o|
+                parity.add(self.outs0[h].float().cpu().numpy().reshape(r["out"].shape), r["out"],
+                           slack=2e-2 * float(np.max(np.abs(s * r["o"]))))
+            secs += t["seconds"]
+            tc += self.tc_per_launch
+            hooks += 1
+        return {"value": tc / secs, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "%d sidecar hooks (%d scan token-channels), %.1f s of oracle time "
+                          "(numpy fp64 projections on the host's BLAS threads, C scan)"
+                          % (hooks, tc, secs)}
+
+    parity_spec = ("out", "bf16", 2e-2,
+                   "out = hidden + s * sidecar(hidden) of all 7 hooks (first buffer set) vs the "
+                   "oracle's (intermediates rounded to bf16 where the GPU stores them); element "
+                   "bound: one bf16 ulp + 2e-2 * max|s * o|, as in the sidecar's GPU tests")
+
+
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
              "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward,
-             "bidir": DenoiseBidir}
+             "bidir": DenoiseBidir, "sidecar": DenoiseSidecar}
 
 
 def main():
@@ -789,7 +885,7 @@ def main():
 
     # (2) the step captured once per rotating set in a hipGraph and replayed
     graph_s = None
-    if not (args.no_graph or args.queue_ahead) and wl.launches_per_step > 1:
+    if not (args.no_graph or args.queue_ahead) and wl.launches_per_step > 1 and wl.graph_ok:
         graphs = []
         s = torch.cuda.Stream()
         with torch.cuda.stream(s):
@@ -824,6 +920,13 @@ def main():
         alu = {"bound": "alu", "achieved": round(alu_t, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
                "unit": "Tlane-op/s", "frac": round(alu_t / VALU_PEAK_TLANEOPS, 4),
                "traffic": hbm["traffic"]}
+        if m.get("flops"):
+            tf = m["flops"] / kern_s / 1e12
+            mf = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "traffic": hbm["traffic"],
+                  "note": "the whole call (GEMMs, conv, scan) against the bf16 matrix peak"}
+            return mf, alu
         return (alu, hbm) if alu["frac"] >= hbm["frac"] else (hbm, alu)
 
     kernels = []
@@ -834,7 +937,7 @@ def main():
                         "tc_per_launch": m["tc"], "tc_per_s": m["tc"] / (m["ms"] * 1e-3),
                         "roofline": bind_, "roofline_other": other_})
     binding, other = kernels[0]["roofline"], kernels[0]["roofline_other"]
-    hbm_gbs = (binding if binding["bound"] == "hbm" else other)["achieved"]
+    hbm_gbs = round(timed[0]["bytes"] / (timed[0]["ms"] * 1e-3) / 1e9, 1)
 
     cpu = parity = None
     if args.cpu_seconds > 0:

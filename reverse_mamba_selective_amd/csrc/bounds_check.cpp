@@ -601,8 +601,9 @@ void check_conv(Checker &ck, const Launch &l, const int32_t *cu_host) {
             ck.access("conv_w", rw, U(p.w) + d * p.K * 4, p.K * 4);
             if (rb) ck.access("conv_b", rb, U(p.b) + d * 4, 4);
         }
-        // loads: rows lo .. min(hi + K - 1, len) - 1 (the window's start-up and its steps)
-        const int64_t last = hi - 1 + p.K - 1 < len ? hi - 1 + p.K - 1 : len - 1;
+        // loads: the chunk and a halo of kConvMaxTaps - 1 rows, cut at the sequence's end
+        const int64_t halo_end = lo + kConvTokens + kConvMaxTaps - 1;
+        const int64_t last = (halo_end < len ? halo_end : len) - 1;
         for (int64_t t = lo; t <= last && ck.ok(); ++t)
             for (int64_t d : {d0, d1}) {
                 const uintptr_t addr = U(p.x) + ((s0 + t) * p.xs + d) * es;

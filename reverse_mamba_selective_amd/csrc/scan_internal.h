@@ -85,7 +85,7 @@ struct SegParams {
 // u[t,d] = SiLU(b[d] + sum_{j<K} w[d, K-1-j] * x[t+j, d]) within each
 // sequence. One workgroup per (sequence, chunk of kConvTokens, tile of kWG
 // channels).
-constexpr int kConvTokens = 64;
+constexpr int kConvTokens = 16;
 constexpr int kConvMaxTaps = 4;
 struct ConvParams {
     int64_t seqlen;              // dense tokens per sequence (cu_seqlens == nullptr)

@@ -7,9 +7,10 @@
 //
 // The conv of the reversed sequence is, in the original order, an
 // anti-causal conv: tap K-1-j weighs the token j positions to the right. A
-// lane owns one channel and walks its chunk of tokens right to left with a
-// register window of the K inputs it needs, so each x is loaded once (plus a
-// K-1 halo per chunk); a wave reads 64 consecutive channels of a token row.
+// lane owns one channel of a chunk of kConvTokens tokens: it issues the loads
+// of the chunk and its K-1 halo together (the conv is bound by memory
+// latency otherwise), then computes the chunk; a wave reads 64 consecutive
+// channels of a token row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,6 +25,7 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(kWG) void conv_silu_kernel(const ConvParams p) {
     using E = Elem<T>;
+    constexpr int CT = kConvTokens, W = kConvTokens + kConvMaxTaps - 1;
     const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
     if (!bg.valid) return;
     const int64_t b = bg.b;
@@ -35,9 +37,8 @@ __global__ __launch_bounds__(kWG) void conv_silu_kernel(const ConvParams p) {
         s0 = b * p.seqlen;
         len = p.seqlen;
     }
-    const int64_t lo = static_cast<int64_t>(bg.c) * kConvTokens;
+    const int64_t lo = static_cast<int64_t>(bg.c) * CT;
     if (lo >= len) return;
-    const int64_t hi = lo + kConvTokens < len ? lo + kConvTokens : len;
     const int64_t d = static_cast<int64_t>(bg.tile) * kWG + threadIdx.x;
     if (d >= p.D) return;
 
@@ -46,24 +47,23 @@ __global__ __launch_bounds__(kWG) void conv_silu_kernel(const ConvParams p) {
 #pragma unroll
     for (int j = 0; j < kConvMaxTaps; ++j) w[j] = j < p.K ? p.w[d * p.K + (p.K - 1 - j)] : 0.0f;
     const float bias = p.b ? p.b[d] : 0.0f;
-    const T *x = static_cast<const T *>(p.x) + s0 * p.xs + d;
-    T *u = static_cast<T *>(p.u) + s0 * p.us + d;
+    const T *x = static_cast<const T *>(p.x) + (s0 + lo) * p.xs + d;
+    T *u = static_cast<T *>(p.u) + (s0 + lo) * p.us + d;
+    const int64_t n = len - lo;   // tokens of the sequence from lo on (>= 1)
 
-    float win[kConvMaxTaps];   // win[j] = x[t + j] (zero past the sequence)
+    // every input of the chunk and its halo first (independent loads in
+    // flight together), zero past the sequence
+    float v[W];
 #pragma unroll
-    for (int j = 0; j < kConvMaxTaps; ++j) {
-        const int64_t t = hi - 1 + j;
-        win[j] = (j < p.K && t < len) ? E::ld(x + t * p.xs) : 0.0f;
-    }
-    for (int64_t t = hi - 1; t >= lo; --t) {
+    for (int i = 0; i < W; ++i) v[i] = i < n ? E::ld(x + i * p.xs) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < CT; ++i) {
+        if (i >= n) break;
         float acc = bias;
 #pragma unroll
-        for (int j = 0; j < kConvMaxTaps; ++j) acc = fmaf(w[j], win[j], acc);
+        for (int j = 0; j < kConvMaxTaps; ++j) acc = fmaf(w[j], v[i + j], acc);
         // SiLU(v) = v / (1 + e^-v)
-        E::st(u + t * p.us, acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * kLog2e)));
-#pragma unroll
-        for (int j = kConvMaxTaps - 1; j > 0; --j) win[j] = win[j - 1];
-        win[0] = t > lo ? E::ld(x + (t - 1) * p.xs) : 0.0f;
+        E::st(u + i * p.us, acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * kLog2e)));
     }
 }
 
