@@ -773,9 +773,237 @@ class DenoiseSidecar(Denoise):
                    "bound: one bf16 ulp + 2e-2 * max|s * o|, as in the sidecar's GPU tests")
 
 
+class _Call:
+    """A unit of a step that bench.py's timing loop launches: ``fn(stream)``."""
+
+    def __init__(self, fn):
+        self.fn = fn
+
+    def launch(self, stream):
+        self.fn(stream)
+
+
+class ServingStep(Workload):
+    """A denoising step of the serving harness: a stub causal backbone shaped like
+    Qwen3-1.7B (28 decoder layers, hidden 2048, 16 query / 8 key-value heads of
+    128, MLP 6144; random weights, no rotary embedding) over a generation block of
+    32 tokens for a batch of 8 whose 4096-token prompts were prefilled into a KV
+    cache, with the sidecar block (r2l_sidecar_forward, d_inner 4096) hooked after
+    every 4th layer. Prefill runs once in setup (timed with events, reported);
+    the timed step is the block's pass through all 28 layers and 7 hooks, with an
+    event before every layer and hook, so that the hooks' share of the step is
+    measured in place. The backbone is plain torch (matmuls on contiguous
+    operands, softmax accumulating in fp32), its layers between two hooks replayed as one
+    hipGraph; only the hooks are this library."""
+    name = "serving_step_bf16_b8_P4096_blk32_qwen3-1.7b-stub_28L_7hooks"
+    B, P, L = 8, 4096, 32
+    DM, HQ, HKV, HD, FF, LAYERS, EVERY = 2048, 16, 8, 128, 6144, 28, 4
+    DI, R = 4096, 128
+    graph_ok = False
+
+    def _layer(self, torch, l, h, write_cache_at=None, q_chunk=None):
+        """One pre-norm decoder layer on h [B, T, DM] in place. With write_cache_at
+        (prefill) the keys / values of h go to cache positions [at, at + T) and the
+        queries attend causally over the cache up to their own position."""
+        import torch.nn.functional as F
+        W = self.W[l]
+        B, T, _ = h.shape
+        g = self.HQ // self.HKV
+        a = h.float()
+        a = (a * torch.rsqrt(a.pow(2).mean(-1, keepdim=True) + 1e-6)).to(h.dtype) * W["ln1"]
+        qkv = torch.matmul(a, W["qkv"])                       # [B, T, (HQ + 2 HKV) HD]
+        q = qkv[..., :self.HQ * self.HD].reshape(B, T, self.HKV, g, self.HD)
+        k = qkv[..., self.HQ * self.HD:(self.HQ + self.HKV) * self.HD].reshape(B, T, self.HKV, self.HD)
+        v = qkv[..., (self.HQ + self.HKV) * self.HD:].reshape(B, T, self.HKV, self.HD)
+        at = self.P if write_cache_at is None else write_cache_at
+        Kt, V = self.Kt[l], self.V[l]                          # [B, HKV, HD, S], [B, HKV, S, HD]
+        Kt[:, :, :, at:at + T] = k.permute(0, 2, 3, 1)
+        V[:, :, at:at + T, :] = v.permute(0, 2, 1, 3)
+        # queries grouped per key-value head, scaled: [B, HKV, T * g, HD] (token-major)
+        qg = (q.permute(0, 2, 1, 3, 4).reshape(B, self.HKV, T * g, self.HD) *
+              (self.HD ** -0.5)).contiguous()
+        out = torch.empty((B, self.HKV, T * g, self.HD), dtype=h.dtype, device=h.device)
+        step = T if q_chunk is None else q_chunk
+        for c0 in range(0, T, step):
+            c1 = min(T, c0 + step)
+            end = at + c1                                      # keys visible to the chunk
+            sc = torch.matmul(qg[:, :, c0 * g:c1 * g].contiguous(),
+                              Kt[:, :, :, :end].contiguous())
+            # only the chunk's own keys can lie in a query's future
+            pos = torch.arange(c0, c1, device=h.device).repeat_interleave(g)
+            keys = torch.arange(c0, c1, device=h.device)
+            sc[..., at + c0:end].masked_fill_(keys[None, :] > pos[:, None], float("-inf"))
+            pr = torch.softmax(sc, dim=-1)                     # fp32 inside, bf16 out
+            out[:, :, c0 * g:c1 * g] = torch.matmul(pr, V[:, :, :end].contiguous())
+        o = out.reshape(B, self.HKV, T, g, self.HD).permute(0, 2, 1, 3, 4).reshape(B, T, -1)
+        h += torch.matmul(o, W["o"])
+        m = h.float()
+        m = (m * torch.rsqrt(m.pow(2).mean(-1, keepdim=True) + 1e-6)).to(h.dtype) * W["ln2"]
+        h += torch.matmul(F.silu(torch.matmul(m, W["gate"])) * torch.matmul(m, W["up"]), W["down"])
+
+    def setup(self, torch, r2l):
+        import synth
+        self.torch = torch
+        dev = "cuda"
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(707)
+        bf = torch.bfloat16
+
+        def w(i, o):
+            return (torch.randn((i, o), generator=gen, device=dev) / math.sqrt(i)).to(bf)
+
+        nq, nkv = self.HQ * self.HD, self.HKV * self.HD
+        self.W = [{"ln1": torch.ones(self.DM, dtype=bf, device=dev),
+                   "ln2": torch.ones(self.DM, dtype=bf, device=dev),
+                   "qkv": w(self.DM, nq + 2 * nkv), "o": w(nq, self.DM),
+                   "gate": w(self.DM, self.FF), "up": w(self.DM, self.FF), "down": w(self.FF, self.DM)}
+                  for _ in range(self.LAYERS)]
+        S = self.P + self.L
+        self.Kt = [torch.zeros((self.B, self.HKV, self.HD, S), dtype=bf, device=dev)
+                   for _ in range(self.LAYERS)]
+        self.V = [torch.zeros((self.B, self.HKV, S, self.HD), dtype=bf, device=dev)
+                  for _ in range(self.LAYERS)]
+        # prefill: the prompt through every layer, its keys / values into the cache
+        # (the R2L stream covers generation tokens only, so no hook runs here)
+        prompt = torch.randn((self.B, self.P, self.DM), generator=gen, device=dev).to(bf)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for l in range(self.LAYERS):
+            self._layer(torch, l, prompt, write_cache_at=0, q_chunk=512)
+        e1.record()
+        torch.cuda.synchronize()
+        self.prefill_ms = e0.elapsed_time(e1)
+        del prompt
+        # the sidecar hooks (random init), one per hooked layer
+        self.hook_layers = [l for l in range(self.LAYERS) if (l + 1) % self.EVERY == 0]
+        self.hooks = []
+        for j, l in enumerate(self.hook_layers):
+            wt = synth.sidecar_weights(SERVING_KEY * 100 + j, self.DM, self.DI, self.R,
+                                       dtype="bf16")
+            wd = {k: (torch.from_numpy(v).cuda() if k in ("conv_w", "conv_b", "dt_bias", "A",
+                                                          "Dskip") else _dev(torch, v, "bf16"))
+                  for k, v in wt.items()}
+            self.hooks.append((wt, wd, float(synth.gates(SERVING_KEY, 7, 0.0, 0.1)[j])))
+        # rotating generation blocks (noisy-token embeddings stand-ins)
+        self.R_sets = 4
+        self.blocks = [torch.randn((self.B, self.L, self.DM), generator=gen, device=dev).to(bf)
+                       for _ in range(self.R_sets)]
+        self.h = torch.empty_like(self.blocks[0])
+        ws = None
+        self.bound = []
+        for j in range(len(self.hook_layers)):
+            wt, wd, s = self.hooks[j]
+            c = r2l.bind_sidecar(self.h, wd, s=s, out=self.h, workspace=ws)
+            ws = c.workspace
+            self.bound.append(c)
+        self.R = self.R_sets
+        # The stub's layers between two hooks replay as one hipGraph each (the
+        # host would otherwise pace the ~25 small torch kernels of every layer);
+        # the hooks launch eagerly in between. Only timing depends on the stub.
+        starts = [0] + [l + 1 for l in self.hook_layers[:-1]]
+        segs = [list(range(a, l + 1)) for a, l in zip(starts, self.hook_layers)]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):            # warm-up before capture
+            self.h.copy_(self.blocks[0])
+            for seg in segs:
+                for l in seg:
+                    self._layer(torch, l, self.h)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+
+        def capture(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            return g
+
+        def run_seg(seg, r=None):
+            if r is not None:
+                self.h.copy_(self.blocks[r])
+            for l in seg:
+                self._layer(torch, l, self.h)
+
+        first = [capture(lambda r=r: run_seg(segs[0], r)) for r in range(self.R_sets)]
+        rest = [capture(lambda seg=seg: run_seg(seg)) for seg in segs[1:]]
+        torch.cuda.synchronize()
+        self._graphs = first + rest
+        self.step_calls, entries = [], []
+        for r in range(self.R_sets):
+            row, ent = [], []
+            for j in range(len(segs)):
+                g = first[r] if j == 0 else rest[j - 1]
+                row.append(_Call(lambda st, g=g: g.replay()))
+                ent.append(1)
+                row.append(self.bound[j])
+                ent.append(0)
+            self.step_calls.append(row)
+            entries = ent
+        self.step_entries = entries
+        tok = self.B * self.L
+        self.tc_per_launch = tok * self.DI
+        self.tc_per_step = self.tc_per_launch * len(self.hook_layers)
+        N, dm, di, R = 16, self.DM, self.DI, self.R
+        flops = 2 * tok * (dm * 2 * di + di * (R + 2 * N) + R * di + di * dm)
+        wbytes = 2 * (2 * di * dm + (R + 2 * N) * di + di * R + dm * di) + 4 * di * (4 + 3 + N)
+        self.measure = [dict(label="r2l_sidecar_forward (one hook, in the step)",
+                             calls=[c for row in self.step_calls for c in row if c in self.bound],
+                             bytes=tok * dm * 2 * 2 + wbytes,
+                             alu=self.tc_per_launch * alu_ops_per_tc(True, False),
+                             tc=self.tc_per_launch, flops=flops),
+                        dict(label="backbone: 4 stub layers between hooks (one hipGraph replay)",
+                             calls=[], bytes=0, alu=0, tc=0)]
+        # one hook's input and output inside a step, for parity against the oracle
+        self.h.copy_(self.blocks[0])
+        for l in range(self.LAYERS):
+            self._layer(torch, l, self.h)
+            if l == self.hook_layers[0]:
+                self.hook_in = self.h.clone()
+                self.bound[0].launch(torch.cuda.current_stream().cuda_stream)
+                self.hook_out = self.h.clone()
+                break
+        torch.cuda.synchronize()
+        self.config = {"workload": self.name, "batch": self.B, "prompt_tokens": self.P,
+                       "block_tokens": self.L, "backbone": "stub: 28 layers, hidden 2048, 16/8 "
+                       "heads x 128, MLP 6144, random init, no rotary", "hooks_per_step": 7,
+                       "hook": "r2l_sidecar_forward (d_inner 4096, N 16, dt_rank 128, K 4)",
+                       "in_dtype": "bf16", "prefill_ms": round(self.prefill_ms, 3),
+                       "parallelism": "single_gpu", "weights": "random init (synthetic)"}
+
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
+        import numpy as np
+        import oracle
+        hid = self.hook_in.float().cpu().numpy().reshape(-1, self.DM)
+        wt, _, s = self.hooks[0]
+        tc, secs, n = 0, 0.0, 0
+        while secs < budget_s and n < 50:
+            t = {}
+            r = oracle.sidecar_forward(hid, wt["W_in"], wt["conv_w"], wt["conv_b"], wt["W_x"],
+                                       wt["W_dt"], wt["dt_bias"], wt["A"], wt["Dskip"],
+                                       wt["W_out"], s=s, batch=self.B, seqlen=self.L,
+                                       store="bf16", nthreads=nthreads, timing=t)
+            if parity is not None and n == 0:
+                parity.add(self.hook_out.float().cpu().numpy().reshape(r["out"].shape), r["out"],
+                           slack=2e-2 * float(np.max(np.abs(s * r["o"]))))
+            secs += t["seconds"]
+            tc += self.tc_per_launch
+            n += 1
+        return {"value": tc / secs, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "%d runs of the first hook's sidecar block on its input inside a "
+                          "step (%d scan token-channels), %.1f s of oracle time" % (n, tc, secs)}
+
+    parity_spec = ("out", "bf16", 2e-2,
+                   "the first hook's output inside a denoising step vs the oracle's sidecar "
+                   "block on the same input; element bound one bf16 ulp + 2e-2 * max|s * o|")
+
+
+SERVING_KEY = 107
+
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
              "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward,
-             "bidir": DenoiseBidir, "sidecar": DenoiseSidecar}
+             "bidir": DenoiseBidir, "sidecar": DenoiseSidecar, "serving": ServingStep}
 
 
 def main():
@@ -854,6 +1082,7 @@ def main():
     eager_s = (time.perf_counter() - t0) / args.steps
     region_ms = ev_start.elapsed_time(ev_end)
     timed = []
+    step_split = None
     if per_call:
         marks = call_ev + [ev_end]
         dur = [marks[k].elapsed_time(marks[k + 1]) for k in range(len(call_ev))]
@@ -863,6 +1092,8 @@ def main():
         n = len(entries)
         step_ms = [sum(dur[i * n:(i + 1) * n]) for i in range(args.steps)]
         spread_how = "per-step sums of the per-call events of the timed region"
+        step_split = {t["label"]: round(t["ms"] * sum(1 for e in entries if e == k), 4)
+                      for k, t in enumerate(timed)}
     elif args.queue_ahead:
         launches = args.steps * len(entries)
         timed.append(dict(wl.measure[0], ms=region_ms / launches, reps=launches))
@@ -982,6 +1213,9 @@ def main():
         "ms_per_step_graph": graph_s * 1e3 if graph_s else None,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "step_split_ms": step_split,
+        "step_share": ({k: round(v / sum(step_split.values()), 4) for k, v in step_split.items()}
+                       if step_split else None),
     }
     print(json.dumps(line))
 
