@@ -371,6 +371,18 @@ typedef struct r2l_sidecar_args {
 
 R2L_API r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream);
 
+/*
+ * r2l_sidecar_tune -- for the four projections of a call with these
+ * arguments, times hipBLASLt's candidate algorithms on `stream` and keeps the
+ * fastest for every later r2l_sidecar_forward with the same shapes (process-
+ * wide, per device). Call it once before serving or graph capture: it
+ * synchronizes the stream, and it overwrites the workspace (never hidden or
+ * out, except that when the out-projection's rows do not fit the workspace's
+ * in-projection rows it is timed in out itself, or, when out is hidden, not
+ * tuned). The same checks as r2l_sidecar_forward; s == 0 does nothing.
+ */
+R2L_API r2l_status r2l_sidecar_tune(const r2l_sidecar_args *a, void *stream);
+
 /* Bytes of workspace r2l_sidecar_forward needs for these arguments (shape
  * fields and s only). */
 R2L_API r2l_status r2l_sidecar_workspace_size(const r2l_sidecar_args *a, size_t *bytes);

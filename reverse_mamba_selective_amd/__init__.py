@@ -23,6 +23,7 @@ from . import _abi
 from ._abi import R2LError  # noqa: F401
 
 __all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "bidir_scan", "sidecar_forward",
+           "sidecar_tune",
            "bind_sidecar", "SIDECAR_WEIGHTS",
            "workspace_size", "bind",
            "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "prefix_scan_backward",
@@ -403,6 +404,18 @@ def _sidecar_workspace(a, workspace, device):
     return workspace
 
 
+def sidecar_tune(hidden, weights: dict, *, s, cu_seqlens=None, max_seqlen=None, out=None,
+                 workspace=None):
+    """r2l_sidecar_tune for these arguments (see ``BoundSidecar.tune``)."""
+    if out is None:
+        out = torch.empty_like(hidden)
+    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out)
+    workspace = _sidecar_workspace(a, workspace, hidden.device)
+    with torch.cuda.device(hidden.device):
+        stream = torch.cuda.current_stream(hidden.device).cuda_stream
+    _abi.call_sidecar(a, stream, tune=True)
+
+
 def sidecar_forward(hidden, weights: dict, *, s, cu_seqlens=None, max_seqlen=None, out=None,
                     workspace=None):
     """The R2L sidecar block as a hook: out = hidden + s * sidecar(hidden)
@@ -436,6 +449,14 @@ class BoundSidecar:
         st = self._fn(self._ref, _abi._vp(stream))
         if st != _abi.R2L_OK:
             raise R2LError(st, "r2l_sidecar_forward", _abi.last_error())
+
+    def tune(self, stream=None):
+        """Time the library's GEMM candidates for this call's shapes and keep the
+        fastest (r2l_sidecar_tune; synchronizes the stream, overwrites the
+        workspace)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        _abi.call_sidecar(self.args, stream, tune=True)
 
 
 def bind_sidecar(hidden, weights: dict, *, s, out, cu_seqlens=None, max_seqlen=None,

@@ -34,7 +34,7 @@ EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace
            "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
            "r2l_check_access_backward", "prefix_scan_backward", "bidir_scan",
            "r2l_check_access_bidir", "r2l_sidecar_forward", "r2l_sidecar_workspace_size",
-           "r2l_check_access_sidecar")
+           "r2l_check_access_sidecar", "r2l_sidecar_tune")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -158,8 +158,9 @@ def load(path: str = LIB_PATH):
     lib.r2l_check_access_bidir.argtypes = [ptr, dptr, ctypes.POINTER(_i32),
                                            ctypes.POINTER(AccessReport)]
     sptr = ctypes.POINTER(SidecarArgs)
-    lib.r2l_sidecar_forward.restype = _i32
-    lib.r2l_sidecar_forward.argtypes = [sptr, _vp]
+    for fn in (lib.r2l_sidecar_forward, lib.r2l_sidecar_tune):
+        fn.restype = _i32
+        fn.argtypes = [sptr, _vp]
     lib.r2l_sidecar_workspace_size.restype = _i32
     lib.r2l_sidecar_workspace_size.argtypes = [sptr, ctypes.POINTER(ctypes.c_size_t)]
     lib.r2l_check_access_sidecar.restype = _i32
@@ -270,10 +271,11 @@ def sidecar_workspace_size(args: SidecarArgs) -> int:
     return int(n.value)
 
 
-def call_sidecar(args: SidecarArgs, stream: int | None) -> None:
-    st = load().r2l_sidecar_forward(ctypes.byref(args), _vp(stream or 0))
+def call_sidecar(args: SidecarArgs, stream: int | None, tune: bool = False) -> None:
+    func = "r2l_sidecar_tune" if tune else "r2l_sidecar_forward"
+    st = getattr(load(), func)(ctypes.byref(args), _vp(stream or 0))
     if st != R2L_OK:
-        raise R2LError(st, "r2l_sidecar_forward", last_error())
+        raise R2LError(st, func, last_error())
 
 
 def check_access_sidecar(args: SidecarArgs, cu_seqlens_host=None):

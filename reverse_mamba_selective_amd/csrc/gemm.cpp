@@ -6,7 +6,9 @@
 // Y^T = W X^T: A = W (stored K x N, transposed), B = X^T (K x M, as stored),
 // the "TN" layout. One hipBLASLt handle per device and one algorithm per
 // GEMM shape are kept for the life of the process (host memory only); the
-// library's scratch is a slice of the caller's workspace.
+// library's scratch is a slice of the caller's workspace. The algorithm is
+// the library's first heuristic choice unless a tuning call has timed its
+// candidates for that shape and kept the fastest.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -37,63 +39,157 @@ struct Prepared {
     size_t ws = 0;
 };
 
+constexpr int kTuneCandidates = 16;
+
 std::mutex g_mutex;
 std::map<int, hipblasLtHandle_t> g_handles;
 std::map<Shape, Prepared> g_plans;
 
-const char *prepare(const Shape &s, hipblasLtHandle_t h, Prepared *out) {
+Shape shape_of(int dev, int dtype, const GemmParams &g) {
+    return Shape{dev, dtype, g.M, g.N, g.K, g.ldx, g.ldw, g.ldc, g.ldy, g.beta != 0.0f, g.ws_bytes};
+}
+
+hipblasLtHandle_t handle_of(int dev, const char **err) {
+    auto hit = g_handles.find(dev);
+    if (hit != g_handles.end()) return hit->second;
+    hipblasLtHandle_t h;
+    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) {
+        *err = "hipblasLtCreate failed";
+        return nullptr;
+    }
+    g_handles[dev] = h;
+    return h;
+}
+
+// The matmul and matrix descriptors of shape s.
+const char *describe(const Shape &s, Prepared *p) {
     const hipDataType t = s.dtype == 1 ? HIP_R_16BF : HIP_R_32F;
-    Prepared p;
-    if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS)
+    if (hipblasLtMatmulDescCreate(&p->desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS)
         return "hipblasLtMatmulDescCreate failed";
     const int32_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
-    hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT));
-    hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN));
-    if (hipblasLtMatrixLayoutCreate(&p.a, t, s.K, s.N, s.ldw) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&p.b, t, s.K, s.M, s.ldx) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&p.c, t, s.N, s.M, s.beta ? s.ldc : s.ldy) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatrixLayoutCreate(&p.d, t, s.N, s.M, s.ldy) != HIPBLAS_STATUS_SUCCESS)
+    hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT));
+    hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN));
+    if (hipblasLtMatrixLayoutCreate(&p->a, t, s.K, s.N, s.ldw) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&p->b, t, s.K, s.M, s.ldx) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&p->c, t, s.N, s.M, s.beta ? s.ldc : s.ldy) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatrixLayoutCreate(&p->d, t, s.N, s.M, s.ldy) != HIPBLAS_STATUS_SUCCESS)
         return "hipblasLtMatrixLayoutCreate failed";
+    return nullptr;
+}
+
+// The library's candidates for shape s, best first by its own heuristic.
+const char *candidates(const Shape &s, hipblasLtHandle_t h, const Prepared &p, int want,
+                       hipblasLtMatmulHeuristicResult_t *res, int *count) {
     hipblasLtMatmulPreference_t pref;
     if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS)
         return "hipblasLtMatmulPreferenceCreate failed";
     const uint64_t ws = s.ws;
     hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws,
                                           sizeof(ws));
-    hipblasLtMatmulHeuristicResult_t res[1];
-    int count = 0;
+    *count = 0;
     const hipblasStatus_t st = hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.a, p.b, p.c, p.d, pref,
-                                                               1, res, &count);
+                                                               want, res, count);
     hipblasLtMatmulPreferenceDestroy(pref);
-    if (st != HIPBLAS_STATUS_SUCCESS || count < 1) return "hipBLASLt has no algorithm for this GEMM";
-    p.algo = res[0].algo;
-    p.ws = res[0].workspaceSize;
-    *out = p;
+    if (st != HIPBLAS_STATUS_SUCCESS || *count < 1) return "hipBLASLt has no algorithm for this GEMM";
     return nullptr;
 }
 
 }  // namespace
 
+const char *tune_gemm(int dtype, const GemmParams &g, void *y_scratch, hipStream_t stream) {
+    if (g.M <= 0 || g.N <= 0) return nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return "hipGetDevice failed";
+    const Shape s = shape_of(dev, dtype, g);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    const char *err = nullptr;
+    hipblasLtHandle_t h = handle_of(dev, &err);
+    if (!h) return err;
+    Prepared p;
+    err = describe(s, &p);
+    if (err) return err;
+    hipblasLtMatmulHeuristicResult_t res[kTuneCandidates];
+    int count = 0;
+    err = candidates(s, h, p, kTuneCandidates, res, &count);
+    if (err) return err;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return "hipEventCreate failed";
+    if (hipEventCreate(&e1) != hipSuccess) {
+        hipEventDestroy(e0);
+        return "hipEventCreate failed";
+    }
+    void *Y = y_scratch ? y_scratch : g.Y;
+    const float alpha = g.alpha, beta = g.beta;
+    float best = -1.0f;
+    int pick = 0;
+    for (int i = 0; i < count && !err; ++i) {
+        if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > g.ws_bytes) continue;
+        auto run = [&]() {
+            return hipblasLtMatmul(h, p.desc, &alpha, g.W, p.a, g.X, p.b, &beta,
+                                   g.beta != 0.0f ? g.C : Y, p.c, Y, p.d, &res[i].algo,
+                                   res[i].workspaceSize ? g.ws : nullptr, res[i].workspaceSize,
+                                   stream);
+        };
+        if (run() != HIPBLAS_STATUS_SUCCESS) continue;          // warm-up, and a validity check
+        constexpr int kReps = 5;
+        bool ok = true;
+        hipEventRecord(e0, stream);
+        for (int r = 0; r < kReps && ok; ++r) ok = run() == HIPBLAS_STATUS_SUCCESS;
+        hipEventRecord(e1, stream);
+        if (hipEventSynchronize(e1) != hipSuccess) {
+            err = "hipEventSynchronize failed";
+            break;
+        }
+        float ms = 0.0f;
+        hipEventElapsedTime(&ms, e0, e1);
+        if (ok && (best < 0.0f || ms < best)) {
+            best = ms;
+            pick = i;
+        }
+    }
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    if (err) return err;
+    if (best < 0.0f) return "no hipBLASLt candidate ran";
+    auto it = g_plans.find(s);
+    if (it != g_plans.end()) {   // keep the existing descriptors of this shape
+        it->second.algo = res[pick].algo;
+        it->second.ws = res[pick].workspaceSize;
+        hipblasLtMatrixLayoutDestroy(p.a);
+        hipblasLtMatrixLayoutDestroy(p.b);
+        hipblasLtMatrixLayoutDestroy(p.c);
+        hipblasLtMatrixLayoutDestroy(p.d);
+        hipblasLtMatmulDescDestroy(p.desc);
+    } else {
+        p.algo = res[pick].algo;
+        p.ws = res[pick].workspaceSize;
+        g_plans[s] = p;
+    }
+    return nullptr;
+}
+
 const char *run_gemm(int dtype, const GemmParams &g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return nullptr;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return "hipGetDevice failed";
-    const Shape s{dev, dtype, g.M, g.N, g.K, g.ldx, g.ldw, g.ldc, g.ldy, g.beta != 0.0f, g.ws_bytes};
+    const Shape s = shape_of(dev, dtype, g);
     hipblasLtHandle_t h;
     Prepared p;
     {
         std::lock_guard<std::mutex> lock(g_mutex);
-        auto hit = g_handles.find(dev);
-        if (hit == g_handles.end()) {
-            if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return "hipblasLtCreate failed";
-            g_handles[dev] = h;
-        } else {
-            h = hit->second;
-        }
+        const char *err = nullptr;
+        h = handle_of(dev, &err);
+        if (!h) return err;
         auto it = g_plans.find(s);
         if (it == g_plans.end()) {
-            const char *err = prepare(s, h, &p);
+            err = describe(s, &p);
             if (err) return err;
+            hipblasLtMatmulHeuristicResult_t res[1];
+            int count = 0;
+            err = candidates(s, h, p, 1, res, &count);
+            if (err) return err;
+            p.algo = res[0].algo;
+            p.ws = res[0].workspaceSize;
             g_plans[s] = p;
         } else {
             p = it->second;

@@ -676,6 +676,32 @@ r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream) {
     return run_sidecar(a, static_cast<hipStream_t>(stream));
 }
 
+r2l_status r2l_sidecar_tune(const r2l_sidecar_args *a, void *stream) {
+    r2l::SidecarPlan sp;
+    r2l_status st = prepare_sidecar(a, &sp);
+    if (st != R2L_OK) return st;
+    Launch ls[r2l::kMaxSidecarLaunches];
+    const int n = r2l::build_sidecar_launches(a, sp, ls);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t es = elem_size(a->dtype);
+    for (int i = 0; i < n; ++i) {
+        if (ls[i].kind != Launch::Gemm) continue;
+        const r2l::GemmParams &g = ls[i].gemm;
+        void *scratch = nullptr;
+        if (g.Y == a->out) {
+            // the out-projection: time it into the x|z rows (dead by then), never into out
+            const size_t need = static_cast<size_t>(((g.M - 1) * g.ldy + g.N) * es);
+            if (need <= sp.off_u - sp.off_xz)
+                scratch = static_cast<char *>(a->workspace) + sp.off_xz;
+            else if (a->out == a->hidden)
+                continue;   // in place and no room: keep the library's first choice
+        }
+        const char *err = r2l::tune_gemm(a->dtype, g, scratch, s);
+        if (err) return fail(R2L_ERR_HIP, "sidecar projection tuning: %s", err);
+    }
+    return ok();
+}
+
 r2l_status r2l_sidecar_workspace_size(const r2l_sidecar_args *a, size_t *bytes) {
     if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
     if (!a) return fail(R2L_ERR_INVALID_ARG, "args is NULL");

@@ -216,6 +216,10 @@ hipError_t launch_conv(int dtype, const ConvParams &p, hipStream_t stream);
 hipError_t launch_sidecar_segment(int dtype, int mode, const SegParams &p, hipStream_t stream);
 // a GEMM through hipBLASLt; returns a description of a failure, or nullptr
 const char *run_gemm(int dtype, const GemmParams &p, hipStream_t stream);
+// times the library's candidates for this GEMM on `stream` (writing Y, or
+// y_scratch when given, with the same leading dimension) and keeps the fastest
+// for later calls of the same shape; synchronizes the stream
+const char *tune_gemm(int dtype, const GemmParams &p, void *y_scratch, hipStream_t stream);
 // G in {2, 4}
 hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, hipStream_t stream);
 hipError_t launch_sums(const SumBatch &p, hipStream_t stream);

@@ -138,3 +138,19 @@ def test_sidecar_is_deterministic(gpu):
     b = r2l.sidecar_forward(h, w, s=0.7, cu_seqlens=cu)
     torch.cuda.synchronize()
     assert np.array_equal(bits(a), bits(b))
+
+
+def test_sidecar_tuned_projections(gpu):
+    """After r2l_sidecar_tune has timed the library's candidates, the call (with
+    whichever algorithms won) still meets the bar; hidden is left untouched by the
+    tuning, in place included."""
+    lengths = [32] * 8
+    w_np = synth.sidecar_weights(84, 256, 512, 16, dtype="bf16")
+    h_np = synth.hidden_states(85, lengths, 256, "bf16")
+    w = to_gpu(w_np, "bf16")
+    h = dev(h_np, "bf16").view(8, 32, -1)
+    before = h.clone()
+    r2l.sidecar_tune(h, w, s=0.6, out=h)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(h), bits(before))
+    check(h_np, w_np, 0.6, lengths, "bf16", "tuned", dense=True)
