@@ -19,11 +19,10 @@
 //    kN / G states each, and walks the groups backwards: it recomputes the
 //    group's states in registers from its checkpoint, then runs the adjoint
 //    over the group in reverse.
-//  * dBm and dCm are sums over channels of per-lane products: a wave sums its
-//    64 / G channels with a transpose-reduce (each shuffle step halves the
-//    values a lane carries: 2 * (kN / G) - 1 exchanges instead of
-//    kN * log2(64 / G)), the four waves add up in LDS, and the block writes
-//    one partial row per token and tile; the sums over tiles, over sequences
+//  * dBm and dCm are sums over channels of per-lane products: each 16-lane
+//    row of a wave adds its 16 / G channels with DPP row rotations (VALU adds,
+//    no lane permutes through LDS), the block's 16 rows add up in LDS, and the
+//    block writes one partial row per token and tile; the sums over tiles, over sequences
 //    (dA, dDskip) and over blocks (ds) are separate launches in a fixed order,
 //    so the result is deterministic (no atomics).
 //  * Bm / Cm rows are staged in LDS per tile of kTile tokens (double-buffered,
@@ -46,30 +45,28 @@ __device__ __forceinline__ float sigmoid(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
 }
 
-// Sum of v[] over the channels of each 16-lane row of a wave (the lanes that
-// hold the same slice of states: lanes with the same index mod G). Lane l
-// returns its row's total of state reduced_state(G, l % 16); the rows are
-// added up later, with the other waves, in the block sum.
-template <int G>
-__device__ __forceinline__ float row_state_sum(float (&v)[kN / G]) {
-    constexpr int NS = kN / G;
-    constexpr int LG = G == 1 ? 0 : (G == 2 ? 1 : 2);
-    constexpr int STAGES = NS == 16 ? 4 : (NS == 8 ? 3 : (NS == 4 ? 2 : (NS == 2 ? 1 : 0)));
-    const int lane = threadIdx.x & 63;
+// Sum of v[] over the channels of each 16-lane row of a wave: the lanes of
+// a row that hold the same states (same lane % G) are the orbit of rotations
+// by G, 2G, 4G, ... within the row, so adding DPP row rotations of G, 2G, ...
+// leaves every lane with its row's totals of its own NS states (lanes of one
+// orbit hold equal values). One VALU add per value and step; no selects, no
+// LDS permutes.
+template <int R, int NS>
+__device__ __forceinline__ void add_row_ror(float (&v)[NS]) {
 #pragma unroll
-    for (int j = 0; j < STAGES; ++j) {
-        const int bit = 1 << (LG + j);
-        const bool up = (lane & bit) != 0;
-        const int half = NS >> (j + 1);
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const float send = up ? v[i] : v[i + half];
-            const float keep = up ? v[i + half] : v[i];
-            v[i] = keep + __shfl_xor(send, bit);
-        }
+    for (int i = 0; i < NS; ++i) {
+        const int o = __builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0x120 + R, 0xF, 0xF, true);
+        v[i] += __int_as_float(o);   // v + (v of the lane R places along the row)
     }
-    static_assert(LG + STAGES == 4, "a row of 16 lanes ends up holding all kN states");
-    return v[0];
+}
+
+template <int G>
+__device__ __forceinline__ void row_channel_sum(float (&v)[kN / G]) {
+    constexpr int NS = kN / G;
+    if constexpr (G <= 1) add_row_ror<1, NS>(v);
+    if constexpr (G <= 2) add_row_ror<2, NS>(v);
+    if constexpr (G <= 4) add_row_ror<4, NS>(v);
+    add_row_ror<8, NS>(v);
 }
 
 template <bool REV, typename T, int G, bool SP>
@@ -83,7 +80,9 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
     static_assert(K * NBC == kWG, "one thread per (group token, column) in the block sum");
     __shared__ __align__(16) float lds_bc[2][kTile * NBC];
     constexpr int ROWS = WAVES * 4;              // 16-lane rows per block
-    __shared__ float red[ROWS][K][NBC];
+    // row partials of a group, double-buffered: a group's block sum overlaps
+    // the next group's adjoint (one barrier per group)
+    __shared__ float red[2][ROWS][K][NBC];
     __shared__ float red_s[WAVES];
     using E = Elem<T>;
     using R = typename E::raw_t;
@@ -156,8 +155,10 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                                  E::word_elem(stw, 4 * q + 2), E::word_elem(stw, 4 * q + 3));
     };
 
-    // per-token inputs of one group (positions past its end repeat its last one)
+    // per-token inputs of one group (positions past its end repeat its last
+    // one) and the state entering it (its checkpoint)
     R nx[K], nd[K], ng[K];
+    float nck[NS];
     auto load_group = [&](int gpos, int gcnt) {
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -166,6 +167,9 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             nd[j] = E::bload(rd, doff, row * drb);
             ng[j] = E::bload(rg, doff, row * grb);
         }
+        const float *cp = p.ckpt + (ckpt_row(b, sq.s0p, gpos) * p.D + dl) * kN + sub * NS;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) nck[n] = cp[n];
     };
 
     // tiles (and the groups inside them) from the last visited to the first
@@ -191,17 +195,17 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             // this group's per-token inputs were requested during the previous
             // group; request the next group's (gpos - K) now
             R xr[K], dr[K], gr[K];
+            float hck[NS];
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 xr[j] = nx[j];
                 dr[j] = nd[j];
                 gr[j] = ng[j];
             }
-            if (gpos > 0) load_group(gpos - K, K);
-            float hck[NS];
-            const float *cp = p.ckpt + (ckpt_row(b, sq.s0p, gpos) * p.D + dl) * kN + sub * NS;
 #pragma unroll
-            for (int n = 0; n < NS; ++n) hck[n] = cp[n];
+            for (int n = 0; n < NS; ++n) hck[n] = nck[n];
+            if (gpos > 0) load_group(gpos - K, K);
+            float (*rd_)[K][NBC] = red[gi & 1];
 
             // the group's states and decays, recomputed forward from the checkpoint
             float hs[K][NS], ab[K][NS], delta[K];
@@ -260,11 +264,14 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                     if (p.dx) E::bstore(E::pack(dxv), rdx, doff, orow * dxrb);
                     if (p.ddt) E::bstore(E::pack(ddtv), rdd, doff, orow * ddrb);
                 }
-                const float rb = row_state_sum<G>(pb);
-                const float rc = row_state_sum<G>(pc);
-                const int n = reduced_state(G, lane & 15);
-                red[wave * 4 + (lane >> 4)][j][n] = rb;
-                red[wave * 4 + (lane >> 4)][j][kN + n] = rc;
+                row_channel_sum<G>(pb);
+                row_channel_sum<G>(pc);
+                float *rw = rd_[wave * 4 + (lane >> 4)][j];
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {   // equal values from every lane of an orbit
+                    rw[sub * NS + n] = pb[n];
+                    rw[kN + sub * NS + n] = pc[n];
+                }
             };
             if (gcnt == K) {   // every group but a sequence's last: no branch per token
 #pragma unroll
@@ -281,12 +288,13 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 if (j < gcnt && dst) {
                     float v = 0.0f;
 #pragma unroll
-                    for (int w = 0; w < ROWS; ++w) v += red[w][j][col];
+                    for (int w = 0; w < ROWS; ++w) v += rd_[w][j][col];
                     const int64_t t = sq.s0p + seg_row(sg, gpos + j);
                     dst[(bg.tile * p.tokens + t) * kN + (col % kN)] = v;
                 }
             }
-            __syncthreads();
+            // no barrier here: the next group writes the other half of red, and
+            // the one after it this half only past the next group's barrier
         }
         if (more) stage_store((ti - 1) & 1);
         __syncthreads();

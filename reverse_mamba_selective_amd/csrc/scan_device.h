@@ -136,11 +136,11 @@ __device__ __forceinline__ float softplus(float v) {
 template <int G>
 __device__ __forceinline__ float group_sum(float y) {
     if constexpr (G >= 2) {
-        const int o = __builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+        const int o = __builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
         y += __int_as_float(o);
     }
     if constexpr (G >= 4) {
-        const int o = __builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+        const int o = __builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
         y += __int_as_float(o);
     }
     return y;

@@ -231,19 +231,6 @@ R2L_HD BwdSeqGeom bwd_seq_geom(const BwdParams &p, int64_t b, int64_t s0, int64_
     return q;
 }
 
-// The state index whose sum over a wave's channels lane `lane` (< 16) holds
-// after the transpose-reduce with G lanes per channel (each exchange step on
-// lane bit log2(G) + j keeps the upper half of the remaining states in the
-// lanes whose bit is set).
-R2L_HD int reduced_state(int G, int lane) {
-    const int lg = G == 1 ? 0 : (G == 2 ? 1 : 2);
-    const int ns = kN / G;
-    int n = (lane & (G - 1)) * ns;
-    for (int j = 0; (ns >> j) > 1; ++j)
-        if ((lane >> (lg + j)) & 1) n += ns >> (j + 1);
-    return n;
-}
-
 // Row copy: kCopyThreads columns per block along x, rows along y (looping
 // when there are more rows than kCopyMaxRowBlocks).
 constexpr int kCopyThreads = 256;
