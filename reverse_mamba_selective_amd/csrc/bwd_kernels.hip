@@ -240,6 +240,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 dD = fmaf(dy, xv, dD);
                 const float dlx = delta[j] * xv;
                 float pb[NS], pc[NS];
+                // dDelta = sum_n g_n (B_n x + A_n abar_n h_prev_n)
+                //        = x * sum_n g_n B_n + sum_n (g_n abar_n h_prev_n) A_n
                 float dd = 0.0f, dxs = 0.0f;
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
@@ -247,15 +249,14 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                     pc[n] = dy * hs[j][n];
                     const float hp = j > 0 ? hs[j - 1][n] : hck[n];
                     const float a = ab[j][n];
-                    const float ah = a * hp;
-                    const float bn = row[n];
-                    dd = fmaf(g[n], fmaf(bn, xv, An[n] * ah), dd);
-                    dA[n] = fmaf(g[n] * delta[j], ah, dA[n]);
-                    dxs = fmaf(g[n], bn, dxs);
+                    const float gah = g[n] * (a * hp);
+                    dA[n] = fmaf(gah, delta[j], dA[n]);
+                    dd = fmaf(gah, An[n], dd);
+                    dxs = fmaf(g[n], row[n], dxs);
                     pb[n] = g[n] * dlx;
                     g[n] *= a;
                 }
-                const float ddelta = group_sum<G>(dd);
+                const float ddelta = group_sum<G>(fmaf(xv, dxs, dd));
                 const float dxv = fmaf(delta[j], group_sum<G>(dxs), fmaf(dy, dsk, dxr * gv));
                 float ddtv = ddelta;
                 if constexpr (SP) ddtv *= sigmoid(E::widen(dr[j]));
