@@ -374,8 +374,9 @@ R2L_API r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream);
 /*
  * r2l_sidecar_tune -- for the four projections of a call with these
  * arguments, times hipBLASLt's candidate algorithms on `stream` and keeps the
- * fastest for every later r2l_sidecar_forward with the same shapes (process-
- * wide, per device). Call it once before serving or graph capture: it
+ * fastest (the library's first choice unless another is at least 5% faster)
+ * for every later r2l_sidecar_forward with the same shapes (process-wide,
+ * per device). Call it once before serving or graph capture: it
  * synchronizes the stream, and it overwrites the workspace (never hidden or
  * out, except that when the out-projection's rows do not fit the workspace's
  * in-projection rows it is timed in out itself, or, when out is hidden, not

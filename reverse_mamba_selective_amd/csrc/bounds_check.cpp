@@ -594,9 +594,16 @@ void check_conv(Checker &ck, const Launch &l, const int32_t *cu_host) {
         const int64_t lo = static_cast<int64_t>(bg.c) * kConvTokens;
         if (lo >= len) continue;
         const int64_t hi = lo + kConvTokens < len ? lo + kConvTokens : len;
-        const int64_t d0 = static_cast<int64_t>(bg.tile) * kWG;
-        const int64_t d1 = (d0 + kWG < p.D ? d0 + kWG : p.D) - 1;   // last active channel
+        const int64_t V = conv_lane_channels(static_cast<int>(es));   // channels per lane
+        if (p.D % V) return ck.fail("conv: %lld channels, not a multiple of %lld per lane",
+                                    (long long)p.D, (long long)V);
+        const int64_t d0 = static_cast<int64_t>(bg.tile) * kWG * V;
+        const int64_t d1 = (d0 + kWG * V < p.D ? d0 + kWG * V : p.D) - 1;   // last active channel
         if (d0 > d1) continue;
+        // 8-byte accesses: every lane's run starts 8-byte aligned
+        if ((U(p.x) + ((s0 + lo) * p.xs + d0) * es) % 8 || (U(p.u) + ((s0 + lo) * p.us + d0) * es) % 8 ||
+            (p.xs * es) % 8 || (p.us * es) % 8)
+            return ck.fail("conv: an 8-byte access is not 8-byte aligned");
         for (int64_t d : {d0, d1}) {
             ck.access("conv_w", rw, U(p.w) + d * p.K * 4, p.K * 4);
             if (rb) ck.access("conv_b", rb, U(p.b) + d * 4, 4);

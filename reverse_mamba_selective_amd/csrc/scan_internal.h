@@ -87,6 +87,8 @@ struct SegParams {
 // channels).
 constexpr int kConvTokens = 16;
 constexpr int kConvMaxTaps = 4;
+// channels one conv lane covers: one 8-byte access (4 bf16 or 2 fp32)
+__host__ __device__ constexpr int conv_lane_channels(int elem_bytes) { return 8 / elem_bytes; }
 struct ConvParams {
     int64_t seqlen;              // dense tokens per sequence (cu_seqlens == nullptr)
     const int32_t *cu_seqlens;

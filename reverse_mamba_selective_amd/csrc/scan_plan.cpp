@@ -429,7 +429,8 @@ int build_sidecar_launches(const r2l_sidecar_args *a, const SidecarPlan &sp,
         c.K = a->d_conv;
         const int64_t maxlen = a->cu_seqlens ? a->max_seqlen : a->seqlen;
         c.nchunks = static_cast<int32_t>(std::max<int64_t>((maxlen + kConvTokens - 1) / kConvTokens, 1));
-        c.tiles = static_cast<int32_t>((di + kWG - 1) / kWG);
+        const int64_t lane_ch = conv_lane_channels(a->dtype == R2L_DTYPE_BF16 ? 2 : 4);
+        c.tiles = static_cast<int32_t>((di + kWG * lane_ch - 1) / (kWG * lane_ch));
         c.nblocks = a->batch * c.nchunks * c.tiles;
         c.x = xz; c.xs = 2 * di;
         c.w = a->conv_w;

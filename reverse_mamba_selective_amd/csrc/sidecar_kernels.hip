@@ -7,10 +7,10 @@
 //
 // The conv of the reversed sequence is, in the original order, an
 // anti-causal conv: tap K-1-j weighs the token j positions to the right. A
-// lane owns one channel of a chunk of kConvTokens tokens: it issues the loads
-// of the chunk and its K-1 halo together (the conv is bound by memory
-// latency otherwise), then computes the chunk; a wave reads 64 consecutive
-// channels of a token row.
+// lane owns 8 bytes of channels (4 bf16 or 2 fp32) of a chunk of
+// kConvTokens tokens: it issues the loads of the chunk and its halo together
+// (the conv is bound by memory latency otherwise), then computes the chunk;
+// a wave moves 512 consecutive bytes of a token row per access.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,6 +26,7 @@ template <typename T>
 __global__ __launch_bounds__(kWG) void conv_silu_kernel(const ConvParams p) {
     using E = Elem<T>;
     constexpr int CT = kConvTokens, W = kConvTokens + kConvMaxTaps - 1;
+    constexpr int V = conv_lane_channels(sizeof(T));      // channels per lane, one 8-byte access
     const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
     if (!bg.valid) return;
     const int64_t b = bg.b;
@@ -39,31 +40,56 @@ __global__ __launch_bounds__(kWG) void conv_silu_kernel(const ConvParams p) {
     }
     const int64_t lo = static_cast<int64_t>(bg.c) * CT;
     if (lo >= len) return;
-    const int64_t d = static_cast<int64_t>(bg.tile) * kWG + threadIdx.x;
-    if (d >= p.D) return;
+    const int64_t d0 = (static_cast<int64_t>(bg.tile) * kWG + threadIdx.x) * V;
+    if (d0 >= p.D) return;                  // D is a multiple of V
 
-    // w_eff[j] weighs x[t + j]; taps past K are zero
-    float w[kConvMaxTaps];
+    // w[c][j] weighs x[t + j] of channel d0 + c; taps past K are zero
+    float w[V][kConvMaxTaps], bias[V];
 #pragma unroll
-    for (int j = 0; j < kConvMaxTaps; ++j) w[j] = j < p.K ? p.w[d * p.K + (p.K - 1 - j)] : 0.0f;
-    const float bias = p.b ? p.b[d] : 0.0f;
-    const T *x = static_cast<const T *>(p.x) + (s0 + lo) * p.xs + d;
-    T *u = static_cast<T *>(p.u) + (s0 + lo) * p.us + d;
+    for (int c = 0; c < V; ++c) {
+#pragma unroll
+        for (int j = 0; j < kConvMaxTaps; ++j)
+            w[c][j] = j < p.K ? p.w[(d0 + c) * p.K + (p.K - 1 - j)] : 0.0f;
+        bias[c] = p.b ? p.b[d0 + c] : 0.0f;
+    }
+    const T *x = static_cast<const T *>(p.x) + (s0 + lo) * p.xs + d0;
+    T *u = static_cast<T *>(p.u) + (s0 + lo) * p.us + d0;
     const int64_t n = len - lo;   // tokens of the sequence from lo on (>= 1)
 
-    // every input of the chunk and its halo first (independent loads in
-    // flight together), zero past the sequence
-    float v[W];
+    // every input of the chunk and its halo first (independent 8-byte loads
+    // in flight together), zero past the sequence
+    uint2 v[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) v[i] = i < n ? E::ld(x + i * p.xs) : 0.0f;
+    for (int i = 0; i < W; ++i)
+        v[i] = i < n ? *reinterpret_cast<const uint2 *>(x + i * p.xs) : make_uint2(0u, 0u);
+    auto elem = [&](const uint2 &q, int c) {   // channel c of a loaded run
+        const uint32_t word = c * static_cast<int>(sizeof(T)) < 4 ? q.x : q.y;
+        if constexpr (sizeof(T) == 2)
+            return __uint_as_float((c & 1) ? (word & 0xFFFF0000u) : (word << 16));
+        else
+            return __uint_as_float(word);
+    };
 #pragma unroll
     for (int i = 0; i < CT; ++i) {
         if (i >= n) break;
-        float acc = bias;
+        float o[V];
 #pragma unroll
-        for (int j = 0; j < kConvMaxTaps; ++j) acc = fmaf(w[j], v[i + j], acc);
-        // SiLU(v) = v / (1 + e^-v)
-        E::st(u + i * p.us, acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * kLog2e)));
+        for (int c = 0; c < V; ++c) {
+            float acc = bias[c];
+#pragma unroll
+            for (int j = 0; j < kConvMaxTaps; ++j) acc = fmaf(w[c][j], elem(v[i + j], c), acc);
+            // SiLU(v) = v / (1 + e^-v)
+            o[c] = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * kLog2e));
+        }
+        uint2 q;
+        if constexpr (sizeof(T) == 2) {
+            q.x = static_cast<uint32_t>(E::pack(o[0])) | (static_cast<uint32_t>(E::pack(o[1])) << 16);
+            q.y = static_cast<uint32_t>(E::pack(o[2])) | (static_cast<uint32_t>(E::pack(o[3])) << 16);
+        } else {
+            q.x = __float_as_uint(o[0]);
+            q.y = __float_as_uint(o[1]);
+        }
+        *reinterpret_cast<uint2 *>(u + i * p.us) = q;
     }
 }
 
