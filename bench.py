@@ -482,6 +482,71 @@ class Prefill(Workload):
     parity_spec = ("y", "bf16", 2e-2, "y of the sampled sequences (first buffer set)")
 
 
+class PrefillBackward(Prefill):
+    """The backward of the prefill-shape reverse scan (8 x 4096 x 4096, bf16, out = y):
+    the training shape of the R2L stream at the expanded width, all gradients."""
+    name = "prefill_backward_bf16_b8_L4096_D4096_N16"
+
+    def setup(self, torch, r2l):
+        import numpy as np
+        super().setup(torch, r2l)
+        tok, N = self.B * self.L, 16
+        g = self.g
+        view = lambda t: t.view(self.B, self.L, -1)   # noqa: E731
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(7103)
+        self.dout = torch.randn((tok, self.D), generator=gen, device="cuda").to(torch.bfloat16)
+        # x, dt, dout in and dx, ddt out (bf16); Bm, Cm in (bf16) and dBm, dCm out (fp32);
+        # A, Dskip in and dA, dDskip out
+        self.bytes_per_launch = (tok * self.D * 2 * 5 + tok * N * (2 * 2 + 4 * 2) +
+                                 self.D * N * 4 * 2 + self.D * 4 * 2)
+        self.alu_per_launch = self.tc_per_launch * bwd_alu_ops_per_tc()
+        self.R = 1   # 1.3 GB of inputs and outputs per call: HBM-resident, not cache-resident
+        self.bcall = r2l.bind_backward(view(g["x"]), view(g["dt"]), view(g["Bm"]), view(g["Cm"]),
+                                       g["A"], g["Dskip"], dout=view(self.dout))
+        self.calls = [self.bcall]
+        self.step_calls = [[self.bcall]]
+        self.measure = [dict(label="r2l_scan_backward", calls=self.calls,
+                             bytes=self.bytes_per_launch, alu=self.alu_per_launch,
+                             tc=self.tc_per_launch)]
+        self.config = {"workload": self.name, "batch": self.B, "seqlen": self.L, "D": self.D,
+                       "N": 16, "in_dtype": "bf16", "state_dtype": "fp32", "res": None,
+                       "op": "r2l_scan_backward", "grads": ["dx", "ddt", "dBm", "dCm", "dA",
+                                                            "dDskip", "dh_in"],
+                       "parallelism": "single_gpu"}
+
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
+        import numpy as np
+        import oracle
+        torch = self.torch
+        L, D = self.L, self.D
+        tc, secs, n = 0, 0.0, 0
+        grads = self.bcall.grads
+        for b in range(self.B):     # whole sequences, until the budget is spent
+            if secs >= budget_s:
+                break
+            rows = slice(b * L, (b + 1) * L)
+            host = lambda t: t[rows].float().cpu().numpy()   # noqa: E731
+            t = {}
+            ref = oracle.selective_scan_backward(
+                host(self.g["x"]), host(self.g["dt"]), host(self.g["Bm"]), host(self.g["Cm"]),
+                self.g["A"].cpu().numpy(), self.g["Dskip"].cpu().numpy(), reverse=True,
+                dout=host(self.dout), batch=1, seqlen=L, timing=t, nthreads=nthreads)
+            if parity is not None:
+                parity.add(grads["dx"].reshape(-1, D)[rows].float().cpu().numpy(), ref["dx"])
+                parity.add(grads["ddt"].reshape(-1, D)[rows].float().cpu().numpy(), ref["ddt"])
+            secs += t["seconds"]
+            tc += L * D
+            n += 1
+        return {"value": tc / secs, "unit": "tokens*channels/s",
+                "cores": nthreads or oracle.max_threads(), "kind": "oracle",
+                "sample": "%d of the %d sequences (%d token-channels), %.1f s of oracle time"
+                          % (n, self.B, tc, secs)}
+
+    parity_spec = ("dx, ddt", "bf16", 2e-2,
+                   "dx and ddt of the sampled sequences vs the oracle's fp64 backward")
+
+
 class RaggedServing(Workload):
     """256 ragged blocks of U{16..64} tokens at D = 4096, bf16: the reverse scan over
     the active blocks and block_commit_state over the committed blocks."""
@@ -1007,7 +1072,8 @@ SERVING_KEY = 107
 
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
              "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward,
-             "bidir": DenoiseBidir, "sidecar": DenoiseSidecar, "serving": ServingStep}
+             "bidir": DenoiseBidir, "sidecar": DenoiseSidecar, "serving": ServingStep,
+             "prefill_bwd": PrefillBackward}
 
 
 def main():

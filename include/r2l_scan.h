@@ -211,8 +211,10 @@ R2L_API r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t
  * Gradients of r2l_scan, for training the R2L stream (the pages train the
  * sidecar jointly with the backbone, or, plug-in, only the sidecar and s).
  * The forward call is described by the same r2l_scan_args (x, dt, Bm, Cm, A,
- * Dskip, h_in, res, s, delta_softplus, layout; out, h_out, chunk_tokens,
- * state_split and the workspace fields are not read). With a residual,
+ * Dskip, h_in, res, s, delta_softplus, layout; out, h_out, state_split and the
+ * workspace fields are not read). chunk_tokens is the planning hint of the
+ * backward's forward state pass (rounded up to a multiple of 8 tokens; the
+ * same meaning of > 0, < 0 and 0 as above). With a residual,
  * dL/dy = s * dout; without, dL/dy = dout. A separate residual's gradient is
  * dout itself and is not written; when the residual is x, dx includes dout.
  *

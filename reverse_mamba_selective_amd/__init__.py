@@ -532,15 +532,17 @@ def prefix_scan_backward(x, dt, Bm, Cm, A, Dskip=None, **kw):
 
 def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seqlens=None,
                       max_seqlen=None, h_in=None, res=None, s=0.0, delta_softplus=True,
-                      grads=GRADS, out=None, workspace=None, _bind=False, _reverse=True):
+                      grads=GRADS, out=None, workspace=None, chunk_tokens=0, _bind=False,
+                      _reverse=True):
     """Gradients of ``r2l_scan`` (same forward arguments) for ``dout`` = dL/dout
     and ``dh_out`` = dL/dh_out. Returns a dict of the names in ``grads``: dx,
     ddt (like x), dBm, dCm (fp32, shaped like Bm), dA [D, N], dDskip [D],
     dh_in [batch, D, N], ds [1] (with a residual only). ``out`` may hold
     preallocated tensors for some of them. A separate residual's gradient is
-    dout itself; when res is x, dx includes it."""
+    dout itself; when res is x, dx includes it. ``chunk_tokens`` is the
+    planning hint of the backward's state pass (0: the library chooses)."""
     a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, None, res, s, None,
-              delta_softplus, 0, 0)
+              delta_softplus, chunk_tokens, 0)
     D, N = int(a.dim), int(a.dstate)
     outs = dict(out or {})
     wanted = [n for n in grads if n != "ds" or res is not None]

@@ -215,10 +215,15 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
                 for (int lane = 0; lane < kWG; ++lane) {
                     const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
                     if (!lg.active) continue;
-                    const uintptr_t a = U(p.ckpt) +
-                        ((ckpt_row(bg.b, sq.s0p, pos) * p.D + lg.d) * kN + lg.sub * NS) * 4;
+                    const int64_t row = ckpt_row(bg.b, sq.s0p, static_cast<int64_t>(bg.c) * p.chunk_len + pos);
+                    const uintptr_t a = U(p.ckpt) + ((row * p.D + lg.d) * kN + lg.sub * NS) * 4;
                     ck.access("checkpoint", ck.region_of(p.ckpt), a, NS * 4);
                     ck.wrote(a, NS * 4);
+                    if (p.ckpt_s && lg.sub == 0) {
+                        const uintptr_t as = U(p.ckpt_s) + (row * p.D + lg.d) * 4;
+                        ck.access("checkpoint delta sum", ck.region_of(p.ckpt_s), as, 4);
+                        ck.wrote(as, 4);
+                    }
                 }
         if (ntok > 0)
             for (int j = 0; j < kPrefetch; ++j) load_pos(prefetch_pos(j, ntok));
@@ -394,10 +399,22 @@ void check_backward(Checker &ck, const Launch &l, const int32_t *cu_host) {
             }
             for (int lane = 0; lane < kWG; ++lane) {
                 const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
-                const uintptr_t a = U(p.ckpt) +
-                    ((ckpt_row(bg.b, sq.s0p, gpos) * p.D + lg.d) * kN + lg.sub * NS) * 4;
+                const int64_t row = ckpt_row(bg.b, sq.s0p, gpos);
+                const uintptr_t a = U(p.ckpt) + ((row * p.D + lg.d) * kN + lg.sub * NS) * 4;
                 ck.access("checkpoint", rCk, a, NS * 4);
                 ck.read_written("checkpoint", a, NS * 4);
+                if (p.Hc) {   // chunked phase 1: the chunk's entry state and the delta sum
+                    if (p.chunk_len <= 0 || p.chunk_len % K)
+                        return ck.fail("chunk length %d is not a multiple of the group", p.chunk_len);
+                    const int64_t c = gpos / p.chunk_len;
+                    if (c >= p.nchunks) return ck.fail("group %d past the last chunk", gpos);
+                    const uintptr_t ah = U(p.Hc) + (((bg.b * p.nchunks + c) * p.D + lg.d) * kN + lg.sub * NS) * 4;
+                    ck.access("chunk entry state", ck.region_of(p.Hc), ah, NS * 4);
+                    ck.read_written("chunk entry state", ah, NS * 4);
+                    const uintptr_t as = U(p.ckpt_s) + (row * p.D + lg.d) * 4;
+                    ck.access("checkpoint delta sum", ck.region_of(p.ckpt_s), as, 4);
+                    ck.read_written("checkpoint delta sum", as, 4);
+                }
             }
         }
         // Bm / Cm staging: the last tile first, then each earlier (full) tile
@@ -471,11 +488,18 @@ r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r
     add("ds", g->ds, 4);
     add("cu_seqlens", a->cu_seqlens, static_cast<uint64_t>((a->batch + 1) * 4));
     const char *ws = static_cast<const char *>(g->workspace);
-    const size_t offs[] = {pl.off_ck, pl.off_B, pl.off_C, pl.off_A, pl.off_D, pl.off_S, pl.ws_bytes};
+    const size_t end_S = pl.chunked ? pl.off_Q : pl.ws_bytes;
+    const size_t offs[] = {pl.off_ck, pl.off_B, pl.off_C, pl.off_A, pl.off_D, pl.off_S, end_S};
     const char *names[] = {"workspace checkpoints", "workspace dBm partials", "workspace dCm partials",
                            "workspace dA partials", "workspace dDskip partials", "workspace ds partials"};
     for (int i = 0; i < 6; ++i)
         if (ws) add(names[i], ws + offs[i], offs[i + 1] - offs[i]);
+    if (ws && pl.chunked) {
+        const size_t co[] = {pl.off_Q, pl.off_Sc, pl.off_H, pl.off_cks, pl.ws_bytes};
+        const char *cn[] = {"workspace chunk states", "workspace chunk delta sums",
+                            "workspace chunk entry states", "workspace checkpoint delta sums"};
+        for (int i = 0; i < 4; ++i) add(cn[i], ws + co[i], co[i + 1] - co[i]);
+    }
     Checker ck(std::move(regs), rep);
     ck.set_workspace(g->workspace, pl.ws_bytes);
     Launch ls[kMaxBwdLaunches];
@@ -490,6 +514,9 @@ r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r
             case Launch::Backward:
                 if (ls[i].bwd.bc_vec) ++rep->vector_staging;
                 check_backward(ck, ls[i], cu_host);
+                break;
+            case Launch::Carry:
+                check_carry(ck, ls[i], cu_host);
                 break;
             case Launch::Sum:
                 check_sum(ck, ls[i]);

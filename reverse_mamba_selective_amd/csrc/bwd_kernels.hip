@@ -14,7 +14,11 @@
 //
 // Mapping onto CDNA4:
 //  * Phase 1 (the forward segment kernel, state only) stored the state
-//    entering every group of kCkptTokens visited positions. Here one workgroup
+//    entering every group of kCkptTokens visited positions. When the shape has
+//    too few channels to fill the machine, phase 1 scans chunks of the
+//    sequence from zero in parallel; by linearity the true state entering a
+//    group is its chunk-local checkpoint plus exp(A * sum of Delta since the
+//    chunk's start) times the state entering the chunk. Here one workgroup
 //    owns (sequence, tile of kWG / G channels), G lanes per channel holding
 //    kN / G states each, and walks the groups backwards: it recomputes the
 //    group's states in registers from its checkpoint, then runs the adjoint
@@ -156,9 +160,14 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
     };
 
     // per-token inputs of one group (positions past its end repeat its last
-    // one) and the state entering it (its checkpoint)
+    // one) and the state entering it (its checkpoint; chunked phase 1: the
+    // chunk-local checkpoint, the chunk's Delta sum up to it and the state
+    // entering the chunk, combined when the group is consumed)
     R nx[K], nd[K], ng[K];
-    float nck[NS];
+    float nck[NS], nH[NS], nS = 0.0f;
+    const bool chunked = p.Hc != nullptr;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) nH[n] = 0.0f;
     auto load_group = [&](int gpos, int gcnt) {
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -167,9 +176,17 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             nd[j] = E::bload(rd, doff, row * drb);
             ng[j] = E::bload(rg, doff, row * grb);
         }
-        const float *cp = p.ckpt + (ckpt_row(b, sq.s0p, gpos) * p.D + dl) * kN + sub * NS;
+        const int64_t ckr = ckpt_row(b, sq.s0p, gpos);
+        const float *cp = p.ckpt + (ckr * p.D + dl) * kN + sub * NS;
 #pragma unroll
         for (int n = 0; n < NS; ++n) nck[n] = cp[n];
+        if (chunked) {
+            const int64_t c = gpos / p.chunk_len;
+            const float *hp = p.Hc + ((b * p.nchunks + c) * p.D + dl) * kN + sub * NS;
+#pragma unroll
+            for (int n = 0; n < NS; ++n) nH[n] = hp[n];
+            nS = p.ckpt_s[ckr * p.D + dl];
+        }
     };
 
     // tiles (and the groups inside them) from the last visited to the first
@@ -202,8 +219,14 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 dr[j] = nd[j];
                 gr[j] = ng[j];
             }
+            if (chunked) {   // the chunk's entry state decayed over the chunk so far
 #pragma unroll
-            for (int n = 0; n < NS; ++n) hck[n] = nck[n];
+                for (int n = 0; n < NS; ++n)
+                    hck[n] = fmaf(__builtin_amdgcn_exp2f(a2[n] * nS), nH[n], nck[n]);
+            } else {
+#pragma unroll
+                for (int n = 0; n < NS; ++n) hck[n] = nck[n];
+            }
             if (gpos > 0) load_group(gpos - K, K);
             float (*rd_)[K][NBC] = red[gi & 1];
 

@@ -547,7 +547,8 @@ r2l_status check_backward(const r2l_scan_args *a, const r2l_grad_args *g, const 
     if (pl.ws_bytes > 0 && (!g->workspace || g->workspace_bytes < pl.ws_bytes))
         return fail(R2L_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", pl.ws_bytes,
                     g->workspace ? g->workspace_bytes : (size_t)0);
-    if (a->batch * pl.tiles > INT32_MAX - 8) return fail(R2L_ERR_UNSUPPORTED, "grid too large");
+    if (a->batch * pl.tiles > INT32_MAX - 8 || a->batch * pl.nchunks * pl.fwd_tiles > INT32_MAX - 8)
+        return fail(R2L_ERR_UNSUPPORTED, "grid too large");
 
     const struct { const void *p; uintptr_t al; const char *n; } al[] = {
         {a->x, (uintptr_t)es, "x"},       {a->dt, (uintptr_t)es, "dt"},     {a->Bm, (uintptr_t)es, "Bm"},

@@ -68,9 +68,13 @@ struct SegParams {
     int32_t skip_c0;    // readout pass: chunk 0 was written by the chunk pass
     int32_t skip_last;  // chunk pass: skip each sequence's last chunk (c > 0)
 
-    // backward, phase 1 (state-only, unchunked): the state before every
-    // kCkptTokens-th visited position, at ckpt + (ckpt_row * D + d) * kN
+    // backward, phase 1 (state only): the state before every kCkptTokens-th
+    // visited position of the sequence, at ckpt + (ckpt_row * D + d) * kN.
+    // A chunked phase 1 scans each chunk from zero: its checkpoints are
+    // chunk-local, and ckpt_s (when set) receives, at ckpt_row * D + d, the
+    // sum of Delta from the chunk's start to the checkpoint.
     float *ckpt;
+    float *ckpt_s;
 
     // bidirectional scan: fp32 [packed tokens, D] rows of y written by the
     // first pass (kModeWs) and added by the second (kModeAdd)
@@ -144,6 +148,12 @@ struct BwdParams {
     int32_t want_ds;             // accumulate dout * y for ds
 
     const float *ckpt;           // phase 1's checkpoints
+    // chunked phase 1 (Hc != nullptr): the true state entering a group of
+    // chunk c = pos / chunk_len is ckpt + exp(A * ckpt_s) * Hc[b][c], Hc the
+    // state entering the chunk ([batch][nchunks][D][kN], from the carry)
+    int32_t chunk_len, nchunks;
+    const float *Hc;
+    const float *ckpt_s;
     const void *dout; int64_t gs, gbs;
     const float *dh_out;         // [batch, D, kN] or nullptr
     void *dx;  int64_t dxs, dxbs;     // or nullptr

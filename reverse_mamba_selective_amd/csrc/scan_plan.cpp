@@ -466,6 +466,28 @@ BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
     pl.fwd_tiles = (a->dim + kWG - 1) / kWG;
     pl.tokens = tokens_of(a);
     pl.ck_rows = ckpt_rows(pl.tokens, a->batch);
+    // Phase 1 runs one lane per channel; a shape with too few channels to
+    // fill the machine scans chunks from zero in parallel (chunks are whole
+    // checkpoint groups) and phase 2 adds each chunk's entry state to its
+    // checkpoints. Phase 2 itself is not chunked.
+    const int64_t maxlen = max_len_of(a);
+    int64_t chunk = 0;
+    if (a->chunk_tokens > 0) {
+        chunk = a->chunk_tokens;
+    } else if (a->chunk_tokens == 0 && maxlen > 0) {
+        const int64_t lanes = std::max<int64_t>(a->batch * a->dim, 1);
+        const int64_t fill = (kTargetLanes + lanes - 1) / lanes;
+        if (fill > 1) chunk = std::max<int64_t>(kMinChunk, (maxlen + fill - 1) / fill);
+    }
+    chunk = (chunk + kCkptTokens - 1) / kCkptTokens * kCkptTokens;
+    if (chunk > 0 && chunk < maxlen) {
+        pl.chunked = true;
+        pl.chunk_len = chunk;
+        pl.nchunks = (maxlen + chunk - 1) / chunk;
+    } else {
+        pl.chunk_len = std::max<int64_t>(maxlen, 1);
+        pl.nchunks = 1;
+    }
     if (a->res) {
         const bool is_x = a->res == a->x && a->res_stride == a->x_stride &&
                           eff_bstride(a, a->res_batch_stride, a->res_stride) ==
@@ -486,6 +508,13 @@ BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
     pl.off_A = take(g->dA ? B * D * kN * 4 : 0);
     pl.off_D = take(g->dDskip ? B * D * 4 : 0);
     pl.off_S = take(g->ds ? B * tiles * 4 : 0);
+    if (pl.chunked) {
+        const size_t nc = static_cast<size_t>(pl.nchunks);
+        pl.off_Q = take(B * nc * D * kN * 4);
+        pl.off_Sc = take(B * nc * D * 4);
+        pl.off_H = take(B * nc * D * kN * 4);
+        pl.off_cks = take(static_cast<size_t>(pl.ck_rows) * D * 4);
+    }
     pl.ws_bytes = off;
     return pl;
 }
@@ -498,23 +527,33 @@ int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args
     float *pB = at(pl.off_B, g->dBm != nullptr), *pC = at(pl.off_C, g->dCm != nullptr);
     float *pA = at(pl.off_A, g->dA != nullptr), *pD = at(pl.off_D, g->dDskip != nullptr);
     float *pS = at(pl.off_S, g->ds != nullptr);
+    const bool chunked = pl.chunked && pl.tokens > 0;
+    float *Q = at(pl.off_Q, chunked), *Sc = at(pl.off_Sc, chunked);
+    float *H = at(pl.off_H, chunked), *cks = at(pl.off_cks, chunked);
     const int64_t D = a->dim;
     int n = 0;
 
     if (a->batch > 0) {
-        // phase 1: the forward state scan, one lane per channel, unchunked, with checkpoints
+        // phase 1: the forward state scan, one lane per channel, with checkpoints
         if (pl.tokens > 0) {
             Plan fp;
             fp.G = 1;
-            fp.chunk_len = std::max<int64_t>(max_len_of(a), 1);
-            fp.nchunks = 1;
+            fp.chunk_len = pl.chunk_len;
+            fp.nchunks = pl.nchunks;
             fp.tiles = pl.fwd_tiles;
             SegParams p = base_params(a, fp);
-            p.hin = a->h_in; p.hin_b = D * kN; p.hin_c = 0;
             p.res = nullptr;
             p.out = nullptr;
             p.ckpt = ck;
             p.bc_vec = bc_vector_ok(a, false) ? 1 : 0;
+            if (chunked) {   // every chunk from zero: local checkpoints, Q, Delta sums
+                p.hin = nullptr;
+                p.hfin = Q; p.hfin_b = pl.nchunks * D * kN; p.hfin_c = D * kN;
+                p.sdelta = Sc; p.sd_b = pl.nchunks * D; p.sd_c = D;
+                p.ckpt_s = cks;
+            } else {
+                p.hin = a->h_in; p.hin_b = D * kN; p.hin_c = 0;
+            }
             Launch l{};
             l.kind = Launch::Segment;
             l.reverse = reverse;
@@ -523,6 +562,26 @@ int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args
             l.mode = kModeState;
             l.seg = p;
             out[n++] = l;
+        }
+        if (chunked) {   // the state entering every chunk (h_in before chunk 0)
+            Launch c{};
+            c.kind = Launch::Carry;
+            c.reverse = reverse;
+            c.dtype = a->dtype;
+            c.carry.batch = a->batch;
+            c.carry.seqlen = is_ragged(a) ? 0 : a->seqlen;
+            c.carry.cu_seqlens = a->cu_seqlens;
+            c.carry.D = D;
+            c.carry.chunk_len = static_cast<int32_t>(pl.chunk_len);
+            c.carry.nchunks = static_cast<int32_t>(pl.nchunks);
+            c.carry.A = a->A;
+            c.carry.hin = a->h_in;
+            c.carry.c0_seeded = 0;
+            c.carry.Q = Q;
+            c.carry.S = Sc;
+            c.carry.Hc = H;
+            c.carry.hout = nullptr;
+            out[n++] = c;
         }
         // phase 2: the adjoint
         BwdParams q{};
@@ -544,6 +603,12 @@ int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args
         q.dxres = pl.res_kind == 1 ? 1.0f : 0.0f;
         q.want_ds = g->ds ? 1 : 0;
         q.ckpt = ck;
+        if (chunked) {
+            q.chunk_len = static_cast<int32_t>(pl.chunk_len);
+            q.nchunks = static_cast<int32_t>(pl.nchunks);
+            q.Hc = H;
+            q.ckpt_s = cks;
+        }
         q.dout = g->dout; q.gs = g->dout_stride;
         q.gbs = eff_bstride(a, g->dout_batch_stride, g->dout_stride);
         q.dh_out = g->dh_out;

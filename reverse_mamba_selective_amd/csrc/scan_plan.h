@@ -40,16 +40,22 @@ struct Launch {
 };
 
 // The backward of r2l_scan: phase 1 (state-only segment scan writing
-// checkpoints), phase 2 (the adjoint) and one launch of ordered sums.
-constexpr int kMaxBwdLaunches = 3;
+// checkpoints; when chunked, from zero per chunk, then the carry of the
+// chunk entry states), phase 2 (the adjoint) and one launch of ordered sums.
+constexpr int kMaxBwdLaunches = 4;
 struct BwdPlan {
     int G = 4;               // lanes per channel in phase 2
     int64_t tiles = 0;       // phase-2 channel tiles per sequence
     int64_t fwd_tiles = 0;   // phase-1 tiles (one lane per channel)
     int64_t tokens = 0;
     int64_t ck_rows = 0;
+    bool chunked = false;    // phase 1 cut into chunks (a multiple of kCkptTokens)
+    int64_t chunk_len = 0, nchunks = 1;
     size_t ws_bytes = 0;
     size_t off_ck = 0, off_B = 0, off_C = 0, off_A = 0, off_D = 0, off_S = 0;
+    // chunked phase 1: local final states Q, Delta sums, entry states H
+    // ([batch][nchunks][D](x kN)) and the checkpoints' Delta sums [ck_rows][D]
+    size_t off_Q = 0, off_Sc = 0, off_H = 0, off_cks = 0;
     int res_kind = 0;        // 0: none, 1: the residual is x, 2: a separate residual
 };
 

@@ -199,13 +199,16 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     };
 
     // Backward phase 1: the state entering each group of kCkptTokens visited
-    // positions (the groups are the prefetch groups).
+    // positions (the groups are the prefetch groups; chunks are whole groups)
+    // and, in a chunked phase 1, the chunk's Delta sum up to it.
     static_assert(PF == kCkptTokens, "checkpoint groups are the prefetch groups");
     auto checkpoint = [&](int pos) {
         if (!p.ckpt || !lg.active) return;
-        float *cp = p.ckpt + (ckpt_row(b, sq.s0p, pos) * p.D + dl) * kN + sub * NS;
+        const int64_t row = ckpt_row(b, sq.s0p, static_cast<int64_t>(c) * p.chunk_len + pos);
+        float *cp = p.ckpt + (row * p.D + dl) * kN + sub * NS;
 #pragma unroll
         for (int j = 0; j < NS; ++j) cp[j] = h[j];
+        if (p.ckpt_s && sub == 0) p.ckpt_s[row * p.D + dl] = dsum;
     };
 
     // Start-up: the first tile's Bm/Cm rows are requested first (they gate

@@ -334,10 +334,52 @@ def test_backward_workspace_tracks_the_outputs():
     assert full > only_dx > 0   # checkpoints always; partial sums only when wanted
 
 
+BWD_CHUNKED = [
+    dict(lengths=[5, 0, 1, 64, 65, 130, 300], chunk=16),
+    dict(lengths=[5, 0, 1, 64, 65, 130, 300], chunk=13),    # rounded up to 16
+    dict(lengths=[7, 8, 9, 41], chunk=8),
+    dict(batch=2, seqlen=200, D=37, chunk=40),
+    dict(batch=2, seqlen=200, D=100, pad_row=8, pad_batch=40, chunk=64),
+    dict(batch=2, seqlen=1000, D=64, chunk=0),                # chunked by the planner
+]
+
+
+@pytest.mark.parametrize("case", range(len(BWD_CHUNKED)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_chunked_state_pass(case, dtype):
+    """Phase 1 cut into chunks scanned from zero, the carry of the chunk entry
+    states, and phase 2 reading them beside the chunk-local checkpoints."""
+    kw = dict(BWD_CHUNKED[case], dtype=dtype)
+    kw.setdefault("D", 64)
+    for res in ("none", "x"):
+        for reverse in (True, False):
+            rep = check_bwd(res=res, h_in=True, reverse=reverse, **kw)
+            assert rep.launches == 4   # phase 1, carry, phase 2, the sums
+    check_bwd(grads=("dx",), dh_out=False, **kw)
+
+
+def test_backward_chunk_plan():
+    """The planner chunks phase 1 only when there are too few channels, in
+    whole checkpoint groups; chunk_tokens < 0 keeps it whole."""
+    heap = FakeHeap()
+    heap.next = BASE + (1 << 40)
+    a, _ = make_args("scan", batch=2, seqlen=1000, D=64, chunk=0)
+    g = make_grad(a, heap)
+    chunked = _abi.backward_workspace_size(a, g)
+    a.chunk_tokens = -1
+    assert chunked > _abi.backward_workspace_size(a, g)
+    a, _ = make_args("scan", batch=64, seqlen=32, D=2048, chunk=0)
+    g = make_grad(a, heap)
+    auto = _abi.backward_workspace_size(a, g)
+    a.chunk_tokens = -1
+    assert auto == _abi.backward_workspace_size(a, g)
+
+
 def test_backward_benchmarked_shapes():
-    check_bwd(batch=64, seqlen=32, D=2048, res="x")
-    rep = check_bwd(batch=8, seqlen=4096, D=4096)
-    assert rep.launches == 3   # phase 1, phase 2, the sums (dBm, dCm, dA, dDskip: no residual, no ds)
+    rep = check_bwd(batch=64, seqlen=32, D=2048, res="x", chunk=0)
+    assert rep.launches == 3   # phase 1, phase 2, the sums: 131072 channels need no chunks
+    rep = check_bwd(batch=8, seqlen=4096, D=4096, chunk=0)
+    assert rep.launches == 4   # phase 1 in chunks, the carry, phase 2, the sums
 
 
 # ---- the bidirectional scan ---------------------------------------------------------

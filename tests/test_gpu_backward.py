@@ -47,7 +47,8 @@ def check_grad(name, got_t, ref, dtype):
         assert worst <= 1.0, "%s: an element is %.2f x (1 bf16 ulp + bound) off" % (name, worst)
 
 
-def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None, reverse=True):
+def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None, reverse=True,
+             chunk_tokens=0):
     dtype = dtype or inp.dtype
     B, D = inp.batch, inp.x.shape[1]
     rng = np.random.default_rng(seed)
@@ -77,7 +78,8 @@ def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None, re
     bwd = r2l.r2l_scan_backward if reverse else r2l.prefix_scan_backward
     g = bwd(x, **kw, dout=shaped(dev(dout_np, dtype)),
                               dh_out=dev32(dh_out_np) if with_dhout else None,
-                              h_in=dev32(h0) if with_hin else None, res=res, s=s)
+                              h_in=dev32(h0) if with_hin else None, res=res, s=s,
+                              chunk_tokens=chunk_tokens)
     torch.cuda.synchronize()
     for name in ("dx", "ddt") + FP32_GRADS:
         check_grad(name, g[name], ref[name], dtype)
@@ -108,6 +110,28 @@ def test_backward_ragged_edges(gpu, dtype, res_kind, reverse):
                  seed=33, reverse=reverse)
 
 
+@pytest.mark.parametrize("reverse", [True, False], ids=["r2l", "forward"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [8, 13, 40])
+def test_backward_chunked_state_pass(gpu, dtype, chunk, reverse):
+    """The forward state pass cut into chunks scanned from zero (13 rounds up
+    to 16 tokens: chunks are whole checkpoint groups), the carry of the chunk
+    entry states and phase 2's fix-up of the chunk-local checkpoints; sequences
+    of 0 to 300 tokens, h_in and dh_out given."""
+    lengths = [5, 0, 1, 64, 65, 130, 300, 9]
+    inp = synth.scan_inputs(41, lengths, D=100, dtype=dtype, dt_mean=-3.0)
+    for res_kind, with_hin in (("x", True), ("none", False)):
+        run_case(inp, False, res_kind, 0.0 if res_kind == "none" else 0.6, with_hin, True,
+                 seed=42, reverse=reverse, chunk_tokens=chunk)
+
+
+def test_backward_long_few_channels(gpu):
+    """Long sequences and few channels: the planner chunks the state pass
+    (3000 tokens, 64 channels: 256-token chunks)."""
+    inp = synth.scan_inputs(43, [3000, 1, 700], D=64, dtype="f32")
+    run_case(inp, False, "x", 0.3, with_hin=True, with_dhout=True, seed=44)
+
+
 def test_backward_gate_zero(gpu):
     """s = 0: dL/dy = 0, so only ds (and dx = dout when res is x) survive."""
     inp = synth.scan_inputs(34, [40, 3], D=72, dtype="f32")
@@ -136,11 +160,12 @@ def test_backward_is_deterministic(gpu):
               A=dev32(inp.A), Dskip=dev32(inp.Dskip),
               cu_seqlens=torch.from_numpy(inp.offsets.astype(np.int32)).cuda(), max_seqlen=90,
               dout=torch.randn_like(x), res=x, s=0.3)
-    a = r2l.r2l_scan_backward(x, **kw)
-    for _ in range(2):
-        b = r2l.r2l_scan_backward(x, **kw)
-        for k in a:
-            assert np.array_equal(bits(a[k]), bits(b[k])), k
+    for chunk in (0, 16):   # whole and chunked state pass
+        a = r2l.r2l_scan_backward(x, **kw, chunk_tokens=chunk)
+        for _ in range(2):
+            b = r2l.r2l_scan_backward(x, **kw, chunk_tokens=chunk)
+            for k in a:
+                assert np.array_equal(bits(a[k]), bits(b[k])), k
     torch.cuda.synchronize()
 
 
