@@ -57,6 +57,9 @@ __device__ __forceinline__ float sigmoid(float v) {
 // LDS permutes.
 template <int R, int NS>
 __device__ __forceinline__ void add_row_ror(float (&v)[NS]) {
+    // kept as a plain add: fused into the product that made v, the rotated
+    // copy would be the fma's addend, which DPP cannot supply (mov + fma)
+#pragma clang fp contract(off)
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int o = __builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0x120 + R, 0xF, 0xF, true);
@@ -73,7 +76,8 @@ __device__ __forceinline__ void row_channel_sum(float (&v)[kN / G]) {
     add_row_ror<8, NS>(v);
 }
 
-template <bool REV, typename T, int G, bool SP>
+// DS: accumulate dout * y for ds (the readout y is recomputed only then).
+template <bool REV, typename T, int G, bool SP, bool DS>
 __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
     constexpr int NS = kN / G;
     constexpr int K = kCkptTokens;
@@ -255,11 +259,13 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 const float xv = E::widen(xr[j]);
                 const float gv = E::widen(gr[j]);
                 const float dy = dys * gv;
-                float yp = 0.0f;
+                if constexpr (DS) {
+                    float yp = 0.0f;
 #pragma unroll
-                for (int n = 0; n < NS; ++n) yp = fmaf(row[kN + n], hs[j][n], yp);
-                const float y = fmaf(dsk, xv, group_sum<G>(yp));
-                dsum = fmaf(dsw * gv, y, dsum);
+                    for (int n = 0; n < NS; ++n) yp = fmaf(row[kN + n], hs[j][n], yp);
+                    const float y = fmaf(dsk, xv, group_sum<G>(yp));
+                    dsum = fmaf(dsw * gv, y, dsum);
+                }
                 dD = fmaf(dy, xv, dD);
                 const float dlx = delta[j] * xv;
                 float pb[NS], pc[NS];
@@ -388,19 +394,15 @@ __global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumBatch sb) {
     p.dst[i] = acc;
 }
 
+// 4 lanes per channel (2 would need 341 VGPRs: one wave per SIMD)
 template <bool REV, typename T, bool SP>
 hipError_t launch_bwd_g(int G, const BwdParams &p, hipStream_t stream) {
+    if (G != 4) return hipErrorInvalidValue;
     const int64_t grid = padded_grid(p.nblocks);
-    switch (G) {
-        case 2:
-            hipLaunchKernelGGL((bwd_kernel<REV, T, 2, SP>), dim3(grid), dim3(kWG), 0, stream, p);
-            break;
-        case 4:
-            hipLaunchKernelGGL((bwd_kernel<REV, T, 4, SP>), dim3(grid), dim3(kWG), 0, stream, p);
-            break;
-        default:
-            return hipErrorInvalidValue;
-    }
+    if (p.want_ds)
+        hipLaunchKernelGGL((bwd_kernel<REV, T, 4, SP, true>), dim3(grid), dim3(kWG), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_kernel<REV, T, 4, SP, false>), dim3(grid), dim3(kWG), 0, stream, p);
     return hipGetLastError();
 }
 
