@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one fp32 VALU instruction per lane per clock
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# issue slots one v_exp_f32 / v_log_f32 takes, measured on gfx950
+# issue slots one v_exp_f32 / v_log_f32 takes on gfx950 (an issue-rate micro-benchmark:
+# 2 VALU slots, not co-issued with FMAs)
 TRANS_SLOTS = float(os.environ.get("R2L_TRANS_SLOTS", "2"))
 
 
