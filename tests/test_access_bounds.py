@@ -568,6 +568,17 @@ def test_sidecar_benchmarked_shape():
     assert rep.launches == 6 and rep.vector_staging == 1
 
 
+def test_sidecar_projection_shapes():
+    """d_inner off the conv's channel tiles, dt_rank 8 to 232, ragged sequences,
+    conv chunks with tails."""
+    for kw in (dict(lengths=[31, 0, 1, 33, 64, 97], di=136, R=8),
+               dict(batch=3, seqlen=45, di=520, R=24, K=3),
+               dict(lengths=[5, 300, 2], di=1032, R=224, pad_row=8),
+               dict(batch=2, seqlen=70, di=512, R=96, K=1, bias=False),
+               dict(batch=2, seqlen=20, R=232)):
+        assert check_sidecar(**kw).launches == 6
+
+
 def test_sidecar_rejects_bad_arguments():
     a, cu = make_sidecar(batch=2, seqlen=16)
     assert _abi.check_access_sidecar(a, cu)[0] == _abi.R2L_OK

@@ -112,6 +112,32 @@ def test_sidecar_long_sequences_chunked_scan(gpu):
     check(h, w, 0.5, lengths, "f32", "chunked", dense=False)
 
 
+@pytest.mark.parametrize("di,R,K", [(520, 24, 3), (1032, 224, 4), (136, 8, 2)])
+def test_sidecar_projection_shapes_bf16(gpu, di, R, K):
+    """bf16 with d_inner off the conv's 1024-channel tiles, dt_rank 24, 224 and 8,
+    ragged sequences with conv-chunk tails."""
+    lengths = [31, 0, 1, 33, 64, 97]
+    w = synth.sidecar_weights(86 + R, 64, di, R, K=K, dtype="bf16")
+    h = synth.hidden_states(87, lengths, 64, "bf16")
+    check(h, w, 0.7, lengths, "bf16", "di %d R %d" % (di, R), dense=False)
+
+
+def test_sidecar_wide_dt_rank_bf16(gpu):
+    """bf16 with dt_rank 232 (an x-projection of 264 columns)."""
+    lengths = [20, 13]
+    w = synth.sidecar_weights(90, 64, 256, 232, dtype="bf16")
+    h = synth.hidden_states(91, lengths, 64, "bf16")
+    check(h, w, 0.4, lengths, "bf16", "R 232", dense=False)
+
+
+def test_sidecar_long_sequences_bf16(gpu):
+    """bf16, few channels and long sequences: the chunked scan inside the block."""
+    lengths = [2000, 1, 700]
+    w = synth.sidecar_weights(92, 64, 64, 8, dtype="bf16")
+    h = synth.hidden_states(93, lengths, 64, "bf16")
+    check(h, w, 0.5, lengths, "bf16", "chunked bf16", dense=False)
+
+
 def test_sidecar_gate_zero(gpu):
     lengths = [12, 7]
     w = synth.sidecar_weights(80, 64, 128, 8, dtype="bf16")
