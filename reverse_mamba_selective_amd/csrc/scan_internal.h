@@ -89,7 +89,7 @@ struct SegParams {
 // u[t,d] = SiLU(b[d] + sum_{j<K} w[d, K-1-j] * x[t+j, d]) within each
 // sequence. One workgroup per (sequence, chunk of kConvTokens, tile of kWG
 // channels).
-constexpr int kConvTokens = 16;
+constexpr int kConvTokens = 32;
 constexpr int kConvMaxTaps = 4;
 // channels one conv lane covers: one 8-byte access (4 bf16 or 2 fp32)
 __host__ __device__ constexpr int conv_lane_channels(int elem_bytes) { return 8 / elem_bytes; }
