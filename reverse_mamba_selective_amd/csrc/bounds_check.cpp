@@ -108,8 +108,10 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const Region *rR = reads_res ? ck.region_of(p.res) : nullptr;
     const Region *rBias = (l.mode & kModeBias) && p.dt_bias ? ck.region_of(p.dt_bias) : nullptr;
     const Region *rO = launch_readout && !to_ws ? ck.region_of(p.out) : nullptr;
-    const Region *rW = to_ws ? ck.region_of(p.yws) : nullptr;
-    const Region *rAdd = (l.mode & kModeAdd) ? ck.region_of(p.yadd) : nullptr;
+    // kModeLds: the bidirectional rows live in LDS (row < kBidirLdsTokens), not the workspace
+    const bool lrows = (l.mode & kModeLds) != 0;
+    const Region *rW = to_ws && !lrows ? ck.region_of(p.yws) : nullptr;
+    const Region *rAdd = (l.mode & kModeAdd) && !lrows ? ck.region_of(p.yadd) : nullptr;
 
     for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
         const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, bid);
@@ -177,6 +179,12 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
         // resource starts at the sequence's first packed row
         auto ws_row = [&](const char *what, const Region *reg, const float *base, int k, bool write) {
             const int row = seg_row(sg, k);
+            if (lrows) {   // ylds[row * kWG + thread]
+                if (row < 0 || row >= kBidirLdsTokens || row >= sq.len)
+                    return ck.fail("%s: LDS row %d outside 0..%d (block %lld)", what, row,
+                                   kBidirLdsTokens - 1, (long long)bid);
+                return;
+            }
             if (row < 0 || row >= sq.len)
                 return ck.fail("%s: row %d outside the sequence of %lld rows (block %lld)", what, row,
                                (long long)sq.len, (long long)bid);
@@ -581,7 +589,7 @@ r2l_status check_bidir_accesses(const r2l_scan_args *a, const r2l_dir_args *rev,
             Launch pass = l;
             pass.kind = Launch::Segment;
             pass.reverse = true;
-            pass.mode = kModeWs;
+            pass.mode = kModeWs | (l.mode & kModeLds);
             pass.seg = l.seg;
             if (pass.seg.bc_vec) ++rep->vector_staging;
             check_segment(ck, pass, cu_host);

@@ -270,7 +270,8 @@ r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
                 break;
             }
             case Launch::Bidir:
-                e = r2l::launch_bidir_fused(l.dtype, l.mode & r2l::kModeOutMask, l.seg, l.seg2,
+                e = r2l::launch_bidir_fused(l.dtype, l.mode & r2l::kModeOutMask,
+                                            (l.mode & r2l::kModeLds) != 0, l.seg, l.seg2,
                                             stream);
                 what = "bidirectional scan launch";
                 break;

@@ -28,6 +28,11 @@ constexpr int kModeAdd = 8;
 // state-only chunks of its plans).
 constexpr int kModeGate = 5;
 constexpr int kModeBias = 16;
+// The fused bidirectional launch over sequences of at most kBidirLdsTokens
+// tokens keeps the first pass's fp32 rows in LDS instead of the workspace
+// (each lane reads back only its own channel's rows).
+constexpr int kModeLds = 32;
+constexpr int kBidirLdsTokens = 32;
 
 // One launch of the segment kernel scans "segments": chunk c (in visiting
 // order) of sequence b, for a tile of kWG lanes. With G lanes per channel a
@@ -217,8 +222,8 @@ hipError_t launch_segment_scan(bool reverse, int dtype, int G, int mode,
 hipError_t launch_carry(const CarryParams &p, hipStream_t stream);
 // bidirectional scan: one launch running both passes (unchunked plans), or a
 // segment launch of one direction's chunked plan (modes kModeWs, kModeAdd | m)
-hipError_t launch_bidir_fused(int dtype, int out_mode, const SegParams &pr, const SegParams &pf,
-                              hipStream_t stream);
+hipError_t launch_bidir_fused(int dtype, int out_mode, bool lds_rows, const SegParams &pr,
+                              const SegParams &pf, hipStream_t stream);
 hipError_t launch_bidir_segment(bool reverse, int dtype, int mode, const SegParams &p,
                                 hipStream_t stream);
 hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream);

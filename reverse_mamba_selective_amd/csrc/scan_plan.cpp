@@ -306,6 +306,7 @@ int build_bidir_launches(const r2l_scan_args *a, const r2l_dir_args *rev, const 
         l.dtype = a->dtype;
         l.G = 1;
         l.mode = kModeAdd | out_mode(&f, pf);
+        if (bp.pl.chunk_len <= kBidirLdsTokens) l.mode |= kModeLds;   // the rows stay in LDS
         l.seg = pr;
         l.seg2 = pf;
         out[0] = l;

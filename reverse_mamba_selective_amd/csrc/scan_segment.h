@@ -31,9 +31,11 @@ using namespace dev;
 template <bool REV, typename T, int G, int MODE, bool SP>
 __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, const BlockGeom &bg,
                                              const SeqGeom &sq, const SegGeom &sg,
-                                             const float *hin) {
+                                             const float *hin, float *ylds = nullptr) {
     constexpr int OUT = MODE & kModeOutMask;     // what the readout writes
     constexpr bool ADD = (MODE & kModeAdd) != 0;  // y += an fp32 addend per token
+    // the fp32 rows (kModeWs / kModeAdd) at ylds[row * kWG + thread] in LDS
+    constexpr bool LROWS = (MODE & kModeLds) != 0;
     constexpr bool BIAS = (MODE & kModeBias) != 0;  // dt += dt_bias[d] before softplus
     constexpr bool READS_RES = OUT == kModeRes || OUT == kModeGate;
     constexpr bool READOUT = OUT != kModeState;
@@ -91,10 +93,10 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     // fp32 rows [packed token, D] of the workspace: y written (kModeWs) or the
     // addend read (kModeAdd), at the sequence's packed rows
     const uint32_t wrb = static_cast<uint32_t>(p.D) * 4u, woff = dl * 4u;
-    const auto rw_ = make_rsrc(OUT == kModeWs ? p.yws + sq.s0p * p.D : nullptr,
-                               OUT == kModeWs ? seq_span_bytes(sq.len, p.D, p.D, 4) : 0);
-    const auto ra_ = make_rsrc(ADD ? p.yadd + sq.s0p * p.D : nullptr,
-                               ADD ? seq_span_bytes(sq.len, p.D, p.D, 4) : 0);
+    const auto rw_ = make_rsrc(OUT == kModeWs && !LROWS ? p.yws + sq.s0p * p.D : nullptr,
+                               OUT == kModeWs && !LROWS ? seq_span_bytes(sq.len, p.D, p.D, 4) : 0);
+    const auto ra_ = make_rsrc(ADD && !LROWS ? p.yadd + sq.s0p * p.D : nullptr,
+                               ADD && !LROWS ? seq_span_bytes(sq.len, p.D, p.D, 4) : 0);
     // Staging: this thread's matrix (uniform per wave) as one resource.
     const StageSlot ss = stage_slot(threadIdx.x, NBC);
     const bool stage_c = READOUT && __builtin_amdgcn_readfirstlane(ss.mat) != 0;
@@ -114,7 +116,7 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
         xq[slot] = E::bload(rx, doff, row * xrb);
         dq[slot] = E::bload(rd, doff, row * drb);
         if constexpr (READS_RES) rq[slot] = E::bload(rr_, doff, row * rrb);
-        if constexpr (ADD) aq[slot] = __builtin_amdgcn_raw_buffer_load_b32(ra_, woff, row * wrb, 0);
+        if constexpr (ADD && !LROWS) aq[slot] = __builtin_amdgcn_raw_buffer_load_b32(ra_, woff, row * wrb, 0);
     };
 
     // ---- Bm/Cm staging of one tile of kTile tokens
@@ -175,13 +177,21 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
         if constexpr (READOUT) {
             float y = group_sum<G>(y0 + y1);
             y = fmaf(dskip, xv, y);
-            if constexpr (ADD) y += __uint_as_float(addend);
             // Every lane stores: the G lanes of a channel, and idle lanes
             // shadowing the last channel, hold bit-identical values for the
             // same address.
             const uint32_t orow = static_cast<uint32_t>(seg_row(sg, k));
+            if constexpr (ADD) {
+                if constexpr (LROWS)
+                    y += ylds[orow * kWG + threadIdx.x];
+                else
+                    y += __uint_as_float(addend);
+            }
             if constexpr (OUT == kModeWs) {
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rw_, woff, orow * wrb, 0);
+                if constexpr (LROWS)
+                    ylds[orow * kWG + threadIdx.x] = y;
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rw_, woff, orow * wrb, 0);
             } else {
                 R o;
                 if constexpr (OUT == kModeY) {

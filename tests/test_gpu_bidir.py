@@ -103,6 +103,19 @@ def test_bidir_ragged_edges(gpu, dtype, res_kind, s, rev_kind):
                seed=43)
 
 
+@pytest.mark.parametrize("rev_kind", ["shared", "separate"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("res_kind,s", [("none", 0.0), ("x", 0.3), ("separate", -0.6)])
+def test_bidir_short_windows(gpu, dtype, res_kind, s, rev_kind):
+    """Windows of at most 32 tokens, whose reverse readout stays in LDS: lengths
+    0, 1 and 5..32 (prefetch-group tails and a full 32), a channel tile tail."""
+    lengths = [5, 0, 1, 7, 8, 9, 31, 32, 16]
+    inp = synth.scan_inputs(52, lengths, D=100, dtype=dtype)
+    rev = None if rev_kind == "shared" else synth.reverse_params(52, lengths, 100, dtype=dtype)
+    check_case(inp, rev, dense=False, res_kind=res_kind, s=s, with_hin=True, with_hout=True,
+               seed=53)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bidir_chunked_plans(gpu, dtype):
     """Chunked plans (the reverse direction's plan writing the fp32 rows, then
@@ -156,10 +169,13 @@ def test_bidir_window_bf16_y(gpu):
     check_case(inp, rev, dense=True, with_hout=True, seed=51)
 
 
-def test_bidir_direction_sums_exact(gpu):
+@pytest.mark.parametrize("lengths", [[9, 0, 1, 70, 33], [9, 0, 1, 32, 20]],
+                         ids=["workspace_rows", "lds_rows"])
+def test_bidir_direction_sums_exact(gpu, lengths):
     """A = 0, Delta = 1, one unit state, integer x: y_t is the prefix sum plus
-    twice the suffix sum of the sequence, exactly (fp32, |sums| < 2^24)."""
-    lengths = [9, 0, 1, 70, 33]
+    twice the suffix sum of the sequence, exactly (fp32, |sums| < 2^24); with
+    the reverse readout in the workspace (a 70-token window) and in LDS (at
+    most 32 tokens)."""
     inp = synth.scan_inputs(52, lengths, D=40, dtype="f32")
     r = np.random.default_rng(53)
     x = r.integers(-8, 9, inp.x.shape).astype(np.float32)
