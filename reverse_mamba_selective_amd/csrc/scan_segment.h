@@ -181,15 +181,18 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
             // shadowing the last channel, hold bit-identical values for the
             // same address.
             const uint32_t orow = static_cast<uint32_t>(seg_row(sg, k));
+            // LDS row, clamped: a sequence longer than the plan's maximum (a
+            // broken max_seqlen) stays inside the array
+            const uint32_t lrow = orow < kBidirLdsTokens ? orow : kBidirLdsTokens - 1;
             if constexpr (ADD) {
                 if constexpr (LROWS)
-                    y += ylds[orow * kWG + threadIdx.x];
+                    y += ylds[lrow * kWG + threadIdx.x];
                 else
                     y += __uint_as_float(addend);
             }
             if constexpr (OUT == kModeWs) {
                 if constexpr (LROWS)
-                    ylds[orow * kWG + threadIdx.x] = y;
+                    ylds[lrow * kWG + threadIdx.x] = y;
                 else
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rw_, woff, orow * wrb, 0);
             } else {
