@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define R2L_ABI_VERSION 3
+#define R2L_ABI_VERSION 4
 
 /* exported from libr2l_scan.so (everything else in it is hidden) */
 #if defined(__GNUC__)
@@ -115,6 +115,7 @@ typedef int32_t r2l_status;
 #define R2L_OP_PREFIX 1
 #define R2L_OP_COMMIT 2
 #define R2L_OP_BIDIR 3
+#define R2L_OP_SAVE 4   /* r2l_scan_save */
 
 typedef struct r2l_scan_args {
     /* ---- shape ---- */
@@ -268,6 +269,44 @@ R2L_API r2l_status prefix_scan_backward(const r2l_scan_args *fwd, const r2l_grad
  * arguments (only shape fields and which outputs are wanted are read). */
 R2L_API r2l_status r2l_backward_workspace_size(const r2l_scan_args *fwd,
                                                const r2l_grad_args *grad, size_t *bytes);
+
+/*
+ * Saving the forward states for the backward (training the R2L stream: the
+ * forward runs anyway, so the backward need not scan the states again).
+ *
+ * r2l_scan_save -- r2l_scan with the same arguments and results, which also
+ * stores the state entering every 8th visited position of each sequence (its
+ * "checkpoints") at ckpt: fp32, [rows, dim, dstate] with
+ * rows = (tokens / 8 + batch + 1), the row of visited position p (a multiple
+ * of 8) of sequence b being (packed start of b + p) / 8 + b; ckpt_bytes of at
+ * least r2l_checkpoint_size(). ckpt is an output (16-byte aligned, overlapping
+ * no other buffer of the call); state_split must be 0 or 1. The workspace
+ * is sized by r2l_workspace_size with R2L_OP_SAVE (the plan may chunk
+ * differently from r2l_scan's). The states are
+ * those of the readout (with s == 0 and a residual, where r2l_scan runs no
+ * readout, one more state-only scan stores them). A chunked plan may cut
+ * sequences at other points than r2l_scan's (whole groups of 8 tokens);
+ * results differ from r2l_scan's by rounding only, and are bit-identical to
+ * them when the plan does not chunk.
+ * Source: "Bifocal Diffusion Language Models", section 2 (the R2L stream is
+ * trained with the backbone or alone).
+ */
+R2L_API r2l_status r2l_scan_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes,
+                                 void *stream);
+
+/* Bytes of the checkpoints of a call with these arguments (0 with no token). */
+R2L_API r2l_status r2l_checkpoint_size(const r2l_scan_args *a, size_t *bytes);
+
+/*
+ * r2l_scan_backward_saved -- r2l_scan_backward whose states come from the
+ * checkpoints that r2l_scan_save stored for the same forward arguments
+ * (ckpt: input, ckpt_bytes >= r2l_checkpoint_size()). It runs no forward state
+ * pass; its workspace needs no checkpoint area (r2l_backward_workspace_size
+ * still suffices). Same gradients, layouts and guarantees as
+ * r2l_scan_backward (bit-identical to it when neither plan chunks).
+ */
+R2L_API r2l_status r2l_scan_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                           const float *ckpt, size_t ckpt_bytes, void *stream);
 
 /*
  * bidir_scan -- the bidirectional full-window scan: over each whole sequence,

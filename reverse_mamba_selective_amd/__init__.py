@@ -28,7 +28,7 @@ __all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "bidir_scan", 
            "workspace_size", "bind",
            "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "prefix_scan_backward",
            "bind_backward",
-           "BoundBackward", "R2LScan", "GRADS"]
+           "BoundBackward", "R2LScan", "GRADS", "r2l_scan_save", "checkpoint_size"]
 
 _DTYPES = {torch.float32: _abi.R2L_DTYPE_F32, torch.bfloat16: _abi.R2L_DTYPE_BF16}
 
@@ -216,9 +216,10 @@ def bind(op: str, **kw) -> BoundCall:
 def workspace_size(op: str, x, A, *, cu_seqlens=None, max_seqlen=None, out=True,
                    chunk_tokens=0, state_split=0) -> int:
     """Workspace bytes for op in {"r2l_scan", "prefix_scan_state", "block_commit_state",
-    "bidir_scan"}."""
+    "bidir_scan", "r2l_scan_save"}."""
     codes = {"r2l_scan": _abi.R2L_OP_SCAN, "prefix_scan_state": _abi.R2L_OP_PREFIX,
-             "block_commit_state": _abi.R2L_OP_COMMIT, "bidir_scan": _abi.R2L_OP_BIDIR}
+             "block_commit_state": _abi.R2L_OP_COMMIT, "bidir_scan": _abi.R2L_OP_BIDIR,
+             "r2l_scan_save": _abi.R2L_OP_SAVE}
     a = _fill(x, None, None, None, A, None, cu_seqlens, max_seqlen, None, None, None, 0.0,
               None, True, chunk_tokens, state_split)
     if out:
@@ -241,6 +242,36 @@ def r2l_scan(x, dt, Bm, Cm, A, Dskip=None, *, cu_seqlens=None, max_seqlen=None, 
               delta_softplus, chunk_tokens, state_split)
     _run("r2l_scan", _abi.R2L_OP_SCAN, a, workspace, x.device)
     return out
+
+
+def checkpoint_size(x, A, *, cu_seqlens=None, max_seqlen=None) -> int:
+    """Bytes of the checkpoints that ``r2l_scan_save`` stores for this shape."""
+    a = _fill(x, None, None, None, A, None, cu_seqlens, max_seqlen, None, None, None, 0.0, None,
+              True, 0, 0)
+    return _abi.checkpoint_size(a)
+
+
+def r2l_scan_save(x, dt, Bm, Cm, A, Dskip=None, *, cu_seqlens=None, max_seqlen=None,
+                  h_in=None, h_out=None, res=None, s=0.0, out=None, delta_softplus=True,
+                  chunk_tokens=0, ckpt=None, workspace=None):
+    """``r2l_scan`` that also stores the states the backward needs (the state
+    entering every 8th visited position of each sequence). Returns (out, ckpt);
+    ckpt is an fp32 tensor to hand to ``r2l_scan_backward(..., ckpt=ckpt)``
+    with the same forward arguments."""
+    if out is None:
+        out = torch.empty_like(x)
+    a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
+              delta_softplus, chunk_tokens, 1)
+    need = _abi.checkpoint_size(a)
+    if ckpt is None:
+        ckpt = torch.empty(max(need // 4, 1), dtype=torch.float32, device=x.device)
+    elif ckpt.dtype != torch.float32 or not ckpt.is_contiguous() or ckpt.numel() * 4 < need:
+        raise ValueError("ckpt must be a contiguous fp32 tensor of at least %d bytes" % need)
+    workspace = _attach_workspace(_abi.R2L_OP_SAVE, a, workspace, x.device)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _abi.call_save(a, ckpt.data_ptr(), ckpt.numel() * 4, stream)
+    return out, ckpt
 
 
 def prefix_scan_state(x, dt, Bm, A, *, cu_seqlens=None, max_seqlen=None, h_in=None,
@@ -532,15 +563,19 @@ def prefix_scan_backward(x, dt, Bm, Cm, A, Dskip=None, **kw):
 
 def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seqlens=None,
                       max_seqlen=None, h_in=None, res=None, s=0.0, delta_softplus=True,
-                      grads=GRADS, out=None, workspace=None, chunk_tokens=0, _bind=False,
-                      _reverse=True):
+                      grads=GRADS, out=None, workspace=None, chunk_tokens=0, ckpt=None,
+                      _bind=False, _reverse=True):
     """Gradients of ``r2l_scan`` (same forward arguments) for ``dout`` = dL/dout
     and ``dh_out`` = dL/dh_out. Returns a dict of the names in ``grads``: dx,
     ddt (like x), dBm, dCm (fp32, shaped like Bm), dA [D, N], dDskip [D],
     dh_in [batch, D, N], ds [1] (with a residual only). ``out`` may hold
     preallocated tensors for some of them. A separate residual's gradient is
     dout itself; when res is x, dx includes it. ``chunk_tokens`` is the
-    planning hint of the backward's state pass (0: the library chooses)."""
+    planning hint of the backward's state pass (0: the library chooses).
+    ``ckpt``: the checkpoints ``r2l_scan_save`` stored for the same forward
+    arguments; the backward then runs no forward state pass."""
+    if ckpt is not None and (not _reverse or _bind):
+        raise ValueError("saved checkpoints serve r2l_scan_backward only")
     a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, None, res, s, None,
               delta_softplus, chunk_tokens, 0)
     D, N = int(a.dim), int(a.dstate)
@@ -571,30 +606,37 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
         return BoundBackward(a, g, keep, outs, workspace, x.device, reverse=_reverse)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    _abi.call_backward(a, g, stream, reverse=_reverse)
+    if ckpt is not None:
+        if ckpt.dtype != torch.float32 or not ckpt.is_contiguous():
+            raise ValueError("ckpt must be a contiguous fp32 tensor")
+        _abi.call_backward_saved(a, g, ckpt.data_ptr(), ckpt.numel() * 4, stream)
+    else:
+        _abi.call_backward(a, g, stream, reverse=_reverse)
     return outs
 
 
 class R2LScan(torch.autograd.Function):
     """The R2L stream as a differentiable op (dense [batch, L, D] tensors):
     out = x + s * y (the hook; ``s`` a float) or y (``s`` None). Gradients flow
-    to x, dt, Bm, Cm, A and Dskip through ``r2l_scan_backward``."""
+    to x, dt, Bm, Cm, A and Dskip through ``r2l_scan_backward``, from the
+    state checkpoints that the forward (``r2l_scan_save``) stored."""
 
     @staticmethod
     def forward(ctx, x, dt, Bm, Cm, A, Dskip, s=None):
         res = x if s is not None else None
-        out = r2l_scan(x, dt, Bm, Cm, A, Dskip, res=res, s=0.0 if s is None else float(s))
-        ctx.save_for_backward(x, dt, Bm, Cm, A, Dskip)
+        out, ckpt = r2l_scan_save(x, dt, Bm, Cm, A, Dskip, res=res,
+                                  s=0.0 if s is None else float(s))
+        ctx.save_for_backward(x, dt, Bm, Cm, A, Dskip, ckpt)
         ctx.s = s
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        x, dt, Bm, Cm, A, Dskip = ctx.saved_tensors
+        x, dt, Bm, Cm, A, Dskip, ckpt = ctx.saved_tensors
         s = ctx.s
         g = r2l_scan_backward(x, dt, Bm, Cm, A, Dskip, dout=dout.contiguous(),
                               res=x if s is not None else None,
-                              s=0.0 if s is None else float(s),
+                              s=0.0 if s is None else float(s), ckpt=ckpt,
                               grads=("dx", "ddt", "dBm", "dCm", "dA", "dDskip"))
         return (g["dx"], g["ddt"], g["dBm"].to(Bm.dtype), g["dCm"].to(Cm.dtype), g["dA"],
                 g["dDskip"] if Dskip is not None else None, None)

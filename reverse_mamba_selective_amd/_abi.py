@@ -26,15 +26,17 @@ R2L_OP_SCAN = 0
 R2L_OP_PREFIX = 1
 R2L_OP_COMMIT = 2
 R2L_OP_BIDIR = 3
+R2L_OP_SAVE = 4
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
            "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
            "r2l_check_access_backward", "prefix_scan_backward", "bidir_scan",
            "r2l_check_access_bidir", "r2l_sidecar_forward", "r2l_sidecar_workspace_size",
-           "r2l_check_access_sidecar", "r2l_sidecar_tune")
+           "r2l_check_access_sidecar", "r2l_sidecar_tune", "r2l_scan_save", "r2l_checkpoint_size",
+           "r2l_scan_backward_saved", "r2l_check_access_save", "r2l_check_access_backward_saved")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -151,6 +153,19 @@ def load(path: str = LIB_PATH):
     lib.r2l_check_access_backward.restype = _i32
     lib.r2l_check_access_backward.argtypes = [_i32, ptr, gptr, ctypes.POINTER(_i32),
                                               ctypes.POINTER(AccessReport)]
+    fptr, szt = ctypes.POINTER(ctypes.c_float), ctypes.c_size_t
+    lib.r2l_scan_save.restype = _i32
+    lib.r2l_scan_save.argtypes = [ptr, fptr, szt, _vp]
+    lib.r2l_checkpoint_size.restype = _i32
+    lib.r2l_checkpoint_size.argtypes = [ptr, ctypes.POINTER(szt)]
+    lib.r2l_scan_backward_saved.restype = _i32
+    lib.r2l_scan_backward_saved.argtypes = [ptr, gptr, fptr, szt, _vp]
+    lib.r2l_check_access_save.restype = _i32
+    lib.r2l_check_access_save.argtypes = [ptr, fptr, szt, ctypes.POINTER(_i32),
+                                          ctypes.POINTER(AccessReport)]
+    lib.r2l_check_access_backward_saved.restype = _i32
+    lib.r2l_check_access_backward_saved.argtypes = [ptr, gptr, fptr, szt, ctypes.POINTER(_i32),
+                                                    ctypes.POINTER(AccessReport)]
     dptr = ctypes.POINTER(DirArgs)
     lib.bidir_scan.restype = _i32
     lib.bidir_scan.argtypes = [ptr, dptr, _vp]
@@ -238,6 +253,58 @@ def check_access_backward(args: ScanArgs, grad: GradArgs, cu_seqlens_host=None, 
         cu = ctypes.cast(arr, ctypes.POINTER(_i32))
     st = lib.r2l_check_access_backward(1 if reverse else 0, ctypes.byref(args), ctypes.byref(grad),
                                        cu, ctypes.byref(rep))
+    return st, rep
+
+
+def _fptr(addr):
+    return ctypes.cast(_vp(addr or 0), ctypes.POINTER(ctypes.c_float))
+
+
+def _cu_ptr(cu_seqlens_host):
+    if cu_seqlens_host is None:
+        return None, None
+    arr = (_i32 * len(cu_seqlens_host))(*[int(v) for v in cu_seqlens_host])
+    return arr, ctypes.cast(arr, ctypes.POINTER(_i32))
+
+
+def checkpoint_size(args: ScanArgs) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().r2l_checkpoint_size(ctypes.byref(args), ctypes.byref(n))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_checkpoint_size", last_error())
+    return int(n.value)
+
+
+def call_save(args: ScanArgs, ckpt: int, ckpt_bytes: int, stream: int | None) -> None:
+    st = load().r2l_scan_save(ctypes.byref(args), _fptr(ckpt), ckpt_bytes, _vp(stream or 0))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_scan_save", last_error())
+
+
+def call_backward_saved(args: ScanArgs, grad: GradArgs, ckpt: int, ckpt_bytes: int,
+                        stream: int | None) -> None:
+    st = load().r2l_scan_backward_saved(ctypes.byref(args), ctypes.byref(grad), _fptr(ckpt),
+                                        ckpt_bytes, _vp(stream or 0))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_scan_backward_saved", last_error())
+
+
+def check_access_save(args: ScanArgs, ckpt: int, ckpt_bytes: int, cu_seqlens_host=None):
+    """Host replay of r2l_scan_save; (status, report)."""
+    rep = AccessReport()
+    keep, cu = _cu_ptr(cu_seqlens_host)
+    st = load().r2l_check_access_save(ctypes.byref(args), _fptr(ckpt), ckpt_bytes, cu,
+                                      ctypes.byref(rep))
+    return st, rep
+
+
+def check_access_backward_saved(args: ScanArgs, grad: GradArgs, ckpt: int, ckpt_bytes: int,
+                                cu_seqlens_host=None):
+    """Host replay of r2l_scan_backward_saved; (status, report)."""
+    rep = AccessReport()
+    keep, cu = _cu_ptr(cu_seqlens_host)
+    st = load().r2l_check_access_backward_saved(ctypes.byref(args), ctypes.byref(grad), _fptr(ckpt),
+                                                ckpt_bytes, cu, ctypes.byref(rep))
     return st, rep
 
 

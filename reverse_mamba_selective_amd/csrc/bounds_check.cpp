@@ -50,23 +50,27 @@ class Checker {
                  (unsigned long long)reg->lo, (unsigned long long)reg->hi);
     }
 
-    // Workspace words written so far by the call's launches, in order: every
-    // read of the workspace must find its words written by an earlier launch.
-    void set_workspace(const void *base, uint64_t bytes) {
-        ws_lo_ = reinterpret_cast<uintptr_t>(base);
-        ws_written_.assign(base ? bytes / 4 : 0, false);
+    // Words of the tracked buffers (the workspace; a saving forward's
+    // checkpoints) written so far by the call's launches, in order: every read
+    // of them must find its words written by an earlier launch.
+    void set_workspace(const void *base, uint64_t bytes) { track(base, bytes); }
+    void track(const void *base, uint64_t bytes) {
+        if (base && bytes >= 4)
+            tracked_.push_back({reinterpret_cast<uintptr_t>(base), std::vector<bool>(bytes / 4, false)});
     }
     void wrote(uintptr_t addr, uint64_t bytes) {
-        if (!in_ws(addr)) return;
-        for (uint64_t w = (addr - ws_lo_) / 4; w < (addr - ws_lo_ + bytes) / 4; ++w)
-            if (w < ws_written_.size()) ws_written_[w] = true;
+        Tracked *t = tracked_at(addr);
+        if (!t) return;
+        for (uint64_t w = (addr - t->lo) / 4; w < (addr - t->lo + bytes) / 4; ++w)
+            if (w < t->written.size()) t->written[w] = true;
     }
     void read_written(const char *what, uintptr_t addr, uint64_t bytes) {
-        if (!in_ws(addr) || failed_) return;
-        for (uint64_t w = (addr - ws_lo_) / 4; w < (addr - ws_lo_ + bytes) / 4; ++w)
-            if (w >= ws_written_.size() || !ws_written_[w])
-                return fail("%s: reads workspace byte 0x%llx that no earlier launch wrote", what,
-                            (unsigned long long)(ws_lo_ + 4 * w));
+        Tracked *t = tracked_at(addr);
+        if (!t || failed_) return;
+        for (uint64_t w = (addr - t->lo) / 4; w < (addr - t->lo + bytes) / 4; ++w)
+            if (w >= t->written.size() || !t->written[w])
+                return fail("%s: reads byte 0x%llx that no earlier launch wrote", what,
+                            (unsigned long long)(t->lo + 4 * w));
     }
 
     void fail(const char *fmt, ...) __attribute__((format(printf, 2, 3))) {
@@ -79,15 +83,20 @@ class Checker {
     }
 
   private:
-    bool in_ws(uintptr_t a) const {
-        return !ws_written_.empty() && a >= ws_lo_ && a < ws_lo_ + 4 * ws_written_.size();
+    struct Tracked {
+        uintptr_t lo;
+        std::vector<bool> written;
+    };
+    Tracked *tracked_at(uintptr_t a) {
+        for (Tracked &t : tracked_)
+            if (a >= t.lo && a < t.lo + 4 * t.written.size()) return &t;
+        return nullptr;
     }
 
     std::vector<Region> regions_;
     r2l_access_report *rep_;
     bool failed_ = false;
-    uintptr_t ws_lo_ = 0;
-    std::vector<bool> ws_written_;
+    std::vector<Tracked> tracked_;
 };
 
 uintptr_t U(const void *p) { return reinterpret_cast<uintptr_t>(p); }
@@ -126,6 +135,8 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
         // the body this block runs: a split chunk pass scans chunks > 0 state only
         const bool readout = launch_readout && !(p.split_c0 && bg.c > 0);
         const int mode = readout ? l.mode : kModeState;
+        // checkpoints: kModeCkpt launches, except the state-only chunks of a split pass
+        const bool ckpt_on = (l.mode & kModeCkpt) && !(p.split_c0 && bg.c > 0);
         const int NBC = readout ? 2 * kN : kN, STAGE = stage_cols(NBC);
         const float *hin = segment_hin(p, bg.b, bg.c);
 
@@ -216,9 +227,9 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
             if (mode & kModeAdd) ws_row("reverse readout rows", rAdd, p.yadd, k, false);
         };
         const int ntok = sg.ntok;
-        // backward phase 1: the state entering every group of kCkptTokens
-        // positions (state-only scans), written by the active lanes
-        if (p.ckpt && !readout)
+        // checkpoints: the state entering every group of kCkptTokens
+        // positions, written by the active lanes
+        if (p.ckpt && ckpt_on)
             for (int pos = 0; pos < ntok && ck.ok(); pos += kCkptTokens)
                 for (int lane = 0; lane < kWG; ++lane) {
                     const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
@@ -227,7 +238,7 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
                     const uintptr_t a = U(p.ckpt) + ((row * p.D + lg.d) * kN + lg.sub * NS) * 4;
                     ck.access("checkpoint", ck.region_of(p.ckpt), a, NS * 4);
                     ck.wrote(a, NS * 4);
-                    if (p.ckpt_s && lg.sub == 0) {
+                    if (p.ckpt_s && !readout && lg.sub == 0) {
                         const uintptr_t as = U(p.ckpt_s) + (row * p.D + lg.d) * 4;
                         ck.access("checkpoint delta sum", ck.region_of(p.ckpt_s), as, 4);
                         ck.wrote(as, 4);
@@ -463,7 +474,8 @@ void check_sum(Checker &ck, const Launch &l) {
 }  // namespace
 
 r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r2l_grad_args *g,
-                                   const BwdPlan &pl, const int32_t *cu_host, r2l_access_report *rep) {
+                                   const BwdPlan &pl, const int32_t *cu_host, r2l_access_report *rep,
+                                   const float *saved, size_t saved_bytes) {
     const int64_t es = elem_size(a->dtype), D = a->dim, N = kN;
     const int64_t tok = tokens_of(a);
     std::vector<Region> regs;
@@ -508,10 +520,11 @@ r2l_status check_backward_accesses(bool reverse, const r2l_scan_args *a, const r
                             "workspace chunk entry states", "workspace checkpoint delta sums"};
         for (int i = 0; i < 4; ++i) add(cn[i], ws + co[i], co[i + 1] - co[i]);
     }
+    if (saved) add("saved checkpoints", saved, saved_bytes);   // an input: written by the forward
     Checker ck(std::move(regs), rep);
     ck.set_workspace(g->workspace, pl.ws_bytes);
     Launch ls[kMaxBwdLaunches];
-    const int n = build_bwd_launches(reverse, a, g, pl, ls);
+    const int n = build_bwd_launches(reverse, a, g, pl, ls, saved);
     for (int i = 0; i < n && ck.ok(); ++i) {
         ++rep->launches;
         switch (ls[i].kind) {
@@ -749,7 +762,7 @@ r2l_status check_sidecar_accesses(const r2l_sidecar_args *a, const SidecarPlan &
 }
 
 r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const int32_t *cu_host,
-                          r2l_access_report *rep) {
+                          r2l_access_report *rep, float *ckpt, size_t ckpt_bytes) {
     const int64_t es = elem_size(a->dtype), D = a->dim, N = kN;
     const int64_t tok = tokens_of(a);
     std::vector<Region> regs;
@@ -780,10 +793,13 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
         add("workspace S", ws + pl.off_S, (runs_readout(op, a) ? pl.off_H : pl.ws_bytes) - pl.off_S);
         if (runs_readout(op, a)) add("workspace H", ws + pl.off_H, pl.ws_bytes - pl.off_H);
     }
+    const bool saving = ckpt != nullptr;
+    if (saving) add("checkpoints", ckpt, ckpt_bytes);
     Checker ck(std::move(regs), rep);
     if (pl.chunked) ck.set_workspace(a->workspace, pl.ws_bytes);
-    Launch ls[3];
-    const int n = build_launches(op, a, pl, ls);
+    if (saving) ck.track(ckpt, checkpoint_bytes(a));
+    Launch ls[kMaxSaveLaunches];
+    const int n = saving ? build_save_launches(a, pl, ckpt, ls) : build_launches(op, a, pl, ls);
     for (int i = 0; i < n && ck.ok(); ++i) {
         ++rep->launches;
         if (ls[i].kind == Launch::Segment) {
@@ -794,6 +810,14 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
         } else {
             check_carry(ck, ls[i], cu_host);
         }
+    }
+    // a saving forward leaves every checkpoint row the backward reads written
+    for (int64_t b = 0; saving && b < a->batch && ck.ok(); ++b) {
+        const int64_t s0 = is_ragged(a) ? cu_host[b] : b * a->seqlen;
+        const int64_t len = is_ragged(a) ? cu_host[b + 1] - cu_host[b] : a->seqlen;
+        for (int64_t pos = 0; pos < len && ck.ok(); pos += kCkptTokens)
+            ck.read_written("checkpoint row (for the backward)",
+                            U(ckpt) + static_cast<uint64_t>(ckpt_row(b, s0, pos) * D * N) * 4, D * N * 4);
     }
     return ck.ok() ? R2L_OK : R2L_ERR_INVALID_ARG;
 }

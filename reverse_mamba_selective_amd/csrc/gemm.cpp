@@ -115,7 +115,7 @@ const char *tune_gemm(int dtype, const GemmParams &g, void *y_scratch, hipStream
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return "hipEventCreate failed";
     if (hipEventCreate(&e1) != hipSuccess) {
-        hipEventDestroy(e0);
+        (void)hipEventDestroy(e0);
         return "hipEventCreate failed";
     }
     void *Y = y_scratch ? y_scratch : g.Y;
@@ -134,15 +134,20 @@ const char *tune_gemm(int dtype, const GemmParams &g, void *y_scratch, hipStream
             continue;                                            // warm-up, and a validity check
         constexpr int kReps = 20;
         bool ok = true;
-        hipEventRecord(e0, stream);
+        if (hipEventRecord(e0, stream) != hipSuccess) {
+            err = "hipEventRecord failed";
+            break;
+        }
         for (int r = 0; r < kReps && ok; ++r) ok = run() == HIPBLAS_STATUS_SUCCESS;
-        hipEventRecord(e1, stream);
-        if (hipEventSynchronize(e1) != hipSuccess) {
-            err = "hipEventSynchronize failed";
+        if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
+            err = "hipEventRecord or hipEventSynchronize failed";
             break;
         }
         float ms = 0.0f;
-        hipEventElapsedTime(&ms, e0, e1);
+        if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+            err = "hipEventElapsedTime failed";
+            break;
+        }
         if (!ok) continue;
         // keep the library's first choice unless another is clearly faster
         if (best < 0.0f || (pick == 0 && i > 0 ? ms < 0.95f * best : ms < best)) {
@@ -150,8 +155,8 @@ const char *tune_gemm(int dtype, const GemmParams &g, void *y_scratch, hipStream
             pick = i;
         }
     }
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
     if (err) return err;
     if (best < 0.0f) return "no hipBLASLt candidate ran";
     auto it = g_plans.find(s);

@@ -255,7 +255,7 @@ r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
             case Launch::Segment:
                 if (l.mode & r2l::kModeBias)
                     e = r2l::launch_sidecar_segment(l.dtype, l.mode, l.seg, stream);
-                else if (l.mode >= r2l::kModeWs)
+                else if ((l.mode & r2l::kModeOutMask) == r2l::kModeWs || (l.mode & r2l::kModeAdd))
                     e = r2l::launch_bidir_segment(l.reverse, l.dtype, l.mode, l.seg, stream);
                 else
                     e = r2l::launch_segment_scan(l.reverse, l.dtype, l.G, l.mode, l.seg, stream);
@@ -311,6 +311,69 @@ r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
 
     Launch ls[3];
     const int n = r2l::build_launches(op, a, pl, ls);
+    return execute(ls, n, stream);
+}
+
+// ---- saved checkpoints ------------------------------------------------------------
+// The checkpoint buffer is one more output of the forward (and an input of the
+// backward): 16-byte aligned, large enough, overlapping no other buffer.
+r2l_status check_ckpt(const r2l_scan_args *a, const void *ckpt, size_t bytes, bool is_output,
+                      const void *workspace, size_t ws_bytes) {
+    const size_t need = r2l::checkpoint_bytes(a);
+    if (need == 0) return R2L_OK;
+    if (!ckpt) return fail(R2L_ERR_INVALID_ARG, "ckpt is NULL");
+    if (!aligned(ckpt, 16)) return fail(R2L_ERR_MISALIGNED, "ckpt is not 16-byte aligned");
+    if (bytes < need)
+        return fail(R2L_ERR_WORKSPACE, "the checkpoints need %zu bytes, got %zu", need, bytes);
+    const int64_t D = a->dim, N = r2l::kN, es = elem_size(a->dtype), B = a->batch;
+    const Range c{"ckpt", reinterpret_cast<uintptr_t>(ckpt), reinterpret_cast<uintptr_t>(ckpt) + need,
+                  is_output};
+    const Range others[] = {
+        token_span("x", a, a->x, a->x_stride, a->x_batch_stride, D, es, false),
+        token_span("dt", a, a->dt, a->dt_stride, a->dt_batch_stride, D, es, false),
+        token_span("Bm", a, a->Bm, a->Bm_stride, a->Bm_batch_stride, N, es, false),
+        token_span("Cm", a, a->Cm, a->Cm_stride, a->Cm_batch_stride, N, es, false),
+        token_span("res", a, a->res, a->res_stride, a->res_batch_stride, D, es, false),
+        token_span("out", a, a->out, a->out_stride, a->out_batch_stride, D, es, true),
+        span("A", a->A, D, N, N, 4, false),
+        span("Dskip", a->Dskip, 1, D, D, 4, false),
+        span("h_in", a->h_in, B, D * N, D * N, 4, false),
+        span("h_out", a->h_out, B, D * N, D * N, 4, true),
+        span("cu_seqlens", a->cu_seqlens, 1, B + 1, B + 1, 4, false),
+        span("workspace", workspace, 1, (int64_t)ws_bytes, (int64_t)ws_bytes, 1, true)};
+    for (const Range &o : others)
+        if ((is_output || o.is_output) && overlap(c, o))
+            return fail(R2L_ERR_ALIAS, "ckpt overlaps %s", o.name);
+    return R2L_OK;
+}
+
+r2l_status prepare_save(const r2l_scan_args *a, r2l_scan_args *v, Plan *pl) {
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    if (a->state_split > 1)
+        return fail(R2L_ERR_UNSUPPORTED, "r2l_scan_save runs one lane per channel (state_split 0 or 1)");
+    *v = *a;
+    v->state_split = 1;
+    *pl = r2l::make_plan(Op::Scan, v, true);
+    st = check_buffers(Op::Scan, v, *pl);
+    if (st != R2L_OK) return st;
+    if (v->batch * pl->nchunks * pl->tiles > INT32_MAX - 8)
+        return fail(R2L_ERR_UNSUPPORTED, "grid too large");
+    return R2L_OK;
+}
+
+r2l_status run_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes, hipStream_t stream) {
+    r2l_scan_args v;
+    Plan pl;
+    r2l_status st = prepare_save(a, &v, &pl);
+    if (st != R2L_OK) return st;
+    st = check_ckpt(&v, ckpt, ckpt_bytes, true, pl.chunked ? v.workspace : nullptr,
+                    pl.chunked ? pl.ws_bytes : 0);
+    if (st != R2L_OK) return st;
+    st = check_seqlens_on_device(&v);
+    if (st != R2L_OK) return st;
+    Launch ls[r2l::kMaxSaveLaunches];
+    const int n = r2l::build_save_launches(&v, pl, ckpt, ls);
     return execute(ls, n, stream);
 }
 
@@ -595,18 +658,47 @@ r2l_status check_backward(const r2l_scan_args *a, const r2l_grad_args *g, const 
     return R2L_OK;
 }
 
+// The checkpoints a backward reads: sized and aligned, overlapping no output of
+// the forward's arguments nor any gradient output.
+r2l_status check_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad, const r2l::BwdPlan &pl,
+                       const float *saved, size_t saved_bytes) {
+    r2l_status st = check_ckpt(fwd, saved, saved_bytes, false, grad->workspace, pl.ws_bytes);
+    if (st != R2L_OK) return st;
+    const size_t need = r2l::checkpoint_bytes(fwd);
+    if (need == 0) return R2L_OK;
+    const int64_t T = tokens_of(fwd), D = fwd->dim, N = r2l::kN, es = elem_size(fwd->dtype);
+    const Range c{"ckpt", reinterpret_cast<uintptr_t>(saved), reinterpret_cast<uintptr_t>(saved) + need,
+                  false};
+    const Range outs[] = {
+        token_span("dx", fwd, grad->dx, grad->dx_stride, grad->dx_batch_stride, D, es, true),
+        token_span("ddt", fwd, grad->ddt, grad->ddt_stride, grad->ddt_batch_stride, D, es, true),
+        span("dBm", grad->dBm, T, N, N, 4, true), span("dCm", grad->dCm, T, N, N, 4, true),
+        span("dA", grad->dA, D, N, N, 4, true), span("dDskip", grad->dDskip, 1, D, D, 4, true),
+        span("dh_in", grad->dh_in, fwd->batch, D * N, D * N, 4, true),
+        span("ds", grad->ds, 1, 1, 1, 4, true)};
+    for (const Range &o : outs)
+        if (overlap(c, o)) return fail(R2L_ERR_ALIAS, "%s overlaps ckpt", o.name);
+    return R2L_OK;
+}
+
+// use_saved: the checkpoints come from r2l_scan_save (saved, saved_bytes)
 r2l_status run_backward(bool reverse, const r2l_scan_args *fwd, const r2l_grad_args *grad,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool use_saved = false, const float *saved = nullptr,
+                        size_t saved_bytes = 0) {
     r2l_status st = check_shape(fwd);
     if (st != R2L_OK) return st;
     if (!grad) return fail(R2L_ERR_INVALID_ARG, "grad is NULL");
-    const r2l::BwdPlan pl = r2l::make_bwd_plan(fwd, grad);
+    const r2l::BwdPlan pl = r2l::make_bwd_plan(fwd, grad, use_saved);
     st = check_backward(fwd, grad, pl);
     if (st != R2L_OK) return st;
+    if (use_saved) {
+        st = check_saved(fwd, grad, pl, saved, saved_bytes);
+        if (st != R2L_OK) return st;
+    }
     st = check_seqlens_on_device(fwd);
     if (st != R2L_OK) return st;
     Launch ls[r2l::kMaxBwdLaunches];
-    const int n = r2l::build_bwd_launches(reverse, fwd, grad, pl, ls);
+    const int n = r2l::build_bwd_launches(reverse, fwd, grad, pl, ls, saved);
     return execute(ls, n, stream);
 }
 
@@ -620,6 +712,23 @@ r2l_status r2l_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad
 
 r2l_status prefix_scan_backward(const r2l_scan_args *fwd, const r2l_grad_args *grad, void *stream) {
     return run_backward(false, fwd, grad, static_cast<hipStream_t>(stream));
+}
+
+r2l_status r2l_checkpoint_size(const r2l_scan_args *a, size_t *bytes) {
+    if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    *bytes = r2l::checkpoint_bytes(a);
+    return ok();
+}
+
+r2l_status r2l_scan_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes, void *stream) {
+    return run_save(a, ckpt, ckpt_bytes, static_cast<hipStream_t>(stream));
+}
+
+r2l_status r2l_scan_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                   const float *ckpt, size_t ckpt_bytes, void *stream) {
+    return run_backward(true, fwd, grad, static_cast<hipStream_t>(stream), true, ckpt, ckpt_bytes);
 }
 
 r2l_status r2l_check_access_backward(int32_t reverse, const r2l_scan_args *fwd,
@@ -745,12 +854,19 @@ r2l_status block_commit_state(const r2l_scan_args *a, void *stream) {
 
 r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes) {
     if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
-    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT && op != R2L_OP_BIDIR)
+    if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT && op != R2L_OP_BIDIR &&
+        op != R2L_OP_SAVE)
         return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);
     r2l_status st = check_shape(a);
     if (st != R2L_OK) return st;
     if (op == R2L_OP_BIDIR) {
         *bytes = r2l::make_bidir_plan(a).ws_bytes;
+        return ok();
+    }
+    if (op == R2L_OP_SAVE) {
+        r2l_scan_args v = *a;
+        v.state_split = 1;
+        *bytes = r2l::make_plan(Op::Scan, &v, true).ws_bytes;
         return ok();
     }
     const Op o = op == R2L_OP_SCAN ? Op::Scan : (op == R2L_OP_PREFIX ? Op::Prefix : Op::Commit);
@@ -784,6 +900,49 @@ r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *c
     st = r2l::check_accesses(o, a, pl, cu_seqlens_host, report);
     if (st != R2L_OK) return fail(st, "%s", report->message);
     return ok();
+}
+
+r2l_status r2l_check_access_save(const r2l_scan_args *a, const float *ckpt, size_t ckpt_bytes,
+                                 const int32_t *cu_seqlens_host, r2l_access_report *report) {
+    if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
+    report->launches = report->accesses = report->vector_staging = 0;
+    report->message[0] = '\0';
+    r2l_scan_args v;
+    Plan pl;
+    r2l_status st = prepare_save(a, &v, &pl);
+    if (st != R2L_OK) return st;
+    st = check_ckpt(&v, ckpt, ckpt_bytes, true, pl.chunked ? v.workspace : nullptr,
+                    pl.chunked ? pl.ws_bytes : 0);
+    if (st != R2L_OK) return st;
+    st = check_host_offsets(&v, cu_seqlens_host);
+    if (st != R2L_OK) return st;
+    st = r2l::check_accesses(Op::Scan, &v, pl, cu_seqlens_host, report, const_cast<float *>(ckpt),
+                             ckpt_bytes);
+    if (st != R2L_OK) return fail(st, "%s", report->message);
+    return ok();
+}
+
+r2l_status r2l_check_access_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                           const float *ckpt, size_t ckpt_bytes,
+                                           const int32_t *cu_seqlens_host,
+                                           r2l_access_report *report) {
+    if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
+    report->launches = report->accesses = report->vector_staging = 0;
+    report->message[0] = '\0';
+    r2l_status st = check_shape(fwd);
+    if (st != R2L_OK) return st;
+    if (!grad) return fail(R2L_ERR_INVALID_ARG, "grad is NULL");
+    const r2l::BwdPlan pl = r2l::make_bwd_plan(fwd, grad, true);
+    st = check_backward(fwd, grad, pl);
+    if (st != R2L_OK) return st;
+    st = check_saved(fwd, grad, pl, ckpt, ckpt_bytes);
+    if (st != R2L_OK) return st;
+    st = check_host_offsets(fwd, cu_seqlens_host);
+    if (st != R2L_OK) return st;
+    st = r2l::check_backward_accesses(true, fwd, grad, pl, cu_seqlens_host, report, ckpt,
+                                      ckpt_bytes);
+    if (st != R2L_OK && report->message[0]) fail(st, "%s", report->message);
+    return st == R2L_OK ? ok() : st;
 }
 
 r2l_status r2l_describe_plan(int32_t op, const r2l_scan_args *a, r2l_plan_info *info) {

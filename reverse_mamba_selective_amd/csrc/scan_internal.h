@@ -33,6 +33,11 @@ constexpr int kModeBias = 16;
 // (each lane reads back only its own channel's rows).
 constexpr int kModeLds = 32;
 constexpr int kBidirLdsTokens = 32;
+// The scan stores the state entering every kCkptTokens-th visited position
+// at SegParams::ckpt: the backward's phase 1 (state only), or a forward scan
+// with readout that saves them for the backward (chunks scanned state-only
+// from zero inside a readout plan never store).
+constexpr int kModeCkpt = 64;
 
 // One launch of the segment kernel scans "segments": chunk c (in visiting
 // order) of sequence b, for a tile of kWG lanes. With G lanes per channel a

@@ -105,9 +105,22 @@ hipError_t launch_g(int G, const SegParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Checkpointing scans run one lane per channel.
+template <bool REV, typename T, int MODE, bool SP>
+hipError_t launch_ck(int G, const SegParams &p, hipStream_t stream) {
+    if (G != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((segment_scan_kernel<REV, T, 1, MODE | kModeCkpt, SP>),
+                       dim3(padded_grid(p.nblocks)), dim3(kWG), 0, stream, p);
+    return hipGetLastError();
+}
+
 template <bool REV, typename T, bool SP>
 hipError_t launch_m(int mode, int G, const SegParams &p, hipStream_t stream) {
     switch (mode) {
+        case kModeState | kModeCkpt: return launch_ck<REV, T, kModeState, SP>(G, p, stream);
+        case kModeY | kModeCkpt: return launch_ck<REV, T, kModeY, SP>(G, p, stream);
+        case kModeResX | kModeCkpt: return launch_ck<REV, T, kModeResX, SP>(G, p, stream);
+        case kModeRes | kModeCkpt: return launch_ck<REV, T, kModeRes, SP>(G, p, stream);
         case kModeState: return launch_g<REV, T, kModeState, SP>(G, p, stream);
         case kModeY: return launch_g<REV, T, kModeY, SP>(G, p, stream);
         case kModeResX: return launch_g<REV, T, kModeResX, SP>(G, p, stream);

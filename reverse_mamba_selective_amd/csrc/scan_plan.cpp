@@ -80,7 +80,7 @@ int out_mode(const r2l_scan_args *a, const SegParams &p) {
 
 }  // namespace
 
-Plan make_plan(Op op, const r2l_scan_args *a) {
+Plan make_plan(Op op, const r2l_scan_args *a, bool ckpt) {
     Plan pl;
     const int64_t channels = a->batch * a->dim;
     const int64_t maxlen = max_len_of(a);
@@ -101,6 +101,7 @@ Plan make_plan(Op op, const r2l_scan_args *a) {
         // a readout plan of two chunks runs one chunk per pass: no gain
         if (readout && chunk > 0 && (maxlen + chunk - 1) / chunk < 3) chunk = 0;
     }
+    if (ckpt) chunk = (chunk + kCkptTokens - 1) / kCkptTokens * kCkptTokens;
     if (chunk > 0 && chunk < maxlen) {
         pl.chunked = true;
         pl.chunk_len = chunk;
@@ -239,6 +240,56 @@ int build_scan_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch ou
 }
 
 }  // namespace
+
+// ---- checkpoints ------------------------------------------------------------------
+size_t checkpoint_bytes(const r2l_scan_args *a) {
+    const int64_t T = tokens_of(a);
+    if (T <= 0) return 0;
+    return static_cast<size_t>(ckpt_rows(T, a->batch)) * static_cast<size_t>(a->dim) * kN * 4;
+}
+
+namespace {
+
+// One unchunked state-only scan over every sequence from h_in, one lane per
+// channel, storing the checkpoints (the true states).
+Launch ckpt_state_launch(bool reverse, const r2l_scan_args *a, int64_t fwd_tiles, float *ck) {
+    Plan fp;
+    fp.G = 1;
+    fp.chunk_len = std::max<int64_t>(max_len_of(a), 1);
+    fp.nchunks = 1;
+    fp.tiles = fwd_tiles;
+    SegParams p = base_params(a, fp);
+    p.res = nullptr;
+    p.out = nullptr;
+    p.ckpt = ck;
+    p.bc_vec = bc_vector_ok(a, false) ? 1 : 0;
+    p.hin = a->h_in; p.hin_b = a->dim * kN; p.hin_c = 0;
+    Launch l{};
+    l.kind = Launch::Segment;
+    l.reverse = reverse;
+    l.dtype = a->dtype;
+    l.G = 1;
+    l.mode = kModeState | kModeCkpt;
+    l.seg = p;
+    return l;
+}
+
+}  // namespace
+
+int build_save_launches(const r2l_scan_args *a, const Plan &pl, float *ckpt,
+                        Launch out[kMaxSaveLaunches]) {
+    int n = build_launches(Op::Scan, a, pl, out);
+    bool stored = false;
+    for (int i = 0; i < n; ++i)
+        if (out[i].kind == Launch::Segment && (out[i].mode & kModeOutMask) != kModeState) {
+            out[i].mode |= kModeCkpt;
+            out[i].seg.ckpt = ckpt;
+            stored = true;
+        }
+    if (!stored && tokens_of(a) > 0 && a->batch > 0)
+        out[n++] = ckpt_state_launch(true, a, (a->dim + kWG - 1) / kWG, ckpt);
+    return n;
+}
 
 // ---- bidirectional scan ------------------------------------------------------------
 BidirPlan make_bidir_plan(const r2l_scan_args *a) {
@@ -460,7 +511,7 @@ int build_sidecar_launches(const r2l_sidecar_args *a, const SidecarPlan &sp,
 }
 
 // ---- backward ------------------------------------------------------------------
-BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
+BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g, bool saved) {
     BwdPlan pl;
     pl.G = 4;
     pl.tiles = (a->dim * pl.G + kWG - 1) / kWG;
@@ -481,7 +532,7 @@ BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
         if (fill > 1) chunk = std::max<int64_t>(kMinChunk, (maxlen + fill - 1) / fill);
     }
     chunk = (chunk + kCkptTokens - 1) / kCkptTokens * kCkptTokens;
-    if (chunk > 0 && chunk < maxlen) {
+    if (!saved && chunk > 0 && chunk < maxlen) {
         pl.chunked = true;
         pl.chunk_len = chunk;
         pl.nchunks = (maxlen + chunk - 1) / chunk;
@@ -489,6 +540,7 @@ BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
         pl.chunk_len = std::max<int64_t>(maxlen, 1);
         pl.nchunks = 1;
     }
+    pl.saved = saved;
     if (a->res) {
         const bool is_x = a->res == a->x && a->res_stride == a->x_stride &&
                           eff_bstride(a, a->res_batch_stride, a->res_stride) ==
@@ -503,7 +555,7 @@ BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
     };
     const size_t D = static_cast<size_t>(a->dim), B = static_cast<size_t>(a->batch);
     const size_t T = static_cast<size_t>(pl.tokens), tiles = static_cast<size_t>(pl.tiles);
-    pl.off_ck = take(pl.tokens > 0 ? static_cast<size_t>(pl.ck_rows) * D * kN * 4 : 0);
+    pl.off_ck = take(pl.tokens > 0 && !saved ? static_cast<size_t>(pl.ck_rows) * D * kN * 4 : 0);
     pl.off_B = take(g->dBm ? tiles * T * kN * 4 : 0);
     pl.off_C = take(g->dCm ? tiles * T * kN * 4 : 0);
     pl.off_A = take(g->dA ? B * D * kN * 4 : 0);
@@ -521,10 +573,10 @@ BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g) {
 }
 
 int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args *g,
-                       const BwdPlan &pl, Launch out[kMaxBwdLaunches]) {
+                       const BwdPlan &pl, Launch out[kMaxBwdLaunches], const float *saved_ckpt) {
     char *ws = static_cast<char *>(g->workspace);
     auto at = [&](size_t off, bool want) { return want ? reinterpret_cast<float *>(ws + off) : nullptr; };
-    float *ck = at(pl.off_ck, pl.tokens > 0);
+    float *ck = pl.saved ? nullptr : at(pl.off_ck, pl.tokens > 0);
     float *pB = at(pl.off_B, g->dBm != nullptr), *pC = at(pl.off_C, g->dCm != nullptr);
     float *pA = at(pl.off_A, g->dA != nullptr), *pD = at(pl.off_D, g->dDskip != nullptr);
     float *pS = at(pl.off_S, g->ds != nullptr);
@@ -536,7 +588,8 @@ int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args
 
     if (a->batch > 0) {
         // phase 1: the forward state scan, one lane per channel, with checkpoints
-        if (pl.tokens > 0) {
+        // (none when the forward saved them)
+        if (pl.tokens > 0 && !pl.saved) {
             Plan fp;
             fp.G = 1;
             fp.chunk_len = pl.chunk_len;
@@ -560,7 +613,7 @@ int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args
             l.reverse = reverse;
             l.dtype = a->dtype;
             l.G = 1;
-            l.mode = kModeState;
+            l.mode = kModeState | kModeCkpt;
             l.seg = p;
             out[n++] = l;
         }
@@ -603,7 +656,7 @@ int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args
         q.dyscale = pl.res_kind ? a->s : 1.0f;
         q.dxres = pl.res_kind == 1 ? 1.0f : 0.0f;
         q.want_ds = g->ds ? 1 : 0;
-        q.ckpt = ck;
+        q.ckpt = pl.saved ? saved_ckpt : ck;
         if (chunked) {
             q.chunk_len = static_cast<int32_t>(pl.chunk_len);
             q.nchunks = static_cast<int32_t>(pl.nchunks);

@@ -50,6 +50,7 @@ struct BwdPlan {
     int64_t tokens = 0;
     int64_t ck_rows = 0;
     bool chunked = false;    // phase 1 cut into chunks (a multiple of kCkptTokens)
+    bool saved = false;      // the checkpoints were saved by the forward: no phase 1
     int64_t chunk_len = 0, nchunks = 1;
     size_t ws_bytes = 0;
     size_t off_ck = 0, off_B = 0, off_C = 0, off_A = 0, off_D = 0, off_S = 0;
@@ -59,10 +60,12 @@ struct BwdPlan {
     int res_kind = 0;        // 0: none, 1: the residual is x, 2: a separate residual
 };
 
-BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g);
+// saved: the checkpoints come from r2l_scan_save (no phase 1, no checkpoint area)
+BwdPlan make_bwd_plan(const r2l_scan_args *a, const r2l_grad_args *g, bool saved = false);
 // reverse: the backward of r2l_scan (true) or of the forward-direction readout (false)
 int build_bwd_launches(bool reverse, const r2l_scan_args *a, const r2l_grad_args *g,
-                       const BwdPlan &pl, Launch out[kMaxBwdLaunches]);
+                       const BwdPlan &pl, Launch out[kMaxBwdLaunches],
+                       const float *saved_ckpt = nullptr);
 
 inline bool is_ragged(const r2l_scan_args *a) { return a->cu_seqlens != nullptr; }
 inline int64_t tokens_of(const r2l_scan_args *a) {
@@ -95,7 +98,9 @@ inline int64_t eff_bstride(const r2l_scan_args *a, int64_t bstride, int64_t stri
     return bstride ? bstride : a->seqlen * stride;
 }
 
-Plan make_plan(Op op, const r2l_scan_args *a);
+// ckpt: the plan of a scan that saves the backward's checkpoints (chunks are
+// whole checkpoint groups)
+Plan make_plan(Op op, const r2l_scan_args *a, bool ckpt = false);
 
 // The bidirectional scan (bidir_scan): the reverse direction's readout into
 // fp32 workspace rows, then the forward direction's readout adding them; one
@@ -139,5 +144,14 @@ int build_sidecar_launches(const r2l_sidecar_args *a, const SidecarPlan &sp,
 // The launches of a call, in order (at most 3). Arguments must have passed
 // the entry point's checks. Returns the count.
 int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3]);
+
+// r2l_scan_save: the r2l_scan launches (plan made with ckpt = true, one lane
+// per channel) whose readout scans also store the checkpoints at ckpt; when
+// no readout runs (s == 0), one more state-only scan stores them.
+constexpr int kMaxSaveLaunches = 4;
+int build_save_launches(const r2l_scan_args *a, const Plan &pl, float *ckpt,
+                        Launch out[kMaxSaveLaunches]);
+// Bytes of the checkpoints of a call: ckpt_rows(tokens, batch) x D x kN fp32.
+size_t checkpoint_bytes(const r2l_scan_args *a);
 
 }  // namespace r2l

@@ -36,6 +36,7 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     constexpr bool ADD = (MODE & kModeAdd) != 0;  // y += an fp32 addend per token
     // the fp32 rows (kModeWs / kModeAdd) at ylds[row * kWG + thread] in LDS
     constexpr bool LROWS = (MODE & kModeLds) != 0;
+    constexpr bool CK = (MODE & kModeCkpt) != 0;   // store checkpoints
     constexpr bool BIAS = (MODE & kModeBias) != 0;  // dt += dt_bias[d] before softplus
     constexpr bool READS_RES = OUT == kModeRes || OUT == kModeGate;
     constexpr bool READOUT = OUT != kModeState;
@@ -211,9 +212,10 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
         }
     };
 
-    // Backward phase 1: the state entering each group of kCkptTokens visited
-    // positions (the groups are the prefetch groups; chunks are whole groups)
-    // and, in a chunked phase 1, the chunk's Delta sum up to it.
+    // Checkpoints (kModeCkpt): the state entering each group of kCkptTokens
+    // visited positions (the groups are the prefetch groups; chunks are whole
+    // groups) and, in the backward's chunked phase 1, the chunk's Delta sum
+    // up to it.
     static_assert(PF == kCkptTokens, "checkpoint groups are the prefetch groups");
     auto checkpoint = [&](int pos) {
         if (!p.ckpt || !lg.active) return;
@@ -221,7 +223,8 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
         float *cp = p.ckpt + (row * p.D + dl) * kN + sub * NS;
 #pragma unroll
         for (int j = 0; j < NS; ++j) cp[j] = h[j];
-        if (p.ckpt_s && sub == 0) p.ckpt_s[row * p.D + dl] = dsum;
+        if constexpr (!READOUT)
+            if (p.ckpt_s && sub == 0) p.ckpt_s[row * p.D + dl] = dsum;
     };
 
     // Start-up: the first tile's Bm/Cm rows are requested first (they gate
@@ -252,11 +255,11 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
 
         const int full = cnt - cnt % PF;
         for (int k0 = 0; k0 < full; k0 += PF) {
-            if constexpr (!READOUT) checkpoint(base + k0);
+            if constexpr (CK) checkpoint(base + k0);
 #pragma unroll
             for (int j = 0; j < PF; ++j) token(base + k0 + j, bc + (k0 + j) * NBC, j);
         }
-        if constexpr (!READOUT)
+        if constexpr (CK)
             if (full < cnt) checkpoint(base + full);
 #pragma unroll
         for (int j = 0; j < PF; ++j)            // the last tile's partial group

@@ -382,6 +382,90 @@ def test_backward_benchmarked_shapes():
     assert rep.launches == 4   # phase 1 in chunks, the carry, phase 2, the sums
 
 
+# ---- the saving forward and the backward from its checkpoints -------------------------
+def check_save(**kw):
+    """Replay r2l_scan_save and then r2l_scan_backward_saved on its checkpoints."""
+    res = kw.pop("res", "none")
+    a, cu = make_args("scan", res=res, **kw)
+    # the saving forward plans its own workspace (chunks in whole groups of 8 tokens)
+    need = _abi.workspace_size(_abi.R2L_OP_SAVE, a)
+    heap = FakeHeap()
+    heap.next = BASE + (1 << 40)
+    a.workspace, a.workspace_bytes = (heap.alloc(need), need) if need else (None, 0)
+    nbytes = _abi.checkpoint_size(a)
+    ckpt = heap.alloc(nbytes)
+    st, rep = _abi.check_access_save(a, ckpt, nbytes, cu)
+    msg = rep.message.decode() or _abi.last_error()
+    assert st == _abi.R2L_OK, "save %s: %s" % (kw, msg)
+    heap.next = BASE + (2 << 40)
+    g = make_grad(a, heap, dtype=kw.get("dtype", "bf16"), pad_row=kw.get("pad_row", 0))
+    st, brep = _abi.check_access_backward_saved(a, g, ckpt, nbytes, cu)
+    msg = brep.message.decode() or _abi.last_error()
+    assert st == _abi.R2L_OK, "backward from checkpoints %s: %s" % (kw, msg)
+    return a, rep, brep
+
+
+SAVE_EDGE = BWD_EDGE + BWD_CHUNKED + [
+    dict(lengths=[700, 1, 0, 333, 64, 1025], D=96, chunk=100),   # rounded up to 104
+    dict(batch=2, seqlen=300, D=256, chunk=64, pad_row=8, pad_batch=40),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SAVE_EDGE)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_save_and_saved_backward(case, dtype):
+    """Every checkpoint row the backward reads is written by the saving
+    forward (the replay checks it), and neither call leaves its buffers."""
+    kw = dict(SAVE_EDGE[case], dtype=dtype)
+    kw.setdefault("D", 64)
+    for res in ("none", "x", "sep", "inplace"):
+        for h in (False, True):
+            check_save(res=res, h_in=h, h_out=h, **kw)
+    check_save(res="x", s=0.0, **kw)    # gate closed: a state-only scan stores them
+
+
+def test_save_plans():
+    """Unchunked, the saving forward runs r2l_scan's launches; the backward
+    from its checkpoints runs no forward state pass; the checkpoint rows
+    follow the documented count."""
+    a, rep, brep = check_save(batch=64, seqlen=32, D=2048, res="x", chunk=0)
+    assert rep.launches == 1 and brep.launches == 2
+    assert _abi.checkpoint_size(a) == (64 * 32 // 8 + 64 + 1) * 2048 * 16 * 4
+    a, rep, brep = check_save(batch=8, seqlen=4096, D=4096, chunk=0)
+    assert rep.launches == 3 and brep.launches == 2       # chunk states, carry, readout
+    a, rep, brep = check_save(batch=2, seqlen=64, D=64, res="x", s=0.0)
+    assert rep.launches == 2                              # res copied to out, state-only scan
+    a, rep, brep = check_save(batch=2, seqlen=64, D=64, res="inplace", s=0.0)
+    assert rep.launches == 1                              # out is res: the state-only scan
+    a, rep, brep = check_save(lengths=[0, 0], D=64)
+    assert _abi.checkpoint_size(a) == 0 or rep.launches <= 1
+
+
+def test_save_rejects_bad_arguments():
+    a, cu = make_args("scan", batch=2, seqlen=64, D=64, res="x")
+    nbytes = _abi.checkpoint_size(a)
+    heap = FakeHeap()
+    heap.next = BASE + (1 << 40)
+    ckpt = heap.alloc(nbytes)
+    st, _ = _abi.check_access_save(a, ckpt, nbytes - 4, cu)
+    assert st == _abi.R2L_ERR_WORKSPACE
+    st, _ = _abi.check_access_save(a, None, nbytes, cu)
+    assert st == _abi.R2L_ERR_INVALID_ARG
+    st, _ = _abi.check_access_save(a, ckpt + 4, nbytes, cu)
+    assert st == _abi.R2L_ERR_MISALIGNED
+    st, _ = _abi.check_access_save(a, a.x, nbytes, cu)     # overlaps x
+    assert st == _abi.R2L_ERR_ALIAS
+    a.state_split = 2
+    st, _ = _abi.check_access_save(a, ckpt, nbytes, cu)
+    assert st == _abi.R2L_ERR_UNSUPPORTED
+    a.state_split = 0
+    g = make_grad(a, heap)
+    st, _ = _abi.check_access_backward_saved(a, g, ckpt, nbytes - 4, cu)
+    assert st == _abi.R2L_ERR_WORKSPACE
+    st, _ = _abi.check_access_backward_saved(a, g, g.dx, nbytes, cu)    # overlaps dx
+    assert st == _abi.R2L_ERR_ALIAS
+
+
 # ---- the bidirectional scan ---------------------------------------------------------
 def make_dir(a, heap, kind, *, dtype="bf16", pad_row=0, bc_shift=0):
     """Reverse-direction parameters for the forward call `a`: "shared" (NULL
