@@ -189,6 +189,7 @@ class Workload:
     step_entries: list = [0]  # index into measure of each call of a step
     launches_per_step = 1
     graph_ok = True           # the step may be captured in a hipGraph
+    isolate_entries = False   # time each entry point in a loop of its own (see main)
 
     def step(self, i, stream):
         for c in self.step_calls[i % len(self.step_calls)]:
@@ -317,14 +318,16 @@ class DenoiseBackward(Denoise):
         self.bytes_per_launch = (tok * self.D * 2 * 5 + tok * 16 * (2 * 2 + 4 * 2) +
                                  self.D * 16 * 4 * 2 + self.D * 4 * 2 + 4)
         self.alu_per_launch = self.tc_per_launch * bwd_alu_ops_per_tc()
-        self.bwd_calls, self.bwd_grads = [], []
+        self.bwd_calls, self.bwd_grads, self._douts = [], [], []
         for r, row in enumerate(self.step_calls):
             brow = []
+            self._douts.append([])
             for h in range(len(row)):
                 x = self._bound_inputs[r][h]["x"]
                 g = torch.Generator(device="cuda")
                 g.manual_seed(5000 + 7 * r + h)
                 dout = torch.randn(x.shape, generator=g, device="cuda").to(x.dtype)
+                self._douts[r].append(dout)
                 inp_args = self._bound_inputs[r][h]
                 bc = r2l.bind_backward(x, inp_args["dt"], inp_args["Bm"], inp_args["Cm"],
                                        inp_args["A"], inp_args["Dskip"], dout=dout, res=x,
@@ -365,6 +368,82 @@ class DenoiseBackward(Denoise):
 
     parity_spec = ("dA, dBm", "f32", 1e-4,
                    "dA and dBm of all 7 hooks (first buffer set) vs the oracle's fp64 backward")
+
+
+class DenoiseTrain(DenoiseBackward):
+    """Training the R2L stream over one denoising step: per hook, the forward
+    that saves the backward's state checkpoints (r2l_scan_save, out = x + s*y)
+    and the backward from them (r2l_scan_backward_saved, all gradients); 7
+    hooks of 64 x 32 x 2048, bf16. The unsaved pair (r2l_scan, then
+    r2l_scan_backward, whose state pass rescans the forward) is the
+    "denoise" and "denoise_bwd" workloads."""
+    name = "denoise_train_bf16_b64_blk32_D2048_N16_7hooks"
+    # an event between every call of this step costs ~2.6 us per call (the
+    # eager step with them against the graph-replayed step without them), so
+    # each entry point is timed again in a loop of its own calls
+    isolate_entries = True
+
+    def setup(self, torch, r2l):
+        super().setup(torch, r2l)
+        tok = self.B * self.L
+        # checkpoint rows written (and read back): one per started group of 8
+        # visited tokens of each sequence (the buffer also holds one unused
+        # row per sequence and one more, which are not traffic)
+        ck_bytes = self.B * ((self.L + 7) // 8) * self.D * 16 * 4
+        fwd_bytes = scan_bytes(tok, self.D, 2, readout=True) + ck_bytes
+        bwd_bytes = self.bytes_per_launch + ck_bytes
+        fwd_alu = self.tc_per_launch * alu_ops_per_tc(True, True)
+        # the backward's algorithmic work without the forward states, which the
+        # saving forward computed already
+        bwd_alu = self.tc_per_launch * (bwd_alu_ops_per_tc() - alu_ops_per_tc(False, False))
+        self.step_calls, self.train_grads = [], []
+        save_calls, bwd_calls = [], []
+        for r in range(self.R):
+            row = []
+            for h in range(self.HOOKS):
+                ins = self._bound_inputs[r][h]
+                x = ins["x"]
+                sc = r2l.bind("r2l_scan_save", x=x, res=x, s=float(self.gates[h]),
+                              out=self.outs0[h] if r == 0 else torch.empty_like(x),
+                              **{k: v for k, v in ins.items() if k != "x"})
+                bc = r2l.bind_backward(x, ins["dt"], ins["Bm"], ins["Cm"], ins["A"],
+                                       ins["Dskip"], dout=self._douts[r][h], res=x,
+                                       s=float(self.gates[h]), ckpt=sc.ckpt)
+                row += [sc, bc]
+                save_calls.append(sc)
+                bwd_calls.append(bc)
+                if r == 0:
+                    self.train_grads.append((h, self._douts[r][h], bc.grads))
+            self.step_calls.append(row)
+        self.bwd_calls = None
+        self.bwd_grads = self.train_grads
+        self.step_entries = [0, 1] * self.HOOKS
+        self.launches_per_step = 2 * self.HOOKS
+        self.measure = [dict(label="r2l_scan_save (one hook)", calls=save_calls,
+                             bytes=fwd_bytes, alu=fwd_alu, tc=self.tc_per_launch),
+                        dict(label="r2l_scan_backward_saved (one hook)", calls=bwd_calls,
+                             bytes=bwd_bytes, alu=bwd_alu, tc=self.tc_per_launch)]
+        self.config = dict(self.config, workload=self.name,
+                           op="r2l_scan_save + r2l_scan_backward_saved",
+                           checkpoint_bytes_per_hook=ck_bytes)
+
+    def cpu_baseline(self, budget_s, nthreads=0, parity=None):
+        import oracle
+        if parity is not None:   # the saving forward's outputs of the first buffer set
+            fwd = Parity("out", "bf16", 2e-2)
+            for h, inp in enumerate(self.inputs):
+                r = oracle.selective_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip,
+                                          reverse=True, res=inp.x, s=float(self.gates[h]),
+                                          seq_offsets=inp.offsets, want_y=False,
+                                          want_out=True, nthreads=nthreads)
+                fwd.add(self.outs0[h].float().cpu().numpy().reshape(r["out"].shape), r["out"])
+            self.parity_extra = dict(fwd.result(), sample="out = x + s*y of all 7 hooks "
+                                     "(first buffer set) vs the oracle's")
+        return super().cpu_baseline(budget_s, nthreads, parity)
+
+    parity_spec = ("dA, dBm", "f32", 1e-4,
+                   "dA and dBm of the backward from the saved checkpoints, all 7 hooks (first "
+                   "buffer set) vs the oracle's fp64 backward; the forward's out in 'forward'")
 
 
 class DenoiseL2R(Denoise):
@@ -1074,7 +1153,7 @@ SERVING_KEY = 107
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
              "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward,
              "bidir": DenoiseBidir, "sidecar": DenoiseSidecar, "serving": ServingStep,
-             "prefill_bwd": PrefillBackward}
+             "prefill_bwd": PrefillBackward, "denoise_train": DenoiseTrain}
 
 
 def main():
@@ -1159,10 +1238,27 @@ def main():
         dur = [marks[k].elapsed_time(marks[k + 1]) for k in range(len(call_ev))]
         for e, m in enumerate(wl.measure):
             mine = [d for k, d in enumerate(dur) if entries[k % len(entries)] == e]
-            timed.append(dict(m, ms=sum(mine) / len(mine), reps=len(mine)))
+            timed.append(dict(m, ms=sum(mine) / len(mine), reps=len(mine), src=m))
         n = len(entries)
         step_ms = [sum(dur[i * n:(i + 1) * n]) for i in range(args.steps)]
         spread_how = "per-step sums of the per-call events of the timed region"
+        if wl.isolate_entries and not args.queue_ahead:
+            # each entry point's calls again, back to back in a loop of their own
+            # between two events (no event between the calls)
+            for t in timed:
+                calls = t["calls"]
+                reps = args.steps * sum(1 for e in entries if wl.measure[e] is t["src"])
+                for c in calls:
+                    c.launch(stream)
+                a0, a1 = ev(), ev()
+                torch.cuda.synchronize()
+                a0.record()
+                for k in range(reps):
+                    calls[k % len(calls)].launch(stream)
+                a1.record()
+                torch.cuda.synchronize()
+                t["ms_per_call_events"] = t["ms"]
+                t["ms"], t["reps"] = a0.elapsed_time(a1) / reps, reps
         step_split = {t["label"]: round(t["ms"] * sum(1 for e in entries if e == k), 4)
                       for k, t in enumerate(timed)}
     elif args.queue_ahead:
@@ -1235,7 +1331,14 @@ def main():
     for m in timed:
         bind_, other_ = rooflines(m)
         kernels.append({"entry": m["label"], "avg_launch_us": round(m["ms"] * 1e3, 3),
-                        "launches_timed": m["reps"], "bytes_per_launch": m["bytes"],
+                        "launches_timed": m["reps"],
+                        "timed_how": ("its calls back to back in a loop of their own, two events"
+                                      if "ms_per_call_events" in m else
+                                      "events of the timed region"),
+                        "avg_launch_us_per_call_events": (
+                            round(m["ms_per_call_events"] * 1e3, 3)
+                            if "ms_per_call_events" in m else None),
+                        "bytes_per_launch": m["bytes"],
                         "tc_per_launch": m["tc"], "tc_per_s": m["tc"] / (m["ms"] * 1e-3),
                         "roofline": bind_, "roofline_other": other_})
     binding, other = kernels[0]["roofline"], kernels[0]["roofline_other"]
@@ -1247,6 +1350,10 @@ def main():
         par = Parity(what, pdtype, tol)
         cpu = wl.cpu_baseline(args.cpu_seconds, parity=par)
         parity = dict(par.result(), sample=sample)
+        extra = getattr(wl, "parity_extra", None)
+        if extra:
+            parity["forward"] = extra
+            parity["pass"] = parity["pass"] and extra["pass"]
         single = wl.cpu_baseline(args.cpu_seconds / 4, nthreads=1)
         cpu.update(single_thread_value=single["value"], single_thread_sample=single["sample"],
                    **host_cpu())

@@ -149,14 +149,20 @@ class BoundCall:
     change between launches, their storage may not.
     """
 
-    def __init__(self, func, op, args, keep, workspace, device, rev=None):
+    def __init__(self, func, op, args, keep, workspace, device, rev=None, ckpt=None):
         self.func, self.op, self.args = func, op, args
         self._keep, self.workspace, self.device = keep, workspace, device
         self._fn = getattr(_abi.load(), func)
         self._ref = _abi.ctypes.byref(args)
-        # bidir_scan takes the reverse direction's struct (or NULL) as well
-        self.rev = rev
-        self._refs = (self._ref, _abi._dir_ref(rev)) if func == "bidir_scan" else (self._ref,)
+        # bidir_scan takes the reverse direction's struct (or NULL) as well,
+        # r2l_scan_save the checkpoint buffer and its size
+        self.rev, self.ckpt = rev, ckpt
+        if func == "bidir_scan":
+            self._refs = (self._ref, _abi._dir_ref(rev))
+        elif func == "r2l_scan_save":
+            self._refs = (self._ref, _abi._fptr(ckpt.data_ptr()), ckpt.numel() * 4)
+        else:
+            self._refs = (self._ref,)
 
     def plan(self) -> dict:
         """The plan the library picks for this call (lanes per channel, chunking,
@@ -175,15 +181,23 @@ class BoundCall:
 
 def bind(op: str, **kw) -> BoundCall:
     """Check and marshal the arguments of ``r2l_scan``, ``prefix_scan_state``,
-    ``block_commit_state`` or ``bidir_scan`` once (same keywords as those
-    functions; outputs must be given) and return a :class:`BoundCall`.
+    ``block_commit_state``, ``bidir_scan`` or ``r2l_scan_save`` once (same
+    keywords as those functions; outputs must be given; the checkpoints of
+    ``r2l_scan_save`` are allocated here unless ``ckpt`` is given, and are the
+    returned object's ``ckpt``) and return a :class:`BoundCall`.
     """
     kw = dict(kw)
     ws = kw.pop("workspace", None)
     rev = kw.pop("rev", None)
+    ckpt = kw.pop("ckpt", None)
     if rev is not None and op != "bidir_scan":
         raise ValueError("rev is an argument of bidir_scan only")
-    if op == "bidir_scan":
+    if ckpt is not None and op != "r2l_scan_save":
+        raise ValueError("ckpt is an argument of r2l_scan_save only")
+    if op == "r2l_scan_save":
+        func, code = "r2l_scan_save", _abi.R2L_OP_SAVE
+        kw["state_split"] = 1
+    elif op == "bidir_scan":
         func, code = "bidir_scan", _abi.R2L_OP_BIDIR
     elif op == "r2l_scan":
         func, code = "r2l_scan", _abi.R2L_OP_SCAN
@@ -195,7 +209,7 @@ def bind(op: str, **kw) -> BoundCall:
     else:
         raise ValueError("unknown entry point %r" % op)
     x = kw["x"]
-    if op in ("r2l_scan", "bidir_scan") and kw.get("out") is None:
+    if op in ("r2l_scan", "bidir_scan", "r2l_scan_save") and kw.get("out") is None:
         raise ValueError("bind() needs the output tensor")
     names = ("x", "dt", "Bm", "Cm", "A", "Dskip", "cu_seqlens", "max_seqlen", "h_in", "h_out",
              "res", "s", "out", "delta_softplus", "chunk_tokens", "state_split")
@@ -210,7 +224,18 @@ def bind(op: str, **kw) -> BoundCall:
     r = _fill_dir(a, x, rev) if op == "bidir_scan" else None
     ws = _attach_workspace(code, a, ws, x.device)
     keep = [v for v in vals if isinstance(v, torch.Tensor)] + list((rev or {}).values())
-    return BoundCall(func, code, a, keep, ws, x.device, rev=r)
+    if op == "r2l_scan_save":
+        ckpt = _checkpoints(a, ckpt, x.device)
+    return BoundCall(func, code, a, keep, ws, x.device, rev=r, ckpt=ckpt)
+
+
+def _checkpoints(a, ckpt, device):
+    need = _abi.checkpoint_size(a)
+    if ckpt is None:
+        return torch.empty(max(need // 4, 1), dtype=torch.float32, device=device)
+    if ckpt.dtype != torch.float32 or not ckpt.is_contiguous() or ckpt.numel() * 4 < need:
+        raise ValueError("ckpt must be a contiguous fp32 tensor of at least %d bytes" % need)
+    return ckpt
 
 
 def workspace_size(op: str, x, A, *, cu_seqlens=None, max_seqlen=None, out=True,
@@ -262,11 +287,7 @@ def r2l_scan_save(x, dt, Bm, Cm, A, Dskip=None, *, cu_seqlens=None, max_seqlen=N
         out = torch.empty_like(x)
     a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
               delta_softplus, chunk_tokens, 1)
-    need = _abi.checkpoint_size(a)
-    if ckpt is None:
-        ckpt = torch.empty(max(need // 4, 1), dtype=torch.float32, device=x.device)
-    elif ckpt.dtype != torch.float32 or not ckpt.is_contiguous() or ckpt.numel() * 4 < need:
-        raise ValueError("ckpt must be a contiguous fp32 tensor of at least %d bytes" % need)
+    ckpt = _checkpoints(a, ckpt, x.device)
     workspace = _attach_workspace(_abi.R2L_OP_SAVE, a, workspace, x.device)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
@@ -532,17 +553,22 @@ class BoundBackward:
     """One r2l_scan_backward call with its argument structs filled once (see
     BoundCall); ``grads`` holds the output tensors."""
 
-    def __init__(self, args, grad, keep, grads, workspace, device, reverse=True):
+    def __init__(self, args, grad, keep, grads, workspace, device, reverse=True, ckpt=None):
         self.args, self.grad, self._keep = args, grad, keep
         self.grads, self.workspace, self.device = grads, workspace, device
         self.func = "r2l_scan_backward" if reverse else "prefix_scan_backward"
-        self._fn = getattr(_abi.load(), self.func)
         self._a, self._g = _abi.ctypes.byref(args), _abi.ctypes.byref(grad)
+        self._refs = (self._a, self._g)
+        self.ckpt = ckpt
+        if ckpt is not None:   # from the checkpoints of r2l_scan_save
+            self.func = "r2l_scan_backward_saved"
+            self._refs = (self._a, self._g, _abi._fptr(ckpt.data_ptr()), ckpt.numel() * 4)
+        self._fn = getattr(_abi.load(), self.func)
 
     def launch(self, stream=None):
         if stream is None:
             stream = torch.cuda.current_stream(self.device).cuda_stream
-        st = self._fn(self._a, self._g, _abi._vp(stream))
+        st = self._fn(*self._refs, _abi._vp(stream))
         if st != _abi.R2L_OK:
             raise R2LError(st, self.func, _abi.last_error())
 
@@ -574,8 +600,10 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
     planning hint of the backward's state pass (0: the library chooses).
     ``ckpt``: the checkpoints ``r2l_scan_save`` stored for the same forward
     arguments; the backward then runs no forward state pass."""
-    if ckpt is not None and (not _reverse or _bind):
+    if ckpt is not None and not _reverse:
         raise ValueError("saved checkpoints serve r2l_scan_backward only")
+    if ckpt is not None and (ckpt.dtype != torch.float32 or not ckpt.is_contiguous()):
+        raise ValueError("ckpt must be a contiguous fp32 tensor")
     a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, None, res, s, None,
               delta_softplus, chunk_tokens, 0)
     D, N = int(a.dim), int(a.dstate)
@@ -603,12 +631,10 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
         g.workspace, g.workspace_bytes = workspace.data_ptr(), need
     if _bind:
         keep = (x, dt, Bm, Cm, A, Dskip, dout, dh_out, cu_seqlens, h_in, res)
-        return BoundBackward(a, g, keep, outs, workspace, x.device, reverse=_reverse)
+        return BoundBackward(a, g, keep, outs, workspace, x.device, reverse=_reverse, ckpt=ckpt)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
     if ckpt is not None:
-        if ckpt.dtype != torch.float32 or not ckpt.is_contiguous():
-            raise ValueError("ckpt must be a contiguous fp32 tensor")
         _abi.call_backward_saved(a, g, ckpt.data_ptr(), ckpt.numel() * 4, stream)
     else:
         _abi.call_backward(a, g, stream, reverse=_reverse)

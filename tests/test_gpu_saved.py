@@ -198,3 +198,23 @@ def test_saved_rejects_bad_checkpoints(gpu):
                   kw["max_seqlen"], None, None, None, 0.0, torch.empty_like(x), True, 0, 2)
     with pytest.raises(r2l.R2LError):
         r2l._abi.call_save(a, full.data_ptr(), need, None)
+
+
+def test_saved_bound_calls(gpu):
+    """bind("r2l_scan_save") and bind_backward(ckpt=...) launch the same calls
+    as the functions, bit for bit, on every launch."""
+    inp = synth.scan_inputs(64, [32] * 4, D=128, dtype="bf16", dt_mean=-3.0)
+    x, kw, shaped = device_inputs(inp, True, "bf16")
+    dout = torch.randn_like(x)
+    out0, ck0 = r2l.r2l_scan_save(x, **kw, res=x, s=0.2)
+    g0 = r2l.r2l_scan_backward(x, **kw, dout=dout, res=x, s=0.2, ckpt=ck0)
+    out1 = torch.empty_like(x)
+    sc = r2l.bind("r2l_scan_save", x=x, res=x, s=0.2, out=out1, **kw)
+    bc = r2l.bind_backward(x, **kw, dout=dout, res=x, s=0.2, ckpt=sc.ckpt)
+    for _ in range(2):
+        sc.launch()
+        bc.launch()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out1), bits(out0))
+        for name in g0:
+            assert np.array_equal(bits(bc.grads[name]), bits(g0[name])), name
