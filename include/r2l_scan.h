@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define R2L_ABI_VERSION 4
+#define R2L_ABI_VERSION 5
 
 /* exported from libr2l_scan.so (everything else in it is hidden) */
 #if defined(__GNUC__)
@@ -115,7 +115,8 @@ typedef int32_t r2l_status;
 #define R2L_OP_PREFIX 1
 #define R2L_OP_COMMIT 2
 #define R2L_OP_BIDIR 3
-#define R2L_OP_SAVE 4   /* r2l_scan_save */
+#define R2L_OP_SAVE 4          /* r2l_scan_save */
+#define R2L_OP_PREFIX_SAVE 5   /* prefix_scan_save */
 
 typedef struct r2l_scan_args {
     /* ---- shape ---- */
@@ -307,6 +308,20 @@ R2L_API r2l_status r2l_checkpoint_size(const r2l_scan_args *a, size_t *bytes);
  */
 R2L_API r2l_status r2l_scan_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
                                            const float *ckpt, size_t ckpt_bytes, void *stream);
+
+/*
+ * prefix_scan_save / prefix_scan_backward_saved -- the same pair for the
+ * left-to-right stream (prefix_scan_state with a readout, and
+ * prefix_scan_backward): visited positions count from each sequence's first
+ * token; the rows, sizes (r2l_checkpoint_size), checks and guarantees are those
+ * above; the workspace of the saving call is sized with R2L_OP_PREFIX_SAVE.
+ * Source: "Bifocal Diffusion Language Models", section 4 (the ablation that
+ * trains a left-to-right stream in place of the right-to-left one).
+ */
+R2L_API r2l_status prefix_scan_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes,
+                                    void *stream);
+R2L_API r2l_status prefix_scan_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                              const float *ckpt, size_t ckpt_bytes, void *stream);
 
 /*
  * bidir_scan -- the bidirectional full-window scan: over each whole sequence,

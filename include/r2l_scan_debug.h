@@ -48,14 +48,16 @@ R2L_API r2l_status r2l_check_access_backward(int32_t reverse, const r2l_scan_arg
                                              r2l_access_report *report);
 
 /*
- * The same replays for r2l_scan_save (the checkpoints are one more output
- * buffer) and r2l_scan_backward_saved (the checkpoints an input the replay
- * treats as written).
+ * The same replays for r2l_scan_save / prefix_scan_save (reverse 1 / 0; the
+ * checkpoints are one more output buffer, and every row the backward reads
+ * must be written) and r2l_scan_backward_saved / prefix_scan_backward_saved
+ * (the checkpoints an input the replay treats as written).
  */
-R2L_API r2l_status r2l_check_access_save(const r2l_scan_args *a, const float *ckpt,
-                                         size_t ckpt_bytes, const int32_t *cu_seqlens_host,
+R2L_API r2l_status r2l_check_access_save(int32_t reverse, const r2l_scan_args *a,
+                                         const float *ckpt, size_t ckpt_bytes,
+                                         const int32_t *cu_seqlens_host,
                                          r2l_access_report *report);
-R2L_API r2l_status r2l_check_access_backward_saved(const r2l_scan_args *fwd,
+R2L_API r2l_status r2l_check_access_backward_saved(int32_t reverse, const r2l_scan_args *fwd,
                                                    const r2l_grad_args *grad, const float *ckpt,
                                                    size_t ckpt_bytes,
                                                    const int32_t *cu_seqlens_host,

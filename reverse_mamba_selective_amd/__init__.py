@@ -28,7 +28,8 @@ __all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "bidir_scan", 
            "workspace_size", "bind",
            "BoundCall", "R2LError", "library_path", "r2l_scan_backward", "prefix_scan_backward",
            "bind_backward",
-           "BoundBackward", "R2LScan", "GRADS", "r2l_scan_save", "checkpoint_size"]
+           "BoundBackward", "R2LScan", "GRADS", "r2l_scan_save", "prefix_scan_save",
+           "checkpoint_size"]
 
 _DTYPES = {torch.float32: _abi.R2L_DTYPE_F32, torch.bfloat16: _abi.R2L_DTYPE_BF16}
 
@@ -159,7 +160,7 @@ class BoundCall:
         self.rev, self.ckpt = rev, ckpt
         if func == "bidir_scan":
             self._refs = (self._ref, _abi._dir_ref(rev))
-        elif func == "r2l_scan_save":
+        elif func in ("r2l_scan_save", "prefix_scan_save"):
             self._refs = (self._ref, _abi._fptr(ckpt.data_ptr()), ckpt.numel() * 4)
         else:
             self._refs = (self._ref,)
@@ -192,10 +193,13 @@ def bind(op: str, **kw) -> BoundCall:
     ckpt = kw.pop("ckpt", None)
     if rev is not None and op != "bidir_scan":
         raise ValueError("rev is an argument of bidir_scan only")
-    if ckpt is not None and op != "r2l_scan_save":
-        raise ValueError("ckpt is an argument of r2l_scan_save only")
+    if ckpt is not None and op not in ("r2l_scan_save", "prefix_scan_save"):
+        raise ValueError("ckpt is an argument of r2l_scan_save and prefix_scan_save only")
     if op == "r2l_scan_save":
         func, code = "r2l_scan_save", _abi.R2L_OP_SAVE
+        kw["state_split"] = 1
+    elif op == "prefix_scan_save":
+        func, code = "prefix_scan_save", _abi.R2L_OP_PREFIX_SAVE
         kw["state_split"] = 1
     elif op == "bidir_scan":
         func, code = "bidir_scan", _abi.R2L_OP_BIDIR
@@ -209,7 +213,8 @@ def bind(op: str, **kw) -> BoundCall:
     else:
         raise ValueError("unknown entry point %r" % op)
     x = kw["x"]
-    if op in ("r2l_scan", "bidir_scan", "r2l_scan_save") and kw.get("out") is None:
+    if op in ("r2l_scan", "bidir_scan", "r2l_scan_save", "prefix_scan_save") and \
+            kw.get("out") is None:
         raise ValueError("bind() needs the output tensor")
     names = ("x", "dt", "Bm", "Cm", "A", "Dskip", "cu_seqlens", "max_seqlen", "h_in", "h_out",
              "res", "s", "out", "delta_softplus", "chunk_tokens", "state_split")
@@ -224,7 +229,7 @@ def bind(op: str, **kw) -> BoundCall:
     r = _fill_dir(a, x, rev) if op == "bidir_scan" else None
     ws = _attach_workspace(code, a, ws, x.device)
     keep = [v for v in vals if isinstance(v, torch.Tensor)] + list((rev or {}).values())
-    if op == "r2l_scan_save":
+    if op in ("r2l_scan_save", "prefix_scan_save"):
         ckpt = _checkpoints(a, ckpt, x.device)
     return BoundCall(func, code, a, keep, ws, x.device, rev=r, ckpt=ckpt)
 
@@ -241,10 +246,10 @@ def _checkpoints(a, ckpt, device):
 def workspace_size(op: str, x, A, *, cu_seqlens=None, max_seqlen=None, out=True,
                    chunk_tokens=0, state_split=0) -> int:
     """Workspace bytes for op in {"r2l_scan", "prefix_scan_state", "block_commit_state",
-    "bidir_scan", "r2l_scan_save"}."""
+    "bidir_scan", "r2l_scan_save", "prefix_scan_save"}."""
     codes = {"r2l_scan": _abi.R2L_OP_SCAN, "prefix_scan_state": _abi.R2L_OP_PREFIX,
              "block_commit_state": _abi.R2L_OP_COMMIT, "bidir_scan": _abi.R2L_OP_BIDIR,
-             "r2l_scan_save": _abi.R2L_OP_SAVE}
+             "r2l_scan_save": _abi.R2L_OP_SAVE, "prefix_scan_save": _abi.R2L_OP_PREFIX_SAVE}
     a = _fill(x, None, None, None, A, None, cu_seqlens, max_seqlen, None, None, None, 0.0,
               None, True, chunk_tokens, state_split)
     if out:
@@ -278,7 +283,7 @@ def checkpoint_size(x, A, *, cu_seqlens=None, max_seqlen=None) -> int:
 
 def r2l_scan_save(x, dt, Bm, Cm, A, Dskip=None, *, cu_seqlens=None, max_seqlen=None,
                   h_in=None, h_out=None, res=None, s=0.0, out=None, delta_softplus=True,
-                  chunk_tokens=0, ckpt=None, workspace=None):
+                  chunk_tokens=0, ckpt=None, workspace=None, _reverse=True):
     """``r2l_scan`` that also stores the states the backward needs (the state
     entering every 8th visited position of each sequence). Returns (out, ckpt);
     ckpt is an fp32 tensor to hand to ``r2l_scan_backward(..., ckpt=ckpt)``
@@ -288,11 +293,19 @@ def r2l_scan_save(x, dt, Bm, Cm, A, Dskip=None, *, cu_seqlens=None, max_seqlen=N
     a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
               delta_softplus, chunk_tokens, 1)
     ckpt = _checkpoints(a, ckpt, x.device)
-    workspace = _attach_workspace(_abi.R2L_OP_SAVE, a, workspace, x.device)
+    op = _abi.R2L_OP_SAVE if _reverse else _abi.R2L_OP_PREFIX_SAVE
+    workspace = _attach_workspace(op, a, workspace, x.device)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    _abi.call_save(a, ckpt.data_ptr(), ckpt.numel() * 4, stream)
+    _abi.call_save(a, ckpt.data_ptr(), ckpt.numel() * 4, stream, reverse=_reverse)
     return out, ckpt
+
+
+def prefix_scan_save(x, dt, Bm, Cm, A, Dskip=None, **kw):
+    """The left-to-right stream (``prefix_scan_state`` with readout into
+    ``out``) that also stores the backward's checkpoints; same keywords and
+    result as ``r2l_scan_save``; hand ckpt to ``prefix_scan_backward``."""
+    return r2l_scan_save(x, dt, Bm, Cm, A, Dskip, _reverse=False, **kw)
 
 
 def prefix_scan_state(x, dt, Bm, A, *, cu_seqlens=None, max_seqlen=None, h_in=None,
@@ -560,8 +573,8 @@ class BoundBackward:
         self._a, self._g = _abi.ctypes.byref(args), _abi.ctypes.byref(grad)
         self._refs = (self._a, self._g)
         self.ckpt = ckpt
-        if ckpt is not None:   # from the checkpoints of r2l_scan_save
-            self.func = "r2l_scan_backward_saved"
+        if ckpt is not None:   # from the checkpoints of r2l_scan_save / prefix_scan_save
+            self.func = self.func + "_saved"
             self._refs = (self._a, self._g, _abi._fptr(ckpt.data_ptr()), ckpt.numel() * 4)
         self._fn = getattr(_abi.load(), self.func)
 
@@ -600,8 +613,6 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
     planning hint of the backward's state pass (0: the library chooses).
     ``ckpt``: the checkpoints ``r2l_scan_save`` stored for the same forward
     arguments; the backward then runs no forward state pass."""
-    if ckpt is not None and not _reverse:
-        raise ValueError("saved checkpoints serve r2l_scan_backward only")
     if ckpt is not None and (ckpt.dtype != torch.float32 or not ckpt.is_contiguous()):
         raise ValueError("ckpt must be a contiguous fp32 tensor")
     a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, None, res, s, None,
@@ -635,7 +646,7 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
     if ckpt is not None:
-        _abi.call_backward_saved(a, g, ckpt.data_ptr(), ckpt.numel() * 4, stream)
+        _abi.call_backward_saved(a, g, ckpt.data_ptr(), ckpt.numel() * 4, stream, reverse=_reverse)
     else:
         _abi.call_backward(a, g, stream, reverse=_reverse)
     return outs

@@ -27,8 +27,9 @@ R2L_OP_PREFIX = 1
 R2L_OP_COMMIT = 2
 R2L_OP_BIDIR = 3
 R2L_OP_SAVE = 4
+R2L_OP_PREFIX_SAVE = 5
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
@@ -36,7 +37,8 @@ EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace
            "r2l_check_access_backward", "prefix_scan_backward", "bidir_scan",
            "r2l_check_access_bidir", "r2l_sidecar_forward", "r2l_sidecar_workspace_size",
            "r2l_check_access_sidecar", "r2l_sidecar_tune", "r2l_scan_save", "r2l_checkpoint_size",
-           "r2l_scan_backward_saved", "r2l_check_access_save", "r2l_check_access_backward_saved")
+           "r2l_scan_backward_saved", "r2l_check_access_save", "r2l_check_access_backward_saved",
+           "prefix_scan_save", "prefix_scan_backward_saved")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -154,17 +156,20 @@ def load(path: str = LIB_PATH):
     lib.r2l_check_access_backward.argtypes = [_i32, ptr, gptr, ctypes.POINTER(_i32),
                                               ctypes.POINTER(AccessReport)]
     fptr, szt = ctypes.POINTER(ctypes.c_float), ctypes.c_size_t
-    lib.r2l_scan_save.restype = _i32
-    lib.r2l_scan_save.argtypes = [ptr, fptr, szt, _vp]
+    for fn in (lib.r2l_scan_save, lib.prefix_scan_save):
+        fn.restype = _i32
+        fn.argtypes = [ptr, fptr, szt, _vp]
     lib.r2l_checkpoint_size.restype = _i32
     lib.r2l_checkpoint_size.argtypes = [ptr, ctypes.POINTER(szt)]
-    lib.r2l_scan_backward_saved.restype = _i32
-    lib.r2l_scan_backward_saved.argtypes = [ptr, gptr, fptr, szt, _vp]
+    for fn in (lib.r2l_scan_backward_saved, lib.prefix_scan_backward_saved):
+        fn.restype = _i32
+        fn.argtypes = [ptr, gptr, fptr, szt, _vp]
     lib.r2l_check_access_save.restype = _i32
-    lib.r2l_check_access_save.argtypes = [ptr, fptr, szt, ctypes.POINTER(_i32),
+    lib.r2l_check_access_save.argtypes = [_i32, ptr, fptr, szt, ctypes.POINTER(_i32),
                                           ctypes.POINTER(AccessReport)]
     lib.r2l_check_access_backward_saved.restype = _i32
-    lib.r2l_check_access_backward_saved.argtypes = [ptr, gptr, fptr, szt, ctypes.POINTER(_i32),
+    lib.r2l_check_access_backward_saved.argtypes = [_i32, ptr, gptr, fptr, szt,
+                                                    ctypes.POINTER(_i32),
                                                     ctypes.POINTER(AccessReport)]
     dptr = ctypes.POINTER(DirArgs)
     lib.bidir_scan.restype = _i32
@@ -275,36 +280,42 @@ def checkpoint_size(args: ScanArgs) -> int:
     return int(n.value)
 
 
-def call_save(args: ScanArgs, ckpt: int, ckpt_bytes: int, stream: int | None) -> None:
-    st = load().r2l_scan_save(ctypes.byref(args), _fptr(ckpt), ckpt_bytes, _vp(stream or 0))
+def call_save(args: ScanArgs, ckpt: int, ckpt_bytes: int, stream: int | None,
+              reverse: bool = True) -> None:
+    func = "r2l_scan_save" if reverse else "prefix_scan_save"
+    st = getattr(load(), func)(ctypes.byref(args), _fptr(ckpt), ckpt_bytes, _vp(stream or 0))
     if st != R2L_OK:
-        raise R2LError(st, "r2l_scan_save", last_error())
+        raise R2LError(st, func, last_error())
 
 
 def call_backward_saved(args: ScanArgs, grad: GradArgs, ckpt: int, ckpt_bytes: int,
-                        stream: int | None) -> None:
-    st = load().r2l_scan_backward_saved(ctypes.byref(args), ctypes.byref(grad), _fptr(ckpt),
-                                        ckpt_bytes, _vp(stream or 0))
+                        stream: int | None, reverse: bool = True) -> None:
+    func = "r2l_scan_backward_saved" if reverse else "prefix_scan_backward_saved"
+    st = getattr(load(), func)(ctypes.byref(args), ctypes.byref(grad), _fptr(ckpt), ckpt_bytes,
+                               _vp(stream or 0))
     if st != R2L_OK:
-        raise R2LError(st, "r2l_scan_backward_saved", last_error())
+        raise R2LError(st, func, last_error())
 
 
-def check_access_save(args: ScanArgs, ckpt: int, ckpt_bytes: int, cu_seqlens_host=None):
-    """Host replay of r2l_scan_save; (status, report)."""
+def check_access_save(args: ScanArgs, ckpt: int, ckpt_bytes: int, cu_seqlens_host=None,
+                      reverse: bool = True):
+    """Host replay of r2l_scan_save (prefix_scan_save); (status, report)."""
     rep = AccessReport()
     keep, cu = _cu_ptr(cu_seqlens_host)
-    st = load().r2l_check_access_save(ctypes.byref(args), _fptr(ckpt), ckpt_bytes, cu,
-                                      ctypes.byref(rep))
+    st = load().r2l_check_access_save(1 if reverse else 0, ctypes.byref(args), _fptr(ckpt),
+                                      ckpt_bytes, cu, ctypes.byref(rep))
     return st, rep
 
 
 def check_access_backward_saved(args: ScanArgs, grad: GradArgs, ckpt: int, ckpt_bytes: int,
-                                cu_seqlens_host=None):
-    """Host replay of r2l_scan_backward_saved; (status, report)."""
+                                cu_seqlens_host=None, reverse: bool = True):
+    """Host replay of r2l_scan_backward_saved (prefix_scan_backward_saved);
+    (status, report)."""
     rep = AccessReport()
     keep, cu = _cu_ptr(cu_seqlens_host)
-    st = load().r2l_check_access_backward_saved(ctypes.byref(args), ctypes.byref(grad), _fptr(ckpt),
-                                                ckpt_bytes, cu, ctypes.byref(rep))
+    st = load().r2l_check_access_backward_saved(1 if reverse else 0, ctypes.byref(args),
+                                                ctypes.byref(grad), _fptr(ckpt), ckpt_bytes, cu,
+                                                ctypes.byref(rep))
     return st, rep
 
 

@@ -799,7 +799,7 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
     if (pl.chunked) ck.set_workspace(a->workspace, pl.ws_bytes);
     if (saving) ck.track(ckpt, checkpoint_bytes(a));
     Launch ls[kMaxSaveLaunches];
-    const int n = saving ? build_save_launches(a, pl, ckpt, ls) : build_launches(op, a, pl, ls);
+    const int n = saving ? build_save_launches(op, a, pl, ckpt, ls) : build_launches(op, a, pl, ls);
     for (int i = 0; i < n && ck.ok(); ++i) {
         ++rep->launches;
         if (ls[i].kind == Launch::Segment) {

@@ -347,25 +347,28 @@ r2l_status check_ckpt(const r2l_scan_args *a, const void *ckpt, size_t bytes, bo
     return R2L_OK;
 }
 
-r2l_status prepare_save(const r2l_scan_args *a, r2l_scan_args *v, Plan *pl) {
+// op: Scan (r2l_scan_save) or Prefix (prefix_scan_save)
+r2l_status prepare_save(Op op, const r2l_scan_args *a, r2l_scan_args *v, Plan *pl) {
     r2l_status st = check_shape(a);
     if (st != R2L_OK) return st;
     if (a->state_split > 1)
-        return fail(R2L_ERR_UNSUPPORTED, "r2l_scan_save runs one lane per channel (state_split 0 or 1)");
+        return fail(R2L_ERR_UNSUPPORTED, "%s runs one lane per channel (state_split 0 or 1)",
+                    op == Op::Scan ? "r2l_scan_save" : "prefix_scan_save");
     *v = *a;
     v->state_split = 1;
-    *pl = r2l::make_plan(Op::Scan, v, true);
-    st = check_buffers(Op::Scan, v, *pl);
+    *pl = r2l::make_plan(op, v, true);
+    st = check_buffers(op, v, *pl);
     if (st != R2L_OK) return st;
     if (v->batch * pl->nchunks * pl->tiles > INT32_MAX - 8)
         return fail(R2L_ERR_UNSUPPORTED, "grid too large");
     return R2L_OK;
 }
 
-r2l_status run_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes, hipStream_t stream) {
+r2l_status run_save(Op op, const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes,
+                    hipStream_t stream) {
     r2l_scan_args v;
     Plan pl;
-    r2l_status st = prepare_save(a, &v, &pl);
+    r2l_status st = prepare_save(op, a, &v, &pl);
     if (st != R2L_OK) return st;
     st = check_ckpt(&v, ckpt, ckpt_bytes, true, pl.chunked ? v.workspace : nullptr,
                     pl.chunked ? pl.ws_bytes : 0);
@@ -373,7 +376,7 @@ r2l_status run_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes, hipS
     st = check_seqlens_on_device(&v);
     if (st != R2L_OK) return st;
     Launch ls[r2l::kMaxSaveLaunches];
-    const int n = r2l::build_save_launches(&v, pl, ckpt, ls);
+    const int n = r2l::build_save_launches(op, &v, pl, ckpt, ls);
     return execute(ls, n, stream);
 }
 
@@ -723,12 +726,21 @@ r2l_status r2l_checkpoint_size(const r2l_scan_args *a, size_t *bytes) {
 }
 
 r2l_status r2l_scan_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes, void *stream) {
-    return run_save(a, ckpt, ckpt_bytes, static_cast<hipStream_t>(stream));
+    return run_save(Op::Scan, a, ckpt, ckpt_bytes, static_cast<hipStream_t>(stream));
 }
 
 r2l_status r2l_scan_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
                                    const float *ckpt, size_t ckpt_bytes, void *stream) {
     return run_backward(true, fwd, grad, static_cast<hipStream_t>(stream), true, ckpt, ckpt_bytes);
+}
+
+r2l_status prefix_scan_save(const r2l_scan_args *a, float *ckpt, size_t ckpt_bytes, void *stream) {
+    return run_save(Op::Prefix, a, ckpt, ckpt_bytes, static_cast<hipStream_t>(stream));
+}
+
+r2l_status prefix_scan_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+                                      const float *ckpt, size_t ckpt_bytes, void *stream) {
+    return run_backward(false, fwd, grad, static_cast<hipStream_t>(stream), true, ckpt, ckpt_bytes);
 }
 
 r2l_status r2l_check_access_backward(int32_t reverse, const r2l_scan_args *fwd,
@@ -855,7 +867,7 @@ r2l_status block_commit_state(const r2l_scan_args *a, void *stream) {
 r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes) {
     if (!bytes) return fail(R2L_ERR_INVALID_ARG, "bytes is NULL");
     if (op != R2L_OP_SCAN && op != R2L_OP_PREFIX && op != R2L_OP_COMMIT && op != R2L_OP_BIDIR &&
-        op != R2L_OP_SAVE)
+        op != R2L_OP_SAVE && op != R2L_OP_PREFIX_SAVE)
         return fail(R2L_ERR_INVALID_ARG, "unknown op %d", op);
     r2l_status st = check_shape(a);
     if (st != R2L_OK) return st;
@@ -863,10 +875,10 @@ r2l_status r2l_workspace_size(int32_t op, const r2l_scan_args *a, size_t *bytes)
         *bytes = r2l::make_bidir_plan(a).ws_bytes;
         return ok();
     }
-    if (op == R2L_OP_SAVE) {
+    if (op == R2L_OP_SAVE || op == R2L_OP_PREFIX_SAVE) {
         r2l_scan_args v = *a;
         v.state_split = 1;
-        *bytes = r2l::make_plan(Op::Scan, &v, true).ws_bytes;
+        *bytes = r2l::make_plan(op == R2L_OP_SAVE ? Op::Scan : Op::Prefix, &v, true).ws_bytes;
         return ok();
     }
     const Op o = op == R2L_OP_SCAN ? Op::Scan : (op == R2L_OP_PREFIX ? Op::Prefix : Op::Commit);
@@ -902,27 +914,30 @@ r2l_status r2l_check_access(int32_t op, const r2l_scan_args *a, const int32_t *c
     return ok();
 }
 
-r2l_status r2l_check_access_save(const r2l_scan_args *a, const float *ckpt, size_t ckpt_bytes,
-                                 const int32_t *cu_seqlens_host, r2l_access_report *report) {
+r2l_status r2l_check_access_save(int32_t reverse, const r2l_scan_args *a, const float *ckpt,
+                                 size_t ckpt_bytes, const int32_t *cu_seqlens_host,
+                                 r2l_access_report *report) {
     if (!report) return fail(R2L_ERR_INVALID_ARG, "report is NULL");
     report->launches = report->accesses = report->vector_staging = 0;
     report->message[0] = '\0';
+    const Op op = reverse ? Op::Scan : Op::Prefix;
     r2l_scan_args v;
     Plan pl;
-    r2l_status st = prepare_save(a, &v, &pl);
+    r2l_status st = prepare_save(op, a, &v, &pl);
     if (st != R2L_OK) return st;
     st = check_ckpt(&v, ckpt, ckpt_bytes, true, pl.chunked ? v.workspace : nullptr,
                     pl.chunked ? pl.ws_bytes : 0);
     if (st != R2L_OK) return st;
     st = check_host_offsets(&v, cu_seqlens_host);
     if (st != R2L_OK) return st;
-    st = r2l::check_accesses(Op::Scan, &v, pl, cu_seqlens_host, report, const_cast<float *>(ckpt),
+    st = r2l::check_accesses(op, &v, pl, cu_seqlens_host, report, const_cast<float *>(ckpt),
                              ckpt_bytes);
     if (st != R2L_OK) return fail(st, "%s", report->message);
     return ok();
 }
 
-r2l_status r2l_check_access_backward_saved(const r2l_scan_args *fwd, const r2l_grad_args *grad,
+r2l_status r2l_check_access_backward_saved(int32_t reverse, const r2l_scan_args *fwd,
+                                           const r2l_grad_args *grad,
                                            const float *ckpt, size_t ckpt_bytes,
                                            const int32_t *cu_seqlens_host,
                                            r2l_access_report *report) {
@@ -939,7 +954,7 @@ r2l_status r2l_check_access_backward_saved(const r2l_scan_args *fwd, const r2l_g
     if (st != R2L_OK) return st;
     st = check_host_offsets(fwd, cu_seqlens_host);
     if (st != R2L_OK) return st;
-    st = r2l::check_backward_accesses(true, fwd, grad, pl, cu_seqlens_host, report, ckpt,
+    st = r2l::check_backward_accesses(reverse != 0, fwd, grad, pl, cu_seqlens_host, report, ckpt,
                                       ckpt_bytes);
     if (st != R2L_OK && report->message[0]) fail(st, "%s", report->message);
     return st == R2L_OK ? ok() : st;

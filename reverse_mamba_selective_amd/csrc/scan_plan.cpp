@@ -276,9 +276,9 @@ Launch ckpt_state_launch(bool reverse, const r2l_scan_args *a, int64_t fwd_tiles
 
 }  // namespace
 
-int build_save_launches(const r2l_scan_args *a, const Plan &pl, float *ckpt,
+int build_save_launches(Op op, const r2l_scan_args *a, const Plan &pl, float *ckpt,
                         Launch out[kMaxSaveLaunches]) {
-    int n = build_launches(Op::Scan, a, pl, out);
+    int n = build_launches(op, a, pl, out);
     bool stored = false;
     for (int i = 0; i < n; ++i)
         if (out[i].kind == Launch::Segment && (out[i].mode & kModeOutMask) != kModeState) {
@@ -287,7 +287,7 @@ int build_save_launches(const r2l_scan_args *a, const Plan &pl, float *ckpt,
             stored = true;
         }
     if (!stored && tokens_of(a) > 0 && a->batch > 0)
-        out[n++] = ckpt_state_launch(true, a, (a->dim + kWG - 1) / kWG, ckpt);
+        out[n++] = ckpt_state_launch(op == Op::Scan, a, (a->dim + kWG - 1) / kWG, ckpt);
     return n;
 }
 

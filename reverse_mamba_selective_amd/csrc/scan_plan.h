@@ -145,11 +145,12 @@ int build_sidecar_launches(const r2l_sidecar_args *a, const SidecarPlan &sp,
 // the entry point's checks. Returns the count.
 int build_launches(Op op, const r2l_scan_args *a, const Plan &pl, Launch out[3]);
 
-// r2l_scan_save: the r2l_scan launches (plan made with ckpt = true, one lane
-// per channel) whose readout scans also store the checkpoints at ckpt; when
-// no readout runs (s == 0), one more state-only scan stores them.
+// r2l_scan_save (op Scan) and prefix_scan_save (op Prefix): the launches of
+// the call (plan made with ckpt = true, one lane per channel) whose readout
+// scans also store the checkpoints at ckpt; when no readout runs (s == 0, or
+// a prefix call without one), one more state-only scan stores them.
 constexpr int kMaxSaveLaunches = 4;
-int build_save_launches(const r2l_scan_args *a, const Plan &pl, float *ckpt,
+int build_save_launches(Op op, const r2l_scan_args *a, const Plan &pl, float *ckpt,
                         Launch out[kMaxSaveLaunches]);
 // Bytes of the checkpoints of a call: ckpt_rows(tokens, batch) x D x kN fp32.
 size_t checkpoint_bytes(const r2l_scan_args *a);

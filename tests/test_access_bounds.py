@@ -383,23 +383,26 @@ def test_backward_benchmarked_shapes():
 
 
 # ---- the saving forward and the backward from its checkpoints -------------------------
-def check_save(**kw):
-    """Replay r2l_scan_save and then r2l_scan_backward_saved on its checkpoints."""
+def check_save(reverse=True, **kw):
+    """Replay r2l_scan_save (prefix_scan_save) and then the backward from its
+    checkpoints."""
     res = kw.pop("res", "none")
     a, cu = make_args("scan", res=res, **kw)
     # the saving forward plans its own workspace (chunks in whole groups of 8 tokens)
-    need = _abi.workspace_size(_abi.R2L_OP_SAVE, a)
+    need = _abi.workspace_size(_abi.R2L_OP_SAVE if reverse else _abi.R2L_OP_PREFIX_SAVE, a)
     heap = FakeHeap()
     heap.next = BASE + (1 << 40)
     a.workspace, a.workspace_bytes = (heap.alloc(need), need) if need else (None, 0)
+    if not reverse and not a.out and not a.h_out:   # prefix_scan_state needs out or h_out
+        a.h_out = heap.alloc(4 * a.batch * a.dim * 16)
     nbytes = _abi.checkpoint_size(a)
     ckpt = heap.alloc(nbytes)
-    st, rep = _abi.check_access_save(a, ckpt, nbytes, cu)
+    st, rep = _abi.check_access_save(a, ckpt, nbytes, cu, reverse=reverse)
     msg = rep.message.decode() or _abi.last_error()
     assert st == _abi.R2L_OK, "save %s: %s" % (kw, msg)
     heap.next = BASE + (2 << 40)
     g = make_grad(a, heap, dtype=kw.get("dtype", "bf16"), pad_row=kw.get("pad_row", 0))
-    st, brep = _abi.check_access_backward_saved(a, g, ckpt, nbytes, cu)
+    st, brep = _abi.check_access_backward_saved(a, g, ckpt, nbytes, cu, reverse=reverse)
     msg = brep.message.decode() or _abi.last_error()
     assert st == _abi.R2L_OK, "backward from checkpoints %s: %s" % (kw, msg)
     return a, rep, brep
@@ -411,17 +414,18 @@ SAVE_EDGE = BWD_EDGE + BWD_CHUNKED + [
 ]
 
 
+@pytest.mark.parametrize("reverse", [True, False], ids=["r2l", "l2r"])
 @pytest.mark.parametrize("case", range(len(SAVE_EDGE)))
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_save_and_saved_backward(case, dtype):
+def test_save_and_saved_backward(case, dtype, reverse):
     """Every checkpoint row the backward reads is written by the saving
     forward (the replay checks it), and neither call leaves its buffers."""
     kw = dict(SAVE_EDGE[case], dtype=dtype)
     kw.setdefault("D", 64)
     for res in ("none", "x", "sep", "inplace"):
         for h in (False, True):
-            check_save(res=res, h_in=h, h_out=h, **kw)
-    check_save(res="x", s=0.0, **kw)    # gate closed: a state-only scan stores them
+            check_save(res=res, h_in=h, h_out=h, reverse=reverse, **kw)
+    check_save(res="x", s=0.0, reverse=reverse, **kw)   # gate closed: a state-only scan stores them
 
 
 def test_save_plans():

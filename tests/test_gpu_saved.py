@@ -42,9 +42,9 @@ def device_inputs(inp, dense, dtype):
     return x, kw, shaped
 
 
-def run_saved(inp, dense, res_kind, s, with_hin, with_dhout, seed, chunk_tokens=0):
+def run_saved(inp, dense, res_kind, s, with_hin, with_dhout, seed, chunk_tokens=0, reverse=True):
     """Saving forward, then the backward from its checkpoints; both against
-    the oracle."""
+    the oracle (reverse False: the left-to-right pair)."""
     dtype = inp.dtype
     B, D = inp.batch, inp.x.shape[1]
     rng = np.random.default_rng(seed)
@@ -54,22 +54,22 @@ def run_saved(inp, dense, res_kind, s, with_hin, with_dhout, seed, chunk_tokens=
     h0 = synth.initial_state(seed, B, D, 16) if with_hin else None
     res_np = {"none": None, "x": inp.x,
               "separate": synth.scan_inputs(seed + 1, inp.lengths, D=D, dtype=dtype).x}[res_kind]
-    fwd = oracle.selective_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=True,
+    fwd = oracle.selective_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=reverse,
                                 seq_offsets=inp.offsets, h_in=h0, want_h_out=True, res=res_np,
                                 s=s, want_out=res_np is not None)
     ref = oracle.selective_scan_backward(
-        inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=True, dout=dout_np,
+        inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=reverse, dout=dout_np,
         dh_out=dh_out_np, res_kind=res_kind, s=s, seq_offsets=inp.offsets, h_in=h0)
 
     x, kw, shaped = device_inputs(inp, dense, dtype)
+    save = r2l.r2l_scan_save if reverse else r2l.prefix_scan_save
+    bwd = r2l.r2l_scan_backward if reverse else r2l.prefix_scan_backward
     res = None if res_np is None else (x if res_kind == "x" else shaped(dev(res_np, dtype)))
     h_in = dev32(h0) if with_hin else None
     h_out = torch.empty((B, D, 16), dtype=torch.float32, device="cuda")
-    out, ckpt = r2l.r2l_scan_save(x, **kw, h_in=h_in, h_out=h_out, res=res, s=s,
-                                  chunk_tokens=chunk_tokens)
-    g = r2l.r2l_scan_backward(x, **kw, dout=shaped(dev(dout_np, dtype)),
-                              dh_out=dev32(dh_out_np) if with_dhout else None, h_in=h_in,
-                              res=res, s=s, ckpt=ckpt)
+    out, ckpt = save(x, **kw, h_in=h_in, h_out=h_out, res=res, s=s, chunk_tokens=chunk_tokens)
+    g = bwd(x, **kw, dout=shaped(dev(dout_np, dtype)),
+            dh_out=dev32(dh_out_np) if with_dhout else None, h_in=h_in, res=res, s=s, ckpt=ckpt)
     torch.cuda.synchronize()
     if res is not None and s == 0.0:
         assert np.array_equal(bits(out), bits(res)), "s == 0: out is not res bit for bit"
@@ -218,3 +218,54 @@ def test_saved_bound_calls(gpu):
         assert np.array_equal(bits(out1), bits(out0))
         for name in g0:
             assert np.array_equal(bits(bc.grads[name]), bits(g0[name])), name
+
+
+# ---- the left-to-right pair (prefix_scan_save / prefix_scan_backward_saved) --------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("res_kind", ["none", "x", "separate"])
+def test_saved_l2r_ragged_edges(gpu, dtype, res_kind):
+    """The L2R stream's saving forward and backward: sequences of 0, 1 and
+    7..130 tokens, a channel tail."""
+    lengths = [5, 0, 1, 7, 8, 9, 64, 65, 130]
+    inp = synth.scan_inputs(71, lengths, D=100, dtype=dtype, dt_mean=-3.0)
+    for with_hin, with_dhout in ((False, False), (True, True)):
+        run_saved(inp, False, res_kind, 0.0 if res_kind == "none" else 0.4, with_hin,
+                  with_dhout, seed=72, reverse=False)
+
+
+@pytest.mark.parametrize("chunk", [13, 40])
+def test_saved_l2r_chunked_forward(gpu, chunk):
+    lengths = [5, 0, 1, 64, 65, 130, 300, 9]
+    inp = synth.scan_inputs(73, lengths, D=100, dtype="bf16", dt_mean=-3.0)
+    run_saved(inp, False, "x", 0.6, True, True, seed=74, chunk_tokens=chunk, reverse=False)
+
+
+def test_saved_l2r_gate_closed(gpu):
+    inp = synth.scan_inputs(75, [40, 3, 17], D=72, dtype="f32")
+    run_saved(inp, False, "x", 0.0, True, True, seed=76, reverse=False)
+
+
+def test_saved_l2r_matches_unsaved_bitwise(gpu):
+    """Unchunked, prefix_scan_save is prefix_scan_state with readout bit for
+    bit, and the backward from its checkpoints is prefix_scan_backward."""
+    inp = synth.scan_inputs(77, [32] * 8, D=256, dtype="bf16", dt_mean=-3.0)
+    x, kw, shaped = device_inputs(inp, True, "bf16")
+    B, D = inp.batch, 256
+    rng = np.random.default_rng(78)
+    dout = shaped(dev(synth.round_bf16(rng.standard_normal(inp.x.shape)), "bf16"))
+    h_in = dev32(synth.initial_state(78, B, D, 16))
+    hs = [torch.empty((B, D, 16), dtype=torch.float32, device="cuda") for _ in range(2)]
+    base = torch.empty_like(x)
+    r2l.prefix_scan_state(x, kw["dt"], kw["Bm"], kw["A"], Cm=kw["Cm"], Dskip=kw["Dskip"],
+                          h_in=h_in, h_out=hs[0], res=x, s=0.3, out=base, chunk_tokens=-1,
+                          state_split=1)
+    out, ckpt = r2l.prefix_scan_save(x, **kw, h_in=h_in, h_out=hs[1], res=x, s=0.3,
+                                     chunk_tokens=-1)
+    g0 = r2l.prefix_scan_backward(x, **kw, dout=dout, h_in=h_in, res=x, s=0.3, chunk_tokens=-1)
+    g1 = r2l.prefix_scan_backward(x, **kw, dout=dout, h_in=h_in, res=x, s=0.3, chunk_tokens=-1,
+                                  ckpt=ckpt)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(base))
+    assert np.array_equal(bits(hs[1]), bits(hs[0]))
+    for name in g0:
+        assert np.array_equal(bits(g1[name]), bits(g0[name])), name
