@@ -661,8 +661,11 @@ class R2LScan(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, dt, Bm, Cm, A, Dskip, s=None):
         res = x if s is not None else None
-        out, ckpt = r2l_scan_save(x, dt, Bm, Cm, A, Dskip, res=res,
-                                  s=0.0 if s is None else float(s))
+        gate = 0.0 if s is None else float(s)
+        if any(ctx.needs_input_grad[:6]):
+            out, ckpt = r2l_scan_save(x, dt, Bm, Cm, A, Dskip, res=res, s=gate)
+        else:   # no gradient will be asked for: no checkpoints
+            out, ckpt = r2l_scan(x, dt, Bm, Cm, A, Dskip, res=res, s=gate), None
         ctx.save_for_backward(x, dt, Bm, Cm, A, Dskip, ckpt)
         ctx.s = s
         return out

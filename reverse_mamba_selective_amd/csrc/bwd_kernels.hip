@@ -357,20 +357,37 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 constexpr int kSumThreads = 256;
 constexpr int64_t kNarrowSum = 4096;
 
+// A whole block per output: few outputs, each with at least a block's worth
+// of partials (ds over every block of the call). Fewer partials go one per
+// thread (dDskip of the denoising hook: 2048 outputs of 64 partials).
+__host__ __device__ inline bool narrow_sum(const SumParams &p) {
+    return p.n < kNarrowSum && p.P >= kSumThreads;
+}
+
 // The ordered sums of one backward call in one launch: segment k owns blocks
-// [first[k], first[k + 1]). Segments with fewer than kNarrowSum outputs give
-// each output a whole block (threads split the partials in order, then a
-// fixed tree in LDS); the others give each thread one output, its partials
-// summed in order with four independent loads in flight.
+// [first[k], first[k + 1]). Narrow segments (narrow_sum) give each output a
+// whole block (threads split the partials in order, then a fixed tree in
+// LDS); the others give each thread one output, its partials added in order.
+// Either way each thread has sixteen loads in flight before it adds them:
+// the sums are latency-bound (a handful of threads per SIMD).
 __global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumBatch sb) {
     __shared__ float part[kSumThreads];
     int k = 0;
     while (k + 1 < sb.count && blockIdx.x >= sb.first[k + 1]) ++k;
     const SumParams &p = sb.seg[k];
     const int64_t blk = static_cast<int64_t>(blockIdx.x) - sb.first[k];
-    if (p.n < kNarrowSum) {
+    constexpr int kInFlight = 16;
+    if (narrow_sum(p)) {
         float acc = 0.0f;
-        for (int64_t q = threadIdx.x; q < p.P; q += kSumThreads) acc += p.src[q * p.pstride + blk];
+        int64_t q = threadIdx.x;
+        for (; q + (kInFlight - 1) * kSumThreads < p.P; q += kInFlight * kSumThreads) {
+            float v[kInFlight];
+#pragma unroll
+            for (int j = 0; j < kInFlight; ++j) v[j] = p.src[(q + j * kSumThreads) * p.pstride + blk];
+#pragma unroll
+            for (int j = 0; j < kInFlight; ++j) acc += v[j];
+        }
+        for (; q < p.P; q += kSumThreads) acc += p.src[q * p.pstride + blk];
         part[threadIdx.x] = acc;
         __syncthreads();
 #pragma unroll
@@ -385,6 +402,13 @@ __global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumBatch sb) {
     if (i >= p.n) return;
     float acc = 0.0f;
     int64_t q = 0;
+    for (; q + kInFlight <= p.P; q += kInFlight) {
+        float v[kInFlight];
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) v[j] = p.src[(q + j) * p.pstride + i];
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) acc += v[j];
+    }
     for (; q + 4 <= p.P; q += 4) {
         const float v0 = p.src[q * p.pstride + i], v1 = p.src[(q + 1) * p.pstride + i];
         const float v2 = p.src[(q + 2) * p.pstride + i], v3 = p.src[(q + 3) * p.pstride + i];
@@ -424,7 +448,7 @@ hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, h
 
 int64_t sum_blocks(const SumParams &p) {
     if (p.n <= 0) return 0;
-    return p.n < kNarrowSum ? p.n : (p.n + kSumThreads - 1) / kSumThreads;
+    return narrow_sum(p) ? p.n : (p.n + kSumThreads - 1) / kSumThreads;
 }
 
 hipError_t launch_sums(const SumBatch &in, hipStream_t stream) {

@@ -269,3 +269,21 @@ def test_saved_l2r_matches_unsaved_bitwise(gpu):
     assert np.array_equal(bits(hs[1]), bits(hs[0]))
     for name in g0:
         assert np.array_equal(bits(g1[name]), bits(g0[name])), name
+
+
+def test_autograd_saves_only_when_needed(gpu):
+    """R2LScan runs r2l_scan when no input needs a gradient and the saving
+    forward otherwise (bit for bit those calls)."""
+    inp = synth.scan_inputs(79, [32] * 4, D=128, dtype="f32")
+    x, kw, _ = device_inputs(inp, True, "f32")
+    ref0 = r2l.r2l_scan(x, **kw, res=x, s=0.25)
+    ref1, _ = r2l.r2l_scan_save(x, **kw, res=x, s=0.25)
+    with torch.no_grad():
+        out0 = r2l.R2LScan.apply(x, kw["dt"], kw["Bm"], kw["Cm"], kw["A"], kw["Dskip"], 0.25)
+    xg = x.clone().requires_grad_()
+    out1 = r2l.R2LScan.apply(xg, kw["dt"], kw["Bm"], kw["Cm"], kw["A"], kw["Dskip"], 0.25)
+    out1.sum().backward()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out0), bits(ref0))
+    assert np.array_equal(bits(out1.detach()), bits(ref1))
+    assert xg.grad is not None and torch.isfinite(xg.grad).all()
