@@ -368,8 +368,11 @@ __host__ __device__ inline bool narrow_sum(const SumParams &p) {
 // [first[k], first[k + 1]). Narrow segments (narrow_sum) give each output a
 // whole block (threads split the partials in order, then a fixed tree in
 // LDS); the others give each thread one output, its partials added in order.
-// Either way each thread has sixteen loads in flight before it adds them:
-// the sums are latency-bound (a handful of threads per SIMD).
+// A segment of few outputs (at most one block per CU) is latency-bound: its
+// threads have sixteen loads in flight before they add them; a large one
+// (the prefill's dBm, dCm: 0.5 M outputs) streams HBM and keeps four, which
+// measured faster there.
+constexpr int64_t kFewSumOutputs = 65536;
 __global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumBatch sb) {
     __shared__ float part[kSumThreads];
     int k = 0;
@@ -402,12 +405,14 @@ __global__ __launch_bounds__(kSumThreads) void sum_kernel(const SumBatch sb) {
     if (i >= p.n) return;
     float acc = 0.0f;
     int64_t q = 0;
-    for (; q + kInFlight <= p.P; q += kInFlight) {
-        float v[kInFlight];
+    if (p.n <= kFewSumOutputs) {
+        for (; q + kInFlight <= p.P; q += kInFlight) {
+            float v[kInFlight];
 #pragma unroll
-        for (int j = 0; j < kInFlight; ++j) v[j] = p.src[(q + j) * p.pstride + i];
+            for (int j = 0; j < kInFlight; ++j) v[j] = p.src[(q + j) * p.pstride + i];
 #pragma unroll
-        for (int j = 0; j < kInFlight; ++j) acc += v[j];
+            for (int j = 0; j < kInFlight; ++j) acc += v[j];
+        }
     }
     for (; q + 4 <= p.P; q += 4) {
         const float v0 = p.src[q * p.pstride + i], v1 = p.src[(q + 1) * p.pstride + i];
