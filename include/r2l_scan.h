@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define R2L_ABI_VERSION 5
+#define R2L_ABI_VERSION 6
 
 /* exported from libr2l_scan.so (everything else in it is hidden) */
 #if defined(__GNUC__)
@@ -277,9 +277,12 @@ R2L_API r2l_status r2l_backward_workspace_size(const r2l_scan_args *fwd,
  *
  * r2l_scan_save -- r2l_scan with the same arguments and results, which also
  * stores the state entering every 8th visited position of each sequence (its
- * "checkpoints") at ckpt: fp32, [rows, dim, dstate] with
- * rows = (tokens / 8 + batch + 1), the row of visited position p (a multiple
- * of 8) of sequence b being (packed start of b + p) / 8 + b; ckpt_bytes of at
+ * "checkpoints") at ckpt: fp32, rows = (tokens / 8 + batch + 1) of
+ * dim * dstate floats, the row of visited position p (a multiple of 8) of
+ * sequence b being r = (packed start of b + p) / 8 + b; a row holds dstate/4
+ * planes of [dim][4]: state n of channel d at ((r * dstate/4 + n/4) * dim + d)
+ * * 4 + n % 4 (so that stores and loads by consecutive channels are
+ * contiguous); ckpt_bytes of at
  * least r2l_checkpoint_size(). ckpt is an output (16-byte aligned, overlapping
  * no other buffer of the call); state_split must be 0 or 1. The workspace
  * is sized by r2l_workspace_size with R2L_OP_SAVE (the plan may chunk

@@ -29,7 +29,7 @@ R2L_OP_BIDIR = 3
 R2L_OP_SAVE = 4
 R2L_OP_PREFIX_SAVE = 5
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",

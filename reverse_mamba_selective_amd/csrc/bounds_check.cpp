@@ -235,9 +235,11 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
                     const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
                     if (!lg.active) continue;
                     const int64_t row = ckpt_row(bg.b, sq.s0p, static_cast<int64_t>(bg.c) * p.chunk_len + pos);
-                    const uintptr_t a = U(p.ckpt) + ((row * p.D + lg.d) * kN + lg.sub * NS) * 4;
-                    ck.access("checkpoint", ck.region_of(p.ckpt), a, NS * 4);
-                    ck.wrote(a, NS * 4);
+                    for (int q = 0; q < NS / 4; ++q) {
+                        const uintptr_t a = U(p.ckpt) + ckpt_quad(row, p.D, lg.d, lg.sub * (NS / 4) + q) * 4;
+                        ck.access("checkpoint", ck.region_of(p.ckpt), a, 16);
+                        ck.wrote(a, 16);
+                    }
                     if (p.ckpt_s && !readout && lg.sub == 0) {
                         const uintptr_t as = U(p.ckpt_s) + (row * p.D + lg.d) * 4;
                         ck.access("checkpoint delta sum", ck.region_of(p.ckpt_s), as, 4);
@@ -419,9 +421,10 @@ void check_backward(Checker &ck, const Launch &l, const int32_t *cu_host) {
             for (int lane = 0; lane < kWG; ++lane) {
                 const LaneGeom lg = lane_geom(bg.tile, lane, G, p.D);
                 const int64_t row = ckpt_row(bg.b, sq.s0p, gpos);
-                const uintptr_t a = U(p.ckpt) + ((row * p.D + lg.d) * kN + lg.sub * NS) * 4;
-                ck.access("checkpoint", rCk, a, NS * 4);
-                ck.read_written("checkpoint", a, NS * 4);
+                if (NS != 4) return ck.fail("the backward reads one checkpoint quad per lane");
+                const uintptr_t a = U(p.ckpt) + ckpt_quad(row, p.D, lg.d, lg.sub) * 4;
+                ck.access("checkpoint", rCk, a, 16);
+                ck.read_written("checkpoint", a, 16);
                 if (p.Hc) {   // chunked phase 1: the chunk's entry state and the delta sum
                     if (p.chunk_len <= 0 || p.chunk_len % K)
                         return ck.fail("chunk length %d is not a multiple of the group", p.chunk_len);

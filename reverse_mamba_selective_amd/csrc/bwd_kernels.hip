@@ -181,7 +181,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             ng[j] = E::bload(rg, doff, row * grb);
         }
         const int64_t ckr = ckpt_row(b, sq.s0p, gpos);
-        const float *cp = p.ckpt + (ckr * p.D + dl) * kN + sub * NS;
+        static_assert(NS == 4, "one checkpoint quad per lane");
+        const float *cp = p.ckpt + ckpt_quad(ckr, p.D, dl, sub);
 #pragma unroll
         for (int n = 0; n < NS; ++n) nck[n] = cp[n];
         if (chunked) {

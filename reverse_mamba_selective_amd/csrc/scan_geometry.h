@@ -210,6 +210,12 @@ R2L_HD CarryGeom carry_geom(int64_t D, int64_t bx, int64_t by, int tid) {
 // every (sequence, group), below ckpt_rows().
 R2L_HD int64_t ckpt_row(int64_t b, int64_t s0p, int64_t pos) { return (s0p + pos) / kCkptTokens + b; }
 R2L_HD int64_t ckpt_rows(int64_t tokens, int64_t batch) { return tokens / kCkptTokens + batch + 1; }
+// Float offset of states [4q, 4q + 4) of channel d in checkpoint row `row`.
+// A row holds kN/4 planes of [D][4]: a wave whose lanes (consecutive
+// channels) store or load one quad each touches one contiguous run.
+R2L_HD int64_t ckpt_quad(int64_t row, int64_t D, int64_t d, int q) {
+    return ((row * (kN / 4) + q) * D + d) * 4;
+}
 
 // Sequence b in the backward's tensors (element offsets of its first row).
 struct BwdSeqGeom {

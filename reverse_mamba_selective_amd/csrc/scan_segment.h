@@ -220,9 +220,11 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     auto checkpoint = [&](int pos) {
         if (!p.ckpt || !lg.active) return;
         const int64_t row = ckpt_row(b, sq.s0p, static_cast<int64_t>(c) * p.chunk_len + pos);
-        float *cp = p.ckpt + (row * p.D + dl) * kN + sub * NS;
+        static_assert(NS % 4 == 0, "checkpoints are stored by quads of states");
 #pragma unroll
-        for (int j = 0; j < NS; ++j) cp[j] = h[j];
+        for (int q = 0; q < NS / 4; ++q)
+            *reinterpret_cast<float4 *>(p.ckpt + ckpt_quad(row, p.D, dl, sub * (NS / 4) + q)) =
+                make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
         if constexpr (!READOUT)
             if (p.ckpt_s && sub == 0) p.ckpt_s[row * p.D + dl] = dsum;
     };
