@@ -287,3 +287,24 @@ def test_autograd_saves_only_when_needed(gpu):
     assert np.array_equal(bits(out0), bits(ref0))
     assert np.array_equal(bits(out1.detach()), bits(ref1))
     assert xg.grad is not None and torch.isfinite(xg.grad).all()
+
+
+def test_saved_l2r_bound_calls(gpu):
+    """bind("prefix_scan_save") and bind_backward(ckpt=..., _reverse=False)
+    launch the same calls as prefix_scan_save / prefix_scan_backward."""
+    inp = synth.scan_inputs(80, [32] * 4, D=128, dtype="bf16", dt_mean=-3.0)
+    x, kw, _ = device_inputs(inp, True, "bf16")
+    dout = torch.randn_like(x)
+    out0, ck0 = r2l.prefix_scan_save(x, **kw, res=x, s=0.2)
+    g0 = r2l.prefix_scan_backward(x, **kw, dout=dout, res=x, s=0.2, ckpt=ck0)
+    out1 = torch.empty_like(x)
+    sc = r2l.bind("prefix_scan_save", x=x, res=x, s=0.2, out=out1, **kw)
+    bc = r2l.bind_backward(x, **kw, dout=dout, res=x, s=0.2, ckpt=sc.ckpt, _reverse=False)
+    assert bc.func == "prefix_scan_backward_saved"
+    for _ in range(2):
+        sc.launch()
+        bc.launch()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out1), bits(out0))
+        for name in g0:
+            assert np.array_equal(bits(bc.grads[name]), bits(g0[name])), name
