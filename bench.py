@@ -627,6 +627,46 @@ class PrefillBackward(Prefill):
                    "dx and ddt of the sampled sequences vs the oracle's fp64 backward")
 
 
+class PrefillTrain(PrefillBackward):
+    """Training the R2L stream at the prefill shape (8 x 4096 x 4096, bf16, out =
+    y): the forward that saves the backward's checkpoints (r2l_scan_save) and the
+    backward from them (r2l_scan_backward_saved), all gradients. The unsaved
+    pair is the "prefill" and "prefill_bwd" workloads."""
+    name = "prefill_train_bf16_b8_L4096_D4096_N16"
+    isolate_entries = True
+
+    def setup(self, torch, r2l):
+        super().setup(torch, r2l)
+        g = self.g
+        tok, N = self.B * self.L, 16
+        view = lambda t: t.view(self.B, self.L, -1)   # noqa: E731
+        # checkpoint rows written and read back: one per started group of 8
+        ck_bytes = self.B * ((self.L + 7) // 8) * self.D * N * 4
+        self.out_save = torch.empty_like(view(g["x"]))
+        sc = r2l.bind("r2l_scan_save", x=view(g["x"]), dt=view(g["dt"]), Bm=view(g["Bm"]),
+                      Cm=view(g["Cm"]), A=g["A"], Dskip=g["Dskip"], out=self.out_save)
+        self.bcall = r2l.bind_backward(view(g["x"]), view(g["dt"]), view(g["Bm"]), view(g["Cm"]),
+                                       g["A"], g["Dskip"], dout=view(self.dout), ckpt=sc.ckpt)
+        self.step_calls = [[sc, self.bcall]]
+        self.step_entries = [0, 1]
+        self.launches_per_step = 2
+        fwd_alu = self.tc_per_launch * alu_ops_per_tc(True, False)
+        bwd_alu = self.tc_per_launch * (bwd_alu_ops_per_tc() - alu_ops_per_tc(False, False))
+        self.measure = [dict(label="r2l_scan_save", calls=[sc],
+                             bytes=scan_bytes(tok, self.D, 2, readout=True) + ck_bytes,
+                             alu=fwd_alu, tc=self.tc_per_launch),
+                        dict(label="r2l_scan_backward_saved", calls=[self.bcall],
+                             bytes=self.bytes_per_launch + ck_bytes, alu=bwd_alu,
+                             tc=self.tc_per_launch)]
+        self.config = dict(self.config, workload=self.name,
+                           op="r2l_scan_save + r2l_scan_backward_saved",
+                           checkpoint_bytes=ck_bytes)
+
+    parity_spec = ("dx, ddt", "bf16", 2e-2,
+                   "dx and ddt of the backward from the saved checkpoints, sampled sequences, "
+                   "vs the oracle's fp64 backward")
+
+
 class RaggedServing(Workload):
     """256 ragged blocks of U{16..64} tokens at D = 4096, bf16: the reverse scan over
     the active blocks and block_commit_state over the committed blocks."""
@@ -1153,7 +1193,8 @@ SERVING_KEY = 107
 WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
              "prefix": RaggedPrefix, "l2r": DenoiseL2R, "denoise_bwd": DenoiseBackward,
              "bidir": DenoiseBidir, "sidecar": DenoiseSidecar, "serving": ServingStep,
-             "prefill_bwd": PrefillBackward, "denoise_train": DenoiseTrain}
+             "prefill_bwd": PrefillBackward, "denoise_train": DenoiseTrain,
+             "prefill_train": PrefillTrain}
 
 
 def main():
