@@ -803,6 +803,22 @@ r2l_status check_accesses(Op op, const r2l_scan_args *a, const Plan &pl, const i
     if (saving) ck.track(ckpt, checkpoint_bytes(a));
     Launch ls[kMaxSaveLaunches];
     const int n = saving ? build_save_launches(op, a, pl, ckpt, ls) : build_launches(op, a, pl, ls);
+    // launch order: no scan may read an input after the residual copy of the
+    // same call has overwritten it (out aliasing x, dt, Bm or Cm)
+    for (int i = 0; i < n && ck.ok(); ++i) {
+        if (ls[i].kind != Launch::Copy) continue;
+        const Region *dst = ck.region_of(ls[i].copy.dst);
+        for (int j = i + 1; j < n && ck.ok(); ++j) {
+            if (ls[j].kind != Launch::Segment) continue;
+            const SegParams &p = ls[j].seg;
+            const void *ins[] = {p.x, p.dt, p.Bm, p.Cm, p.res};
+            const char *names[] = {"x", "dt", "Bm", "Cm", "res"};
+            for (int k = 0; k < 5; ++k)
+                if (ins[k] && ck.region_of(ins[k]) == dst)
+                    ck.fail("launch %d reads %s after launch %d (the residual copy) overwrote it",
+                            j, names[k], i);
+        }
+    }
     for (int i = 0; i < n && ck.ok(); ++i) {
         ++rep->launches;
         if (ls[i].kind == Launch::Segment) {

@@ -286,8 +286,15 @@ int build_save_launches(Op op, const r2l_scan_args *a, const Plan &pl, float *ck
             out[i].seg.ckpt = ckpt;
             stored = true;
         }
-    if (!stored && tokens_of(a) > 0 && a->batch > 0)
-        out[n++] = ckpt_state_launch(op == Op::Scan, a, (a->dim + kWG - 1) / kWG, ckpt);
+    if (!stored && tokens_of(a) > 0 && a->batch > 0) {
+        // before the residual copy, which may overwrite x (out == x with a
+        // separate residual): the checkpoints are the states of the x given
+        int at = n;
+        while (at > 0 && out[at - 1].kind == Launch::Copy) --at;
+        for (int i = n; i > at; --i) out[i] = out[i - 1];
+        out[at] = ckpt_state_launch(op == Op::Scan, a, (a->dim + kWG - 1) / kWG, ckpt);
+        ++n;
+    }
     return n;
 }
 

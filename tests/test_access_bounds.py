@@ -85,6 +85,9 @@ def make_args(op, *, dtype="bf16", D=64, batch=None, seqlen=None, lengths=None, 
             a.res, a.res_stride, a.res_batch_stride = a.x, a.x_stride, a.x_batch_stride
         elif res == "sep":
             a.res, a.res_stride, a.res_batch_stride = tensor(D)
+        elif res == "sep_into_x":   # a separate residual, out is x
+            a.res, a.res_stride, a.res_batch_stride = tensor(D)
+            a.out, a.out_stride, a.out_batch_stride = a.x, a.x_stride, a.x_batch_stride
         elif res == "inplace":  # out is x is res
             a.res, a.res_stride, a.res_batch_stride = a.x, a.x_stride, a.x_batch_stride
             a.out, a.out_stride, a.out_batch_stride = a.x, a.x_stride, a.x_batch_stride
@@ -426,6 +429,9 @@ def test_save_and_saved_backward(case, dtype, reverse):
         for h in (False, True):
             check_save(res=res, h_in=h, h_out=h, reverse=reverse, **kw)
     check_save(res="x", s=0.0, reverse=reverse, **kw)   # gate closed: a state-only scan stores them
+    # gate closed, out = x with a separate residual: the state-only scan that
+    # stores them reads x before the residual copy overwrites it
+    check_save(res="sep_into_x", s=0.0, h_out=True, reverse=reverse, **kw)
 
 
 def test_save_plans():
@@ -441,6 +447,8 @@ def test_save_plans():
     assert rep.launches == 2                              # res copied to out, state-only scan
     a, rep, brep = check_save(batch=2, seqlen=64, D=64, res="inplace", s=0.0)
     assert rep.launches == 1                              # out is res: the state-only scan
+    a, rep, brep = check_save(batch=2, seqlen=64, D=64, res="sep_into_x", s=0.0, h_out=True)
+    assert rep.launches == 3                              # state scan (h_out), checkpoints, copy
     a, rep, brep = check_save(lengths=[0, 0], D=64)
     assert _abi.checkpoint_size(a) == 0 or rep.launches <= 1
 

@@ -122,6 +122,37 @@ def test_saved_gate_closed(gpu, res_kind):
     run_saved(inp, False, res_kind, 0.0, True, True, seed=58)
 
 
+@pytest.mark.parametrize("reverse", [True, False], ids=["r2l", "l2r"])
+def test_saved_gate_closed_out_is_x(gpu, reverse):
+    """s = 0 with out = x and a separate residual: x is overwritten by the
+    residual, and the checkpoints (stored by a state-only scan) and h_out are
+    still the states of the x that was passed in."""
+    inp = synth.scan_inputs(64, [40, 3, 17, 0, 9], D=72, dtype="bf16")
+    B, D = inp.batch, 72
+    res_np = synth.scan_inputs(65, inp.lengths, D=D, dtype="bf16").x
+    fwd = oracle.selective_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip,
+                                reverse=reverse, seq_offsets=inp.offsets, want_h_out=True)
+    rng = np.random.default_rng(66)
+    dout_np = synth.round_bf16(rng.standard_normal(inp.x.shape))
+    ref = oracle.selective_scan_backward(
+        inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=reverse, dout=dout_np,
+        res_kind="separate", s=0.0, seq_offsets=inp.offsets)
+    x, kw, _ = device_inputs(inp, False, "bf16")
+    x_keep = x.clone()
+    res = dev(res_np, "bf16")
+    h_out = torch.empty((B, D, 16), dtype=torch.float32, device="cuda")
+    save = r2l.r2l_scan_save if reverse else r2l.prefix_scan_save
+    bwd = r2l.r2l_scan_backward if reverse else r2l.prefix_scan_backward
+    out, ckpt = save(x, **kw, h_out=h_out, res=res, s=0.0, out=x)
+    g = bwd(x_keep, **kw, dout=dev(dout_np, "bf16"), res=res, s=0.0, ckpt=ckpt)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == x.data_ptr()
+    assert np.array_equal(bits(x), bits(res)), "s == 0: out is not res bit for bit"
+    check_state(h_out, fwd["h_out"], "h_out")
+    for name in ("dx", "ddt") + FP32_GRADS:
+        check_grad(name, g[name], ref[name], "bf16")
+
+
 @pytest.mark.parametrize("dense", [True, False], ids=["dense", "ragged"])
 def test_saved_matches_unsaved_bitwise(gpu, dense):
     """Unchunked, the saving forward is r2l_scan bit for bit, and the backward
