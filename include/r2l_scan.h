@@ -58,6 +58,7 @@
  *  Memory   Every pointer except `a` itself is device memory. The caller owns
  *           every buffer; the library allocates nothing, keeps no state
  *           between calls and is safe to call from several host threads.
+ *           (Exception: r2l_scan_noalloc's scratch array, described there.)
  *  Streams  `stream` is a hipStream_t (NULL: the null stream). Work is queued
  *           on it and the call returns without waiting.
  *  Aliasing out may be exactly x and/or exactly res (same base pointer and
@@ -88,7 +89,7 @@
 extern "C" {
 #endif
 
-#define R2L_ABI_VERSION 6
+#define R2L_ABI_VERSION 7
 
 /* exported from libr2l_scan.so (everything else in it is hidden) */
 #if defined(__GNUC__)
@@ -177,6 +178,26 @@ typedef struct r2l_scan_args {
  * limited to the active block).
  */
 R2L_API r2l_status r2l_scan(const r2l_scan_args *a, void *stream);
+
+/*
+ * r2l_scan_noalloc -- r2l_scan for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, checks and results as r2l_scan, except:
+ *  - the workspace fields are ignored: a chunked plan's carry data goes to a
+ *    scratch array of R2L_NOALLOC_SCRATCH_BYTES that the library holds in
+ *    device memory on each GPU it runs on, for the life of the process (its
+ *    address is looked up on the first call on each device);
+ *  - a plan needing more scratch than that returns R2L_ERR_WORKSPACE and
+ *    launches nothing (r2l_workspace_size with R2L_OP_SCAN tells the need);
+ *  - the optional R2L_CHECK_SEQLENS copy is not made.
+ * Nothing is allocated, by the library or by any routine it calls. Every
+ * word of scratch a launch reads was written earlier in the same call, so
+ * nothing is cleared between calls. All calls on one GPU share its scratch:
+ * calls on one stream are ordered, but calls that may overlap on one GPU (other
+ * streams, other host threads) race on it and must not be made.
+ */
+#define R2L_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+R2L_API r2l_status r2l_scan_noalloc(const r2l_scan_args *a, void *stream);
 
 /*
  * prefix_scan_state -- the forward-only boundary state of each prefix: tokens

@@ -22,7 +22,7 @@ import torch
 from . import _abi
 from ._abi import R2LError  # noqa: F401
 
-__all__ = ["r2l_scan", "prefix_scan_state", "block_commit_state", "bidir_scan", "sidecar_forward",
+__all__ = ["r2l_scan", "r2l_scan_noalloc", "prefix_scan_state", "block_commit_state", "bidir_scan", "sidecar_forward",
            "sidecar_tune",
            "bind_sidecar", "SIDECAR_WEIGHTS",
            "workspace_size", "bind",
@@ -272,6 +272,24 @@ def r2l_scan(x, dt, Bm, Cm, A, Dskip=None, *, cu_seqlens=None, max_seqlen=None, 
               delta_softplus, chunk_tokens, state_split)
     _run("r2l_scan", _abi.R2L_OP_SCAN, a, workspace, x.device)
     return out
+
+
+def r2l_scan_noalloc(x, dt, Bm, Cm, A, Dskip=None, *, out, cu_seqlens=None, max_seqlen=None,
+                     h_in=None, h_out=None, res=None, s=0.0, delta_softplus=True,
+                     chunk_tokens=0, state_split=0):
+    """``r2l_scan`` that allocates nothing, for callers that cannot (graph
+    capture, serving loops): ``out`` must be given, and a chunked plan's carry
+    data goes to the library's own device scratch array (``NOALLOC_SCRATCH_BYTES``
+    per GPU); a plan needing more raises. Calls that may overlap on one GPU
+    (other streams or threads) race on that array. Returns ``out``."""
+    a = _fill(x, dt, Bm, Cm, A, Dskip, cu_seqlens, max_seqlen, h_in, h_out, res, s, out,
+              delta_softplus, chunk_tokens, state_split)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _abi.call("r2l_scan_noalloc", a, stream)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = _abi.NOALLOC_SCRATCH_BYTES
 
 
 def checkpoint_size(x, A, *, cu_seqlens=None, max_seqlen=None) -> int:

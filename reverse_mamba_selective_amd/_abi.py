@@ -29,9 +29,11 @@ R2L_OP_BIDIR = 3
 R2L_OP_SAVE = 4
 R2L_OP_PREFIX_SAVE = 5
 
-ABI_VERSION = 6
+ABI_VERSION = 7
+NOALLOC_SCRATCH_BYTES = 64 << 20   # r2l_scan_noalloc's scratch array per device
 
-EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_workspace_size",
+EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_scan_noalloc",
+           "r2l_workspace_size",
            "r2l_status_string", "r2l_last_error", "r2l_abi_version", "r2l_check_access",
            "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
            "r2l_check_access_backward", "prefix_scan_backward", "bidir_scan",
@@ -130,7 +132,7 @@ def load(path: str = LIB_PATH):
             "(hipcc for gfx950). There is no fallback implementation." % path)
     lib = ctypes.CDLL(path)
     ptr = ctypes.POINTER(ScanArgs)
-    for name in ("r2l_scan", "prefix_scan_state", "block_commit_state"):
+    for name in ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_scan_noalloc"):
         f = getattr(lib, name)
         f.restype = _i32
         f.argtypes = [ptr, _vp]

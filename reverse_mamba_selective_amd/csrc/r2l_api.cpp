@@ -298,14 +298,16 @@ r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
     return ok();
 }
 
-r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream) {
+r2l_status run(Op op, const r2l_scan_args *a, hipStream_t stream, bool device_check = true) {
     r2l_status st = check_shape(a);
     if (st != R2L_OK) return st;
     const Plan pl = r2l::make_plan(op, a);
     st = check_buffers(op, a, pl);
     if (st != R2L_OK) return st;
-    st = check_seqlens_on_device(a);
-    if (st != R2L_OK) return st;
+    if (device_check) {
+        st = check_seqlens_on_device(a);
+        if (st != R2L_OK) return st;
+    }
     if (a->batch * pl.nchunks * pl.tiles > INT32_MAX - 8)
         return fail(R2L_ERR_UNSUPPORTED, "grid too large");
 
@@ -854,6 +856,31 @@ r2l_status r2l_check_access_sidecar(const r2l_sidecar_args *a, const int32_t *cu
 
 r2l_status r2l_scan(const r2l_scan_args *a, void *stream) {
     return run(Op::Scan, a, static_cast<hipStream_t>(stream));
+}
+
+static_assert(r2l::kNoallocScratchBytes == R2L_NOALLOC_SCRATCH_BYTES,
+              "the scratch size in the header");
+
+r2l_status r2l_scan_noalloc(const r2l_scan_args *a, void *stream) {
+    r2l_status st = check_shape(a);
+    if (st != R2L_OK) return st;
+    r2l_scan_args v = *a;
+    v.workspace = nullptr;
+    v.workspace_bytes = 0;
+    const Plan pl = r2l::make_plan(Op::Scan, &v);
+    if (pl.ws_bytes > r2l::kNoallocScratchBytes)
+        return fail(R2L_ERR_WORKSPACE,
+                    "the plan needs %zu bytes of scratch, more than the %zu that "
+                    "r2l_scan_noalloc holds (use r2l_scan with a workspace)",
+                    pl.ws_bytes, r2l::kNoallocScratchBytes);
+    if (pl.ws_bytes > 0) {
+        void *p = nullptr;
+        st = hip_status(r2l::noalloc_scratch(&p), "scratch address lookup");
+        if (st != R2L_OK) return st;
+        v.workspace = p;
+        v.workspace_bytes = r2l::kNoallocScratchBytes;
+    }
+    return run(Op::Scan, &v, static_cast<hipStream_t>(stream), false);
 }
 
 r2l_status prefix_scan_state(const r2l_scan_args *a, void *stream) {

@@ -242,6 +242,10 @@ const char *run_gemm(int dtype, const GemmParams &p, hipStream_t stream);
 // y_scratch when given, with the same leading dimension) and keeps the fastest
 // for later calls of the same shape; synchronizes the stream
 const char *tune_gemm(int dtype, const GemmParams &p, void *y_scratch, hipStream_t stream);
+// r2l_scan_noalloc: the device address of the library's scratch array on the
+// current device (looked up once per device), kNoallocScratchBytes long
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void **ptr);
 // G in {2, 4}
 hipError_t launch_backward(bool reverse, int dtype, int G, const BwdParams &p, hipStream_t stream);
 hipError_t launch_sums(const SumBatch &p, hipStream_t stream);

@@ -217,3 +217,24 @@ def test_bad_workspace_query():
     assert lib.r2l_workspace_size(9, ctypes.byref(good_args()), ctypes.byref(n)) \
         == _abi.R2L_ERR_INVALID_ARG
     assert lib.r2l_workspace_size(0, ctypes.byref(good_args()), None) == _abi.R2L_ERR_INVALID_ARG
+
+
+def test_noalloc_checks_and_scratch_limit():
+    """r2l_scan_noalloc: the header's scratch size is the binding's; the same
+    argument checks as r2l_scan; a plan needing more scratch than the array
+    holds is refused with R2L_ERR_WORKSPACE before anything is launched."""
+    m = re.search(r"#define R2L_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == _abi.NOALLOC_SCRATCH_BYTES
+    for field, value, code in [("x", None, _abi.R2L_ERR_INVALID_ARG),
+                               ("dstate", 8, _abi.R2L_ERR_UNSUPPORTED),
+                               ("x", BASE + 1, _abi.R2L_ERR_MISALIGNED),
+                               ("Bm_stride", 15, _abi.R2L_ERR_INVALID_ARG)]:
+        assert status("r2l_scan_noalloc", good_args(**{field: value})) == code
+    a = good_args(batch=1, seqlen=300000, dim=512, chunk_tokens=256)
+    a.x, a.dt, a.Bm, a.Cm, a.A, a.Dskip, a.out = (BASE + (i << 32) for i in range(1, 8))
+    a.x_stride = a.dt_stride = a.out_stride = 512
+    need = _abi.workspace_size(_abi.R2L_OP_SCAN, a)
+    assert need > _abi.NOALLOC_SCRATCH_BYTES
+    assert status("r2l_scan_noalloc", a) == _abi.R2L_ERR_WORKSPACE
+    assert "scratch" in _abi.last_error()
