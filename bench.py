@@ -37,9 +37,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one fp32 VALU instruction per lane per clock
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# issue slots one v_exp_f32 / v_log_f32 takes on gfx950 (an issue-rate micro-benchmark:
-# 2 VALU slots, not co-issued with FMAs)
-TRANS_SLOTS = float(os.environ.get("R2L_TRANS_SLOTS", "2"))
+# VALU issue slots one v_exp_f32 / v_log_f32 takes on gfx950 in code that mixes
+# it with fp32 FMAs as the scan does (one exp per four FMAs): the issue-rate
+# micro-benchmark `bench.py --alu-rates` (csrc/alu_rates.hip), summarised with
+# its command in profiles/alu_rates__v_exp_f32_issue_rate.md
+TRANS_SLOTS = 1.75
 
 
 def alu_ops_per_tc(readout: bool, res: bool) -> float:
@@ -296,7 +298,7 @@ class Denoise(Workload):
 
 def bwd_alu_ops_per_tc() -> float:
     """Algorithmic VALU lane-ops per token·channel of the backward (N = 16,
-    trans ops weighted), without recomputation: the forward states (89), per
+    trans ops weighted), without recomputation: the forward states (84.5), per
     state the adjoint (g += dy*C; dy*h and its sum over channels; the dDelta
     term B*x + A*(abar*h_prev) and its fma; dA += g*Delta*(abar*h_prev); dx's
     g*B; g*Delta*x and its sum over channels; g *= abar: 13), per channel the
@@ -1197,6 +1199,110 @@ WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
              "prefill_train": PrefillTrain}
 
 
+def build_info() -> dict:
+    """git commit and ROCm release of the build (the GPU machine has no .git:
+    there the file the build wrote is read), torch's HIP version."""
+    info = {"git_sha": None, "git_dirty": None, "git_sha_from": None, "rocm": None}
+    try:
+        import subprocess
+        info["git_sha"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"],
+                                         capture_output=True, text=True,
+                                         check=True).stdout.strip()
+        info["git_dirty"] = bool(subprocess.run(
+            ["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+            capture_output=True, text=True, check=True).stdout.strip())
+        info["git_sha_from"] = "git"
+    except Exception:
+        p = os.path.join(ROOT, "reverse_mamba_selective_amd", "BUILD_INFO.json")
+        if os.path.exists(p):
+            b = json.load(open(p))
+            info.update(git_sha=b.get("git_sha"), git_dirty=b.get("git_dirty"),
+                        git_sha_from="the library's build")
+    try:
+        info["rocm"] = open(os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), ".info",
+                                         "version")).read().strip()
+    except OSError:
+        pass
+    try:
+        import torch
+        info["torch"] = torch.__version__
+        info["torch_hip"] = torch.version.hip
+    except Exception:
+        pass
+    return info
+
+
+def alu_rates(blocks_per_cu=(1, 2, 4, 8), iters=4000, reps=5):
+    """Issue rates of the vector ALU on this device (csrc/alu_rates.hip). Each
+    kind runs 16 independent dependency chains per lane at 1, 2, 4 and 8 waves
+    per SIMD (blocks of 4 waves, 1..8 blocks per CU, all resident at once).
+    Thread 0 of every block reads the shader clock counter and the constant
+    wall clock around its loop, which gives the shader clock the device ran at
+    and the SIMD cycles per wave64 instruction (the block's loop cycles over
+    the wave instructions its SIMD issued in that time). Slots are FMA issue
+    slots: a transcendental's cycles over an FMA's, alone (kinds 1 and 3) and
+    beside four FMAs (kind 2: its cycles minus those of the 65 other VALU
+    instructions of the iteration, per exp)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "reverse_mamba_selective_amd", "libr2l_alu_rates.so"))
+    lib.r2l_alu_rate_launch.restype = ctypes.c_int
+    lib.r2l_alu_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.r2l_alu_wall_clock_khz.restype = ctypes.c_int
+    khz = ctypes.c_int(0)
+    assert lib.r2l_alu_wall_clock_khz(ctypes.byref(khz)) == 0 and khz.value > 0
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+    # wave instructions per iteration: (label, all VALU incl. transcendental, transcendental)
+    kinds = {0: ("v_fma_f32", 16, 0), 1: ("v_exp_f32", 16, 16),
+             2: ("v_exp_f32 + 4 v_fma_f32", 81, 16), 3: ("v_log_f32", 16, 16)}
+    nb = max(blocks_per_cu) * cus
+    out = torch.empty(nb * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(nb * 4, dtype=torch.int64, device="cuda")
+    res = {"cus": cus, "iters": iters, "threads_per_block": 256,
+           "wall_clock_khz": khz.value,
+           "loop_body_per_iteration": {"0": "16 v_fma_f32", "1": "16 v_exp_f32",
+                                       "2": "16 v_exp_f32, 64 v_fma_f32, 1 v_mov_b32",
+                                       "3": "16 v_log_f32"},
+           "per_waves_per_simd": {}}
+    for bpc in blocks_per_cu:
+        blocks = bpc * cus
+        row = {"ms": {}, "clock_ghz": {}, "cycles_per_wave_instr": {}}
+        cyc = {}
+        for k, (label, nv, nt) in kinds.items():
+            for _ in range(2):
+                assert lib.r2l_alu_rate_launch(k, blocks, iters, out.data_ptr(), clk.data_ptr(),
+                                               stream) == 0
+            times, cycles, ghz = [], [], []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                assert lib.r2l_alu_rate_launch(k, blocks, iters, out.data_ptr(), clk.data_ptr(),
+                                               stream) == 0
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+                c = clk[:blocks * 4].view(blocks, 4).cpu().double()
+                dc, dw = c[:, 1] - c[:, 0], c[:, 3] - c[:, 2]
+                cycles.append(float(dc.median()))
+                ghz.append(float((dc / (dw / (khz.value * 1e3))).median()) / 1e9)
+            med = lambda v: sorted(v)[len(v) // 2]   # noqa: E731
+            # bpc waves share each SIMD for the whole loop
+            cyc[k] = med(cycles) / (bpc * iters * nv)
+            row["ms"][label] = round(med(times), 4)
+            row["clock_ghz"][label] = round(med(ghz), 3)
+            row["cycles_per_wave_instr"][label] = round(cyc[k], 3)
+        fma = cyc[0]
+        row["exp_slots_alone"] = round(cyc[1] / fma, 3)
+        row["log_slots_alone"] = round(cyc[3] / fma, 3)
+        row["exp_slots_beside_4_fma"] = round((cyc[2] * 81 - 65 * fma) / 16 / fma, 3)
+        row["fma_tlane_ops_at_measured_clock"] = round(
+            cus * 4 * 64 / fma * row["clock_ghz"]["v_fma_f32"] * 1e9 / 1e12, 3)
+        res["per_waves_per_simd"][str(bpc)] = row
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1212,7 +1318,12 @@ def main():
                          "dispatches); implies --no-graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch copies of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--alu-rates", action="store_true",
+                    help="only run the vector-ALU issue-rate micro-benchmark (FMA, exp, log)")
     args = ap.parse_args()
+    if args.alu_rates:
+        print(json.dumps(dict(alu_rates(), build=build_info())))
+        return
     if args.copy_calibration:
         import torch
         n = args.copy_calibration << 20
@@ -1424,6 +1535,7 @@ def main():
                       "lane_ops_per_tc_state_only": alu_ops_per_tc(False, False),
                       "trans_slots": TRANS_SLOTS},
         "source_sha": kernel_sha(),
+        "build": build_info(),
         "timing": ("queued ahead of a spinning kernel, GPU events" if args.queue_ahead
                    else "host clock around the steps (synchronised); GPU events per entry point"),
         "ms_per_step_eager": eager_s * 1e3,
