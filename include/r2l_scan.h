@@ -58,7 +58,9 @@
  *  Memory   Every pointer except `a` itself is device memory. The caller owns
  *           every buffer; the library allocates nothing, keeps no state
  *           between calls and is safe to call from several host threads.
- *           (Exception: r2l_scan_noalloc's scratch array, described there.)
+ *           (Exceptions, each described where it is declared: the GEMM
+ *           context the sidecar block's caller creates and passes in, and
+ *           r2l_scan_noalloc's scratch array.)
  *  Streams  `stream` is a hipStream_t (NULL: the null stream). Work is queued
  *           on it and the call returns without waiting.
  *  Aliasing out may be exactly x and/or exactly res (same base pointer and
@@ -89,7 +91,7 @@
 extern "C" {
 #endif
 
-#define R2L_ABI_VERSION 7
+#define R2L_ABI_VERSION 8
 
 /* exported from libr2l_scan.so (everything else in it is hidden) */
 #if defined(__GNUC__)
@@ -416,11 +418,36 @@ R2L_API r2l_status bidir_scan(const r2l_scan_args *a, const r2l_dir_args *rev, v
  * contiguous. out may be exactly hidden; any other overlap is R2L_ERR_ALIAS.
  * d_conv is 1..4, dstate 16; d_model, d_inner and dt_rank are multiples of 8
  * and the rows of hidden and out start on 16-byte boundaries (the GEMMs'
- * operands). The four projections run as
- * hipBLASLt GEMMs: the library keeps one hipBLASLt handle per device and one
- * algorithm per GEMM shape (host memory) for the life of the process; their
- * scratch is part of the workspace (r2l_sidecar_workspace_size).
+ * operands). The four projections run as hipBLASLt GEMMs through `gemm`, a
+ * context the caller creates (r2l_gemm_context_create) on the device of the
+ * call and keeps for as long as it calls: it holds the hipBLASLt handle and
+ * the algorithm chosen for each GEMM shape (the library's first choice, or
+ * what r2l_sidecar_tune found); the GEMMs' scratch is part of the workspace
+ * (r2l_sidecar_workspace_size). Required unless s == 0.
  */
+/* Opaque: one device's hipBLASLt handle and per-shape algorithm choices. */
+typedef struct r2l_gemm_context_s *r2l_gemm_context;
+
+/*
+ * r2l_gemm_context_create -- a GEMM context for the current device, written to
+ * *ctx (NULL on failure). It allocates host memory and the hipBLASLt handle's
+ * resources; the caller owns it and releases it with r2l_gemm_context_destroy.
+ * Calls on several host threads may share one context (its plan table is
+ * locked); a context is only valid on the device it was created on.
+ * Errors: R2L_ERR_INVALID_ARG (ctx NULL), R2L_ERR_HIP (no device, or the
+ * library refused a handle).
+ */
+R2L_API r2l_status r2l_gemm_context_create(r2l_gemm_context *ctx);
+
+/*
+ * r2l_gemm_context_destroy -- releases a context made by
+ * r2l_gemm_context_create (on its own device, whichever is current). No call
+ * that uses it may still be queued. NULL, or a handle that is not a live
+ * context the library can recognise, is R2L_ERR_INVALID_ARG; destroying a
+ * context twice is undefined.
+ */
+R2L_API r2l_status r2l_gemm_context_destroy(r2l_gemm_context ctx);
+
 typedef struct r2l_sidecar_args {
     int64_t batch;
     int64_t seqlen;             /* dense */
@@ -447,6 +474,7 @@ typedef struct r2l_sidecar_args {
     void *out; int64_t out_stride;
     void *workspace;            /* device, 256-byte aligned */
     size_t workspace_bytes;
+    r2l_gemm_context gemm;      /* the caller's GEMM context (required unless s == 0) */
 } r2l_sidecar_args;
 
 R2L_API r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream);
@@ -455,8 +483,8 @@ R2L_API r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream);
  * r2l_sidecar_tune -- for the four projections of a call with these
  * arguments, times hipBLASLt's candidate algorithms on `stream` and keeps the
  * fastest (the library's first choice unless another is at least 5% faster)
- * for every later r2l_sidecar_forward with the same shapes (process-wide,
- * per device). Call it once before serving or graph capture: it
+ * in the call's GEMM context, for every later r2l_sidecar_forward with the
+ * same shapes and that context. Call it once before serving or graph capture: it
  * synchronizes the stream, and it overwrites the workspace (never hidden or
  * out, except that when the out-projection's rows do not fit the workspace's
  * in-projection rows it is timed in out itself, or, when out is hidden, not

@@ -22,7 +22,7 @@ import torch
 from . import _abi
 from ._abi import R2LError  # noqa: F401
 
-__all__ = ["r2l_scan", "r2l_scan_noalloc", "prefix_scan_state", "block_commit_state", "bidir_scan", "sidecar_forward",
+__all__ = ["r2l_scan", "r2l_scan_noalloc", "GemmContext", "prefix_scan_state", "block_commit_state", "bidir_scan", "sidecar_forward",
            "sidecar_tune",
            "bind_sidecar", "SIDECAR_WEIGHTS",
            "workspace_size", "bind",
@@ -425,7 +425,46 @@ def bidir_scan(x, dt, Bm, Cm, A, Dskip=None, *, rev=None, cu_seqlens=None, max_s
 SIDECAR_WEIGHTS = ("W_in", "conv_w", "conv_b", "W_x", "W_dt", "dt_bias", "A", "Dskip", "W_out")
 
 
-def _fill_sidecar(hidden, w, s, cu_seqlens, max_seqlen, out):
+class GemmContext:
+    """A GEMM context of the library (r2l_gemm_context): one device's hipBLASLt
+    handle and the algorithm chosen for each projection shape. Created on
+    ``device`` (default: the current one); ``close()`` releases it (no call
+    using it may still be queued). Pass it as ``gemm=`` to the sidecar calls;
+    without one they use the device's default context, which this module
+    creates on first use and keeps for the life of the process."""
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        with torch.cuda.device(self.device):
+            self.handle = _abi.gemm_context_create()
+
+    def close(self):
+        if self.handle:
+            with torch.cuda.device(self.device):
+                _abi.gemm_context_destroy(self.handle)
+            self.handle = 0
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+_default_gemm = {}
+
+
+def default_gemm_context(device) -> GemmContext:
+    """The device's default GEMM context (created on first use, never closed)."""
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    if idx not in _default_gemm:
+        _default_gemm[idx] = GemmContext(torch.device("cuda", idx))
+    return _default_gemm[idx]
+
+
+def _fill_sidecar(hidden, w, s, cu_seqlens, max_seqlen, out, gemm=None):
     if hidden.dtype not in _DTYPES:
         raise ValueError("hidden must be float32 or bfloat16, got %s" % hidden.dtype)
     unknown = set(w) - set(SIDECAR_WEIGHTS)
@@ -472,6 +511,10 @@ def _fill_sidecar(hidden, w, s, cu_seqlens, max_seqlen, out):
         _check_f32(w.get(n), shape, n)
         setattr(a, n, _ptr(w.get(n)))
     a.s = float(s)
+    if gemm is not None:
+        a.gemm = gemm.handle
+    elif a.s != 0.0 and hidden.is_cuda:
+        a.gemm = default_gemm_context(hidden.device).handle
     return a
 
 
@@ -488,11 +531,11 @@ def _sidecar_workspace(a, workspace, device):
 
 
 def sidecar_tune(hidden, weights: dict, *, s, cu_seqlens=None, max_seqlen=None, out=None,
-                 workspace=None):
+                 workspace=None, gemm=None):
     """r2l_sidecar_tune for these arguments (see ``BoundSidecar.tune``)."""
     if out is None:
         out = torch.empty_like(hidden)
-    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out)
+    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out, gemm)
     workspace = _sidecar_workspace(a, workspace, hidden.device)
     with torch.cuda.device(hidden.device):
         stream = torch.cuda.current_stream(hidden.device).cuda_stream
@@ -500,17 +543,18 @@ def sidecar_tune(hidden, weights: dict, *, s, cu_seqlens=None, max_seqlen=None, 
 
 
 def sidecar_forward(hidden, weights: dict, *, s, cu_seqlens=None, max_seqlen=None, out=None,
-                    workspace=None):
+                    workspace=None, gemm=None):
     """The R2L sidecar block as a hook: out = hidden + s * sidecar(hidden)
     (in-projection, anti-causal depthwise conv + SiLU, x/dt projections, the
     R2L scan, SiLU(z) gate, out-projection; see r2l_sidecar_forward).
     ``weights``: W_in [2 di, dm], W_x [R + 2N, di], W_dt [di, R], W_out [dm, di]
     in hidden's dtype; conv_w [di, K], conv_b [di], dt_bias [di], A [di, N],
     Dskip [di] fp32 (conv_b, dt_bias, Dskip optional). ``out`` may be
-    ``hidden``. Returns ``out``."""
+    ``hidden``. ``gemm``: a :class:`GemmContext` (default: the device's).
+    Returns ``out``."""
     if out is None:
         out = torch.empty_like(hidden)
-    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out)
+    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out, gemm)
     workspace = _sidecar_workspace(a, workspace, hidden.device)
     with torch.cuda.device(hidden.device):
         stream = torch.cuda.current_stream(hidden.device).cuda_stream
@@ -543,11 +587,11 @@ class BoundSidecar:
 
 
 def bind_sidecar(hidden, weights: dict, *, s, out, cu_seqlens=None, max_seqlen=None,
-                 workspace=None) -> BoundSidecar:
+                 workspace=None, gemm=None) -> BoundSidecar:
     """Check and marshal a ``sidecar_forward`` call once (``out`` required)."""
-    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out)
+    a = _fill_sidecar(hidden, weights, s, cu_seqlens, max_seqlen, out, gemm)
     workspace = _sidecar_workspace(a, workspace, hidden.device)
-    keep = [hidden, out, cu_seqlens] + [v for v in weights.values() if v is not None]
+    keep = [hidden, out, cu_seqlens, gemm] + [v for v in weights.values() if v is not None]
     return BoundSidecar(a, keep, workspace, hidden.device)
 
 

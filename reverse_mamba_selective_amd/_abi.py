@@ -29,7 +29,7 @@ R2L_OP_BIDIR = 3
 R2L_OP_SAVE = 4
 R2L_OP_PREFIX_SAVE = 5
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 NOALLOC_SCRATCH_BYTES = 64 << 20   # r2l_scan_noalloc's scratch array per device
 
 EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_scan_noalloc",
@@ -38,7 +38,8 @@ EXPORTS = ("r2l_scan", "prefix_scan_state", "block_commit_state", "r2l_scan_noal
            "r2l_describe_plan", "r2l_scan_backward", "r2l_backward_workspace_size",
            "r2l_check_access_backward", "prefix_scan_backward", "bidir_scan",
            "r2l_check_access_bidir", "r2l_sidecar_forward", "r2l_sidecar_workspace_size",
-           "r2l_check_access_sidecar", "r2l_sidecar_tune", "r2l_scan_save", "r2l_checkpoint_size",
+           "r2l_check_access_sidecar", "r2l_sidecar_tune", "r2l_gemm_context_create",
+           "r2l_gemm_context_destroy", "r2l_scan_save", "r2l_checkpoint_size",
            "r2l_scan_backward_saved", "r2l_check_access_save", "r2l_check_access_backward_saved",
            "prefix_scan_save", "prefix_scan_backward_saved")
 
@@ -96,7 +97,7 @@ class SidecarArgs(ctypes.Structure):
         ("hidden", _vp), ("hidden_stride", _i64), ("W_in", _vp), ("conv_w", _vp), ("conv_b", _vp),
         ("W_x", _vp), ("W_dt", _vp), ("dt_bias", _vp), ("A", _vp), ("Dskip", _vp), ("W_out", _vp),
         ("s", ctypes.c_float), ("out", _vp), ("out_stride", _i64),
-        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("gemm", _vp),
     ]
 
 
@@ -183,6 +184,10 @@ def load(path: str = LIB_PATH):
     for fn in (lib.r2l_sidecar_forward, lib.r2l_sidecar_tune):
         fn.restype = _i32
         fn.argtypes = [sptr, _vp]
+    lib.r2l_gemm_context_create.restype = _i32
+    lib.r2l_gemm_context_create.argtypes = [ctypes.POINTER(_vp)]
+    lib.r2l_gemm_context_destroy.restype = _i32
+    lib.r2l_gemm_context_destroy.argtypes = [_vp]
     lib.r2l_sidecar_workspace_size.restype = _i32
     lib.r2l_sidecar_workspace_size.argtypes = [sptr, ctypes.POINTER(ctypes.c_size_t)]
     lib.r2l_check_access_sidecar.restype = _i32
@@ -377,3 +382,18 @@ def describe_plan(op: int, args: ScanArgs) -> dict:
     if st != R2L_OK:
         raise R2LError(st, "r2l_describe_plan", last_error())
     return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+
+
+def gemm_context_create() -> int:
+    """r2l_gemm_context_create on the current device; returns the handle."""
+    h = _vp(0)
+    st = load().r2l_gemm_context_create(ctypes.byref(h))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_gemm_context_create", last_error())
+    return h.value
+
+
+def gemm_context_destroy(handle: int) -> None:
+    st = load().r2l_gemm_context_destroy(_vp(handle))
+    if st != R2L_OK:
+        raise R2LError(st, "r2l_gemm_context_destroy", last_error())

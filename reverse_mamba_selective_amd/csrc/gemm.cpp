@@ -4,18 +4,22 @@
 //
 // Row-major Y[M, N] = alpha * X[M, K] W[N, K]^T + beta * C is, column-major,
 // Y^T = W X^T: A = W (stored K x N, transposed), B = X^T (K x M, as stored),
-// the "TN" layout. One hipBLASLt handle per device and one algorithm per
-// GEMM shape are kept for the life of the process (host memory only); the
-// library's scratch is a slice of the caller's workspace. The algorithm is
-// the library's first heuristic choice unless a tuning call has timed its
-// candidates for that shape and found one at least 5% faster.
+// the "TN" layout. The hipBLASLt handle and the algorithm chosen for each GEMM
+// shape live in a context that the caller creates and destroys
+// (r2l_gemm_context_create / _destroy), one per device; nothing here is
+// file-scope state. The library's scratch is a slice of the caller's
+// workspace. The algorithm is the library's first heuristic choice unless a
+// tuning call has timed its candidates for that shape and found one at least
+// 5% faster.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
 #include <map>
 #include <mutex>
+#include <new>
 #include <tuple>
 
+#include "r2l_scan.h"
 #include "scan_internal.h"
 
 namespace r2l {
@@ -41,24 +45,17 @@ struct Prepared {
 
 constexpr int kTuneCandidates = 16;
 
-std::mutex g_mutex;
-std::map<int, hipblasLtHandle_t> g_handles;
-std::map<Shape, Prepared> g_plans;
-
 Shape shape_of(int dev, int dtype, const GemmParams &g) {
     return Shape{dev, dtype, g.M, g.N, g.K, g.ldx, g.ldw, g.ldc, g.ldy, g.beta != 0.0f, g.ws_bytes};
 }
 
-hipblasLtHandle_t handle_of(int dev, const char **err) {
-    auto hit = g_handles.find(dev);
-    if (hit != g_handles.end()) return hit->second;
-    hipblasLtHandle_t h;
-    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) {
-        *err = "hipblasLtCreate failed";
-        return nullptr;
-    }
-    g_handles[dev] = h;
-    return h;
+void release(Prepared &p) {
+    if (p.a) hipblasLtMatrixLayoutDestroy(p.a);
+    if (p.b) hipblasLtMatrixLayoutDestroy(p.b);
+    if (p.c) hipblasLtMatrixLayoutDestroy(p.c);
+    if (p.d) hipblasLtMatrixLayoutDestroy(p.d);
+    if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+    p = Prepared{};
 }
 
 // The matmul and matrix descriptors of shape s.
@@ -95,27 +92,87 @@ const char *candidates(const Shape &s, hipblasLtHandle_t h, const Prepared &p, i
 }
 
 }  // namespace
+}  // namespace r2l
 
-const char *tune_gemm(int dtype, const GemmParams &g, void *y_scratch, hipStream_t stream) {
-    if (g.M <= 0 || g.N <= 0) return nullptr;
+// The context behind r2l_gemm_context: one device's hipBLASLt handle and the
+// prepared GEMM of every shape used with it. The mutex guards the plan map
+// (calls from several host threads may share a context).
+struct r2l_gemm_context_s {
+    static constexpr uint32_t kMagic = 0x52324c47u;   // "R2LG"
+    uint32_t magic = kMagic;
+    int device = -1;
+    hipblasLtHandle_t handle = nullptr;
+    std::mutex mutex;
+    std::map<r2l::Shape, r2l::Prepared> plans;
+};
+
+namespace r2l {
+
+const char *gemm_context_create(r2l_gemm_context *out) {
+    *out = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return "hipGetDevice failed (no device?)";
+    r2l_gemm_context c = new (std::nothrow) r2l_gemm_context_s;
+    if (!c) return "out of host memory";
+    c->device = dev;
+    if (hipblasLtCreate(&c->handle) != HIPBLAS_STATUS_SUCCESS) {
+        delete c;
+        return "hipblasLtCreate failed";
+    }
+    *out = c;
+    return nullptr;
+}
+
+const char *gemm_context_check(r2l_gemm_context c) {
+    if (!c) return "the GEMM context is NULL";
+    if (c->magic != r2l_gemm_context_s::kMagic) return "not a live GEMM context";
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return "hipGetDevice failed";
-    const Shape s = shape_of(dev, dtype, g);
-    std::lock_guard<std::mutex> lock(g_mutex);
+    if (dev != c->device) return "the GEMM context belongs to another device";
+    return nullptr;
+}
+
+const char *gemm_context_destroy(r2l_gemm_context c) {
+    if (!c || c->magic != r2l_gemm_context_s::kMagic) return "not a live GEMM context";
+    int cur = 0;
+    const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != c->device;
+    if (switch_dev) (void)hipSetDevice(c->device);
+    for (auto &kv : c->plans) release(kv.second);
+    const bool ok = hipblasLtDestroy(c->handle) == HIPBLAS_STATUS_SUCCESS;
+    if (switch_dev) (void)hipSetDevice(cur);
+    c->magic = 0;
+    delete c;
+    return ok ? nullptr : "hipblasLtDestroy failed";
+}
+
+const char *tune_gemm(r2l_gemm_context ctx, int dtype, const GemmParams &g, void *y_scratch,
+                      hipStream_t stream) {
+    if (g.M <= 0 || g.N <= 0) return nullptr;
+    const Shape s = shape_of(ctx->device, dtype, g);
+    std::lock_guard<std::mutex> lock(ctx->mutex);
     const char *err = nullptr;
-    hipblasLtHandle_t h = handle_of(dev, &err);
-    if (!h) return err;
+    hipblasLtHandle_t h = ctx->handle;
     Prepared p;
     err = describe(s, &p);
-    if (err) return err;
+    if (err) {
+        release(p);
+        return err;
+    }
     hipblasLtMatmulHeuristicResult_t res[kTuneCandidates];
     int count = 0;
     err = candidates(s, h, p, kTuneCandidates, res, &count);
-    if (err) return err;
+    if (err) {
+        release(p);
+        return err;
+    }
     hipEvent_t e0, e1;
-    if (hipEventCreate(&e0) != hipSuccess) return "hipEventCreate failed";
+    if (hipEventCreate(&e0) != hipSuccess) {
+        release(p);
+        return "hipEventCreate failed";
+    }
     if (hipEventCreate(&e1) != hipSuccess) {
         (void)hipEventDestroy(e0);
+        release(p);
         return "hipEventCreate failed";
     }
     void *Y = y_scratch ? y_scratch : g.Y;
@@ -157,48 +214,48 @@ const char *tune_gemm(int dtype, const GemmParams &g, void *y_scratch, hipStream
     }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
-    if (err) return err;
-    if (best < 0.0f) return "no hipBLASLt candidate ran";
-    auto it = g_plans.find(s);
-    if (it != g_plans.end()) {   // keep the existing descriptors of this shape
+    if (!err && best < 0.0f) err = "no hipBLASLt candidate ran";
+    if (err) {
+        release(p);
+        return err;
+    }
+    auto it = ctx->plans.find(s);
+    if (it != ctx->plans.end()) {   // keep the existing descriptors of this shape
         it->second.algo = res[pick].algo;
         it->second.ws = res[pick].workspaceSize;
-        hipblasLtMatrixLayoutDestroy(p.a);
-        hipblasLtMatrixLayoutDestroy(p.b);
-        hipblasLtMatrixLayoutDestroy(p.c);
-        hipblasLtMatrixLayoutDestroy(p.d);
-        hipblasLtMatmulDescDestroy(p.desc);
+        release(p);
     } else {
         p.algo = res[pick].algo;
         p.ws = res[pick].workspaceSize;
-        g_plans[s] = p;
+        ctx->plans[s] = p;
     }
     return nullptr;
 }
 
-const char *run_gemm(int dtype, const GemmParams &g, hipStream_t stream) {
+const char *run_gemm(r2l_gemm_context ctx, int dtype, const GemmParams &g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return nullptr;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return "hipGetDevice failed";
-    const Shape s = shape_of(dev, dtype, g);
-    hipblasLtHandle_t h;
+    const Shape s = shape_of(ctx->device, dtype, g);
+    hipblasLtHandle_t h = ctx->handle;
     Prepared p;
     {
-        std::lock_guard<std::mutex> lock(g_mutex);
-        const char *err = nullptr;
-        h = handle_of(dev, &err);
-        if (!h) return err;
-        auto it = g_plans.find(s);
-        if (it == g_plans.end()) {
-            err = describe(s, &p);
-            if (err) return err;
+        std::lock_guard<std::mutex> lock(ctx->mutex);
+        auto it = ctx->plans.find(s);
+        if (it == ctx->plans.end()) {
+            const char *err = describe(s, &p);
+            if (err) {
+                release(p);
+                return err;
+            }
             hipblasLtMatmulHeuristicResult_t res[1];
             int count = 0;
             err = candidates(s, h, p, 1, res, &count);
-            if (err) return err;
+            if (err) {
+                release(p);
+                return err;
+            }
             p.algo = res[0].algo;
             p.ws = res[0].workspaceSize;
-            g_plans[s] = p;
+            ctx->plans[s] = p;
         } else {
             p = it->second;
         }

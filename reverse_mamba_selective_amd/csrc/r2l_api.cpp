@@ -265,7 +265,7 @@ r2l_status execute(const Launch *ls, int n, hipStream_t stream) {
                 what = "sidecar conv launch";
                 break;
             case Launch::Gemm: {
-                const char *err = r2l::run_gemm(l.dtype, l.gemm, stream);
+                const char *err = r2l::run_gemm(l.gemm.ctx, l.dtype, l.gemm, stream);
                 if (err) return fail(R2L_ERR_HIP, "sidecar projection: %s", err);
                 break;
             }
@@ -496,6 +496,7 @@ r2l_status check_sidecar(const r2l_sidecar_args *a, const r2l::SidecarPlan &sp) 
         if (overlap(h, o)) return fail(R2L_ERR_ALIAS, "out overlaps hidden");
     }
     if (!sp.runs) return R2L_OK;
+    if (!a->gemm) return fail(R2L_ERR_INVALID_ARG, "gemm (the GEMM context) is NULL");
     if (!a->workspace || a->workspace_bytes < sp.ws_bytes)
         return fail(R2L_ERR_WORKSPACE, "the sidecar needs %zu workspace bytes, got %zu", sp.ws_bytes,
                     a->workspace ? a->workspace_bytes : (size_t)0);
@@ -546,9 +547,19 @@ r2l_status prepare_sidecar(const r2l_sidecar_args *a, r2l::SidecarPlan *sp) {
     return R2L_OK;
 }
 
+// The GEMM context of a call that runs: live, and made for the current device.
+r2l_status check_gemm_context(const r2l_sidecar_args *a, const r2l::SidecarPlan &sp) {
+    if (!sp.runs || sp.tokens == 0) return R2L_OK;
+    const char *err = r2l::gemm_context_check(a->gemm);
+    if (err) return fail(R2L_ERR_INVALID_ARG, "gemm: %s", err);
+    return R2L_OK;
+}
+
 r2l_status run_sidecar(const r2l_sidecar_args *a, hipStream_t stream) {
     r2l::SidecarPlan sp;
     r2l_status st = prepare_sidecar(a, &sp);
+    if (st != R2L_OK) return st;
+    st = check_gemm_context(a, sp);
     if (st != R2L_OK) return st;
     const r2l_scan_args v = r2l::sidecar_scan_view(a, sp);
     st = check_seqlens_on_device(&v);
@@ -801,9 +812,27 @@ r2l_status r2l_sidecar_forward(const r2l_sidecar_args *a, void *stream) {
     return run_sidecar(a, static_cast<hipStream_t>(stream));
 }
 
+r2l_status r2l_gemm_context_create(r2l_gemm_context *ctx) {
+    if (!ctx) return fail(R2L_ERR_INVALID_ARG, "ctx is NULL");
+    *ctx = nullptr;
+    const char *err = r2l::gemm_context_create(ctx);
+    if (err) return fail(R2L_ERR_HIP, "r2l_gemm_context_create: %s", err);
+    return ok();
+}
+
+r2l_status r2l_gemm_context_destroy(r2l_gemm_context ctx) {
+    if (!ctx) return fail(R2L_ERR_INVALID_ARG, "ctx is NULL");
+    const char *err = r2l::gemm_context_destroy(ctx);
+    if (err) return fail(strstr(err, "live") ? R2L_ERR_INVALID_ARG : R2L_ERR_HIP,
+                         "r2l_gemm_context_destroy: %s", err);
+    return ok();
+}
+
 r2l_status r2l_sidecar_tune(const r2l_sidecar_args *a, void *stream) {
     r2l::SidecarPlan sp;
     r2l_status st = prepare_sidecar(a, &sp);
+    if (st != R2L_OK) return st;
+    st = check_gemm_context(a, sp);
     if (st != R2L_OK) return st;
     Launch ls[r2l::kMaxSidecarLaunches];
     const int n = r2l::build_sidecar_launches(a, sp, ls);
@@ -821,7 +850,7 @@ r2l_status r2l_sidecar_tune(const r2l_sidecar_args *a, void *stream) {
             else if (a->out == a->hidden)
                 continue;   // in place and no room: keep the library's first choice
         }
-        const char *err = r2l::tune_gemm(a->dtype, g, scratch, s);
+        const char *err = r2l::tune_gemm(a->gemm, a->dtype, g, scratch, s);
         if (err) return fail(R2L_ERR_HIP, "sidecar projection tuning: %s", err);
     }
     return ok();

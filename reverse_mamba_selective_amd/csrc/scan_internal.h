@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "r2l_scan.h"
+
 namespace r2l {
 
 constexpr int kN = 16;      // state size the kernels are built for
@@ -121,6 +123,7 @@ struct ConvParams {
 // + beta * C[M, N] (C read only when beta != 0), in the storage type (fp32
 // accumulation).
 struct GemmParams {
+    r2l_gemm_context ctx;        // the caller's hipBLASLt handle and algorithm choices
     int64_t M, N, K;
     const void *X; int64_t ldx;
     const void *W; int64_t ldw;
@@ -236,12 +239,20 @@ hipError_t launch_copy(int dtype, const CopyParams &p, hipStream_t stream);
 // kModeGate | kModeBias, or kModeState | kModeBias)
 hipError_t launch_conv(int dtype, const ConvParams &p, hipStream_t stream);
 hipError_t launch_sidecar_segment(int dtype, int mode, const SegParams &p, hipStream_t stream);
-// a GEMM through hipBLASLt; returns a description of a failure, or nullptr
-const char *run_gemm(int dtype, const GemmParams &p, hipStream_t stream);
+// The caller-owned GEMM context (include/r2l_scan.h): create on the current
+// device, check that a handle is a live context of the current device,
+// destroy. Each returns a description of a failure, or nullptr.
+const char *gemm_context_create(r2l_gemm_context *out);
+const char *gemm_context_check(r2l_gemm_context ctx);
+const char *gemm_context_destroy(r2l_gemm_context ctx);
+// a GEMM through hipBLASLt with the context's handle and its algorithm for the
+// shape (chosen on first use); returns a description of a failure, or nullptr
+const char *run_gemm(r2l_gemm_context ctx, int dtype, const GemmParams &p, hipStream_t stream);
 // times the library's candidates for this GEMM on `stream` (writing Y, or
 // y_scratch when given, with the same leading dimension) and keeps the fastest
-// for later calls of the same shape; synchronizes the stream
-const char *tune_gemm(int dtype, const GemmParams &p, void *y_scratch, hipStream_t stream);
+// in the context for later calls of the same shape; synchronizes the stream
+const char *tune_gemm(r2l_gemm_context ctx, int dtype, const GemmParams &p, void *y_scratch,
+                      hipStream_t stream);
 // r2l_scan_noalloc: the device address of the library's scratch array on the
 // current device (looked up once per device), kNoallocScratchBytes long
 constexpr size_t kNoallocScratchBytes = size_t(64) << 20;

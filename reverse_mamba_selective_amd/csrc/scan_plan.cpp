@@ -471,7 +471,8 @@ int build_sidecar_launches(const r2l_sidecar_args *a, const SidecarPlan &sp,
         Launch l{};
         l.kind = Launch::Gemm;
         l.dtype = a->dtype;
-        l.gemm = GemmParams{T, N, K, X, ldx, W, K, C, ldc, Y, ldy, alpha, beta, gws, kGemmWorkspace};
+        l.gemm = GemmParams{a->gemm, T, N, K, X, ldx, W, K, C, ldc, Y, ldy, alpha, beta, gws,
+                            kGemmWorkspace};
         out[n++] = l;
     };
     // 1. [x | z] = hidden W_in^T

@@ -238,3 +238,32 @@ def test_noalloc_checks_and_scratch_limit():
     assert need > _abi.NOALLOC_SCRATCH_BYTES
     assert status("r2l_scan_noalloc", a) == _abi.R2L_ERR_WORKSPACE
     assert "scratch" in _abi.last_error()
+
+
+def test_gemm_context_create_destroy_and_misuse():
+    """The sidecar's GEMM context is the caller's: create / destroy through the
+    ABI, and every misuse refused with a status (no device needed)."""
+    import torch
+    from test_access_bounds import make_sidecar
+    lib = _abi.load()
+    assert lib.r2l_gemm_context_create(None) == _abi.R2L_ERR_INVALID_ARG
+    assert lib.r2l_gemm_context_destroy(None) == _abi.R2L_ERR_INVALID_ARG
+    # a host buffer that is not a context (zeros): refused, not freed
+    junk = (ctypes.c_uint8 * 256)()
+    assert lib.r2l_gemm_context_destroy(ctypes.addressof(junk)) == _abi.R2L_ERR_INVALID_ARG
+    h = ctypes.c_void_p(0)
+    st = lib.r2l_gemm_context_create(ctypes.byref(h))
+    if torch.cuda.is_available():
+        assert st == _abi.R2L_OK and h.value
+        assert lib.r2l_gemm_context_destroy(h) == _abi.R2L_OK
+    else:
+        assert st == _abi.R2L_ERR_HIP and not h.value, (st, _abi.last_error())
+    # a sidecar call that runs needs a live context: NULL and junk are refused
+    # by the argument checks, before anything reaches HIP
+    a, _ = make_sidecar(batch=2, seqlen=16)
+    a.gemm = None
+    assert lib.r2l_sidecar_forward(ctypes.byref(a), None) == _abi.R2L_ERR_INVALID_ARG
+    assert lib.r2l_sidecar_tune(ctypes.byref(a), None) == _abi.R2L_ERR_INVALID_ARG
+    a.gemm = ctypes.addressof(junk)
+    assert lib.r2l_sidecar_forward(ctypes.byref(a), None) == _abi.R2L_ERR_INVALID_ARG
+    assert "not a live GEMM context" in _abi.last_error()

@@ -600,6 +600,7 @@ def make_sidecar(*, dtype="bf16", dm=64, di=128, R=8, K=4, batch=None, seqlen=No
     N = 16
     heap = FakeHeap()
     a = _abi.SidecarArgs()
+    a.gemm = heap.alloc(64)   # a GEMM context handle; the replay never looks inside it
     a.d_model, a.d_inner, a.dstate, a.dt_rank, a.d_conv = dm, di, N, R, K
     a.dtype = _abi.R2L_DTYPE_BF16 if dtype == "bf16" else _abi.R2L_DTYPE_F32
     cu = None
@@ -699,3 +700,7 @@ def test_sidecar_rejects_bad_arguments():
     bad = _abi.SidecarArgs.from_buffer_copy(a)
     bad.W_x = None
     assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_INVALID_ARG
+    bad = _abi.SidecarArgs.from_buffer_copy(a)
+    bad.gemm = None               # s != 0 needs the caller's GEMM context
+    assert _abi.check_access_sidecar(bad, cu)[0] == _abi.R2L_ERR_INVALID_ARG
+    assert "gemm" in _abi.last_error()

@@ -180,3 +180,55 @@ def test_sidecar_tuned_projections(gpu):
     torch.cuda.synchronize()
     assert np.array_equal(bits(h), bits(before))
     check(h_np, w_np, 0.6, lengths, "bf16", "tuned", dense=True)
+
+
+def test_sidecar_bf16_against_unrounded_oracle(gpu):
+    """The bf16 block at the full hook shape (64 x 32 x 2048 -> 4096) against the
+    fp64 oracle with no storage rounding at all: its contribution out - hidden
+    within 2e-2 of max|s * o| (the bf16 bar). s = 1 so that out's own bf16
+    rounding (half an ulp of |hidden + c| <= 2^-6 here) stays a small part of it."""
+    lengths = [32] * 64
+    w_np = synth.sidecar_weights(86, 2048, 4096, 128, dtype="bf16")
+    h_np = synth.hidden_states(87, lengths, 2048, "bf16")
+    ref = oracle.sidecar_forward(h_np, w_np["W_in"], w_np["conv_w"], w_np["conv_b"], w_np["W_x"],
+                                 w_np["W_dt"], w_np["dt_bias"], w_np["A"], w_np["Dskip"],
+                                 w_np["W_out"], s=1.0, seq_offsets=synth.offsets(lengths),
+                                 store=None)
+    h = dev(h_np, "bf16").view(64, 32, -1)
+    out = r2l.sidecar_forward(h, to_gpu(w_np, "bf16"), s=1.0)
+    torch.cuda.synchronize()
+    c = host(out).reshape(-1, 2048) - h_np.astype(np.float64)
+    e = float(np.max(np.abs(c - ref["o"])) / np.max(np.abs(ref["o"])))
+    report("contribution vs unrounded oracle", e, TOL["bf16"])
+    assert e <= TOL["bf16"], e
+
+
+def test_sidecar_caller_gemm_contexts(gpu):
+    """The GEMM handle and algorithm choices live in contexts the caller
+    creates and closes: two contexts give the default context's bits; tuning
+    one leaves the other's choices alone and the call within the bar."""
+    lengths = [32] * 8
+    w_np = synth.sidecar_weights(88, 256, 512, 16, dtype="bf16")
+    h_np = synth.hidden_states(89, lengths, 256, "bf16")
+    w = to_gpu(w_np, "bf16")
+    h = dev(h_np, "bf16").view(8, 32, -1)
+    base = r2l.sidecar_forward(h, w, s=0.4)
+    with r2l.GemmContext() as c1, r2l.GemmContext() as c2:
+        o1 = r2l.sidecar_forward(h, w, s=0.4, gemm=c1)
+        o2 = r2l.sidecar_forward(h, w, s=0.4, gemm=c2)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o1), bits(base)) and np.array_equal(bits(o2), bits(base))
+        r2l.sidecar_tune(h, w, s=0.4, gemm=c2)
+        o1b = r2l.sidecar_forward(h, w, s=0.4, gemm=c1)
+        o2b = r2l.sidecar_forward(h, w, s=0.4, gemm=c2)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o1b), bits(base))
+        ref = oracle.sidecar_forward(h_np, w_np["W_in"], w_np["conv_w"], w_np["conv_b"],
+                                     w_np["W_x"], w_np["W_dt"], w_np["dt_bias"], w_np["A"],
+                                     w_np["Dskip"], w_np["W_out"], s=0.4,
+                                     seq_offsets=synth.offsets(lengths), store="bf16")
+        e = float(np.max(np.abs(host(o2b).reshape(-1, 256) - ref["out"])) /
+                  np.max(np.abs(ref["out"])))
+        assert e <= TOL["bf16"], e
+    assert c1.handle == 0 and c2.handle == 0
+    c1.close()   # closing again is a no-op
