@@ -972,39 +972,56 @@ class _Call:
         self.fn(stream)
 
 
-class ServingStep(Workload):
-    """A denoising step of the serving harness: a stub causal backbone shaped like
-    Qwen3-1.7B (28 decoder layers, hidden 2048, 16 query / 8 key-value heads of
-    128, MLP 6144; random weights, no rotary embedding) over a generation block of
-    32 tokens for a batch of 8 whose 4096-token prompts were prefilled into a KV
-    cache, with the sidecar block (r2l_sidecar_forward, d_inner 4096) hooked after
-    every 4th layer. Prefill runs once in setup (timed with events, reported);
-    the timed step is the block's pass through all 28 layers and 7 hooks, with an
-    event before every layer and hook, so that the hooks' share of the step is
-    measured in place. The backbone is plain torch (matmuls on contiguous
-    operands, softmax accumulating in fp32), its layers between two hooks replayed as one
-    hipGraph; only the hooks are this library."""
-    name = "serving_step_bf16_b8_P4096_blk32_qwen3-1.7b-stub_28L_7hooks"
-    B, P, L = 8, 4096, 32
-    DM, HQ, HKV, HD, FF, LAYERS, EVERY = 2048, 16, 8, 128, 6144, 28, 4
-    DI, R = 4096, 128
-    graph_ok = False
+class StubBackbone:
+    """A causal decoder stub shaped like Qwen3-1.7B (pre-norm RMSNorm, grouped-query
+    attention, SiLU-gated MLP; random weights, no rotary embedding) with a KV
+    cache, in plain torch on any device and dtype. ``forward(h, at, hooks)``
+    runs every layer on h [B, T, dm] in place for the tokens at cache positions
+    [at, at + T): their keys and values go to the cache and each query attends
+    causally over the cache up to its own position; after layer l, hooks[l](h)
+    (if given) updates h in place — the R2L sidecar hooks. Only timing and the
+    hooks' inputs depend on this stub."""
 
-    def _layer(self, torch, l, h, write_cache_at=None, q_chunk=None):
-        """One pre-norm decoder layer on h [B, T, DM] in place. With write_cache_at
-        (prefill) the keys / values of h go to cache positions [at, at + T) and the
-        queries attend causally over the cache up to their own position."""
+    def __init__(self, torch, *, layers, dm, hq, hkv, hd, ff, batch, max_tokens, device, dtype,
+                 seed):
+        self.torch = torch
+        self.layers, self.DM, self.HQ, self.HKV, self.HD, self.FF = layers, dm, hq, hkv, hd, ff
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+
+        def w(i, o):
+            return (torch.randn((i, o), generator=gen, device=device, dtype=torch.float32)
+                    / math.sqrt(i)).to(dtype)
+
+        nq, nkv = hq * hd, hkv * hd
+        self.W = [{"ln1": torch.ones(dm, dtype=dtype, device=device),
+                   "ln2": torch.ones(dm, dtype=dtype, device=device),
+                   "qkv": w(dm, nq + 2 * nkv), "o": w(nq, dm),
+                   "gate": w(dm, ff), "up": w(dm, ff), "down": w(ff, dm)}
+                  for _ in range(layers)]
+        self.Kt = [torch.zeros((batch, hkv, hd, max_tokens), dtype=dtype, device=device)
+                   for _ in range(layers)]
+        self.V = [torch.zeros((batch, hkv, max_tokens, hd), dtype=dtype, device=device)
+                  for _ in range(layers)]
+
+    def cache_bytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.Kt + self.V)
+
+    def layer(self, l, h, at, q_chunk=None):
+        """Layer l on h [B, T, DM] in place, the tokens at cache positions
+        [at, at + T); queries in chunks of q_chunk tokens (memory only)."""
+        torch = self.torch
         import torch.nn.functional as F
         W = self.W[l]
         B, T, _ = h.shape
         g = self.HQ // self.HKV
-        a = h.float()
+        acc = torch.promote_types(h.dtype, torch.float32)      # the norms' accumulation type
+        a = h.to(acc)
         a = (a * torch.rsqrt(a.pow(2).mean(-1, keepdim=True) + 1e-6)).to(h.dtype) * W["ln1"]
         qkv = torch.matmul(a, W["qkv"])                       # [B, T, (HQ + 2 HKV) HD]
         q = qkv[..., :self.HQ * self.HD].reshape(B, T, self.HKV, g, self.HD)
         k = qkv[..., self.HQ * self.HD:(self.HQ + self.HKV) * self.HD].reshape(B, T, self.HKV, self.HD)
         v = qkv[..., (self.HQ + self.HKV) * self.HD:].reshape(B, T, self.HKV, self.HD)
-        at = self.P if write_cache_at is None else write_cache_at
         Kt, V = self.Kt[l], self.V[l]                          # [B, HKV, HD, S], [B, HKV, S, HD]
         Kt[:, :, :, at:at + T] = k.permute(0, 2, 3, 1)
         V[:, :, at:at + T, :] = v.permute(0, 2, 1, 3)
@@ -1022,48 +1039,64 @@ class ServingStep(Workload):
             pos = torch.arange(c0, c1, device=h.device).repeat_interleave(g)
             keys = torch.arange(c0, c1, device=h.device)
             sc[..., at + c0:end].masked_fill_(keys[None, :] > pos[:, None], float("-inf"))
-            pr = torch.softmax(sc, dim=-1)                     # fp32 inside, bf16 out
+            pr = torch.softmax(sc, dim=-1)                     # fp32 inside for bf16
             out[:, :, c0 * g:c1 * g] = torch.matmul(pr, V[:, :, :end].contiguous())
         o = out.reshape(B, self.HKV, T, g, self.HD).permute(0, 2, 1, 3, 4).reshape(B, T, -1)
         h += torch.matmul(o, W["o"])
-        m = h.float()
+        m = h.to(acc)
         m = (m * torch.rsqrt(m.pow(2).mean(-1, keepdim=True) + 1e-6)).to(h.dtype) * W["ln2"]
         h += torch.matmul(F.silu(torch.matmul(m, W["gate"])) * torch.matmul(m, W["up"]), W["down"])
+
+    def forward(self, h, at, hooks=None, q_chunk=None, mark=None):
+        """Every layer on h in place (cache positions [at, at + T)), hooks[l](h)
+        after layer l; mark(kind, l), if given, is called before each layer
+        ("layer") and hook ("hook") and once at the end ("end", None)."""
+        for l in range(self.layers):
+            if mark:
+                mark("layer", l)
+            self.layer(l, h, at, q_chunk)
+            if hooks and l in hooks:
+                if mark:
+                    mark("hook", l)
+                hooks[l](h)
+        if mark:
+            mark("end", None)
+        return h
+
+
+class ServingStep(Workload):
+    """A denoising step of the serving harness: a stub causal backbone shaped like
+    Qwen3-1.7B (28 decoder layers, hidden 2048, 16 query / 8 key-value heads of
+    128, MLP 6144; random weights, no rotary embedding) over a generation block of
+    32 tokens for a batch of 8 whose 4096-token prompts were prefilled into a KV
+    cache, with the sidecar block (r2l_sidecar_forward, d_inner 4096) hooked after
+    every 4th layer. Prefill runs once in setup with the hooks active over each
+    prompt (the R2L sidecar over the 4096 prompt tokens at every hooked layer), so
+    the KV cache of the later layers holds keys and values of post-hook hidden
+    states, and the post-hook hidden states of every hooked layer are kept as
+    well; it is timed with an event before every layer and hook (prefill split
+    between hooks and backbone). The timed step is the block's pass through all
+    28 layers and 7 hooks, with an event before every layer group and hook, so
+    that the hooks' share of the step is measured in place. The backbone is plain
+    torch (matmuls on contiguous operands, softmax accumulating in fp32), its
+    layers between two hooks replayed as one hipGraph; only the hooks are this
+    library."""
+    name = "serving_step_bf16_b8_P4096_blk32_qwen3-1.7b-stub_28L_7hooks"
+    B, P, L = 8, 4096, 32
+    DM, HQ, HKV, HD, FF, LAYERS, EVERY = 2048, 16, 8, 128, 6144, 28, 4
+    DI, R = 4096, 128
+    graph_ok = False
 
     def setup(self, torch, r2l):
         import synth
         self.torch = torch
         dev = "cuda"
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(707)
         bf = torch.bfloat16
-
-        def w(i, o):
-            return (torch.randn((i, o), generator=gen, device=dev) / math.sqrt(i)).to(bf)
-
-        nq, nkv = self.HQ * self.HD, self.HKV * self.HD
-        self.W = [{"ln1": torch.ones(self.DM, dtype=bf, device=dev),
-                   "ln2": torch.ones(self.DM, dtype=bf, device=dev),
-                   "qkv": w(self.DM, nq + 2 * nkv), "o": w(nq, self.DM),
-                   "gate": w(self.DM, self.FF), "up": w(self.DM, self.FF), "down": w(self.FF, self.DM)}
-                  for _ in range(self.LAYERS)]
-        S = self.P + self.L
-        self.Kt = [torch.zeros((self.B, self.HKV, self.HD, S), dtype=bf, device=dev)
-                   for _ in range(self.LAYERS)]
-        self.V = [torch.zeros((self.B, self.HKV, S, self.HD), dtype=bf, device=dev)
-                  for _ in range(self.LAYERS)]
-        # prefill: the prompt through every layer, its keys / values into the cache
-        # (the R2L stream covers generation tokens only, so no hook runs here)
-        prompt = torch.randn((self.B, self.P, self.DM), generator=gen, device=dev).to(bf)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for l in range(self.LAYERS):
-            self._layer(torch, l, prompt, write_cache_at=0, q_chunk=512)
-        e1.record()
-        torch.cuda.synchronize()
-        self.prefill_ms = e0.elapsed_time(e1)
-        del prompt
+        self.bb = StubBackbone(torch, layers=self.LAYERS, dm=self.DM, hq=self.HQ, hkv=self.HKV,
+                               hd=self.HD, ff=self.FF, batch=self.B, max_tokens=self.P + self.L,
+                               device=dev, dtype=bf, seed=707)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(708)
         # the sidecar hooks (random init), one per hooked layer
         self.hook_layers = [l for l in range(self.LAYERS) if (l + 1) % self.EVERY == 0]
         self.hooks = []
@@ -1074,6 +1107,51 @@ class ServingStep(Workload):
                                                           "Dskip") else _dev(torch, v, "bf16"))
                   for k, v in wt.items()}
             self.hooks.append((wt, wd, float(synth.gates(SERVING_KEY, 7, 0.0, 0.1)[j])))
+        # Prefill: the prompts through every layer with the hooks active over them
+        # (the R2L sidecar over each whole prompt), keys / values into the cache;
+        # the post-hook hidden states of every hooked layer are kept. An event
+        # before every layer and hook splits its time.
+        prompt = torch.randn((self.B, self.P, self.DM), generator=gen, device=dev).to(bf)
+        pws = None
+        pre_hooks = {}
+        for j, l in enumerate(self.hook_layers):
+            wt, wd, s = self.hooks[j]
+            c = r2l.bind_sidecar(prompt, wd, s=s, out=prompt, workspace=pws)
+            pws = c.workspace
+            pre_hooks[l] = c
+        self.hook_states = {}
+
+        def hook_at(l):
+            def run(h):
+                pre_hooks[l].launch(torch.cuda.current_stream().cuda_stream)
+                self.hook_states[l] = h.clone()
+            return run
+
+        marks = []
+
+        def mark(kind, l):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.append((kind, e))
+
+        for _ in range(2):   # the first pass warms up; the second is timed and kept
+            for t in self.bb.Kt + self.bb.V:
+                t.zero_()
+            x = prompt.clone()
+            marks.clear()
+            torch.cuda.synchronize()
+            self.bb.forward(x, 0, hooks={l: hook_at(l) for l in self.hook_layers}, q_chunk=512,
+                            mark=mark)
+            torch.cuda.synchronize()
+        spans = [(marks[i][0], marks[i][1].elapsed_time(marks[i + 1][1]))
+                 for i in range(len(marks) - 1)]
+        self.prefill_ms = marks[0][1].elapsed_time(marks[-1][1])
+        self.prefill_hooks_ms = sum(t for k, t in spans if k == "hook")
+        self.prefill_backbone_ms = sum(t for k, t in spans if k == "layer")
+        self.prefill_hook_in = None
+        del x, prompt, pws, pre_hooks
+        self.cache_gb = (self.bb.cache_bytes() + sum(t.numel() * t.element_size()
+                                                     for t in self.hook_states.values())) / 1e9
         # rotating generation blocks (noisy-token embeddings stand-ins)
         self.R_sets = 4
         self.blocks = [torch.randn((self.B, self.L, self.DM), generator=gen, device=dev).to(bf)
@@ -1100,7 +1178,7 @@ class ServingStep(Workload):
             self.h.copy_(self.blocks[0])
             for seg in segs:
                 for l in seg:
-                    self._layer(torch, l, self.h)
+                    self.bb.layer(l, self.h, self.P)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
 
@@ -1114,7 +1192,7 @@ class ServingStep(Workload):
             if r is not None:
                 self.h.copy_(self.blocks[r])
             for l in seg:
-                self._layer(torch, l, self.h)
+                self.bb.layer(l, self.h, self.P)
 
         first = [capture(lambda r=r: run_seg(segs[0], r)) for r in range(self.R_sets)]
         rest = [capture(lambda seg=seg: run_seg(seg)) for seg in segs[1:]]
@@ -1148,7 +1226,7 @@ class ServingStep(Workload):
         # one hook's input and output inside a step, for parity against the oracle
         self.h.copy_(self.blocks[0])
         for l in range(self.LAYERS):
-            self._layer(torch, l, self.h)
+            self.bb.layer(l, self.h, self.P)
             if l == self.hook_layers[0]:
                 self.hook_in = self.h.clone()
                 self.bound[0].launch(torch.cuda.current_stream().cuda_stream)
@@ -1160,6 +1238,15 @@ class ServingStep(Workload):
                        "heads x 128, MLP 6144, random init, no rotary", "hooks_per_step": 7,
                        "hook": "r2l_sidecar_forward (d_inner 4096, N 16, dt_rank 128, K 4)",
                        "in_dtype": "bf16", "prefill_ms": round(self.prefill_ms, 3),
+                       "prefill_split_ms": {"hooks (7 x R2L sidecar over 8 x 4096 prompt "
+                                            "tokens)": round(self.prefill_hooks_ms, 3),
+                                            "backbone (28 stub layers)":
+                                                round(self.prefill_backbone_ms, 3)},
+                       "prefill_hook_share": round(self.prefill_hooks_ms / self.prefill_ms, 4),
+                       "prefill_cache_gb": round(self.cache_gb, 3),
+                       "prefill_cache": "K/V of all 28 layers over prompt + block slots (from "
+                                        "post-hook hidden states after the first hook) and the "
+                                        "post-hook hidden states of the 7 hooked layers",
                        "parallelism": "single_gpu", "weights": "random init (synthetic)"}
 
     def cpu_baseline(self, budget_s, nthreads=0, parity=None):
