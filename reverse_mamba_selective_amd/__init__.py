@@ -716,29 +716,37 @@ def r2l_scan_backward(x, dt, Bm, Cm, A, Dskip=None, *, dout, dh_out=None, cu_seq
 
 class R2LScan(torch.autograd.Function):
     """The R2L stream as a differentiable op (dense [batch, L, D] tensors):
-    out = x + s * y (the hook; ``s`` a float) or y (``s`` None). Gradients flow
-    to x, dt, Bm, Cm, A and Dskip through ``r2l_scan_backward``, from the
-    state checkpoints that the forward (``r2l_scan_save``) stored."""
+    out = x + s * y (the hook) or y (``s`` None). ``s`` is a float (a fixed
+    gate) or a one-element fp32 tensor (the learnable gate, initialised at
+    zero, which receives ds = sum(dout * y); its value is read on the host for
+    the call). Gradients flow to x, dt, Bm, Cm, A and Dskip (and s) through
+    ``r2l_scan_backward``: from the state checkpoints that the forward
+    (``r2l_scan_save``) stored when any of x..Dskip needs a gradient, else
+    through the backward's own state pass."""
 
     @staticmethod
     def forward(ctx, x, dt, Bm, Cm, A, Dskip, s=None):
         res = x if s is not None else None
-        gate = 0.0 if s is None else float(s)
+        s_tensor = isinstance(s, torch.Tensor)
+        if s_tensor and s.numel() != 1:
+            raise ValueError("s must be a float or a one-element tensor")
+        gate = 0.0 if s is None else float(s.item() if s_tensor else s)
         if any(ctx.needs_input_grad[:6]):
             out, ckpt = r2l_scan_save(x, dt, Bm, Cm, A, Dskip, res=res, s=gate)
-        else:   # no gradient will be asked for: no checkpoints
+        else:   # no checkpoints: a gradient of s alone runs the backward's state pass
             out, ckpt = r2l_scan(x, dt, Bm, Cm, A, Dskip, res=res, s=gate), None
         ctx.save_for_backward(x, dt, Bm, Cm, A, Dskip, ckpt)
-        ctx.s = s
+        ctx.gate, ctx.has_res, ctx.s_tensor = gate, s is not None, s_tensor
+        ctx.s_like = (s.shape, s.dtype) if s_tensor else None
         return out
 
     @staticmethod
     def backward(ctx, dout):
         x, dt, Bm, Cm, A, Dskip, ckpt = ctx.saved_tensors
-        s = ctx.s
+        want_ds = ctx.s_tensor and ctx.needs_input_grad[6]
+        names = ("dx", "ddt", "dBm", "dCm", "dA", "dDskip") + (("ds",) if want_ds else ())
         g = r2l_scan_backward(x, dt, Bm, Cm, A, Dskip, dout=dout.contiguous(),
-                              res=x if s is not None else None,
-                              s=0.0 if s is None else float(s), ckpt=ckpt,
-                              grads=("dx", "ddt", "dBm", "dCm", "dA", "dDskip"))
+                              res=x if ctx.has_res else None, s=ctx.gate, ckpt=ckpt, grads=names)
+        ds = g["ds"].reshape(ctx.s_like[0]).to(ctx.s_like[1]) if want_ds else None
         return (g["dx"], g["ddt"], g["dBm"].to(Bm.dtype), g["dCm"].to(Cm.dtype), g["dA"],
-                g["dDskip"] if Dskip is not None else None, None)
+                g["dDskip"] if Dskip is not None else None, ds)

@@ -620,3 +620,80 @@ def test_ragged_prefix_prefill_subset(gpu):
     ref = oracle.prefix_scan_state(pre.x, pre.dt, pre.Bm, pre.A, seq_offsets=pre.offsets)
     check_state(h, ref, "prefill prefix states")
     torch.cuda.synchronize()
+
+
+def _device_draws(seed, tok, D, dt_mean):
+    """Seeded inputs drawn on the GPU (the distributions of synth, dt ~ N(dt_mean,
+    0.5)) for the full-size plans, whose inputs are too large to draw on the host;
+    the oracle reads back the sampled sequences."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+    return {"x": torch.randn((tok, D), generator=g, device="cuda").to(bf),
+            "dt": (torch.randn((tok, D), generator=g, device="cuda") * 0.5 + dt_mean).to(bf),
+            "Bm": torch.randn((tok, 16), generator=g, device="cuda").to(bf),
+            "Cm": torch.randn((tok, 16), generator=g, device="cuda").to(bf),
+            "A": -(torch.arange(16, device="cuda", dtype=torch.float32) + 1).repeat(D, 1),
+            "Dskip": torch.randn((D,), generator=g, device="cuda")}
+
+
+def _ulp_factor(got, ref):
+    """Worst element in units of (one bf16 ulp of ref + 1e-5 * max|ref|)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    slack = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7) + \
+        1e-5 * np.max(np.abs(ref))
+    return float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref) / slack))
+
+
+def test_prefill_long_memory_full_plan(gpu):
+    """The prefill shape (8 x 4096 x 4096, bf16) with long-memory inputs (dt ~
+    N(-6, 0.5): Delta ~ 0.0025, state memory of hundreds of tokens) under the
+    planner's own plan (9 chunks of 456 tokens: chunk pass, carry, readout pass);
+    sampled sequences against the oracle. A reverse scan that dropped the carry
+    into the chunks left of the rightmost would be off by more than ten times the
+    element bound there."""
+    B, L, D = 8, 4096, 4096
+    g = _device_draws(3101, B * L, D, -6.0)
+    view = {k: (g[k].view(B, L, -1) if k in ("x", "dt", "Bm", "Cm") else g[k]) for k in g}
+    y = torch.empty_like(view["x"])
+    call = r2l.bind("r2l_scan", out=y, **view)
+    plan = call.plan()
+    assert plan["chunked"] and plan["chunks"] == 9 and plan["chunk_tokens"] == 456, plan
+    call.launch()
+    torch.cuda.synchronize()
+    A, Ds = g["A"].cpu().numpy(), g["Dskip"].cpu().numpy()
+    for b in (0, 7):
+        rows = slice(b * L, (b + 1) * L)
+        x, dt, Bm, Cm = (g[k][rows].float().cpu().numpy() for k in ("x", "dt", "Bm", "Cm"))
+        ref = oracle.selective_scan(x, dt, Bm, Cm, A, Ds, reverse=True,
+                                    seq_offsets=np.array([0, L]))
+        check_y(y[b], ref["y"], "bf16", "long-memory sequence %d" % b)
+        n = L - 456    # left of the rightmost chunk, scanned from zero: no carry
+        nc = oracle.selective_scan(x[:n], dt[:n], Bm[:n], Cm[:n], A, Ds, reverse=True,
+                                   seq_offsets=np.array([0, n]))
+        assert _ulp_factor(nc["y"], ref["y"][:n]) > 10.0
+
+
+def test_ragged_prefix_prefill_full_plan(gpu):
+    """The ragged prefix-state prefill at its full size (256 prefixes of
+    U{256..8192} tokens, D = 4096, bf16: the benchmark's call and plan, chunks
+    of at most 1024 tokens joined by the carry); the final states of sampled
+    prefixes (the shortest, the longest, and spread ones) against the oracle."""
+    lens = synth.ragged_prefix_lengths()
+    off = synth.offsets(lens)
+    D = 4096
+    g = _device_draws(3102, int(off[-1]), D, -2.0)
+    cu = torch.from_numpy(off.astype(np.int32)).cuda()
+    h = torch.empty((len(lens), D, 16), dtype=torch.float32, device="cuda")
+    call = r2l.bind("prefix_scan_state", x=g["x"], dt=g["dt"], Bm=g["Bm"], A=g["A"], h_out=h,
+                    cu_seqlens=cu, max_seqlen=int(lens.max()))
+    plan = call.plan()
+    assert plan["chunked"] and plan["chunk_tokens"] <= 1024, plan
+    call.launch()
+    torch.cuda.synchronize()
+    A = g["A"].cpu().numpy()
+    for b in sorted({0, 100, 255, int(np.argmin(lens)), int(np.argmax(lens))}):
+        rows = slice(int(off[b]), int(off[b + 1]))
+        x, dt, Bm = (g[k][rows].float().cpu().numpy() for k in ("x", "dt", "Bm"))
+        ref = oracle.prefix_scan_state(x, dt, Bm, A, seq_offsets=np.array([0, x.shape[0]]))
+        check_state(h[b:b + 1], ref, "prefix %d (%d tokens)" % (b, lens[b]))

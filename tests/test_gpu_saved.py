@@ -6,8 +6,8 @@ r2l_scan_backward (the same kernels and the same arithmetic).
 
 Tolerances are those of the forward and backward parity tests: outputs
 max|err| / max|ref| <= 1e-5 (fp32) or 2e-2 and one bf16 ulp per element
-(bf16), states 1e-5; gradients 1e-4 (fp32) or 2e-2 and one bf16 ulp plus
-1e-4 * max|ref| per element for dx and ddt stored in bf16.
+(bf16), states 1e-5; gradients 1e-5 (fp32) or 2e-2 and one bf16 ulp plus
+1e-5 * max|ref| per element for dx and ddt stored in bf16.
 """
 from __future__ import annotations
 
