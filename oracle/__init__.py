@@ -42,19 +42,33 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "selective_scan_ref.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SAN_PATH = os.path.join(_HERE, "_san", "liboracle.so")
 _lib = None
 
 _dptr = ctypes.POINTER(ctypes.c_double)
 _i64ptr = ctypes.POINTER(ctypes.c_int64)
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
-    """Compile the oracle with gcc (fp64, no fast-math, no FMA contraction)."""
-    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, no FMA contraction).
+    sanitize: a copy under oracle/_san/ built by ROCm's clang with
+    AddressSanitizer and UndefinedBehaviorSanitizer (no OpenMP), to run with the
+    sanitized library of the scan (whose sanitizer runtime it shares)."""
+    if sanitize:
+        out = _SAN_PATH
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+    elif not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
         return out
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
-           "-ffp-contract=off", "-fno-fast-math", "-o", tmp, src, "-lm"]
+    if sanitize:
+        clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+        cmd = [clang, "-O1", "-g", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer", "-shared-libsan", "-Wno-unknown-pragmas",
+               "-o", tmp, src, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -92,6 +106,10 @@ class OracleLib:
 def _load() -> OracleLib:
     global _lib
     if _lib is None:
+        alt = os.environ.get("R2L_ORACLE_LIB")   # another build (the sanitized one)
+        if alt:
+            _lib = OracleLib(alt)
+            return _lib
         if not os.path.exists(_LIB_PATH) or \
                 os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             build()

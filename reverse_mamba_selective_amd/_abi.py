@@ -9,7 +9,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libr2l_scan.so")
+# R2L_LIB_PATH: another build of the library (the host-sanitized one of build.py --sanitize)
+LIB_PATH = os.environ.get("R2L_LIB_PATH") or os.path.join(HERE, "libr2l_scan.so")
 
 R2L_OK = 0
 R2L_ERR_INVALID_ARG = -1
