@@ -59,18 +59,10 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     const uint32_t dl = lg.d;
     const int sub = lg.sub;
 
+    // A * log2(e), the state and Dskip: read at start-up, after the first
+    // rows are requested (below)
     float a2[NS], h[NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) a2[j] = p.A[dl * kN + sub * NS + j] * kLog2e;
-    if (hin) {
-        const float *hp = hin + dl * kN + sub * NS;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) h[j] = hp[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < NS; ++j) h[j] = 0.0f;
-    }
-    const float dskip = (READOUT && p.Dskip) ? p.Dskip[dl] : 0.0f;
+    float dskip = 0.0f;
     float dsum = 0.0f;
 
     // Per-token rows go through raw buffer resources based at the sequence's
@@ -242,6 +234,21 @@ __device__ __forceinline__ void scan_segment(const SegParams &p, float *lds, con
     if (ntok > 0) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) load_pos(prefetch_pos(j, ntok), j);
+    }
+    // the per-lane constants after the rows, so that their round trip to
+    // memory overlaps the rows' instead of preceding it
+#pragma unroll
+    for (int j = 0; j < NS; ++j) a2[j] = p.A[dl * kN + sub * NS + j] * kLog2e;
+    if (hin) {
+        const float *hp = hin + dl * kN + sub * NS;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) h[j] = hp[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) h[j] = 0.0f;
+    }
+    if (READOUT && p.Dskip) dskip = p.Dskip[dl];
+    if (ntok > 0) {
         stage_store(0);
         dnext = delta_of(dq[0]);
     }
@@ -287,6 +294,19 @@ __global__ __launch_bounds__(kWG) void segment_scan_kernel(const SegParams p) {
     constexpr int NBC_MAX = (MODE & kModeOutMask) != kModeState ? 2 * kN : kN;
     __shared__ __align__(16) float lds[2 * kTile * NBC_MAX];
 
+    // The set-up reads these arguments behind its branches (block validity,
+    // layout, chunk role); loaded where they are first used, each would cost a
+    // dependent round trip to memory before the first row is requested. An
+    // empty asm statement that takes them as scalar operands makes the
+    // compiler fetch them all at once, here.
+    asm volatile("" ::"s"(p.nblocks), "s"(p.tiles), "s"(p.nchunks), "s"(p.chunk_len),
+                 "s"(p.seqlen), "s"(p.cu_seqlens), "s"(p.D), "s"(p.split_c0), "s"(p.skip_c0),
+                 "s"(p.skip_last), "s"(p.hin));
+    asm volatile("" ::"s"(p.x), "s"(p.xs), "s"(p.xbs), "s"(p.dt), "s"(p.dts), "s"(p.dtbs),
+                 "s"(p.Bm), "s"(p.Bs), "s"(p.Bbs), "s"(p.Cm), "s"(p.Cs), "s"(p.Cbs),
+                 "s"(p.bc_vec));
+    asm volatile("" ::"s"(p.A), "s"(p.Dskip), "s"(p.res), "s"(p.rs), "s"(p.rbs), "s"(p.s),
+                 "s"(p.out), "s"(p.os), "s"(p.obs));
     const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, blockIdx.x);
     if (!bg.valid) return;
     const int64_t b = bg.b;
