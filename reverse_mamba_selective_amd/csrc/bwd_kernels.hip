@@ -255,6 +255,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             }
 
             // the adjoint over the group, last visited position first
+            R odx[K], oddt[K];
             auto adjoint = [&](const int j) {
                 const float *row = bc + (gi * K + j) * NBC + sub * NS;   // Bm slice; Cm at + kN
                 const float xv = E::widen(xr[j]);
@@ -290,11 +291,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 const float dxv = fmaf(delta[j], group_sum<G>(dxs), fmaf(dy, dsk, dxr * gv));
                 float ddtv = ddelta;
                 if constexpr (SP) ddtv *= sigmoid(E::widen(dr[j]));
-                const uint32_t orow = static_cast<uint32_t>(seg_row(sg, gpos + j));
-                if (lg.active) {
-                    if (p.dx) E::bstore(E::pack(dxv), rdx, doff, orow * dxrb);
-                    if (p.ddt) E::bstore(E::pack(ddtv), rdd, doff, orow * ddrb);
-                }
+                odx[j] = E::pack(dxv);   // stored after the group: no branch per token
+                oddt[j] = E::pack(ddtv);
                 row_channel_sum<G>(pb);
                 row_channel_sum<G>(pc);
                 float *rw = rd_[wave * 4 + (lane >> 4)][j];
@@ -311,6 +309,16 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 #pragma unroll
                 for (int j = K - 1; j >= 0; --j)
                     if (j < gcnt) adjoint(j);
+            }
+            // the group's dx and ddt rows (lanes past the last channel store nothing)
+            if (lg.active) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    if (j >= gcnt) break;
+                    const uint32_t orow = static_cast<uint32_t>(seg_row(sg, gpos + j));
+                    if (p.dx) E::bstore(odx[j], rdx, doff, orow * dxrb);
+                    if (p.ddt) E::bstore(oddt[j], rdd, doff, orow * ddrb);
+                }
             }
             __syncthreads();
             {   // the block's sums over its channels: one thread per (token, column)
