@@ -213,6 +213,14 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 
         for (int gi = (tcnt - 1) / K; gi >= 0; --gi) {
             const int gpos = tbase + gi * K;
+            {   // groups left after this one: a wave with more left issues first, so
+                // the waves sharing a SIMD stay abreast (as in the segment scan)
+                const int q = gpos / K;
+                if (q >= 3) __builtin_amdgcn_s_setprio(3);
+                else if (q == 2) __builtin_amdgcn_s_setprio(2);
+                else if (q == 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
             const int gcnt = ntok - gpos < K ? ntok - gpos : K;
             // this group's per-token inputs were requested during the previous
             // group; request the next group's (gpos - K) now
