@@ -301,9 +301,11 @@ def bwd_alu_ops_per_tc() -> float:
     trans ops weighted), without recomputation: the forward states (84.5), per
     state the adjoint (g += dy*C; dy*h and its sum over channels; the dDelta
     term B*x + A*(abar*h_prev) and its fma; dA += g*Delta*(abar*h_prev); dx's
-    g*B; g*Delta*x and its sum over channels; g *= abar: 13), per channel the
-    readout for ds (17), dy, ds, dDskip, dx (2) and sigmoid (2 trans + 2)."""
-    return alu_ops_per_tc(False, False) + 16 * 13 + 17 + 1 + 1 + 1 + 2 + (2 * TRANS_SLOTS + 2)
+    g*B; g*Delta*x and its sum over channels; g *= abar: 13), per channel dy,
+    dDskip, dx (2) and sigmoid (2 trans + 2), and ds (1: ds is the contraction
+    of the unscaled dCm and dDskip with Cm and Dskip, so the readout y is not
+    needed)."""
+    return alu_ops_per_tc(False, False) + 16 * 13 + 1 + 1 + 2 + (2 * TRANS_SLOTS + 2) + 1
 
 
 class DenoiseBackward(Denoise):

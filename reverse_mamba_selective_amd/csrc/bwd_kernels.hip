@@ -76,7 +76,12 @@ __device__ __forceinline__ void row_channel_sum(float (&v)[kN / G]) {
     add_row_ror<8, NS>(v);
 }
 
-// DS: accumulate dout * y for ds (the readout y is recomputed only then).
+// DS: also ds = sum over tokens and channels of dout * y. With the readout's
+// partials dout * h and dDskip's dout * x taken before the gate's factor s
+// (which is applied to their sums), ds is their contraction with what they
+// multiply: the sum of Cm * dCm over the group's tokens, made where the block
+// sums its channels, and of Dskip * dDskip over its channels; y itself is
+// never recomputed, and s = 0 is no special case.
 template <bool REV, typename T, int G, bool SP, bool DS>
 __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
     constexpr int NS = kN / G;
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
     // lanes past the last channel shadow it; they must add nothing to any sum
     const float dys = lg.active ? p.dyscale : 0.0f;
     const float dxr = lg.active ? p.dxres : 0.0f;
-    const float dsw = (lg.active && sub == 0 && p.want_ds) ? 1.0f : 0.0f;
+    const float act = lg.active ? 1.0f : 0.0f;
     float dD = 0.0f, dsum = 0.0f;
 
     // per-token rows through raw buffer resources based at the sequence's first
@@ -269,14 +274,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 const float xv = E::widen(xr[j]);
                 const float gv = E::widen(gr[j]);
                 const float dy = dys * gv;
-                if constexpr (DS) {
-                    float yp = 0.0f;
-#pragma unroll
-                    for (int n = 0; n < NS; ++n) yp = fmaf(row[kN + n], hs[j][n], yp);
-                    const float y = fmaf(dsk, xv, group_sum<G>(yp));
-                    dsum = fmaf(dsw * gv, y, dsum);
-                }
-                dD = fmaf(dy, xv, dD);
+                const float wy = DS ? act * gv : dy;   // weight of the dCm and dDskip partials
+                dD = fmaf(wy, xv, dD);
                 const float dlx = delta[j] * xv;
                 float pb[NS], pc[NS];
                 // dDelta = sum_n g_n (B_n x + A_n abar_n h_prev_n)
@@ -285,7 +284,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
                     g[n] = fmaf(dy, row[kN + n], g[n]);
-                    pc[n] = dy * hs[j][n];
+                    pc[n] = wy * hs[j][n];
                     const float hp = j > 0 ? hs[j - 1][n] : hck[n];
                     const float a = ab[j][n];
                     const float gah = g[n] * (a * hp);
@@ -332,12 +331,18 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             {   // the block's sums over its channels: one thread per (token, column)
                 const int j = threadIdx.x / NBC, col = threadIdx.x % NBC;
                 float *dst = col < kN ? p.partB : p.partC;
-                if (j < gcnt && dst) {
+                if (j < gcnt && (dst || (DS && col >= kN))) {
                     float v = 0.0f;
 #pragma unroll
                     for (int w = 0; w < ROWS; ++w) v += rd_[w][j][col];
+                    if constexpr (DS) {
+                        if (col >= kN) {   // Cm * dCm, then dCm takes the factor s
+                            dsum = fmaf(v, bc[(gi * K + j) * NBC + col], dsum);
+                            v *= p.dyscale;
+                        }
+                    }
                     const int64_t t = sq.s0p + seg_row(sg, gpos + j);
-                    dst[(bg.tile * p.tokens + t) * kN + (col % kN)] = v;
+                    if (dst) dst[(bg.tile * p.tokens + t) * kN + (col % kN)] = v;
                 }
             }
             // no barrier here: the next group writes the other half of red, and
@@ -354,7 +359,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             if (p.dh_in) p.dh_in[st + n] = g[n];
             if (p.partA) p.partA[st + n] = dA[n];
         }
-        if (p.partD && sub == 0) p.partD[b * p.D + dl] = dD;
+        if (DS && sub == 0) dsum = fmaf(dsk, dD, dsum);   // Dskip * dDskip
+        if (p.partD && sub == 0) p.partD[b * p.D + dl] = DS ? p.dyscale * dD : dD;
     }
     if (p.partS) {   // uniform: every thread of the block reaches the barrier
         float v = dsum;
