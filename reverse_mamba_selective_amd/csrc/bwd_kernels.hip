@@ -267,10 +267,17 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 }
             }
 
-            // the adjoint over the group, last visited position first
+            // the adjoint over the group, last visited position first; a
+            // token's Bm and Cm slices come from LDS one token ahead of use
             R odx[K], oddt[K];
-            auto adjoint = [&](const int j) {
+            auto ldrow = [&](const int j, float4 &rb, float4 &rc) {
                 const float *row = bc + (gi * K + j) * NBC + sub * NS;   // Bm slice; Cm at + kN
+                rb = *reinterpret_cast<const float4 *>(row);
+                rc = *reinterpret_cast<const float4 *>(row + kN);
+            };
+            auto adjoint = [&](const int j, const float4 rb, const float4 rc) {
+                static_assert(NS == 4, "one Bm and one Cm quad per lane");
+                const float Bn[NS] = {rb.x, rb.y, rb.z, rb.w}, Cn[NS] = {rc.x, rc.y, rc.z, rc.w};
                 const float xv = E::widen(xr[j]);
                 const float gv = E::widen(gr[j]);
                 const float dy = dys * gv;
@@ -283,16 +290,15 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 float dd = 0.0f, dxs = 0.0f;
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
-                    g[n] = fmaf(dy, row[kN + n], g[n]);
+                    g[n] = fmaf(dy, Cn[n], g[n]);
                     pc[n] = wy * hs[j][n];
                     const float hp = j > 0 ? hs[j - 1][n] : hck[n];
-                    const float a = ab[j][n];
-                    const float gah = g[n] * (a * hp);
+                    dxs = fmaf(g[n], Bn[n], dxs);
+                    pb[n] = g[n] * dlx;
+                    g[n] *= ab[j][n];                    // carried to the earlier position
+                    const float gah = g[n] * hp;         // g abar h_prev
                     dA[n] = fmaf(gah, delta[j], dA[n]);
                     dd = fmaf(gah, An[n], dd);
-                    dxs = fmaf(g[n], row[n], dxs);
-                    pb[n] = g[n] * dlx;
-                    g[n] *= a;
                 }
                 const float ddelta = group_sum<G>(fmaf(xv, dxs, dd));
                 const float dxv = fmaf(delta[j], group_sum<G>(dxs), fmaf(dy, dsk, dxr * gv));
@@ -311,11 +317,19 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             };
             if (gcnt == K) {   // every group but a sequence's last: no branch per token
 #pragma unroll
-                for (int j = K - 1; j >= 0; --j) adjoint(j);
+                for (int j = K - 1; j >= 0; --j) {
+                    float4 rb, rc;
+                    ldrow(j, rb, rc);
+                    adjoint(j, rb, rc);
+                }
             } else {
 #pragma unroll
                 for (int j = K - 1; j >= 0; --j)
-                    if (j < gcnt) adjoint(j);
+                    if (j < gcnt) {
+                        float4 rb, rc;
+                        ldrow(j, rb, rc);
+                        adjoint(j, rb, rc);
+                    }
             }
             // the group's dx and ddt rows (lanes past the last channel store nothing)
             if (lg.active) {
