@@ -201,6 +201,8 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
 
     // tiles (and the groups inside them) from the last visited to the first
     const int ntiles = (ntok + kTile - 1) / kTile;
+    // the wave's slot on its SIMD (HW_ID bits 3:0), for the priority turns below
+    const int alt = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | 4) & 1);
     if (ntok > 0) {
         const int lb = (ntiles - 1) * kTile;
         stage_load(lb, ntok - lb);
@@ -219,11 +221,15 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
         for (int gi = (tcnt - 1) / K; gi >= 0; --gi) {
             const int gpos = tbase + gi * K;
             {   // groups left after this one: a wave with more left issues first, so
-                // the waves sharing a SIMD stay abreast (as in the segment scan)
+                // the waves sharing a SIMD stay abreast (as in the segment scan);
+                // before the last four, the two waves of a SIMD take turns at the
+                // higher of two levels (by the parity of their slot on the SIMD),
+                // which keeps long sequences abreast too
                 const int q = gpos / K;
-                if (q >= 3) __builtin_amdgcn_s_setprio(3);
-                else if (q == 2) __builtin_amdgcn_s_setprio(2);
-                else if (q == 1) __builtin_amdgcn_s_setprio(1);
+                const int pr = q >= 4 ? 2 + ((alt + q) & 1) : q;
+                if (pr >= 3) __builtin_amdgcn_s_setprio(3);
+                else if (pr == 2) __builtin_amdgcn_s_setprio(2);
+                else if (pr == 1) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
             }
             const int gcnt = ntok - gpos < K ? ntok - gpos : K;
