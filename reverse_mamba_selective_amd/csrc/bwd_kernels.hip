@@ -31,6 +31,9 @@
 //    so the result is deterministic (no atomics).
 //  * Bm / Cm rows are staged in LDS per tile of kTile tokens (double-buffered,
 //    walking the tiles backwards) as in the forward kernel.
+//  * softplus(dt) and its derivative are per channel: each of a channel's G
+//    lanes takes them for K / G of the group's tokens and quad broadcasts
+//    (DPP) hand Delta and sigmoid to the other lanes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +50,21 @@ using namespace dev;
 // +inf, which gives 1 or 0.
 __device__ __forceinline__ float sigmoid(float v) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+}
+
+// Lane l's value of each quad, to all four lanes of that quad (l is a constant
+// once the caller's loop is unrolled).
+template <int L>
+__device__ __forceinline__ float quad_lane(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), L * 0x55, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_bcast(float v, int l) {
+    switch (l) {
+        case 0: return quad_lane<0>(v);
+        case 1: return quad_lane<1>(v);
+        case 2: return quad_lane<2>(v);
+        default: return quad_lane<3>(v);
+    }
 }
 
 // Sum of v[] over the channels of each 16-lane row of a wave: the lanes of
@@ -172,7 +190,13 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
     // one) and the state entering it (its checkpoint; chunked phase 1: the
     // chunk-local checkpoint, the chunk's Delta sum up to it and the state
     // entering the chunk, combined when the group is consumed)
-    R nx[K], nd[K], ng[K];
+    // SP: each of a channel's G lanes loads dt only for the group's tokens j
+    // with j % G == sub and computes softplus and its derivative for them; the
+    // group's Delta and sigmoid rows then reach every lane of the channel by
+    // quad broadcasts (DPP), instead of all G lanes computing all K tokens
+    constexpr int OWN = SP ? K / G : 1;          // dt values per lane (SP)
+    static_assert(!SP || K % G == 0, "a group splits evenly over the channel's lanes");
+    R nx[K], nd[SP ? OWN : K], ng[K];
     float nck[NS], nH[NS], nS = 0.0f;
     const bool chunked = p.Hc != nullptr;
 #pragma unroll
@@ -182,8 +206,16 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
         for (int j = 0; j < K; ++j) {
             const uint32_t row = static_cast<uint32_t>(seg_row(sg, gpos + (j < gcnt ? j : gcnt - 1)));
             nx[j] = E::bload(rx, doff, row * xrb);
-            nd[j] = E::bload(rd, doff, row * drb);
+            if constexpr (!SP) nd[j] = E::bload(rd, doff, row * drb);
             ng[j] = E::bload(rg, doff, row * grb);
+        }
+        if constexpr (SP) {
+#pragma unroll
+            for (int k = 0; k < OWN; ++k) {   // this lane's tokens sub, sub + G, ...
+                const int jo = sub + G * k;
+                const uint32_t row = static_cast<uint32_t>(seg_row(sg, gpos + (jo < gcnt ? jo : gcnt - 1)));
+                nd[k] = E::bload(rd, doff + row * drb, 0);
+            }
         }
         const int64_t ckr = ckpt_row(b, sq.s0p, gpos);
         static_assert(NS == 4, "one checkpoint quad per lane");
@@ -235,14 +267,15 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             const int gcnt = ntok - gpos < K ? ntok - gpos : K;
             // this group's per-token inputs were requested during the previous
             // group; request the next group's (gpos - K) now
-            R xr[K], dr[K], gr[K];
+            R xr[K], dr[SP ? OWN : K], gr[K];
             float hck[NS];
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 xr[j] = nx[j];
-                dr[j] = nd[j];
                 gr[j] = ng[j];
             }
+#pragma unroll
+            for (int j = 0; j < (SP ? OWN : K); ++j) dr[j] = nd[j];
             if (chunked) {   // the chunk's entry state decayed over the chunk so far
 #pragma unroll
                 for (int n = 0; n < NS; ++n)
@@ -255,14 +288,26 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
             float (*rd_)[K][NBC] = red[gi & 1];
 
             // the group's states and decays, recomputed forward from the checkpoint
-            float hs[K][NS], ab[K][NS], delta[K];
+            float hs[K][NS], ab[K][NS], delta[K], sgm[SP ? K : 1];
+            if constexpr (SP) {
+                float dlo[OWN], slo[OWN];
+#pragma unroll
+                for (int k = 0; k < OWN; ++k) {
+                    const float dv = E::widen(dr[k]);
+                    dlo[k] = softplus(dv);
+                    slo[k] = sigmoid(dv);
+                }
+#pragma unroll
+                for (int j = 0; j < K; ++j) {   // from lane j % G of the channel's quad
+                    delta[j] = quad_bcast(dlo[j / G], j % G);
+                    sgm[j] = quad_bcast(slo[j / G], j % G);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < K; ++j) delta[j] = E::widen(dr[j]);
+            }
 #pragma unroll
             for (int j = 0; j < K; ++j) {
-                const float dv = E::widen(dr[j]);
-                if constexpr (SP)
-                    delta[j] = softplus(dv);
-                else
-                    delta[j] = dv;
                 const float dx_ = delta[j] * E::widen(xr[j]);
                 const float *brow = bc + (gi * K + j) * NBC + sub * NS;
 #pragma unroll
@@ -309,7 +354,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 const float ddelta = group_sum<G>(fmaf(xv, dxs, dd));
                 const float dxv = fmaf(delta[j], group_sum<G>(dxs), fmaf(dy, dsk, dxr * gv));
                 float ddtv = ddelta;
-                if constexpr (SP) ddtv *= sigmoid(E::widen(dr[j]));
+                if constexpr (SP) ddtv *= sgm[j];
                 odx[j] = E::pack(dxv);   // stored after the group: no branch per token
                 oddt[j] = E::pack(ddtv);
                 row_channel_sum<G>(pb);
