@@ -49,7 +49,7 @@ def check_grad(name, got_t, ref, dtype):
 
 
 def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None, reverse=True,
-             chunk_tokens=0):
+             chunk_tokens=0, softplus=True):
     dtype = dtype or inp.dtype
     B, D = inp.batch, inp.x.shape[1]
     rng = np.random.default_rng(seed)
@@ -61,7 +61,8 @@ def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None, re
               "separate": synth.scan_inputs(seed + 1, inp.lengths, D=D, dtype=dtype).x}[res_kind]
     ref = oracle.selective_scan_backward(
         inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=reverse, dout=dout_np,
-        dh_out=dh_out_np, res_kind=res_kind, s=s, seq_offsets=inp.offsets, h_in=h0)
+        dh_out=dh_out_np, res_kind=res_kind, s=s, seq_offsets=inp.offsets, h_in=h0,
+        delta_softplus=softplus)
 
     def shaped(t):
         if dense:
@@ -80,7 +81,7 @@ def run_case(inp, dense, res_kind, s, with_hin, with_dhout, seed, dtype=None, re
     g = bwd(x, **kw, dout=shaped(dev(dout_np, dtype)),
                               dh_out=dev32(dh_out_np) if with_dhout else None,
                               h_in=dev32(h0) if with_hin else None, res=res, s=s,
-                              chunk_tokens=chunk_tokens)
+                              chunk_tokens=chunk_tokens, delta_softplus=softplus)
     torch.cuda.synchronize()
     for name in ("dx", "ddt") + FP32_GRADS:
         check_grad(name, g[name], ref[name], dtype)
@@ -124,6 +125,18 @@ def test_backward_chunked_state_pass(gpu, dtype, chunk, reverse):
     for res_kind, with_hin in (("x", True), ("none", False)):
         run_case(inp, False, res_kind, 0.0 if res_kind == "none" else 0.6, with_hin, True,
                  seed=42, reverse=reverse, chunk_tokens=chunk)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_without_softplus(gpu, dtype):
+    """delta_softplus off: Delta is dt itself (positive draws). The backward
+    kernel's instantiation without softplus reads dt on every lane of a
+    channel for every token, the softplus one on one lane per token."""
+    lengths = [5, 0, 1, 8, 9, 64, 65]
+    inp = synth.scan_inputs(49, lengths, D=100, dtype=dtype, dt_mean=0.1, dt_std=0.02)
+    for res_kind in ("none", "x"):
+        run_case(inp, False, res_kind, 0.0 if res_kind == "none" else 0.4, with_hin=True,
+                 with_dhout=True, seed=50, softplus=False)
 
 
 def test_backward_long_few_channels(gpu):

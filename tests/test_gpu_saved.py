@@ -42,7 +42,8 @@ def device_inputs(inp, dense, dtype):
     return x, kw, shaped
 
 
-def run_saved(inp, dense, res_kind, s, with_hin, with_dhout, seed, chunk_tokens=0, reverse=True):
+def run_saved(inp, dense, res_kind, s, with_hin, with_dhout, seed, chunk_tokens=0, reverse=True,
+              softplus=True):
     """Saving forward, then the backward from its checkpoints; both against
     the oracle (reverse False: the left-to-right pair)."""
     dtype = inp.dtype
@@ -56,10 +57,11 @@ def run_saved(inp, dense, res_kind, s, with_hin, with_dhout, seed, chunk_tokens=
               "separate": synth.scan_inputs(seed + 1, inp.lengths, D=D, dtype=dtype).x}[res_kind]
     fwd = oracle.selective_scan(inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=reverse,
                                 seq_offsets=inp.offsets, h_in=h0, want_h_out=True, res=res_np,
-                                s=s, want_out=res_np is not None)
+                                s=s, want_out=res_np is not None, delta_softplus=softplus)
     ref = oracle.selective_scan_backward(
         inp.x, inp.dt, inp.Bm, inp.Cm, inp.A, inp.Dskip, reverse=reverse, dout=dout_np,
-        dh_out=dh_out_np, res_kind=res_kind, s=s, seq_offsets=inp.offsets, h_in=h0)
+        dh_out=dh_out_np, res_kind=res_kind, s=s, seq_offsets=inp.offsets, h_in=h0,
+        delta_softplus=softplus)
 
     x, kw, shaped = device_inputs(inp, dense, dtype)
     save = r2l.r2l_scan_save if reverse else r2l.prefix_scan_save
@@ -67,9 +69,11 @@ def run_saved(inp, dense, res_kind, s, with_hin, with_dhout, seed, chunk_tokens=
     res = None if res_np is None else (x if res_kind == "x" else shaped(dev(res_np, dtype)))
     h_in = dev32(h0) if with_hin else None
     h_out = torch.empty((B, D, 16), dtype=torch.float32, device="cuda")
-    out, ckpt = save(x, **kw, h_in=h_in, h_out=h_out, res=res, s=s, chunk_tokens=chunk_tokens)
+    out, ckpt = save(x, **kw, h_in=h_in, h_out=h_out, res=res, s=s, chunk_tokens=chunk_tokens,
+                     delta_softplus=softplus)
     g = bwd(x, **kw, dout=shaped(dev(dout_np, dtype)),
-            dh_out=dev32(dh_out_np) if with_dhout else None, h_in=h_in, res=res, s=s, ckpt=ckpt)
+            dh_out=dev32(dh_out_np) if with_dhout else None, h_in=h_in, res=res, s=s, ckpt=ckpt,
+            delta_softplus=softplus)
     torch.cuda.synchronize()
     if res is not None and s == 0.0:
         assert np.array_equal(bits(out), bits(res)), "s == 0: out is not res bit for bit"
@@ -95,6 +99,16 @@ def test_saved_ragged_edges(gpu, dtype, res_kind):
     for with_hin, with_dhout in ((False, False), (True, True)):
         run_saved(inp, False, res_kind, 0.0 if res_kind == "none" else 0.4, with_hin,
                   with_dhout, seed=52)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_saved_without_softplus(gpu, dtype):
+    """delta_softplus off (Delta = dt, positive draws): the saving forward and
+    the backward from its checkpoints, unchunked and chunked."""
+    inp = synth.scan_inputs(66, [5, 0, 1, 8, 9, 64, 65], D=100, dtype=dtype, dt_mean=0.1,
+                            dt_std=0.02)
+    for chunk in (0, 16):
+        run_saved(inp, False, "x", 0.4, True, True, seed=67, chunk_tokens=chunk, softplus=False)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
