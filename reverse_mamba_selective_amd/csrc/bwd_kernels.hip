@@ -318,8 +318,9 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 }
             }
 
-            // the adjoint over the group, last visited position first; a
-            // token's Bm and Cm slices come from LDS one token ahead of use
+            // the adjoint over the group, last visited position first (loading a
+            // token's Bm and Cm slices one token ahead, to hide the LDS latency,
+            // measured slower: 101 -> 109 us per denoising hook)
             R odx[K], oddt[K];
             auto ldrow = [&](const int j, float4 &rb, float4 &rc) {
                 const float *row = bc + (gi * K + j) * NBC + sub * NS;   // Bm slice; Cm at + kN
