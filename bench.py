@@ -1289,8 +1289,9 @@ WORKLOADS = {"denoise": Denoise, "prefill": Prefill, "ragged": RaggedServing,
 
 
 def build_info() -> dict:
-    """git commit and ROCm release of the build (the GPU machine has no .git:
-    there the file the build wrote is read), torch's HIP version."""
+    """git commit and ROCm release of the build (where the tree has no .git,
+    as on a machine the tree was copied to, the file the build wrote is
+    read), torch's HIP version."""
     info = {"git_sha": None, "git_dirty": None, "git_sha_from": None, "rocm": None}
     try:
         import subprocess
