@@ -318,9 +318,7 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                 }
             }
 
-            // the adjoint over the group, last visited position first (loading a
-            // token's Bm and Cm slices one token ahead, to hide the LDS latency,
-            // measured slower: 101 -> 109 us per denoising hook)
+            // the adjoint over the group, last visited position first
             R odx[K], oddt[K];
             auto ldrow = [&](const int j, float4 &rb, float4 &rc) {
                 const float *row = bc + (gi * K + j) * NBC + sub * NS;   // Bm slice; Cm at + kN
@@ -367,7 +365,23 @@ __global__ __launch_bounds__(kWG) void bwd_kernel(const BwdParams p) {
                     rw[kN + sub * NS + n] = pc[n];
                 }
             };
-            if (gcnt == K) {   // every group but a sequence's last: no branch per token
+            if (gcnt == K && DS) {
+                // every group but a sequence's last: no branch per token; the
+                // slices of the token before are requested before this token's
+                // arithmetic, so their LDS round trip overlaps it (the compiler
+                // otherwise waits on each token's read 4 instructions after
+                // issuing it): the denoising hook's backward from saved
+                // checkpoints 76.5 -> 73.3 us. Without ds the same order makes
+                // the compiler spill 173 scalar registers into vector lanes
+                // (prefill backward +16%), so that instance keeps the plain one.
+                float4 rb[2], rc[2];   // token j's slices in [j & 1]
+                ldrow(K - 1, rb[(K - 1) & 1], rc[(K - 1) & 1]);
+#pragma unroll
+                for (int j = K - 1; j >= 0; --j) {
+                    if (j > 0) ldrow(j - 1, rb[(j - 1) & 1], rc[(j - 1) & 1]);
+                    adjoint(j, rb[j & 1], rc[j & 1]);
+                }
+            } else if (gcnt == K) {
 #pragma unroll
                 for (int j = K - 1; j >= 0; --j) {
                     float4 rb, rc;
