@@ -41,10 +41,24 @@ R2L_HD BlockGeom block_geom(int64_t nblocks, int32_t tiles, int32_t nchunks, int
     if (logical >= nb) return g;
     g.valid = true;
     const uint32_t t = static_cast<uint32_t>(tiles), nc = static_cast<uint32_t>(nchunks);
-    g.tile = static_cast<int>(logical % t);
-    const uint32_t seg = logical / t;
-    g.c = static_cast<int>(seg % nc);
-    g.b = static_cast<int64_t>(seg / nc);
+    // An integer division by a runtime value is ~20 scalar instructions at
+    // every wave's start; the common shapes take the short ways (a power-of-two
+    // tile count, one chunk).
+    uint32_t seg;
+    if ((t & (t - 1)) == 0) {
+        g.tile = static_cast<int>(logical & (t - 1));
+        seg = logical >> __builtin_ctz(t);
+    } else {
+        g.tile = static_cast<int>(logical % t);
+        seg = logical / t;
+    }
+    if (nc == 1) {
+        g.c = 0;
+        g.b = static_cast<int64_t>(seg);
+    } else {
+        g.c = static_cast<int>(seg % nc);
+        g.b = static_cast<int64_t>(seg / nc);
+    }
     return g;
 }
 
