@@ -73,6 +73,30 @@ class Checker {
                             (unsigned long long)(t->lo + 4 * w));
     }
 
+    // The launch's grid covers its work exactly once: its valid blocks map one
+    // to one onto the (sequence, chunk, tile) triples of `nblocks` =
+    // sequences x chunks x tiles.
+    void cover_blocks(const char *what, int64_t nblocks, int32_t tiles, int32_t nchunks) {
+        if (failed_ || nblocks <= 0) return;
+        std::vector<bool> seen(static_cast<size_t>(nblocks), false);
+        for (int64_t bid = 0; bid < padded_grid(nblocks); ++bid) {
+            const BlockGeom bg = block_geom(nblocks, tiles, nchunks, bid);
+            if (!bg.valid) continue;
+            const int64_t at = (bg.b * nchunks + bg.c) * tiles + bg.tile;
+            if (bg.tile < 0 || bg.tile >= tiles || bg.c < 0 || bg.c >= nchunks || at < 0 ||
+                at >= nblocks || seen[static_cast<size_t>(at)])
+                return fail("%s: block %lld takes sequence %lld, chunk %d, tile %d: outside the "
+                            "grid's work or taken twice", what, (long long)bid, (long long)bg.b,
+                            bg.c, bg.tile);
+            seen[static_cast<size_t>(at)] = true;
+        }
+        for (int64_t i = 0; i < nblocks; ++i)
+            if (!seen[static_cast<size_t>(i)])
+                return fail("%s: no block takes sequence %lld, chunk %lld, tile %lld", what,
+                            (long long)(i / (int64_t(tiles) * nchunks)), (long long)((i / tiles) % nchunks),
+                            (long long)(i % tiles));
+    }
+
     void fail(const char *fmt, ...) __attribute__((format(printf, 2, 3))) {
         if (failed_) return;
         failed_ = true;
@@ -122,6 +146,7 @@ void check_segment(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const Region *rW = to_ws && !lrows ? ck.region_of(p.yws) : nullptr;
     const Region *rAdd = (l.mode & kModeAdd) && !lrows ? ck.region_of(p.yadd) : nullptr;
 
+    ck.cover_blocks("segment launch", p.nblocks, p.tiles, p.nchunks);
     for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
         const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, bid);
         if (!bg.valid) continue;
@@ -347,6 +372,7 @@ void check_backward(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const Region *rCk = p.ckpt ? ck.region_of(p.ckpt) : nullptr;
     const Region *rHo = p.dh_out ? ck.region_of(p.dh_out) : nullptr;
     const Region *rHi = p.dh_in ? ck.region_of(p.dh_in) : nullptr;
+    ck.cover_blocks("backward launch", p.nblocks, p.tiles, 1);
     for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
         const BlockGeom bg = block_geom(p.nblocks, p.tiles, 1, bid);
         if (!bg.valid) continue;
@@ -636,6 +662,7 @@ void check_conv(Checker &ck, const Launch &l, const int32_t *cu_host) {
     const Region *rx = ck.region_of(p.x), *ru = ck.region_of(p.u), *rw = ck.region_of(p.w);
     const Region *rb = p.b ? ck.region_of(p.b) : nullptr;
     if (p.K < 1 || p.K > kConvMaxTaps) return ck.fail("conv: %d taps", p.K);
+    ck.cover_blocks("conv launch", p.nblocks, p.tiles, p.nchunks);
     for (int64_t bid = 0; bid < padded_grid(p.nblocks) && ck.ok(); ++bid) {
         const BlockGeom bg = block_geom(p.nblocks, p.tiles, p.nchunks, bid);
         if (!bg.valid) continue;
